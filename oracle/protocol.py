@@ -1,0 +1,396 @@
+"""Protocol oracle: pipeline cursor, mbarrier model and an interleaving checker.
+
+Test infrastructure only (see the package docstring).
+
+Sources (pages, by title and section):
+  * "cute（12）async_pipeline"
+      - section 2 (PipelineState: the (index, phase, count) cursor, its ++ and
+        the producer start state with phase 1) and section 6.1 (the batch
+        ``advance`` rule);
+      - sections 6.2-6.9 (empty barrier = arrival count only; full barrier =
+        arrivals plus transaction bytes; wait(p) passes once the barrier's
+        phase differs from p; producer_acquire / consumer_wait /
+        consumer_release / producer_tail);
+      - section 7 (the full barrier timeline of 3 stages and 8 tiles).
+  * "chapter_async_barriers" (mlc.ai), sections "mbarrier" and "phase 如何区分
+    不同轮次": init sets phase 0 and the pending count; a phase completes when
+    the pending arrivals and the transaction count are both zero; the parity
+    table for a 2-stage ring.
+  * "cuda-features-10-pipelines", section 4.10.2-4.10.3: acquire/commit on the
+    producer side, wait/release on the consumer side; releasing early lets the
+    producer overwrite live data.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+# --------------------------------------------------------------------------
+# Cursor
+# --------------------------------------------------------------------------
+@dataclass
+class PipelineState:
+    """Ring cursor over ``stages`` slots: which slot, which phase parity, how many steps."""
+
+    stages: int
+    index: int = 0
+    phase: int = 0
+    count: int = 0
+
+    def inc(self) -> "PipelineState":
+        """One step: next slot; wrapping from the last slot to 0 flips the phase."""
+        self.index += 1
+        self.count += 1
+        if self.index == self.stages:
+            self.index = 0
+            self.phase ^= 1
+        return self
+
+    def advance(self, n: int) -> "PipelineState":
+        """n steps at once.
+
+        Fewer than ``stages`` steps flip the phase iff they cross the end of
+        the ring; ``stages`` or more steps flip it iff the number of ring
+        boundaries crossed, (index + n) // stages, is odd.
+        """
+        S = self.stages
+        if n < S and self.index + n >= S:
+            self.phase ^= 1
+        if n >= S and ((self.index + n) // S) % 2 == 1:
+            self.phase ^= 1
+        self.index = (self.index + n) % S
+        self.count += n
+        return self
+
+    def tup(self):
+        return (self.index, self.phase, self.count)
+
+    def copy(self) -> "PipelineState":
+        return PipelineState(self.stages, self.index, self.phase, self.count)
+
+
+def producer_start_state(stages: int) -> PipelineState:
+    """Slot 0, phase 1, count 0: the ring starts empty, so the first lap never waits."""
+    return PipelineState(stages, 0, 1, 0)
+
+
+def consumer_start_state(stages: int) -> PipelineState:
+    return PipelineState(stages, 0, 0, 0)
+
+
+def cursor_after(stages: int, k: int, start_phase: int) -> tuple:
+    """(index, phase) of a cursor after k single steps from (0, start_phase)."""
+    st = PipelineState(stages, 0, start_phase, 0)
+    for _ in range(k):
+        st.inc()
+    return (st.index, st.phase)
+
+
+# --------------------------------------------------------------------------
+# mbarrier model
+# --------------------------------------------------------------------------
+class MBarrier:
+    """Arrival counter + phase + transaction-byte counter.
+
+    ``init(n)``: phase 0, n pending arrivals. A phase completes (phase flips,
+    pending reloads to n) when pending arrivals and outstanding transaction
+    bytes are both zero. ``try_wait(p)`` succeeds once the phase is not p.
+    """
+
+    def __init__(self, expected: int):
+        self.expected = expected
+        self.pending = expected
+        self.phase = 0
+        self.tx = 0
+        self.completions = 0
+
+    def _settle(self):
+        if self.pending == 0 and self.tx == 0:
+            self.phase ^= 1
+            self.pending = self.expected
+            self.completions += 1
+
+    def arrive(self):
+        self.pending -= 1
+        self._settle()
+
+    def arrive_and_expect_tx(self, nbytes: int):
+        self.tx += nbytes
+        self.pending -= 1
+        self._settle()
+
+    def complete_tx(self, nbytes: int):
+        self.tx -= nbytes
+        self._settle()
+
+    def try_wait(self, parity: int) -> bool:
+        return self.phase != parity
+
+    def state(self):
+        return (self.pending, self.phase, self.tx)
+
+
+# --------------------------------------------------------------------------
+# Lock-step timeline (the order in which the pages walk through the ring)
+# --------------------------------------------------------------------------
+def lockstep_timeline(stages: int, tiles: int, tile_bytes: int = 16384,
+                      consumers: int = 1):
+    """Run producer and consumers one tile at a time and record each handshake.
+
+    Per tile: the producer acquires (waits on empty), arrives with expect_tx,
+    the copy lands (complete_tx), the consumers wait on full and release
+    empty. Returns one dict per tile with the cursor values and barrier phase
+    changes, the quantities printed in the pages' timeline table.
+    """
+    full = [MBarrier(1) for _ in range(stages)]
+    empty = [MBarrier(consumers) for _ in range(stages)]
+    w = producer_start_state(stages)
+    r = consumer_start_state(stages)
+    rows = []
+    for t in range(tiles):
+        s = w.index
+        row = {"tile": t, "write": (w.index, w.phase), "empty_wait_arg": w.phase,
+               "empty_phase_seen": empty[s].phase,
+               "producer_blocked": not empty[s].try_wait(w.phase)}
+        assert empty[s].try_wait(w.phase), "lock-step schedule never blocks"
+        f0 = full[s].phase
+        full[s].arrive_and_expect_tx(tile_bytes)
+        assert full[s].phase == f0, "arrival alone must not complete the phase"
+        full[s].complete_tx(tile_bytes)
+        row["full_flip"] = (f0, full[s].phase)
+        assert r.index == s
+        row["read"] = (r.index, r.phase)
+        row["full_wait_arg"] = r.phase
+        row["full_phase_seen"] = full[s].phase
+        assert full[s].try_wait(r.phase)
+        e0 = empty[s].phase
+        for _ in range(consumers):
+            empty[s].arrive()
+        row["empty_flip"] = (e0, empty[s].phase)
+        rows.append(row)
+        w.inc()
+        r.inc()
+    return rows
+
+
+def parity_walk(stages: int, iterations: int):
+    """Single-waiter walk over a ring of full barriers with one phase variable.
+
+    The waiter uses slot ``it % stages``, waits on the current phase variable
+    and flips that variable after the last slot of each lap. Returns
+    (iteration, slot, parity waited on, barrier parity after completion,
+    phase variable after the iteration).
+    """
+    bars = [MBarrier(1) for _ in range(stages)]
+    phase_var = 0
+    out = []
+    for it in range(iterations):
+        s = it % stages
+        waited = phase_var
+        bars[s].arrive()  # the phase this iteration waits for completes
+        assert bars[s].try_wait(waited)
+        if s == stages - 1:
+            phase_var ^= 1
+        out.append((it, s, waited, bars[s].phase, phase_var))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Explicit-state checker of the full/empty protocol
+# --------------------------------------------------------------------------
+@dataclass
+class ProtocolResult:
+    states: int
+    deadlock: bool
+    completed: bool
+    violations: list
+    max_ahead: int
+
+
+def _producer_program(S, T, mode, lag, start_phase, tail):
+    ops = []
+    cur = PipelineState(S, 0, start_phase, 0)
+    if mode == "tx":
+        for t in range(T):
+            ops.append(("wait_empty", cur.index, cur.phase))
+            ops.append(("arrive_tx", cur.index))
+            ops.append(("issue", t, cur.index))
+            cur.inc()
+    elif mode == "landed":
+        for t in range(T):
+            ops.append(("wait_empty", cur.index, cur.phase))
+            ops.append(("issue", t, cur.index))
+            u = t - lag
+            if u >= 0:
+                ops.append(("wait_landed", u))
+                ops.append(("arrive_full", u % S))
+            cur.inc()
+        for u in range(max(0, T - lag), T):
+            ops.append(("wait_landed", u))
+            ops.append(("arrive_full", u % S))
+    else:
+        raise ValueError(mode)
+    if tail:
+        for _ in range(S):
+            ops.append(("wait_empty", cur.index, cur.phase))
+            cur.inc()
+    return ops
+
+
+def _consumer_program(S, T, release_before_read):
+    ops = []
+    cur = PipelineState(S, 0, 0, 0)
+    for t in range(T):
+        ops.append(("wait_full", cur.index, cur.phase))
+        if release_before_read:
+            ops.append(("arrive_empty", cur.index))
+            ops.append(("read", t, cur.index))
+        else:
+            ops.append(("read", t, cur.index))
+            ops.append(("arrive_empty", cur.index))
+        cur.inc()
+    return ops
+
+
+def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
+                   producer_start_phase: int = 1, full_expected: int = 1,
+                   empty_expected=None, release_before_read: bool = False,
+                   tail: bool = True, tile_bytes: int = 16384,
+                   max_states: int = 2_000_000) -> ProtocolResult:
+    """Explore every interleaving of one producer, C consumers and the copy engine.
+
+    ``mode="tx"``: the producer arrives with expect_tx before issuing the copy
+    and the copy's landing performs complete_tx (the mbarrier design).
+    ``mode="landed"``: the producer issues the copy, and ``lag`` tiles later
+    waits until it has landed and then arrives on full (a counter barrier with
+    no transaction bytes).
+
+    Checked: (I1) a consumer reads a slot only after that tile landed;
+    (I2) a slot is not overwritten before all consumers of its previous tile
+    are done with it; (I3) no reachable deadlock and all tiles consumed;
+    (I4) the producer is at most S tiles ahead of the slowest consumer.
+    """
+    if empty_expected is None:
+        empty_expected = C
+    P = _producer_program(S, T, mode, lag, producer_start_phase, tail)
+    Q = _consumer_program(S, T, release_before_read)
+    nP, nQ = len(P), len(Q)
+    nbar = 2 * S
+
+    def bar_exp(b):
+        return full_expected if b < S else empty_expected
+
+    def settle(bars, b):
+        pend, ph, tx = bars[b]
+        if pend == 0 and tx == 0:
+            bars[b] = (bar_exp(b), ph ^ 1, 0)
+
+    init_bars = tuple((bar_exp(b), 0, 0) for b in range(nbar))
+    init = (0, (0,) * C, init_bars, (None,) * S, frozenset())
+    seen = {init}
+    stack = [init]
+    violations = set()
+    deadlock = False
+    completed = False
+    max_ahead = 0
+
+    def released_tiles(qpc):
+        # tiles whose arrive_empty has executed: 3 ops per tile
+        done = qpc // 3
+        if qpc % 3 == 2 and release_before_read:
+            done += 1
+        return done
+
+    while stack:
+        if len(seen) > max_states:
+            raise RuntimeError("state bound exceeded")
+        st = stack.pop()
+        ppc, qpcs, bars, slots, inflight = st
+        succ = []
+        # producer
+        if ppc < nP:
+            op = P[ppc]
+            kind = op[0]
+            if kind == "wait_empty":
+                _, s, ph = op
+                if bars[S + s][1] != ph:
+                    succ.append((ppc + 1, qpcs, bars, slots, inflight))
+            elif kind == "arrive_tx":
+                s = op[1]
+                b = list(bars)
+                pend, ph, tx = b[s]
+                b[s] = (pend - 1, ph, tx + tile_bytes)
+                settle(b, s)
+                succ.append((ppc + 1, qpcs, tuple(b), slots, inflight))
+            elif kind == "issue":
+                _, t, s = op
+                slowest = min(released_tiles(q) for q in qpcs)
+                ahead = (t + 1) - slowest
+                max_ahead = max(max_ahead, ahead)
+                if ahead > S:
+                    violations.add(("I4", t, ahead))
+                sl = list(slots)
+                sl[s] = (t, False)
+                succ.append((ppc + 1, qpcs, bars, tuple(sl), inflight | {t}))
+            elif kind == "wait_landed":
+                u = op[1]
+                if u not in inflight:
+                    succ.append((ppc + 1, qpcs, bars, slots, inflight))
+            elif kind == "arrive_full":
+                s = op[1]
+                b = list(bars)
+                pend, ph, tx = b[s]
+                b[s] = (pend - 1, ph, tx)
+                settle(b, s)
+                succ.append((ppc + 1, qpcs, tuple(b), slots, inflight))
+        # copy engine: any in-flight tile may land
+        for t in inflight:
+            s = t % S
+            sl = list(slots)
+            if sl[s] == (t, False):
+                sl[s] = (t, True)
+            b = bars
+            if mode == "tx":
+                b = list(bars)
+                pend, ph, tx = b[s]
+                b[s] = (pend, ph, tx - tile_bytes)
+                settle(b, s)
+                b = tuple(b)
+            succ.append((ppc, qpcs, b, tuple(sl), inflight - {t}))
+        # consumers
+        for c in range(C):
+            qpc = qpcs[c]
+            if qpc >= nQ:
+                continue
+            op = Q[qpc]
+            kind = op[0]
+            nq = qpcs[:c] + (qpc + 1,) + qpcs[c + 1:]
+            if kind == "wait_full":
+                _, s, ph = op
+                if bars[s][1] != ph:
+                    succ.append((ppc, nq, bars, slots, inflight))
+            elif kind == "read":
+                _, t, s = op
+                if slots[s] != (t, True):
+                    tag = "I1" if slots[s] == (t, False) else "I2"
+                    violations.add((tag, t, c, slots[s]))
+                succ.append((ppc, nq, bars, slots, inflight))
+            elif kind == "arrive_empty":
+                s = op[1]
+                b = list(bars)
+                pend, ph, tx = b[S + s]
+                b[S + s] = (pend - 1, ph, tx)
+                settle(b, S + s)
+                succ.append((ppc, nq, tuple(b), slots, inflight))
+        if not succ:
+            if ppc == nP and all(q == nQ for q in qpcs) and not inflight:
+                completed = True
+            else:
+                deadlock = True
+            continue
+        for n in succ:
+            if n not in seen:
+                seen.add(n)
+                stack.append(n)
+    return ProtocolResult(len(seen), deadlock, completed and not deadlock,
+                          sorted(violations, key=repr), max_ahead)

@@ -1,0 +1,127 @@
+"""Pins of the protocol oracle against the pages' printed tables, closed forms
+and exhaustive exploration (CPU)."""
+import pytest
+
+from oracle import protocol as P
+from tests.conftest import golden_lines
+
+
+def _golden(name):
+    out = {}
+    for ln in golden_lines("cursor_3stage.txt"):
+        k, *v = ln.split()
+        out.setdefault(k, []).append(tuple(int(x) for x in v))
+    return out[name]
+
+
+def test_consumer_increment_table():
+    st = P.consumer_start_state(3)
+    seq = [st.tup()]
+    for _ in range(6):
+        seq.append(st.inc().tup())
+    assert seq == _golden("consumer_inc")
+
+
+def test_producer_and_consumer_tile_lists():
+    assert [P.cursor_after(3, k, 1) for k in range(8)] == _golden("producer_tile")
+    assert [P.cursor_after(3, k, 0) for k in range(5)] == _golden("consumer_tile")
+    assert [P.cursor_after(3, k, 1) for k in range(4)] == _golden("trace_producer")
+    assert [P.cursor_after(3, k, 0) for k in range(4)] == _golden("trace_consumer")
+    assert P.producer_start_state(3).tup() == (0, 1, 0)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
+def test_advance_equals_repeated_increment(S):
+    for i0 in range(S):
+        for p0 in (0, 1):
+            for n in range(0, 40):
+                a = P.PipelineState(S, i0, p0, 7).advance(n)
+                b = P.PipelineState(S, i0, p0, 7)
+                for _ in range(n):
+                    b.inc()
+                assert a.tup() == b.tup(), (S, i0, p0, n)
+                # closed form: index (i0+n) mod S, phase flips per lap crossed
+                assert a.tup() == ((i0 + n) % S, p0 ^ (((i0 + n) // S) & 1), 7 + n)
+
+
+def test_timeline_matches_page_table():
+    rows = golden_lines("timeline_3stage_8tiles.csv")[1:]
+    got = P.lockstep_timeline(3, 8)
+    for ln, g in zip(rows, got):
+        v = [int(x) for x in ln.split(",")]
+        assert v[0] == g["tile"]
+        assert (v[1], v[2]) == g["write"]
+        assert v[3] == g["empty_phase_seen"]
+        assert (v[4], v[5]) == g["full_flip"]
+        assert (v[6], v[7]) == g["read"]
+        assert v[8] == g["full_phase_seen"]
+        assert (v[9], v[10]) == g["empty_flip"]
+        assert g["empty_wait_arg"] == g["write"][1]
+        assert g["full_wait_arg"] == g["read"][1]
+    assert len(got) == len(rows) == 8
+
+
+def test_parity_walk_matches_page_table():
+    rows = [tuple(int(x) for x in ln.split(",")) for ln in golden_lines("parity_2stage.csv")[1:]]
+    assert P.parity_walk(2, 4) == rows
+
+
+def test_mbarrier_needs_arrivals_and_bytes():
+    b = P.MBarrier(1)
+    b.arrive_and_expect_tx(2048)
+    assert b.phase == 0
+    b.complete_tx(1024)
+    assert b.phase == 0
+    b.complete_tx(1024)
+    assert b.phase == 1 and b.pending == 1 and b.tx == 0
+    # two copies of 2048 bytes complete one phase only when both landed
+    b2 = P.MBarrier(1)
+    b2.arrive_and_expect_tx(4096)
+    b2.complete_tx(2048)
+    assert not b2.try_wait(0)
+    b2.complete_tx(2048)
+    assert b2.try_wait(0)
+
+
+@pytest.mark.parametrize("S,T,C", [(1, 4, 1), (1, 3, 3), (2, 5, 2), (2, 4, 3), (3, 7, 1),
+                                   (3, 5, 2), (3, 4, 3)])
+@pytest.mark.parametrize("mode", ["tx", "landed"])
+def test_protocol_safe_and_live(S, T, C, mode):
+    r = P.check_protocol(S, T, C, mode=mode, lag=S - 1 if mode == "landed" else 0)
+    assert r.completed and not r.deadlock
+    assert r.violations == []
+    assert r.max_ahead <= S
+    # the ring fills completely in some interleaving (producer S tiles ahead)
+    assert r.max_ahead == min(S, T)
+
+
+def test_start_phase_zero_deadlocks():
+    r = P.check_protocol(3, 4, 2, producer_start_phase=0)
+    assert r.deadlock and not r.completed
+
+
+def test_full_expected_arrivals_mismatch_deadlocks():
+    r = P.check_protocol(3, 4, 1, full_expected=32)
+    assert r.deadlock and not r.completed
+
+
+def test_release_before_read_overwrites_live_data():
+    r = P.check_protocol(2, 4, 2, release_before_read=True)
+    assert any(v[0] == "I2" for v in r.violations)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_commit_lag_rule(S):
+    """A counter barrier without transaction bytes: committing tile t-L after
+    issuing tile t is live iff L <= S-1."""
+    for L in range(0, S + 1):
+        r = P.check_protocol(S, S + 2, 1, mode="landed", lag=L)
+        if L <= S - 1:
+            assert r.completed and r.violations == [], (S, L)
+        else:
+            assert r.deadlock, (S, L)
+
+
+def test_no_tail_still_consumes_everything():
+    r = P.check_protocol(2, 3, 2, tail=False)
+    assert r.completed

@@ -1,0 +1,53 @@
+"""Swizzle model pins: the page's printed CuTe layout, bijection, involution (CPU)."""
+import re
+
+import pytest
+
+from oracle import swizzle as Z
+from tests.conftest import golden_lines
+
+
+def _parse_layout():
+    ln = golden_lines("tile_layout_128x64.txt")[0]
+    B, M, S = (int(x) for x in re.match(r"Sw<(\d+),(\d+),(\d+)>", ln).groups())
+    nums = [int(x) for x in re.findall(r"_(\d+)", ln.split(" o ")[-1])]
+    # ((r0,r1),(c0,c1)):((sr0,sr1),(sc0,sc1))
+    r0, r1, c0, c1, sr0, sr1, sc0, sc1 = nums
+    return (B, M, S), (r0, r1, c0, c1), (sr0, sr1, sc0, sc1)
+
+
+def test_page_layout_is_128B_chunk_xor():
+    (B, M, S), (r0, r1, c0, c1), (sr0, sr1, sc0, sc1) = _parse_layout()
+    assert (r0 * r1, c0 * c1) == (128, 64)
+    sw = Z.cute_swizzle(B, M, S)
+    for r in range(128):
+        for c in range(64):
+            elem = (r % r0) * sr0 + (r // r0) * sr1 + (c % c0) * sc0 + (c // c0) * sc1
+            assert sw(2 * elem) == Z.slot_byte_address(r, c, shift=0)
+            assert Z.page_tile_byte_address(r, c) == Z.slot_byte_address(r, c, shift=0)
+
+
+@pytest.mark.parametrize("shift", [0, 1, 2])
+def test_chunk_swizzle_bijective_involution(shift):
+    seen = set()
+    for r in range(128):
+        for c in range(8):
+            p = Z.chunk_position(r, c, shift)
+            assert 0 <= p < 8
+            assert Z.chunk_position(r, p, shift) == c  # involution
+            seen.add((r, p))
+    assert len(seen) == 128 * 8
+    addrs = {Z.slot_byte_address(r, c, shift) for r in range(128) for c in range(64)}
+    assert addrs == set(range(0, 16384, 2))
+
+
+def test_bank_model_basics():
+    contiguous = [16 * l for l in range(64)]
+    assert Z.bank_conflicts(contiguous, 16, nbanks=32) == 0
+    assert Z.bank_conflicts(contiguous, 16, nbanks=64) == 0
+    column = [128 * l for l in range(64)]  # same chunk of 64 rows, no swizzle
+    assert Z.bank_conflicts(column, 16, nbanks=32) > 0
+    swz = [Z.slot_byte_address(l, 0, 0) for l in range(64)]
+    assert Z.bank_conflicts(swz, 16, nbanks=32) == 0
+    broadcast = [64] * 64
+    assert Z.bank_conflicts(broadcast, 4, nbanks=32) == 0
