@@ -1,0 +1,278 @@
+"""Python binding of libpipetile.so (the pipelined tile stream for MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+the shared library. PyTorch supplies device memory and the current stream.
+The functions carry the C ABI's names (``include/pipe_tile.h``):
+
+    pipe_tile_copy(src, dst=None, checksums=False, **cfg)  -> dst [, checksums]
+    pipe_rowsum(A, out=None, workspace=None, **cfg)        -> out
+    pipe_gemm_mainloop(A, B, C=None, **cfg)                -> C
+    pipe_query_kernel(op, M, N, K=0, **cfg)                -> dict
+    pipe_rowsum_workspace_bytes(M, N, **cfg)               -> int
+    pipe_device_status(clear=False)                        -> int
+
+``cfg`` keywords are the fields of ``pipe_config_t`` (stages, consumer_waves,
+grid, split, swizzle_shift, flags, spin_limit, trace, status, ...).
+
+If the shared library has not been built, every call raises ``PipeBuildError``:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libpipetile.so")
+
+PIPE_OK = 0
+PIPE_ERR_NULL = 1
+PIPE_ERR_SHAPE = 2
+PIPE_ERR_ALIGN = 3
+PIPE_ERR_STAGES = 4
+PIPE_ERR_CONFIG = 5
+PIPE_ERR_WORKSPACE = 6
+PIPE_ERR_HIP = 7
+PIPE_ERR_TIMEOUT = 8
+
+PIPE_OP_COPY = 0
+PIPE_OP_ROWSUM = 1
+PIPE_OP_GEMM = 2
+
+PIPE_FLAG_TRACE = 0x1
+PIPE_FLAG_ROW_STRIPS = 0x2
+PIPE_FLAG_TEST_START_PHASE0 = 0x100
+PIPE_FLAG_TEST_NO_RELEASE = 0x200
+
+PIPE_STATUS_TIMEOUT_PRODUCER = 0x1
+PIPE_STATUS_TIMEOUT_CONSUMER = 0x2
+
+PIPE_TRACE_WORDS = 8
+
+
+class PipeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class PipeBuildError(RuntimeError):
+    pass
+
+
+class pipe_config_t(ctypes.Structure):
+    _fields_ = [
+        ("stages", ctypes.c_int32),
+        ("tile_m", ctypes.c_int32),
+        ("tile_n", ctypes.c_int32),
+        ("tile_k", ctypes.c_int32),
+        ("producer_waves", ctypes.c_int32),
+        ("consumer_waves", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("split", ctypes.c_int32),
+        ("swizzle_shift", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("spin_limit", ctypes.c_uint32),
+        ("trace_capacity", ctypes.c_int32),
+        ("trace", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+class pipe_kernel_info_t(ctypes.Structure):
+    _fields_ = [
+        ("lds_bytes", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("items", ctypes.c_int32),
+        ("tiles_per_item", ctypes.c_int32),
+        ("split", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+_c = ctypes
+_SIGS = {
+    "pipe_abi_version": (_c.c_int, []),
+    "pipe_status_str": (_c.c_char_p, [_c.c_int]),
+    "pipe_config_default": (_c.c_int, [_c.c_int, _c.POINTER(pipe_config_t)]),
+    "pipe_tile_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
+                                  _c.c_int64, _c.POINTER(pipe_config_t), _c.c_void_p,
+                                  _c.c_void_p]),
+    "pipe_rowsum_workspace_bytes": (_c.c_int, [_c.c_int64, _c.c_int64,
+                                               _c.POINTER(pipe_config_t),
+                                               _c.POINTER(_c.c_size_t)]),
+    "pipe_rowsum": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
+                               _c.POINTER(pipe_config_t), _c.c_void_p, _c.c_size_t,
+                               _c.c_void_p]),
+    "pipe_gemm_mainloop": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                                      _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                      _c.c_int64, _c.POINTER(pipe_config_t), _c.c_void_p]),
+    "pipe_query_kernel": (_c.c_int, [_c.c_int, _c.POINTER(pipe_config_t), _c.c_int64,
+                                     _c.c_int64, _c.c_int64, _c.POINTER(pipe_kernel_info_t)]),
+    "pipe_device_status": (_c.c_int, [_c.POINTER(_c.c_uint32), _c.c_int]),
+}
+
+
+def lib():
+    """The loaded shared library (loaded once; raises PipeBuildError if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise PipeBuildError(
+                    f"{LIB_PATH} is missing: build it with `python -m async_stage_tile_amd.build`"
+                    " (or __graft_entry__.build())")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def abi_version() -> int:
+    return int(lib().pipe_abi_version())
+
+
+def status_str(status: int) -> str:
+    return lib().pipe_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != PIPE_OK:
+        raise PipeError(status, where)
+
+
+def make_config(op: int, **kw) -> pipe_config_t:
+    cfg = pipe_config_t()
+    _check(lib().pipe_config_default(op, ctypes.byref(cfg)), "pipe_config_default")
+    for k, v in kw.items():
+        if k in ("trace", "status"):
+            v = _ptr(v) if v is not None else None
+        if not hasattr(cfg, k):
+            raise TypeError(f"unknown config field {k!r}")
+        setattr(cfg, k, v)
+    return cfg
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(int(s.cuda_stream))
+
+
+def _check_matrix(t, name, dtypes):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} dtype {t.dtype} not in {dtypes}")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D row-major tensor (unit column stride)")
+    return t.shape[0], t.shape[1], max(t.stride(0), t.shape[1])
+
+
+def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):
+    """Copy a 16-bit matrix through the tile ring; optionally per-tile code sums."""
+    import torch
+    M, N, ld_src = _check_matrix(src, "src", (torch.float16, torch.bfloat16, torch.int16))
+    if dst is None:
+        dst = torch.empty_like(src, memory_format=torch.contiguous_format)
+    Md, Nd, ld_dst = _check_matrix(dst, "dst", (src.dtype,))
+    if (Md, Nd) != (M, N):
+        raise ValueError("dst shape differs from src")
+    chk = None
+    if checksums:
+        chk = torch.empty((M // 128) * (N // 64), dtype=torch.int32, device=src.device)
+    c = make_config(PIPE_OP_COPY, **cfg)
+    st = lib().pipe_tile_copy(_ptr(src), _ptr(dst), M, N, ld_src, ld_dst, ctypes.byref(c),
+                              _ptr(chk), _stream(stream))
+    _check(st, "pipe_tile_copy")
+    return (dst, chk) if checksums else dst
+
+
+def pipe_rowsum_workspace_bytes(M, N, **cfg) -> int:
+    c = make_config(PIPE_OP_ROWSUM, **cfg)
+    out = ctypes.c_size_t(0)
+    _check(lib().pipe_rowsum_workspace_bytes(M, N, ctypes.byref(c), ctypes.byref(out)),
+           "pipe_rowsum_workspace_bytes")
+    return int(out.value)
+
+
+def pipe_rowsum(A, out=None, workspace=None, stream=None, **cfg):
+    """fp32 row sums of an fp16 matrix streamed through the tile ring."""
+    import torch
+    M, N, lda = _check_matrix(A, "A", (torch.float16,))
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=A.device)
+    need = pipe_rowsum_workspace_bytes(M, N, **cfg)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = make_config(PIPE_OP_ROWSUM, **cfg)
+    st = lib().pipe_rowsum(_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c), _ptr(workspace),
+                           wbytes, _stream(stream))
+    _check(st, "pipe_rowsum")
+    return out
+
+
+def pipe_gemm_mainloop(A, B, C=None, stream=None, **cfg):
+    """C = A @ B (bf16 in, fp32 accumulate and out) with A/B tiles fed through the ring."""
+    import torch
+    M, K, lda = _check_matrix(A, "A", (torch.bfloat16,))
+    K2, N, ldb = _check_matrix(B, "B", (torch.bfloat16,))
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32,))
+    if (Mc, Nc) != (M, N):
+        raise ValueError("C shape mismatch")
+    c = make_config(PIPE_OP_GEMM, **cfg)
+    st = lib().pipe_gemm_mainloop(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                  ctypes.byref(c), _stream(stream))
+    _check(st, "pipe_gemm_mainloop")
+    return C
+
+
+def pipe_query_kernel(op: int, M: int, N: int, K: int = 0, **cfg) -> dict:
+    c = make_config(op, **cfg)
+    info = pipe_kernel_info_t()
+    _check(lib().pipe_query_kernel(op, ctypes.byref(c), M, N, K, ctypes.byref(info)),
+           "pipe_query_kernel")
+    return {f: getattr(info, f) for f, _ in pipe_kernel_info_t._fields_}
+
+
+def pipe_device_status(clear: bool = False) -> int:
+    out = ctypes.c_uint32(0)
+    _check(lib().pipe_device_status(ctypes.byref(out), 1 if clear else 0), "pipe_device_status")
+    return int(out.value)
+
+
+# short aliases
+tile_copy = pipe_tile_copy
+rowsum = pipe_rowsum
+gemm_mainloop = pipe_gemm_mainloop
+query_kernel = pipe_query_kernel
+device_status = pipe_device_status

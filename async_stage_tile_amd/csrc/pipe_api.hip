@@ -1,0 +1,368 @@
+// C ABI of the pipelined tile stream: argument validation, launch geometry and
+// dispatch. Validation happens before any HIP call, so the library can be
+// loaded and its argument checks exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/pipe_tile.h"
+#include "pipe_kernels.hpp"
+
+namespace {
+
+using namespace pipe;
+
+__device__ uint32_t g_status_word;
+
+constexpr uint32_t kDefaultSpin = 1u << 22;
+constexpr int kMaxDevices = 64;
+constexpr int kLdsLimit = 163840;
+constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS |
+                                 PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
+
+std::mutex g_status_mu;
+uint32_t* g_status_ptr[kMaxDevices] = {nullptr};
+
+// Address of this device's library status word (looked up once per device).
+pipe_status_t library_status_word(uint32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PIPE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_status_mu);
+  if (g_status_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_status_word)) != hipSuccess || p == nullptr)
+      return PIPE_ERR_HIP;
+    g_status_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_status_ptr[dev];
+  return PIPE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+pipe_config_t defaults(pipe_op_t op) {
+  pipe_config_t c{};
+  c.stages = 3;
+  c.tile_m = 128;
+  c.tile_n = (op == PIPE_OP_GEMM) ? 128 : 64;
+  c.tile_k = (op == PIPE_OP_GEMM) ? 64 : 0;
+  c.producer_waves = (op == PIPE_OP_GEMM) ? 2 : 1;
+  c.consumer_waves = (op == PIPE_OP_GEMM) ? 4 : 3;
+  c.grid = 0;
+  c.split = 0;
+  c.swizzle_shift = 0;
+  c.flags = 0;
+  c.spin_limit = 0;
+  c.trace_capacity = 0;
+  c.trace = nullptr;
+  c.status = nullptr;
+  return c;
+}
+
+pipe_status_t check_common(const pipe_config_t& c) {
+  if (c.flags & ~kKnownFlags) return PIPE_ERR_CONFIG;
+  if (c.grid < 0 || c.split < 0 || c.swizzle_shift < 0 || c.swizzle_shift > 3)
+    return PIPE_ERR_CONFIG;
+  if (c.trace_capacity < 0) return PIPE_ERR_CONFIG;
+  if ((c.flags & PIPE_FLAG_TRACE) && (c.trace == nullptr || c.trace_capacity == 0))
+    return PIPE_ERR_NULL;
+  if (c.status != nullptr && !aligned4(c.status)) return PIPE_ERR_ALIGN;
+  if (c.trace != nullptr && !aligned4(c.trace)) return PIPE_ERR_ALIGN;
+  return PIPE_OK;
+}
+
+pipe_status_t check_stream_cfg(const pipe_config_t& c) {
+  pipe_status_t s = check_common(c);
+  if (s != PIPE_OK) return s;
+  if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
+  if (c.tile_m != 128 || c.tile_n != 64) return PIPE_ERR_CONFIG;
+  if (c.producer_waves != 1) return PIPE_ERR_CONFIG;
+  const int cw = c.consumer_waves;
+  if (!(cw == 1 || cw == 2 || cw == 3 || cw == 4 || cw == 8)) return PIPE_ERR_CONFIG;
+  if (stream_lds_bytes(c.stages, cw) > kLdsLimit) return PIPE_ERR_STAGES;
+  return PIPE_OK;
+}
+
+struct StreamGeom {
+  int32_t tile_rows, tile_cols, n_strips, strip_len, seg_len, split, items, grid;
+};
+
+// Rowsum default split: the smallest power of two that gives >= 512 work items.
+int rowsum_default_split(int n_strips, int strip_len) {
+  int split = 1;
+  while ((int64_t)n_strips * split < 512 && split < strip_len) split *= 2;
+  return split < strip_len ? split : strip_len;
+}
+
+pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool row_strips,
+                              bool rowsum, StreamGeom* g) {
+  const int64_t tr = M / 128, tc = N / 64;
+  if (tr > INT32_MAX || tc > INT32_MAX) return PIPE_ERR_SHAPE;
+  g->tile_rows = (int32_t)tr;
+  g->tile_cols = (int32_t)tc;
+  g->n_strips = row_strips ? g->tile_rows : g->tile_cols;
+  g->strip_len = row_strips ? g->tile_cols : g->tile_rows;
+  int split = c.split;
+  if (split == 0) split = rowsum ? rowsum_default_split(g->n_strips, g->strip_len) : 1;
+  if (split > g->strip_len) split = g->strip_len;
+  if (split < 1) split = 1;
+  g->seg_len = (g->strip_len + split - 1) / split;
+  g->split = (g->strip_len + g->seg_len - 1) / g->seg_len;  // no empty segments
+  const int64_t items = (int64_t)g->n_strips * g->split;
+  if (items > INT32_MAX) return PIPE_ERR_SHAPE;
+  g->items = (int32_t)items;
+  g->grid = (c.grid == 0 || c.grid > g->items) ? g->items : c.grid;
+  return PIPE_OK;
+}
+
+void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_strips,
+                        StreamParams* p) {
+  p->tile_rows = g.tile_rows;
+  p->tile_cols = g.tile_cols;
+  p->n_strips = g.n_strips;
+  p->strip_len = g.strip_len;
+  p->seg_len = g.seg_len;
+  p->split = g.split;
+  p->items = g.items;
+  p->row_strips = row_strips ? 1 : 0;
+  p->swz_shift = c.swizzle_shift;
+  p->lag = c.stages - 1 < 2 ? c.stages - 1 : 2;
+  p->spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
+  p->start_phase = (c.flags & PIPE_FLAG_TEST_START_PHASE0) ? 0u : 1u;
+  p->no_release = (c.flags & PIPE_FLAG_TEST_NO_RELEASE) ? 1 : 0;
+  p->trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
+  p->trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
+}
+
+pipe_status_t resolve_status(const pipe_config_t& c, uint32_t** out) {
+  if (c.status != nullptr) {
+    *out = c.status;
+    return PIPE_OK;
+  }
+  return library_status_word(out);
+}
+
+pipe_status_t hip_status(hipError_t e) { return e == hipSuccess ? PIPE_OK : PIPE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int pipe_abi_version(void) { return PIPE_ABI_VERSION; }
+
+const char* pipe_status_str(int status) {
+  switch (status) {
+    case PIPE_OK: return "ok";
+    case PIPE_ERR_NULL: return "null pointer";
+    case PIPE_ERR_SHAPE: return "unsupported shape";
+    case PIPE_ERR_ALIGN: return "misaligned pointer or pitch";
+    case PIPE_ERR_STAGES: return "stage count out of range or ring exceeds LDS";
+    case PIPE_ERR_CONFIG: return "unsupported configuration";
+    case PIPE_ERR_WORKSPACE: return "workspace missing or too small";
+    case PIPE_ERR_HIP: return "HIP runtime error";
+    case PIPE_ERR_TIMEOUT: return "pipeline wait timed out";
+    default: return "unknown status";
+  }
+}
+
+pipe_status_t pipe_config_default(pipe_op_t op, pipe_config_t* cfg) {
+  if (cfg == nullptr) return PIPE_ERR_NULL;
+  if (op != PIPE_OP_COPY && op != PIPE_OP_ROWSUM && op != PIPE_OP_GEMM) return PIPE_ERR_CONFIG;
+  *cfg = defaults(op);
+  return PIPE_OK;
+}
+
+pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, int64_t ld_src,
+                             int64_t ld_dst, const pipe_config_t* cfg, uint32_t* tile_checksums,
+                             void* stream) {
+  const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_COPY);
+  pipe_status_t s = check_stream_cfg(c);
+  if (s != PIPE_OK) return s;
+  if (M < 0 || N < 0 || ld_src < N || ld_dst < N) return PIPE_ERR_SHAPE;
+  if (M % 128 != 0 || N % 64 != 0) return PIPE_ERR_SHAPE;
+  if (M == 0 || N == 0) return PIPE_OK;
+  if (src == nullptr || dst == nullptr) return PIPE_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst) || (ld_src % 8) || (ld_dst % 8)) return PIPE_ERR_ALIGN;
+  if (tile_checksums != nullptr && !aligned4(tile_checksums)) return PIPE_ERR_ALIGN;
+  const bool row_strips = (c.flags & PIPE_FLAG_ROW_STRIPS) != 0;
+  StreamGeom g;
+  s = stream_geometry(M, N, c, row_strips, false, &g);
+  if (s != PIPE_OK) return s;
+
+  StreamParams p{};
+  fill_stream_params(c, g, row_strips, &p);
+  p.src = static_cast<const uint8_t*>(src);
+  p.dst = static_cast<uint8_t*>(dst);
+  p.out = nullptr;
+  p.checksums = tile_checksums;
+  p.ld_src = ld_src * 2;
+  p.ld_dst = ld_dst * 2;
+  p.M = M;
+  s = resolve_status(c, &p.status);
+  if (s != PIPE_OK) return s;
+  return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, g.grid, p,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_config_t* cfg,
+                                          size_t* bytes) {
+  if (bytes == nullptr) return PIPE_ERR_NULL;
+  const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
+  pipe_status_t s = check_stream_cfg(c);
+  if (s != PIPE_OK) return s;
+  if (M < 0 || N < 0 || M % 128 != 0 || N % 64 != 0) return PIPE_ERR_SHAPE;
+  *bytes = 0;
+  if (M == 0 || N == 0) return PIPE_OK;
+  StreamGeom g;
+  s = stream_geometry(M, N, c, true, true, &g);
+  if (s != PIPE_OK) return s;
+  *bytes = g.split > 1 ? (size_t)g.split * (size_t)M * sizeof(float) : 0;
+  return PIPE_OK;
+}
+
+pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
+                          const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
+  pipe_status_t s = check_stream_cfg(c);
+  if (s != PIPE_OK) return s;
+  if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // always row strips
+  if (M < 0 || N < 0 || lda < N) return PIPE_ERR_SHAPE;
+  if (M % 128 != 0 || N % 64 != 0) return PIPE_ERR_SHAPE;
+  if (M == 0) return PIPE_OK;
+  if (out == nullptr) return PIPE_ERR_NULL;
+  if (!aligned4(out)) return PIPE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(launch_fill_f32(out, M, 1, 1, 0.f, st));
+  if (A == nullptr) return PIPE_ERR_NULL;
+  if (!aligned16(A) || (lda % 8)) return PIPE_ERR_ALIGN;
+  StreamGeom g;
+  s = stream_geometry(M, N, c, true, true, &g);
+  if (s != PIPE_OK) return s;
+  const size_t need = g.split > 1 ? (size_t)g.split * (size_t)M * sizeof(float) : 0;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return PIPE_ERR_WORKSPACE;
+    if (!aligned4(workspace)) return PIPE_ERR_ALIGN;
+  }
+  StreamParams p{};
+  fill_stream_params(c, g, true, &p);
+  p.src = static_cast<const uint8_t*>(A);
+  p.dst = nullptr;
+  p.out = need > 0 ? static_cast<float*>(workspace) : out;
+  p.checksums = nullptr;
+  p.ld_src = lda * 2;
+  p.ld_dst = 0;
+  p.M = M;
+  s = resolve_status(c, &p.status);
+  if (s != PIPE_OK) return s;
+  s = hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, g.grid, p, st));
+  if (s != PIPE_OK || need == 0) return s;
+  return hip_status(launch_rowsum_finalize(static_cast<const float*>(workspace), out, M,
+                                           g.split, st));
+}
+
+pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t M, int64_t N,
+                                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                 const pipe_config_t* cfg, void* stream) {
+  const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_GEMM);
+  pipe_status_t s = check_common(c);
+  if (s != PIPE_OK) return s;
+  if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
+  if (c.tile_m != 128 || c.tile_n != 128 || c.tile_k != 64) return PIPE_ERR_CONFIG;
+  if (c.producer_waves != 2 || c.consumer_waves != 4) return PIPE_ERR_CONFIG;
+  if (c.split > 1) return PIPE_ERR_CONFIG;
+  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE)) return PIPE_ERR_CONFIG;
+  if (gemm_lds_bytes(c.stages) > kLdsLimit) return PIPE_ERR_STAGES;
+  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return PIPE_ERR_SHAPE;
+  if (M % 128 != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
+  if (M == 0 || N == 0) return PIPE_OK;
+  if (C == nullptr) return PIPE_ERR_NULL;
+  if (!aligned4(C)) return PIPE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (K == 0) return hip_status(launch_fill_f32(C, M, N, ldc, 0.f, st));
+  if (A == nullptr || B == nullptr) return PIPE_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return PIPE_ERR_ALIGN;
+  GemmParams p{};
+  p.A = static_cast<const uint8_t*>(A);
+  p.B = static_cast<const uint8_t*>(B);
+  p.C = C;
+  p.lda = lda * 2;
+  p.ldb = ldb * 2;
+  p.ldc = ldc;
+  p.M = (int32_t)M;
+  p.N = (int32_t)N;
+  p.K = (int32_t)K;
+  p.tiles_m = (int32_t)(M / 128);
+  p.tiles_n = (int32_t)(N / 128);
+  p.k_steps = (int32_t)(K / 64);
+  const int64_t items = (int64_t)p.tiles_m * p.tiles_n;
+  if (items > INT32_MAX) return PIPE_ERR_SHAPE;
+  p.items = (int32_t)items;
+  p.swz_shift = c.swizzle_shift;
+  p.spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
+  p.trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
+  p.trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
+  if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
+  const int grid = (c.grid == 0 || c.grid > p.items) ? p.items : c.grid;
+  s = resolve_status(c, &p.status);
+  if (s != PIPE_OK) return s;
+  return hip_status(launch_gemm(c.stages, grid, p, st));
+}
+
+pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
+                                int64_t K, pipe_kernel_info_t* info) {
+  if (info == nullptr) return PIPE_ERR_NULL;
+  const pipe_config_t c = cfg ? *cfg : defaults(op);
+  *info = pipe_kernel_info_t{};
+  if (op == PIPE_OP_GEMM) {
+    pipe_status_t s = check_common(c);
+    if (s != PIPE_OK) return s;
+    if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
+    if (M < 0 || N < 0 || K < 0 || M % 128 || N % 128 || K % 64) return PIPE_ERR_SHAPE;
+    const int64_t items = (M / 128) * (N / 128);
+    if (items > INT32_MAX) return PIPE_ERR_SHAPE;
+    info->lds_bytes = gemm_lds_bytes(c.stages);
+    info->threads = 64 * 6;
+    info->items = (int32_t)items;
+    info->grid = (c.grid == 0 || c.grid > info->items) ? info->items : c.grid;
+    info->tiles_per_item = (int32_t)(K / 64);
+    info->split = 1;
+    return PIPE_OK;
+  }
+  if (op != PIPE_OP_COPY && op != PIPE_OP_ROWSUM) return PIPE_ERR_CONFIG;
+  pipe_status_t s = check_stream_cfg(c);
+  if (s != PIPE_OK) return s;
+  if (M < 0 || N < 0 || M % 128 || N % 64) return PIPE_ERR_SHAPE;
+  const bool rowsum = op == PIPE_OP_ROWSUM;
+  const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);
+  info->lds_bytes = stream_lds_bytes(c.stages, c.consumer_waves);
+  info->threads = 64 * (1 + c.consumer_waves);
+  if (M == 0 || N == 0) return PIPE_OK;
+  StreamGeom g;
+  s = stream_geometry(M, N, c, row_strips, rowsum, &g);
+  if (s != PIPE_OK) return s;
+  info->grid = g.grid;
+  info->items = g.items;
+  info->tiles_per_item = g.seg_len;
+  info->split = g.split;
+  return PIPE_OK;
+}
+
+pipe_status_t pipe_device_status(uint32_t* out, int clear) {
+  if (out == nullptr) return PIPE_ERR_NULL;
+  uint32_t* word = nullptr;
+  pipe_status_t s = library_status_word(&word);
+  if (s != PIPE_OK) return s;
+  if (hipMemcpy(out, word, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return PIPE_ERR_HIP;
+  if (clear) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(word, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess)
+      return PIPE_ERR_HIP;
+  }
+  return PIPE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// Device primitives of the pipelined tile stream (gfx950 / CDNA4).
+//
+// What the pages describe and how it maps onto one gfx950 workgroup:
+//   * Ring of S stage slots in shared memory, each with a "full" and an
+//     "empty" barrier ("cute（12）async_pipeline", sections 1 and 6.4).
+//     Here: S slots in LDS, and one 32-bit LDS word per barrier.
+//   * mbarrier = pending-arrival count + phase bit; the arrival that completes
+//     a phase flips the phase and reloads the count; wait(p) passes once the
+//     phase is no longer p ("cute（12）async_pipeline" 6.2; mlc.ai
+//     "chapter_async_barriers", section mbarrier). Here: bit 31 of the LDS word
+//     is the phase, bits 0..30 count arrivals of the current phase; the last
+//     arriver adds (2^31 - expected), which clears the count and flips bit 31
+//     in one atomic step. gfx950 has no transaction-byte counter, so the
+//     producer arrives on "full" only after `s_waitcnt vmcnt` shows that the
+//     stage's loads have landed in LDS: arrivals == 0 and bytes == 0 collapse
+//     into one arrival.
+//   * PipelineState (index, phase, count) with ++ wrapping the index and
+//     flipping the phase; producers start at phase 1 so the first lap never
+//     waits ("cute（12）async_pipeline" 2.2-2.3, 6.1). Kept in SGPRs (the
+//     control path is wave-uniform, as "cuda-features-10-pipelines" 4.10.4
+//     asks of the pipeline's control flow).
+//   * One waiter per wave polls the barrier word (the single-poller rule of
+//     "cute（11）hopper之TMA_copy" 3.4): a uniform-address ds_read_b32
+//     broadcasts to all lanes, then `s_sleep` between polls. Every wait is
+//     bounded: after `spin_limit` polls it records a timeout and the wave
+//     abandons the stream, so a broken handshake ends the kernel instead of
+//     hanging the device.
+//   * The copy engine is the gfx950 direct-to-LDS load
+//     (global_load_lds_dwordx4): the LDS destination is M0 + lane*16 (wave
+//     uniform), only the global address is per lane. It is issued from inline
+//     asm so that the compiler's wait-count pass, which cannot tell the ring
+//     slots from the barrier words, does not put `s_waitcnt vmcnt(0)` in front
+//     of every barrier access.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pipe {
+
+constexpr int kWave = 64;
+constexpr int kTileRows = 128;                            // tile_m
+constexpr int kTileCols = 64;                             // tile_n (fp16 elements)
+constexpr int kRowBytes = kTileCols * 2;                  // 128 B per tile row
+constexpr int kChunkBytes = 16;                           // one b128 access
+constexpr int kChunksPerRow = kRowBytes / kChunkBytes;    // 8
+constexpr int kTileBytes = kTileRows * kRowBytes;         // 16384
+constexpr int kBlockBytes = kWave * kChunkBytes;          // 1024 = one wave-wide DMA
+constexpr int kBlocksPerTile = kTileBytes / kBlockBytes;  // 16
+constexpr int kRowsPerBlock = kBlockBytes / kRowBytes;    // 8
+
+constexpr uint32_t kPhaseBit = 0x80000000u;
+
+// Status bits written to the caller's status word.
+constexpr uint32_t kStatusTimeoutProducer = 1u;
+constexpr uint32_t kStatusTimeoutConsumer = 2u;
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const lds_u8*)(p));
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// ---------------------------------------------------------------------------
+// PipelineState: ring cursor, wave-uniform.
+// ---------------------------------------------------------------------------
+struct PipeState {
+  int index;
+  uint32_t phase;
+  uint32_t count;
+  int stages;
+
+  __device__ __forceinline__ void inc() {
+    ++index;
+    ++count;
+    if (index == stages) {
+      index = 0;
+      phase ^= 1u;
+    }
+  }
+};
+
+__device__ __forceinline__ PipeState producer_start(int stages, uint32_t start_phase) {
+  return PipeState{0, start_phase, 0u, stages};
+}
+__device__ __forceinline__ PipeState consumer_start(int stages) {
+  return PipeState{0, 0u, 0u, stages};
+}
+
+// ---------------------------------------------------------------------------
+// LDS barrier word: bit 31 = phase, bits 0..30 = arrivals in this phase.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bar_read(uint32_t* bar) {
+  return __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// One arrival on behalf of the whole wave (lane 0 performs it). Returns the
+// number of arrivals of this phase that preceded it (wave-uniform).
+__device__ __forceinline__ uint32_t bar_arrive(uint32_t* bar, uint32_t expected) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t before = 0;
+  if (lane_id() == 0) {
+    uint32_t old = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = old & ~kPhaseBit;
+    if (before + 1u == expected) {
+      // Completes the phase: count back to 0, phase bit flips.
+      __hip_atomic_fetch_add(bar, kPhaseBit - expected, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return uniform(before);
+}
+
+// Wait until the barrier's phase differs from `phase`. Returns false on timeout.
+__device__ __forceinline__ bool bar_wait(uint32_t* bar, uint32_t phase, uint32_t spin_limit) {
+  uint32_t polls = 0;
+  while (true) {
+    uint32_t w = uniform(bar_read(bar));
+    if ((w >> 31) != phase) break;
+    if (++polls >= spin_limit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Wait counters (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14]).
+// ---------------------------------------------------------------------------
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// s_waitcnt vmcnt(16 * k) for a wave-uniform k in [0, 3].
+__device__ __forceinline__ void wait_vmcnt_tiles(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<16>(); break;
+    case 2: wait_vmcnt<32>(); break;
+    default: wait_vmcnt<48>(); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Copy engine: one wave-wide direct-to-LDS load of 64 x 16 B.
+// Lane l's 16 bytes land at LDS address m0 + 16*l.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void dma_block(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "{m0}"(lds_base)
+               : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Swizzle: the 16-byte chunk c of tile row r lives at chunk position
+// c ^ ((r >> shift) & 7) of that row (shift 0 = the 128-byte pattern of the
+// page's Sw<3,4,3> layout). An involution, so position -> chunk is the same map.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r, int c, int shift) {
+  return c ^ ((r >> shift) & (kChunksPerRow - 1));
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums.
+// ---------------------------------------------------------------------------
+// Sum over each aligned group of 8 lanes (DPP quad permutes + half mirror).
+__device__ __forceinline__ float sum8_lanes(float v) {
+  int x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false)); // row_half_mirror
+  return v;
+}
+
+// Integer sum over all 64 lanes, result in every lane.
+__device__ __forceinline__ uint32_t sum64_lanes_u32(uint32_t v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace pipe

@@ -1,0 +1,233 @@
+// GEMM mainloop fed by the tile ring: C = A * B, bf16 inputs, fp32 accumulate.
+//
+// The ring is the one of the tile stream ("cute（12）async_pipeline", sections
+// 1-3 and 6): per stage two producer waves move the A tile (128 x 64) and the
+// B tile (64 x 128) of one 64-deep K step into slot `index` with
+// direct-to-LDS loads; each waits for its copy to land and arrives on
+// full[index], which expects both arrivals (a stage is complete only when all
+// its copies have landed, as in the two-copy example of
+// "chapter_async_barriers", section 常见的同步规则). Four consumer waves each
+// own a 64 x 64 quarter of the 128 x 128 output tile, wait on full, run
+// 4 x (2 x 2) v_mfma_f32_32x32x16_bf16 per stage, release empty, and write
+// their fp32 accumulators to C after the last K step.
+//
+// Why two producer waves: each stage is 32 wave-wide DMA instructions. One
+// wave keeping a second stage in flight would need more than the 63
+// outstanding loads vmcnt can count; split over two waves (A and B), each
+// keeps up to 2 stages of lag with at most 48 loads outstanding.
+//
+// LDS layout of a stage: A rows of 128 B with 16-byte chunk c of row r at
+// position c ^ ((r >> shift) & 7) (the MFMA A fragment reads one chunk of 32
+// consecutive rows, so the XOR spreads them across banks); B rows of 256 B
+// (128 bf16), unswizzled.
+//
+// MFMA 32x32x16 operand layout (lane l, element e): A[i][k] with i = l % 32,
+// k = 8 * (l / 32) + e; B[k][j] with j = l % 32, k = 8 * (l / 32) + e; the
+// 16 accumulators hold D[i][j] with j = l % 32,
+// i = 8 * (e / 4) + 4 * (l / 32) + e % 4.
+#include "pipe_device.hpp"
+#include "pipe_kernels.hpp"
+
+namespace pipe {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmTile = 128;
+constexpr int kGemmK = 64;
+constexpr int kAStageBytes = kGemmTile * kGemmK * 2;  // 16 KiB
+constexpr int kBStageBytes = kGemmK * kGemmTile * 2;  // 16 KiB
+constexpr int kBRowBytes = kGemmTile * 2;             // 256
+constexpr int kGemmThreads = 64 * 6;                  // 2 producer + 4 consumer waves
+
+template <int S>
+struct GemmLds {
+  uint8_t a[S][kAStageBytes];
+  uint8_t b[S][kBStageBytes];
+  uint32_t full[S];
+  uint32_t empty[S];
+};
+
+__device__ __forceinline__ void gemm_tile_of(const GemmParams& p, int item, int& tm, int& tn) {
+  tm = item / p.tiles_n;
+  tn = item % p.tiles_n;
+}
+
+template <int S>
+__device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int role) {
+  const int lane = lane_id();
+  PipeState w = producer_start(S, 1u);
+  const int lag = S - 1 < 2 ? S - 1 : 2;
+  int pending = 0;
+  bool ok = true;
+  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+    int tm, tn;
+    gemm_tile_of(p, item, tm, tn);
+    const uint8_t* ga = p.A + (int64_t)tm * kGemmTile * p.lda;
+    const uint8_t* gb = p.B + (int64_t)tn * kBRowBytes;
+    for (int ks = 0; ks < p.k_steps; ++ks) {
+      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      if (role == 0) {
+        const uint32_t sa = uniform(lds_addr(&lds.a[w.index][0]));
+        const uint8_t* a0 = ga + (int64_t)ks * kGemmK * 2;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          // A: rows 8q..8q+7, lane -> (row 8q + l/8, position l%8).
+          const int r = q * 8 + (lane >> 3);
+          const int c = swz(r, lane & 7, p.swz_shift);
+          dma_block(a0 + (int64_t)r * p.lda + c * 16, sa + q * kBlockBytes);
+        }
+      } else {
+        const uint32_t sb = uniform(lds_addr(&lds.b[w.index][0]));
+        const uint8_t* b0 = gb + (int64_t)ks * kGemmK * p.ldb;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          // B: rows 4q..4q+3 of 256 B, lane -> (row 4q + l/16, chunk l%16).
+          const int r = q * 4 + (lane >> 4);
+          dma_block(b0 + (int64_t)r * p.ldb + (lane & 15) * 16, sb + q * kBlockBytes);
+        }
+      }
+      ++pending;
+      if (pending > lag) {
+        wait_vmcnt_tiles(pending - 1);
+        int oldest = w.index - (pending - 1);
+        if (oldest < 0) oldest += S;
+        bar_arrive(&lds.full[oldest], 2u);
+        --pending;
+      }
+      w.inc();
+    }
+  }
+  while (pending > 0) {
+    wait_vmcnt_tiles(pending - 1);
+    int oldest = w.index - pending;
+    if (oldest < 0) oldest += S;
+    bar_arrive(&lds.full[oldest], 2u);
+    --pending;
+  }
+  if (ok) {
+    for (int i = 0; i < S; ++i) {
+      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      w.inc();
+    }
+  }
+  wait_vmcnt<0>();
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutProducer);
+}
+
+__device__ __forceinline__ bf16x8 load_b_column(const uint8_t* bslot, int k0, int col) {
+  // 8 consecutive K values of one B column (row-major B): a strided gather.
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(bslot) + col;
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t x = base[(k0 + e) * kGemmTile];
+    v[e] = __builtin_bit_cast(__bf16, x);
+  }
+  return v;
+}
+
+template <int S>
+__device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
+  const int lane = lane_id();
+  const int wm = cw >> 1, wn = cw & 1;
+  const int li = lane & 31, lk = lane >> 5;
+  PipeState rd = consumer_start(S);
+  bool ok = true;
+  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+    int tm, tn;
+    gemm_tile_of(p, item, tm, tn);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int ks = 0; ks < p.k_steps; ++ks) {
+      if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      const uint8_t* sa = &lds.a[rd.index][0];
+      const uint8_t* sb = &lds.b[rd.index][0];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 af[2], bfr[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int r = wm * 64 + mi * 32 + li;
+          const int c = swz(r, kk * 2 + lk, p.swz_shift);
+          af[mi] = *reinterpret_cast<const bf16x8*>(sa + r * 128 + c * 16);
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          bfr[ni] = load_b_column(sb, kk * 16 + lk * 8, wn * 64 + ni * 32 + li);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      }
+      wait_lgkmcnt0();
+      bar_arrive(&lds.empty[rd.index], 4u);
+      rd.inc();
+    }
+    if (!ok) break;
+    // Epilogue: fp32 accumulators -> C.
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int col = tn * kGemmTile + wn * 64 + ni * 32 + li;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = tm * kGemmTile + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+          p.C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+        }
+      }
+  }
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
+}
+
+template <int S>
+__global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmParams p) {
+  __shared__ GemmLds<S> lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  if (threadIdx.x < S) {
+    lds.full[threadIdx.x] = 0u;
+    lds.empty[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  if (wave < 2)
+    gemm_producer<S>(p, lds, wave);
+  else
+    gemm_consumer<S>(p, lds, wave - 2);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int stages, int grid, const GemmParams& p, hipStream_t stream) {
+  const dim3 g(grid), b(kGemmThreads);
+  switch (stages) {
+    case 1: hipLaunchKernelGGL(gemm_kernel<1>, g, b, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(gemm_kernel<2>, g, b, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(gemm_kernel<3>, g, b, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(gemm_kernel<4>, g, b, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int gemm_lds_bytes(int stages) { return stages * (kAStageBytes + kBStageBytes) + stages * 8; }
+
+}  // namespace pipe

@@ -1,0 +1,66 @@
+// Kernel parameter blocks and launchers shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pipe {
+
+enum StreamOp : int { kOpCopy = 0, kOpRowsum = 1 };
+
+struct StreamParams {
+  const uint8_t* src;     // copy source / rowsum input (fp16)
+  uint8_t* dst;           // copy destination
+  float* out;             // rowsum: final sums (split 1) or segment partials [split][M]
+  uint32_t* checksums;    // copy: per-tile code sums (nullable)
+  uint32_t* trace;        // nullable
+  uint32_t* status;       // never null
+  int64_t ld_src;         // row pitch, bytes
+  int64_t ld_dst;         // row pitch, bytes
+  int64_t M;              // rows (rowsum partial stride)
+  int32_t tile_rows;      // M / 128
+  int32_t tile_cols;      // N / 64
+  int32_t n_strips;
+  int32_t strip_len;      // tiles per strip
+  int32_t seg_len;        // tiles per segment
+  int32_t split;          // segments per strip
+  int32_t items;          // n_strips * split
+  int32_t row_strips;     // 1: a strip is one tile row walked along the columns
+  int32_t swz_shift;
+  int32_t lag;            // producer commit lag in tiles (<= stages - 1, <= 2)
+  uint32_t spin_limit;
+  uint32_t start_phase;   // producer start phase (1; 0 only in the deadlock test)
+  int32_t no_release;     // test: consumers never release
+  int32_t trace_cap;      // trace records
+};
+
+// Launch the stream kernel for (op, stages, consumers). Returns hipSuccess or the
+// launch error. `grid` workgroups of 64 * (1 + consumers) threads.
+hipError_t launch_stream(int op, int stages, int consumers, int grid, const StreamParams& p,
+                         hipStream_t stream);
+int stream_lds_bytes(int stages, int consumers);
+
+hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
+                                  hipStream_t stream);
+hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, float value,
+                           hipStream_t stream);
+
+struct GemmParams {
+  const uint8_t* A;       // bf16 M x K
+  const uint8_t* B;       // bf16 K x N
+  float* C;               // fp32 M x N
+  int64_t lda, ldb, ldc;  // bytes for A, B; elements for C
+  int32_t M, N, K;
+  int32_t tiles_m, tiles_n, k_steps;
+  int32_t items;          // output tiles
+  int32_t swz_shift;
+  uint32_t spin_limit;
+  uint32_t* status;
+  uint32_t* trace;
+  int32_t trace_cap;
+};
+
+hipError_t launch_gemm(int stages, int grid, const GemmParams& p, hipStream_t stream);
+int gemm_lds_bytes(int stages);
+
+}  // namespace pipe

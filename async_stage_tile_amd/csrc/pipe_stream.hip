@@ -1,0 +1,355 @@
+// Warp-specialised tile stream: one producer wave fills an S-slot LDS ring with
+// direct-to-LDS loads; C consumer waves copy each tile back out (with optional
+// per-tile checksums) or reduce it into fp32 row sums.
+//
+// Follows "cute（12）async_pipeline": producer loop = acquire (wait on empty)
+// -> copy into slot `index` -> commit -> ++ (section 3.1, code listing);
+// consumer loop = wait on full -> use slot `index` -> release -> ++ (3.2);
+// producer_tail waits S more empty phases (6.9); the producer starts at
+// phase 1 (2.3). The tile use of the copy is the write-back of
+// "cute（11）hopper之TMA_copy" (code step 6, section 4).
+//
+// Work decomposition: tiles are 128 rows x 64 fp16 (16 KiB). A strip is one
+// tile column walked downwards (copy default) or one tile row walked along the
+// columns (rowsum, or copy with PIPE_FLAG_ROW_STRIPS). Each strip is cut into
+// `split` segments; item i is segment i / n_strips of strip i % n_strips, so
+// workgroups launched together touch neighbouring strips. A workgroup walks
+// items blockIdx.x, blockIdx.x + gridDim.x, ... and its cursors run on across
+// items (a persistent ring).
+//
+// Slot layout: tile row r (128 B) holds its 16-byte chunk c at position
+// c ^ ((r >> shift) & 7). One producer DMA instruction q moves rows 8q..8q+7:
+// lane l writes LDS position l & 7 of row 8q + (l >> 3), so it fetches the
+// global chunk swz(row, l & 7).
+#include "pipe_device.hpp"
+#include "pipe_kernels.hpp"
+
+namespace pipe {
+
+template <int S, int C>
+struct StreamLds {
+  uint8_t slots[S][kTileBytes];
+  uint32_t full[S];
+  uint32_t empty[S];
+  uint32_t fin[S];         // checksum: consumer waves done with the slot's tile
+  uint32_t part[S][C];     // checksum: per-wave partial sums
+};
+
+__device__ __forceinline__ void trace_record(const StreamParams& p, int t, int event,
+                                             const PipeState& st, int wave) {
+  if (p.trace == nullptr || blockIdx.x != 0) return;
+  int rec = 2 * t + event;
+  if (rec >= p.trace_cap) return;
+  if (lane_id() == 0) {
+    uint64_t now = __builtin_amdgcn_s_memrealtime();
+    uint32_t* r = p.trace + (size_t)rec * 8;
+    r[0] = (uint32_t)event;
+    r[1] = (uint32_t)t;
+    r[2] = (uint32_t)st.index;
+    r[3] = st.phase;
+    r[4] = st.count;
+    r[5] = (uint32_t)wave;
+    r[6] = (uint32_t)now;
+    r[7] = (uint32_t)(now >> 32);
+  }
+}
+
+__device__ __forceinline__ void tile_coords(const StreamParams& p, int item, int k,
+                                            int& tile_row, int& tile_col) {
+  int strip = item % p.n_strips;
+  int seg = item / p.n_strips;
+  int pos = seg * p.seg_len + k;
+  if (p.row_strips) {
+    tile_row = strip;
+    tile_col = pos;
+  } else {
+    tile_row = pos;
+    tile_col = strip;
+  }
+}
+
+__device__ __forceinline__ int item_len(const StreamParams& p, int item) {
+  int seg = item / p.n_strips;
+  int start = seg * p.seg_len;
+  int len = p.strip_len - start;
+  return len < p.seg_len ? len : p.seg_len;
+}
+
+// ---------------------------------------------------------------------------
+// Producer wave
+// ---------------------------------------------------------------------------
+template <int S, int C>
+__device__ void producer(const StreamParams& p, StreamLds<S, C>& lds) {
+  const int lane = lane_id();
+  const int lrow = lane >> 3;  // row within a 1 KiB block
+  const int lpos = lane & 7;   // chunk position within the row
+  PipeState w = producer_start(S, p.start_phase);
+  int pending = 0;  // tiles issued but not yet committed (their full not arrived)
+  int t = 0;
+  bool ok = true;
+
+  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+    const int len = item_len(p, item);
+    for (int k = 0; k < len; ++k, ++t) {
+      // producer_acquire: wait until consumers released this slot.
+      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      trace_record(p, t, 0, w, 0);
+      int tr, tc;
+      tile_coords(p, item, k, tr, tc);
+      const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc * kRowBytes;
+      const uint32_t slot = uniform(lds_addr(&lds.slots[w.index][0]));
+#pragma unroll
+      for (int q = 0; q < kBlocksPerTile; ++q) {
+        const int r = q * kRowsPerBlock + lrow;
+        const int c = swz(r, lpos, p.swz_shift);
+        dma_block(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
+      }
+      ++pending;
+      // Commit the oldest in-flight tile once `lag` newer tiles are in flight:
+      // its 16 loads are done when at most 16*(pending-1) remain outstanding.
+      if (pending > p.lag) {
+        wait_vmcnt_tiles(pending - 1);
+        int oldest = w.index - (pending - 1);
+        if (oldest < 0) oldest += S;
+        bar_arrive(&lds.full[oldest], 1u);
+        --pending;
+      }
+      w.inc();
+    }
+  }
+  // Commit whatever is still in flight, oldest first.
+  while (pending > 0) {
+    wait_vmcnt_tiles(pending - 1);
+    int oldest = w.index - pending;
+    if (oldest < 0) oldest += S;
+    bar_arrive(&lds.full[oldest], 1u);
+    --pending;
+  }
+  // producer_tail: S more empty phases, so every slot has been drained.
+  if (ok) {
+    for (int i = 0; i < S; ++i) {
+      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      w.inc();
+    }
+  }
+  wait_vmcnt<0>();
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutProducer);
+}
+
+// ---------------------------------------------------------------------------
+// Consumer waves
+// ---------------------------------------------------------------------------
+template <int S, int C, int OP>
+__device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
+  constexpr int NB = (kBlocksPerTile + C - 1) / C;  // blocks per wave (last may idle)
+  const int lane = lane_id();
+  const int lrow = lane >> 3;
+  const int lpos = lane & 7;
+  PipeState rd = consumer_start(S);
+  float acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = 0.f;
+  int t = 0;
+  bool ok = true;
+
+  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+    const int len = item_len(p, item);
+    int tr = 0, tc = 0;
+    for (int k = 0; k < len; ++k, ++t) {
+      // consumer_wait: the slot's full phase must have completed.
+      if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      if (cw == 0) trace_record(p, t, 1, rd, 1 + cw);
+      tile_coords(p, item, k, tr, tc);
+      const uint8_t* slot = &lds.slots[rd.index][0];
+      uint4 v[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int q = cw + j * C;
+        if (q < kBlocksPerTile)
+          v[j] = *reinterpret_cast<const uint4*>(slot + q * kBlockBytes + lane * kChunkBytes);
+      }
+      if constexpr (OP == kOpCopy) {
+        uint32_t csum = 0;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int q = cw + j * C;
+          if (q < kBlocksPerTile) {
+            const int r = q * kRowsPerBlock + lrow;
+            const int c = swz(r, lpos, p.swz_shift);
+            uint8_t* gd = p.dst + ((int64_t)tr * kTileRows + r) * p.ld_dst +
+                          (int64_t)tc * kRowBytes + c * kChunkBytes;
+            *reinterpret_cast<uint4*>(gd) = v[j];
+            if (p.checksums) {
+              csum += (v[j].x & 0xFFFFu) + (v[j].x >> 16) + (v[j].y & 0xFFFFu) + (v[j].y >> 16) +
+                      (v[j].z & 0xFFFFu) + (v[j].z >> 16) + (v[j].w & 0xFFFFu) + (v[j].w >> 16);
+            }
+          }
+        }
+        wait_lgkmcnt0();
+        if (p.checksums) {
+          // Per-wave partial -> LDS; the last wave to finish the tile adds the
+          // partials and writes the tile's checksum before it releases.
+          csum = sum64_lanes_u32(csum);
+          if (lane == 0) lds.part[rd.index][cw] = csum;
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          uint32_t before = 0;
+          if (lane == 0)
+            before = __hip_atomic_fetch_add(&lds.fin[rd.index], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_WORKGROUP);
+          before = uniform(before);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (before % C == C - 1) {
+            uint32_t tot = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < C; ++w2) tot += lds.part[rd.index][w2];
+            if (lane == 0) p.checksums[(int64_t)tr * p.tile_cols + tc] = tot;
+          }
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int q = cw + j * C;
+          if (q < kBlocksPerTile) {
+            const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(w4[e] & 0xFFFFu));
+              const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(w4[e] >> 16));
+              s += (float)lo;
+              s += (float)hi;
+            }
+            acc[j] += s;
+          }
+        }
+        wait_lgkmcnt0();
+      }
+      // consumer_release.
+      if (!p.no_release) bar_arrive(&lds.empty[rd.index], (uint32_t)C);
+      rd.inc();
+    }
+    if constexpr (OP == kOpRowsum) {
+      if (ok && len > 0) {
+        const int seg = item / p.n_strips;
+        float* o = p.out + (int64_t)seg * p.M + (int64_t)tr * kTileRows;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int q = cw + j * C;
+          if (q < kBlocksPerTile) {
+            const float s = sum8_lanes(acc[j]);
+            if (lpos == 0) o[q * kRowsPerBlock + lrow] = s;
+          }
+          acc[j] = 0.f;
+        }
+      }
+    }
+  }
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
+}
+
+template <int S, int C, int OP>
+__global__ void __launch_bounds__(64 * (1 + C)) stream_kernel(StreamParams p) {
+  __shared__ StreamLds<S, C> lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  if (threadIdx.x < S) {
+    lds.full[threadIdx.x] = 0u;
+    lds.empty[threadIdx.x] = 0u;
+    lds.fin[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  if (wave == 0)
+    producer<S, C>(p, lds);
+  else
+    consumer<S, C, OP>(p, lds, wave - 1);
+}
+
+// ---------------------------------------------------------------------------
+// Row-sum finalize: out[r] = sum_{s < split} partial[s][r], in order s = 0..split-1.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) rowsum_finalize(const float* __restrict__ part,
+                                                       float* __restrict__ out, int64_t M,
+                                                       int split) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= M) return;
+  float s = part[r];
+  for (int k = 1; k < split; ++k) s += part[(int64_t)k * M + r];
+  out[r] = s;
+}
+
+__global__ void __launch_bounds__(256) fill_f32(float* __restrict__ out, int64_t rows,
+                                                int64_t cols, int64_t ld, float value) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * cols) return;
+  out[(i / cols) * ld + (i % cols)] = value;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int S, int C>
+static hipError_t launch_sc(int op, int grid, const StreamParams& p, hipStream_t stream) {
+  dim3 block(64 * (1 + C));
+  if (op == kOpCopy)
+    hipLaunchKernelGGL((stream_kernel<S, C, kOpCopy>), dim3(grid), block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((stream_kernel<S, C, kOpRowsum>), dim3(grid), block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int S>
+static hipError_t launch_s(int op, int consumers, int grid, const StreamParams& p,
+                           hipStream_t stream) {
+  switch (consumers) {
+    case 1: return launch_sc<S, 1>(op, grid, p, stream);
+    case 2: return launch_sc<S, 2>(op, grid, p, stream);
+    case 3: return launch_sc<S, 3>(op, grid, p, stream);
+    case 4: return launch_sc<S, 4>(op, grid, p, stream);
+    case 8: return launch_sc<S, 8>(op, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stream(int op, int stages, int consumers, int grid, const StreamParams& p,
+                         hipStream_t stream) {
+  switch (stages) {
+    case 1: return launch_s<1>(op, consumers, grid, p, stream);
+    case 2: return launch_s<2>(op, consumers, grid, p, stream);
+    case 3: return launch_s<3>(op, consumers, grid, p, stream);
+    case 4: return launch_s<4>(op, consumers, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int stream_lds_bytes(int stages, int consumers) {
+  return stages * kTileBytes + stages * 4 * (3 + consumers);
+}
+
+hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
+                                  hipStream_t stream) {
+  const int64_t blocks = (M + 255) / 256;
+  hipLaunchKernelGGL(rowsum_finalize, dim3((unsigned)blocks), dim3(256), 0, stream, partials,
+                     out, M, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, float value,
+                           hipStream_t stream) {
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_f32, dim3((unsigned)blocks), dim3(256), 0, stream, out, rows, cols,
+                     ld, value);
+  return hipGetLastError();
+}
+
+}  // namespace pipe

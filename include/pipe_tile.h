@@ -1,0 +1,166 @@
+/*
+ * pipe_tile -- a pipelined tile stream for AMD MI355X (gfx950).
+ *
+ * One hot path: a producer wavefront streams 2D tiles from HBM into a ring of
+ * S swizzled LDS slots; every slot carries a full/empty handshake with phase
+ * parity; consumer wavefronts wait on a slot, use the tile, and release it.
+ * Three uses are exported: copy the tile back out, reduce it into fp32 row
+ * sums, and feed a bf16 matrix-multiply mainloop.
+ *
+ * Sources (pages, by title and section):
+ *   "cute（12）async_pipeline" -- the ring of stages, full/empty barrier pair
+ *       per stage, PipelineState cursor, producer start phase 1, producer /
+ *       consumer API (sections 1-3, 6, 7), Params (section 4);
+ *   "cute（11）hopper之TMA_copy" -- one 128x64 fp16 tile round trip
+ *       global -> swizzled shared memory -> global (code, sections 1-4);
+ *   "cuda-features-10-pipelines" 4.10 -- acquire / commit / wait / release,
+ *       stage-count trade-offs (4.10.7), 16-byte alignment advice (4.10.6);
+ *   "chapter_async_barriers" (mlc.ai) -- mbarrier phase semantics.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major: element (r, c) of an M x N matrix with leading
+ *     dimension ld (in elements) is at base + r*ld + c.
+ *   - All data pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates or frees memory, never synchronises the stream and keeps
+ *     no per-call host state; it is safe to call from several host threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *     asynchronous: results are visible after the caller synchronises.
+ *   - Arguments are validated before anything is launched; on any error no
+ *     work is enqueued and the error code is returned.
+ *   - A stalled handshake never hangs the device: each wait gives up after
+ *     cfg->spin_limit polls and sets a bit in the status word (cfg->status, or
+ *     the library's own word read back by pipe_device_status()).
+ */
+#ifndef PIPE_TILE_H
+#define PIPE_TILE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PIPE_ABI_VERSION 1
+
+typedef enum {
+  PIPE_OK = 0,
+  PIPE_ERR_NULL = 1,      /* a required pointer is NULL */
+  PIPE_ERR_SHAPE = 2,     /* negative size, ld < width, or a shape the op does not support */
+  PIPE_ERR_ALIGN = 3,     /* base pointer or row pitch not 16-byte aligned */
+  PIPE_ERR_STAGES = 4,    /* stage count out of range or the ring does not fit in LDS */
+  PIPE_ERR_CONFIG = 5,    /* unsupported tile shape, wave counts, grid, split or flags */
+  PIPE_ERR_WORKSPACE = 6, /* workspace missing or smaller than required */
+  PIPE_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
+  PIPE_ERR_TIMEOUT = 8    /* (device status) a pipeline wait exceeded spin_limit */
+} pipe_status_t;
+
+typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_t;
+
+/* cfg->flags */
+#define PIPE_FLAG_TRACE 0x1u           /* record per-tile cursor values into cfg->trace */
+#define PIPE_FLAG_ROW_STRIPS 0x2u      /* copy: walk tiles along rows instead of down columns */
+#define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
+                                              deadlock of the pages); must end in a timeout */
+#define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the
+                                              producer's first wait of lap 2 times out */
+
+/* Status-word bits (cfg->status or pipe_device_status). */
+#define PIPE_STATUS_TIMEOUT_PRODUCER 0x1u
+#define PIPE_STATUS_TIMEOUT_CONSUMER 0x2u
+
+/* One trace record: 8 uint32 words. Written only by workgroup 0, for the first
+ * cfg->trace_capacity / 2 tiles of its stream, at record index 2*t + event.
+ *   [0] event (0 = producer acquired the slot, 1 = consumer wave 0 passed its wait)
+ *   [1] tile ordinal t in the workgroup's stream
+ *   [2] cursor index   [3] cursor phase   [4] cursor count
+ *   [5] wave id        [6] s_memrealtime low   [7] s_memrealtime high          */
+#define PIPE_TRACE_WORDS 8
+
+typedef struct {
+  int32_t stages;         /* S, ring depth: 1..4 (copy/rowsum), 1..4 (gemm)              */
+  int32_t tile_m;         /* copy/rowsum: 128; gemm: 128                                  */
+  int32_t tile_n;         /* copy/rowsum: 64 fp16; gemm: 128                              */
+  int32_t tile_k;         /* gemm only: 64                                                */
+  int32_t producer_waves; /* copy/rowsum: 1; gemm: 2 (one for A, one for B)               */
+  int32_t consumer_waves; /* copy/rowsum: 1..8; gemm: 4                                   */
+  int32_t grid;           /* workgroups; 0 = one per work item (capped by the device)     */
+  int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default 1  */
+  int32_t swizzle_shift;  /* row bits XOR-ed into the 16-byte chunk index: 0..3           */
+  uint32_t flags;         /* PIPE_FLAG_*                                                  */
+  uint32_t spin_limit;    /* polls per wait before giving up; 0 = default (1 << 22)       */
+  int32_t trace_capacity; /* records available at trace                                   */
+  uint32_t* trace;        /* device, nullable; used with PIPE_FLAG_TRACE                  */
+  uint32_t* status;       /* device, nullable; OR-ed with PIPE_STATUS_* bits              */
+} pipe_config_t;
+
+typedef struct {
+  int32_t lds_bytes;      /* LDS per workgroup (ring + barrier words)                    */
+  int32_t threads;        /* threads per workgroup                                        */
+  int32_t grid;           /* workgroups that would be launched                            */
+  int32_t items;          /* strips x segments (copy/rowsum) or output tiles (gemm)       */
+  int32_t tiles_per_item; /* tiles streamed through the ring per work item (max)          */
+  int32_t split;          /* segments per strip actually used                             */
+} pipe_kernel_info_t;
+
+/* ABI version of the loaded library (PIPE_ABI_VERSION). */
+int pipe_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* pipe_status_str(int status);
+
+/* Fill *cfg with the defaults of an op: stages 3, tile 128x64 (gemm 128x128x64),
+ * 1 producer wave (gemm 2), 3 consumer waves (gemm 4), grid/split auto, swizzle 0. */
+pipe_status_t pipe_config_default(pipe_op_t op, pipe_config_t* cfg);
+
+/* Tile copy (configs: "cute（11）hopper之TMA_copy" round trip; "cute（12）
+ * async_pipeline" ring).  dst[r][c] = src[r][c] bit for bit for r < M, c < N;
+ * the 16-bit payload is opaque (fp16, bf16, raw codes). Each tile passes
+ * through a swizzled LDS slot.
+ *   src, dst: device, 16-byte aligned; ld_src, ld_dst: row pitch in elements,
+ *   multiples of 8, >= N. M % 128 == 0 and N % 64 == 0 (else PIPE_ERR_SHAPE);
+ *   M == 0 or N == 0 is a no-op.
+ *   tile_checksums: device, nullable; if given, receives for every tile
+ *   (i, j) in row-major tile order the uint32 sum of its 8192 raw 16-bit codes. */
+pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N,
+                             int64_t ld_src, int64_t ld_dst, const pipe_config_t* cfg,
+                             uint32_t* tile_checksums, void* stream);
+
+/* Bytes of workspace pipe_rowsum needs for this shape and config (0 when each
+ * row strip is handled by one workgroup). */
+pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_config_t* cfg,
+                                          size_t* bytes);
+
+/* Row sums of an fp16 matrix with fp32 accumulation: out[r] = sum_c A[r][c].
+ * Row strips of 128 rows are cut into cfg->split segments along the columns;
+ * segment partials go to the workspace and are added in a fixed order, so the
+ * result is deterministic.
+ *   A: device fp16, 16-byte aligned, lda multiple of 8 and >= N;
+ *   M % 128 == 0, N % 64 == 0; N == 0 gives out = 0; M == 0 is a no-op.
+ *   out: device float[M]. workspace: device, >= pipe_rowsum_workspace_bytes. */
+pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
+                          const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* GEMM mainloop: C = A * B with bf16 A (M x K, row-major) and B (K x N,
+ * row-major), fp32 accumulation and fp32 C (M x N, row-major). A and B tiles
+ * of each 64-deep K step pass through the LDS ring to MFMA consumer waves.
+ *   M % 128 == 0, N % 128 == 0, K % 64 == 0; lda, ldb multiples of 8;
+ *   ldc >= N; K == 0 gives C = 0. */
+pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t M,
+                                 int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                 const pipe_config_t* cfg, void* stream);
+
+/* Launch geometry an op would use for this shape and config (no launch). */
+pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
+                                int64_t K, pipe_kernel_info_t* info);
+
+/* Blocking read of the library's own device status word on the current
+ * device (used when cfg->status is NULL); clears it when `clear` != 0. */
+pipe_status_t pipe_device_status(uint32_t* out, int clear);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIPE_TILE_H */

@@ -22,3 +22,20 @@ def golden_lines(name):
 @pytest.fixture
 def golden():
     return golden_lines
+
+
+def _gpu_ok():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    if _gpu_ok():
+        return
+    skip = pytest.mark.skip(reason="no ROCm device visible")
+    for it in items:
+        if "gpu" in it.keywords:
+            it.add_marker(skip)

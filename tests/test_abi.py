@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import async_stage_tile_amd as pt
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pipe_tile.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pipe_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = pt.lib()
+    declared = _declared()
+    assert len(declared) == 9
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(pt.exported_symbols()) == declared
+
+
+def test_version_and_status_strings():
+    assert pt.abi_version() == 1
+    assert pt.status_str(pt.PIPE_OK) == "ok"
+    assert "timed out" in pt.status_str(pt.PIPE_ERR_TIMEOUT)
+    assert pt.status_str(99) == "unknown status"
+
+
+def test_config_defaults():
+    c = pt.make_config(pt.PIPE_OP_COPY)
+    assert (c.stages, c.tile_m, c.tile_n, c.producer_waves, c.consumer_waves) == (3, 128, 64, 1, 3)
+    g = pt.make_config(pt.PIPE_OP_GEMM)
+    assert (g.tile_m, g.tile_n, g.tile_k, g.producer_waves, g.consumer_waves) == (128, 128, 64, 2, 4)
+    assert pt.lib().pipe_config_default(7, ctypes.byref(c)) == pt.PIPE_ERR_CONFIG
+    assert pt.lib().pipe_config_default(0, None) == pt.PIPE_ERR_NULL
+
+
+def _copy(src, dst, M, N, lds, ldd, cfg=None, chk=None):
+    c = cfg if cfg is not None else pt.make_config(pt.PIPE_OP_COPY)
+    return pt.lib().pipe_tile_copy(src, dst, M, N, lds, ldd, ctypes.byref(c), chk, None)
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+def test_copy_validation():
+    assert _copy(None, FAKE, 256, 128, 128, 128) == pt.PIPE_ERR_NULL
+    assert _copy(FAKE, FAKE, 200, 128, 128, 128) == pt.PIPE_ERR_SHAPE   # ragged M
+    assert _copy(FAKE, FAKE, 256, 100, 128, 128) == pt.PIPE_ERR_SHAPE   # ragged N
+    assert _copy(FAKE, FAKE, -128, 128, 128, 128) == pt.PIPE_ERR_SHAPE
+    assert _copy(FAKE, FAKE, 256, 128, 64, 128) == pt.PIPE_ERR_SHAPE    # ld < N
+    assert _copy(FAKE + 8, FAKE, 256, 128, 128, 128) == pt.PIPE_ERR_ALIGN
+    assert _copy(FAKE, FAKE, 256, 128, 132, 128) == pt.PIPE_ERR_ALIGN  # pitch not 16 B
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, chk=FAKE + 2) == pt.PIPE_ERR_ALIGN
+    for bad in (0, 5):
+        assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, stages=bad)) \
+            == pt.PIPE_ERR_STAGES
+    for bad in (0, 5, 9):
+        assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, consumer_waves=bad)) \
+            == pt.PIPE_ERR_CONFIG
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, tile_n=32)) == pt.PIPE_ERR_CONFIG
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, swizzle_shift=4)) \
+        == pt.PIPE_ERR_CONFIG
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=0x8000)) \
+        == pt.PIPE_ERR_CONFIG
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=pt.PIPE_FLAG_TRACE)) \
+        == pt.PIPE_ERR_NULL
+    # empty matrices are a no-op, with or without pointers
+    assert _copy(None, None, 0, 128, 128, 128) == pt.PIPE_OK
+    assert _copy(None, None, 256, 0, 0, 0) == pt.PIPE_OK
+
+
+def test_rowsum_and_gemm_validation():
+    L = pt.lib()
+    c = pt.make_config(pt.PIPE_OP_ROWSUM, split=4)
+    need = ctypes.c_size_t()
+    assert L.pipe_rowsum_workspace_bytes(1024, 4096, ctypes.byref(c), ctypes.byref(need)) == 0
+    assert need.value == 4 * 1024 * 4
+    assert L.pipe_rowsum(FAKE, FAKE, 1024, 4096, 4096, ctypes.byref(c), None, 0, None) \
+        == pt.PIPE_ERR_WORKSPACE
+    assert L.pipe_rowsum(FAKE, FAKE, 1024, 4096, 4096, ctypes.byref(c), FAKE, need.value - 4,
+                         None) == pt.PIPE_ERR_WORKSPACE
+    assert L.pipe_rowsum(FAKE, FAKE, 1000, 4096, 4096, ctypes.byref(c), FAKE, 1 << 20, None) \
+        == pt.PIPE_ERR_SHAPE
+    assert L.pipe_rowsum(FAKE, None, 1024, 4096, 4096, ctypes.byref(c), FAKE, 1 << 20, None) \
+        == pt.PIPE_ERR_NULL
+    assert L.pipe_rowsum(None, None, 0, 4096, 4096, ctypes.byref(c), None, 0, None) == pt.PIPE_OK
+    g = pt.make_config(pt.PIPE_OP_GEMM)
+    args = lambda M, N, K, **kw: L.pipe_gemm_mainloop(kw.get("A", FAKE), FAKE, FAKE, M, N, K,
+                                                       K, N, N, ctypes.byref(kw.get("cfg", g)), None)
+    assert args(256, 256, 100) == pt.PIPE_ERR_SHAPE
+    assert args(256, 192, 128) == pt.PIPE_ERR_SHAPE
+    assert args(256, 256, 128, A=FAKE + 4) == pt.PIPE_ERR_ALIGN
+    assert args(256, 256, 128, cfg=pt.make_config(2, stages=5)) == pt.PIPE_ERR_STAGES
+    assert args(256, 256, 128, cfg=pt.make_config(2, consumer_waves=3)) == pt.PIPE_ERR_CONFIG
+    assert args(0, 256, 128) == pt.PIPE_OK
+
+
+def test_query_geometry():
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, stages=4)
+    assert q["items"] == 256 and q["tiles_per_item"] == 128 and q["grid"] == 256
+    assert q["lds_bytes"] >= 4 * 16384 and q["threads"] == 256
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, split=3, grid=100)
+    assert q["split"] == 3 and q["tiles_per_item"] == 43 and q["items"] == 768 and q["grid"] == 100
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 128, 512, grid=1)
+    assert (q["items"], q["tiles_per_item"], q["grid"]) == (8, 1, 1)
+    q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 8192, 65536)
+    assert q["items"] >= 512 and q["items"] == 64 * q["split"]
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096)
+    assert (q["items"], q["tiles_per_item"], q["threads"]) == (1024, 64, 384)
+    assert q["lds_bytes"] >= 3 * 32768
+    with pytest.raises(pt.PipeError):
+        pt.pipe_query_kernel(pt.PIPE_OP_COPY, 100, 64)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(pt, "_lib", None)
+    monkeypatch.setattr(pt, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(pt.PipeBuildError):
+        pt.lib()

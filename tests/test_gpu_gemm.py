@@ -1,0 +1,79 @@
+"""GPU parity of the ring-fed GEMM mainloop against the fp64 CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import async_stage_tile_amd as pt
+import synth
+from oracle import results as R
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _f32(t):
+    return t.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_gemm_small_integers_bit_exact(S):
+    M, N, K = 256, 384, 512
+    A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=3, stream=0).to(DEV)
+    B = synth.small_int((K, N), -2, 2, torch.bfloat16, seed=3, stream=1).to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, stages=S, grid=5, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = R.gemm_f64(_f32(A), _f32(B))
+    got = C.cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+
+
+def test_gemm_identity_operands():
+    K = 256
+    A = torch.eye(K, dtype=torch.bfloat16, device=DEV)
+    B = synth.uniform((K, 128), torch.bfloat16, seed=8).to(DEV)
+    C = pt.pipe_gemm_mainloop(A, B)
+    torch.cuda.synchronize()
+    assert torch.equal(C, B.float())
+    A2 = synth.uniform((128, K), torch.bfloat16, seed=9).to(DEV)
+    C2 = pt.pipe_gemm_mainloop(A2, torch.eye(K, dtype=torch.bfloat16, device=DEV)[:, :128]
+                               .contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(C2, A2[:, :128].float())
+
+
+def test_gemm_uniform_within_tolerance():
+    M, N, K = 512, 256, 1024
+    A = synth.uniform((M, K), torch.bfloat16, seed=42, stream=0).to(DEV)
+    B = synth.uniform((K, N), torch.bfloat16, seed=42, stream=1).to(DEV)
+    C = pt.pipe_gemm_mainloop(A, B)
+    torch.cuda.synchronize()
+    res = R.within_tol(C.cpu().numpy(), R.gemm_f64(_f32(A), _f32(B)), 1e-2)
+    assert res["ok"], res
+
+
+def test_gemm_full_size_sampled_rows():
+    """bf16 4096^3 uniform[-1,1): 64 sampled rows checked against fp64."""
+    n = 4096
+    A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device=DEV)
+    B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, stages=3, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rows = np.random.default_rng(42).choice(n, 64, replace=False)
+    rows.sort()
+    ref = R.gemm_f64(_f32(A[rows]), _f32(B))
+    res = R.within_tol(C[rows].cpu().numpy(), ref, 1e-2)
+    assert res["ok"], res
+
+
+def test_gemm_k_zero_gives_zero():
+    A = torch.empty((128, 0), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    C = torch.full((128, 128), 3.0, device=DEV)
+    pt.pipe_gemm_mainloop(A, B, C)
+    torch.cuda.synchronize()
+    assert int((C != 0).sum()) == 0

@@ -1,0 +1,208 @@
+"""GPU parity of the tile stream (copy and row sum) against the CPU oracle.
+
+Every input comes from ``synth`` (seeded); the expected values come from
+``oracle`` on the same bits. Copies and integer-data row sums must match bit
+for bit; fp row sums within |err| <= 1e-3 * max(|ref|, rms(ref)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import async_stage_tile_amd as pt
+import synth
+from oracle import protocol as P
+from oracle import results as R
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _status():
+    return torch.zeros(1, dtype=torch.int32, device=DEV)
+
+
+# ---------------------------------------------------------------- copy
+def test_copy_single_tile_per_workgroup_index_codes():
+    """128x64 tiles of a 256x128 matrix, one tile per workgroup (2x2), S=1."""
+    src = synth.index_coded(256, 128).to(DEV)
+    st = _status()
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 256, 128, stages=1, split=2)
+    assert (q["items"], q["grid"], q["tiles_per_item"]) == (4, 4, 1)
+    dst = pt.pipe_tile_copy(src, stages=1, split=2, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst), R.tile_copy(src.cpu().numpy()).view(np.uint16))
+    # unique codes: a misplaced element names its source
+    u = synth.unique_codes(256, 128).to(DEV)
+    du = pt.pipe_tile_copy(u, stages=1, split=2)
+    torch.cuda.synchronize()
+    got, exp = _bits(du), _bits(u)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"first mismatches (r,c): {bad[:5].tolist()} got {got[tuple(bad[0])]}"
+
+
+def test_copy_three_stage_ring_checksums_and_trace():
+    """One workgroup (1 producer + 3 consumer waves), 8 tiles along the columns."""
+    src = synth.uniform((128, 512), torch.float16, seed=42).to(DEV)
+    trace = torch.zeros(16 * pt.PIPE_TRACE_WORDS, dtype=torch.int32, device=DEV)
+    st = _status()
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, stages=3, consumer_waves=3, grid=1,
+                                 flags=pt.PIPE_FLAG_TRACE, trace=trace, trace_capacity=16,
+                                 status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    s_np = src.cpu().numpy()
+    assert np.array_equal(_bits(dst), R.tile_copy(s_np).view(np.uint16))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(s_np))
+    tr = trace.cpu().numpy().view(np.uint32).reshape(16, pt.PIPE_TRACE_WORDS)
+    prod = tr[0::2]
+    cons = tr[1::2]
+    for t in range(8):
+        assert prod[t][0] == 0 and prod[t][1] == t and cons[t][0] == 1 and cons[t][1] == t
+        assert tuple(prod[t][2:4]) == P.cursor_after(3, t, 1)   # producer starts at phase 1
+        assert tuple(cons[t][2:4]) == P.cursor_after(3, t, 0)
+        assert prod[t][4] == t and cons[t][4] == t
+    clock = lambda rec: (int(rec[7]) << 32) | int(rec[6])
+    for t in range(8):
+        # a consumer passes its wait only after the producer acquired that slot
+        assert clock(cons[t]) >= clock(prod[t])
+        # back-pressure: slot reuse for tile t+3 only after consumers passed tile t
+        if t + 3 < 8:
+            assert clock(prod[t + 3]) >= clock(cons[t])
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("C", [1, 2, 3, 4, 8])
+def test_copy_stage_and_wave_sweep(S, C):
+    M, N = 1024, 640  # 8 x 10 tiles
+    src = synth.unique_codes(M, N).to(DEV)
+    st = _status()
+    # persistent grid smaller than the item count; strips cut in 3 segments
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, stages=S, consumer_waves=C, split=3,
+                                 grid=7, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
+
+
+@pytest.mark.parametrize("shift", [0, 1, 2, 3])
+@pytest.mark.parametrize("row_strips", [False, True])
+def test_copy_swizzle_and_walk_order(shift, row_strips):
+    src = synth.unique_codes(512, 1024).to(DEV)
+    flags = pt.PIPE_FLAG_ROW_STRIPS if row_strips else 0
+    dst = pt.pipe_tile_copy(src, stages=3, swizzle_shift=shift, flags=flags, grid=5)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst), _bits(src))
+
+
+def test_copy_strided_views():
+    big = synth.unique_codes(640, 1024).to(DEV)
+    src = big[:512, 128:640]          # ld_src = 1024
+    out = torch.zeros(512, 768, dtype=torch.float16, device=DEV)
+    dst = out[:, 64:576]              # ld_dst = 768
+    pt.pipe_tile_copy(src, dst, stages=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst.contiguous()), _bits(src.contiguous()))
+    assert int((out[:, :64] != 0).sum()) == 0 and int((out[:, 576:] != 0).sum()) == 0
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_copy_full_size_bit_exact(S):
+    """fp16 16384 x 16384 uniform[-1,1), persistent column strips."""
+    src = synth.uniform((16384, 16384), torch.float16, seed=42, device=DEV)
+    st = _status()
+    dst = pt.pipe_tile_copy(src, stages=S, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
+    # and a sample of rows against the oracle on the host
+    rows = torch.tensor([0, 1, 127, 128, 8191, 16383], device=DEV)
+    s_np = src[rows].cpu().numpy()
+    assert np.array_equal(_bits(dst[rows]), R.tile_copy(s_np).view(np.uint16))
+
+
+# ---------------------------------------------------------------- watchdog
+def test_start_phase_zero_times_out_instead_of_hanging():
+    src = synth.unique_codes(256, 256).to(DEV)
+    st = _status()
+    pt.pipe_tile_copy(src, stages=3, spin_limit=2000, status=st,
+                      flags=pt.PIPE_FLAG_TEST_START_PHASE0)
+    torch.cuda.synchronize()
+    v = int(st.item())
+    assert v & pt.PIPE_STATUS_TIMEOUT_PRODUCER and v & pt.PIPE_STATUS_TIMEOUT_CONSUMER
+
+
+def test_missing_release_times_out_instead_of_hanging():
+    src = synth.unique_codes(128, 640).to(DEV)  # 10 tiles in one strip walk
+    st = _status()
+    pt.pipe_tile_copy(src, stages=3, grid=1, spin_limit=2000, status=st,
+                      flags=pt.PIPE_FLAG_TEST_NO_RELEASE | pt.PIPE_FLAG_ROW_STRIPS)
+    torch.cuda.synchronize()
+    assert int(st.item()) & pt.PIPE_STATUS_TIMEOUT_PRODUCER
+
+
+def test_library_status_word_when_no_status_given():
+    pt.pipe_device_status(clear=True)
+    src = synth.unique_codes(256, 256).to(DEV)
+    pt.pipe_tile_copy(src, stages=2, spin_limit=1000, flags=pt.PIPE_FLAG_TEST_START_PHASE0)
+    torch.cuda.synchronize()
+    assert pt.pipe_device_status(clear=True) != 0
+    pt.pipe_tile_copy(src, stages=2)
+    torch.cuda.synchronize()
+    assert pt.pipe_device_status() == 0
+
+
+# ---------------------------------------------------------------- row sum
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("C", [1, 3, 4, 8])
+@pytest.mark.parametrize("split", [1, 3, 8])
+def test_rowsum_small_integers_bit_exact(S, C, split):
+    """Integer data keeps every partial sum exact in fp32: any order is exact."""
+    A = synth.small_int((512, 2048), -8, 8, torch.float16, seed=5).to(DEV)
+    st = _status()
+    out = pt.pipe_rowsum(A, stages=S, consumer_waves=C, split=split, grid=11, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+def test_rowsum_normal_within_tolerance_and_deterministic():
+    A = synth.normal((1024, 8192), torch.float16, seed=42).to(DEV)
+    out1 = pt.pipe_rowsum(A)
+    out2 = pt.pipe_rowsum(A)
+    torch.cuda.synchronize()
+    ref = R.rowsum_exact(A.cpu().numpy())
+    res = R.within_tol(out1.cpu().numpy(), ref, 1e-3)
+    assert res["ok"], res
+    assert torch.equal(out1, out2)
+
+
+def test_rowsum_full_size_within_tolerance():
+    """fp16 8192 x 65536 normal(0,1), 3-stage ring (the full 1 GiB input)."""
+    A = synth.normal((8192, 65536), torch.float16, seed=42, device=DEV)
+    st = _status()
+    out = pt.pipe_rowsum(A, stages=3, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = R.rowsum_exact(A.cpu().numpy())
+    res = R.within_tol(out.cpu().numpy(), ref, 1e-3)
+    assert res["ok"], res
+
+
+def test_rowsum_degenerate_shapes():
+    A = torch.empty((256, 0), dtype=torch.float16, device=DEV)
+    out = torch.full((256,), 7.0, device=DEV)
+    pt.pipe_rowsum(A, out)
+    torch.cuda.synchronize()
+    assert int((out != 0).sum()) == 0
+    E = torch.empty((0, 128), dtype=torch.float16, device=DEV)
+    assert pt.pipe_rowsum(E).numel() == 0
+    ones = torch.ones((128, 65536), dtype=torch.float16, device=DEV)
+    o = pt.pipe_rowsum(ones, split=5)
+    torch.cuda.synchronize()
+    assert torch.equal(o, torch.full((128,), 65536.0, device=DEV))
