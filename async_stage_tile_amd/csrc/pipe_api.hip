@@ -17,7 +17,8 @@ __device__ uint32_t g_status_word;
 constexpr uint32_t kDefaultSpin = 1u << 22;
 constexpr int kMaxDevices = 64;
 constexpr int kLdsLimit = 163840;
-constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS |
+constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_NONTEMPORAL |
+                                 PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_XCD_REMAP |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -77,7 +78,7 @@ pipe_status_t check_stream_cfg(const pipe_config_t& c) {
   if (s != PIPE_OK) return s;
   if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
   if (c.tile_m != 128 || c.tile_n != 64) return PIPE_ERR_CONFIG;
-  if (c.producer_waves != 1) return PIPE_ERR_CONFIG;
+  if (c.producer_waves != 1 && c.producer_waves != 2) return PIPE_ERR_CONFIG;
   const int cw = c.consumer_waves;
   if (!(cw == 1 || cw == 2 || cw == 3 || cw == 4 || cw == 8)) return PIPE_ERR_CONFIG;
   if (stream_lds_bytes(c.stages, cw) > kLdsLimit) return PIPE_ERR_STAGES;
@@ -127,12 +128,17 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   p->items = g.items;
   p->row_strips = row_strips ? 1 : 0;
   p->swz_shift = c.swizzle_shift;
-  p->lag = c.stages - 1 < 2 ? c.stages - 1 : 2;
+  // Commit lag: at most S-1 tiles (the protocol's liveness bound) and at most
+  // 48 loads outstanding per producer wave (16 / producer_waves per tile).
+  const int max_lag = c.producer_waves == 2 ? 3 : 2;
+  p->lag = c.stages - 1 < max_lag ? c.stages - 1 : max_lag;
+  p->xcd_remap = ((c.flags & PIPE_FLAG_XCD_REMAP) && g.items % 8 == 0) ? 1 : 0;
   p->spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
   p->start_phase = (c.flags & PIPE_FLAG_TEST_START_PHASE0) ? 0u : 1u;
   p->no_release = (c.flags & PIPE_FLAG_TEST_NO_RELEASE) ? 1 : 0;
   p->trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
   p->trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
+  p->nt = (c.flags & PIPE_FLAG_NONTEMPORAL) ? 1 : 0;
 }
 
 pipe_status_t resolve_status(const pipe_config_t& c, uint32_t** out) {
@@ -201,7 +207,7 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   p.M = M;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, g.grid, p,
+  return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, c.producer_waves, g.grid, p,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -256,7 +262,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   p.M = M;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  s = hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, g.grid, p, st));
+  s = hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, c.producer_waves, g.grid, p, st));
   if (s != PIPE_OK || need == 0) return s;
   return hip_status(launch_rowsum_finalize(static_cast<const float*>(workspace), out, M,
                                            g.split, st));
@@ -301,6 +307,7 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t
   if (items > INT32_MAX) return PIPE_ERR_SHAPE;
   p.items = (int32_t)items;
   p.swz_shift = c.swizzle_shift;
+  p.b_swz = (c.flags & PIPE_FLAG_GEMM_B_LINEAR) ? 0 : 1;
   p.spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
   p.trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
   p.trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
@@ -338,7 +345,7 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   const bool rowsum = op == PIPE_OP_ROWSUM;
   const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);
   info->lds_bytes = stream_lds_bytes(c.stages, c.consumer_waves);
-  info->threads = 64 * (1 + c.consumer_waves);
+  info->threads = 64 * (c.producer_waves + c.consumer_waves);
   if (M == 0 || N == 0) return PIPE_OK;
   StreamGeom g;
   s = stream_geometry(M, N, c, row_strips, rowsum, &g);

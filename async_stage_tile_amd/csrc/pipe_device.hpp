@@ -167,6 +167,14 @@ __device__ __forceinline__ void dma_block(const void* gptr, uint32_t lds_base) {
                : "memory");
 }
 
+// Same, with the non-temporal hint (streamed data that is read once).
+__device__ __forceinline__ void dma_block_nt(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(gptr), "{m0}"(lds_base)
+               : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Swizzle: the 16-byte chunk c of tile row r lives at chunk position
 // c ^ ((r >> shift) & 7) of that row (shift 0 = the 128-byte pattern of the

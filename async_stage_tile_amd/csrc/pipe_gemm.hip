@@ -19,7 +19,16 @@
 // LDS layout of a stage: A rows of 128 B with 16-byte chunk c of row r at
 // position c ^ ((r >> shift) & 7) (the MFMA A fragment reads one chunk of 32
 // consecutive rows, so the XOR spreads them across banks); B rows of 256 B
-// (128 bf16), unswizzled.
+// (128 bf16) with chunk c of K-row k at position c ^ fb(k),
+// fb(k) = ((k & 3) << 2) ^ (((k >> 3) & 1) << 1), which puts the four K-rows
+// (and the two K-halves) that one transposing read touches on different banks.
+//
+// B fragments use the gfx950 transposing LDS read ds_read_b64_tr_b16. Within
+// each group of 16 lanes, lane i receives element e (0..3) from the address
+// given by lane 4e + i/4 of its group, offset by 2*(i%4) bytes (lane layout
+// checked on the device by an index-coded probe). So if lane i of the group
+// points at B[k0 + i/4][j0 + 4*(i%4)], it receives B[k0..k0+3][j0 + i]: four
+// consecutive K values of its own column, which is half an MFMA B operand.
 //
 // MFMA 32x32x16 operand layout (lane l, element e): A[i][k] with i = l % 32,
 // k = 8 * (l / 32) + e; B[k][j] with j = l % 32, k = 8 * (l / 32) + e; the
@@ -34,6 +43,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kGemmTile = 128;
 constexpr int kGemmK = 64;
@@ -53,6 +65,11 @@ struct GemmLds {
 __device__ __forceinline__ void gemm_tile_of(const GemmParams& p, int item, int& tm, int& tn) {
   tm = item / p.tiles_n;
   tn = item % p.tiles_n;
+}
+
+// B-row chunk swizzle (positions of the 16 chunks of a 256-byte K-row).
+__device__ __forceinline__ int swz_b(int k, int on) {
+  return on ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : 0;
 }
 
 template <int S>
@@ -87,9 +104,10 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int role) {
         const uint8_t* b0 = gb + (int64_t)ks * kGemmK * p.ldb;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          // B: rows 4q..4q+3 of 256 B, lane -> (row 4q + l/16, chunk l%16).
+          // B: rows 4q..4q+3 of 256 B, lane -> (row 4q + l/16, position l%16).
           const int r = q * 4 + (lane >> 4);
-          dma_block(b0 + (int64_t)r * p.ldb + (lane & 15) * 16, sb + q * kBlockBytes);
+          const int c = (lane & 15) ^ swz_b(r, p.b_swz);
+          dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + q * kBlockBytes);
         }
       }
       ++pending;
@@ -123,16 +141,22 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int role) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutProducer);
 }
 
-__device__ __forceinline__ bf16x8 load_b_column(const uint8_t* bslot, int k0, int col) {
-  // 8 consecutive K values of one B column (row-major B): a strided gather.
-  const uint16_t* base = reinterpret_cast<const uint16_t*>(bslot) + col;
-  bf16x8 v;
+// MFMA B operand (K 16 x N 32 block at K-rows k16.., columns col0..col0+31)
+// from the row-major B slot, via two transposing reads.
+__device__ __forceinline__ bf16x8 load_b_frag(const uint8_t* bslot, int k16, int col0, int lane,
+                                              int b_swz) {
+  const int g = lane >> 4, i = lane & 15;
+  const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
+  const int chunk = col >> 3, within = (col & 7) * 2;
+  s16x4 h[2];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint16_t x = base[(k0 + e) * kGemmTile];
-    v[e] = __builtin_bit_cast(__bf16, x);
+  for (int half = 0; half < 2; ++half) {
+    const int k = k16 + 8 * (g >> 1) + 4 * half + (i >> 2);
+    const uint8_t* a = bslot + k * kBRowBytes + ((chunk ^ swz_b(k, b_swz)) << 4) + within;
+    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
   }
-  return v;
+  const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 template <int S>
@@ -170,7 +194,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
         }
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          bfr[ni] = load_b_column(sb, kk * 16 + lk * 8, wn * 64 + ni * 32 + li);
+          bfr[ni] = load_b_frag(sb, kk * 16, wn * 64 + ni * 32, lane, p.b_swz);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll

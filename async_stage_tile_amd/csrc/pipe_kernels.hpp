@@ -32,12 +32,15 @@ struct StreamParams {
   uint32_t start_phase;   // producer start phase (1; 0 only in the deadlock test)
   int32_t no_release;     // test: consumers never release
   int32_t trace_cap;      // trace records
+  int32_t nt;             // non-temporal hints on the streamed loads and stores
+  int32_t xcd_remap;      // permute items so each XCD streams neighbouring strips
 };
 
-// Launch the stream kernel for (op, stages, consumers). Returns hipSuccess or the
-// launch error. `grid` workgroups of 64 * (1 + consumers) threads.
-hipError_t launch_stream(int op, int stages, int consumers, int grid, const StreamParams& p,
-                         hipStream_t stream);
+// Launch the stream kernel for (op, stages, consumers, producers). Returns
+// hipSuccess or the launch error. `grid` workgroups of 64 * (producers +
+// consumers) threads.
+hipError_t launch_stream(int op, int stages, int consumers, int producers, int grid,
+                         const StreamParams& p, hipStream_t stream);
 int stream_lds_bytes(int stages, int consumers);
 
 hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
@@ -54,6 +57,7 @@ struct GemmParams {
   int32_t tiles_m, tiles_n, k_steps;
   int32_t items;          // output tiles
   int32_t swz_shift;
+  int32_t b_swz;          // 1: XOR-swizzle the B K-rows (default)
   uint32_t spin_limit;
   uint32_t* status;
   uint32_t* trace;

@@ -1,4 +1,4 @@
-// Warp-specialised tile stream: one producer wave fills an S-slot LDS ring with
+// Warp-specialised tile stream: PW producer waves fill an S-slot LDS ring with
 // direct-to-LDS loads; C consumer waves copy each tile back out (with optional
 // per-tile checksums) or reduce it into fp32 row sums.
 //
@@ -15,16 +15,22 @@
 // `split` segments; item i is segment i / n_strips of strip i % n_strips, so
 // workgroups launched together touch neighbouring strips. A workgroup walks
 // items blockIdx.x, blockIdx.x + gridDim.x, ... and its cursors run on across
-// items (a persistent ring).
+// items (a persistent ring). With `xcd_remap`, the item a workgroup takes is
+// permuted so that the workgroups of one XCD (dispatch is round-robin over
+// the 8 XCDs) stream neighbouring strips.
 //
 // Slot layout: tile row r (128 B) holds its 16-byte chunk c at position
 // c ^ ((r >> shift) & 7). One producer DMA instruction q moves rows 8q..8q+7:
 // lane l writes LDS position l & 7 of row 8q + (l >> 3), so it fetches the
-// global chunk swz(row, l & 7).
+// global chunk swz(row, l & 7). With PW = 2 producer waves, wave w issues
+// blocks 8w..8w+7 of every tile; full[s] then expects PW arrivals, and each
+// wave can keep up to 3 tiles of lag (24 loads outstanding).
 #include "pipe_device.hpp"
 #include "pipe_kernels.hpp"
 
 namespace pipe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int S, int C>
 struct StreamLds {
@@ -54,6 +60,13 @@ __device__ __forceinline__ void trace_record(const StreamParams& p, int t, int e
   }
 }
 
+// Work item taken by the workgroup for its n-th item slot.
+__device__ __forceinline__ int item_index(const StreamParams& p, int slot_item) {
+  if (!p.xcd_remap) return slot_item;
+  const int per = p.items >> 3;  // items % 8 == 0 whenever xcd_remap is set
+  return (slot_item & 7) * per + (slot_item >> 3);
+}
+
 __device__ __forceinline__ void tile_coords(const StreamParams& p, int item, int k,
                                             int& tile_row, int& tile_col) {
   int strip = item % p.n_strips;
@@ -75,20 +88,35 @@ __device__ __forceinline__ int item_len(const StreamParams& p, int item) {
   return len < p.seg_len ? len : p.seg_len;
 }
 
+// s_waitcnt vmcnt(k * LOADS) for a wave-uniform number k of younger tiles.
+template <int LOADS>
+__device__ __forceinline__ void wait_tiles_younger(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<LOADS>(); break;
+    case 2: wait_vmcnt<2 * LOADS>(); break;
+    default: wait_vmcnt<3 * LOADS>(); break;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Producer wave
+// Producer waves
 // ---------------------------------------------------------------------------
-template <int S, int C>
-__device__ void producer(const StreamParams& p, StreamLds<S, C>& lds) {
+template <int S, int C, int PW>
+__device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
+  constexpr int kLoads = kBlocksPerTile / PW;  // DMA instructions per tile per wave
+  static_assert(3 * kLoads < 64, "vmcnt counts at most 63 outstanding loads");
   const int lane = lane_id();
   const int lrow = lane >> 3;  // row within a 1 KiB block
   const int lpos = lane & 7;   // chunk position within the row
+  const int lag = p.lag;
   PipeState w = producer_start(S, p.start_phase);
   int pending = 0;  // tiles issued but not yet committed (their full not arrived)
   int t = 0;
   bool ok = true;
 
-  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+  for (int it = blockIdx.x; ok && it < p.items; it += gridDim.x) {
+    const int item = item_index(p, it);
     const int len = item_len(p, item);
     for (int k = 0; k < len; ++k, ++t) {
       // producer_acquire: wait until consumers released this slot.
@@ -96,25 +124,36 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds) {
         ok = false;
         break;
       }
-      trace_record(p, t, 0, w, 0);
+      if (pw == 0) trace_record(p, t, 0, w, 0);
       int tr, tc;
       tile_coords(p, item, k, tr, tc);
       const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc * kRowBytes;
       const uint32_t slot = uniform(lds_addr(&lds.slots[w.index][0]));
+      if (p.nt) {
 #pragma unroll
-      for (int q = 0; q < kBlocksPerTile; ++q) {
-        const int r = q * kRowsPerBlock + lrow;
-        const int c = swz(r, lpos, p.swz_shift);
-        dma_block(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
+        for (int j = 0; j < kLoads; ++j) {
+          const int q = pw * kLoads + j;
+          const int r = q * kRowsPerBlock + lrow;
+          const int c = swz(r, lpos, p.swz_shift);
+          dma_block_nt(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+          const int q = pw * kLoads + j;
+          const int r = q * kRowsPerBlock + lrow;
+          const int c = swz(r, lpos, p.swz_shift);
+          dma_block(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
+        }
       }
       ++pending;
       // Commit the oldest in-flight tile once `lag` newer tiles are in flight:
-      // its 16 loads are done when at most 16*(pending-1) remain outstanding.
-      if (pending > p.lag) {
-        wait_vmcnt_tiles(pending - 1);
+      // its loads are done when at most kLoads*(pending-1) remain outstanding.
+      if (pending > lag) {
+        wait_tiles_younger<kLoads>(pending - 1);
         int oldest = w.index - (pending - 1);
         if (oldest < 0) oldest += S;
-        bar_arrive(&lds.full[oldest], 1u);
+        bar_arrive(&lds.full[oldest], (uint32_t)PW);
         --pending;
       }
       w.inc();
@@ -122,10 +161,10 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds) {
   }
   // Commit whatever is still in flight, oldest first.
   while (pending > 0) {
-    wait_vmcnt_tiles(pending - 1);
+    wait_tiles_younger<kLoads>(pending - 1);
     int oldest = w.index - pending;
     if (oldest < 0) oldest += S;
-    bar_arrive(&lds.full[oldest], 1u);
+    bar_arrive(&lds.full[oldest], (uint32_t)PW);
     --pending;
   }
   // producer_tail: S more empty phases, so every slot has been drained.
@@ -158,7 +197,8 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
   int t = 0;
   bool ok = true;
 
-  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+  for (int it = blockIdx.x; ok && it < p.items; it += gridDim.x) {
+    const int item = item_index(p, it);
     const int len = item_len(p, item);
     int tr = 0, tc = 0;
     for (int k = 0; k < len; ++k, ++t) {
@@ -187,7 +227,12 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
             const int c = swz(r, lpos, p.swz_shift);
             uint8_t* gd = p.dst + ((int64_t)tr * kTileRows + r) * p.ld_dst +
                           (int64_t)tc * kRowBytes + c * kChunkBytes;
-            *reinterpret_cast<uint4*>(gd) = v[j];
+            if (p.nt) {
+              const u32x4 nv = {v[j].x, v[j].y, v[j].z, v[j].w};
+              __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(gd));
+            } else {
+              *reinterpret_cast<uint4*>(gd) = v[j];
+            }
             if (p.checksums) {
               csum += (v[j].x & 0xFFFFu) + (v[j].x >> 16) + (v[j].y & 0xFFFFu) + (v[j].y >> 16) +
                       (v[j].z & 0xFFFFu) + (v[j].z >> 16) + (v[j].w & 0xFFFFu) + (v[j].w >> 16);
@@ -257,8 +302,8 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int C, int OP>
-__global__ void __launch_bounds__(64 * (1 + C)) stream_kernel(StreamParams p) {
+template <int S, int C, int PW, int OP>
+__global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
   __shared__ StreamLds<S, C> lds;
   const int wave = (int)(threadIdx.x >> 6);
   if (threadIdx.x < S) {
@@ -267,10 +312,10 @@ __global__ void __launch_bounds__(64 * (1 + C)) stream_kernel(StreamParams p) {
     lds.fin[threadIdx.x] = 0u;
   }
   __syncthreads();
-  if (wave == 0)
-    producer<S, C>(p, lds);
+  if (wave < PW)
+    producer<S, C, PW>(p, lds, wave);
   else
-    consumer<S, C, OP>(p, lds, wave - 1);
+    consumer<S, C, OP>(p, lds, wave - PW);
 }
 
 // ---------------------------------------------------------------------------
@@ -296,36 +341,44 @@ __global__ void __launch_bounds__(256) fill_f32(float* __restrict__ out, int64_t
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int S, int C>
-static hipError_t launch_sc(int op, int grid, const StreamParams& p, hipStream_t stream) {
-  dim3 block(64 * (1 + C));
+template <int S, int C, int PW>
+static hipError_t launch_scp(int op, int grid, const StreamParams& p, hipStream_t stream) {
+  dim3 block(64 * (PW + C));
   if (op == kOpCopy)
-    hipLaunchKernelGGL((stream_kernel<S, C, kOpCopy>), dim3(grid), block, 0, stream, p);
+    hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy>), dim3(grid), block, 0, stream, p);
   else
-    hipLaunchKernelGGL((stream_kernel<S, C, kOpRowsum>), dim3(grid), block, 0, stream, p);
+    hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum>), dim3(grid), block, 0, stream, p);
   return hipGetLastError();
 }
 
+template <int S, int C>
+static hipError_t launch_sc(int op, int pw, int grid, const StreamParams& p,
+                            hipStream_t stream) {
+  if (pw == 2) return launch_scp<S, C, 2>(op, grid, p, stream);
+  return launch_scp<S, C, 1>(op, grid, p, stream);
+}
+
 template <int S>
-static hipError_t launch_s(int op, int consumers, int grid, const StreamParams& p,
+static hipError_t launch_s(int op, int consumers, int pw, int grid, const StreamParams& p,
                            hipStream_t stream) {
   switch (consumers) {
-    case 1: return launch_sc<S, 1>(op, grid, p, stream);
-    case 2: return launch_sc<S, 2>(op, grid, p, stream);
-    case 3: return launch_sc<S, 3>(op, grid, p, stream);
-    case 4: return launch_sc<S, 4>(op, grid, p, stream);
-    case 8: return launch_sc<S, 8>(op, grid, p, stream);
+    case 1: return launch_sc<S, 1>(op, pw, grid, p, stream);
+    case 2: return launch_sc<S, 2>(op, pw, grid, p, stream);
+    case 3: return launch_sc<S, 3>(op, pw, grid, p, stream);
+    case 4: return launch_sc<S, 4>(op, pw, grid, p, stream);
+    case 8: return launch_sc<S, 8>(op, pw, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_stream(int op, int stages, int consumers, int grid, const StreamParams& p,
-                         hipStream_t stream) {
+hipError_t launch_stream(int op, int stages, int consumers, int producers, int grid,
+                         const StreamParams& p, hipStream_t stream) {
+  if (producers != 1 && producers != 2) return hipErrorInvalidValue;
   switch (stages) {
-    case 1: return launch_s<1>(op, consumers, grid, p, stream);
-    case 2: return launch_s<2>(op, consumers, grid, p, stream);
-    case 3: return launch_s<3>(op, consumers, grid, p, stream);
-    case 4: return launch_s<4>(op, consumers, grid, p, stream);
+    case 1: return launch_s<1>(op, consumers, producers, grid, p, stream);
+    case 2: return launch_s<2>(op, consumers, producers, grid, p, stream);
+    case 3: return launch_s<3>(op, consumers, producers, grid, p, stream);
+    case 4: return launch_s<4>(op, consumers, producers, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

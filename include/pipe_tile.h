@@ -60,6 +60,10 @@ typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_
 /* cfg->flags */
 #define PIPE_FLAG_TRACE 0x1u           /* record per-tile cursor values into cfg->trace */
 #define PIPE_FLAG_ROW_STRIPS 0x2u      /* copy: walk tiles along rows instead of down columns */
+#define PIPE_FLAG_NONTEMPORAL 0x4u     /* copy/rowsum: non-temporal hint on streamed loads/stores */
+#define PIPE_FLAG_GEMM_B_LINEAR 0x8u   /* gemm: store B K-rows in LDS without the XOR swizzle */
+#define PIPE_FLAG_XCD_REMAP 0x10u      /* copy/rowsum: give each XCD neighbouring strips (when the
+                                          item count is a multiple of 8) */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the
@@ -82,7 +86,7 @@ typedef struct {
   int32_t tile_m;         /* copy/rowsum: 128; gemm: 128                                  */
   int32_t tile_n;         /* copy/rowsum: 64 fp16; gemm: 128                              */
   int32_t tile_k;         /* gemm only: 64                                                */
-  int32_t producer_waves; /* copy/rowsum: 1; gemm: 2 (one for A, one for B)               */
+  int32_t producer_waves; /* copy/rowsum: 1 or 2 (2 splits each tile's loads); gemm: 2     */
   int32_t consumer_waves; /* copy/rowsum: 1..8; gemm: 4                                   */
   int32_t grid;           /* workgroups; 0 = one per work item (capped by the device)     */
   int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default 1  */

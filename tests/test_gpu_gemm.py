@@ -30,6 +30,18 @@ def test_gemm_small_integers_bit_exact(S):
     assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
 
 
+@pytest.mark.parametrize("shift", [0, 1])
+@pytest.mark.parametrize("b_linear", [False, True])
+def test_gemm_swizzle_variants_bit_exact(shift, b_linear):
+    M, N, K = 256, 256, 256
+    A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=4, stream=0).to(DEV)
+    B = synth.small_int((K, N), -2, 2, torch.bfloat16, seed=4, stream=1).to(DEV)
+    C = pt.pipe_gemm_mainloop(A, B, swizzle_shift=shift,
+                              flags=pt.PIPE_FLAG_GEMM_B_LINEAR if b_linear else 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), R.gemm_f64(_f32(A), _f32(B)))
+
+
 def test_gemm_identity_operands():
     K = 256
     A = torch.eye(K, dtype=torch.bfloat16, device=DEV)

@@ -90,6 +90,22 @@ def test_copy_stage_and_wave_sweep(S, C):
     assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
 
 
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("C", [2, 3, 8])
+@pytest.mark.parametrize("remap", [False, True])
+def test_copy_two_producer_waves(S, C, remap):
+    M, N = 1024, 1024  # 8 x 16 tiles, 16 column strips x 2 segments = 32 items
+    src = synth.unique_codes(M, N).to(DEV)
+    st = _status()
+    flags = pt.PIPE_FLAG_XCD_REMAP if remap else 0
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, stages=S, consumer_waves=C,
+                                 producer_waves=2, split=2, grid=9, flags=flags, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
+
+
 @pytest.mark.parametrize("shift", [0, 1, 2, 3])
 @pytest.mark.parametrize("row_strips", [False, True])
 def test_copy_swizzle_and_walk_order(shift, row_strips):
@@ -168,6 +184,16 @@ def test_rowsum_small_integers_bit_exact(S, C, split):
     out = pt.pipe_rowsum(A, stages=S, consumer_waves=C, split=split, grid=11, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+@pytest.mark.parametrize("S", [2, 4])
+@pytest.mark.parametrize("remap", [False, True])
+def test_rowsum_two_producer_waves_bit_exact(S, remap):
+    A = synth.small_int((1024, 4096), -8, 8, torch.float16, seed=6).to(DEV)
+    flags = pt.PIPE_FLAG_XCD_REMAP | pt.PIPE_FLAG_NONTEMPORAL if remap else 0
+    out = pt.pipe_rowsum(A, stages=S, consumer_waves=8, producer_waves=2, split=4, flags=flags)
+    torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
 
 
