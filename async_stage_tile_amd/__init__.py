@@ -207,7 +207,8 @@ def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):
         raise ValueError("dst shape differs from src")
     chk = None
     if checksums:
-        chk = torch.empty((M // 128) * (N // 64), dtype=torch.int32, device=src.device)
+        chk = torch.empty(((M + 127) // 128) * ((N + 63) // 64), dtype=torch.int32,
+                          device=src.device)
     c = make_config(PIPE_OP_COPY, **cfg)
     st = lib().pipe_tile_copy(_ptr(src), _ptr(dst), M, N, ld_src, ld_dst, ctypes.byref(c),
                               _ptr(chk), _stream(stream))

@@ -42,18 +42,38 @@ pipe_status_t library_status_word(uint32_t** out) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Defaults per op, from the launch-shape sweeps on MI355X (bandwidth of the
+// 16384^2 copy and 8192 x 65536 row sum, TFLOP/s of the 4096^3 GEMM).
 pipe_config_t defaults(pipe_op_t op) {
   pipe_config_t c{};
-  c.stages = 3;
   c.tile_m = 128;
   c.tile_n = (op == PIPE_OP_GEMM) ? 128 : 64;
   c.tile_k = (op == PIPE_OP_GEMM) ? 64 : 0;
-  c.producer_waves = (op == PIPE_OP_GEMM) ? 2 : 1;
-  c.consumer_waves = (op == PIPE_OP_GEMM) ? 4 : 3;
   c.grid = 0;
   c.split = 0;
-  c.swizzle_shift = 0;
-  c.flags = 0;
+  switch (op) {
+    case PIPE_OP_COPY:
+      c.stages = 2;
+      c.producer_waves = 2;
+      c.consumer_waves = 4;
+      c.swizzle_shift = 0;
+      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP;
+      break;
+    case PIPE_OP_ROWSUM:
+      c.stages = 4;
+      c.producer_waves = 1;
+      c.consumer_waves = 8;
+      c.swizzle_shift = 0;
+      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP;
+      break;
+    default:
+      c.stages = 4;
+      c.producer_waves = 2;
+      c.consumer_waves = 4;
+      c.swizzle_shift = 1;
+      c.flags = 0;
+      break;
+  }
   c.spin_limit = 0;
   c.trace_capacity = 0;
   c.trace = nullptr;
@@ -89,16 +109,17 @@ struct StreamGeom {
   int32_t tile_rows, tile_cols, n_strips, strip_len, seg_len, split, items, grid;
 };
 
-// Rowsum default split: the smallest power of two that gives >= 512 work items.
+// Rowsum default split: the smallest power of two that gives >= 256 work
+// items (one workgroup per CU of an MI355X).
 int rowsum_default_split(int n_strips, int strip_len) {
   int split = 1;
-  while ((int64_t)n_strips * split < 512 && split < strip_len) split *= 2;
+  while ((int64_t)n_strips * split < 256 && split < strip_len) split *= 2;
   return split < strip_len ? split : strip_len;
 }
 
 pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool row_strips,
                               bool rowsum, StreamGeom* g) {
-  const int64_t tr = M / 128, tc = N / 64;
+  const int64_t tr = (M + 127) / 128, tc = (N + 63) / 64;
   if (tr > INT32_MAX || tc > INT32_MAX) return PIPE_ERR_SHAPE;
   g->tile_rows = (int32_t)tr;
   g->tile_cols = (int32_t)tc;
@@ -186,7 +207,7 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
   if (M < 0 || N < 0 || ld_src < N || ld_dst < N) return PIPE_ERR_SHAPE;
-  if (M % 128 != 0 || N % 64 != 0) return PIPE_ERR_SHAPE;
+  if (N % 8 != 0) return PIPE_ERR_SHAPE;
   if (M == 0 || N == 0) return PIPE_OK;
   if (src == nullptr || dst == nullptr) return PIPE_ERR_NULL;
   if (!aligned16(src) || !aligned16(dst) || (ld_src % 8) || (ld_dst % 8)) return PIPE_ERR_ALIGN;
@@ -205,6 +226,7 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   p.ld_src = ld_src * 2;
   p.ld_dst = ld_dst * 2;
   p.M = M;
+  p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
   return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, c.producer_waves, g.grid, p,
@@ -217,7 +239,7 @@ pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_confi
   const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
-  if (M < 0 || N < 0 || M % 128 != 0 || N % 64 != 0) return PIPE_ERR_SHAPE;
+  if (M < 0 || N < 0 || N % 8 != 0) return PIPE_ERR_SHAPE;
   *bytes = 0;
   if (M == 0 || N == 0) return PIPE_OK;
   StreamGeom g;
@@ -235,7 +257,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   if (s != PIPE_OK) return s;
   if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // always row strips
   if (M < 0 || N < 0 || lda < N) return PIPE_ERR_SHAPE;
-  if (M % 128 != 0 || N % 64 != 0) return PIPE_ERR_SHAPE;
+  if (N % 8 != 0) return PIPE_ERR_SHAPE;
   if (M == 0) return PIPE_OK;
   if (out == nullptr) return PIPE_ERR_NULL;
   if (!aligned4(out)) return PIPE_ERR_ALIGN;
@@ -260,6 +282,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   p.ld_src = lda * 2;
   p.ld_dst = 0;
   p.M = M;
+  p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
   s = hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, c.producer_waves, g.grid, p, st));
@@ -276,7 +299,8 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t
   if (s != PIPE_OK) return s;
   if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
   if (c.tile_m != 128 || c.tile_n != 128 || c.tile_k != 64) return PIPE_ERR_CONFIG;
-  if (c.producer_waves != 2 || c.consumer_waves != 4) return PIPE_ERR_CONFIG;
+  if ((c.producer_waves != 2 && c.producer_waves != 4) || c.consumer_waves != 4)
+    return PIPE_ERR_CONFIG;
   if (c.split > 1) return PIPE_ERR_CONFIG;
   if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE)) return PIPE_ERR_CONFIG;
   if (gemm_lds_bytes(c.stages) > kLdsLimit) return PIPE_ERR_STAGES;
@@ -315,7 +339,7 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t
   const int grid = (c.grid == 0 || c.grid > p.items) ? p.items : c.grid;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  return hip_status(launch_gemm(c.stages, grid, p, st));
+  return hip_status(launch_gemm(c.stages, c.producer_waves, grid, p, st));
 }
 
 pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
@@ -331,7 +355,7 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     const int64_t items = (M / 128) * (N / 128);
     if (items > INT32_MAX) return PIPE_ERR_SHAPE;
     info->lds_bytes = gemm_lds_bytes(c.stages);
-    info->threads = 64 * 6;
+    info->threads = 64 * (c.producer_waves + 4);
     info->items = (int32_t)items;
     info->grid = (c.grid == 0 || c.grid > info->items) ? info->items : c.grid;
     info->tiles_per_item = (int32_t)(K / 64);
@@ -341,7 +365,7 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   if (op != PIPE_OP_COPY && op != PIPE_OP_ROWSUM) return PIPE_ERR_CONFIG;
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
-  if (M < 0 || N < 0 || M % 128 || N % 64) return PIPE_ERR_SHAPE;
+  if (M < 0 || N < 0 || N % 8) return PIPE_ERR_SHAPE;
   const bool rowsum = op == PIPE_OP_ROWSUM;
   const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);
   info->lds_bytes = stream_lds_bytes(c.stages, c.consumer_waves);

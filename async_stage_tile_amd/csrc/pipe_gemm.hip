@@ -11,10 +11,14 @@
 // 4 x (2 x 2) v_mfma_f32_32x32x16_bf16 per stage, release empty, and write
 // their fp32 accumulators to C after the last K step.
 //
-// Why two producer waves: each stage is 32 wave-wide DMA instructions. One
-// wave keeping a second stage in flight would need more than the 63
-// outstanding loads vmcnt can count; split over two waves (A and B), each
-// keeps up to 2 stages of lag with at most 48 loads outstanding.
+// Producer waves: each stage is 32 wave-wide DMA instructions. One wave
+// keeping a second stage in flight would need more than the 63 outstanding
+// loads vmcnt can count, so the loads are split over PW waves (PW = 2: A and
+// B; PW = 4: each half of A and of B), each committing with up to
+// min(S - 1, 48 / (32 / PW)) stages of lag.
+//
+// Consumers interleave the LDS fragment reads of each 16-deep K sub-step with
+// the MFMAs of the previous one, and release the slot after the last read.
 //
 // LDS layout of a stage: A rows of 128 B with 16-byte chunk c of row r at
 // position c ^ ((r >> shift) & 7) (the MFMA A fragment reads one chunk of 32
@@ -52,7 +56,6 @@ constexpr int kGemmK = 64;
 constexpr int kAStageBytes = kGemmTile * kGemmK * 2;  // 16 KiB
 constexpr int kBStageBytes = kGemmK * kGemmTile * 2;  // 16 KiB
 constexpr int kBRowBytes = kGemmTile * 2;             // 256
-constexpr int kGemmThreads = 64 * 6;                  // 2 producer + 4 consumer waves
 
 template <int S>
 struct GemmLds {
@@ -67,16 +70,31 @@ __device__ __forceinline__ void gemm_tile_of(const GemmParams& p, int item, int&
   tn = item % p.tiles_n;
 }
 
+// s_waitcnt vmcnt(k * LOADS) for a wave-uniform number k of younger stages.
+template <int LOADS>
+__device__ __forceinline__ void wait_stages_younger(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<LOADS>(); break;
+    case 2: wait_vmcnt<2 * LOADS>(); break;
+    default: wait_vmcnt<(3 * LOADS < 63 ? 3 * LOADS : 48)>(); break;
+  }
+}
+
 // B-row chunk swizzle (positions of the 16 chunks of a 256-byte K-row).
 __device__ __forceinline__ int swz_b(int k, int on) {
   return on ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : 0;
 }
 
-template <int S>
-__device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int role) {
+template <int S, int PW>
+__device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
+  constexpr int kLoads = 32 / PW;                     // DMA instructions per stage per wave
+  constexpr int kMaxLag = 48 / kLoads;                // <= 48 loads outstanding
   const int lane = lane_id();
+  const bool is_a = pw < PW / 2;                      // first half of the waves load A
+  const int part = is_a ? pw : pw - PW / 2;           // which share of the 16 blocks
   PipeState w = producer_start(S, 1u);
-  const int lag = S - 1 < 2 ? S - 1 : 2;
+  const int lag = S - 1 < kMaxLag ? S - 1 : kMaxLag;
   int pending = 0;
   bool ok = true;
   for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
@@ -89,12 +107,13 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int role) {
         ok = false;
         break;
       }
-      if (role == 0) {
+      if (is_a) {
         const uint32_t sa = uniform(lds_addr(&lds.a[w.index][0]));
         const uint8_t* a0 = ga + (int64_t)ks * kGemmK * 2;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int j = 0; j < kLoads; ++j) {
           // A: rows 8q..8q+7, lane -> (row 8q + l/8, position l%8).
+          const int q = part * kLoads + j;
           const int r = q * 8 + (lane >> 3);
           const int c = swz(r, lane & 7, p.swz_shift);
           dma_block(a0 + (int64_t)r * p.lda + c * 16, sa + q * kBlockBytes);
@@ -103,8 +122,9 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int role) {
         const uint32_t sb = uniform(lds_addr(&lds.b[w.index][0]));
         const uint8_t* b0 = gb + (int64_t)ks * kGemmK * p.ldb;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int j = 0; j < kLoads; ++j) {
           // B: rows 4q..4q+3 of 256 B, lane -> (row 4q + l/16, position l%16).
+          const int q = part * kLoads + j;
           const int r = q * 4 + (lane >> 4);
           const int c = (lane & 15) ^ swz_b(r, p.b_swz);
           dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + q * kBlockBytes);
@@ -112,20 +132,20 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int role) {
       }
       ++pending;
       if (pending > lag) {
-        wait_vmcnt_tiles(pending - 1);
+        wait_stages_younger<kLoads>(pending - 1);
         int oldest = w.index - (pending - 1);
         if (oldest < 0) oldest += S;
-        bar_arrive(&lds.full[oldest], 2u);
+        bar_arrive(&lds.full[oldest], (uint32_t)PW);
         --pending;
       }
       w.inc();
     }
   }
   while (pending > 0) {
-    wait_vmcnt_tiles(pending - 1);
+    wait_stages_younger<kLoads>(pending - 1);
     int oldest = w.index - pending;
     if (oldest < 0) oldest += S;
-    bar_arrive(&lds.full[oldest], 2u);
+    bar_arrive(&lds.full[oldest], (uint32_t)PW);
     --pending;
   }
   if (ok) {
@@ -202,6 +222,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
             acc[mi][ni] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
       }
+      // consumer_release once this wave's LDS reads of the slot have returned.
       wait_lgkmcnt0();
       bar_arrive(&lds.empty[rd.index], 4u);
       rd.inc();
@@ -223,8 +244,8 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S>
-__global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmParams p) {
+template <int S, int PW>
+__global__ void __launch_bounds__(64 * (PW + 4)) gemm_kernel(GemmParams p) {
   __shared__ GemmLds<S> lds;
   const int wave = (int)(threadIdx.x >> 6);
   if (threadIdx.x < S) {
@@ -232,24 +253,32 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmParams p) {
     lds.empty[threadIdx.x] = 0u;
   }
   __syncthreads();
-  if (wave < 2)
-    gemm_producer<S>(p, lds, wave);
+  if (wave < PW)
+    gemm_producer<S, PW>(p, lds, wave);
   else
-    gemm_consumer<S>(p, lds, wave - 2);
+    gemm_consumer<S>(p, lds, wave - PW);
+}
+
+template <int PW>
+hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t stream) {
+  const dim3 g(grid), b(64 * (PW + 4));
+  switch (stages) {
+    case 1: hipLaunchKernelGGL((gemm_kernel<1, PW>), g, b, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<2, PW>), g, b, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((gemm_kernel<3, PW>), g, b, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<4, PW>), g, b, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int stages, int grid, const GemmParams& p, hipStream_t stream) {
-  const dim3 g(grid), b(kGemmThreads);
-  switch (stages) {
-    case 1: hipLaunchKernelGGL(gemm_kernel<1>, g, b, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(gemm_kernel<2>, g, b, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL(gemm_kernel<3>, g, b, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(gemm_kernel<4>, g, b, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
+                       hipStream_t stream) {
+  if (producers == 4) return launch_gemm_pw<4>(stages, grid, p, stream);
+  if (producers == 2) return launch_gemm_pw<2>(stages, grid, p, stream);
+  return hipErrorInvalidValue;
 }
 
 int gemm_lds_bytes(int stages) { return stages * (kAStageBytes + kBStageBytes) + stages * 8; }

@@ -17,9 +17,10 @@ struct StreamParams {
   uint32_t* status;       // never null
   int64_t ld_src;         // row pitch, bytes
   int64_t ld_dst;         // row pitch, bytes
-  int64_t M;              // rows (rowsum partial stride)
-  int32_t tile_rows;      // M / 128
-  int32_t tile_cols;      // N / 64
+  int64_t M;              // rows (also the rowsum partial stride)
+  int64_t N;              // columns (fp16 elements, a multiple of 8)
+  int32_t tile_rows;      // ceil(M / 128)
+  int32_t tile_cols;      // ceil(N / 64)
   int32_t n_strips;
   int32_t strip_len;      // tiles per strip
   int32_t seg_len;        // tiles per segment
@@ -64,7 +65,8 @@ struct GemmParams {
   int32_t trace_cap;
 };
 
-hipError_t launch_gemm(int stages, int grid, const GemmParams& p, hipStream_t stream);
+hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
+                       hipStream_t stream);
 int gemm_lds_bytes(int stages);
 
 }  // namespace pipe

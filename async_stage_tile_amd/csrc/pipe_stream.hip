@@ -19,6 +19,12 @@
 // permuted so that the workgroups of one XCD (dispatch is round-robin over
 // the 8 XCDs) stream neighbouring strips.
 //
+// Ragged edges: when M or N is not a multiple of the tile, the last tile row /
+// column is partial. Every producer lane still issues its DMA (so each
+// instruction counts once in vmcnt); a lane whose (row, chunk) lies outside
+// the matrix fetches the matrix's first chunk instead, and consumers skip the
+// out-of-range positions when they store, checksum or sum.
+//
 // Slot layout: tile row r (128 B) holds its 16-byte chunk c at position
 // c ^ ((r >> shift) & 7). One producer DMA instruction q moves rows 8q..8q+7:
 // lane l writes LDS position l & 7 of row 8q + (l >> 3), so it fetches the
@@ -88,6 +94,14 @@ __device__ __forceinline__ int item_len(const StreamParams& p, int item) {
   return len < p.seg_len ? len : p.seg_len;
 }
 
+// Global address of the 16-byte chunk starting at (row, col); chunks outside
+// the matrix map to its first chunk (always readable when M, N > 0).
+__device__ __forceinline__ const uint8_t* src_chunk(const StreamParams& p, int64_t row,
+                                                    int64_t col) {
+  const bool in = row < p.M && col < p.N;
+  return p.src + (in ? row * p.ld_src + col * 2 : 0);
+}
+
 // s_waitcnt vmcnt(k * LOADS) for a wave-uniform number k of younger tiles.
 template <int LOADS>
 __device__ __forceinline__ void wait_tiles_younger(int k) {
@@ -127,7 +141,8 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
       if (pw == 0) trace_record(p, t, 0, w, 0);
       int tr, tc;
       tile_coords(p, item, k, tr, tc);
-      const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc * kRowBytes;
+      const int64_t row0 = (int64_t)tr * kTileRows;
+      const int64_t col0 = (int64_t)tc * kTileCols;
       const uint32_t slot = uniform(lds_addr(&lds.slots[w.index][0]));
       if (p.nt) {
 #pragma unroll
@@ -135,7 +150,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
           const int q = pw * kLoads + j;
           const int r = q * kRowsPerBlock + lrow;
           const int c = swz(r, lpos, p.swz_shift);
-          dma_block_nt(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
+          dma_block_nt(src_chunk(p, row0 + r, col0 + c * 8), slot + q * kBlockBytes);
         }
       } else {
 #pragma unroll
@@ -143,7 +158,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
           const int q = pw * kLoads + j;
           const int r = q * kRowsPerBlock + lrow;
           const int c = swz(r, lpos, p.swz_shift);
-          dma_block(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
+          dma_block(src_chunk(p, row0 + r, col0 + c * 8), slot + q * kBlockBytes);
         }
       }
       ++pending;
@@ -225,8 +240,10 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
           if (q < kBlocksPerTile) {
             const int r = q * kRowsPerBlock + lrow;
             const int c = swz(r, lpos, p.swz_shift);
-            uint8_t* gd = p.dst + ((int64_t)tr * kTileRows + r) * p.ld_dst +
-                          (int64_t)tc * kRowBytes + c * kChunkBytes;
+            const int64_t row = (int64_t)tr * kTileRows + r;
+            const int64_t col = (int64_t)tc * kTileCols + c * 8;
+            if (row >= p.M || col >= p.N) continue;
+            uint8_t* gd = p.dst + row * p.ld_dst + col * 2;
             if (p.nt) {
               const u32x4 nv = {v[j].x, v[j].y, v[j].z, v[j].w};
               __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(gd));
@@ -265,6 +282,11 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
         for (int j = 0; j < NB; ++j) {
           const int q = cw + j * C;
           if (q < kBlocksPerTile) {
+            // Lane order within the block is row-major over (row, position),
+            // so the position's logical chunk decides the column.
+            const int r = q * kRowsPerBlock + lrow;
+            const int64_t col = (int64_t)tc * kTileCols + swz(r, lpos, p.swz_shift) * 8;
+            if ((int64_t)tr * kTileRows + r >= p.M || col >= p.N) continue;
             const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
             float s = 0.f;
 #pragma unroll
@@ -292,7 +314,8 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
           const int q = cw + j * C;
           if (q < kBlocksPerTile) {
             const float s = sum8_lanes(acc[j]);
-            if (lpos == 0) o[q * kRowsPerBlock + lrow] = s;
+            const int r = q * kRowsPerBlock + lrow;
+            if (lpos == 0 && (int64_t)tr * kTileRows + r < p.M) o[r] = s;
           }
           acc[j] = 0.f;
         }

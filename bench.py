@@ -7,9 +7,14 @@ column strip. One step = one launch of the whole hot path over the matrix
 (tile walk, cursor/barrier handshakes, direct-to-LDS producer, consumer
 copy-out, release, tail).
 
-Also reported (in "extras", each timed the same way): the S sweep of the
-copy, the 3-stage row sum of fp16 8192 x 65536 (GB/s) and the 3-stage GEMM
-mainloop 4096^3 bf16 (TFLOP/s).
+Also reported (in "extras", each timed the same way): the S = 1..4 sweep of
+the copy, the row sum of fp16 8192 x 65536 (GB/s) and the GEMM mainloop
+4096^3 bf16 (TFLOP/s), each at the library's default configuration.
+
+roofline.traffic: HBM bytes per launch of the headline kernel from rocprofv3
+FETCH_SIZE / WRITE_SIZE counters (scaled by the counts the same counters give
+for a known-size device copy), read from the committed counter summary under
+profiles/ -- reported only while the kernel sources are unchanged since.
 
 Timing: `warmup` untimed steps, then exactly `steps` steps between
 synchronisations; per-launch kernel time from HIP events recorded on the
@@ -39,8 +44,40 @@ ROWSUM_M, ROWSUM_N = 8192, 65536
 GEMM_N = 4096
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "copy_16384x16384_counters.md")
+KERNEL_SOURCES = ("pipe_device.hpp", "pipe_kernels.hpp", "pipe_stream.hip")
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """sha256 (first 16 hex digits) of the device sources of the stream kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "async_stage_tile_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_name):
+    """HBM bytes per launch measured by rocprofv3 counters for this exact kernel.
+
+    Read from the `traffic_record:` line of the committed counter summary; None
+    when there is none, or when the kernel or its sources changed since the
+    counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            lines = [ln for ln in f if ln.startswith("traffic_record:")]
+    except OSError:
+        return None
+    for ln in lines:
+        rec = json.loads(ln.split(":", 1)[1])
+        if rec.get("kernel") == kernel_name and rec.get("source_hash") == kernel_source_hash():
+            return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 def timed_launches(fn, steps, warmup):
@@ -64,29 +101,44 @@ def timed_launches(fn, steps, warmup):
     return wall, kern
 
 
-def bench_copy(stages, steps, warmup, consumer_waves=3, split=1, grid=0):
+_COPY_BUF = {}
+
+
+def copy_buffers():
+    import torch
+
+    import synth
+    if not _COPY_BUF:
+        src = synth.uniform((COPY_M, COPY_N), torch.float16, seed=42, device="cuda")
+        _COPY_BUF["src"] = src
+        _COPY_BUF["dst"] = torch.empty_like(src)
+    return _COPY_BUF["src"], _COPY_BUF["dst"]
+
+
+def bench_copy(stages, steps, warmup, **cfg):
+    """The library's default copy configuration, with `stages` and any overrides."""
     import torch
 
     import async_stage_tile_amd as pt
-    import synth
-    src = synth.uniform((COPY_M, COPY_N), torch.float16, seed=42, device="cuda")
-    dst = torch.empty_like(src)
+    src, dst = copy_buffers()
+    dst.zero_()
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    kw = dict(stages=stages, consumer_waves=consumer_waves, split=split, grid=grid, status=st)
-    fn = lambda: pt.pipe_tile_copy(src, dst, **kw)
+    kw = dict(cfg, stages=stages)
+    fn = lambda: pt.pipe_tile_copy(src, dst, status=st, **kw)
     wall, kern = timed_launches(fn, steps, warmup)
     ok = int(st.item()) == 0 and torch.equal(dst.view(torch.int16), src.view(torch.int16))
-    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, COPY_M, COPY_N, **{k: v for k, v in kw.items()
-                                                                   if k != "status"})
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, COPY_M, COPY_N, **kw)
+    c = pt.make_config(pt.PIPE_OP_COPY, **kw)
     nbytes = 2 * COPY_M * COPY_N * 2
-    del src, dst
-    return {"stages": stages, "consumer_waves": consumer_waves, "split": q["split"],
+    return {"stages": stages, "producer_waves": c.producer_waves,
+            "consumer_waves": c.consumer_waves, "flags": c.flags, "split": q["split"],
             "grid": q["grid"], "lds_bytes": q["lds_bytes"], "wall_ms": wall, "kernel_ms": kern,
             "bytes": nbytes, "gbs": nbytes / (wall * 1e-3) / 1e9,
             "kernel_gbs": nbytes / (kern * 1e-3) / 1e9, "bit_exact": ok}
 
 
 def bench_rowsum(steps, warmup, stages=3):
+    """The library's default row-sum configuration at `stages`."""
     import torch
 
     import async_stage_tile_amd as pt
@@ -105,6 +157,7 @@ def bench_rowsum(steps, warmup, stages=3):
 
 
 def bench_gemm(steps, warmup, stages=3):
+    """The library's default GEMM configuration at `stages`."""
     import torch
 
     import async_stage_tile_amd as pt
@@ -144,11 +197,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--stages", type=int, default=4)
-    ap.add_argument("--consumer-waves", type=int, default=3)
-    ap.add_argument("--split", type=int, default=1)
-    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--stages", type=int, default=2,
+                    help="copy ring depth for the headline (2 = the library default, the "
+                         "best of the S sweeps measured on MI355X); 0 = best of this run's "
+                         "1..4 sweep")
     ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--only", choices=["copy", "rowsum", "gemm", "calib"], default=None,
+                    help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -162,23 +217,50 @@ def main():
         print("bench.py needs a ROCm device", file=sys.stderr)
         sys.exit(1)
 
-    log("[bench] headline copy ...")
-    head = bench_copy(args.stages, args.steps, args.warmup, args.consumer_waves, args.split,
-                      args.grid)
-    log(f"[bench] copy S={args.stages}: {head['gbs']:.1f} GB/s (kernel {head['kernel_gbs']:.1f})")
+    if args.only == "calib":
+        # Known-size reference for the traffic counters: torch's device copy of
+        # 512 MiB (512 MiB read + 512 MiB written per launch).
+        x = torch.empty(256 << 20, dtype=torch.float16, device="cuda")
+        y = torch.empty_like(x)
+        x.fill_(1.0)
+        wall, kern = timed_launches(lambda: y.copy_(x), args.steps, args.warmup)
+        log(f"[bench] calib copy of {x.numel() * 2} bytes: {kern:.4f} ms")
+        return
+    if args.only == "copy":
+        r = bench_copy(args.stages or 2, args.steps, args.warmup)
+        log(f"[bench] copy: {r}")
+        return
+    if args.only == "rowsum":
+        r = bench_rowsum(args.steps, args.warmup, args.stages or 4)
+        log(f"[bench] rowsum: {r}")
+        return
+    if args.only == "gemm":
+        r = bench_gemm(args.steps, args.warmup, args.stages or 4)
+        log(f"[bench] gemm: {r}")
+        return
+
     extras = {}
-    if not args.no_extras:
+    stages = args.stages
+    if not args.no_extras or stages == 0:
         sweep = []
         for s in (1, 2, 3, 4):
-            r = bench_copy(s, max(3, args.steps // 2), 2, args.consumer_waves, args.split,
-                           args.grid)
+            r = bench_copy(s, max(3, args.steps // 2), 2)
             log(f"[bench] sweep S={s}: {r['gbs']:.1f} GB/s")
-            sweep.append({k: r[k] for k in ("stages", "kernel_ms", "gbs", "bit_exact", "lds_bytes")})
+            sweep.append({k: r[k] for k in ("stages", "kernel_ms", "gbs", "bit_exact",
+                                            "lds_bytes")})
         extras["copy_stage_sweep"] = sweep
-        r = bench_rowsum(max(3, args.steps // 2), 2)
+        if stages == 0:
+            stages = max(sweep, key=lambda r: r["gbs"])["stages"]
+    log(f"[bench] headline copy S={stages} ...")
+    head = bench_copy(stages, args.steps, args.warmup)
+    log(f"[bench] copy S={stages}: {head['gbs']:.1f} GB/s (kernel {head['kernel_gbs']:.1f})")
+    if not args.no_extras:
+        _COPY_BUF.clear()
+        torch.cuda.empty_cache()
+        r = bench_rowsum(max(3, args.steps // 2), 2, 4)
         log(f"[bench] rowsum: {r['gbs']:.1f} GB/s")
         extras["rowsum_8192x65536_fp16"] = r
-        g = bench_gemm(max(3, args.steps // 2), 2)
+        g = bench_gemm(max(3, args.steps // 2), 2, 4)
         log(f"[bench] gemm: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16"] = g
     cpu = None
@@ -188,6 +270,9 @@ def main():
         log(f"[bench] cpu oracle: {cpu['value']:.2f} GB/s")
 
     achieved = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
+    kname = (f"void pipe::stream_kernel<{head['stages']}, {head['consumer_waves']}, "
+             f"{head['producer_waves']}, 0>(pipe::StreamParams)")
+    traffic = recorded_traffic(kname)
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -203,12 +288,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": "tile copy fp16 16384x16384 uniform[-1,1) seed 42, 128x64 tiles, "
                                "persistent column strips",
-                   "stages": head["stages"], "consumer_waves": head["consumer_waves"],
+                   "stages": head["stages"], "producer_waves": head["producer_waves"],
+                   "consumer_waves": head["consumer_waves"], "flags": head["flags"],
                    "split": head["split"], "grid": head["grid"], "parallelism": "1 GPU"},
         "pct_of_peak": round(100.0 * head["gbs"] / PEAK_HBM_GBS, 2),
         "bit_exact": head["bit_exact"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": kname},
         "cpu_baseline": cpu,
         "extras": extras,
     }

@@ -86,7 +86,7 @@ typedef struct {
   int32_t tile_m;         /* copy/rowsum: 128; gemm: 128                                  */
   int32_t tile_n;         /* copy/rowsum: 64 fp16; gemm: 128                              */
   int32_t tile_k;         /* gemm only: 64                                                */
-  int32_t producer_waves; /* copy/rowsum: 1 or 2 (2 splits each tile's loads); gemm: 2     */
+  int32_t producer_waves; /* copy/rowsum: 1 or 2; gemm: 2 or 4 (each tile's loads split) */
   int32_t consumer_waves; /* copy/rowsum: 1..8; gemm: 4                                   */
   int32_t grid;           /* workgroups; 0 = one per work item (capped by the device)     */
   int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default 1  */
@@ -113,8 +113,13 @@ int pipe_abi_version(void);
 /* Static, human-readable name of a status code. */
 const char* pipe_status_str(int status);
 
-/* Fill *cfg with the defaults of an op: stages 3, tile 128x64 (gemm 128x128x64),
- * 1 producer wave (gemm 2), 3 consumer waves (gemm 4), grid/split auto, swizzle 0. */
+/* Fill *cfg with the defaults of an op (grid and split automatic):
+ *   copy:   stages 2, tile 128x64, 2 producer + 4 consumer waves,
+ *           flags NONTEMPORAL | XCD_REMAP, swizzle shift 0;
+ *   rowsum: stages 4, tile 128x64, 1 producer + 8 consumer waves,
+ *           flags NONTEMPORAL | XCD_REMAP, swizzle shift 0;
+ *   gemm:   stages 4, tile 128x128x64, 2 producer + 4 consumer waves,
+ *           swizzle shift 1, flags 0. */
 pipe_status_t pipe_config_default(pipe_op_t op, pipe_config_t* cfg);
 
 /* Tile copy (configs: "cute（11）hopper之TMA_copy" round trip; "cute（12）
@@ -122,10 +127,12 @@ pipe_status_t pipe_config_default(pipe_op_t op, pipe_config_t* cfg);
  * the 16-bit payload is opaque (fp16, bf16, raw codes). Each tile passes
  * through a swizzled LDS slot.
  *   src, dst: device, 16-byte aligned; ld_src, ld_dst: row pitch in elements,
- *   multiples of 8, >= N. M % 128 == 0 and N % 64 == 0 (else PIPE_ERR_SHAPE);
+ *   multiples of 8, >= N. N must be a multiple of 8 (16-byte chunks; else
+ *   PIPE_ERR_SHAPE); M is arbitrary: the last tile row / column may be partial.
  *   M == 0 or N == 0 is a no-op.
  *   tile_checksums: device, nullable; if given, receives for every tile
- *   (i, j) in row-major tile order the uint32 sum of its 8192 raw 16-bit codes. */
+ *   (i, j) of the ceil(M/128) x ceil(N/64) grid, in row-major tile order, the
+ *   uint32 sum of the raw 16-bit codes of the tile's in-range elements. */
 pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N,
                              int64_t ld_src, int64_t ld_dst, const pipe_config_t* cfg,
                              uint32_t* tile_checksums, void* stream);
@@ -140,7 +147,8 @@ pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_confi
  * segment partials go to the workspace and are added in a fixed order, so the
  * result is deterministic.
  *   A: device fp16, 16-byte aligned, lda multiple of 8 and >= N;
- *   M % 128 == 0, N % 64 == 0; N == 0 gives out = 0; M == 0 is a no-op.
+ *   N a multiple of 8, M arbitrary (partial edge tiles are masked);
+ *   N == 0 gives out = 0; M == 0 is a no-op.
  *   out: device float[M]. workspace: device, >= pipe_rowsum_workspace_bytes. */
 pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
                           const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,

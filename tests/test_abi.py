@@ -36,7 +36,10 @@ def test_version_and_status_strings():
 
 def test_config_defaults():
     c = pt.make_config(pt.PIPE_OP_COPY)
-    assert (c.stages, c.tile_m, c.tile_n, c.producer_waves, c.consumer_waves) == (3, 128, 64, 1, 3)
+    assert (c.stages, c.tile_m, c.tile_n, c.producer_waves, c.consumer_waves) == (2, 128, 64, 2, 4)
+    assert c.flags == pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP
+    r = pt.make_config(pt.PIPE_OP_ROWSUM)
+    assert (r.stages, r.producer_waves, r.consumer_waves) == (4, 1, 8)
     g = pt.make_config(pt.PIPE_OP_GEMM)
     assert (g.tile_m, g.tile_n, g.tile_k, g.producer_waves, g.consumer_waves) == (128, 128, 64, 2, 4)
     assert pt.lib().pipe_config_default(7, ctypes.byref(c)) == pt.PIPE_ERR_CONFIG
@@ -53,8 +56,8 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
 
 def test_copy_validation():
     assert _copy(None, FAKE, 256, 128, 128, 128) == pt.PIPE_ERR_NULL
-    assert _copy(FAKE, FAKE, 200, 128, 128, 128) == pt.PIPE_ERR_SHAPE   # ragged M
-    assert _copy(FAKE, FAKE, 256, 100, 128, 128) == pt.PIPE_ERR_SHAPE   # ragged N
+    assert _copy(FAKE, FAKE, 200, 100, 128, 128) == pt.PIPE_ERR_SHAPE   # N not a multiple of 8
+    assert _copy(FAKE, FAKE, 256, 12, 128, 128) == pt.PIPE_ERR_SHAPE
     assert _copy(FAKE, FAKE, -128, 128, 128, 128) == pt.PIPE_ERR_SHAPE
     assert _copy(FAKE, FAKE, 256, 128, 64, 128) == pt.PIPE_ERR_SHAPE    # ld < N
     assert _copy(FAKE + 8, FAKE, 256, 128, 128, 128) == pt.PIPE_ERR_ALIGN
@@ -88,7 +91,7 @@ def test_rowsum_and_gemm_validation():
         == pt.PIPE_ERR_WORKSPACE
     assert L.pipe_rowsum(FAKE, FAKE, 1024, 4096, 4096, ctypes.byref(c), FAKE, need.value - 4,
                          None) == pt.PIPE_ERR_WORKSPACE
-    assert L.pipe_rowsum(FAKE, FAKE, 1000, 4096, 4096, ctypes.byref(c), FAKE, 1 << 20, None) \
+    assert L.pipe_rowsum(FAKE, FAKE, 1000, 4090, 4096, ctypes.byref(c), FAKE, 1 << 20, None) \
         == pt.PIPE_ERR_SHAPE
     assert L.pipe_rowsum(FAKE, None, 1024, 4096, 4096, ctypes.byref(c), FAKE, 1 << 20, None) \
         == pt.PIPE_ERR_NULL
@@ -107,18 +110,22 @@ def test_rowsum_and_gemm_validation():
 def test_query_geometry():
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, stages=4)
     assert q["items"] == 256 and q["tiles_per_item"] == 128 and q["grid"] == 256
-    assert q["lds_bytes"] >= 4 * 16384 and q["threads"] == 256
+    assert q["lds_bytes"] >= 4 * 16384 and q["threads"] == 384
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, split=3, grid=100)
     assert q["split"] == 3 and q["tiles_per_item"] == 43 and q["items"] == 768 and q["grid"] == 100
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 128, 512, grid=1)
     assert (q["items"], q["tiles_per_item"], q["grid"]) == (8, 1, 1)
     q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 8192, 65536)
-    assert q["items"] >= 512 and q["items"] == 64 * q["split"]
+    assert q["items"] >= 256 and q["items"] == 64 * q["split"]
     q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096)
     assert (q["items"], q["tiles_per_item"], q["threads"]) == (1024, 64, 384)
     assert q["lds_bytes"] >= 3 * 32768
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 300, 200, split=1)   # ragged: 3 x 4 tiles
+    assert (q["items"], q["tiles_per_item"]) == (4, 3)
+    q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 1000, 3000, split=2)
+    assert (q["items"], q["tiles_per_item"]) == (8 * 2, 24)
     with pytest.raises(pt.PipeError):
-        pt.pipe_query_kernel(pt.PIPE_OP_COPY, 100, 64)
+        pt.pipe_query_kernel(pt.PIPE_OP_COPY, 100, 60)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

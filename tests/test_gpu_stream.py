@@ -32,7 +32,7 @@ def test_copy_single_tile_per_workgroup_index_codes():
     st = _status()
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 256, 128, stages=1, split=2)
     assert (q["items"], q["grid"], q["tiles_per_item"]) == (4, 4, 1)
-    dst = pt.pipe_tile_copy(src, stages=1, split=2, status=st)
+    dst = pt.pipe_tile_copy(src, stages=1, split=2, producer_waves=1, flags=0, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert np.array_equal(_bits(dst), R.tile_copy(src.cpu().numpy()).view(np.uint16))
@@ -50,9 +50,9 @@ def test_copy_three_stage_ring_checksums_and_trace():
     src = synth.uniform((128, 512), torch.float16, seed=42).to(DEV)
     trace = torch.zeros(16 * pt.PIPE_TRACE_WORDS, dtype=torch.int32, device=DEV)
     st = _status()
-    dst, chk = pt.pipe_tile_copy(src, checksums=True, stages=3, consumer_waves=3, grid=1,
-                                 flags=pt.PIPE_FLAG_TRACE, trace=trace, trace_capacity=16,
-                                 status=st)
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, stages=3, producer_waves=1,
+                                 consumer_waves=3, grid=1, flags=pt.PIPE_FLAG_TRACE, trace=trace,
+                                 trace_capacity=16, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     s_np = src.cpu().numpy()
@@ -142,6 +142,27 @@ def test_copy_full_size_bit_exact(S):
     assert np.array_equal(_bits(dst[rows]), R.tile_copy(s_np).view(np.uint16))
 
 
+@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("shape", [(300, 200), (1000, 1000), (129, 8), (1, 72), (640, 4104)])
+@pytest.mark.parametrize("row_strips", [False, True])
+def test_copy_ragged_edges(S, shape, row_strips):
+    """Partial last tile row / column: in-range elements copied, checksums over them."""
+    M, N = shape
+    src = synth.unique_codes(M, N).to(DEV)
+    pitch = N + 24
+    out = torch.full((M, pitch), -7.0, dtype=torch.float16, device=DEV)
+    dst = out[:, :N]
+    st = _status()
+    flags = pt.PIPE_FLAG_ROW_STRIPS if row_strips else 0
+    _, chk = pt.pipe_tile_copy(src, dst, checksums=True, stages=S, grid=3, flags=flags,
+                               status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst.contiguous()), _bits(src))
+    assert bool((out[:, N:] == -7.0).all())       # pitch padding untouched
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
+
+
 # ---------------------------------------------------------------- watchdog
 def test_start_phase_zero_times_out_instead_of_hanging():
     src = synth.unique_codes(256, 256).to(DEV)
@@ -217,6 +238,26 @@ def test_rowsum_full_size_within_tolerance():
     assert int(st.item()) == 0
     ref = R.rowsum_exact(A.cpu().numpy())
     res = R.within_tol(out.cpu().numpy(), ref, 1e-3)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("shape", [(1000, 3000), (129, 72), (5, 8), (2050, 640)])
+@pytest.mark.parametrize("split", [1, 4])
+def test_rowsum_ragged_bit_exact(shape, split):
+    M, N = shape
+    A = synth.small_int((M, N), -8, 8, torch.float16, seed=11).to(DEV)
+    st = _status()
+    out = pt.pipe_rowsum(A, split=split, grid=13, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+def test_rowsum_ragged_normal_within_tolerance():
+    A = synth.normal((777, 10000), torch.float16, seed=42).to(DEV)
+    out = pt.pipe_rowsum(A)
+    torch.cuda.synchronize()
+    res = R.within_tol(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()), 1e-3)
     assert res["ok"], res
 
 
