@@ -150,7 +150,7 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   p->row_strips = row_strips ? 1 : 0;
   p->swz_shift = c.swizzle_shift;
   // Commit lag: at most S-1 tiles (the protocol's liveness bound) and at most
-  // 48 loads outstanding per producer wave (16 / producer_waves per tile).
+  // 48 loads outstanding per producer wave: (lag + 1) tiles of 16 / producer_waves.
   const int max_lag = c.producer_waves == 2 ? 3 : 2;
   p->lag = c.stages - 1 < max_lag ? c.stages - 1 : max_lag;
   p->xcd_remap = ((c.flags & PIPE_FLAG_XCD_REMAP) && g.items % 8 == 0) ? 1 : 0;

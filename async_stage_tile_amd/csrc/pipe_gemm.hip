@@ -15,7 +15,8 @@
 // keeping a second stage in flight would need more than the 63 outstanding
 // loads vmcnt can count, so the loads are split over PW waves (PW = 2: A and
 // B; PW = 4: each half of A and of B), each committing with up to
-// min(S - 1, 48 / (32 / PW)) stages of lag.
+// min(S - 1, 48 / (32 / PW) - 1) stages of lag, so that the stages in flight
+// never exceed 48 outstanding loads per wave.
 //
 // Consumers interleave the LDS fragment reads of each 16-deep K sub-step with
 // the MFMAs of the previous one, and release the slot after the last read.
@@ -89,7 +90,7 @@ __device__ __forceinline__ int swz_b(int k, int on) {
 template <int S, int PW>
 __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
   constexpr int kLoads = 32 / PW;                     // DMA instructions per stage per wave
-  constexpr int kMaxLag = 48 / kLoads;                // <= 48 loads outstanding
+  constexpr int kMaxLag = 48 / kLoads - 1;            // (lag + 1) stages <= 48 loads
   const int lane = lane_id();
   const bool is_a = pw < PW / 2;                      // first half of the waves load A
   const int part = is_a ? pw : pw - PW / 2;           // which share of the 16 blocks

@@ -19,11 +19,12 @@
 // permuted so that the workgroups of one XCD (dispatch is round-robin over
 // the 8 XCDs) stream neighbouring strips.
 //
-// Ragged edges: when M or N is not a multiple of the tile, the last tile row /
-// column is partial. Every producer lane still issues its DMA (so each
+// Ragged edges: when M or N is not a multiple of the tile, the host launches
+// the MASKED instantiation. Every producer lane still issues its DMA (so each
 // instruction counts once in vmcnt); a lane whose (row, chunk) lies outside
 // the matrix fetches the matrix's first chunk instead, and consumers skip the
-// out-of-range positions when they store, checksum or sum.
+// out-of-range positions when they store, checksum or sum. Divisible shapes
+// run the unmasked instantiation, which carries none of these tests.
 //
 // Slot layout: tile row r (128 B) holds its 16-byte chunk c at position
 // c ^ ((r >> shift) & 7). One producer DMA instruction q moves rows 8q..8q+7:
@@ -94,12 +95,15 @@ __device__ __forceinline__ int item_len(const StreamParams& p, int item) {
   return len < p.seg_len ? len : p.seg_len;
 }
 
-// Global address of the 16-byte chunk starting at (row, col); chunks outside
-// the matrix map to its first chunk (always readable when M, N > 0).
-__device__ __forceinline__ const uint8_t* src_chunk(const StreamParams& p, int64_t row,
-                                                    int64_t col) {
-  const bool in = row < p.M && col < p.N;
-  return p.src + (in ? row * p.ld_src + col * 2 : 0);
+// Rows and columns of tile (tr, tc) inside the matrix (128 and 64 except at
+// ragged edges); wave-uniform.
+__device__ __forceinline__ int rows_in(const StreamParams& p, int tr) {
+  const int64_t left = p.M - (int64_t)tr * kTileRows;
+  return left < kTileRows ? (int)left : kTileRows;
+}
+__device__ __forceinline__ int cols_in(const StreamParams& p, int tc) {
+  const int64_t left = p.N - (int64_t)tc * kTileCols;
+  return left < kTileCols ? (int)left : kTileCols;
 }
 
 // s_waitcnt vmcnt(k * LOADS) for a wave-uniform number k of younger tiles.
@@ -116,7 +120,7 @@ __device__ __forceinline__ void wait_tiles_younger(int k) {
 // ---------------------------------------------------------------------------
 // Producer waves
 // ---------------------------------------------------------------------------
-template <int S, int C, int PW>
+template <int S, int C, int PW, bool MASKED>
 __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
   constexpr int kLoads = kBlocksPerTile / PW;  // DMA instructions per tile per wave
   static_assert(3 * kLoads < 64, "vmcnt counts at most 63 outstanding loads");
@@ -141,16 +145,25 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
       if (pw == 0) trace_record(p, t, 0, w, 0);
       int tr, tc;
       tile_coords(p, item, k, tr, tc);
-      const int64_t row0 = (int64_t)tr * kTileRows;
-      const int64_t col0 = (int64_t)tc * kTileCols;
+      const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc * kRowBytes;
       const uint32_t slot = uniform(lds_addr(&lds.slots[w.index][0]));
-      if (p.nt) {
+      if constexpr (MASKED) {
+        const int rin = rows_in(p, tr), cin = cols_in(p, tc);
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
           const int q = pw * kLoads + j;
           const int r = q * kRowsPerBlock + lrow;
           const int c = swz(r, lpos, p.swz_shift);
-          dma_block_nt(src_chunk(p, row0 + r, col0 + c * 8), slot + q * kBlockBytes);
+          const uint8_t* a = g + (int64_t)r * p.ld_src + c * kChunkBytes;
+          dma_block((r < rin && c * 8 < cin) ? a : p.src, slot + q * kBlockBytes);
+        }
+      } else if (p.nt) {
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+          const int q = pw * kLoads + j;
+          const int r = q * kRowsPerBlock + lrow;
+          const int c = swz(r, lpos, p.swz_shift);
+          dma_block_nt(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
         }
       } else {
 #pragma unroll
@@ -158,7 +171,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
           const int q = pw * kLoads + j;
           const int r = q * kRowsPerBlock + lrow;
           const int c = swz(r, lpos, p.swz_shift);
-          dma_block(src_chunk(p, row0 + r, col0 + c * 8), slot + q * kBlockBytes);
+          dma_block(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
         }
       }
       ++pending;
@@ -199,7 +212,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
 // ---------------------------------------------------------------------------
 // Consumer waves
 // ---------------------------------------------------------------------------
-template <int S, int C, int OP>
+template <int S, int C, int OP, bool MASKED>
 __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
   constexpr int NB = (kBlocksPerTile + C - 1) / C;  // blocks per wave (last may idle)
   const int lane = lane_id();
@@ -224,6 +237,11 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
       }
       if (cw == 0) trace_record(p, t, 1, rd, 1 + cw);
       tile_coords(p, item, k, tr, tc);
+      int rin = kTileRows, cin = kTileCols;
+      if constexpr (MASKED) {
+        rin = rows_in(p, tr);
+        cin = cols_in(p, tc);
+      }
       const uint8_t* slot = &lds.slots[rd.index][0];
       uint4 v[NB];
 #pragma unroll
@@ -240,10 +258,11 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
           if (q < kBlocksPerTile) {
             const int r = q * kRowsPerBlock + lrow;
             const int c = swz(r, lpos, p.swz_shift);
-            const int64_t row = (int64_t)tr * kTileRows + r;
-            const int64_t col = (int64_t)tc * kTileCols + c * 8;
-            if (row >= p.M || col >= p.N) continue;
-            uint8_t* gd = p.dst + row * p.ld_dst + col * 2;
+            if constexpr (MASKED) {
+              if (r >= rin || c * 8 >= cin) continue;
+            }
+            uint8_t* gd = p.dst + ((int64_t)tr * kTileRows + r) * p.ld_dst +
+                          (int64_t)tc * kRowBytes + c * kChunkBytes;
             if (p.nt) {
               const u32x4 nv = {v[j].x, v[j].y, v[j].z, v[j].w};
               __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(gd));
@@ -282,11 +301,11 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
         for (int j = 0; j < NB; ++j) {
           const int q = cw + j * C;
           if (q < kBlocksPerTile) {
-            // Lane order within the block is row-major over (row, position),
-            // so the position's logical chunk decides the column.
-            const int r = q * kRowsPerBlock + lrow;
-            const int64_t col = (int64_t)tc * kTileCols + swz(r, lpos, p.swz_shift) * 8;
-            if ((int64_t)tr * kTileRows + r >= p.M || col >= p.N) continue;
+            if constexpr (MASKED) {
+              // Position lpos of row r holds logical chunk swz(r, lpos).
+              const int r = q * kRowsPerBlock + lrow;
+              if (r >= rin || swz(r, lpos, p.swz_shift) * 8 >= cin) continue;
+            }
             const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
             float s = 0.f;
 #pragma unroll
@@ -315,7 +334,7 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
           if (q < kBlocksPerTile) {
             const float s = sum8_lanes(acc[j]);
             const int r = q * kRowsPerBlock + lrow;
-            if (lpos == 0 && (int64_t)tr * kTileRows + r < p.M) o[r] = s;
+            if (lpos == 0 && (!MASKED || (int64_t)tr * kTileRows + r < p.M)) o[r] = s;
           }
           acc[j] = 0.f;
         }
@@ -325,7 +344,7 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int C, int PW, int OP>
+template <int S, int C, int PW, int OP, bool MASKED>
 __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
   __shared__ StreamLds<S, C> lds;
   const int wave = (int)(threadIdx.x >> 6);
@@ -336,9 +355,9 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
   }
   __syncthreads();
   if (wave < PW)
-    producer<S, C, PW>(p, lds, wave);
+    producer<S, C, PW, MASKED>(p, lds, wave);
   else
-    consumer<S, C, OP>(p, lds, wave - PW);
+    consumer<S, C, OP, MASKED>(p, lds, wave - PW);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,10 +386,22 @@ __global__ void __launch_bounds__(256) fill_f32(float* __restrict__ out, int64_t
 template <int S, int C, int PW>
 static hipError_t launch_scp(int op, int grid, const StreamParams& p, hipStream_t stream) {
   dim3 block(64 * (PW + C));
-  if (op == kOpCopy)
-    hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy>), dim3(grid), block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum>), dim3(grid), block, 0, stream, p);
+  const bool masked = (p.M % kTileRows) != 0 || (p.N % kTileCols) != 0;
+  if (op == kOpCopy) {
+    if (masked)
+      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, true>), dim3(grid), block, 0, stream,
+                         p);
+    else
+      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, false>), dim3(grid), block, 0, stream,
+                         p);
+  } else {
+    if (masked)
+      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, true>), dim3(grid), block, 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, false>), dim3(grid), block, 0,
+                         stream, p);
+  }
   return hipGetLastError();
 }
 
