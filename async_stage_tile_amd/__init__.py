@@ -274,6 +274,58 @@ def pipe_device_status(clear: bool = False) -> int:
     return int(out.value)
 
 
+# ---------------------------------------------------------------------------
+# Pre-marshalled launchers: validate and marshal once, then each call is a
+# single C-ABI call on the current stream (for repeated launches on the same
+# buffers, e.g. timing loops).
+# ---------------------------------------------------------------------------
+def copy_launcher(src, dst, checksums=None, stream=None, **cfg):
+    import torch
+    M, N, ld_src = _check_matrix(src, "src", (torch.float16, torch.bfloat16, torch.int16))
+    Md, Nd, ld_dst = _check_matrix(dst, "dst", (src.dtype,))
+    if (Md, Nd) != (M, N):
+        raise ValueError("dst shape differs from src")
+    c = make_config(PIPE_OP_COPY, **cfg)
+    fn, args = lib().pipe_tile_copy, (_ptr(src), _ptr(dst), M, N, ld_src, ld_dst,
+                                       ctypes.byref(c), _ptr(checksums), _stream(stream))
+
+    def launch():
+        _check(fn(*args), "pipe_tile_copy")
+    launch.keep = (c, src, dst, checksums)
+    return launch
+
+
+def rowsum_launcher(A, out, workspace=None, stream=None, **cfg):
+    import torch
+    M, N, lda = _check_matrix(A, "A", (torch.float16,))
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = make_config(PIPE_OP_ROWSUM, **cfg)
+    fn, args = lib().pipe_rowsum, (_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c),
+                                    _ptr(workspace), wbytes, _stream(stream))
+
+    def launch():
+        _check(fn(*args), "pipe_rowsum")
+    launch.keep = (c, A, out, workspace)
+    return launch
+
+
+def gemm_launcher(A, B, C, stream=None, **cfg):
+    import torch
+    M, K, lda = _check_matrix(A, "A", (torch.bfloat16,))
+    K2, N, ldb = _check_matrix(B, "B", (torch.bfloat16,))
+    Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32,))
+    if K2 != K or (Mc, Nc) != (M, N):
+        raise ValueError("shape mismatch")
+    c = make_config(PIPE_OP_GEMM, **cfg)
+    fn, args = lib().pipe_gemm_mainloop, (_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                           ctypes.byref(c), _stream(stream))
+
+    def launch():
+        _check(fn(*args), "pipe_gemm_mainloop")
+    launch.keep = (c, A, B, C)
+    return launch
+
+
 # short aliases
 tile_copy = pipe_tile_copy
 rowsum = pipe_rowsum

@@ -81,23 +81,25 @@ def recorded_traffic(kernel_name):
 
 
 def timed_launches(fn, steps, warmup):
-    """Run fn() warmup times, then `steps` times with an event pair per launch.
+    """Run fn() warmup times, then exactly `steps` times back to back.
 
-    Returns (wall ms per step, mean kernel ms from events)."""
+    One HIP event pair on the launch stream brackets the `steps` launches; the
+    host clock brackets the same region between two synchronisations.
+    Returns (wall ms per step, event ms per step)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
+    a.record()
+    for _ in range(steps):
         fn()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    kern = sum(a.elapsed_time(b) for a, b in evs) / steps
+    kern = a.elapsed_time(b) / steps
     return wall, kern
 
 
@@ -124,7 +126,7 @@ def bench_copy(stages, steps, warmup, **cfg):
     dst.zero_()
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     kw = dict(cfg, stages=stages)
-    fn = lambda: pt.pipe_tile_copy(src, dst, status=st, **kw)
+    fn = pt.copy_launcher(src, dst, status=st, **kw)
     wall, kern = timed_launches(fn, steps, warmup)
     ok = int(st.item()) == 0 and torch.equal(dst.view(torch.int16), src.view(torch.int16))
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, COPY_M, COPY_N, **kw)
@@ -147,7 +149,7 @@ def bench_rowsum(steps, warmup, stages=3):
     out = torch.empty(ROWSUM_M, dtype=torch.float32, device="cuda")
     ws = torch.empty(max(1, pt.pipe_rowsum_workspace_bytes(ROWSUM_M, ROWSUM_N, stages=stages)),
                      dtype=torch.uint8, device="cuda")
-    fn = lambda: pt.pipe_rowsum(A, out, ws, stages=stages)
+    fn = pt.rowsum_launcher(A, out, ws, stages=stages)
     wall, kern = timed_launches(fn, steps, warmup)
     nbytes = ROWSUM_M * ROWSUM_N * 2 + ROWSUM_M * 4
     q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, ROWSUM_M, ROWSUM_N, stages=stages)
@@ -166,7 +168,7 @@ def bench_gemm(steps, warmup, stages=3):
     A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device="cuda")
     B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device="cuda")
     C = torch.empty((n, n), dtype=torch.float32, device="cuda")
-    fn = lambda: pt.pipe_gemm_mainloop(A, B, C, stages=stages)
+    fn = pt.gemm_launcher(A, B, C, stages=stages)
     wall, kern = timed_launches(fn, steps, warmup)
     flops = 2.0 * n * n * n
     return {"stages": stages, "wall_ms": wall, "kernel_ms": kern, "flops": flops,
@@ -197,10 +199,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--stages", type=int, default=2,
-                    help="copy ring depth for the headline (2 = the library default, the "
-                         "best of the S sweeps measured on MI355X); 0 = best of this run's "
-                         "1..4 sweep")
+    ap.add_argument("--stages", type=int, default=None,
+                    help="ring depth (default: the library default of the workload, 2 for "
+                         "the copy -- the best of the S sweeps measured on MI355X); 0 = the "
+                         "best of this run's 1..4 copy sweep")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--only", choices=["copy", "rowsum", "gemm", "calib"], default=None,
                     help="time one workload only (for profiling); prints no JSON line")
@@ -240,7 +242,7 @@ def main():
         return
 
     extras = {}
-    stages = args.stages
+    stages = 2 if args.stages is None else args.stages
     if not args.no_extras or stages == 0:
         sweep = []
         for s in (1, 2, 3, 4):
@@ -271,7 +273,7 @@ def main():
 
     achieved = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
     kname = (f"void pipe::stream_kernel<{head['stages']}, {head['consumer_waves']}, "
-             f"{head['producer_waves']}, 0>(pipe::StreamParams)")
+             f"{head['producer_waves']}, 0, false>(pipe::StreamParams)")
     traffic = recorded_traffic(kname)
     line = {
         "metric": METRIC,

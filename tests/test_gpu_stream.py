@@ -273,3 +273,18 @@ def test_rowsum_degenerate_shapes():
     o = pt.pipe_rowsum(ones, split=5)
     torch.cuda.synchronize()
     assert torch.equal(o, torch.full((128,), 65536.0, device=DEV))
+
+
+def test_premarshalled_launchers_match():
+    src = synth.unique_codes(512, 512).to(DEV)
+    dst = torch.zeros_like(src)
+    launch = pt.copy_launcher(src, dst, stages=3)
+    launch()
+    launch()
+    A = synth.small_int((512, 1024), -8, 8, torch.float16, seed=2).to(DEV)
+    out = torch.empty(512, device=DEV)
+    ws = torch.empty(pt.pipe_rowsum_workspace_bytes(512, 1024) + 4, dtype=torch.uint8, device=DEV)
+    pt.rowsum_launcher(A, out, ws)()
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
