@@ -45,6 +45,7 @@ PIPE_FLAG_ROW_STRIPS = 0x2
 PIPE_FLAG_NONTEMPORAL = 0x4
 PIPE_FLAG_GEMM_B_LINEAR = 0x8
 PIPE_FLAG_XCD_REMAP = 0x10
+PIPE_FLAG_SPLIT_INTERLEAVE = 0x20
 PIPE_FLAG_TEST_START_PHASE0 = 0x100
 PIPE_FLAG_TEST_NO_RELEASE = 0x200
 

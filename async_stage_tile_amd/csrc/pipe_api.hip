@@ -19,6 +19,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kLdsLimit = 163840;
 constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_NONTEMPORAL |
                                  PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_XCD_REMAP |
+                                 PIPE_FLAG_SPLIT_INTERLEAVE |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -154,6 +155,7 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   const int max_lag = c.producer_waves == 2 ? 3 : 2;
   p->lag = c.stages - 1 < max_lag ? c.stages - 1 : max_lag;
   p->xcd_remap = ((c.flags & PIPE_FLAG_XCD_REMAP) && g.items % 8 == 0) ? 1 : 0;
+  p->interleave = (c.flags & PIPE_FLAG_SPLIT_INTERLEAVE) ? 1 : 0;
   p->spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
   p->start_phase = (c.flags & PIPE_FLAG_TEST_START_PHASE0) ? 0u : 1u;
   p->no_release = (c.flags & PIPE_FLAG_TEST_NO_RELEASE) ? 1 : 0;

@@ -18,8 +18,9 @@
 // min(S - 1, 48 / (32 / PW) - 1) stages of lag, so that the stages in flight
 // never exceed 48 outstanding loads per wave.
 //
-// Consumers interleave the LDS fragment reads of each 16-deep K sub-step with
-// the MFMAs of the previous one, and release the slot after the last read.
+// Consumers read fragments one 16-deep K sub-step ahead of the MFMAs (two
+// register buffers), release a slot as soon as their reads of it have
+// returned, and wait for the next stage while the last MFMAs still run.
 //
 // LDS layout of a stage: A rows of 128 B with 16-byte chunk c of row r at
 // position c ^ ((r >> shift) & 7) (the MFMA A fragment reads one chunk of 32
@@ -180,6 +181,39 @@ __device__ __forceinline__ bf16x8 load_b_frag(const uint8_t* bslot, int k16, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Fragments of one 16-deep K sub-step for one consumer wave: A (2 x 32 rows)
+// and B (2 x 32 columns).
+struct SubFrags {
+  bf16x8 a[2];
+  bf16x8 b[2];
+};
+
+__device__ __forceinline__ void load_sub(SubFrags& f, int kk, const uint8_t* sa,
+                                         const uint8_t* sb, int wm, int wn, int li, int lk,
+                                         int lane, const GemmParams& p) {
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int r = wm * 64 + mi * 32 + li;
+    const int c = swz(r, kk * 2 + lk, p.swz_shift);
+    f.a[mi] = *reinterpret_cast<const bf16x8*>(sa + r * 128 + c * 16);
+  }
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) f.b[ni] = load_b_frag(sb, kk * 16, wn * 64 + ni * 32, lane, p.b_swz);
+}
+
+__device__ __forceinline__ void mfma_sub(f32x16 (&acc)[2][2], const SubFrags& f) {
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// Consumer wave. Fragment reads run one K sub-step ahead of the MFMAs through
+// two register buffers. At the last sub-step of a stage the wave waits for its
+// reads of the slot to return, releases the slot, then waits on full for the
+// next stage (while the previous MFMAs still execute) and reads that stage's
+// first sub-step before issuing the last MFMAs of the current one.
 template <int S>
 __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
   const int lane = lane_id();
@@ -197,36 +231,35 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    SubFrags b0, b1;
+    if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+      ok = false;
+      break;
+    }
+    const uint8_t* sa = &lds.a[rd.index][0];
+    const uint8_t* sb = &lds.b[rd.index][0];
+    load_sub(b0, 0, sa, sb, wm, wn, li, lk, lane, p);
     for (int ks = 0; ks < p.k_steps; ++ks) {
-      if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
-        ok = false;
-        break;
-      }
-      const uint8_t* sa = &lds.a[rd.index][0];
-      const uint8_t* sb = &lds.b[rd.index][0];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 af[2], bfr[2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const int r = wm * 64 + mi * 32 + li;
-          const int c = swz(r, kk * 2 + lk, p.swz_shift);
-          af[mi] = *reinterpret_cast<const bf16x8*>(sa + r * 128 + c * 16);
-        }
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          bfr[ni] = load_b_frag(sb, kk * 16, wn * 64 + ni * 32, lane, p.b_swz);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-      }
-      // consumer_release once this wave's LDS reads of the slot have returned.
+      load_sub(b1, 1, sa, sb, wm, wn, li, lk, lane, p);
+      mfma_sub(acc, b0);
+      load_sub(b0, 2, sa, sb, wm, wn, li, lk, lane, p);
+      mfma_sub(acc, b1);
+      load_sub(b1, 3, sa, sb, wm, wn, li, lk, lane, p);
+      mfma_sub(acc, b0);
+      // consumer_release: this wave's reads of the slot have all returned.
       wait_lgkmcnt0();
       bar_arrive(&lds.empty[rd.index], 4u);
       rd.inc();
+      if (ks + 1 < p.k_steps) {
+        if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+          ok = false;
+          break;
+        }
+        sa = &lds.a[rd.index][0];
+        sb = &lds.b[rd.index][0];
+        load_sub(b0, 0, sa, sb, wm, wn, li, lk, lane, p);
+      }
+      mfma_sub(acc, b1);
     }
     if (!ok) break;
     // Epilogue: fp32 accumulators -> C.

@@ -35,6 +35,7 @@ struct StreamParams {
   int32_t trace_cap;      // trace records
   int32_t nt;             // non-temporal hints on the streamed loads and stores
   int32_t xcd_remap;      // permute items so each XCD streams neighbouring strips
+  int32_t interleave;     // segment s takes tiles s, s + split, s + 2 split, ...
 };
 
 // Launch the stream kernel for (op, stages, consumers, producers). Returns

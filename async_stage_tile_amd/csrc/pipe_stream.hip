@@ -13,7 +13,10 @@
 // tile column walked downwards (copy default) or one tile row walked along the
 // columns (rowsum, or copy with PIPE_FLAG_ROW_STRIPS). Each strip is cut into
 // `split` segments; item i is segment i / n_strips of strip i % n_strips, so
-// workgroups launched together touch neighbouring strips. A workgroup walks
+// workgroups launched together touch neighbouring strips. A segment is either
+// a contiguous run of the strip's tiles, or (interleaved) every split-th tile
+// starting at the segment index, so that the workgroups sharing a strip read
+// neighbouring tiles at the same time. A workgroup walks
 // items blockIdx.x, blockIdx.x + gridDim.x, ... and its cursors run on across
 // items (a persistent ring). With `xcd_remap`, the item a workgroup takes is
 // permuted so that the workgroups of one XCD (dispatch is round-robin over
@@ -78,7 +81,7 @@ __device__ __forceinline__ void tile_coords(const StreamParams& p, int item, int
                                             int& tile_row, int& tile_col) {
   int strip = item % p.n_strips;
   int seg = item / p.n_strips;
-  int pos = seg * p.seg_len + k;
+  int pos = p.interleave ? seg + k * p.split : seg * p.seg_len + k;
   if (p.row_strips) {
     tile_row = strip;
     tile_col = pos;
@@ -90,6 +93,7 @@ __device__ __forceinline__ void tile_coords(const StreamParams& p, int item, int
 
 __device__ __forceinline__ int item_len(const StreamParams& p, int item) {
   int seg = item / p.n_strips;
+  if (p.interleave) return (p.strip_len - seg + p.split - 1) / p.split;
   int start = seg * p.seg_len;
   int len = p.strip_len - start;
   return len < p.seg_len ? len : p.seg_len;

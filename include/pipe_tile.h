@@ -64,6 +64,8 @@ typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_
 #define PIPE_FLAG_GEMM_B_LINEAR 0x8u   /* gemm: store B K-rows in LDS without the XOR swizzle */
 #define PIPE_FLAG_XCD_REMAP 0x10u      /* copy/rowsum: give each XCD neighbouring strips (when the
                                           item count is a multiple of 8) */
+#define PIPE_FLAG_SPLIT_INTERLEAVE 0x20u /* copy/rowsum: segment s of a strip takes every split-th
+                                            tile from s on, instead of a contiguous run */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the

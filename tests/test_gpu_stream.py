@@ -106,6 +106,19 @@ def test_copy_two_producer_waves(S, C, remap):
     assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
 
 
+@pytest.mark.parametrize("split", [2, 3, 5])
+@pytest.mark.parametrize("row_strips", [False, True])
+def test_copy_interleaved_segments(split, row_strips):
+    src = synth.unique_codes(1280, 640).to(DEV)   # 10 x 10 tiles
+    flags = pt.PIPE_FLAG_SPLIT_INTERLEAVE | (pt.PIPE_FLAG_ROW_STRIPS if row_strips else 0)
+    st = _status()
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, split=split, grid=7, flags=flags, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
+
+
 @pytest.mark.parametrize("shift", [0, 1, 2, 3])
 @pytest.mark.parametrize("row_strips", [False, True])
 def test_copy_swizzle_and_walk_order(shift, row_strips):
@@ -214,6 +227,15 @@ def test_rowsum_two_producer_waves_bit_exact(S, remap):
     A = synth.small_int((1024, 4096), -8, 8, torch.float16, seed=6).to(DEV)
     flags = pt.PIPE_FLAG_XCD_REMAP | pt.PIPE_FLAG_NONTEMPORAL if remap else 0
     out = pt.pipe_rowsum(A, stages=S, consumer_waves=8, producer_waves=2, split=4, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+@pytest.mark.parametrize("split", [2, 4, 7])
+@pytest.mark.parametrize("shape", [(1024, 4096), (300, 1000)])
+def test_rowsum_interleaved_segments_bit_exact(split, shape):
+    A = synth.small_int(shape, -8, 8, torch.float16, seed=8).to(DEV)
+    out = pt.pipe_rowsum(A, split=split, flags=pt.PIPE_FLAG_SPLIT_INTERLEAVE, grid=9)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
 
