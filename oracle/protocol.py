@@ -207,26 +207,26 @@ class ProtocolResult:
     max_ahead: int
 
 
-def _producer_program(S, T, mode, lag, start_phase, tail):
+def _producer_program(S, T, mode, lag, start_phase, tail, part=0):
     ops = []
     cur = PipelineState(S, 0, start_phase, 0)
     if mode == "tx":
         for t in range(T):
             ops.append(("wait_empty", cur.index, cur.phase))
             ops.append(("arrive_tx", cur.index))
-            ops.append(("issue", t, cur.index))
+            ops.append(("issue", t, cur.index, part))
             cur.inc()
     elif mode == "landed":
         for t in range(T):
             ops.append(("wait_empty", cur.index, cur.phase))
-            ops.append(("issue", t, cur.index))
+            ops.append(("issue", t, cur.index, part))
             u = t - lag
             if u >= 0:
-                ops.append(("wait_landed", u))
+                ops.append(("wait_landed", u, part))
                 ops.append(("arrive_full", u % S))
             cur.inc()
         for u in range(max(0, T - lag), T):
-            ops.append(("wait_landed", u))
+            ops.append(("wait_landed", u, part))
             ops.append(("arrive_full", u % S))
     else:
         raise ValueError(mode)
@@ -253,29 +253,37 @@ def _consumer_program(S, T, release_before_read):
 
 
 def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
-                   producer_start_phase: int = 1, full_expected: int = 1,
+                   producers: int = 1, producer_start_phase: int = 1, full_expected=None,
                    empty_expected=None, release_before_read: bool = False,
                    tail: bool = True, tile_bytes: int = 16384,
                    max_states: int = 2_000_000) -> ProtocolResult:
-    """Explore every interleaving of one producer, C consumers and the copy engine.
+    """Explore every interleaving of the producers, C consumers and the copy engine.
 
     ``mode="tx"``: the producer arrives with expect_tx before issuing the copy
     and the copy's landing performs complete_tx (the mbarrier design).
-    ``mode="landed"``: the producer issues the copy, and ``lag`` tiles later
-    waits until it has landed and then arrives on full (a counter barrier with
-    no transaction bytes).
+    ``mode="landed"``: each of ``producers`` producer agents issues its share of
+    every tile, and ``lag`` tiles later waits until that share has landed and
+    then arrives on full (a counter barrier with no transaction bytes, which
+    expects one arrival per producer by default).
 
-    Checked: (I1) a consumer reads a slot only after that tile landed;
-    (I2) a slot is not overwritten before all consumers of its previous tile
-    are done with it; (I3) no reachable deadlock and all tiles consumed;
-    (I4) the producer is at most S tiles ahead of the slowest consumer.
+    Checked: (I1) a consumer reads a slot only after every share of that tile
+    landed; (I2) a slot is not overwritten before all consumers of its previous
+    tile are done with it; (I3) no reachable deadlock and all tiles consumed;
+    (I4) the producers are at most S tiles ahead of the slowest consumer.
     """
+    P = producers
+    if mode == "tx" and P != 1:
+        raise ValueError("the transaction-count model has a single producer")
+    if full_expected is None:
+        full_expected = P
     if empty_expected is None:
         empty_expected = C
-    P = _producer_program(S, T, mode, lag, producer_start_phase, tail)
+    progs = [_producer_program(S, T, mode, lag, producer_start_phase, tail, part=i)
+             for i in range(P)]
     Q = _consumer_program(S, T, release_before_read)
-    nP, nQ = len(P), len(Q)
+    nQ = len(Q)
     nbar = 2 * S
+    all_parts = frozenset(range(P))
 
     def bar_exp(b):
         return full_expected if b < S else empty_expected
@@ -285,8 +293,9 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
         if pend == 0 and tx == 0:
             bars[b] = (bar_exp(b), ph ^ 1, 0)
 
+    # slot: None or (tile, landed parts); inflight: frozenset of (tile, part)
     init_bars = tuple((bar_exp(b), 0, 0) for b in range(nbar))
-    init = (0, (0,) * C, init_bars, (None,) * S, frozenset())
+    init = ((0,) * P, (0,) * C, init_bars, (None,) * S, frozenset())
     seen = {init}
     stack = [init]
     violations = set()
@@ -295,7 +304,6 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
     max_ahead = 0
 
     def released_tiles(qpc):
-        # tiles whose arrive_empty has executed: 3 ops per tile
         done = qpc // 3
         if qpc % 3 == 2 and release_before_read:
             done += 1
@@ -305,59 +313,63 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
         if len(seen) > max_states:
             raise RuntimeError("state bound exceeded")
         st = stack.pop()
-        ppc, qpcs, bars, slots, inflight = st
+        ppcs, qpcs, bars, slots, inflight = st
         succ = []
-        # producer
-        if ppc < nP:
-            op = P[ppc]
+        for i in range(P):
+            ppc = ppcs[i]
+            prog = progs[i]
+            if ppc >= len(prog):
+                continue
+            op = prog[ppc]
             kind = op[0]
+            npp = ppcs[:i] + (ppc + 1,) + ppcs[i + 1:]
             if kind == "wait_empty":
-                _, s, ph = op
-                if bars[S + s][1] != ph:
-                    succ.append((ppc + 1, qpcs, bars, slots, inflight))
+                _, s_, ph = op
+                if bars[S + s_][1] != ph:
+                    succ.append((npp, qpcs, bars, slots, inflight))
             elif kind == "arrive_tx":
-                s = op[1]
+                s_ = op[1]
                 b = list(bars)
-                pend, ph, tx = b[s]
-                b[s] = (pend - 1, ph, tx + tile_bytes)
-                settle(b, s)
-                succ.append((ppc + 1, qpcs, tuple(b), slots, inflight))
+                pend, ph, tx = b[s_]
+                b[s_] = (pend - 1, ph, tx + tile_bytes)
+                settle(b, s_)
+                succ.append((npp, qpcs, tuple(b), slots, inflight))
             elif kind == "issue":
-                _, t, s = op
+                _, t, s_, part = op
                 slowest = min(released_tiles(q) for q in qpcs)
                 ahead = (t + 1) - slowest
                 max_ahead = max(max_ahead, ahead)
                 if ahead > S:
                     violations.add(("I4", t, ahead))
                 sl = list(slots)
-                sl[s] = (t, False)
-                succ.append((ppc + 1, qpcs, bars, tuple(sl), inflight | {t}))
+                if sl[s_] is None or sl[s_][0] != t:
+                    sl[s_] = (t, frozenset())          # older contents destroyed
+                succ.append((npp, qpcs, bars, tuple(sl), inflight | {(t, part)}))
             elif kind == "wait_landed":
-                u = op[1]
-                if u not in inflight:
-                    succ.append((ppc + 1, qpcs, bars, slots, inflight))
+                _, u, part = op
+                if (u, part) not in inflight:
+                    succ.append((npp, qpcs, bars, slots, inflight))
             elif kind == "arrive_full":
-                s = op[1]
+                s_ = op[1]
                 b = list(bars)
-                pend, ph, tx = b[s]
-                b[s] = (pend - 1, ph, tx)
-                settle(b, s)
-                succ.append((ppc + 1, qpcs, tuple(b), slots, inflight))
-        # copy engine: any in-flight tile may land
-        for t in inflight:
-            s = t % S
+                pend, ph, tx = b[s_]
+                b[s_] = (pend - 1, ph, tx)
+                settle(b, s_)
+                succ.append((npp, qpcs, tuple(b), slots, inflight))
+        # copy engine: any in-flight share may land
+        for (t, part) in inflight:
+            s_ = t % S
             sl = list(slots)
-            if sl[s] == (t, False):
-                sl[s] = (t, True)
+            if sl[s_] is not None and sl[s_][0] == t:
+                sl[s_] = (t, sl[s_][1] | {part})
             b = bars
             if mode == "tx":
                 b = list(bars)
-                pend, ph, tx = b[s]
-                b[s] = (pend, ph, tx - tile_bytes)
-                settle(b, s)
+                pend, ph, tx = b[s_]
+                b[s_] = (pend, ph, tx - tile_bytes)
+                settle(b, s_)
                 b = tuple(b)
-            succ.append((ppc, qpcs, b, tuple(sl), inflight - {t}))
-        # consumers
+            succ.append((ppcs, qpcs, b, tuple(sl), inflight - {(t, part)}))
         for c in range(C):
             qpc = qpcs[c]
             if qpc >= nQ:
@@ -366,24 +378,25 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
             kind = op[0]
             nq = qpcs[:c] + (qpc + 1,) + qpcs[c + 1:]
             if kind == "wait_full":
-                _, s, ph = op
-                if bars[s][1] != ph:
-                    succ.append((ppc, nq, bars, slots, inflight))
+                _, s_, ph = op
+                if bars[s_][1] != ph:
+                    succ.append((ppcs, nq, bars, slots, inflight))
             elif kind == "read":
-                _, t, s = op
-                if slots[s] != (t, True):
-                    tag = "I1" if slots[s] == (t, False) else "I2"
-                    violations.add((tag, t, c, slots[s]))
-                succ.append((ppc, nq, bars, slots, inflight))
+                _, t, s_ = op
+                if slots[s_] != (t, all_parts):
+                    tag = "I1" if slots[s_] is not None and slots[s_][0] == t else "I2"
+                    violations.add((tag, t, c, slots[s_]))
+                succ.append((ppcs, nq, bars, slots, inflight))
             elif kind == "arrive_empty":
-                s = op[1]
+                s_ = op[1]
                 b = list(bars)
-                pend, ph, tx = b[S + s]
-                b[S + s] = (pend - 1, ph, tx)
-                settle(b, S + s)
-                succ.append((ppc, nq, tuple(b), slots, inflight))
+                pend, ph, tx = b[S + s_]
+                b[S + s_] = (pend - 1, ph, tx)
+                settle(b, S + s_)
+                succ.append((ppcs, nq, tuple(b), slots, inflight))
         if not succ:
-            if ppc == nP and all(q == nQ for q in qpcs) and not inflight:
+            if (all(pc == len(progs[i]) for i, pc in enumerate(ppcs))
+                    and all(q == nQ for q in qpcs) and not inflight):
                 completed = True
             else:
                 deadlock = True

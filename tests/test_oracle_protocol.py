@@ -125,3 +125,27 @@ def test_commit_lag_rule(S):
 def test_no_tail_still_consumes_everything():
     r = P.check_protocol(2, 3, 2, tail=False)
     assert r.completed
+
+
+@pytest.mark.parametrize("S,T,C", [(1, 3, 2), (2, 4, 2), (3, 4, 2), (3, 5, 1), (4, 5, 1)])
+def test_two_producer_waves_safe_and_live(S, T, C):
+    """Each producer wave moves its share of every tile and arrives on full,
+    which expects one arrival per producer wave."""
+    r = P.check_protocol(S, T, C, mode="landed", lag=S - 1, producers=2)
+    assert r.completed and not r.deadlock and r.violations == []
+    assert r.max_ahead == min(S, T)
+
+
+def test_full_expecting_fewer_arrivals_than_producers_reads_half_landed_tiles():
+    r = P.check_protocol(2, 3, 1, mode="landed", lag=1, producers=2, full_expected=1)
+    assert any(v[0] == "I1" for v in r.violations)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3])
+def test_two_producer_commit_lag_rule(S):
+    for L in range(0, S + 1):
+        r = P.check_protocol(S, S + 1, 1, mode="landed", lag=L, producers=2)
+        if L <= S - 1:
+            assert r.completed and r.violations == [], (S, L)
+        else:
+            assert r.deadlock, (S, L)
