@@ -46,6 +46,7 @@ PIPE_FLAG_NONTEMPORAL = 0x4
 PIPE_FLAG_GEMM_B_LINEAR = 0x8
 PIPE_FLAG_XCD_REMAP = 0x10
 PIPE_FLAG_SPLIT_INTERLEAVE = 0x20
+PIPE_FLAG_UNIFIED = 0x40
 PIPE_FLAG_TEST_START_PHASE0 = 0x100
 PIPE_FLAG_TEST_NO_RELEASE = 0x200
 

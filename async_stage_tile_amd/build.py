@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpipetile.so")
-SOURCES = ["pipe_api.hip", "pipe_stream.hip", "pipe_gemm.hip"]
+SOURCES = ["pipe_api.hip", "pipe_stream.hip", "pipe_unified.hip", "pipe_gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -19,7 +19,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kLdsLimit = 163840;
 constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_NONTEMPORAL |
                                  PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_XCD_REMAP |
-                                 PIPE_FLAG_SPLIT_INTERLEAVE |
+                                 PIPE_FLAG_SPLIT_INTERLEAVE | PIPE_FLAG_UNIFIED |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -103,6 +103,17 @@ pipe_status_t check_stream_cfg(const pipe_config_t& c) {
   const int cw = c.consumer_waves;
   if (!(cw == 1 || cw == 2 || cw == 3 || cw == 4 || cw == 8)) return PIPE_ERR_CONFIG;
   if (stream_lds_bytes(c.stages, cw) > kLdsLimit) return PIPE_ERR_STAGES;
+  return PIPE_OK;
+}
+
+// The unified variant's extra constraints (see PIPE_FLAG_UNIFIED).
+pipe_status_t check_unified(const pipe_config_t& c, int64_t M, int64_t N, bool checksums) {
+  const int w = c.consumer_waves;
+  if (!(w == 2 || w == 4 || w == 8)) return PIPE_ERR_CONFIG;
+  if (checksums || (c.flags & (PIPE_FLAG_TRACE | PIPE_FLAG_TEST_START_PHASE0 |
+                               PIPE_FLAG_TEST_NO_RELEASE)))
+    return PIPE_ERR_CONFIG;
+  if (M % 128 != 0 || N % 64 != 0) return PIPE_ERR_CONFIG;
   return PIPE_OK;
 }
 
@@ -215,6 +226,11 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   if (!aligned16(src) || !aligned16(dst) || (ld_src % 8) || (ld_dst % 8)) return PIPE_ERR_ALIGN;
   if (tile_checksums != nullptr && !aligned4(tile_checksums)) return PIPE_ERR_ALIGN;
   const bool row_strips = (c.flags & PIPE_FLAG_ROW_STRIPS) != 0;
+  const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
+  if (unified) {
+    s = check_unified(c, M, N, tile_checksums != nullptr);
+    if (s != PIPE_OK) return s;
+  }
   StreamGeom g;
   s = stream_geometry(M, N, c, row_strips, false, &g);
   if (s != PIPE_OK) return s;
@@ -231,6 +247,9 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
+  if (unified)
+    return hip_status(launch_unified(kOpCopy, c.stages, c.consumer_waves, g.grid, p,
+                                     static_cast<hipStream_t>(stream)));
   return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, c.producer_waves, g.grid, p,
                                   static_cast<hipStream_t>(stream)));
 }
@@ -267,6 +286,11 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   if (N == 0) return hip_status(launch_fill_f32(out, M, 1, 1, 0.f, st));
   if (A == nullptr) return PIPE_ERR_NULL;
   if (!aligned16(A) || (lda % 8)) return PIPE_ERR_ALIGN;
+  const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
+  if (unified) {
+    s = check_unified(c, M, N, false);
+    if (s != PIPE_OK) return s;
+  }
   StreamGeom g;
   s = stream_geometry(M, N, c, true, true, &g);
   if (s != PIPE_OK) return s;
@@ -287,7 +311,9 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  s = hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, c.producer_waves, g.grid, p, st));
+  s = unified ? hip_status(launch_unified(kOpRowsum, c.stages, c.consumer_waves, g.grid, p, st))
+              : hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, c.producer_waves,
+                                         g.grid, p, st));
   if (s != PIPE_OK || need == 0) return s;
   return hip_status(launch_rowsum_finalize(static_cast<const float*>(workspace), out, M,
                                            g.split, st));
@@ -370,8 +396,9 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   if (M < 0 || N < 0 || N % 8) return PIPE_ERR_SHAPE;
   const bool rowsum = op == PIPE_OP_ROWSUM;
   const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);
-  info->lds_bytes = stream_lds_bytes(c.stages, c.consumer_waves);
-  info->threads = 64 * (c.producer_waves + c.consumer_waves);
+  const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
+  info->lds_bytes = unified ? c.stages * 16384 : stream_lds_bytes(c.stages, c.consumer_waves);
+  info->threads = 64 * (unified ? c.consumer_waves : c.producer_waves + c.consumer_waves);
   if (M == 0 || N == 0) return PIPE_OK;
   StreamGeom g;
   s = stream_geometry(M, N, c, row_strips, rowsum, &g);

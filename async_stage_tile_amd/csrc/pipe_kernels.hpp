@@ -45,6 +45,11 @@ hipError_t launch_stream(int op, int stages, int consumers, int producers, int g
                          const StreamParams& p, hipStream_t stream);
 int stream_lds_bytes(int stages, int consumers);
 
+// Unified variant: `waves` waves (2, 4 or 8) each load and consume 16 / waves
+// blocks of every tile; divisible shapes only, no checksums or trace.
+hipError_t launch_unified(int op, int stages, int waves, int grid, const StreamParams& p,
+                          hipStream_t stream);
+
 hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
                                   hipStream_t stream);
 hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, float value,

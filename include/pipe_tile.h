@@ -66,6 +66,11 @@ typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_
                                           item count is a multiple of 8) */
 #define PIPE_FLAG_SPLIT_INTERLEAVE 0x20u /* copy/rowsum: segment s of a strip takes every split-th
                                             tile from s on, instead of a contiguous run */
+#define PIPE_FLAG_UNIFIED 0x40u        /* copy/rowsum: the unified (non-specialised) pipeline --
+                                          consumer_waves waves (2, 4 or 8) each load and use their
+                                          share of every tile, with per-wave batch waits and no
+                                          full/empty barriers; M % 128 == N % 64 == 0 only, no
+                                          checksums or trace (else PIPE_ERR_CONFIG) */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the

@@ -81,6 +81,18 @@ def test_copy_validation():
     assert _copy(None, None, 256, 0, 0, 0) == pt.PIPE_OK
 
 
+def test_unified_variant_constraints():
+    U = pt.PIPE_FLAG_UNIFIED
+    assert _copy(FAKE, FAKE, 200, 128, 128, 128, pt.make_config(0, flags=U, consumer_waves=4)) \
+        == pt.PIPE_ERR_CONFIG                                           # ragged M
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=U, consumer_waves=3)) \
+        == pt.PIPE_ERR_CONFIG                                           # 3 waves do not divide 16
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=U, consumer_waves=4),
+                 chk=FAKE) == pt.PIPE_ERR_CONFIG                       # no checksums
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, flags=U, consumer_waves=8, stages=3)
+    assert q["threads"] == 512 and q["lds_bytes"] == 3 * 16384
+
+
 def test_rowsum_and_gemm_validation():
     L = pt.lib()
     c = pt.make_config(pt.PIPE_OP_ROWSUM, split=4)

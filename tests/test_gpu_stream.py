@@ -310,3 +310,49 @@ def test_premarshalled_launchers_match():
     torch.cuda.synchronize()
     assert np.array_equal(_bits(dst), _bits(src))
     assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+def test_copy_offsets_beyond_4gib():
+    """fp16 (32768 + 72) x 65536 (4.3 GB per matrix): byte offsets pass 2**32, a
+    ragged last tile row included."""
+    M, N = 32768 + 72, 65536
+    src = synth.uniform((M, N), torch.float16, seed=7, device=DEV)
+    dst = torch.empty_like(src)
+    st = _status()
+    pt.pipe_tile_copy(src, dst, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
+    rows = torch.tensor([0, 32767, 32768, M - 1], device=DEV)
+    assert np.array_equal(_bits(dst[rows]), R.tile_copy(src[rows].cpu().numpy()).view(np.uint16))
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- unified variant
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_unified_copy_bit_exact(S, W):
+    src = synth.unique_codes(1024, 640).to(DEV)
+    dst = pt.pipe_tile_copy(src, stages=S, consumer_waves=W, split=3, grid=7,
+                            flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst), _bits(src))
+
+
+@pytest.mark.parametrize("S", [1, 3, 4])
+@pytest.mark.parametrize("W", [2, 8])
+@pytest.mark.parametrize("interleave", [False, True])
+def test_unified_rowsum_bit_exact(S, W, interleave):
+    A = synth.small_int((512, 4096), -8, 8, torch.float16, seed=12).to(DEV)
+    flags = pt.PIPE_FLAG_UNIFIED | (pt.PIPE_FLAG_SPLIT_INTERLEAVE if interleave else 0)
+    out = pt.pipe_rowsum(A, stages=S, consumer_waves=W, split=4, grid=5, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+def test_unified_copy_full_size_bit_exact():
+    src = synth.uniform((16384, 16384), torch.float16, seed=42, device=DEV)
+    dst = pt.pipe_tile_copy(src, stages=3, consumer_waves=4, flags=pt.PIPE_FLAG_UNIFIED)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
