@@ -208,6 +208,13 @@ class ProtocolResult:
 
 
 def _producer_program(S, T, mode, lag, start_phase, tail, part=0):
+    """The producer's instruction list.
+
+    "tx" mode is fully static. In "landed" mode the commits are dynamic: after
+    issuing a tile the producer commits its oldest uncommitted tile while more
+    than ``lag`` are uncommitted ("commit_lag"), and at the end it commits all
+    of them ("commit_all"); each commit waits until that tile's share landed.
+    """
     ops = []
     cur = PipelineState(S, 0, start_phase, 0)
     if mode == "tx":
@@ -220,14 +227,9 @@ def _producer_program(S, T, mode, lag, start_phase, tail, part=0):
         for t in range(T):
             ops.append(("wait_empty", cur.index, cur.phase))
             ops.append(("issue", t, cur.index, part))
-            u = t - lag
-            if u >= 0:
-                ops.append(("wait_landed", u, part))
-                ops.append(("arrive_full", u % S))
+            ops.append(("commit_lag",))
             cur.inc()
-        for u in range(max(0, T - lag), T):
-            ops.append(("wait_landed", u, part))
-            ops.append(("arrive_full", u % S))
+        ops.append(("commit_all",))
     else:
         raise ValueError(mode)
     if tail:
@@ -255,7 +257,7 @@ def _consumer_program(S, T, release_before_read):
 def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
                    producers: int = 1, producer_start_phase: int = 1, full_expected=None,
                    empty_expected=None, release_before_read: bool = False,
-                   tail: bool = True, tile_bytes: int = 16384,
+                   tail: bool = True, eager_min: int = 0, tile_bytes: int = 16384,
                    max_states: int = 2_000_000) -> ProtocolResult:
     """Explore every interleaving of the producers, C consumers and the copy engine.
 
@@ -264,7 +266,10 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
     ``mode="landed"``: each of ``producers`` producer agents issues its share of
     every tile, and ``lag`` tiles later waits until that share has landed and
     then arrives on full (a counter barrier with no transaction bytes, which
-    expects one arrival per producer by default).
+    expects one arrival per producer by default). With ``eager_min`` > 0 a
+    producer whose acquire finds the slot still in use, while it has at least
+    ``eager_min`` uncommitted tiles, commits its oldest uncommitted tile first
+    (waiting for that tile to land), then polls again.
 
     Checked: (I1) a consumer reads a slot only after every share of that tile
     landed; (I2) a slot is not overwritten before all consumers of its previous
@@ -278,6 +283,8 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
         full_expected = P
     if empty_expected is None:
         empty_expected = C
+    if eager_min and mode != "landed":
+        raise ValueError("eager commits exist in the landed mode only")
     progs = [_producer_program(S, T, mode, lag, producer_start_phase, tail, part=i)
              for i in range(P)]
     Q = _consumer_program(S, T, release_before_read)
@@ -295,7 +302,8 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
 
     # slot: None or (tile, landed parts); inflight: frozenset of (tile, part)
     init_bars = tuple((bar_exp(b), 0, 0) for b in range(nbar))
-    init = ((0,) * P, (0,) * C, init_bars, (None,) * S, frozenset())
+    # producer i: (pc, tiles committed, 1 while blocked in an eager commit)
+    init = (((0, 0, 0),) * P, (0,) * C, init_bars, (None,) * S, frozenset())
     seen = {init}
     stack = [init]
     violations = set()
@@ -316,17 +324,38 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
         ppcs, qpcs, bars, slots, inflight = st
         succ = []
         for i in range(P):
-            ppc = ppcs[i]
+            ppc, done, flushing = ppcs[i]
             prog = progs[i]
             if ppc >= len(prog):
                 continue
             op = prog[ppc]
             kind = op[0]
-            npp = ppcs[:i] + (ppc + 1,) + ppcs[i + 1:]
+
+            def at(pc, committed=done, fl=0, i=i):
+                return ppcs[:i] + ((pc, committed, fl),) + ppcs[i + 1:]
+
+            def commit_oldest(next_pc, fl=0, i=i, done=done):
+                # wait until the oldest uncommitted tile's share landed, then arrive
+                if (done, i) in inflight:
+                    return None
+                b = list(bars)
+                pend, ph, tx = b[done % S]
+                b[done % S] = (pend - 1, ph, tx)
+                settle(b, done % S)
+                return (at(next_pc, done + 1, fl), qpcs, tuple(b), slots, inflight)
+
+            issued = sum(1 for o in prog[:ppc] if o[0] == "issue")
+            npp = at(ppc + 1)
             if kind == "wait_empty":
                 _, s_, ph = op
-                if bars[S + s_][1] != ph:
+                if flushing:
+                    n = commit_oldest(ppc)
+                    if n is not None:
+                        succ.append(n)
+                elif bars[S + s_][1] != ph:
                     succ.append((npp, qpcs, bars, slots, inflight))
+                elif eager_min > 0 and issued - done >= eager_min:
+                    succ.append((at(ppc, done, 1), qpcs, bars, slots, inflight))
             elif kind == "arrive_tx":
                 s_ = op[1]
                 b = list(bars)
@@ -345,17 +374,20 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
                 if sl[s_] is None or sl[s_][0] != t:
                     sl[s_] = (t, frozenset())          # older contents destroyed
                 succ.append((npp, qpcs, bars, tuple(sl), inflight | {(t, part)}))
-            elif kind == "wait_landed":
-                _, u, part = op
-                if (u, part) not in inflight:
+            elif kind == "commit_lag":
+                if issued - done > lag:
+                    n = commit_oldest(ppc + 1)
+                    if n is not None:
+                        succ.append(n)
+                else:
                     succ.append((npp, qpcs, bars, slots, inflight))
-            elif kind == "arrive_full":
-                s_ = op[1]
-                b = list(bars)
-                pend, ph, tx = b[s_]
-                b[s_] = (pend - 1, ph, tx)
-                settle(b, s_)
-                succ.append((npp, qpcs, tuple(b), slots, inflight))
+            elif kind == "commit_all":
+                if issued > done:
+                    n = commit_oldest(ppc)
+                    if n is not None:
+                        succ.append(n)
+                else:
+                    succ.append((npp, qpcs, bars, slots, inflight))
         # copy engine: any in-flight share may land
         for (t, part) in inflight:
             s_ = t % S
@@ -395,7 +427,7 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
                 settle(b, S + s_)
                 succ.append((ppcs, nq, tuple(b), slots, inflight))
         if not succ:
-            if (all(pc == len(progs[i]) for i, pc in enumerate(ppcs))
+            if (all(pc[0] == len(progs[i]) for i, pc in enumerate(ppcs))
                     and all(q == nQ for q in qpcs) and not inflight):
                 completed = True
             else:

@@ -110,7 +110,7 @@ def test_release_before_read_overwrites_live_data():
     assert any(v[0] == "I2" for v in r.violations)
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 6, 8])
 def test_commit_lag_rule(S):
     """A counter barrier without transaction bytes: committing tile t-L after
     issuing tile t is live iff L <= S-1."""
@@ -149,3 +149,45 @@ def test_two_producer_commit_lag_rule(S):
             assert r.completed and r.violations == [], (S, L)
         else:
             assert r.deadlock, (S, L)
+
+
+@pytest.mark.parametrize("S,T,C,producers", [(5, 7, 1, 1), (6, 8, 2, 1), (8, 10, 1, 1),
+                                             (8, 9, 2, 1), (5, 6, 1, 2), (6, 7, 1, 2),
+                                             (2, 3, 1, 4)])
+def test_deep_rings_and_four_producer_waves_safe_and_live(S, T, C, producers):
+    """Rings deeper than 4 stages, with the commit lag at its liveness bound S-1,
+    and four producer waves each moving a quarter of every tile."""
+    r = P.check_protocol(S, T, C, mode="landed", lag=S - 1, producers=producers)
+    assert r.completed and not r.deadlock and r.violations == []
+    assert r.max_ahead == min(S, T)
+
+
+@pytest.mark.parametrize("S,T,C,producers", [(1, 3, 2, 1), (2, 5, 2, 1), (3, 5, 2, 1),
+                                             (4, 6, 1, 1), (6, 8, 1, 1), (2, 4, 1, 2),
+                                             (3, 4, 1, 2)])
+@pytest.mark.parametrize("eager_min", [1, 2])
+def test_eager_commit_safe_and_live(S, T, C, producers, eager_min):
+    """Committing the oldest landed tile while the acquire is blocked never
+    publishes a tile early and never loses a slot."""
+    r = P.check_protocol(S, T, C, mode="landed", lag=S - 1, producers=producers,
+                         eager_min=eager_min)
+    assert r.completed and not r.deadlock and r.violations == []
+    assert r.max_ahead == min(S, T)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_eager_commit_lifts_the_lag_bound(S):
+    """Without eager commits a lag of S tiles deadlocks (the producer holds back
+    the tile the consumers need while it waits for them); with them any lag is live."""
+    for L in (S, S + 2):
+        assert P.check_protocol(S, S + 2, 1, mode="landed", lag=L).deadlock
+        r = P.check_protocol(S, S + 2, 1, mode="landed", lag=L, eager_min=1)
+        assert r.completed and r.violations == [], (S, L)
+        # skipping the newest tile in flight: live as soon as S >= 2 tiles can be pending
+        r2 = P.check_protocol(S, S + 2, 1, mode="landed", lag=L, eager_min=2)
+        assert r2.completed == (S >= 2) and r2.deadlock == (S < 2), (S, L)
+
+
+def test_eager_commit_needs_landed_mode():
+    with pytest.raises(ValueError):
+        P.check_protocol(2, 3, 1, mode="tx", eager_min=1)
