@@ -47,8 +47,10 @@ PIPE_FLAG_GEMM_B_LINEAR = 0x8
 PIPE_FLAG_XCD_REMAP = 0x10
 PIPE_FLAG_SPLIT_INTERLEAVE = 0x20
 PIPE_FLAG_UNIFIED = 0x40
+PIPE_FLAG_LAZY_COMMIT = 0x80
 PIPE_FLAG_TEST_START_PHASE0 = 0x100
 PIPE_FLAG_TEST_NO_RELEASE = 0x200
+PIPE_FLAG_EAGER_NEWEST = 0x400
 
 PIPE_STATUS_TIMEOUT_PRODUCER = 0x1
 PIPE_STATUS_TIMEOUT_CONSUMER = 0x2

@@ -1,0 +1,53 @@
+"""ctypes binding of libpipeceil.so (include/pipe_ceiling.h).
+
+Context-only HBM ceilings, timed beside the tile stream: plain grid-stride
+streaming copy and read kernels and the runtime's device-to-device copy.
+They are a measurement aid and take no part in the tile stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpipeceil.so")
+SYMBOLS = ("ceil_copy", "ceil_read", "ceil_memcpy")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m async_stage_tile_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.ceil_copy.argtypes = [vp, vp, sz, i, i, i, vp]
+        L.ceil_read.argtypes = [vp, vp, sz, i, i, vp]
+        L.ceil_memcpy.argtypes = [vp, vp, sz, vp]
+        for f in SYMBOLS:
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def copy(src, dst, grid: int, unroll: int = 4, nt: int = 1, stream=None) -> None:
+    """dst <- src (torch tensors of equal byte size) with the plain streaming copy."""
+    _check(lib().ceil_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(),
+                           grid, unroll, nt, stream), "ceil_copy")
+
+
+def read(src, sink, grid: int, nt: int = 1, stream=None) -> None:
+    """Stream-read every byte of src; sink is a 1-element int32 device tensor."""
+    _check(lib().ceil_read(src.data_ptr(), sink.data_ptr(), src.numel() * src.element_size(),
+                           grid, nt, stream), "ceil_read")
+
+
+def memcpy(src, dst, stream=None) -> None:
+    _check(lib().ceil_memcpy(dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(),
+                             stream), "ceil_memcpy")

@@ -15,11 +15,18 @@ using namespace pipe;
 __device__ uint32_t g_status_word;
 
 constexpr uint32_t kDefaultSpin = 1u << 22;
+// Eager commits (see acquire_slot): a producer whose acquire waits commits its
+// oldest tile in flight while at least this many are uncommitted (0 = never).
+int eager_min_pending(uint32_t flags) {
+  if (flags & PIPE_FLAG_LAZY_COMMIT) return 0;
+  return (flags & PIPE_FLAG_EAGER_NEWEST) ? 1 : 2;
+}
 constexpr int kMaxDevices = 64;
 constexpr int kLdsLimit = 163840;
 constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_NONTEMPORAL |
                                  PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_XCD_REMAP |
                                  PIPE_FLAG_SPLIT_INTERLEAVE | PIPE_FLAG_UNIFIED |
+                                 PIPE_FLAG_LAZY_COMMIT | PIPE_FLAG_EAGER_NEWEST |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -55,10 +62,10 @@ pipe_config_t defaults(pipe_op_t op) {
   switch (op) {
     case PIPE_OP_COPY:
       c.stages = 2;
-      c.producer_waves = 2;
+      c.producer_waves = 4;
       c.consumer_waves = 4;
       c.swizzle_shift = 0;
-      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP;
+      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP | PIPE_FLAG_LAZY_COMMIT;
       break;
     case PIPE_OP_ROWSUM:
       c.stages = 4;
@@ -68,11 +75,11 @@ pipe_config_t defaults(pipe_op_t op) {
       c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP;
       break;
     default:
-      c.stages = 4;
-      c.producer_waves = 2;
+      c.stages = 2;
+      c.producer_waves = 4;
       c.consumer_waves = 4;
       c.swizzle_shift = 1;
-      c.flags = 0;
+      c.flags = PIPE_FLAG_EAGER_NEWEST;
       break;
   }
   c.spin_limit = 0;
@@ -84,6 +91,8 @@ pipe_config_t defaults(pipe_op_t op) {
 
 pipe_status_t check_common(const pipe_config_t& c) {
   if (c.flags & ~kKnownFlags) return PIPE_ERR_CONFIG;
+  if ((c.flags & PIPE_FLAG_LAZY_COMMIT) && (c.flags & PIPE_FLAG_EAGER_NEWEST))
+    return PIPE_ERR_CONFIG;
   if (c.grid < 0 || c.split < 0 || c.swizzle_shift < 0 || c.swizzle_shift > 3)
     return PIPE_ERR_CONFIG;
   if (c.trace_capacity < 0) return PIPE_ERR_CONFIG;
@@ -97,11 +106,16 @@ pipe_status_t check_common(const pipe_config_t& c) {
 pipe_status_t check_stream_cfg(const pipe_config_t& c) {
   pipe_status_t s = check_common(c);
   if (s != PIPE_OK) return s;
-  if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
+  if (c.stages < 1 || c.stages > 8) return PIPE_ERR_STAGES;
   if (c.tile_m != 128 || c.tile_n != 64) return PIPE_ERR_CONFIG;
-  if (c.producer_waves != 1 && c.producer_waves != 2) return PIPE_ERR_CONFIG;
-  const int cw = c.consumer_waves;
+  const int cw = c.consumer_waves, pw = c.producer_waves;
+  if (c.flags & PIPE_FLAG_UNIFIED) {
+    if (!(cw == 2 || cw == 4 || cw == 8)) return PIPE_ERR_CONFIG;
+    return c.stages * 16384 > kLdsLimit ? PIPE_ERR_STAGES : PIPE_OK;
+  }
+  if (!(pw == 1 || pw == 2 || pw == 4)) return PIPE_ERR_CONFIG;
   if (!(cw == 1 || cw == 2 || cw == 3 || cw == 4 || cw == 8)) return PIPE_ERR_CONFIG;
+  if (!stream_shape_supported(c.stages, cw, pw)) return PIPE_ERR_CONFIG;
   if (stream_lds_bytes(c.stages, cw) > kLdsLimit) return PIPE_ERR_STAGES;
   return PIPE_OK;
 }
@@ -162,8 +176,8 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   p->row_strips = row_strips ? 1 : 0;
   p->swz_shift = c.swizzle_shift;
   // Commit lag: at most S-1 tiles (the protocol's liveness bound) and at most
-  // 48 loads outstanding per producer wave: (lag + 1) tiles of 16 / producer_waves.
-  const int max_lag = c.producer_waves == 2 ? 3 : 2;
+  // what the vmcnt counter can track: (lag + 1) tiles of 16 / producer_waves loads.
+  const int max_lag = stream_max_lag(c.producer_waves);
   p->lag = c.stages - 1 < max_lag ? c.stages - 1 : max_lag;
   p->xcd_remap = ((c.flags & PIPE_FLAG_XCD_REMAP) && g.items % 8 == 0) ? 1 : 0;
   p->interleave = (c.flags & PIPE_FLAG_SPLIT_INTERLEAVE) ? 1 : 0;
@@ -173,6 +187,7 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   p->trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
   p->trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
   p->nt = (c.flags & PIPE_FLAG_NONTEMPORAL) ? 1 : 0;
+  p->eager = eager_min_pending(c.flags);
 }
 
 pipe_status_t resolve_status(const pipe_config_t& c, uint32_t** out) {
@@ -360,6 +375,7 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t
   p.items = (int32_t)items;
   p.swz_shift = c.swizzle_shift;
   p.b_swz = (c.flags & PIPE_FLAG_GEMM_B_LINEAR) ? 0 : 1;
+  p.eager = eager_min_pending(c.flags);
   p.spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
   p.trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
   p.trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;

@@ -146,14 +146,52 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// s_waitcnt vmcnt(16 * k) for a wave-uniform k in [0, 3].
-__device__ __forceinline__ void wait_vmcnt_tiles(int k) {
-  switch (k) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<16>(); break;
-    case 2: wait_vmcnt<32>(); break;
-    default: wait_vmcnt<48>(); break;
+// s_waitcnt vmcnt(k * STEP) for a wave-uniform k >= 0 (a chain of scalar
+// compares, since the count is an immediate). Nothing is emitted when
+// k * STEP > 63: the counter never holds more than 63 operations (issue stalls
+// first), so the operation waited for has already completed.
+template <int STEP, int K = 0>
+__device__ __forceinline__ void wait_vmcnt_mul(int k) {
+  if constexpr (K * STEP <= 63) {
+    if (k == K) {
+      wait_vmcnt<K * STEP>();
+      return;
+    }
+    wait_vmcnt_mul<STEP, K + 1>(k);
   }
+}
+
+// producer_acquire with eager commits. Waits until slot `index` is released
+// (its empty barrier left phase `phase`). While the slot is still in use and
+// this wave has at least `eager_min` tiles in flight that it has not yet
+// committed (eager_min = 0: never), it commits the oldest of them (once its
+// LOADS loads have landed, i.e. at most LOADS * (pending - 1) remain
+// outstanding) instead of idling: the consumers may be waiting for exactly
+// that tile, and holding it back until the next issue would put a consumer
+// release and a producer wake-up between every two hand-offs. With
+// eager_min = 2 the newest tile in flight is never waited for here, so the
+// producer does not stall its next issue on a load it has only just begun.
+// Returns false on timeout.
+template <int LOADS, int S>
+__device__ __forceinline__ bool acquire_slot(uint32_t* empty_bar, uint32_t phase,
+                                             uint32_t* full_bars, int index, int& pending,
+                                             uint32_t arrivals, int eager_min,
+                                             uint32_t spin_limit) {
+  uint32_t polls = 0;
+  while ((uniform(bar_read(empty_bar)) >> 31) == phase) {
+    if (eager_min > 0 && pending >= eager_min) {
+      wait_vmcnt_mul<LOADS>(pending - 1);
+      int oldest = index - pending;
+      if (oldest < 0) oldest += S;
+      bar_arrive(&full_bars[oldest], arrivals);
+      --pending;
+      continue;
+    }
+    if (++polls >= spin_limit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return true;
 }
 
 // ---------------------------------------------------------------------------

@@ -72,17 +72,6 @@ __device__ __forceinline__ void gemm_tile_of(const GemmParams& p, int item, int&
   tn = item % p.tiles_n;
 }
 
-// s_waitcnt vmcnt(k * LOADS) for a wave-uniform number k of younger stages.
-template <int LOADS>
-__device__ __forceinline__ void wait_stages_younger(int k) {
-  switch (k) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<LOADS>(); break;
-    case 2: wait_vmcnt<2 * LOADS>(); break;
-    default: wait_vmcnt<(3 * LOADS < 63 ? 3 * LOADS : 48)>(); break;
-  }
-}
-
 // B-row chunk swizzle (positions of the 16 chunks of a 256-byte K-row).
 __device__ __forceinline__ int swz_b(int k, int on) {
   return on ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : 0;
@@ -105,7 +94,8 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
     const uint8_t* ga = p.A + (int64_t)tm * kGemmTile * p.lda;
     const uint8_t* gb = p.B + (int64_t)tn * kBRowBytes;
     for (int ks = 0; ks < p.k_steps; ++ks) {
-      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+      if (!acquire_slot<kLoads, S>(&lds.empty[w.index], w.phase, lds.full, w.index, pending,
+                                   (uint32_t)PW, p.eager, p.spin_limit)) {
         ok = false;
         break;
       }
@@ -134,7 +124,7 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
       }
       ++pending;
       if (pending > lag) {
-        wait_stages_younger<kLoads>(pending - 1);
+        wait_vmcnt_mul<kLoads>(pending - 1);
         int oldest = w.index - (pending - 1);
         if (oldest < 0) oldest += S;
         bar_arrive(&lds.full[oldest], (uint32_t)PW);
@@ -144,7 +134,7 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
     }
   }
   while (pending > 0) {
-    wait_stages_younger<kLoads>(pending - 1);
+    wait_vmcnt_mul<kLoads>(pending - 1);
     int oldest = w.index - pending;
     if (oldest < 0) oldest += S;
     bar_arrive(&lds.full[oldest], (uint32_t)PW);

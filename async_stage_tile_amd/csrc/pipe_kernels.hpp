@@ -28,7 +28,7 @@ struct StreamParams {
   int32_t items;          // n_strips * split
   int32_t row_strips;     // 1: a strip is one tile row walked along the columns
   int32_t swz_shift;
-  int32_t lag;            // producer commit lag in tiles (<= stages - 1, <= 2)
+  int32_t lag;            // producer commit lag in tiles (<= stages - 1, <= stream_max_lag)
   uint32_t spin_limit;
   uint32_t start_phase;   // producer start phase (1; 0 only in the deadlock test)
   int32_t no_release;     // test: consumers never release
@@ -36,17 +36,36 @@ struct StreamParams {
   int32_t nt;             // non-temporal hints on the streamed loads and stores
   int32_t xcd_remap;      // permute items so each XCD streams neighbouring strips
   int32_t interleave;     // segment s takes tiles s, s + split, s + 2 split, ...
+  int32_t eager;          // eager commits while the acquire waits: min tiles in flight (0 = off)
 };
 
+// Ring shapes (stages S, consumer waves C, producer waves PW) the stream
+// kernel is instantiated for: PW in {1, 2, 4}; C in {1, 2, 3, 4, 8} for
+// S = 1..4, and C in {4, 8} for the deep rings S = 5..8.
+constexpr bool stream_shape_supported(int S, int C, int PW) {
+  if (S < 1 || S > 8) return false;
+  if (!(PW == 1 || PW == 2 || PW == 4)) return false;
+  if (S > 4) return C == 4 || C == 8;
+  return C == 1 || C == 2 || C == 3 || C == 4 || C == 8;
+}
+
+// Largest commit lag for PW producer waves: each wave issues 16 / PW loads per
+// tile and (lag + 1) tiles of them must fit the 63-entry vmcnt counter.
+constexpr int stream_max_lag(int PW) { return 63 / (16 / PW) - 1; }
+
 // Launch the stream kernel for (op, stages, consumers, producers). Returns
-// hipSuccess or the launch error. `grid` workgroups of 64 * (producers +
-// consumers) threads.
+// hipSuccess or the launch error (hipErrorInvalidValue for a shape that is not
+// instantiated). `grid` workgroups of 64 * (producers + consumers) threads.
 hipError_t launch_stream(int op, int stages, int consumers, int producers, int grid,
                          const StreamParams& p, hipStream_t stream);
+template <int S>
+hipError_t launch_stream_stages(int op, int consumers, int producers, int grid,
+                                const StreamParams& p, hipStream_t stream);
 int stream_lds_bytes(int stages, int consumers);
 
 // Unified variant: `waves` waves (2, 4 or 8) each load and consume 16 / waves
-// blocks of every tile; divisible shapes only, no checksums or trace.
+// blocks of every tile; stages 1..8; divisible shapes only, no checksums or
+// trace.
 hipError_t launch_unified(int op, int stages, int waves, int grid, const StreamParams& p,
                           hipStream_t stream);
 
@@ -69,6 +88,7 @@ struct GemmParams {
   uint32_t* status;
   uint32_t* trace;
   int32_t trace_cap;
+  int32_t eager;          // eager commits while the acquire waits: min stages in flight (0 = off)
 };
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,

@@ -32,9 +32,14 @@
 // Slot layout: tile row r (128 B) holds its 16-byte chunk c at position
 // c ^ ((r >> shift) & 7). One producer DMA instruction q moves rows 8q..8q+7:
 // lane l writes LDS position l & 7 of row 8q + (l >> 3), so it fetches the
-// global chunk swz(row, l & 7). With PW = 2 producer waves, wave w issues
-// blocks 8w..8w+7 of every tile; full[s] then expects PW arrivals, and each
-// wave can keep up to 3 tiles of lag (24 loads outstanding).
+// global chunk swz(row, l & 7). With PW producer waves (1, 2 or 4), wave w
+// issues blocks (16/PW)w .. (16/PW)(w+1)-1 of every tile and full[s] expects PW
+// arrivals. A wave may keep `lag` committed-later tiles in flight as long as
+// (lag + 1) * 16/PW loads fit the 63-entry vmcnt counter: lag <= 2, 6, 14.
+//
+// The kernel is compiled once per stage count: this file is built several
+// times, each object instantiating the stage counts PIPE_STREAM_STAGES_LO ..
+// PIPE_STREAM_STAGES_HI (so the instantiations compile in parallel).
 #include "pipe_device.hpp"
 #include "pipe_kernels.hpp"
 
@@ -110,24 +115,14 @@ __device__ __forceinline__ int cols_in(const StreamParams& p, int tc) {
   return left < kTileCols ? (int)left : kTileCols;
 }
 
-// s_waitcnt vmcnt(k * LOADS) for a wave-uniform number k of younger tiles.
-template <int LOADS>
-__device__ __forceinline__ void wait_tiles_younger(int k) {
-  switch (k) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<LOADS>(); break;
-    case 2: wait_vmcnt<2 * LOADS>(); break;
-    default: wait_vmcnt<3 * LOADS>(); break;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Producer waves
 // ---------------------------------------------------------------------------
 template <int S, int C, int PW, bool MASKED>
 __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
   constexpr int kLoads = kBlocksPerTile / PW;  // DMA instructions per tile per wave
-  static_assert(3 * kLoads < 64, "vmcnt counts at most 63 outstanding loads");
+  static_assert((stream_max_lag(PW) + 1) * kLoads <= 63,
+                "vmcnt counts at most 63 outstanding loads");
   const int lane = lane_id();
   const int lrow = lane >> 3;  // row within a 1 KiB block
   const int lpos = lane & 7;   // chunk position within the row
@@ -141,8 +136,10 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
     const int item = item_index(p, it);
     const int len = item_len(p, item);
     for (int k = 0; k < len; ++k, ++t) {
-      // producer_acquire: wait until consumers released this slot.
-      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+      // producer_acquire: wait until consumers released this slot (committing
+      // landed tiles meanwhile, unless commits are lazy).
+      if (!acquire_slot<kLoads, S>(&lds.empty[w.index], w.phase, lds.full, w.index, pending,
+                                   (uint32_t)PW, p.eager, p.spin_limit)) {
         ok = false;
         break;
       }
@@ -182,7 +179,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
       // Commit the oldest in-flight tile once `lag` newer tiles are in flight:
       // its loads are done when at most kLoads*(pending-1) remain outstanding.
       if (pending > lag) {
-        wait_tiles_younger<kLoads>(pending - 1);
+        wait_vmcnt_mul<kLoads>(pending - 1);
         int oldest = w.index - (pending - 1);
         if (oldest < 0) oldest += S;
         bar_arrive(&lds.full[oldest], (uint32_t)PW);
@@ -193,7 +190,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
   }
   // Commit whatever is still in flight, oldest first.
   while (pending > 0) {
-    wait_tiles_younger<kLoads>(pending - 1);
+    wait_vmcnt_mul<kLoads>(pending - 1);
     int oldest = w.index - pending;
     if (oldest < 0) oldest += S;
     bar_arrive(&lds.full[oldest], (uint32_t)PW);
@@ -365,102 +362,87 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Row-sum finalize: out[r] = sum_{s < split} partial[s][r], in order s = 0..split-1.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) rowsum_finalize(const float* __restrict__ part,
-                                                       float* __restrict__ out, int64_t M,
-                                                       int split) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= M) return;
-  float s = part[r];
-  for (int k = 1; k < split; ++k) s += part[(int64_t)k * M + r];
-  out[r] = s;
-}
-
-__global__ void __launch_bounds__(256) fill_f32(float* __restrict__ out, int64_t rows,
-                                                int64_t cols, int64_t ld, float value) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * cols) return;
-  out[(i / cols) * ld + (i % cols)] = value;
-}
-
-// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int S, int C, int PW>
 static hipError_t launch_scp(int op, int grid, const StreamParams& p, hipStream_t stream) {
-  dim3 block(64 * (PW + C));
-  const bool masked = (p.M % kTileRows) != 0 || (p.N % kTileCols) != 0;
-  if (op == kOpCopy) {
-    if (masked)
-      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, true>), dim3(grid), block, 0, stream,
-                         p);
-    else
-      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, false>), dim3(grid), block, 0, stream,
-                         p);
+  if constexpr (!stream_shape_supported(S, C, PW)) {
+    return hipErrorInvalidValue;
   } else {
-    if (masked)
-      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, true>), dim3(grid), block, 0,
-                         stream, p);
-    else
-      hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, false>), dim3(grid), block, 0,
-                         stream, p);
+    dim3 block(64 * (PW + C));
+    const bool masked = (p.M % kTileRows) != 0 || (p.N % kTileCols) != 0;
+    if (op == kOpCopy) {
+      if (masked)
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, true>), dim3(grid), block, 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, false>), dim3(grid), block, 0,
+                           stream, p);
+    } else {
+      if (masked)
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, true>), dim3(grid), block, 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, false>), dim3(grid), block, 0,
+                           stream, p);
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <int S, int C>
 static hipError_t launch_sc(int op, int pw, int grid, const StreamParams& p,
                             hipStream_t stream) {
-  if (pw == 2) return launch_scp<S, C, 2>(op, grid, p, stream);
-  return launch_scp<S, C, 1>(op, grid, p, stream);
+  switch (pw) {
+    case 1: return launch_scp<S, C, 1>(op, grid, p, stream);
+    case 2: return launch_scp<S, C, 2>(op, grid, p, stream);
+    case 4: return launch_scp<S, C, 4>(op, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int S>
-static hipError_t launch_s(int op, int consumers, int pw, int grid, const StreamParams& p,
-                           hipStream_t stream) {
+hipError_t launch_stream_stages(int op, int consumers, int producers, int grid,
+                                const StreamParams& p, hipStream_t stream) {
   switch (consumers) {
-    case 1: return launch_sc<S, 1>(op, pw, grid, p, stream);
-    case 2: return launch_sc<S, 2>(op, pw, grid, p, stream);
-    case 3: return launch_sc<S, 3>(op, pw, grid, p, stream);
-    case 4: return launch_sc<S, 4>(op, pw, grid, p, stream);
-    case 8: return launch_sc<S, 8>(op, pw, grid, p, stream);
+    case 1: return launch_sc<S, 1>(op, producers, grid, p, stream);
+    case 2: return launch_sc<S, 2>(op, producers, grid, p, stream);
+    case 3: return launch_sc<S, 3>(op, producers, grid, p, stream);
+    case 4: return launch_sc<S, 4>(op, producers, grid, p, stream);
+    case 8: return launch_sc<S, 8>(op, producers, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_stream(int op, int stages, int consumers, int producers, int grid,
-                         const StreamParams& p, hipStream_t stream) {
-  if (producers != 1 && producers != 2) return hipErrorInvalidValue;
-  switch (stages) {
-    case 1: return launch_s<1>(op, consumers, producers, grid, p, stream);
-    case 2: return launch_s<2>(op, consumers, producers, grid, p, stream);
-    case 3: return launch_s<3>(op, consumers, producers, grid, p, stream);
-    case 4: return launch_s<4>(op, consumers, producers, grid, p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-int stream_lds_bytes(int stages, int consumers) {
-  return stages * kTileBytes + stages * 4 * (3 + consumers);
-}
-
-hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
-                                  hipStream_t stream) {
-  const int64_t blocks = (M + 255) / 256;
-  hipLaunchKernelGGL(rowsum_finalize, dim3((unsigned)blocks), dim3(256), 0, stream, partials,
-                     out, M, split);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, float value,
-                           hipStream_t stream) {
-  const int64_t n = rows * cols;
-  if (n == 0) return hipSuccess;
-  const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(fill_f32, dim3((unsigned)blocks), dim3(256), 0, stream, out, rows, cols,
-                     ld, value);
-  return hipGetLastError();
-}
+#if !defined(PIPE_STREAM_STAGES_LO) || !defined(PIPE_STREAM_STAGES_HI)
+#error "build with -DPIPE_STREAM_STAGES_LO=<s> -DPIPE_STREAM_STAGES_HI=<s>"
+#endif
+#define PIPE_STREAM_INSTANTIATE(S)                                                      \
+  template hipError_t launch_stream_stages<S>(int, int, int, int, const StreamParams&, \
+                                              hipStream_t);
+#if PIPE_STREAM_STAGES_LO <= 1 && 1 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(1)
+#endif
+#if PIPE_STREAM_STAGES_LO <= 2 && 2 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(2)
+#endif
+#if PIPE_STREAM_STAGES_LO <= 3 && 3 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(3)
+#endif
+#if PIPE_STREAM_STAGES_LO <= 4 && 4 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(4)
+#endif
+#if PIPE_STREAM_STAGES_LO <= 5 && 5 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(5)
+#endif
+#if PIPE_STREAM_STAGES_LO <= 6 && 6 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(6)
+#endif
+#if PIPE_STREAM_STAGES_LO <= 7 && 7 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(7)
+#endif
+#if PIPE_STREAM_STAGES_LO <= 8 && 8 <= PIPE_STREAM_STAGES_HI
+PIPE_STREAM_INSTANTIATE(8)
+#endif
 
 }  // namespace pipe

@@ -1,0 +1,66 @@
+// Stream-kernel dispatch over the stage count, the row-sum finalize and a
+// small fill kernel. The stream kernels themselves are instantiated per stage
+// count in the objects built from pipe_stream.hip.
+#include "pipe_device.hpp"
+#include "pipe_kernels.hpp"
+
+namespace pipe {
+
+hipError_t launch_stream(int op, int stages, int consumers, int producers, int grid,
+                         const StreamParams& p, hipStream_t stream) {
+  switch (stages) {
+    case 1: return launch_stream_stages<1>(op, consumers, producers, grid, p, stream);
+    case 2: return launch_stream_stages<2>(op, consumers, producers, grid, p, stream);
+    case 3: return launch_stream_stages<3>(op, consumers, producers, grid, p, stream);
+    case 4: return launch_stream_stages<4>(op, consumers, producers, grid, p, stream);
+    case 5: return launch_stream_stages<5>(op, consumers, producers, grid, p, stream);
+    case 6: return launch_stream_stages<6>(op, consumers, producers, grid, p, stream);
+    case 7: return launch_stream_stages<7>(op, consumers, producers, grid, p, stream);
+    case 8: return launch_stream_stages<8>(op, consumers, producers, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int stream_lds_bytes(int stages, int consumers) {
+  return stages * kTileBytes + stages * 4 * (3 + consumers);
+}
+
+// ---------------------------------------------------------------------------
+// Row-sum finalize: out[r] = sum_{s < split} partial[s][r], in order s = 0..split-1.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) rowsum_finalize(const float* __restrict__ part,
+                                                       float* __restrict__ out, int64_t M,
+                                                       int split) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= M) return;
+  float s = part[r];
+  for (int k = 1; k < split; ++k) s += part[(int64_t)k * M + r];
+  out[r] = s;
+}
+
+__global__ void __launch_bounds__(256) fill_f32(float* __restrict__ out, int64_t rows,
+                                                int64_t cols, int64_t ld, float value) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * cols) return;
+  out[(i / cols) * ld + (i % cols)] = value;
+}
+
+hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
+                                  hipStream_t stream) {
+  const int64_t blocks = (M + 255) / 256;
+  hipLaunchKernelGGL(rowsum_finalize, dim3((unsigned)blocks), dim3(256), 0, stream, partials,
+                     out, M, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, float value,
+                           hipStream_t stream) {
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_f32, dim3((unsigned)blocks), dim3(256), 0, stream, out, rows, cols,
+                     ld, value);
+  return hipGetLastError();
+}
+
+}  // namespace pipe

@@ -65,19 +65,6 @@ struct Walk {
   }
 };
 
-// s_waitcnt vmcnt(k * STEP) for a wave-uniform k; nothing when k * STEP > 63
-// (the counter never holds more, so such an operation has already completed).
-template <int STEP, int K>
-__device__ __forceinline__ void wait_multiple(int k) {
-  if constexpr (K * STEP <= 63) {
-    if (k == K) {
-      wait_vmcnt<K * STEP>();
-      return;
-    }
-    wait_multiple<STEP, K + 1>(k);
-  }
-}
-
 template <int S>
 struct Marks {
   int m[S];
@@ -143,7 +130,7 @@ __global__ void __launch_bounds__(64 * W) unified_kernel(StreamParams p) {
     const int s = t % S;
     if (S == 1 && iss.valid(p)) issue();
     // Batch wait: this wave's loads of tile t have landed.
-    wait_multiple<kLoads, 0>((vm - mark.get(s)) / kLoads);
+    wait_vmcnt_mul<kLoads>((vm - mark.get(s)) / kLoads);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const uint8_t* slot = &slots[s][0];
     uint4 v[kLoads];
@@ -230,6 +217,10 @@ hipError_t launch_unified(int op, int stages, int waves, int grid, const StreamP
     case 2: return launch_s<2>(op, waves, grid, p, stream);
     case 3: return launch_s<3>(op, waves, grid, p, stream);
     case 4: return launch_s<4>(op, waves, grid, p, stream);
+    case 5: return launch_s<5>(op, waves, grid, p, stream);
+    case 6: return launch_s<6>(op, waves, grid, p, stream);
+    case 7: return launch_s<7>(op, waves, grid, p, stream);
+    case 8: return launch_s<8>(op, waves, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -71,6 +71,14 @@ typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_
                                           share of every tile, with per-wave batch waits and no
                                           full/empty barriers; M % 128 == N % 64 == 0 only, no
                                           checksums or trace (else PIPE_ERR_CONFIG) */
+#define PIPE_FLAG_LAZY_COMMIT 0x80u    /* copy/rowsum/gemm (specialised ring): the producer commits
+                                          a tile only once `lag` younger tiles are in flight, never
+                                          while its acquire waits for a slot. Without this flag a
+                                          producer whose acquire waits commits its oldest tile in
+                                          flight (after it landed) while it has 2 or more in flight */
+#define PIPE_FLAG_EAGER_NEWEST 0x400u  /* as above, but the waiting producer also commits its newest
+                                          tile in flight (waits for it to land); exclusive with
+                                          PIPE_FLAG_LAZY_COMMIT (else PIPE_ERR_CONFIG) */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the
@@ -89,12 +97,14 @@ typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_
 #define PIPE_TRACE_WORDS 8
 
 typedef struct {
-  int32_t stages;         /* S, ring depth: 1..4 (copy/rowsum), 1..4 (gemm)              */
+  int32_t stages;         /* S, ring depth: copy/rowsum 1..8 (5..8 need 4 or 8 consumer
+                             waves; the ring must fit 160 KiB of LDS); gemm 1..4          */
   int32_t tile_m;         /* copy/rowsum: 128; gemm: 128                                  */
   int32_t tile_n;         /* copy/rowsum: 64 fp16; gemm: 128                              */
   int32_t tile_k;         /* gemm only: 64                                                */
-  int32_t producer_waves; /* copy/rowsum: 1 or 2; gemm: 2 or 4 (each tile's loads split) */
-  int32_t consumer_waves; /* copy/rowsum: 1..8; gemm: 4                                   */
+  int32_t producer_waves; /* copy/rowsum: 1, 2 or 4; gemm: 2 or 4 (each tile's loads split
+                             evenly; a wave keeps up to 2, 6 or 14 tiles of commit lag)   */
+  int32_t consumer_waves; /* copy/rowsum: 1, 2, 3, 4 or 8 (unified: 2, 4 or 8); gemm: 4   */
   int32_t grid;           /* workgroups; 0 = one per work item (capped by the device)     */
   int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default 1  */
   int32_t swizzle_shift;  /* row bits XOR-ed into the 16-byte chunk index: 0..3           */
@@ -121,12 +131,12 @@ int pipe_abi_version(void);
 const char* pipe_status_str(int status);
 
 /* Fill *cfg with the defaults of an op (grid and split automatic):
- *   copy:   stages 2, tile 128x64, 2 producer + 4 consumer waves,
- *           flags NONTEMPORAL | XCD_REMAP, swizzle shift 0;
+ *   copy:   stages 2, tile 128x64, 4 producer + 4 consumer waves,
+ *           flags NONTEMPORAL | XCD_REMAP | LAZY_COMMIT, swizzle shift 0;
  *   rowsum: stages 4, tile 128x64, 1 producer + 8 consumer waves,
  *           flags NONTEMPORAL | XCD_REMAP, swizzle shift 0;
- *   gemm:   stages 4, tile 128x128x64, 2 producer + 4 consumer waves,
- *           swizzle shift 1, flags 0. */
+ *   gemm:   stages 2, tile 128x128x64, 4 producer + 4 consumer waves,
+ *           flags EAGER_NEWEST, swizzle shift 1. */
 pipe_status_t pipe_config_default(pipe_op_t op, pipe_config_t* cfg);
 
 /* Tile copy (configs: "cute（11）hopper之TMA_copy" round trip; "cute（12）

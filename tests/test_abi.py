@@ -36,12 +36,15 @@ def test_version_and_status_strings():
 
 def test_config_defaults():
     c = pt.make_config(pt.PIPE_OP_COPY)
-    assert (c.stages, c.tile_m, c.tile_n, c.producer_waves, c.consumer_waves) == (2, 128, 64, 2, 4)
-    assert c.flags == pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP
+    assert (c.stages, c.tile_m, c.tile_n, c.producer_waves, c.consumer_waves) == (2, 128, 64, 4, 4)
+    assert c.flags == (pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP |
+                       pt.PIPE_FLAG_LAZY_COMMIT)
     r = pt.make_config(pt.PIPE_OP_ROWSUM)
     assert (r.stages, r.producer_waves, r.consumer_waves) == (4, 1, 8)
     g = pt.make_config(pt.PIPE_OP_GEMM)
-    assert (g.tile_m, g.tile_n, g.tile_k, g.producer_waves, g.consumer_waves) == (128, 128, 64, 2, 4)
+    assert (g.stages, g.tile_m, g.tile_n, g.tile_k, g.producer_waves, g.consumer_waves) \
+        == (2, 128, 128, 64, 4, 4)
+    assert g.flags == pt.PIPE_FLAG_EAGER_NEWEST
     assert pt.lib().pipe_config_default(7, ctypes.byref(c)) == pt.PIPE_ERR_CONFIG
     assert pt.lib().pipe_config_default(0, None) == pt.PIPE_ERR_NULL
 
@@ -63,7 +66,7 @@ def test_copy_validation():
     assert _copy(FAKE + 8, FAKE, 256, 128, 128, 128) == pt.PIPE_ERR_ALIGN
     assert _copy(FAKE, FAKE, 256, 128, 132, 128) == pt.PIPE_ERR_ALIGN  # pitch not 16 B
     assert _copy(FAKE, FAKE, 256, 128, 128, 128, chk=FAKE + 2) == pt.PIPE_ERR_ALIGN
-    for bad in (0, 5):
+    for bad in (0, 9):
         assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, stages=bad)) \
             == pt.PIPE_ERR_STAGES
     for bad in (0, 5, 9):
@@ -76,9 +79,32 @@ def test_copy_validation():
         == pt.PIPE_ERR_CONFIG
     assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=pt.PIPE_FLAG_TRACE)) \
         == pt.PIPE_ERR_NULL
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(
+        0, flags=pt.PIPE_FLAG_LAZY_COMMIT | pt.PIPE_FLAG_EAGER_NEWEST)) == pt.PIPE_ERR_CONFIG
     # empty matrices are a no-op, with or without pointers
     assert _copy(None, None, 0, 128, 128, 128) == pt.PIPE_OK
     assert _copy(None, None, 256, 0, 0, 0) == pt.PIPE_OK
+
+
+def test_ring_shapes():
+    # Deep rings (S > 4) exist for 4 or 8 consumer waves only.
+    for kw in (dict(stages=5, consumer_waves=3), dict(stages=8, consumer_waves=2),
+               dict(producer_waves=3), dict(producer_waves=0)):
+        assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, **kw)) \
+            == pt.PIPE_ERR_CONFIG, kw
+    for C in (1, 2, 3):
+        q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 4096, 4096, stages=4, producer_waves=4,
+                                 consumer_waves=C)
+        assert q["threads"] == 64 * (4 + C)
+    for S in range(1, 9):
+        for pw in (1, 2, 4):
+            q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, stages=S, producer_waves=pw,
+                                     consumer_waves=8)
+            assert q["threads"] == 64 * (pw + 8)
+            assert S * 16384 <= q["lds_bytes"] <= 160 * 1024
+    q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 8192, 65536, stages=8, producer_waves=4,
+                             consumer_waves=4, flags=pt.PIPE_FLAG_UNIFIED)
+    assert q["lds_bytes"] == 8 * 16384 and q["threads"] == 256
 
 
 def test_unified_variant_constraints():
@@ -122,7 +148,7 @@ def test_rowsum_and_gemm_validation():
 def test_query_geometry():
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, stages=4)
     assert q["items"] == 256 and q["tiles_per_item"] == 128 and q["grid"] == 256
-    assert q["lds_bytes"] >= 4 * 16384 and q["threads"] == 384
+    assert q["lds_bytes"] >= 4 * 16384 and q["threads"] == 512
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, split=3, grid=100)
     assert q["split"] == 3 and q["tiles_per_item"] == 43 and q["items"] == 768 and q["grid"] == 100
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 128, 512, grid=1)
@@ -130,8 +156,8 @@ def test_query_geometry():
     q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 8192, 65536)
     assert q["items"] >= 256 and q["items"] == 64 * q["split"]
     q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096)
-    assert (q["items"], q["tiles_per_item"], q["threads"]) == (1024, 64, 384)
-    assert q["lds_bytes"] >= 3 * 32768
+    assert (q["items"], q["tiles_per_item"], q["threads"]) == (1024, 64, 512)
+    assert q["lds_bytes"] >= 2 * 32768
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 300, 200, split=1)   # ragged: 3 x 4 tiles
     assert (q["items"], q["tiles_per_item"]) == (4, 3)
     q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 1000, 3000, split=2)
@@ -145,3 +171,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(pt, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(pt.PipeBuildError):
         pt.lib()
+
+
+def test_ceiling_library_exports_and_validation():
+    from async_stage_tile_amd import ceiling
+    hdr = open(os.path.join(ROOT, "include", "pipe_ceiling.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(ceil_[a-z_]+)\s*\(", hdr)))
+    assert declared == sorted(ceiling.SYMBOLS)
+    L = ceiling.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    # validation runs before any HIP call
+    assert L.ceil_copy(None, FAKE, 1024, 8, 4, 1, None) == 1
+    assert L.ceil_copy(FAKE, FAKE, 1000, 8, 4, 1, None) == 2
+    assert L.ceil_copy(FAKE + 8, FAKE, 1024, 8, 4, 1, None) == 2
+    assert L.ceil_copy(FAKE, FAKE, 1024, 0, 4, 1, None) == 3
+    assert L.ceil_copy(FAKE, FAKE, 1024, 8, 2, 1, None) == 3
+    assert L.ceil_read(FAKE, None, 1024, 8, 1, None) == 1
+    assert L.ceil_read(FAKE, FAKE, 1024, 8, 2, None) == 3
+    assert L.ceil_memcpy(None, FAKE, 16, None) == 1

@@ -17,12 +17,16 @@ def _f32(t):
 
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
 @pytest.mark.parametrize("PW", [2, 4])
-def test_gemm_small_integers_bit_exact(S, PW):
+@pytest.mark.parametrize("policy", ["eager", "lazy", "newest"])
+def test_gemm_small_integers_bit_exact(S, PW, policy):
     M, N, K = 256, 384, 512
     A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=3, stream=0).to(DEV)
     B = synth.small_int((K, N), -2, 2, torch.bfloat16, seed=3, stream=1).to(DEV)
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    C = pt.pipe_gemm_mainloop(A, B, stages=S, producer_waves=PW, grid=5, status=st)
+    flags = {"eager": 0, "lazy": pt.PIPE_FLAG_LAZY_COMMIT,
+             "newest": pt.PIPE_FLAG_EAGER_NEWEST}[policy]
+    C = pt.pipe_gemm_mainloop(A, B, stages=S, producer_waves=PW, grid=5, status=st,
+                              flags=flags)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     ref = R.gemm_f64(_f32(A), _f32(B))

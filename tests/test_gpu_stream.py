@@ -140,7 +140,7 @@ def test_copy_strided_views():
     assert int((out[:, :64] != 0).sum()) == 0 and int((out[:, 576:] != 0).sum()) == 0
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 6, 8])
 def test_copy_full_size_bit_exact(S):
     """fp16 16384 x 16384 uniform[-1,1), persistent column strips."""
     src = synth.uniform((16384, 16384), torch.float16, seed=42, device=DEV)
@@ -329,8 +329,83 @@ def test_copy_offsets_beyond_4gib():
     torch.cuda.empty_cache()
 
 
+# ---------------------------------------------------------------- deep rings, 4 producer waves
+@pytest.mark.parametrize("S", [3, 5, 6, 7, 8])
+@pytest.mark.parametrize("PW", [1, 2, 4])
+@pytest.mark.parametrize("C", [4, 8])
+def test_copy_deep_rings(S, PW, C):
+    """S up to 8 slots (128 KiB of LDS) and 1, 2 or 4 producer waves; every
+    workgroup walks several items, so the ring wraps many times."""
+    M, N = 2048, 1280  # 16 x 20 tiles; 20 strips x 3 segments = 60 items on 7 workgroups
+    src = synth.unique_codes(M, N).to(DEV)
+    st = _status()
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, stages=S, producer_waves=PW,
+                                 consumer_waves=C, split=3, grid=7, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
+
+
+@pytest.mark.parametrize("S", [5, 8])
+@pytest.mark.parametrize("PW", [1, 2, 4])
+@pytest.mark.parametrize("shape", [(1024, 4096), (1000, 3000)])
+def test_rowsum_deep_rings_bit_exact(S, PW, shape):
+    A = synth.small_int(shape, -8, 8, torch.float16, seed=13).to(DEV)
+    st = _status()
+    out = pt.pipe_rowsum(A, stages=S, producer_waves=PW, consumer_waves=8, split=3, grid=5,
+                         status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+@pytest.mark.parametrize("row_strips", [False, True])
+def test_copy_deep_ring_ragged(row_strips):
+    src = synth.unique_codes(1000, 1000).to(DEV)
+    flags = pt.PIPE_FLAG_ROW_STRIPS if row_strips else 0
+    dst = pt.pipe_tile_copy(src, stages=8, producer_waves=4, consumer_waves=8, split=2, grid=3,
+                            flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst), _bits(src))
+
+
+# ---------------------------------------------------------------- commit policies
+POLICY = {"eager": 0, "lazy": pt.PIPE_FLAG_LAZY_COMMIT, "newest": pt.PIPE_FLAG_EAGER_NEWEST}
+
+
+@pytest.mark.parametrize("policy", ["eager", "lazy", "newest"])
+@pytest.mark.parametrize("S,PW,C", [(1, 1, 3), (2, 1, 4), (3, 1, 8), (4, 2, 4), (6, 4, 8),
+                                    (8, 2, 4)])
+def test_copy_commit_policies_bit_exact(policy, S, PW, C):
+    """Eager commits (two thresholds) and lag-only commits give the same bits,
+    with the lag at its bound S - 1 or below it."""
+    src = synth.unique_codes(1024, 1280).to(DEV)
+    st = _status()
+    flags = POLICY[policy]
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, stages=S, producer_waves=PW,
+                                 consumer_waves=C, split=2, grid=6, flags=flags, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))
+
+
+@pytest.mark.parametrize("policy", ["eager", "lazy", "newest"])
+@pytest.mark.parametrize("S,PW", [(2, 1), (3, 1), (4, 2), (6, 4)])
+def test_rowsum_commit_policies_bit_exact(policy, S, PW):
+    A = synth.small_int((1024, 4096), -8, 8, torch.float16, seed=14).to(DEV)
+    st = _status()
+    flags = POLICY[policy]
+    out = pt.pipe_rowsum(A, stages=S, producer_waves=PW, consumer_waves=8, split=4, grid=9,
+                         flags=flags, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
 # ---------------------------------------------------------------- unified variant
-@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 6, 8])
 @pytest.mark.parametrize("W", [2, 4, 8])
 def test_unified_copy_bit_exact(S, W):
     src = synth.unique_codes(1024, 640).to(DEV)
@@ -340,7 +415,7 @@ def test_unified_copy_bit_exact(S, W):
     assert np.array_equal(_bits(dst), _bits(src))
 
 
-@pytest.mark.parametrize("S", [1, 3, 4])
+@pytest.mark.parametrize("S", [1, 3, 4, 7])
 @pytest.mark.parametrize("W", [2, 8])
 @pytest.mark.parametrize("interleave", [False, True])
 def test_unified_rowsum_bit_exact(S, W, interleave):
