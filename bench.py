@@ -7,9 +7,19 @@ column strip. One step = one launch of the whole hot path over the matrix
 (tile walk, cursor/barrier handshakes, direct-to-LDS producer, consumer
 copy-out, release, tail).
 
-Also reported (in "extras", each timed the same way): the S = 1..4 sweep of
-the copy, the row sum of fp16 8192 x 65536 (GB/s) and the GEMM mainloop
-4096^3 bf16 (TFLOP/s), each at the library's default configuration.
+Also reported (in "extras"):
+  * the copy's ring-depth sweep S = 1..8;
+  * per-launch kernel times (median and min) of the headline copy and of the
+    row sum, both back to back ("hot") and with the 256 MB MALL flushed by
+    writing a 1 GiB scratch buffer before every launch ("cold", untimed flush);
+  * the row sum of fp16 8192 x 65536 (GB/s) and the GEMM mainloop 4096^3 bf16
+    (TFLOP/s) at the library's default configuration;
+  * the unified (non-specialised) variant of the copy and the row sum;
+  * context ceilings on the same device: the runtime's device-to-device copy,
+    torch's copy and plain streaming copy / read kernels with no LDS ring
+    (libpipeceil.so);
+  * the CPU oracle on bounded samples of the copy, row sum and GEMM, on one
+    thread and on all host threads.
 
 roofline.traffic: HBM bytes per launch of the headline kernel from rocprofv3
 FETCH_SIZE / WRITE_SIZE counters (scaled by the counts the same counters give
@@ -22,6 +32,9 @@ launch stream. Inputs are generated on the device before the timed region.
 
 cpu_baseline: the CPU oracle (oracle.results.tile_copy) timed on a bounded
 sample of the same matrix on the host, single-threaded numpy.
+
+`--only copy|rowsum|gemm|ceiling|calib` times one workload (for profiling)
+and prints no JSON line.
 """
 from __future__ import annotations
 
@@ -46,6 +59,7 @@ GEMM_N = 4096
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "copy_16384x16384_counters.md")
 KERNEL_SOURCES = ("pipe_device.hpp", "pipe_kernels.hpp", "pipe_stream.hip")
+MALL_FLUSH_BYTES = 1 << 30
 
 
 def log(msg):
@@ -103,6 +117,52 @@ def timed_launches(fn, steps, warmup):
     return wall, kern
 
 
+def launch_stats(fn, reps, warmup, before=None):
+    """Per-launch kernel time: each of `reps` launches between its own event
+    pair; before() (e.g. a cache flush) runs ahead of each pair, untimed.
+    Returns (median ms, min ms)."""
+    import statistics
+
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return statistics.median(times), min(times)
+
+
+_FLUSH = {}
+
+
+def mall_flush():
+    """Write a 1 GiB scratch buffer: evicts the inputs from the 256 MB MALL."""
+    import torch
+    if "buf" not in _FLUSH:
+        _FLUSH["buf"] = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        _FLUSH["k"] = 0
+    _FLUSH["k"] = (_FLUSH["k"] + 1) % 251
+    _FLUSH["buf"].fill_(_FLUSH["k"])
+
+
+def hot_cold(fn, nbytes, reps, warmup):
+    out = {}
+    for name, before in (("hot", None), ("cold", mall_flush)):
+        med, mn = launch_stats(fn, reps, warmup, before)
+        out[name] = {"median_ms": med, "min_ms": mn, "median_gbs": nbytes / (med * 1e-3) / 1e9,
+                     "best_gbs": nbytes / (mn * 1e-3) / 1e9}
+    return out
+
+
 _COPY_BUF = {}
 
 
@@ -117,7 +177,7 @@ def copy_buffers():
     return _COPY_BUF["src"], _COPY_BUF["dst"]
 
 
-def bench_copy(stages, steps, warmup, **cfg):
+def bench_copy(stages, steps, warmup, stats=False, **cfg):
     """The library's default copy configuration, with `stages` and any overrides."""
     import torch
 
@@ -128,6 +188,7 @@ def bench_copy(stages, steps, warmup, **cfg):
     kw = dict(cfg, stages=stages)
     fn = pt.copy_launcher(src, dst, status=st, **kw)
     wall, kern = timed_launches(fn, steps, warmup)
+    timing = hot_cold(fn, 2 * COPY_M * COPY_N * 2, max(steps, 20), 2) if stats else None
     ok = int(st.item()) == 0 and torch.equal(dst.view(torch.int16), src.view(torch.int16))
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, COPY_M, COPY_N, **kw)
     c = pt.make_config(pt.PIPE_OP_COPY, **kw)
@@ -136,30 +197,46 @@ def bench_copy(stages, steps, warmup, **cfg):
             "consumer_waves": c.consumer_waves, "flags": c.flags, "split": q["split"],
             "grid": q["grid"], "lds_bytes": q["lds_bytes"], "wall_ms": wall, "kernel_ms": kern,
             "bytes": nbytes, "gbs": nbytes / (wall * 1e-3) / 1e9,
-            "kernel_gbs": nbytes / (kern * 1e-3) / 1e9, "bit_exact": ok}
+            "kernel_gbs": nbytes / (kern * 1e-3) / 1e9, "bit_exact": ok,
+            **({"per_launch": timing} if timing else {})}
 
 
-def bench_rowsum(steps, warmup, stages=3):
-    """The library's default row-sum configuration at `stages`."""
+_ROWSUM_BUF = {}
+
+
+def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
+    """The library's default row-sum configuration, with any overrides."""
     import torch
 
     import async_stage_tile_amd as pt
     import synth
-    A = synth.normal((ROWSUM_M, ROWSUM_N), torch.float16, seed=42, device="cuda")
+    if not _ROWSUM_BUF:
+        _ROWSUM_BUF["A"] = synth.normal((ROWSUM_M, ROWSUM_N), torch.float16, seed=42,
+                                        device="cuda")
+    A = _ROWSUM_BUF["A"]
+    kw = dict(cfg)
+    if stages is not None:
+        kw["stages"] = stages
     out = torch.empty(ROWSUM_M, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, pt.pipe_rowsum_workspace_bytes(ROWSUM_M, ROWSUM_N, stages=stages)),
+    ws = torch.empty(max(1, pt.pipe_rowsum_workspace_bytes(ROWSUM_M, ROWSUM_N, **kw)),
                      dtype=torch.uint8, device="cuda")
-    fn = pt.rowsum_launcher(A, out, ws, stages=stages)
+    fn = pt.rowsum_launcher(A, out, ws, **kw)
     wall, kern = timed_launches(fn, steps, warmup)
     nbytes = ROWSUM_M * ROWSUM_N * 2 + ROWSUM_M * 4
-    q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, ROWSUM_M, ROWSUM_N, stages=stages)
-    del A
-    return {"stages": stages, "split": q["split"], "grid": q["grid"], "wall_ms": wall,
-            "kernel_ms": kern, "bytes": nbytes, "gbs": nbytes / (wall * 1e-3) / 1e9}
+    timing = hot_cold(fn, nbytes, max(steps, 20), 2) if stats else None
+    q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, ROWSUM_M, ROWSUM_N, **kw)
+    c = pt.make_config(pt.PIPE_OP_ROWSUM, **kw)
+    r = {"stages": c.stages, "producer_waves": c.producer_waves,
+         "consumer_waves": c.consumer_waves, "flags": c.flags, "split": q["split"],
+         "grid": q["grid"], "wall_ms": wall, "kernel_ms": kern, "bytes": nbytes,
+         "gbs": nbytes / (wall * 1e-3) / 1e9, "kernel_gbs": nbytes / (kern * 1e-3) / 1e9}
+    if timing:
+        r["per_launch"] = timing
+    return r
 
 
-def bench_gemm(steps, warmup, stages=3):
-    """The library's default GEMM configuration at `stages`."""
+def bench_gemm(steps, warmup, stages=None):
+    """The library's default GEMM configuration (at `stages`, if given)."""
     import torch
 
     import async_stage_tile_amd as pt
@@ -168,30 +245,123 @@ def bench_gemm(steps, warmup, stages=3):
     A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device="cuda")
     B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device="cuda")
     C = torch.empty((n, n), dtype=torch.float32, device="cuda")
-    fn = pt.gemm_launcher(A, B, C, stages=stages)
+    kw = {} if stages is None else {"stages": stages}
+    fn = pt.gemm_launcher(A, B, C, **kw)
     wall, kern = timed_launches(fn, steps, warmup)
+    med, mn = launch_stats(fn, max(steps, 20), 0)
     flops = 2.0 * n * n * n
-    return {"stages": stages, "wall_ms": wall, "kernel_ms": kern, "flops": flops,
+    c = pt.make_config(pt.PIPE_OP_GEMM, **kw)
+    return {"stages": c.stages, "producer_waves": c.producer_waves, "flags": c.flags,
+            "wall_ms": wall, "kernel_ms": kern, "flops": flops,
             "tflops": flops / (wall * 1e-3) / 1e12,
-            "mfma_frac": flops / (wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            "mfma_frac": flops / (wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "per_launch": {"median_ms": med, "min_ms": mn,
+                           "median_tflops": flops / (med * 1e-3) / 1e12}}
 
 
-def cpu_baseline(rows):
-    """The oracle's tile copy on `rows` x 16384 of the same matrix, on the host."""
+def bench_ceilings(steps, warmup):
+    """Context ceilings on this device for the copy's traffic (512 MiB each way)
+    and for a 1 GiB read: no LDS ring, no tiles."""
+    import torch
+
+    from async_stage_tile_amd import ceiling
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    out = {}
+    cases = {
+        "hipMemcpyDtoD": lambda: ceiling.memcpy(src, dst),
+        "torch_copy": lambda: dst.copy_(src),
+    }
+    for grid in (2048, 4096, 8192):
+        cases[f"stream_copy_nt_x4_grid{grid}"] = (
+            lambda g=grid: ceiling.copy(src, dst, g, unroll=4, nt=1))
+    for name, fn in cases.items():
+        _, kern = timed_launches(fn, steps, warmup)
+        out[name] = 2 * n / (kern * 1e-3) / 1e9
+    assert torch.equal(src, dst)
+    del dst
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(5)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for grid in (1024, 2048, 4096):
+        _, kern = timed_launches(lambda g=grid: ceiling.read(big, sink, g, nt=1), steps, warmup)
+        out[f"stream_read_nt_grid{grid}"] = big.numel() / (kern * 1e-3) / 1e9
+    best_copy = max(v for k, v in out.items() if "read" not in k)
+    best_read = max(v for k, v in out.items() if "read" in k)
+    return {"gbs": out, "best_copy_gbs": best_copy, "best_read_gbs": best_read}
+
+
+def cpu_baseline(rows, min_seconds=10.0):
+    """The oracle's tile copy on the first `rows` x 16384 of the same matrix, on
+    one host thread, repeated until `min_seconds` of CPU work have elapsed."""
     import numpy as np
     import torch
 
     import synth
     from oracle import results as R
     src = synth.uniform((rows, COPY_N), torch.float16, seed=42).numpy()
-    t0 = time.perf_counter()
-    out = R.tile_copy(src)
-    dt = time.perf_counter() - t0
+    reps, dt = 0, 0.0
+    while dt < min_seconds:
+        t0 = time.perf_counter()
+        out = R.tile_copy(src)
+        dt += time.perf_counter() - t0
+        reps += 1
     assert np.array_equal(out.view(np.uint16), src.view(np.uint16))
-    nbytes = 2 * rows * COPY_N * 2
+    nbytes = 2 * rows * COPY_N * 2 * reps
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"tile copy of the first {rows} of {COPY_M} rows (x {COPY_N} fp16), "
-                      f"{nbytes} bytes read+write, {dt:.2f} s"}
+                      f"{reps} passes, {nbytes} bytes read+write in {dt:.2f} s"}
+
+
+def _threads():
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _parallel_rows(fn, rows, nthreads):
+    """Run fn(r0, r1) over row blocks on nthreads threads (numpy releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    step = (rows + nthreads - 1) // nthreads
+    with ThreadPoolExecutor(max_workers=nthreads) as ex:
+        list(ex.map(lambda r0: fn(r0, min(rows, r0 + step)), range(0, rows, step)))
+
+
+def cpu_oracle_extras(copy_rows, rowsum_rows, gemm_rows):
+    """The CPU oracle on bounded samples, on one thread and on all host threads.
+
+    copy: oracle.results.tile_copy on copy_rows x 16384; rowsum:
+    oracle.results.rowsum_exact on rowsum_rows x 65536; GEMM: oracle.results.gemm_f64
+    on gemm_rows rows of A (4096^2 bf16 inputs) against all of B."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import results as R
+    nt = _threads()
+    res = {"threads_all": nt}
+    src = synth.uniform((copy_rows, COPY_N), torch.float16, seed=42).numpy()
+    A = synth.normal((rowsum_rows, ROWSUM_N), torch.float16, seed=42).numpy()
+    Ga = synth.uniform((gemm_rows, GEMM_N), torch.bfloat16, seed=42, stream=0).float().numpy()
+    Gb = synth.uniform((GEMM_N, GEMM_N), torch.bfloat16, seed=42, stream=1).float().numpy()
+    for label, threads in (("1_thread", 1), ("all_threads", nt)):
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            _parallel_rows(lambda a, b: R.tile_copy(src[a:b]), copy_rows, threads)
+            tc = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            _parallel_rows(lambda a, b: R.rowsum_exact(A[a:b]), rowsum_rows, threads)
+            tr = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            R.gemm_f64(Ga, Gb)
+            tg = time.perf_counter() - t0
+        res[label] = {"copy_gbs": 4 * copy_rows * COPY_N / tc / 1e9,
+                      "rowsum_gbs": 2 * rowsum_rows * ROWSUM_N / tr / 1e9,
+                      "gemm_gflops": 2.0 * gemm_rows * GEMM_N * GEMM_N / tg / 1e9}
+    res["sample"] = (f"copy {copy_rows}x{COPY_N} fp16, rowsum {rowsum_rows}x{ROWSUM_N} fp16, "
+                     f"gemm {gemm_rows}x{GEMM_N} @ {GEMM_N}x{GEMM_N} bf16 in fp64")
+    return res
 
 
 def main():
@@ -204,7 +374,8 @@ def main():
                          "the copy -- the best of the S sweeps measured on MI355X); 0 = the "
                          "best of this run's 1..4 copy sweep")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--only", choices=["copy", "rowsum", "gemm", "calib"], default=None,
+    ap.add_argument("--only", choices=["copy", "rowsum", "gemm", "ceiling", "calib"],
+                    default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -233,19 +404,23 @@ def main():
         log(f"[bench] copy: {r}")
         return
     if args.only == "rowsum":
-        r = bench_rowsum(args.steps, args.warmup, args.stages or 4)
+        r = bench_rowsum(args.steps, args.warmup, args.stages)
         log(f"[bench] rowsum: {r}")
         return
     if args.only == "gemm":
-        r = bench_gemm(args.steps, args.warmup, args.stages or 4)
+        r = bench_gemm(args.steps, args.warmup, args.stages)
         log(f"[bench] gemm: {r}")
+        return
+    if args.only == "ceiling":
+        r = bench_ceilings(args.steps, args.warmup)
+        log(f"[bench] ceilings: {r}")
         return
 
     extras = {}
     stages = 2 if args.stages is None else args.stages
     if not args.no_extras or stages == 0:
         sweep = []
-        for s in (1, 2, 3, 4):
+        for s in (1, 2, 3, 4, 6, 8):
             r = bench_copy(s, max(3, args.steps // 2), 2)
             log(f"[bench] sweep S={s}: {r['gbs']:.1f} GB/s")
             sweep.append({k: r[k] for k in ("stages", "kernel_ms", "gbs", "bit_exact",
@@ -257,19 +432,45 @@ def main():
     head = bench_copy(stages, args.steps, args.warmup)
     log(f"[bench] copy S={stages}: {head['gbs']:.1f} GB/s (kernel {head['kernel_gbs']:.1f})")
     if not args.no_extras:
+        import async_stage_tile_amd as pt
+        t = bench_copy(stages, args.steps, args.warmup, stats=True)["per_launch"]
+        extras["copy_per_launch"] = t
+        log(f"[bench] copy per launch: hot {t['hot']['median_gbs']:.1f}, "
+            f"cold {t['cold']['median_gbs']:.1f} GB/s (median)")
+        u = bench_copy(2, max(3, args.steps // 2), 2, consumer_waves=2,
+                       flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
+                       pt.PIPE_FLAG_XCD_REMAP)
+        extras["copy_unified"] = {k: u[k] for k in ("stages", "consumer_waves", "flags",
+                                                    "kernel_ms", "gbs", "bit_exact")}
+        log(f"[bench] unified copy: {u['gbs']:.1f} GB/s")
         _COPY_BUF.clear()
         torch.cuda.empty_cache()
-        r = bench_rowsum(max(3, args.steps // 2), 2, 4)
+        r = bench_rowsum(max(3, args.steps // 2), 2, stats=True)
         log(f"[bench] rowsum: {r['gbs']:.1f} GB/s")
         extras["rowsum_8192x65536_fp16"] = r
-        g = bench_gemm(max(3, args.steps // 2), 2, 4)
+        r = bench_rowsum(max(3, args.steps // 2), 2, stages=2, consumer_waves=2, split=16,
+                         flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
+                         pt.PIPE_FLAG_XCD_REMAP)
+        log(f"[bench] unified rowsum: {r['gbs']:.1f} GB/s")
+        extras["rowsum_unified"] = r
+        _ROWSUM_BUF.clear()
+        torch.cuda.empty_cache()
+        g = bench_gemm(max(3, args.steps // 2), 2)
         log(f"[bench] gemm: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16"] = g
+        torch.cuda.empty_cache()
+        c = bench_ceilings(max(3, args.steps // 2), 2)
+        log(f"[bench] ceilings: copy {c['best_copy_gbs']:.1f}, read {c['best_read_gbs']:.1f} GB/s")
+        c["copy_frac_of_best_copy_ceiling"] = head["kernel_gbs"] / c["best_copy_gbs"]
+        extras["context_ceilings"] = c
     cpu = None
     if not args.no_cpu:
         log("[bench] cpu baseline ...")
         cpu = cpu_baseline(args.cpu_rows)
         log(f"[bench] cpu oracle: {cpu['value']:.2f} GB/s")
+        if not args.no_extras:
+            extras["cpu_oracle"] = cpu_oracle_extras(2048, 256, 64)
+            log(f"[bench] cpu oracle extras: {extras['cpu_oracle']}")
 
     achieved = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
     kname = (f"void pipe::stream_kernel<{head['stages']}, {head['consumer_waves']}, "
