@@ -51,6 +51,8 @@ PIPE_FLAG_LAZY_COMMIT = 0x80
 PIPE_FLAG_TEST_START_PHASE0 = 0x100
 PIPE_FLAG_TEST_NO_RELEASE = 0x200
 PIPE_FLAG_EAGER_NEWEST = 0x400
+PIPE_FLAG_GEMM_C_BF16 = 0x800
+PIPE_FLAG_GEMM_STORE_WAVE = 0x1000
 
 PIPE_STATUS_TIMEOUT_PRODUCER = 0x1
 PIPE_STATUS_TIMEOUT_CONSUMER = 0x2
@@ -245,19 +247,34 @@ def pipe_rowsum(A, out=None, workspace=None, stream=None, **cfg):
     return out
 
 
-def pipe_gemm_mainloop(A, B, C=None, stream=None, **cfg):
-    """C = A @ B (bf16 in, fp32 accumulate and out) with A/B tiles fed through the ring."""
+def _gemm_config(C, cfg):
+    """The GEMM config, with PIPE_FLAG_GEMM_C_BF16 set from C's dtype."""
+    import torch
+    c = make_config(PIPE_OP_GEMM, **cfg)
+    if C.dtype == torch.bfloat16:
+        c.flags |= PIPE_FLAG_GEMM_C_BF16
+    else:
+        c.flags &= ~PIPE_FLAG_GEMM_C_BF16
+    return c
+
+
+def pipe_gemm_mainloop(A, B, C=None, stream=None, out_dtype=None, **cfg):
+    """C = A @ B (bf16 in, fp32 accumulate) with A/B tiles fed through the ring.
+
+    C is fp32 (default) or bf16 (out_dtype=torch.bfloat16, or a bf16 C): a bf16
+    C is rounded to nearest even from the fp32 sums and written through the
+    staged epilogue."""
     import torch
     M, K, lda = _check_matrix(A, "A", (torch.bfloat16,))
     K2, N, ldb = _check_matrix(B, "B", (torch.bfloat16,))
     if K2 != K:
         raise ValueError("inner dimensions differ")
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32,))
+        C = torch.empty((M, N), dtype=out_dtype or torch.float32, device=A.device)
+    Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32, torch.bfloat16))
     if (Mc, Nc) != (M, N):
         raise ValueError("C shape mismatch")
-    c = make_config(PIPE_OP_GEMM, **cfg)
+    c = _gemm_config(C, cfg)
     st = lib().pipe_gemm_mainloop(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                   ctypes.byref(c), _stream(stream))
     _check(st, "pipe_gemm_mainloop")
@@ -317,10 +334,10 @@ def gemm_launcher(A, B, C, stream=None, **cfg):
     import torch
     M, K, lda = _check_matrix(A, "A", (torch.bfloat16,))
     K2, N, ldb = _check_matrix(B, "B", (torch.bfloat16,))
-    Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32,))
+    Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32, torch.bfloat16))
     if K2 != K or (Mc, Nc) != (M, N):
         raise ValueError("shape mismatch")
-    c = make_config(PIPE_OP_GEMM, **cfg)
+    c = _gemm_config(C, cfg)
     fn, args = lib().pipe_gemm_mainloop, (_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                            ctypes.byref(c), _stream(stream))
 

@@ -27,6 +27,7 @@ constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_F
                                  PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_XCD_REMAP |
                                  PIPE_FLAG_SPLIT_INTERLEAVE | PIPE_FLAG_UNIFIED |
                                  PIPE_FLAG_LAZY_COMMIT | PIPE_FLAG_EAGER_NEWEST |
+                                 PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -106,6 +107,8 @@ pipe_status_t check_common(const pipe_config_t& c) {
 pipe_status_t check_stream_cfg(const pipe_config_t& c) {
   pipe_status_t s = check_common(c);
   if (s != PIPE_OK) return s;
+  if (c.flags & (PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_GEMM_STORE_WAVE))
+    return PIPE_ERR_CONFIG;
   if (c.stages < 1 || c.stages > 8) return PIPE_ERR_STAGES;
   if (c.tile_m != 128 || c.tile_n != 64) return PIPE_ERR_CONFIG;
   const int cw = c.consumer_waves, pw = c.producer_waves;
@@ -334,7 +337,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
                                            g.split, st));
 }
 
-pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t M, int64_t N,
+pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t M, int64_t N,
                                  int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                                  const pipe_config_t* cfg, void* stream) {
   const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_GEMM);
@@ -346,15 +349,21 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t
     return PIPE_ERR_CONFIG;
   if (c.split > 1) return PIPE_ERR_CONFIG;
   if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE)) return PIPE_ERR_CONFIG;
-  if (gemm_lds_bytes(c.stages) > kLdsLimit) return PIPE_ERR_STAGES;
+  const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
+  const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
+  if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
+  if (gemm_lds_bytes(c.stages, c_bf16, store_wave) > kLdsLimit) return PIPE_ERR_STAGES;
   if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return PIPE_ERR_SHAPE;
   if (M % 128 != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
   if (M == 0 || N == 0) return PIPE_OK;
   if (C == nullptr) return PIPE_ERR_NULL;
-  if (!aligned4(C)) return PIPE_ERR_ALIGN;
+  if (c_bf16 ? (!aligned16(C) || (ldc % 8)) : !aligned4(C)) return PIPE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (K == 0) return hip_status(launch_fill_f32(C, M, N, ldc, 0.f, st));
+  if (K == 0) {
+    return hip_status(c_bf16 ? launch_fill_u16(static_cast<uint16_t*>(C), M, N, ldc, 0, st)
+                             : launch_fill_f32(static_cast<float*>(C), M, N, ldc, 0.f, st));
+  }
   if (A == nullptr || B == nullptr) return PIPE_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return PIPE_ERR_ALIGN;
   GemmParams p{};
@@ -376,6 +385,8 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, float* C, int64_t
   p.swz_shift = c.swizzle_shift;
   p.b_swz = (c.flags & PIPE_FLAG_GEMM_B_LINEAR) ? 0 : 1;
   p.eager = eager_min_pending(c.flags);
+  p.c_bf16 = c_bf16 ? 1 : 0;
+  p.store_wave = store_wave ? 1 : 0;
   p.spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
   p.trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
   p.trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
@@ -398,8 +409,11 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     if (M < 0 || N < 0 || K < 0 || M % 128 || N % 128 || K % 64) return PIPE_ERR_SHAPE;
     const int64_t items = (M / 128) * (N / 128);
     if (items > INT32_MAX) return PIPE_ERR_SHAPE;
-    info->lds_bytes = gemm_lds_bytes(c.stages);
-    info->threads = 64 * (c.producer_waves + 4);
+    const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
+    const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
+    if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
+    info->lds_bytes = gemm_lds_bytes(c.stages, c_bf16, store_wave);
+    info->threads = gemm_threads(c.producer_waves, c_bf16, store_wave);
     info->items = (int32_t)items;
     info->grid = (c.grid == 0 || c.grid > info->items) ? info->items : c.grid;
     info->tiles_per_item = (int32_t)(K / 64);

@@ -36,6 +36,25 @@
 // points at B[k0 + i/4][j0 + 4*(i%4)], it receives B[k0..k0+3][j0 + i]: four
 // consecutive K values of its own column, which is half an MFMA B operand.
 //
+// bf16 output goes through LDS in one of two ways.
+//
+// Wave-private staging (the default): each MFMA wave rounds its 64 x 64
+// quarter to bf16 chunk by chunk (16 rows) into its own 16 x 64 LDS buffer,
+// reads it back as 16-byte row pieces and stores 128-byte row segments; no
+// other wave is involved.
+//
+// Store wave (PIPE_FLAG_GEMM_STORE_WAVE): one more wave streams C out of LDS. Each pair of MFMA waves (the two that share 64 output rows)
+// owns a one-slot staging ring with its own full/empty barriers, the same
+// protocol as the input ring run in the store direction: the pair (producers,
+// start phase 1) waits on empty, rounds its accumulators to bf16 and writes
+// one 16-row chunk of the tile into the slot, waits for the writes to return
+// and arrives on full (2 arrivals); the store wave (consumer) waits on full,
+// reads the chunk back as 16-byte row pieces, releases the slot and writes
+// 256-byte row segments to C. The MFMA waves thus hand the tile over in
+// 4 chunks and move on to the next tile while the store wave drains it.
+// Slot rows are padded to 272 bytes so the two half-waves of a fragment write
+// (rows r and r + 4) fall on different banks.
+//
 // MFMA 32x32x16 operand layout (lane l, element e): A[i][k] with i = l % 32,
 // k = 8 * (l / 32) + e; B[k][j] with j = l % 32, k = 8 * (l / 32) + e; the
 // 16 accumulators hold D[i][j] with j = l % 32,
@@ -48,6 +67,7 @@ namespace pipe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -66,6 +86,26 @@ struct GemmLds {
   uint32_t full[S];
   uint32_t empty[S];
 };
+
+constexpr int kOutRows = 16;                          // rows per staged chunk
+constexpr int kOutPitch = kGemmTile * 2 + 16;         // 272 B: padded bf16 row
+constexpr int kOutSlotBytes = kOutRows * kOutPitch;   // 4352 B
+constexpr int kOutChunks = 64 / kOutRows;             // chunks per wave pair per tile
+
+struct OutLds {
+  uint8_t slot[2][kOutSlotBytes];  // one staging slot per MFMA wave pair
+  uint32_t full[2];
+  uint32_t empty[2];
+};
+
+constexpr int kWaveOutPitch = 64 * 2 + 16;                // 144 B: padded 64-column bf16 row
+constexpr int kWaveOutBytes = kOutRows * kWaveOutPitch;   // 2304 B per MFMA wave
+
+struct WaveOutLds {
+  uint8_t buf[4][kWaveOutBytes];
+};
+
+enum GemmEpilogue : int { kEpiF32 = 0, kEpiStoreWave = 1, kEpiWaveStaged = 2 };
 
 __device__ __forceinline__ void gemm_tile_of(const GemmParams& p, int item, int& tm, int& tn) {
   tm = item / p.tiles_n;
@@ -204,12 +244,14 @@ __device__ __forceinline__ void mfma_sub(f32x16 (&acc)[2][2], const SubFrags& f)
 // reads of the slot to return, releases the slot, then waits on full for the
 // next stage (while the previous MFMAs still execute) and reads that stage's
 // first sub-step before issuing the last MFMAs of the current one.
-template <int S>
-__device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
+template <int S, int EPI>
+__device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_lds, int cw) {
+  OutLds* out = static_cast<OutLds*>(out_lds);
   const int lane = lane_id();
   const int wm = cw >> 1, wn = cw & 1;
   const int li = lane & 31, lk = lane >> 5;
   PipeState rd = consumer_start(S);
+  PipeState ost = producer_start(1, 1u);  // staging slot of this wave's pair
   bool ok = true;
   for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
     int tm, tn;
@@ -252,59 +294,208 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, int cw) {
       mfma_sub(acc, b1);
     }
     if (!ok) break;
-    // Epilogue: fp32 accumulators -> C.
+    if constexpr (EPI == kEpiF32) {
+      // Epilogue: fp32 accumulators -> C.
+      float* C = static_cast<float*>(p.C);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int col = tn * kGemmTile + wn * 64 + ni * 32 + li;
+        for (int ni = 0; ni < 2; ++ni) {
+          const int col = tn * kGemmTile + wn * 64 + ni * 32 + li;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = tm * kGemmTile + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
-          p.C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+          for (int e = 0; e < 16; ++e) {
+            const int row = tm * kGemmTile + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+            C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+          }
+        }
+    } else if constexpr (EPI == kEpiWaveStaged) {
+      // Wave-private staging: chunk c = rows 16c..16c+15 of this wave's 64 rows
+      // (accumulator block mi = c / 2, element groups e / 4 = 2 (c % 2) + {0, 1}).
+      uint8_t* buf = &static_cast<WaveOutLds*>(out_lds)->buf[cw][0];
+      uint8_t* C = static_cast<uint8_t*>(p.C);
+      const int64_t ldc_bytes = p.ldc * 2;
+#pragma unroll
+      for (int c = 0; c < kOutChunks; ++c) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const int e = 4 * (2 * (c & 1) + g2) + m;
+              const int rr = 8 * g2 + 4 * lk + m;
+              *reinterpret_cast<__bf16*>(buf + rr * kWaveOutPitch + (ni * 32 + li) * 2) =
+                  (__bf16)acc[c >> 1][ni][e];
+            }
+        wait_lgkmcnt0();
+        uint4 v[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int q = i * 64 + lane;  // 16-byte piece q: row q / 8, piece q % 8
+          v[i] = *reinterpret_cast<const uint4*>(buf + (q >> 3) * kWaveOutPitch + (q & 7) * 16);
+        }
+        wait_lgkmcnt0();  // the buffer is rewritten by the next chunk
+        const int64_t row0 = (int64_t)tm * kGemmTile + wm * 64 + c * kOutRows;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int q = i * 64 + lane;
+          uint8_t* g = C + (row0 + (q >> 3)) * ldc_bytes + ((int64_t)tn * kGemmTile + wn * 64) * 2 +
+                       (q & 7) * 16;
+          const u32x4 nv = {v[i].x, v[i].y, v[i].z, v[i].w};
+          __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(g));
         }
       }
+    } else {
+      // Staged epilogue: chunk c holds rows 16c..16c+15 of this pair's 64 rows,
+      // i.e. accumulator block mi = c / 2, element groups e / 4 = 2 (c % 2) + {0, 1}.
+      uint8_t* slot = &out->slot[wm][0];
+#pragma unroll
+      for (int c = 0; c < kOutChunks; ++c) {
+        if (!bar_wait(&out->empty[wm], ost.phase, p.spin_limit)) {
+          ok = false;
+          break;
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int col = wn * 64 + ni * 32 + li;
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const int e = 4 * (2 * (c & 1) + g2) + m;
+              const int rr = 8 * g2 + 4 * lk + m;
+              *reinterpret_cast<__bf16*>(slot + rr * kOutPitch + col * 2) =
+                  (__bf16)acc[c >> 1][ni][e];
+            }
+        }
+        wait_lgkmcnt0();
+        bar_arrive(&out->full[wm], 2u);
+        ost.inc();
+      }
+      if (!ok) break;
+    }
   }
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int PW>
-__global__ void __launch_bounds__(64 * (PW + 4)) gemm_kernel(GemmParams p) {
+// Store wave of the staged epilogue: for every tile, drains the 4 chunks of
+// each wave pair (pair 0 and pair 1 alternately) and writes them to C.
+__device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
+  const int lane = lane_id();
+  PipeState rd[2] = {consumer_start(1), consumer_start(1)};
+  bool ok = true;
+  uint8_t* C = static_cast<uint8_t*>(p.C);
+  const int64_t ldc_bytes = p.ldc * 2;
+  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+    int tm, tn;
+    gemm_tile_of(p, item, tm, tn);
+    for (int c = 0; ok && c < kOutChunks; ++c) {
+#pragma unroll
+      for (int pair = 0; pair < 2; ++pair) {
+        if (!bar_wait(&out.full[pair], rd[pair].phase, p.spin_limit)) {
+          ok = false;
+          break;
+        }
+        const uint8_t* slot = &out.slot[pair][0];
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = i * 64 + lane;  // 16-byte piece q: row q / 16, piece q % 16
+          v[i] = *reinterpret_cast<const uint4*>(slot + (q >> 4) * kOutPitch + (q & 15) * 16);
+        }
+        wait_lgkmcnt0();
+        bar_arrive(&out.empty[pair], 1u);
+        rd[pair].inc();
+        const int64_t row0 = (int64_t)tm * kGemmTile + pair * 64 + c * kOutRows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = i * 64 + lane;
+          uint8_t* g = C + (row0 + (q >> 4)) * ldc_bytes + (int64_t)tn * kGemmTile * 2 + (q & 15) * 16;
+          const u32x4 nv = {v[i].x, v[i].y, v[i].z, v[i].w};
+          __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(g));
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
+}
+
+template <int S, int PW, int EPI>
+__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)))
+    gemm_kernel(GemmParams p) {
   __shared__ GemmLds<S> lds;
   const int wave = (int)(threadIdx.x >> 6);
   if (threadIdx.x < S) {
     lds.full[threadIdx.x] = 0u;
     lds.empty[threadIdx.x] = 0u;
   }
-  __syncthreads();
-  if (wave < PW)
-    gemm_producer<S, PW>(p, lds, wave);
-  else
-    gemm_consumer<S>(p, lds, wave - PW);
+  if constexpr (EPI == kEpiStoreWave) {
+    __shared__ OutLds out;
+    if (threadIdx.x < 2) {
+      out.full[threadIdx.x] = 0u;
+      out.empty[threadIdx.x] = 0u;
+    }
+    __syncthreads();
+    if (wave < PW)
+      gemm_producer<S, PW>(p, lds, wave);
+    else if (wave < PW + 4)
+      gemm_consumer<S, EPI>(p, lds, &out, wave - PW);
+    else
+      gemm_store_wave(p, out);
+  } else if constexpr (EPI == kEpiWaveStaged) {
+    __shared__ WaveOutLds out;
+    __syncthreads();
+    if (wave < PW)
+      gemm_producer<S, PW>(p, lds, wave);
+    else
+      gemm_consumer<S, EPI>(p, lds, &out, wave - PW);
+  } else {
+    __syncthreads();
+    if (wave < PW)
+      gemm_producer<S, PW>(p, lds, wave);
+    else
+      gemm_consumer<S, EPI>(p, lds, nullptr, wave - PW);
+  }
 }
 
-template <int PW>
+template <int PW, int EPI>
 hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t stream) {
-  const dim3 g(grid), b(64 * (PW + 4));
+  const dim3 g(grid), b(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)));
   switch (stages) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<1, PW>), g, b, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<2, PW>), g, b, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((gemm_kernel<3, PW>), g, b, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<4, PW>), g, b, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((gemm_kernel<1, PW, EPI>), g, b, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<2, PW, EPI>), g, b, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((gemm_kernel<3, PW, EPI>), g, b, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<4, PW, EPI>), g, b, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_gemm_epi(int stages, int producers, int grid, const GemmParams& p,
+                           hipStream_t stream) {
+  if (producers == 4) return launch_gemm_pw<4, EPI>(stages, grid, p, stream);
+  if (producers == 2) return launch_gemm_pw<2, EPI>(stages, grid, p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream) {
-  if (producers == 4) return launch_gemm_pw<4>(stages, grid, p, stream);
-  if (producers == 2) return launch_gemm_pw<2>(stages, grid, p, stream);
-  return hipErrorInvalidValue;
+  if (!p.c_bf16) return launch_gemm_epi<kEpiF32>(stages, producers, grid, p, stream);
+  if (p.store_wave) return launch_gemm_epi<kEpiStoreWave>(stages, producers, grid, p, stream);
+  return launch_gemm_epi<kEpiWaveStaged>(stages, producers, grid, p, stream);
 }
 
-int gemm_lds_bytes(int stages) { return stages * (kAStageBytes + kBStageBytes) + stages * 8; }
+int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave) {
+  const int out = !c_bf16 ? 0 : store_wave ? (int)sizeof(OutLds) : (int)sizeof(WaveOutLds);
+  return stages * (kAStageBytes + kBStageBytes) + stages * 8 + out;
+}
+
+int gemm_threads(int producers, bool c_bf16, bool store_wave) {
+  return 64 * (producers + 4 + (c_bf16 && store_wave ? 1 : 0));
+}
 
 }  // namespace pipe

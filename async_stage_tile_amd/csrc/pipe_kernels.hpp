@@ -73,11 +73,13 @@ hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, 
                                   hipStream_t stream);
 hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, float value,
                            hipStream_t stream);
+hipError_t launch_fill_u16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uint16_t value,
+                           hipStream_t stream);
 
 struct GemmParams {
   const uint8_t* A;       // bf16 M x K
   const uint8_t* B;       // bf16 K x N
-  float* C;               // fp32 M x N
+  void* C;                // M x N, fp32 (or bf16 when c_bf16)
   int64_t lda, ldb, ldc;  // bytes for A, B; elements for C
   int32_t M, N, K;
   int32_t tiles_m, tiles_n, k_steps;
@@ -89,10 +91,13 @@ struct GemmParams {
   uint32_t* trace;
   int32_t trace_cap;
   int32_t eager;          // eager commits while the acquire waits: min stages in flight (0 = off)
+  int32_t c_bf16;         // C is bf16, written through an LDS-staged epilogue
+  int32_t store_wave;     // bf16 C: a dedicated store wave drains the staging slots
 };
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream);
-int gemm_lds_bytes(int stages);
+int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave);
+int gemm_threads(int producers, bool c_bf16, bool store_wave);
 
 }  // namespace pipe

@@ -45,6 +45,13 @@ __global__ void __launch_bounds__(256) fill_f32(float* __restrict__ out, int64_t
   out[(i / cols) * ld + (i % cols)] = value;
 }
 
+__global__ void __launch_bounds__(256) fill_u16(uint16_t* __restrict__ out, int64_t rows,
+                                                int64_t cols, int64_t ld, uint16_t value) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * cols) return;
+  out[(i / cols) * ld + (i % cols)] = value;
+}
+
 hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
                                   hipStream_t stream) {
   const int64_t blocks = (M + 255) / 256;
@@ -60,6 +67,16 @@ hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, f
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(fill_f32, dim3((unsigned)blocks), dim3(256), 0, stream, out, rows, cols,
                      ld, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uint16_t value,
+                           hipStream_t stream) {
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_u16, dim3((unsigned)blocks), dim3(256), 0, stream, out, rows, cols, ld,
+                     value);
   return hipGetLastError();
 }
 

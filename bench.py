@@ -235,8 +235,9 @@ def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
     return r
 
 
-def bench_gemm(steps, warmup, stages=None):
-    """The library's default GEMM configuration (at `stages`, if given)."""
+def bench_gemm(steps, warmup, stages=None, out_dtype=None, **cfg):
+    """The library's default GEMM configuration (at `stages`, if given); C in
+    fp32, or bf16 through the staged epilogue."""
     import torch
 
     import async_stage_tile_amd as pt
@@ -244,14 +245,17 @@ def bench_gemm(steps, warmup, stages=None):
     n = GEMM_N
     A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device="cuda")
     B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device="cuda")
-    C = torch.empty((n, n), dtype=torch.float32, device="cuda")
-    kw = {} if stages is None else {"stages": stages}
+    C = torch.empty((n, n), dtype=out_dtype or torch.float32, device="cuda")
+    kw = dict(cfg)
+    if stages is not None:
+        kw["stages"] = stages
     fn = pt.gemm_launcher(A, B, C, **kw)
     wall, kern = timed_launches(fn, steps, warmup)
     med, mn = launch_stats(fn, max(steps, 20), 0)
     flops = 2.0 * n * n * n
-    c = pt.make_config(pt.PIPE_OP_GEMM, **kw)
-    return {"stages": c.stages, "producer_waves": c.producer_waves, "flags": c.flags,
+    c = pt._gemm_config(C, kw)
+    return {"c_dtype": str(C.dtype).replace("torch.", ""), "stages": c.stages,
+            "producer_waves": c.producer_waves, "flags": c.flags,
             "wall_ms": wall, "kernel_ms": kern, "flops": flops,
             "tflops": flops / (wall * 1e-3) / 1e12,
             "mfma_frac": flops / (wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -374,7 +378,7 @@ def main():
                          "the copy -- the best of the S sweeps measured on MI355X); 0 = the "
                          "best of this run's 1..4 copy sweep")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--only", choices=["copy", "rowsum", "gemm", "ceiling", "calib"],
+    ap.add_argument("--only", choices=["copy", "rowsum", "gemm", "gemm_bf16", "ceiling", "calib"],
                     default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
@@ -410,6 +414,10 @@ def main():
     if args.only == "gemm":
         r = bench_gemm(args.steps, args.warmup, args.stages)
         log(f"[bench] gemm: {r}")
+        return
+    if args.only == "gemm_bf16":
+        r = bench_gemm(args.steps, args.warmup, args.stages, out_dtype=torch.bfloat16)
+        log(f"[bench] gemm, bf16 C: {r}")
         return
     if args.only == "ceiling":
         r = bench_ceilings(args.steps, args.warmup)
@@ -458,6 +466,13 @@ def main():
         g = bench_gemm(max(3, args.steps // 2), 2)
         log(f"[bench] gemm: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16"] = g
+        g = bench_gemm(max(3, args.steps // 2), 2, out_dtype=torch.bfloat16)
+        log(f"[bench] gemm, bf16 C: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_c_bf16"] = g
+        g = bench_gemm(max(3, args.steps // 2), 2, out_dtype=torch.bfloat16,
+                       flags=pt.PIPE_FLAG_EAGER_NEWEST | pt.PIPE_FLAG_GEMM_STORE_WAVE)
+        log(f"[bench] gemm, bf16 C via a store wave: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_c_bf16_store_wave"] = g
         torch.cuda.empty_cache()
         c = bench_ceilings(max(3, args.steps // 2), 2)
         log(f"[bench] ceilings: copy {c['best_copy_gbs']:.1f}, read {c['best_read_gbs']:.1f} GB/s")

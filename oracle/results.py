@@ -128,6 +128,39 @@ def gemm_f64(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     return A.astype(np.float64) @ B.astype(np.float64)
 
 
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round real values (given as float64) to the nearest bf16, ties to even.
+
+    bf16 keeps 8 significant bits and fp32's exponent range: a normal value
+    m * 2**e (0.5 <= |m| < 1) becomes rint(m * 2**8) * 2**(e - 8); below the
+    smallest normal 2**-126 the quantum is fixed at 2**-133 (subnormals);
+    beyond the largest finite bf16 the result is +-inf. NaN stays NaN.
+    Returns the bf16 values as float32 (every bf16 is exactly an fp32).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    nan = np.isnan(x)
+    m, e = np.frexp(np.where(nan, 0.0, x))
+    normal = np.abs(x) >= 2.0 ** -126
+    q = np.where(normal, np.rint(m * 256.0) * np.ldexp(1.0, e - 8),
+                 np.rint(np.where(nan, 0.0, x) * 2.0 ** 133) * 2.0 ** -133)
+    max_bf16 = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    q = np.where(np.abs(q) > max_bf16, np.copysign(np.inf, q), q)
+    out[...] = np.where(nan, np.nan, q)
+    return out.astype(np.float32)
+
+
+def bf16_bits(values_f32: np.ndarray) -> np.ndarray:
+    """Raw 16-bit codes of bf16 values held exactly in float32."""
+    v = np.ascontiguousarray(values_f32, dtype=np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def gemm_bf16(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """R = round_to_bf16(A @ B): the product rounded once to bf16 (as float32)."""
+    return round_to_bf16(gemm_f64(A, B))
+
+
 def gemm_fraction(A: np.ndarray, B: np.ndarray) -> list:
     """Brute-force exact product as Fractions (tiny shapes only)."""
     M, K = A.shape

@@ -142,6 +142,24 @@ def test_rowsum_and_gemm_validation():
     assert args(256, 256, 128, A=FAKE + 4) == pt.PIPE_ERR_ALIGN
     assert args(256, 256, 128, cfg=pt.make_config(2, stages=5)) == pt.PIPE_ERR_STAGES
     assert args(256, 256, 128, cfg=pt.make_config(2, consumer_waves=3)) == pt.PIPE_ERR_CONFIG
+    # bf16 C: 16-byte aligned base and ldc a multiple of 8
+    bf = pt.make_config(2, flags=pt.PIPE_FLAG_GEMM_C_BF16)
+    assert L.pipe_gemm_mainloop(FAKE, FAKE, FAKE + 4, 256, 256, 128, 128, 256, 256,
+                                ctypes.byref(bf), None) == pt.PIPE_ERR_ALIGN
+    assert L.pipe_gemm_mainloop(FAKE, FAKE, FAKE, 256, 256, 128, 128, 256, 260,
+                                ctypes.byref(bf), None) == pt.PIPE_ERR_ALIGN
+    # the GEMM-only flags are rejected by the stream ops
+    for f in (pt.PIPE_FLAG_GEMM_C_BF16, pt.PIPE_FLAG_GEMM_B_LINEAR):
+        assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=f)) \
+            == pt.PIPE_ERR_CONFIG
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096, flags=pt.PIPE_FLAG_GEMM_C_BF16)
+    assert q["threads"] == 64 * (4 + 4) and 2 * q["lds_bytes"] <= 160 * 1024
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096,
+                             flags=pt.PIPE_FLAG_GEMM_C_BF16 | pt.PIPE_FLAG_GEMM_STORE_WAVE)
+    assert q["threads"] == 64 * (4 + 4 + 1) and 2 * q["lds_bytes"] <= 160 * 1024
+    sw = pt.make_config(2, flags=pt.PIPE_FLAG_GEMM_STORE_WAVE)   # store wave needs bf16 C
+    assert L.pipe_gemm_mainloop(FAKE, FAKE, FAKE, 256, 256, 128, 128, 256, 256,
+                                ctypes.byref(sw), None) == pt.PIPE_ERR_CONFIG
     assert args(0, 256, 128) == pt.PIPE_OK
 
 

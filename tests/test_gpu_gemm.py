@@ -94,3 +94,96 @@ def test_gemm_k_zero_gives_zero():
     pt.pipe_gemm_mainloop(A, B, C)
     torch.cuda.synchronize()
     assert int((C != 0).sum()) == 0
+
+
+def test_gemm_default_config_full_size_sampled_rows():
+    n = 4096
+    A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device=DEV)
+    B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rows = np.random.default_rng(7).choice(n, 48, replace=False)
+    rows.sort()
+    res = R.within_tol(C[rows].cpu().numpy(), R.gemm_f64(_f32(A[rows]), _f32(B)), 1e-2)
+    assert res["ok"], res
+
+
+# ---------------------------------------------------------------- bf16 C (staged epilogue)
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("PW", [2, 4])
+@pytest.mark.parametrize("store_wave", [False, True])
+def test_gemm_bf16_out_small_integers_bit_exact(S, PW, store_wave):
+    """Integer sums are exact in fp32, so rounding them once to bf16 must give
+    exactly the oracle's rounding of the exact product. Entries 0..3 make the
+    sums about 500-2000 (at most 4608), well past bf16's 256 exact integers."""
+    M, N, K = 256, 384, 512
+    A = synth.small_int((M, K), 0, 3, torch.bfloat16, seed=31, stream=0).to(DEV)
+    B = synth.small_int((K, N), 0, 3, torch.bfloat16, seed=31, stream=1).to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    flags = pt.PIPE_FLAG_EAGER_NEWEST | (pt.PIPE_FLAG_GEMM_STORE_WAVE if store_wave else 0)
+    C = pt.pipe_gemm_mainloop(A, B, out_dtype=torch.bfloat16, stages=S, producer_waves=PW, grid=5,
+                              flags=flags, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and C.dtype == torch.bfloat16
+    ref = R.gemm_bf16(_f32(A), _f32(B))
+    got = C.float().cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+    assert np.abs(ref).max() > 256  # rounding was exercised
+
+
+@pytest.mark.parametrize("store_wave", [False, True])
+def test_gemm_bf16_out_uniform_within_tolerance(store_wave):
+    M, N, K = 512, 256, 1024
+    A = synth.uniform((M, K), torch.bfloat16, seed=42, stream=0).to(DEV)
+    B = synth.uniform((K, N), torch.bfloat16, seed=42, stream=1).to(DEV)
+    flags = pt.PIPE_FLAG_EAGER_NEWEST | (pt.PIPE_FLAG_GEMM_STORE_WAVE if store_wave else 0)
+    C16 = pt.pipe_gemm_mainloop(A, B, out_dtype=torch.bfloat16, flags=flags)
+    C32 = pt.pipe_gemm_mainloop(A, B)
+    torch.cuda.synchronize()
+    res = R.within_tol(C16.float().cpu().numpy(), R.gemm_f64(_f32(A), _f32(B)), 1e-2)
+    assert res["ok"], res
+    # the two outputs share the accumulation order: bf16 C is the fp32 C rounded once
+    assert np.array_equal(C16.float().cpu().numpy(), R.round_to_bf16(C32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("store_wave", [False, True])
+def test_gemm_bf16_out_strided_c_persistent_grid(store_wave):
+    M, N, K = 384, 256, 256
+    A = synth.small_int((M, K), 0, 3, torch.bfloat16, seed=33, stream=0).to(DEV)
+    B = synth.small_int((K, N), 0, 3, torch.bfloat16, seed=33, stream=1).to(DEV)
+    base = torch.full((M, N + 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    C = base[:, :N]
+    flags = pt.PIPE_FLAG_EAGER_NEWEST | (pt.PIPE_FLAG_GEMM_STORE_WAVE if store_wave else 0)
+    pt.pipe_gemm_mainloop(A, B, C, grid=2, flags=flags)   # 6 output tiles on 2 workgroups
+    torch.cuda.synchronize()
+    assert np.array_equal(C.float().cpu().numpy(), R.gemm_bf16(_f32(A), _f32(B)))
+    assert bool((base[:, N:] == 7.0).all())
+
+
+@pytest.mark.parametrize("store_wave", [False, True])
+def test_gemm_bf16_out_full_size_sampled_rows(store_wave):
+    n = 4096
+    A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device=DEV)
+    B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    flags = pt.PIPE_FLAG_EAGER_NEWEST | (pt.PIPE_FLAG_GEMM_STORE_WAVE if store_wave else 0)
+    C = pt.pipe_gemm_mainloop(A, B, out_dtype=torch.bfloat16, flags=flags, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rows = np.random.default_rng(11).choice(n, 48, replace=False)
+    rows.sort()
+    ref = R.gemm_f64(_f32(A[rows]), _f32(B))
+    res = R.within_tol(C[rows].float().cpu().numpy(), ref, 1e-2)
+    assert res["ok"], res
+
+
+def test_gemm_bf16_out_k_zero_gives_zero():
+    A = torch.empty((128, 0), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    C = torch.full((128, 256), 3.0, dtype=torch.bfloat16, device=DEV)
+    pt.pipe_gemm_mainloop(A, B, C)
+    torch.cuda.synchronize()
+    assert int((C != 0).sum()) == 0

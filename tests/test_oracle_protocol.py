@@ -191,3 +191,12 @@ def test_eager_commit_lifts_the_lag_bound(S):
 def test_eager_commit_needs_landed_mode():
     with pytest.raises(ValueError):
         P.check_protocol(2, 3, 1, mode="tx", eager_min=1)
+
+
+def test_store_side_ring_of_the_gemm_epilogue():
+    """The bf16 epilogue's staging ring: one slot, two producer waves (an MFMA
+    wave pair writes a chunk, synchronously: lag 0) and one consumer (the store
+    wave), 4 chunks per tile over 3 tiles."""
+    r = P.check_protocol(1, 12, 1, mode="landed", lag=0, producers=2)
+    assert r.completed and not r.deadlock and r.violations == []
+    assert r.max_ahead == 1

@@ -131,3 +131,65 @@ def test_within_tol():
     assert not bad["ok"] and bad["n_bad"] == 1
     nan = R.within_tol(np.array([np.nan, 0, 0, 0]), ref, 1e-3)
     assert not nan["ok"]
+
+
+def test_round_to_bf16_hand_cases():
+    """bf16 has 8 significant bits: in [1, 2) the step is 2**-7."""
+    s = 2.0 ** -7
+    cases = [
+        (1.0, 1.0), (-2.5, -2.5), (0.0, 0.0),
+        (1.0 + s / 2, 1.0),                 # tie -> even (1.0)
+        (1.0 + 3 * s / 2, 1.0 + 2 * s),     # tie -> even (mantissa 2)
+        (1.0 + s / 2 + 2.0 ** -30, 1.0 + s),  # just above the tie rounds up
+        (1.0 + s / 2 - 2.0 ** -30, 1.0),    # just below rounds down
+        (2.0 - 2.0 ** -9, 2.0),             # carry into the exponent
+        (-(1.0 + 3 * s / 2), -(1.0 + 2 * s)),
+        (255.0, 255.0), (257.0, 256.0), (259.0, 260.0),  # integers above 2**8: step 2
+        (16384.0 + 31.0, 16384.0 + 0.0),    # step 128 at 2**14: 16415 -> 16384
+        (16384.0 + 64.0, 16384.0),          # tie -> even
+        (16384.0 + 192.0, 16384.0 + 256.0),  # tie -> even
+        (3 * 2.0 ** -133, 3 * 2.0 ** -133),  # subnormal, exact
+        (2.5 * 2.0 ** -133, 2.0 * 2.0 ** -133),  # subnormal tie -> even
+        (3.5 * 2.0 ** -133, 4.0 * 2.0 ** -133),
+        (2.0 ** -126, 2.0 ** -126),
+        (3.5e38, np.inf), (-3.5e38, -np.inf),
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases], dtype=np.float32)
+    got = R.round_to_bf16(x)
+    assert np.array_equal(got, want), list(zip(x, got, want))
+    assert np.isnan(R.round_to_bf16(np.array([np.nan]))[0])
+    # the result is always representable: its low 16 fp32 bits are zero
+    assert np.all(got.view(np.uint32)[np.isfinite(got)] & 0xFFFF == 0)
+    assert R.bf16_bits(np.array([1.0, -2.0], dtype=np.float32)).tolist() == [0x3F80, 0xC000]
+
+
+def test_round_to_bf16_matches_torch_conversion_of_fp32():
+    """For fp32 inputs there is no double rounding: the oracle's rounding of the
+    exact value must equal torch's (independent) fp32 -> bf16 conversion."""
+    g = torch.Generator().manual_seed(0)
+    v = torch.randn(200000, generator=g, dtype=torch.float32) * torch.exp2(
+        torch.randint(-40, 40, (200000,), generator=g).float())
+    ties = (torch.arange(4096, dtype=torch.int32) << 16) | 0x8000  # exact halfway codes
+    v = torch.cat([v, ties.view(torch.float32)[torch.isfinite(ties.view(torch.float32))]])
+    ref = v.to(torch.bfloat16).float().numpy()
+    got = R.round_to_bf16(v.double().numpy())
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_gemm_bf16_is_rounded_exact_product():
+    A = synth.small_int((64, 96), -2, 2, torch.bfloat16, seed=21).float().numpy()
+    B = synth.small_int((96, 32), -2, 2, torch.bfloat16, seed=22).float().numpy()
+    exact = R.gemm_fraction(A, B)
+    got = R.gemm_bf16(A, B)
+    for i in range(0, 64, 7):
+        for j in range(0, 32, 5):
+            e = exact[i][j]
+            assert e.denominator == 1
+            # integers: exact below 2**8, else the nearest multiple of the step
+            v = int(e)
+            step = 1 if abs(v) < 256 else 2 ** (abs(v).bit_length() - 8)
+            q, r = divmod(abs(v), step)
+            if 2 * r > step or (2 * r == step and q % 2 == 1):
+                q += 1
+            assert got[i, j] == np.float32((1 if v >= 0 else -1) * q * step)
