@@ -211,11 +211,12 @@ def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):
     Md, Nd, ld_dst = _check_matrix(dst, "dst", (src.dtype,))
     if (Md, Nd) != (M, N):
         raise ValueError("dst shape differs from src")
-    chk = None
-    if checksums:
-        chk = torch.empty(((M + 127) // 128) * ((N + 63) // 64), dtype=torch.int32,
-                          device=src.device)
     c = make_config(PIPE_OP_COPY, **cfg)
+    chk = None
+    if checksums:   # one word per tile of the configured shape
+        tm, tn = max(1, c.tile_m), max(1, c.tile_n)
+        chk = torch.empty(((M + tm - 1) // tm) * ((N + tn - 1) // tn), dtype=torch.int32,
+                          device=src.device)
     st = lib().pipe_tile_copy(_ptr(src), _ptr(dst), M, N, ld_src, ld_dst, ctypes.byref(c),
                               _ptr(chk), _stream(stream))
     _check(st, "pipe_tile_copy")

@@ -110,15 +110,18 @@ pipe_status_t check_stream_cfg(const pipe_config_t& c) {
   if (c.flags & (PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_GEMM_STORE_WAVE))
     return PIPE_ERR_CONFIG;
   if (c.stages < 1 || c.stages > 8) return PIPE_ERR_STAGES;
-  if (c.tile_m != 128 || c.tile_n != 64) return PIPE_ERR_CONFIG;
+  // 16 KiB tiles: the pages' 128 x 64, or the wider 64 x 128 and 32 x 256.
+  if (!((c.tile_m == 128 && c.tile_n == 64) || (c.tile_m == 64 && c.tile_n == 128) ||
+        (c.tile_m == 32 && c.tile_n == 256)))
+    return PIPE_ERR_CONFIG;
   const int cw = c.consumer_waves, pw = c.producer_waves;
   if (c.flags & PIPE_FLAG_UNIFIED) {
-    if (!(cw == 2 || cw == 4 || cw == 8)) return PIPE_ERR_CONFIG;
+    if (!unified_shape_supported(c.stages, cw, c.tile_n)) return PIPE_ERR_CONFIG;
     return c.stages * 16384 > kLdsLimit ? PIPE_ERR_STAGES : PIPE_OK;
   }
   if (!(pw == 1 || pw == 2 || pw == 4)) return PIPE_ERR_CONFIG;
   if (!(cw == 1 || cw == 2 || cw == 3 || cw == 4 || cw == 8)) return PIPE_ERR_CONFIG;
-  if (!stream_shape_supported(c.stages, cw, pw)) return PIPE_ERR_CONFIG;
+  if (!stream_shape_supported(c.stages, cw, pw, c.tile_n)) return PIPE_ERR_CONFIG;
   if (stream_lds_bytes(c.stages, cw) > kLdsLimit) return PIPE_ERR_STAGES;
   return PIPE_OK;
 }
@@ -130,7 +133,7 @@ pipe_status_t check_unified(const pipe_config_t& c, int64_t M, int64_t N, bool c
   if (checksums || (c.flags & (PIPE_FLAG_TRACE | PIPE_FLAG_TEST_START_PHASE0 |
                                PIPE_FLAG_TEST_NO_RELEASE)))
     return PIPE_ERR_CONFIG;
-  if (M % 128 != 0 || N % 64 != 0) return PIPE_ERR_CONFIG;
+  if (M % c.tile_m != 0 || N % c.tile_n != 0) return PIPE_ERR_CONFIG;
   return PIPE_OK;
 }
 
@@ -148,7 +151,7 @@ int rowsum_default_split(int n_strips, int strip_len) {
 
 pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool row_strips,
                               bool rowsum, StreamGeom* g) {
-  const int64_t tr = (M + 127) / 128, tc = (N + 63) / 64;
+  const int64_t tr = (M + c.tile_m - 1) / c.tile_m, tc = (N + c.tile_n - 1) / c.tile_n;
   if (tr > INT32_MAX || tc > INT32_MAX) return PIPE_ERR_SHAPE;
   g->tile_rows = (int32_t)tr;
   g->tile_cols = (int32_t)tc;
@@ -266,10 +269,10 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
   if (unified)
-    return hip_status(launch_unified(kOpCopy, c.stages, c.consumer_waves, g.grid, p,
+    return hip_status(launch_unified(kOpCopy, c.stages, c.consumer_waves, c.tile_n, g.grid, p,
                                      static_cast<hipStream_t>(stream)));
-  return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, c.producer_waves, g.grid, p,
-                                  static_cast<hipStream_t>(stream)));
+  return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, c.producer_waves, c.tile_n,
+                                  g.grid, p, static_cast<hipStream_t>(stream)));
 }
 
 pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_config_t* cfg,
@@ -329,9 +332,10 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  s = unified ? hip_status(launch_unified(kOpRowsum, c.stages, c.consumer_waves, g.grid, p, st))
+  s = unified ? hip_status(launch_unified(kOpRowsum, c.stages, c.consumer_waves, c.tile_n, g.grid,
+                                          p, st))
               : hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, c.producer_waves,
-                                         g.grid, p, st));
+                                         c.tile_n, g.grid, p, st));
   if (s != PIPE_OK || need == 0) return s;
   return hip_status(launch_rowsum_finalize(static_cast<const float*>(workspace), out, M,
                                            g.split, st));

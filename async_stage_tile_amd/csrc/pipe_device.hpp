@@ -51,6 +51,22 @@ constexpr int kRowsPerBlock = kBlockBytes / kRowBytes;    // 8
 
 constexpr uint32_t kPhaseBit = 0x80000000u;
 
+// Tile shapes of the stream kernels. Every tile is 16 KiB: kRows x TC fp16
+// with TC (tileN) in {64, 128, 256} and kRows (tileM) = 128, 64, 32. One
+// wave-wide DMA moves kBlockBytes = 1 KiB, i.e. kRowsPerBlock rows of
+// kChunksPerRow 16-byte chunks. TC = 64 is the pages' 128 x 64 tile.
+template <int TC>
+struct TileShape {
+  static constexpr int kCols = TC;
+  static constexpr int kRowBytes = TC * 2;
+  static constexpr int kChunksPerRow = kRowBytes / kChunkBytes;
+  static constexpr int kLog2ChunksPerRow = kChunksPerRow == 8 ? 3 : kChunksPerRow == 16 ? 4 : 5;
+  static constexpr int kRows = kTileBytes / kRowBytes;
+  static constexpr int kRowsPerBlock = kBlockBytes / kRowBytes;
+  static_assert(kRowsPerBlock >= 1 && (1 << kLog2ChunksPerRow) == kChunksPerRow,
+                "a tile row is 8, 16 or 32 chunks within one wave-wide DMA");
+};
+
 // Status bits written to the caller's status word.
 constexpr uint32_t kStatusTimeoutProducer = 1u;
 constexpr uint32_t kStatusTimeoutConsumer = 2u;
@@ -222,6 +238,13 @@ __device__ __forceinline__ int swz(int r, int c, int shift) {
   return c ^ ((r >> shift) & (kChunksPerRow - 1));
 }
 
+// The same XOR over a row of CPR chunks (wider tiles): position -> chunk and
+// chunk -> position alike.
+template <int CPR>
+__device__ __forceinline__ int swz_n(int r, int c, int shift) {
+  return c ^ ((r >> shift) & (CPR - 1));
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane sums.
 // ---------------------------------------------------------------------------
@@ -233,6 +256,15 @@ __device__ __forceinline__ float sum8_lanes(float v) {
   v += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
   x = __float_as_int(v);
   v += __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false)); // row_half_mirror
+  return v;
+}
+
+// Sum over each aligned group of CPR lanes (8, 16 or 32), result in every lane.
+template <int CPR>
+__device__ __forceinline__ float sum_lanes(float v) {
+  v = sum8_lanes(v);
+  if constexpr (CPR >= 16) v += __shfl_xor(v, 8, kWave);
+  if constexpr (CPR >= 32) v += __shfl_xor(v, 16, kWave);
   return v;
 }
 

@@ -39,12 +39,17 @@ struct StreamParams {
   int32_t eager;          // eager commits while the acquire waits: min tiles in flight (0 = off)
 };
 
-// Ring shapes (stages S, consumer waves C, producer waves PW) the stream
-// kernel is instantiated for: PW in {1, 2, 4}; C in {1, 2, 3, 4, 8} for
-// S = 1..4, and C in {4, 8} for the deep rings S = 5..8.
-constexpr bool stream_shape_supported(int S, int C, int PW) {
+// Ring shapes (stages S, consumer waves C, producer waves PW, tile columns TC)
+// the stream kernel is instantiated for. The pages' 128 x 64 tile (TC = 64):
+// PW in {1, 2, 4}; C in {1, 2, 3, 4, 8} for S = 1..4, and C in {4, 8} for the
+// deep rings S = 5..8. The wider 16 KiB tiles 64 x 128 and 32 x 256
+// (TC = 128, 256): S = 2..4, PW in {2, 4}, C in {4, 8}.
+constexpr bool stream_shape_supported(int S, int C, int PW, int TC = 64) {
   if (S < 1 || S > 8) return false;
   if (!(PW == 1 || PW == 2 || PW == 4)) return false;
+  if (TC == 128 || TC == 256)
+    return S >= 2 && S <= 4 && (PW == 2 || PW == 4) && (C == 4 || C == 8);
+  if (TC != 64) return false;
   if (S > 4) return C == 4 || C == 8;
   return C == 1 || C == 2 || C == 3 || C == 4 || C == 8;
 }
@@ -53,21 +58,27 @@ constexpr bool stream_shape_supported(int S, int C, int PW) {
 // tile and (lag + 1) tiles of them must fit the 63-entry vmcnt counter.
 constexpr int stream_max_lag(int PW) { return 63 / (16 / PW) - 1; }
 
-// Launch the stream kernel for (op, stages, consumers, producers). Returns
-// hipSuccess or the launch error (hipErrorInvalidValue for a shape that is not
-// instantiated). `grid` workgroups of 64 * (producers + consumers) threads.
-hipError_t launch_stream(int op, int stages, int consumers, int producers, int grid,
+// Launch the stream kernel for (op, stages, consumers, producers, tile
+// columns). Returns hipSuccess or the launch error (hipErrorInvalidValue for a
+// shape that is not instantiated). `grid` workgroups of 64 * (producers +
+// consumers) threads.
+hipError_t launch_stream(int op, int stages, int consumers, int producers, int tile_n, int grid,
                          const StreamParams& p, hipStream_t stream);
 template <int S>
-hipError_t launch_stream_stages(int op, int consumers, int producers, int grid,
+hipError_t launch_stream_stages(int op, int consumers, int producers, int tile_n, int grid,
                                 const StreamParams& p, hipStream_t stream);
 int stream_lds_bytes(int stages, int consumers);
 
-// Unified variant: `waves` waves (2, 4 or 8) each load and consume 16 / waves
-// blocks of every tile; stages 1..8; divisible shapes only, no checksums or
-// trace.
-hipError_t launch_unified(int op, int stages, int waves, int grid, const StreamParams& p,
-                          hipStream_t stream);
+// Unified variant: `waves` waves each load and consume 16 / waves blocks of
+// every tile; divisible shapes only, no checksums or trace. 128 x 64 tiles:
+// waves 2, 4 or 8, stages 1..8; wider tiles: waves 2 or 4, stages 2..4.
+constexpr bool unified_shape_supported(int S, int W, int TC) {
+  if (TC == 64) return S >= 1 && S <= 8 && (W == 2 || W == 4 || W == 8);
+  if (TC == 128 || TC == 256) return S >= 2 && S <= 4 && (W == 2 || W == 4);
+  return false;
+}
+hipError_t launch_unified(int op, int stages, int waves, int tile_n, int grid,
+                          const StreamParams& p, hipStream_t stream);
 
 hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
                                   hipStream_t stream);

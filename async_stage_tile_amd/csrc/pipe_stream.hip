@@ -104,28 +104,32 @@ __device__ __forceinline__ int item_len(const StreamParams& p, int item) {
   return len < p.seg_len ? len : p.seg_len;
 }
 
-// Rows and columns of tile (tr, tc) inside the matrix (128 and 64 except at
+// Rows and columns of tile (tr, tc) inside the matrix (the full tile except at
 // ragged edges); wave-uniform.
+template <int TC>
 __device__ __forceinline__ int rows_in(const StreamParams& p, int tr) {
-  const int64_t left = p.M - (int64_t)tr * kTileRows;
-  return left < kTileRows ? (int)left : kTileRows;
+  constexpr int R = TileShape<TC>::kRows;
+  const int64_t left = p.M - (int64_t)tr * R;
+  return left < R ? (int)left : R;
 }
+template <int TC>
 __device__ __forceinline__ int cols_in(const StreamParams& p, int tc) {
-  const int64_t left = p.N - (int64_t)tc * kTileCols;
-  return left < kTileCols ? (int)left : kTileCols;
+  const int64_t left = p.N - (int64_t)tc * TC;
+  return left < TC ? (int)left : TC;
 }
 
 // ---------------------------------------------------------------------------
 // Producer waves
 // ---------------------------------------------------------------------------
-template <int S, int C, int PW, bool MASKED>
+template <int S, int C, int PW, bool MASKED, int TC>
 __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
+  using Sh = TileShape<TC>;
   constexpr int kLoads = kBlocksPerTile / PW;  // DMA instructions per tile per wave
   static_assert((stream_max_lag(PW) + 1) * kLoads <= 63,
                 "vmcnt counts at most 63 outstanding loads");
   const int lane = lane_id();
-  const int lrow = lane >> 3;  // row within a 1 KiB block
-  const int lpos = lane & 7;   // chunk position within the row
+  const int lrow = lane >> Sh::kLog2ChunksPerRow;  // row within a 1 KiB block
+  const int lpos = lane & (Sh::kChunksPerRow - 1);  // chunk position within the row
   const int lag = p.lag;
   PipeState w = producer_start(S, p.start_phase);
   int pending = 0;  // tiles issued but not yet committed (their full not arrived)
@@ -146,15 +150,16 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
       if (pw == 0) trace_record(p, t, 0, w, 0);
       int tr, tc;
       tile_coords(p, item, k, tr, tc);
-      const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc * kRowBytes;
+      const uint8_t* g =
+          p.src + (int64_t)tr * Sh::kRows * p.ld_src + (int64_t)tc * Sh::kRowBytes;
       const uint32_t slot = uniform(lds_addr(&lds.slots[w.index][0]));
       if constexpr (MASKED) {
-        const int rin = rows_in(p, tr), cin = cols_in(p, tc);
+        const int rin = rows_in<TC>(p, tr), cin = cols_in<TC>(p, tc);
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
           const int q = pw * kLoads + j;
-          const int r = q * kRowsPerBlock + lrow;
-          const int c = swz(r, lpos, p.swz_shift);
+          const int r = q * Sh::kRowsPerBlock + lrow;
+          const int c = swz_n<Sh::kChunksPerRow>(r, lpos, p.swz_shift);
           const uint8_t* a = g + (int64_t)r * p.ld_src + c * kChunkBytes;
           dma_block((r < rin && c * 8 < cin) ? a : p.src, slot + q * kBlockBytes);
         }
@@ -162,16 +167,16 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
           const int q = pw * kLoads + j;
-          const int r = q * kRowsPerBlock + lrow;
-          const int c = swz(r, lpos, p.swz_shift);
+          const int r = q * Sh::kRowsPerBlock + lrow;
+          const int c = swz_n<Sh::kChunksPerRow>(r, lpos, p.swz_shift);
           dma_block_nt(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
           const int q = pw * kLoads + j;
-          const int r = q * kRowsPerBlock + lrow;
-          const int c = swz(r, lpos, p.swz_shift);
+          const int r = q * Sh::kRowsPerBlock + lrow;
+          const int c = swz_n<Sh::kChunksPerRow>(r, lpos, p.swz_shift);
           dma_block(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
         }
       }
@@ -213,12 +218,13 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
 // ---------------------------------------------------------------------------
 // Consumer waves
 // ---------------------------------------------------------------------------
-template <int S, int C, int OP, bool MASKED>
+template <int S, int C, int OP, bool MASKED, int TC>
 __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
+  using Sh = TileShape<TC>;
   constexpr int NB = (kBlocksPerTile + C - 1) / C;  // blocks per wave (last may idle)
   const int lane = lane_id();
-  const int lrow = lane >> 3;
-  const int lpos = lane & 7;
+  const int lrow = lane >> Sh::kLog2ChunksPerRow;
+  const int lpos = lane & (Sh::kChunksPerRow - 1);
   PipeState rd = consumer_start(S);
   float acc[NB];
 #pragma unroll
@@ -238,10 +244,10 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
       }
       if (cw == 0) trace_record(p, t, 1, rd, 1 + cw);
       tile_coords(p, item, k, tr, tc);
-      int rin = kTileRows, cin = kTileCols;
+      int rin = Sh::kRows, cin = TC;
       if constexpr (MASKED) {
-        rin = rows_in(p, tr);
-        cin = cols_in(p, tc);
+        rin = rows_in<TC>(p, tr);
+        cin = cols_in<TC>(p, tc);
       }
       const uint8_t* slot = &lds.slots[rd.index][0];
       uint4 v[NB];
@@ -257,13 +263,13 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
         for (int j = 0; j < NB; ++j) {
           const int q = cw + j * C;
           if (q < kBlocksPerTile) {
-            const int r = q * kRowsPerBlock + lrow;
-            const int c = swz(r, lpos, p.swz_shift);
+            const int r = q * Sh::kRowsPerBlock + lrow;
+            const int c = swz_n<Sh::kChunksPerRow>(r, lpos, p.swz_shift);
             if constexpr (MASKED) {
               if (r >= rin || c * 8 >= cin) continue;
             }
-            uint8_t* gd = p.dst + ((int64_t)tr * kTileRows + r) * p.ld_dst +
-                          (int64_t)tc * kRowBytes + c * kChunkBytes;
+            uint8_t* gd = p.dst + ((int64_t)tr * Sh::kRows + r) * p.ld_dst +
+                          (int64_t)tc * Sh::kRowBytes + c * kChunkBytes;
             if (p.nt) {
               const u32x4 nv = {v[j].x, v[j].y, v[j].z, v[j].w};
               __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(gd));
@@ -304,8 +310,8 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
           if (q < kBlocksPerTile) {
             if constexpr (MASKED) {
               // Position lpos of row r holds logical chunk swz(r, lpos).
-              const int r = q * kRowsPerBlock + lrow;
-              if (r >= rin || swz(r, lpos, p.swz_shift) * 8 >= cin) continue;
+              const int r = q * Sh::kRowsPerBlock + lrow;
+              if (r >= rin || swz_n<Sh::kChunksPerRow>(r, lpos, p.swz_shift) * 8 >= cin) continue;
             }
             const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
             float s = 0.f;
@@ -328,14 +334,14 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
     if constexpr (OP == kOpRowsum) {
       if (ok && len > 0) {
         const int seg = item / p.n_strips;
-        float* o = p.out + (int64_t)seg * p.M + (int64_t)tr * kTileRows;
+        float* o = p.out + (int64_t)seg * p.M + (int64_t)tr * Sh::kRows;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int q = cw + j * C;
           if (q < kBlocksPerTile) {
-            const float s = sum8_lanes(acc[j]);
-            const int r = q * kRowsPerBlock + lrow;
-            if (lpos == 0 && (!MASKED || (int64_t)tr * kTileRows + r < p.M)) o[r] = s;
+            const float s = sum_lanes<Sh::kChunksPerRow>(acc[j]);
+            const int r = q * Sh::kRowsPerBlock + lrow;
+            if (lpos == 0 && (!MASKED || (int64_t)tr * Sh::kRows + r < p.M)) o[r] = s;
           }
           acc[j] = 0.f;
         }
@@ -345,7 +351,7 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int C, int PW, int OP, bool MASKED>
+template <int S, int C, int PW, int OP, bool MASKED, int TC>
 __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
   __shared__ StreamLds<S, C> lds;
   const int wave = (int)(threadIdx.x >> 6);
@@ -356,60 +362,72 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
   }
   __syncthreads();
   if (wave < PW)
-    producer<S, C, PW, MASKED>(p, lds, wave);
+    producer<S, C, PW, MASKED, TC>(p, lds, wave);
   else
-    consumer<S, C, OP, MASKED>(p, lds, wave - PW);
+    consumer<S, C, OP, MASKED, TC>(p, lds, wave - PW);
 }
 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int S, int C, int PW>
-static hipError_t launch_scp(int op, int grid, const StreamParams& p, hipStream_t stream) {
-  if constexpr (!stream_shape_supported(S, C, PW)) {
+template <int S, int C, int PW, int TC>
+static hipError_t launch_scpt(int op, int grid, const StreamParams& p, hipStream_t stream) {
+  if constexpr (!stream_shape_supported(S, C, PW, TC)) {
     return hipErrorInvalidValue;
   } else {
+    constexpr int R = TileShape<TC>::kRows;
     dim3 block(64 * (PW + C));
-    const bool masked = (p.M % kTileRows) != 0 || (p.N % kTileCols) != 0;
+    const bool masked = (p.M % R) != 0 || (p.N % TC) != 0;
     if (op == kOpCopy) {
       if (masked)
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, true>), dim3(grid), block, 0,
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, true, TC>), dim3(grid), block, 0,
                            stream, p);
       else
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, false>), dim3(grid), block, 0,
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, false, TC>), dim3(grid), block, 0,
                            stream, p);
     } else {
       if (masked)
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, true>), dim3(grid), block, 0,
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, true, TC>), dim3(grid), block, 0,
                            stream, p);
       else
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, false>), dim3(grid), block, 0,
-                           stream, p);
+        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, false, TC>), dim3(grid), block,
+                           0, stream, p);
     }
     return hipGetLastError();
   }
 }
 
+template <int S, int C, int PW>
+static hipError_t launch_scp(int op, int tile_n, int grid, const StreamParams& p,
+                             hipStream_t stream) {
+  switch (tile_n) {
+    case 64: return launch_scpt<S, C, PW, 64>(op, grid, p, stream);
+    case 128: return launch_scpt<S, C, PW, 128>(op, grid, p, stream);
+    case 256: return launch_scpt<S, C, PW, 256>(op, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int S, int C>
-static hipError_t launch_sc(int op, int pw, int grid, const StreamParams& p,
+static hipError_t launch_sc(int op, int pw, int tile_n, int grid, const StreamParams& p,
                             hipStream_t stream) {
   switch (pw) {
-    case 1: return launch_scp<S, C, 1>(op, grid, p, stream);
-    case 2: return launch_scp<S, C, 2>(op, grid, p, stream);
-    case 4: return launch_scp<S, C, 4>(op, grid, p, stream);
+    case 1: return launch_scp<S, C, 1>(op, tile_n, grid, p, stream);
+    case 2: return launch_scp<S, C, 2>(op, tile_n, grid, p, stream);
+    case 4: return launch_scp<S, C, 4>(op, tile_n, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int S>
-hipError_t launch_stream_stages(int op, int consumers, int producers, int grid,
+hipError_t launch_stream_stages(int op, int consumers, int producers, int tile_n, int grid,
                                 const StreamParams& p, hipStream_t stream) {
   switch (consumers) {
-    case 1: return launch_sc<S, 1>(op, producers, grid, p, stream);
-    case 2: return launch_sc<S, 2>(op, producers, grid, p, stream);
-    case 3: return launch_sc<S, 3>(op, producers, grid, p, stream);
-    case 4: return launch_sc<S, 4>(op, producers, grid, p, stream);
-    case 8: return launch_sc<S, 8>(op, producers, grid, p, stream);
+    case 1: return launch_sc<S, 1>(op, producers, tile_n, grid, p, stream);
+    case 2: return launch_sc<S, 2>(op, producers, tile_n, grid, p, stream);
+    case 3: return launch_sc<S, 3>(op, producers, tile_n, grid, p, stream);
+    case 4: return launch_sc<S, 4>(op, producers, tile_n, grid, p, stream);
+    case 8: return launch_sc<S, 8>(op, producers, tile_n, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -417,8 +435,8 @@ hipError_t launch_stream_stages(int op, int consumers, int producers, int grid,
 #if !defined(PIPE_STREAM_STAGES_LO) || !defined(PIPE_STREAM_STAGES_HI)
 #error "build with -DPIPE_STREAM_STAGES_LO=<s> -DPIPE_STREAM_STAGES_HI=<s>"
 #endif
-#define PIPE_STREAM_INSTANTIATE(S)                                                      \
-  template hipError_t launch_stream_stages<S>(int, int, int, int, const StreamParams&, \
+#define PIPE_STREAM_INSTANTIATE(S)                                                           \
+  template hipError_t launch_stream_stages<S>(int, int, int, int, int, const StreamParams&, \
                                               hipStream_t);
 #if PIPE_STREAM_STAGES_LO <= 1 && 1 <= PIPE_STREAM_STAGES_HI
 PIPE_STREAM_INSTANTIATE(1)

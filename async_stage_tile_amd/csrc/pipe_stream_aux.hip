@@ -6,17 +6,17 @@
 
 namespace pipe {
 
-hipError_t launch_stream(int op, int stages, int consumers, int producers, int grid,
+hipError_t launch_stream(int op, int stages, int consumers, int producers, int tile_n, int grid,
                          const StreamParams& p, hipStream_t stream) {
   switch (stages) {
-    case 1: return launch_stream_stages<1>(op, consumers, producers, grid, p, stream);
-    case 2: return launch_stream_stages<2>(op, consumers, producers, grid, p, stream);
-    case 3: return launch_stream_stages<3>(op, consumers, producers, grid, p, stream);
-    case 4: return launch_stream_stages<4>(op, consumers, producers, grid, p, stream);
-    case 5: return launch_stream_stages<5>(op, consumers, producers, grid, p, stream);
-    case 6: return launch_stream_stages<6>(op, consumers, producers, grid, p, stream);
-    case 7: return launch_stream_stages<7>(op, consumers, producers, grid, p, stream);
-    case 8: return launch_stream_stages<8>(op, consumers, producers, grid, p, stream);
+    case 1: return launch_stream_stages<1>(op, consumers, producers, tile_n, grid, p, stream);
+    case 2: return launch_stream_stages<2>(op, consumers, producers, tile_n, grid, p, stream);
+    case 3: return launch_stream_stages<3>(op, consumers, producers, tile_n, grid, p, stream);
+    case 4: return launch_stream_stages<4>(op, consumers, producers, tile_n, grid, p, stream);
+    case 5: return launch_stream_stages<5>(op, consumers, producers, tile_n, grid, p, stream);
+    case 6: return launch_stream_stages<6>(op, consumers, producers, tile_n, grid, p, stream);
+    case 7: return launch_stream_stages<7>(op, consumers, producers, tile_n, grid, p, stream);
+    case 8: return launch_stream_stages<8>(op, consumers, producers, tile_n, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -82,14 +82,15 @@ struct Marks {
   }
 };
 
-template <int S, int W, int OP>
+template <int S, int W, int OP, int TC>
 __global__ void __launch_bounds__(64 * W) unified_kernel(StreamParams p) {
+  using Sh = TileShape<TC>;
   __shared__ uint8_t slots[S][kTileBytes];
   constexpr int kLoads = kBlocksPerTile / W;  // blocks loaded and consumed per wave per tile
   constexpr int kStores = OP == kOpCopy ? kLoads : 0;
   const int wave = (int)(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int lrow = lane >> 3, lpos = lane & 7;
+  const int lrow = lane >> Sh::kLog2ChunksPerRow, lpos = lane & (Sh::kChunksPerRow - 1);
 
   Walk iss, use;
   iss.start(p);
@@ -104,14 +105,14 @@ __global__ void __launch_bounds__(64 * W) unified_kernel(StreamParams p) {
   auto issue = [&]() {
     int tr, tc;
     iss.coords(p, tr, tc);
-    const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc * kRowBytes;
+    const uint8_t* g = p.src + (int64_t)tr * Sh::kRows * p.ld_src + (int64_t)tc * Sh::kRowBytes;
     const int s = issued % S;
     const uint32_t slot = uniform(lds_addr(&slots[s][0]));
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int q = wave * kLoads + j;
-      const int r = q * kRowsPerBlock + lrow;
-      const int c = swz(r, lpos, p.swz_shift);
+      const int r = q * Sh::kRowsPerBlock + lrow;
+      const int c = swz_n<Sh::kChunksPerRow>(r, lpos, p.swz_shift);
       if (p.nt)
         dma_block_nt(g + (int64_t)r * p.ld_src + c * kChunkBytes, slot + q * kBlockBytes);
       else
@@ -144,11 +145,11 @@ __global__ void __launch_bounds__(64 * W) unified_kernel(StreamParams p) {
     int tr, tc;
     use.coords(p, tr, tc);
     if constexpr (OP == kOpCopy) {
-      uint8_t* gd = p.dst + (int64_t)tr * kTileRows * p.ld_dst + (int64_t)tc * kRowBytes;
+      uint8_t* gd = p.dst + (int64_t)tr * Sh::kRows * p.ld_dst + (int64_t)tc * Sh::kRowBytes;
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
-        const int r = (wave * kLoads + j) * kRowsPerBlock + lrow;
-        const int c = swz(r, lpos, p.swz_shift);
+        const int r = (wave * kLoads + j) * Sh::kRowsPerBlock + lrow;
+        const int c = swz_n<Sh::kChunksPerRow>(r, lpos, p.swz_shift);
         uint8_t* a = gd + ((int64_t)r * p.ld_dst + c * kChunkBytes);
         if (p.nt) {
           const u32x4 nv = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -172,11 +173,11 @@ __global__ void __launch_bounds__(64 * W) unified_kernel(StreamParams p) {
       }
       if (use.last_of_item()) {
         const int seg = use.item / p.n_strips;
-        float* o = p.out + (int64_t)seg * p.M + (int64_t)tr * kTileRows;
+        float* o = p.out + (int64_t)seg * p.M + (int64_t)tr * Sh::kRows;
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-          const float r8 = sum8_lanes(acc[j]);
-          if (lpos == 0) o[(wave * kLoads + j) * kRowsPerBlock + lrow] = r8;
+          const float rs = sum_lanes<Sh::kChunksPerRow>(acc[j]);
+          if (lpos == 0) o[(wave * kLoads + j) * Sh::kRowsPerBlock + lrow] = rs;
           acc[j] = 0.f;
         }
         // These partial stores are left out of `vm`: counting fewer operations
@@ -188,39 +189,55 @@ __global__ void __launch_bounds__(64 * W) unified_kernel(StreamParams p) {
   wait_vmcnt<0>();
 }
 
+template <int S, int W, int TC>
+hipError_t launch_swt(int op, int grid, const StreamParams& p, hipStream_t stream) {
+  if constexpr (!unified_shape_supported(S, W, TC)) {
+    return hipErrorInvalidValue;
+  } else {
+    if (op == kOpCopy)
+      hipLaunchKernelGGL((unified_kernel<S, W, kOpCopy, TC>), dim3(grid), dim3(64 * W), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((unified_kernel<S, W, kOpRowsum, TC>), dim3(grid), dim3(64 * W), 0,
+                         stream, p);
+    return hipGetLastError();
+  }
+}
+
 template <int S, int W>
-hipError_t launch_sw(int op, int grid, const StreamParams& p, hipStream_t stream) {
-  if (op == kOpCopy)
-    hipLaunchKernelGGL((unified_kernel<S, W, kOpCopy>), dim3(grid), dim3(64 * W), 0, stream, p);
-  else
-    hipLaunchKernelGGL((unified_kernel<S, W, kOpRowsum>), dim3(grid), dim3(64 * W), 0, stream,
-                       p);
-  return hipGetLastError();
+hipError_t launch_sw(int op, int tile_n, int grid, const StreamParams& p, hipStream_t stream) {
+  switch (tile_n) {
+    case 64: return launch_swt<S, W, 64>(op, grid, p, stream);
+    case 128: return launch_swt<S, W, 128>(op, grid, p, stream);
+    case 256: return launch_swt<S, W, 256>(op, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int S>
-hipError_t launch_s(int op, int waves, int grid, const StreamParams& p, hipStream_t stream) {
+hipError_t launch_s(int op, int waves, int tile_n, int grid, const StreamParams& p,
+                    hipStream_t stream) {
   switch (waves) {
-    case 2: return launch_sw<S, 2>(op, grid, p, stream);
-    case 4: return launch_sw<S, 4>(op, grid, p, stream);
-    case 8: return launch_sw<S, 8>(op, grid, p, stream);
+    case 2: return launch_sw<S, 2>(op, tile_n, grid, p, stream);
+    case 4: return launch_sw<S, 4>(op, tile_n, grid, p, stream);
+    case 8: return launch_sw<S, 8>(op, tile_n, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_unified(int op, int stages, int waves, int grid, const StreamParams& p,
-                          hipStream_t stream) {
+hipError_t launch_unified(int op, int stages, int waves, int tile_n, int grid,
+                          const StreamParams& p, hipStream_t stream) {
   switch (stages) {
-    case 1: return launch_s<1>(op, waves, grid, p, stream);
-    case 2: return launch_s<2>(op, waves, grid, p, stream);
-    case 3: return launch_s<3>(op, waves, grid, p, stream);
-    case 4: return launch_s<4>(op, waves, grid, p, stream);
-    case 5: return launch_s<5>(op, waves, grid, p, stream);
-    case 6: return launch_s<6>(op, waves, grid, p, stream);
-    case 7: return launch_s<7>(op, waves, grid, p, stream);
-    case 8: return launch_s<8>(op, waves, grid, p, stream);
+    case 1: return launch_s<1>(op, waves, tile_n, grid, p, stream);
+    case 2: return launch_s<2>(op, waves, tile_n, grid, p, stream);
+    case 3: return launch_s<3>(op, waves, tile_n, grid, p, stream);
+    case 4: return launch_s<4>(op, waves, tile_n, grid, p, stream);
+    case 5: return launch_s<5>(op, waves, tile_n, grid, p, stream);
+    case 6: return launch_s<6>(op, waves, tile_n, grid, p, stream);
+    case 7: return launch_s<7>(op, waves, tile_n, grid, p, stream);
+    case 8: return launch_s<8>(op, waves, tile_n, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

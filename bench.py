@@ -61,6 +61,23 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "copy_16384x16384_counters.md")
 KERNEL_SOURCES = ("pipe_device.hpp", "pipe_kernels.hpp", "pipe_stream.hip")
 MALL_FLUSH_BYTES = 1 << 30
 
+# Wider 16 KiB tiles (64 x 128, 32 x 256) at the launch shapes measured best for
+# them on MI355X: enough interleaved strip segments to give every CU a
+# workgroup, 4 producer waves, lazy commits for the copy.
+_NT, _RM, _IL, _LZ, _U = 0x4, 0x10, 0x20, 0x80, 0x40
+WIDE_COPY = {
+    "64x128": dict(tile_m=64, tile_n=128, stages=3, producer_waves=4, consumer_waves=4, split=2,
+                   flags=_NT | _RM | _IL | _LZ),
+    "32x256": dict(tile_m=32, tile_n=256, stages=2, producer_waves=4, consumer_waves=8, split=4,
+                   flags=_NT | _RM | _IL | _LZ),
+}
+WIDE_ROWSUM = {
+    "32x256": dict(tile_m=32, tile_n=256, stages=3, producer_waves=4, consumer_waves=8, split=1,
+                   flags=_NT | _RM),
+    "32x256_unified": dict(tile_m=32, tile_n=256, stages=2, consumer_waves=4, split=2,
+                           flags=_U | _NT | _RM),
+}
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -193,7 +210,8 @@ def bench_copy(stages, steps, warmup, stats=False, **cfg):
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, COPY_M, COPY_N, **kw)
     c = pt.make_config(pt.PIPE_OP_COPY, **kw)
     nbytes = 2 * COPY_M * COPY_N * 2
-    return {"stages": stages, "producer_waves": c.producer_waves,
+    return {"tile": f"{c.tile_m}x{c.tile_n}", "stages": stages,
+            "producer_waves": c.producer_waves,
             "consumer_waves": c.consumer_waves, "flags": c.flags, "split": q["split"],
             "grid": q["grid"], "lds_bytes": q["lds_bytes"], "wall_ms": wall, "kernel_ms": kern,
             "bytes": nbytes, "gbs": nbytes / (wall * 1e-3) / 1e9,
@@ -226,7 +244,7 @@ def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
     timing = hot_cold(fn, nbytes, max(steps, 20), 2) if stats else None
     q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, ROWSUM_M, ROWSUM_N, **kw)
     c = pt.make_config(pt.PIPE_OP_ROWSUM, **kw)
-    r = {"stages": c.stages, "producer_waves": c.producer_waves,
+    r = {"tile": f"{c.tile_m}x{c.tile_n}", "stages": c.stages, "producer_waves": c.producer_waves,
          "consumer_waves": c.consumer_waves, "flags": c.flags, "split": q["split"],
          "grid": q["grid"], "wall_ms": wall, "kernel_ms": kern, "bytes": nbytes,
          "gbs": nbytes / (wall * 1e-3) / 1e9, "kernel_gbs": nbytes / (kern * 1e-3) / 1e9}
@@ -378,7 +396,8 @@ def main():
                          "the copy -- the best of the S sweeps measured on MI355X); 0 = the "
                          "best of this run's 1..4 copy sweep")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--only", choices=["copy", "rowsum", "gemm", "gemm_bf16", "ceiling", "calib"],
+    ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "rowsum",
+                                       "rowsum_32x256", "gemm", "gemm_bf16", "ceiling", "calib"],
                     default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
@@ -406,6 +425,15 @@ def main():
     if args.only == "copy":
         r = bench_copy(args.stages or 2, args.steps, args.warmup)
         log(f"[bench] copy: {r}")
+        return
+    if args.only in ("copy_32x256", "copy_64x128"):
+        cfg = dict(WIDE_COPY[args.only.split("_")[1]])
+        r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+        log(f"[bench] {args.only}: {r}")
+        return
+    if args.only == "rowsum_32x256":
+        r = bench_rowsum(args.steps, args.warmup, **WIDE_ROWSUM["32x256"])
+        log(f"[bench] {args.only}: {r}")
         return
     if args.only == "rowsum":
         r = bench_rowsum(args.steps, args.warmup, args.stages)
@@ -445,6 +473,16 @@ def main():
         extras["copy_per_launch"] = t
         log(f"[bench] copy per launch: hot {t['hot']['median_gbs']:.1f}, "
             f"cold {t['cold']['median_gbs']:.1f} GB/s (median)")
+        wide = {}
+        for name, cfg in WIDE_COPY.items():
+            cfg = dict(cfg)
+            w = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+            wide[name] = {k: w[k] for k in ("tile", "stages", "producer_waves", "consumer_waves",
+                                            "flags", "split", "grid", "kernel_ms", "gbs",
+                                            "kernel_gbs", "bit_exact")}
+            wide[name]["kernel_pct_of_peak"] = round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)
+            log(f"[bench] copy, {name} tiles: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
+        extras["copy_wide_tiles"] = wide
         u = bench_copy(2, max(3, args.steps // 2), 2, consumer_waves=2,
                        flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
                        pt.PIPE_FLAG_XCD_REMAP)
@@ -461,6 +499,13 @@ def main():
                          pt.PIPE_FLAG_XCD_REMAP)
         log(f"[bench] unified rowsum: {r['gbs']:.1f} GB/s")
         extras["rowsum_unified"] = r
+        wide = {}
+        for name, cfg in WIDE_ROWSUM.items():
+            w = bench_rowsum(max(3, args.steps // 2), 2, **cfg)
+            w["kernel_pct_of_peak"] = round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)
+            wide[name] = w
+            log(f"[bench] rowsum, {name}: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
+        extras["rowsum_wide_tiles"] = wide
         _ROWSUM_BUF.clear()
         torch.cuda.empty_cache()
         g = bench_gemm(max(3, args.steps // 2), 2)
@@ -489,7 +534,7 @@ def main():
 
     achieved = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
     kname = (f"void pipe::stream_kernel<{head['stages']}, {head['consumer_waves']}, "
-             f"{head['producer_waves']}, 0, false>(pipe::StreamParams)")
+             f"{head['producer_waves']}, 0, false, 64>(pipe::StreamParams)")
     traffic = recorded_traffic(kname)
     line = {
         "metric": METRIC,

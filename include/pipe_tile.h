@@ -104,8 +104,10 @@ typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_
 typedef struct {
   int32_t stages;         /* S, ring depth: copy/rowsum 1..8 (5..8 need 4 or 8 consumer
                              waves; the ring must fit 160 KiB of LDS); gemm 1..4          */
-  int32_t tile_m;         /* copy/rowsum: 128; gemm: 128                                  */
-  int32_t tile_n;         /* copy/rowsum: 64 fp16; gemm: 128                              */
+  int32_t tile_m;         /* copy/rowsum: 128, 64 or 32 (with tile_n 64, 128, 256: every
+                             tile is 16 KiB; the wider two need S 2..4, producer_waves
+                             2 or 4, consumer_waves 4 or 8 -- unified: 2 or 4); gemm 128 */
+  int32_t tile_n;         /* copy/rowsum: 64, 128 or 256 fp16 (see tile_m); gemm: 128    */
   int32_t tile_k;         /* gemm only: 64                                                */
   int32_t producer_waves; /* copy/rowsum: 1, 2 or 4; gemm: 2 or 4 (each tile's loads split
                              evenly; a wave keeps up to 2, 6 or 14 tiles of commit lag)   */

@@ -209,3 +209,28 @@ def test_ceiling_library_exports_and_validation():
     assert L.ceil_read(FAKE, None, 1024, 8, 1, None) == 1
     assert L.ceil_read(FAKE, FAKE, 1024, 8, 2, None) == 3
     assert L.ceil_memcpy(None, FAKE, 16, None) == 1
+
+
+def test_tile_shapes():
+    """16 KiB tiles: the pages' 128 x 64, and the wider 64 x 128 and 32 x 256
+    (S 2..4, 2 or 4 producer waves, 4 or 8 consumer waves)."""
+    ok = dict(stages=2, producer_waves=4, consumer_waves=4)
+    for tm, tn in ((64, 128), (32, 256)):
+        q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, tile_m=tm, tile_n=tn, **ok)
+        assert q["items"] == 16384 // tn and q["tiles_per_item"] == 16384 // tm
+        q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 8192, 65536, tile_m=tm, tile_n=tn,
+                                 stages=3, producer_waves=2, consumer_waves=8)
+        assert q["items"] == (8192 // tm) * q["split"]
+        q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 4096, 4096, tile_m=tm, tile_n=tn,
+                                 flags=pt.PIPE_FLAG_UNIFIED, stages=2, consumer_waves=2)
+        assert q["threads"] == 128
+    for kw in (dict(tile_m=64, tile_n=64), dict(tile_m=256, tile_n=32),
+               dict(tile_m=64, tile_n=128, stages=1), dict(tile_m=64, tile_n=128, stages=6,
+                                                           consumer_waves=8),
+               dict(tile_m=32, tile_n=256, producer_waves=1),
+               dict(tile_m=32, tile_n=256, consumer_waves=2),
+               dict(tile_m=32, tile_n=256, flags=pt.PIPE_FLAG_UNIFIED, consumer_waves=8)):
+        args = dict(ok)
+        args.update(kw)
+        assert _copy(FAKE, FAKE, 256, 256, 256, 256, pt.make_config(0, **args)) \
+            == pt.PIPE_ERR_CONFIG, kw

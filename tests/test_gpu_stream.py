@@ -404,6 +404,77 @@ def test_rowsum_commit_policies_bit_exact(policy, S, PW):
     assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
 
 
+# ---------------------------------------------------------------- wider tiles
+SHAPES = [(64, 128), (32, 256)]
+
+
+@pytest.mark.parametrize("tm,tn", SHAPES)
+@pytest.mark.parametrize("S,PW,C", [(2, 4, 4), (3, 2, 8), (4, 4, 8)])
+@pytest.mark.parametrize("split,flags", [(1, 0), (3, pt.PIPE_FLAG_SPLIT_INTERLEAVE),
+                                         (2, pt.PIPE_FLAG_ROW_STRIPS)])
+def test_copy_wide_tiles_bit_exact(tm, tn, S, PW, C, split, flags):
+    src = synth.unique_codes(1024, 1536).to(DEV)
+    st = _status()
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, tile_m=tm, tile_n=tn, stages=S,
+                                 producer_waves=PW, consumer_waves=C, split=split, grid=5,
+                                 flags=flags, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32),
+                          R.tile_checksums(src.cpu().numpy(), tm, tn))
+
+
+@pytest.mark.parametrize("tm,tn", SHAPES)
+@pytest.mark.parametrize("shape", [(1000, 1000), (33, 264), (300, 8)])
+def test_copy_wide_tiles_ragged(tm, tn, shape):
+    src = synth.unique_codes(*shape).to(DEV)
+    dst, chk = pt.pipe_tile_copy(src, checksums=True, tile_m=tm, tile_n=tn, stages=2,
+                                 producer_waves=4, consumer_waves=4, grid=3)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32),
+                          R.tile_checksums(src.cpu().numpy(), tm, tn))
+
+
+@pytest.mark.parametrize("tm,tn", SHAPES)
+@pytest.mark.parametrize("shape", [(1024, 4096), (1000, 3000)])
+@pytest.mark.parametrize("S,PW,C", [(2, 4, 4), (4, 2, 8)])
+def test_rowsum_wide_tiles_bit_exact(tm, tn, shape, S, PW, C):
+    A = synth.small_int(shape, -8, 8, torch.float16, seed=15).to(DEV)
+    st = _status()
+    out = pt.pipe_rowsum(A, tile_m=tm, tile_n=tn, stages=S, producer_waves=PW,
+                         consumer_waves=C, split=3, grid=7, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+@pytest.mark.parametrize("tm,tn", SHAPES)
+@pytest.mark.parametrize("S,W", [(2, 2), (4, 4)])
+def test_unified_wide_tiles_bit_exact(tm, tn, S, W):
+    src = synth.unique_codes(1024, 1536).to(DEV)
+    dst = pt.pipe_tile_copy(src, tile_m=tm, tile_n=tn, stages=S, consumer_waves=W, split=2,
+                            grid=5, flags=pt.PIPE_FLAG_UNIFIED)
+    A = synth.small_int((512, 4096), -8, 8, torch.float16, seed=16).to(DEV)
+    out = pt.pipe_rowsum(A, tile_m=tm, tile_n=tn, stages=S, consumer_waves=W, split=4, grid=5,
+                         flags=pt.PIPE_FLAG_UNIFIED)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy()))
+
+
+@pytest.mark.parametrize("tm,tn", SHAPES)
+def test_copy_wide_tiles_full_size_bit_exact(tm, tn):
+    src = synth.uniform((16384, 16384), torch.float16, seed=42, device=DEV)
+    dst = pt.pipe_tile_copy(src, tile_m=tm, tile_n=tn, stages=2, producer_waves=4,
+                            consumer_waves=8, split=8, flags=pt.PIPE_FLAG_SPLIT_INTERLEAVE |
+                            pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP |
+                            pt.PIPE_FLAG_LAZY_COMMIT)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
+
+
 # ---------------------------------------------------------------- unified variant
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 6, 8])
 @pytest.mark.parametrize("W", [2, 4, 8])
