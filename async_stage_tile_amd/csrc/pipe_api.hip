@@ -167,6 +167,12 @@ pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool
   if (items > INT32_MAX) return PIPE_ERR_SHAPE;
   g->items = (int32_t)items;
   g->grid = (c.grid == 0 || c.grid > g->items) ? g->items : c.grid;
+  // Barrier words count arrivals in 32 bits; keep every count below 2^31 (so
+  // that a wrap never occurs, whatever the arrivals per phase).
+  const int64_t per_wg = ((int64_t)g->items + g->grid - 1) / g->grid * g->seg_len;
+  const int64_t arrivals = c.consumer_waves > c.producer_waves ? c.consumer_waves
+                                                               : c.producer_waves;
+  if (per_wg * arrivals >= (int64_t(1) << 31)) return PIPE_ERR_SHAPE;
   return PIPE_OK;
 }
 
@@ -396,6 +402,9 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
   p.trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
   if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
   const int grid = (c.grid == 0 || c.grid > p.items) ? p.items : c.grid;
+  // Barrier words count arrivals in 32 bits (4 per stage on empty).
+  if (((int64_t)p.items + grid - 1) / grid * p.k_steps * 4 >= (int64_t(1) << 31))
+    return PIPE_ERR_SHAPE;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
   return hip_status(launch_gemm(c.stages, c.producer_waves, grid, p, st));

@@ -7,13 +7,12 @@
 //   * mbarrier = pending-arrival count + phase bit; the arrival that completes
 //     a phase flips the phase and reloads the count; wait(p) passes once the
 //     phase is no longer p ("cute（12）async_pipeline" 6.2; mlc.ai
-//     "chapter_async_barriers", section mbarrier). Here: bit 31 of the LDS word
-//     is the phase, bits 0..30 count arrivals of the current phase; the last
-//     arriver adds (2^31 - expected), which clears the count and flips bit 31
-//     in one atomic step. gfx950 has no transaction-byte counter, so the
-//     producer arrives on "full" only after `s_waitcnt vmcnt` shows that the
-//     stage's loads have landed in LDS: arrivals == 0 and bytes == 0 collapse
-//     into one arrival.
+//     "chapter_async_barriers", section mbarrier). Here one LDS word per
+//     barrier, in one of two encodings (Counter, Flip; see below). gfx950 has
+//     no transaction-byte
+//     counter, so the producer arrives on "full" only after `s_waitcnt vmcnt`
+//     shows that the stage's loads have landed in LDS: arrivals == 0 and
+//     bytes == 0 collapse into one arrival.
 //   * PipelineState (index, phase, count) with ++ wrapping the index and
 //     flipping the phase; producers start at phase 1 so the first lap never
 //     waits ("cute（12）async_pipeline" 2.2-2.3, 6.1). Kept in SGPRs (the
@@ -49,7 +48,6 @@ constexpr int kBlockBytes = kWave * kChunkBytes;          // 1024 = one wave-wid
 constexpr int kBlocksPerTile = kTileBytes / kBlockBytes;  // 16
 constexpr int kRowsPerBlock = kBlockBytes / kRowBytes;    // 8
 
-constexpr uint32_t kPhaseBit = 0x80000000u;
 
 // Tile shapes of the stream kernels. Every tile is 16 KiB: kRows x TC fp16
 // with TC (tileN) in {64, 128, 256} and kRows (tileM) = 128, 64, 32. One
@@ -110,37 +108,63 @@ __device__ __forceinline__ PipeState consumer_start(int stages) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS barrier word: bit 31 = phase, bits 0..30 = arrivals in this phase.
+// LDS barrier words. Two encodings of the same pending-count-and-phase
+// barrier, chosen per kernel (both waiters and arrivers of one barrier use the
+// same one):
+//
+//  * Counter<E>: the word counts arrivals. A barrier that expects E arrivals
+//    per phase has completed floor(count / E) phases; its phase bit is the
+//    parity of that number. Arrivals for the next phase of a slot cannot start
+//    before the current phase completes (the ring's handshake orders them), so
+//    the count never runs ahead. An arrival is one non-returning ds_add: no
+//    wave waits for it, and the phase flips with the last arrival.
+//  * Flip<E>: bit 31 is the phase, bits 0..30 count the arrivals of the
+//    current phase. The last arriver (it learns so from the returned count)
+//    adds 2^31 - E, which clears the count and flips the phase in a second
+//    atomic. Arrivals wait for their atomic to return, and the phase flips one
+//    LDS round trip after the last arrival. The tile copy runs faster on this
+//    slower hand-off (measured), the row sum and the GEMM on Counter.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t bar_read(uint32_t* bar) {
   return __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// One arrival on behalf of the whole wave (lane 0 performs it). Returns the
-// number of arrivals of this phase that preceded it (wave-uniform).
-__device__ __forceinline__ uint32_t bar_arrive(uint32_t* bar, uint32_t expected) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  uint32_t before = 0;
-  if (lane_id() == 0) {
-    uint32_t old = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_WORKGROUP);
-    before = old & ~kPhaseBit;
-    if (before + 1u == expected) {
-      // Completes the phase: count back to 0, phase bit flips.
-      __hip_atomic_fetch_add(bar, kPhaseBit - expected, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+template <uint32_t E>
+struct Counter {
+  static __device__ __forceinline__ uint32_t phase(uint32_t word) { return (word / E) & 1u; }
+  // One arrival on behalf of the whole wave (lane 0).
+  static __device__ __forceinline__ void arrive(uint32_t* bar) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane_id() == 0)
+      (void)__hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return uniform(before);
-}
+};
 
-// Wait until the barrier's phase differs from `phase`. Returns false on timeout.
+template <uint32_t E>
+struct Flip {
+  static constexpr uint32_t kPhaseBit = 0x80000000u;
+  static __device__ __forceinline__ uint32_t phase(uint32_t word) { return word >> 31; }
+  static __device__ __forceinline__ void arrive(uint32_t* bar) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane_id() == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+      if ((old & ~kPhaseBit) + 1u == E)  // completes the phase: count to 0, phase flips
+        __hip_atomic_fetch_add(bar, kPhaseBit - E, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+};
+
+// Wait until barrier B's phase differs from `phase`. Returns false on timeout.
+template <class B>
 __device__ __forceinline__ bool bar_wait(uint32_t* bar, uint32_t phase, uint32_t spin_limit) {
   uint32_t polls = 0;
   while (true) {
-    uint32_t w = uniform(bar_read(bar));
-    if ((w >> 31) != phase) break;
+    const uint32_t w = uniform(bar_read(bar));
+    if (B::phase(w) != phase) break;
     if (++polls >= spin_limit) return false;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -178,7 +202,7 @@ __device__ __forceinline__ void wait_vmcnt_mul(int k) {
 }
 
 // producer_acquire with eager commits. Waits until slot `index` is released
-// (its empty barrier left phase `phase`). While the slot is still in use and
+// (its EMPTY barrier left phase `phase`); commits arrive on FULL barriers. While the slot is still in use and
 // this wave has at least `eager_min` tiles in flight that it has not yet
 // committed (eager_min = 0: never), it commits the oldest of them (once its
 // LOADS loads have landed, i.e. at most LOADS * (pending - 1) remain
@@ -188,18 +212,17 @@ __device__ __forceinline__ void wait_vmcnt_mul(int k) {
 // eager_min = 2 the newest tile in flight is never waited for here, so the
 // producer does not stall its next issue on a load it has only just begun.
 // Returns false on timeout.
-template <int LOADS, int S>
+template <int LOADS, int S, class EMPTY, class FULL>
 __device__ __forceinline__ bool acquire_slot(uint32_t* empty_bar, uint32_t phase,
                                              uint32_t* full_bars, int index, int& pending,
-                                             uint32_t arrivals, int eager_min,
-                                             uint32_t spin_limit) {
+                                             int eager_min, uint32_t spin_limit) {
   uint32_t polls = 0;
-  while ((uniform(bar_read(empty_bar)) >> 31) == phase) {
+  while (EMPTY::phase(uniform(bar_read(empty_bar))) == phase) {
     if (eager_min > 0 && pending >= eager_min) {
       wait_vmcnt_mul<LOADS>(pending - 1);
       int oldest = index - pending;
       if (oldest < 0) oldest += S;
-      bar_arrive(&full_bars[oldest], arrivals);
+      FULL::arrive(&full_bars[oldest]);
       --pending;
       continue;
     }

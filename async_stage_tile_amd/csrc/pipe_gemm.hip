@@ -134,8 +134,9 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
     const uint8_t* ga = p.A + (int64_t)tm * kGemmTile * p.lda;
     const uint8_t* gb = p.B + (int64_t)tn * kBRowBytes;
     for (int ks = 0; ks < p.k_steps; ++ks) {
-      if (!acquire_slot<kLoads, S>(&lds.empty[w.index], w.phase, lds.full, w.index, pending,
-                                   (uint32_t)PW, p.eager, p.spin_limit)) {
+      if (!acquire_slot<kLoads, S, Counter<4>, Counter<PW>>(&lds.empty[w.index], w.phase,
+                                                             lds.full, w.index, pending, p.eager,
+                                                             p.spin_limit)) {
         ok = false;
         break;
       }
@@ -167,7 +168,7 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
         wait_vmcnt_mul<kLoads>(pending - 1);
         int oldest = w.index - (pending - 1);
         if (oldest < 0) oldest += S;
-        bar_arrive(&lds.full[oldest], (uint32_t)PW);
+        Counter<PW>::arrive(&lds.full[oldest]);
         --pending;
       }
       w.inc();
@@ -177,12 +178,12 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
     wait_vmcnt_mul<kLoads>(pending - 1);
     int oldest = w.index - pending;
     if (oldest < 0) oldest += S;
-    bar_arrive(&lds.full[oldest], (uint32_t)PW);
+    Counter<PW>::arrive(&lds.full[oldest]);
     --pending;
   }
   if (ok) {
     for (int i = 0; i < S; ++i) {
-      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+      if (!bar_wait<Counter<4>>(&lds.empty[w.index], w.phase, p.spin_limit)) {
         ok = false;
         break;
       }
@@ -244,7 +245,7 @@ __device__ __forceinline__ void mfma_sub(f32x16 (&acc)[2][2], const SubFrags& f)
 // reads of the slot to return, releases the slot, then waits on full for the
 // next stage (while the previous MFMAs still execute) and reads that stage's
 // first sub-step before issuing the last MFMAs of the current one.
-template <int S, int EPI>
+template <int S, int PW, int EPI>
 __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_lds, int cw) {
   OutLds* out = static_cast<OutLds*>(out_lds);
   const int lane = lane_id();
@@ -264,7 +265,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     SubFrags b0, b1;
-    if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+    if (!bar_wait<Counter<PW>>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
       ok = false;
       break;
     }
@@ -280,10 +281,10 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
       mfma_sub(acc, b0);
       // consumer_release: this wave's reads of the slot have all returned.
       wait_lgkmcnt0();
-      bar_arrive(&lds.empty[rd.index], 4u);
+      Counter<4>::arrive(&lds.empty[rd.index]);
       rd.inc();
       if (ks + 1 < p.k_steps) {
-        if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+        if (!bar_wait<Counter<PW>>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
           ok = false;
           break;
         }
@@ -351,7 +352,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
       uint8_t* slot = &out->slot[wm][0];
 #pragma unroll
       for (int c = 0; c < kOutChunks; ++c) {
-        if (!bar_wait(&out->empty[wm], ost.phase, p.spin_limit)) {
+        if (!bar_wait<Counter<1>>(&out->empty[wm], ost.phase, p.spin_limit)) {
           ok = false;
           break;
         }
@@ -369,7 +370,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
             }
         }
         wait_lgkmcnt0();
-        bar_arrive(&out->full[wm], 2u);
+        Counter<2>::arrive(&out->full[wm]);
         ost.inc();
       }
       if (!ok) break;
@@ -392,7 +393,7 @@ __device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
     for (int c = 0; ok && c < kOutChunks; ++c) {
 #pragma unroll
       for (int pair = 0; pair < 2; ++pair) {
-        if (!bar_wait(&out.full[pair], rd[pair].phase, p.spin_limit)) {
+        if (!bar_wait<Counter<2>>(&out.full[pair], rd[pair].phase, p.spin_limit)) {
           ok = false;
           break;
         }
@@ -404,7 +405,7 @@ __device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
           v[i] = *reinterpret_cast<const uint4*>(slot + (q >> 4) * kOutPitch + (q & 15) * 16);
         }
         wait_lgkmcnt0();
-        bar_arrive(&out.empty[pair], 1u);
+        Counter<1>::arrive(&out.empty[pair]);
         rd[pair].inc();
         const int64_t row0 = (int64_t)tm * kGemmTile + pair * 64 + c * kOutRows;
 #pragma unroll
@@ -440,7 +441,7 @@ __global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0))
     if (wave < PW)
       gemm_producer<S, PW>(p, lds, wave);
     else if (wave < PW + 4)
-      gemm_consumer<S, EPI>(p, lds, &out, wave - PW);
+      gemm_consumer<S, PW, EPI>(p, lds, &out, wave - PW);
     else
       gemm_store_wave(p, out);
   } else if constexpr (EPI == kEpiWaveStaged) {
@@ -449,13 +450,13 @@ __global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0))
     if (wave < PW)
       gemm_producer<S, PW>(p, lds, wave);
     else
-      gemm_consumer<S, EPI>(p, lds, &out, wave - PW);
+      gemm_consumer<S, PW, EPI>(p, lds, &out, wave - PW);
   } else {
     __syncthreads();
     if (wave < PW)
       gemm_producer<S, PW>(p, lds, wave);
     else
-      gemm_consumer<S, EPI>(p, lds, nullptr, wave - PW);
+      gemm_consumer<S, PW, EPI>(p, lds, nullptr, wave - PW);
   }
 }
 

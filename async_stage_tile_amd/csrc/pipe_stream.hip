@@ -40,6 +40,8 @@
 // The kernel is compiled once per stage count: this file is built several
 // times, each object instantiating the stage counts PIPE_STREAM_STAGES_LO ..
 // PIPE_STREAM_STAGES_HI (so the instantiations compile in parallel).
+#include <type_traits>
+
 #include "pipe_device.hpp"
 #include "pipe_kernels.hpp"
 
@@ -121,9 +123,16 @@ __device__ __forceinline__ int cols_in(const StreamParams& p, int tc) {
 // ---------------------------------------------------------------------------
 // Producer waves
 // ---------------------------------------------------------------------------
-template <int S, int C, int PW, bool MASKED, int TC>
+// Barrier encoding per op: the copy runs faster on the two-step Flip hand-off,
+// the row sum on Counter (measured on MI355X).
+template <int OP, uint32_t E>
+using StreamBar = typename std::conditional<OP == kOpCopy, Flip<E>, Counter<E>>::type;
+
+template <int S, int C, int PW, int OP, bool MASKED, int TC>
 __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
   using Sh = TileShape<TC>;
+  using FullBar = StreamBar<OP, PW>;
+  using EmptyBar = StreamBar<OP, C>;
   constexpr int kLoads = kBlocksPerTile / PW;  // DMA instructions per tile per wave
   static_assert((stream_max_lag(PW) + 1) * kLoads <= 63,
                 "vmcnt counts at most 63 outstanding loads");
@@ -142,8 +151,9 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
     for (int k = 0; k < len; ++k, ++t) {
       // producer_acquire: wait until consumers released this slot (committing
       // landed tiles meanwhile, unless commits are lazy).
-      if (!acquire_slot<kLoads, S>(&lds.empty[w.index], w.phase, lds.full, w.index, pending,
-                                   (uint32_t)PW, p.eager, p.spin_limit)) {
+      if (!acquire_slot<kLoads, S, EmptyBar, FullBar>(&lds.empty[w.index], w.phase, lds.full,
+                                                      w.index, pending, p.eager,
+                                                      p.spin_limit)) {
         ok = false;
         break;
       }
@@ -187,7 +197,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
         wait_vmcnt_mul<kLoads>(pending - 1);
         int oldest = w.index - (pending - 1);
         if (oldest < 0) oldest += S;
-        bar_arrive(&lds.full[oldest], (uint32_t)PW);
+        FullBar::arrive(&lds.full[oldest]);
         --pending;
       }
       w.inc();
@@ -198,13 +208,13 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
     wait_vmcnt_mul<kLoads>(pending - 1);
     int oldest = w.index - pending;
     if (oldest < 0) oldest += S;
-    bar_arrive(&lds.full[oldest], (uint32_t)PW);
+    FullBar::arrive(&lds.full[oldest]);
     --pending;
   }
   // producer_tail: S more empty phases, so every slot has been drained.
   if (ok) {
     for (int i = 0; i < S; ++i) {
-      if (!bar_wait(&lds.empty[w.index], w.phase, p.spin_limit)) {
+      if (!bar_wait<EmptyBar>(&lds.empty[w.index], w.phase, p.spin_limit)) {
         ok = false;
         break;
       }
@@ -218,9 +228,11 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
 // ---------------------------------------------------------------------------
 // Consumer waves
 // ---------------------------------------------------------------------------
-template <int S, int C, int OP, bool MASKED, int TC>
+template <int S, int C, int PW, int OP, bool MASKED, int TC>
 __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
   using Sh = TileShape<TC>;
+  using FullBar = StreamBar<OP, PW>;
+  using EmptyBar = StreamBar<OP, C>;
   constexpr int NB = (kBlocksPerTile + C - 1) / C;  // blocks per wave (last may idle)
   const int lane = lane_id();
   const int lrow = lane >> Sh::kLog2ChunksPerRow;
@@ -238,7 +250,7 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
     int tr = 0, tc = 0;
     for (int k = 0; k < len; ++k, ++t) {
       // consumer_wait: the slot's full phase must have completed.
-      if (!bar_wait(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+      if (!bar_wait<FullBar>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
         ok = false;
         break;
       }
@@ -328,7 +340,7 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
         wait_lgkmcnt0();
       }
       // consumer_release.
-      if (!p.no_release) bar_arrive(&lds.empty[rd.index], (uint32_t)C);
+      if (!p.no_release) EmptyBar::arrive(&lds.empty[rd.index]);
       rd.inc();
     }
     if constexpr (OP == kOpRowsum) {
@@ -362,9 +374,9 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
   }
   __syncthreads();
   if (wave < PW)
-    producer<S, C, PW, MASKED, TC>(p, lds, wave);
+    producer<S, C, PW, OP, MASKED, TC>(p, lds, wave);
   else
-    consumer<S, C, OP, MASKED, TC>(p, lds, wave - PW);
+    consumer<S, C, PW, OP, MASKED, TC>(p, lds, wave - PW);
 }
 
 // ---------------------------------------------------------------------------

@@ -130,6 +130,17 @@ class MBarrier:
         return (self.pending, self.phase, self.tx)
 
 
+def counter_phase(count: int, expected: int) -> int:
+    """Phase bit of a barrier kept as a bare arrival counter.
+
+    After `count` arrivals on a barrier that expects `expected` per phase,
+    floor(count / expected) phases have completed; the phase bit is the parity
+    of that number ("completed-phase count, parity = that & 1"). An MBarrier
+    without transaction bytes that has seen the same arrivals is in this phase.
+    """
+    return (count // expected) & 1
+
+
 # --------------------------------------------------------------------------
 # Lock-step timeline (the order in which the pages walk through the ring)
 # --------------------------------------------------------------------------

@@ -234,3 +234,11 @@ def test_tile_shapes():
         args.update(kw)
         assert _copy(FAKE, FAKE, 256, 256, 256, 256, pt.make_config(0, **args)) \
             == pt.PIPE_ERR_CONFIG, kw
+
+
+def test_barrier_arrival_counts_stay_below_2_31():
+    """Barrier words count arrivals in 32 bits: a launch whose workgroup would
+    see 2^31 or more arrivals on one barrier is refused before any HIP call."""
+    cfg = pt.make_config(0, stages=2, producer_waves=1, consumer_waves=8, grid=1)
+    M = 128 << 28                      # 2^28 tiles in one strip, one workgroup
+    assert _copy(FAKE, FAKE, M, 64, 64, 64, cfg) == pt.PIPE_ERR_SHAPE

@@ -200,3 +200,28 @@ def test_store_side_ring_of_the_gemm_epilogue():
     r = P.check_protocol(1, 12, 1, mode="landed", lag=0, producers=2)
     assert r.completed and not r.deadlock and r.violations == []
     assert r.max_ahead == 1
+
+
+@pytest.mark.parametrize("expected", [1, 2, 3, 4, 8])
+def test_counter_phase_equals_mbarrier_phase(expected):
+    """A barrier kept as a bare monotonic arrival counter (parity of the number of
+    completed phases) passes and blocks exactly where the mbarrier model does."""
+    b = P.MBarrier(expected)
+    for count in range(0, 20 * expected + 1):
+        if count:
+            b.arrive()
+        assert P.counter_phase(count, expected) == b.phase
+        for parity in (0, 1):
+            assert (P.counter_phase(count, expected) != parity) == b.try_wait(parity)
+
+
+def test_counter_phase_survives_the_32_bit_wrap_for_powers_of_two():
+    """The device counter is 32 bits. For power-of-two arrival counts per phase,
+    2**32 / expected is even, so the phase read from the wrapped counter is the
+    phase of the true count."""
+    for expected in (1, 2, 4, 8):
+        for count in range(2 ** 32 - 5 * expected, 2 ** 32 + 5 * expected):
+            assert P.counter_phase(count % 2 ** 32, expected) == P.counter_phase(count, expected)
+    # not so for 3: which is why the host bounds the arrivals per slot
+    assert any(P.counter_phase(c % 2 ** 32, 3) != P.counter_phase(c, 3)
+               for c in range(2 ** 32, 2 ** 32 + 6))
