@@ -70,10 +70,10 @@ pipe_config_t defaults(pipe_op_t op) {
       break;
     case PIPE_OP_ROWSUM:
       c.stages = 4;
-      c.producer_waves = 1;
-      c.consumer_waves = 8;
+      c.producer_waves = 4;
+      c.consumer_waves = 4;
       c.swizzle_shift = 0;
-      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP;
+      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP | PIPE_FLAG_EAGER_NEWEST;
       break;
     default:
       c.stages = 2;

@@ -40,7 +40,9 @@ def test_config_defaults():
     assert c.flags == (pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP |
                        pt.PIPE_FLAG_LAZY_COMMIT)
     r = pt.make_config(pt.PIPE_OP_ROWSUM)
-    assert (r.stages, r.producer_waves, r.consumer_waves) == (4, 1, 8)
+    assert (r.stages, r.producer_waves, r.consumer_waves) == (4, 4, 4)
+    assert r.flags == (pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP |
+                       pt.PIPE_FLAG_EAGER_NEWEST)
     g = pt.make_config(pt.PIPE_OP_GEMM)
     assert (g.stages, g.tile_m, g.tile_n, g.tile_k, g.producer_waves, g.consumer_waves) \
         == (2, 128, 128, 64, 4, 4)
