@@ -137,6 +137,15 @@ pipe_status_t check_unified(const pipe_config_t& c, int64_t M, int64_t N, bool c
   return PIPE_OK;
 }
 
+// Device code forms byte offsets in int64: a matrix of `rows` rows (plus up to
+// one partial tile row) at a pitch of `ld` elements of `elem` bytes must span
+// fewer than 2^62 bytes.
+bool extent_fits(int64_t rows, int64_t ld, int64_t elem) {
+  constexpr int64_t kMaxBytes = int64_t(1) << 62;
+  if (rows < 0 || ld < 0 || rows > kMaxBytes) return false;
+  return ld <= kMaxBytes / elem / (rows + 256);
+}
+
 struct StreamGeom {
   int32_t tile_rows, tile_cols, n_strips, strip_len, seg_len, split, items, grid;
 };
@@ -151,7 +160,9 @@ int rowsum_default_split(int n_strips, int strip_len) {
 
 pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool row_strips,
                               bool rowsum, StreamGeom* g) {
-  const int64_t tr = (M + c.tile_m - 1) / c.tile_m, tc = (N + c.tile_n - 1) / c.tile_n;
+  // Ceiling divisions written so that M or N near INT64_MAX cannot overflow.
+  const int64_t tr = M / c.tile_m + (M % c.tile_m != 0);
+  const int64_t tc = N / c.tile_n + (N % c.tile_n != 0);
   if (tr > INT32_MAX || tc > INT32_MAX) return PIPE_ERR_SHAPE;
   g->tile_rows = (int32_t)tr;
   g->tile_cols = (int32_t)tc;
@@ -248,6 +259,7 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   if (s != PIPE_OK) return s;
   if (M < 0 || N < 0 || ld_src < N || ld_dst < N) return PIPE_ERR_SHAPE;
   if (N % 8 != 0) return PIPE_ERR_SHAPE;
+  if (!extent_fits(M, ld_src, 2) || !extent_fits(M, ld_dst, 2)) return PIPE_ERR_SHAPE;
   if (M == 0 || N == 0) return PIPE_OK;
   if (src == nullptr || dst == nullptr) return PIPE_ERR_NULL;
   if (!aligned16(src) || !aligned16(dst) || (ld_src % 8) || (ld_dst % 8)) return PIPE_ERR_ALIGN;
@@ -305,7 +317,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   if (s != PIPE_OK) return s;
   if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // always row strips
   if (M < 0 || N < 0 || lda < N) return PIPE_ERR_SHAPE;
-  if (N % 8 != 0) return PIPE_ERR_SHAPE;
+  if (N % 8 != 0 || !extent_fits(M, lda, 2)) return PIPE_ERR_SHAPE;
   if (M == 0) return PIPE_OK;
   if (out == nullptr) return PIPE_ERR_NULL;
   if (!aligned4(out)) return PIPE_ERR_ALIGN;
@@ -366,6 +378,9 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
   if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return PIPE_ERR_SHAPE;
   if (M % 128 != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
+  if (!extent_fits(M, lda, 2) || !extent_fits(K, ldb, 2) ||
+      !extent_fits(M, ldc, (c.flags & PIPE_FLAG_GEMM_C_BF16) ? 2 : 4))
+    return PIPE_ERR_SHAPE;
   if (M == 0 || N == 0) return PIPE_OK;
   if (C == nullptr) return PIPE_ERR_NULL;
   if (c_bf16 ? (!aligned16(C) || (ldc % 8)) : !aligned4(C)) return PIPE_ERR_ALIGN;
@@ -420,6 +435,7 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     if (s != PIPE_OK) return s;
     if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
     if (M < 0 || N < 0 || K < 0 || M % 128 || N % 128 || K % 64) return PIPE_ERR_SHAPE;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
     const int64_t items = (M / 128) * (N / 128);
     if (items > INT32_MAX) return PIPE_ERR_SHAPE;
     const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;

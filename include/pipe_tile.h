@@ -46,7 +46,8 @@ extern "C" {
 typedef enum {
   PIPE_OK = 0,
   PIPE_ERR_NULL = 1,      /* a required pointer is NULL */
-  PIPE_ERR_SHAPE = 2,     /* negative size, ld < width, or a shape the op does not support */
+  PIPE_ERR_SHAPE = 2,     /* negative size, ld < width, a matrix spanning 2^62 bytes or more,
+                             or a shape the op does not support */
   PIPE_ERR_ALIGN = 3,     /* base pointer or row pitch not 16-byte aligned */
   PIPE_ERR_STAGES = 4,    /* stage count out of range or the ring does not fit in LDS */
   PIPE_ERR_CONFIG = 5,    /* unsupported tile shape, wave counts, grid, split or flags */
