@@ -1,7 +1,8 @@
 """ctypes binding of libpipeceil.so (include/pipe_ceiling.h).
 
 Context-only HBM ceilings, timed beside the tile stream: plain grid-stride
-streaming copy and read kernels and the runtime's device-to-device copy.
+streaming copy and read kernels, the runtime's device-to-device copy, and
+plain kernels that walk column strips the way the tile stream does.
 They are a measurement aid and take no part in the tile stream.
 """
 from __future__ import annotations
@@ -10,7 +11,8 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpipeceil.so")
-SYMBOLS = ("ceil_copy", "ceil_read", "ceil_memcpy")
+SYMBOLS = ("ceil_copy", "ceil_read", "ceil_memcpy", "ceil_strip_copy", "ceil_strip_read",
+           "ceil_strip_write")
 
 _lib = None
 
@@ -25,6 +27,10 @@ def lib() -> ctypes.CDLL:
         L.ceil_copy.argtypes = [vp, vp, sz, i, i, i, vp]
         L.ceil_read.argtypes = [vp, vp, sz, i, i, vp]
         L.ceil_memcpy.argtypes = [vp, vp, sz, vp]
+        i64 = ctypes.c_int64
+        L.ceil_strip_copy.argtypes = [vp, vp, i64, i64, i64, i, i, vp]
+        L.ceil_strip_read.argtypes = [vp, vp, i64, i64, i64, i, i, vp]
+        L.ceil_strip_write.argtypes = [vp, i64, i64, i64, i, i, vp]
         for f in SYMBOLS:
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -51,3 +57,30 @@ def read(src, sink, grid: int, nt: int = 1, stream=None) -> None:
 def memcpy(src, dst, stream=None) -> None:
     _check(lib().ceil_memcpy(dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(),
                              stream), "ceil_memcpy")
+
+
+def _region(t):
+    """(rows, pitch bytes, width bytes) of a row-major 2-D tensor."""
+    assert t.dim() == 2 and t.stride(1) == 1
+    es = t.element_size()
+    return t.shape[0], t.stride(0) * es, t.shape[1] * es
+
+
+def strip_copy(src, dst, strip_bytes: int, split: int = 1, stream=None) -> None:
+    """dst <- src (2-D tensors of one shape and pitch), walked as column strips."""
+    rows, pitch, width = _region(src)
+    assert dst.shape == src.shape and dst.stride() == src.stride()
+    _check(lib().ceil_strip_copy(src.data_ptr(), dst.data_ptr(), rows, pitch, width, strip_bytes,
+                                 split, stream), "ceil_strip_copy")
+
+
+def strip_read(src, sink, strip_bytes: int, split: int = 1, stream=None) -> None:
+    rows, pitch, width = _region(src)
+    _check(lib().ceil_strip_read(src.data_ptr(), sink.data_ptr(), rows, pitch, width, strip_bytes,
+                                 split, stream), "ceil_strip_read")
+
+
+def strip_write(dst, strip_bytes: int, split: int = 1, stream=None) -> None:
+    rows, pitch, width = _region(dst)
+    _check(lib().ceil_strip_write(dst.data_ptr(), rows, pitch, width, strip_bytes, split, stream),
+           "ceil_strip_write")

@@ -50,6 +50,82 @@ __global__ void __launch_bounds__(kThreads) read_kernel(const u32x4* __restrict_
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Column-strip ceilings: the tile stream's access pattern without its ring.
+// The region is `rows` x `width` bytes at a row pitch of `pitch` bytes, cut
+// into column strips WB bytes wide and 16 KiB tiles of 16384/WB rows. Each
+// 512-thread workgroup walks one strip segment (tiles seg, seg + split, ...);
+// consecutive segments share an XCD. A wave moves two 1 KiB pieces of each
+// tile (64 lanes x 16 bytes = 1024/WB rows of WB bytes each), one tile at a
+// time, with non-temporal loads and stores.
+constexpr int kStripThreads = 512;
+enum StripOp { kStripRead = 0, kStripWrite = 1, kStripCopy = 2 };
+
+template <int WB, int OP>
+__global__ void __launch_bounds__(kStripThreads) strip_kernel(const uint8_t* __restrict__ src,
+                                                              uint8_t* __restrict__ dst,
+                                                              uint32_t* __restrict__ sink,
+                                                              int64_t pitch, int64_t rows,
+                                                              int split) {
+  constexpr int kRowsPerPiece = 1024 / WB, kTileRows = 16384 / WB, kLanesPerRow = WB / 16;
+  const int per_xcd = gridDim.x / 8;  // gridDim.x % 8 == 0
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int strip = item / split, seg = item % split;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int64_t col = (int64_t)strip * WB + (lane % kLanesPerRow) * 16;
+  const int lrow = lane / kLanesPerRow;
+  const int64_t n_tiles = rows / kTileRows;
+  uint32_t acc = 0;
+  for (int64_t t = seg; t < n_tiles; t += split) {
+    u32x4 v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = t * kTileRows + (2 * wave + i) * kRowsPerPiece + lrow;
+      if constexpr (OP == kStripWrite) {
+        v[i] = u32x4{(uint32_t)row, (uint32_t)col, ~(uint32_t)row, ~(uint32_t)col};
+      } else {
+        v[i] = ld<true>(reinterpret_cast<const u32x4*>(src + row * pitch + col));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = t * kTileRows + (2 * wave + i) * kRowsPerPiece + lrow;
+      if constexpr (OP == kStripRead)
+        acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+      else
+        st<true>(reinterpret_cast<u32x4*>(dst + row * pitch + col), v[i]);
+    }
+  }
+  if (OP == kStripRead && acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+int check_strips(int64_t rows, int64_t pitch, int64_t width, int strip_bytes, int split) {
+  if (strip_bytes != 128 && strip_bytes != 256 && strip_bytes != 512) return 3;
+  if (rows <= 0 || width <= 0 || pitch < width || pitch % 16 != 0) return 2;
+  if (width % strip_bytes != 0 || rows % (16384 / strip_bytes) != 0) return 2;
+  if (pitch > (int64_t(1) << 40) || rows > (int64_t(1) << 40) / pitch) return 2;
+  const int64_t grid = width / strip_bytes * split;
+  if (split < 1 || grid % 8 != 0 || grid > 65536) return 3;
+  return 0;
+}
+
+template <int OP>
+int launch_strips(const void* src, void* dst, unsigned* sink, int64_t rows, int64_t pitch,
+                  int64_t width, int strip_bytes, int split, hipStream_t stream) {
+  const dim3 grid((unsigned)(width / strip_bytes * split)), block(kStripThreads);
+  const auto* s = static_cast<const uint8_t*>(src);
+  auto* d = static_cast<uint8_t*>(dst);
+  if (strip_bytes == 128)
+    hipLaunchKernelGGL((strip_kernel<128, OP>), grid, block, 0, stream, s, d, sink, pitch, rows,
+                       split);
+  else if (strip_bytes == 256)
+    hipLaunchKernelGGL((strip_kernel<256, OP>), grid, block, 0, stream, s, d, sink, pitch, rows,
+                       split);
+  else
+    hipLaunchKernelGGL((strip_kernel<512, OP>), grid, block, 0, stream, s, d, sink, pitch, rows,
+                       split);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
 int check(const void* a, const void* b, size_t bytes, int grid) {
   if (a == nullptr || b == nullptr) return 1;
   if (bytes == 0 || bytes % 16 != 0) return 2;
@@ -96,4 +172,31 @@ extern "C" int ceil_memcpy(void* dst, const void* src, size_t bytes, hipStream_t
   if (dst == nullptr || src == nullptr) return 1;
   if (bytes == 0) return 2;
   return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream) == hipSuccess ? 0 : 4;
+}
+
+extern "C" int ceil_strip_copy(const void* src, void* dst, int64_t rows, int64_t pitch,
+                               int64_t width, int strip_bytes, int split, hipStream_t stream) {
+  if (src == nullptr || dst == nullptr) return 1;
+  if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return 2;
+  if (int e = check_strips(rows, pitch, width, strip_bytes, split)) return e;
+  return launch_strips<kStripCopy>(src, dst, nullptr, rows, pitch, width, strip_bytes, split,
+                                   stream);
+}
+
+extern "C" int ceil_strip_read(const void* src, unsigned* sink, int64_t rows, int64_t pitch,
+                               int64_t width, int strip_bytes, int split, hipStream_t stream) {
+  if (src == nullptr || sink == nullptr) return 1;
+  if ((uintptr_t)src % 16 != 0 || (uintptr_t)sink % 4 != 0) return 2;
+  if (int e = check_strips(rows, pitch, width, strip_bytes, split)) return e;
+  return launch_strips<kStripRead>(src, nullptr, sink, rows, pitch, width, strip_bytes, split,
+                                   stream);
+}
+
+extern "C" int ceil_strip_write(void* dst, int64_t rows, int64_t pitch, int64_t width,
+                                int strip_bytes, int split, hipStream_t stream) {
+  if (dst == nullptr) return 1;
+  if ((uintptr_t)dst % 16 != 0) return 2;
+  if (int e = check_strips(rows, pitch, width, strip_bytes, split)) return e;
+  return launch_strips<kStripWrite>(nullptr, dst, nullptr, rows, pitch, width, strip_bytes, split,
+                                    stream);
 }

@@ -17,7 +17,9 @@ Also reported (in "extras"):
   * the unified (non-specialised) variant of the copy and the row sum;
   * context ceilings on the same device: the runtime's device-to-device copy,
     torch's copy and plain streaming copy / read kernels with no LDS ring
-    (libpipeceil.so);
+    (libpipeceil.so), and plain kernels that read, write or copy the headline
+    matrix in the tile stream's own pattern (column strips 128 or 512 bytes
+    wide);
   * the CPU oracle on bounded samples of the copy, row sum and GEMM, on one
     thread and on all host threads.
 
@@ -312,7 +314,42 @@ def bench_ceilings(steps, warmup):
         out[f"stream_read_nt_grid{grid}"] = big.numel() / (kern * 1e-3) / 1e9
     best_copy = max(v for k, v in out.items() if "read" not in k)
     best_read = max(v for k, v in out.items() if "read" in k)
-    return {"gbs": out, "best_copy_gbs": best_copy, "best_read_gbs": best_read}
+    del big
+    torch.cuda.empty_cache()
+    return {"gbs": out, "best_copy_gbs": best_copy, "best_read_gbs": best_read,
+            "column_strips": strip_ceilings(steps, warmup)}
+
+
+def strip_ceilings(steps, warmup):
+    """Plain kernels (no LDS ring) with the tile stream's access pattern on the
+    headline matrix: column strips 128 bytes wide (that of 128 x 64 fp16 tiles)
+    and 512 bytes wide (that of 32 x 256 tiles), read only, write only and copy.
+    `serial_rw_gbs` is the copy rate if its reads and writes took turns at the
+    read-only and write-only rates: 2 / (1 / read + 1 / write)."""
+    import torch
+
+    from async_stage_tile_amd import ceiling
+    src, dst = copy_buffers()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nbytes = src.numel() * src.element_size()
+    out = {}
+    for strip_bytes, split in ((128, 1), (512, 4)):
+        r = {}
+        _, kern = timed_launches(lambda: ceiling.strip_read(src, sink, strip_bytes, split),
+                                 steps, warmup)
+        r["read_gbs"] = nbytes / (kern * 1e-3) / 1e9
+        _, kern = timed_launches(lambda: ceiling.strip_write(dst, strip_bytes, split), steps,
+                                 warmup)
+        r["write_gbs"] = nbytes / (kern * 1e-3) / 1e9
+        _, kern = timed_launches(lambda: ceiling.strip_copy(src, dst, strip_bytes, split), steps,
+                                 warmup)
+        r["copy_gbs"] = 2 * nbytes / (kern * 1e-3) / 1e9
+        assert torch.equal(src, dst)
+        r["serial_rw_gbs"] = 2.0 / (1.0 / r["read_gbs"] + 1.0 / r["write_gbs"])
+        r["grid"] = src.shape[1] * src.element_size() // strip_bytes * split
+        out[f"{strip_bytes}B"] = {k: (round(v, 1) if isinstance(v, float) else v)
+                                  for k, v in r.items()}
+    return out
 
 
 def cpu_baseline(rows, min_seconds=10.0):
@@ -522,6 +559,12 @@ def main():
         c = bench_ceilings(max(3, args.steps // 2), 2)
         log(f"[bench] ceilings: copy {c['best_copy_gbs']:.1f}, read {c['best_read_gbs']:.1f} GB/s")
         c["copy_frac_of_best_copy_ceiling"] = head["kernel_gbs"] / c["best_copy_gbs"]
+        s128 = c["column_strips"]["128B"]
+        log(f"[bench] 128-byte column strips, plain: read {s128['read_gbs']}, write "
+            f"{s128['write_gbs']}, copy {s128['copy_gbs']}, serial read+write "
+            f"{s128['serial_rw_gbs']} GB/s")
+        c["copy_frac_of_strip128_copy"] = head["kernel_gbs"] / s128["copy_gbs"]
+        c["copy_frac_of_strip128_serial_rw"] = head["kernel_gbs"] / s128["serial_rw_gbs"]
         extras["context_ceilings"] = c
     cpu = None
     if not args.no_cpu:

@@ -10,10 +10,11 @@
  * stream's interface (include/pipe_tile.h).
  *
  * Common rules:
- *   - Pointers are device pointers, 16-byte aligned; `bytes` is a positive
- *     multiple of 16. The caller owns all memory; nothing is allocated.
- *   - `grid` is the number of 256-thread workgroups (1 .. 65536); each walks
- *     the buffer with a grid-sized stride, so any grid covers all bytes.
+ *   - Pointers are device pointers, 16-byte aligned. The caller owns all
+ *     memory; nothing is allocated.
+ *   - ceil_copy / ceil_read: `bytes` is a positive multiple of 16; `grid` is
+ *     the number of 256-thread workgroups (1 .. 65536), each walking the
+ *     buffer with a grid-sized stride, so any grid covers all bytes.
  *   - Launches are asynchronous on `stream` (0 = the null stream).
  *   - Return 0 on success; 1 for a null pointer, 2 for a bad size or
  *     alignment, 3 for a bad grid or variant, 4 when the HIP launch or copy
@@ -24,6 +25,7 @@
 
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -44,6 +46,33 @@ int ceil_read(const void* src, unsigned* sink, size_t bytes, int grid, int nt,
 
 /* hipMemcpyAsync device to device of `bytes` (the runtime's own copy path). */
 int ceil_memcpy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+/* Column-strip ceilings: the tile stream's access pattern with no LDS ring.
+ * The region is `rows` x `width` bytes at a row pitch of `pitch` bytes (all
+ * row-major, 16-byte aligned). It is cut into column strips `strip_bytes`
+ * wide (128, 256 or 512) and into 16 KiB tiles of 16384 / strip_bytes rows;
+ * `rows` must be a whole number of tiles and `width` of strips. Each strip is
+ * walked by `split` workgroups of 512 threads, segment s taking tiles s,
+ * s + split, ...; the grid, (width / strip_bytes) * split, must be a multiple
+ * of 8 and at most 65536 (consecutive segments share an XCD). A wave moves
+ * two 1 KiB pieces of a tile at a time (64 lanes x 16 bytes), non-temporally.
+ * With 128-byte strips this is the access pattern of 128 x 64 fp16 tiles
+ * streamed down column strips; with 512-byte strips, that of 32 x 256 tiles.
+ * The region may span at most 2^40 bytes. */
+
+/* dst <- src over the region (dst has the same pitch; buffers must not overlap). */
+int ceil_strip_copy(const void* src, void* dst, int64_t rows, int64_t pitch, int64_t width,
+                    int strip_bytes, int split, hipStream_t stream);
+
+/* Reads the region and folds it per thread; `sink` (one uint32, device) as in
+ * ceil_read. */
+int ceil_strip_read(const void* src, unsigned* sink, int64_t rows, int64_t pitch, int64_t width,
+                    int strip_bytes, int split, hipStream_t stream);
+
+/* Writes the region: each 16-byte piece gets the words (row, byte column,
+ * ~row, ~byte column) of its first byte, as uint32. */
+int ceil_strip_write(void* dst, int64_t rows, int64_t pitch, int64_t width, int strip_bytes,
+                     int split, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -211,6 +211,21 @@ def test_ceiling_library_exports_and_validation():
     assert L.ceil_read(FAKE, None, 1024, 8, 1, None) == 1
     assert L.ceil_read(FAKE, FAKE, 1024, 8, 2, None) == 3
     assert L.ceil_memcpy(None, FAKE, 16, None) == 1
+    # column strips: rows x width bytes at pitch; grid = strips * split, a multiple of 8
+    ok = (1024, 32768, 32768, 128, 1)
+    assert L.ceil_strip_copy(None, FAKE, *ok, None) == 1
+    assert L.ceil_strip_copy(FAKE + 8, FAKE, *ok, None) == 2
+    assert L.ceil_strip_copy(FAKE, FAKE, 1000, 32768, 32768, 128, 1, None) == 2  # partial tile
+    assert L.ceil_strip_copy(FAKE, FAKE, 1024, 32768, 32704, 128, 1, None) == 2  # partial strip
+    assert L.ceil_strip_copy(FAKE, FAKE, 1024, 16384, 32768, 128, 1, None) == 2  # pitch < width
+    assert L.ceil_strip_copy(FAKE, FAKE, 1024, 32768, 32768, 64, 1, None) == 3
+    assert L.ceil_strip_copy(FAKE, FAKE, 1024, 32768, 32768, 128, 0, None) == 3
+    assert L.ceil_strip_copy(FAKE, FAKE, 1024, 32768, 3 * 512, 512, 1, None) == 3  # grid 3
+    assert L.ceil_strip_copy(FAKE, FAKE, 1 << 40, 32768, 32768, 128, 1, None) == 2  # > 2^40 B
+    assert L.ceil_strip_read(FAKE, None, *ok, None) == 1
+    assert L.ceil_strip_read(FAKE, FAKE + 2, *ok, None) == 2
+    assert L.ceil_strip_write(None, *ok, None) == 1
+    assert L.ceil_strip_write(FAKE, 1024, 32768, 32768, 1024, 1, None) == 3
 
 
 def test_tile_shapes():
