@@ -240,6 +240,20 @@ __device__ __forceinline__ void mfma_sub(f32x16 (&acc)[2][2], const SubFrags& f)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
 }
 
+// Scheduling hint for a block that holds one sub-step's fragment reads (6 LDS
+// reads) and the previous sub-step's 4 MFMAs: alternate one MFMA with two
+// reads, so that the reads of the next sub-step issue while the matrix core
+// works, instead of being sunk next to their uses.
+__device__ __forceinline__ void interleave_mfma_reads() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
 // Consumer wave. Fragment reads run one K sub-step ahead of the MFMAs through
 // two register buffers. At the last sub-step of a stage the wave waits for its
 // reads of the slot to return, releases the slot, then waits on full for the
@@ -275,10 +289,13 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
     for (int ks = 0; ks < p.k_steps; ++ks) {
       load_sub(b1, 1, sa, sb, wm, wn, li, lk, lane, p);
       mfma_sub(acc, b0);
+      interleave_mfma_reads();
       load_sub(b0, 2, sa, sb, wm, wn, li, lk, lane, p);
       mfma_sub(acc, b1);
+      interleave_mfma_reads();
       load_sub(b1, 3, sa, sb, wm, wn, li, lk, lane, p);
       mfma_sub(acc, b0);
+      interleave_mfma_reads();
       // consumer_release: this wave's reads of the slot have all returned.
       wait_lgkmcnt0();
       Counter<4>::arrive(&lds.empty[rd.index]);
