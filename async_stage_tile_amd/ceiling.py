@@ -12,7 +12,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpipeceil.so")
 SYMBOLS = ("ceil_copy", "ceil_read", "ceil_memcpy", "ceil_strip_copy", "ceil_strip_read",
-           "ceil_strip_write")
+           "ceil_strip_write", "ceil_lds")
 
 _lib = None
 
@@ -31,6 +31,7 @@ def lib() -> ctypes.CDLL:
         L.ceil_strip_copy.argtypes = [vp, vp, i64, i64, i64, i, i, vp]
         L.ceil_strip_read.argtypes = [vp, vp, i64, i64, i64, i, i, vp]
         L.ceil_strip_write.argtypes = [vp, i64, i64, i64, i, i, vp]
+        L.ceil_lds.argtypes = [i, vp, vp, vp, i, i, vp]
         for f in SYMBOLS:
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -84,3 +85,17 @@ def strip_write(dst, strip_bytes: int, split: int = 1, stream=None) -> None:
     rows, pitch, width = _region(dst)
     _check(lib().ceil_strip_write(dst.data_ptr(), rows, pitch, width, strip_bytes, split, stream),
            "ceil_strip_write")
+
+
+LDS_OPS = {0: ("ds_read_b128", 1024), 1: ("ds_read_b64_tr_b16", 512), 2: ("global_load_lds_dwordx4", 1024)}
+
+
+def lds(op: int, src, fold, clocks, grid: int, iters: int, stream=None) -> None:
+    """One launch of the LDS ceiling kernel (see include/pipe_ceiling.h)."""
+    _check(lib().ceil_lds(op, src.data_ptr() if src is not None else None, fold.data_ptr(),
+                          clocks.data_ptr(), grid, iters, stream), "ceil_lds")
+
+
+def lds_bytes(op: int, grid: int, iters: int) -> int:
+    """Bytes one launch moves: 8 waves x 8 instructions per iteration."""
+    return grid * 8 * iters * 8 * LDS_OPS[op][1]

@@ -126,6 +126,67 @@ int launch_strips(const void* src, void* dst, unsigned* sink, int64_t rows, int6
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
+// LDS ceilings: how fast one instruction kind moves bytes into or out of LDS.
+// 512-thread workgroups with 64 KiB of LDS each (two per CU); every wave issues
+// 8 instructions per iteration, all conflict-free. OP 0: ds_read_b128 (1 KiB
+// per wave instruction); OP 1: ds_read_b64_tr_b16 (512 B), with the address
+// pattern of a 32-column MFMA B operand; OP 2: global_load_lds_dwordx4 (1 KiB)
+// from a 64 KiB global buffer that stays in L2. Wave 0 records the shader clock
+// and the 100 MHz real-time clock around the loop, so the host can convert to
+// bytes per clock.
+enum LdsOp { kLdsReadB128 = 0, kLdsReadTr16 = 1, kLdsDma = 2 };
+constexpr int kLdsThreads = 512;
+constexpr int kLdsBytes = 65536;
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int OP>
+__global__ void __launch_bounds__(kLdsThreads) lds_kernel(const uint8_t* __restrict__ src,
+                                                          uint32_t* __restrict__ fold,
+                                                          uint64_t* __restrict__ clocks,
+                                                          int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < kLdsBytes / 16; i += kLdsThreads)
+    reinterpret_cast<u32x4*>(lds)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (OP == kLdsReadB128) {
+        const int a = ((wave * 8 + j) * 1024 + lane * 16 + it * 64) & (kLdsBytes - 16);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + a);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      } else if constexpr (OP == kLdsReadTr16) {
+        // 16 K-rows of 256 bytes per 4 KiB; lane groups of 16 read 4 K-rows x 4 columns
+        const int g = lane >> 4, i = lane & 15;
+        const int k = 8 * (g >> 1) + (i >> 2) + 16 * ((j + it) & 3);
+        const int col = 16 * (g & 1) + 4 * (i & 3) + 32 * (j >> 2) + 64 * (wave & 1);
+        const int sw = ((k & 3) << 2) ^ (((k >> 3) & 1) << 1);
+        const int a = (wave >> 1) * 16384 + k * 256 + (((col >> 3) ^ sw) << 4) + (col & 7) * 2;
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_byte*)lds + a));
+        acc ^= (uint32_t)(uint16_t)v[0] ^ ((uint32_t)(uint16_t)v[3] << 16);
+      } else {
+        const uint8_t* g = src + (((wave * 8 + j) * 1024 + it * 4096) & (kLdsBytes - 1)) + lane * 16;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)((lds_byte*)lds + (((wave * 8 + j) * 1024) & (kLdsBytes - 1))));
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(base) : "memory");
+      }
+    }
+    if constexpr (OP == kLdsDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  }
+  if constexpr (OP == kLdsDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  fold[(size_t)blockIdx.x * kLdsThreads + threadIdx.x] = acc;
+  if (threadIdx.x == 0) {
+    clocks[2 * blockIdx.x] = c1 - c0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 int check(const void* a, const void* b, size_t bytes, int grid) {
   if (a == nullptr || b == nullptr) return 1;
   if (bytes == 0 || bytes % 16 != 0) return 2;
@@ -199,4 +260,23 @@ extern "C" int ceil_strip_write(void* dst, int64_t rows, int64_t pitch, int64_t 
   if (int e = check_strips(rows, pitch, width, strip_bytes, split)) return e;
   return launch_strips<kStripWrite>(nullptr, dst, nullptr, rows, pitch, width, strip_bytes, split,
                                     stream);
+}
+
+extern "C" int ceil_lds(int op, const void* src, unsigned* fold, uint64_t* clocks, int grid,
+                        int iters, hipStream_t stream) {
+  if (fold == nullptr || clocks == nullptr || (op == kLdsDma && src == nullptr)) return 1;
+  if (((uintptr_t)fold % 4) || ((uintptr_t)clocks % 8) || (op == kLdsDma && (uintptr_t)src % 16))
+    return 2;
+  if (grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 20)) return 3;
+  const dim3 g(grid), b(kLdsThreads);
+  const auto* s = static_cast<const uint8_t*>(src);
+  if (op == kLdsReadB128)
+    hipLaunchKernelGGL((lds_kernel<kLdsReadB128>), g, b, 0, stream, s, fold, clocks, iters);
+  else if (op == kLdsReadTr16)
+    hipLaunchKernelGGL((lds_kernel<kLdsReadTr16>), g, b, 0, stream, s, fold, clocks, iters);
+  else if (op == kLdsDma)
+    hipLaunchKernelGGL((lds_kernel<kLdsDma>), g, b, 0, stream, s, fold, clocks, iters);
+  else
+    return 3;
+  return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -317,7 +317,31 @@ def bench_ceilings(steps, warmup):
     del big
     torch.cuda.empty_cache()
     return {"gbs": out, "best_copy_gbs": best_copy, "best_read_gbs": best_read,
-            "column_strips": strip_ceilings(steps, warmup)}
+            "column_strips": strip_ceilings(steps, warmup), "lds": lds_ceilings(steps, warmup)}
+
+
+def lds_ceilings(steps, warmup, grid=512):
+    """LDS traffic of one instruction kind at full rate (two 512-thread
+    workgroups per CU): the fragment reads and the DMA writes that the GEMM
+    mainloop is made of. Bytes per clock per CU use the shader clock that the
+    kernel itself measured."""
+    import torch
+
+    from async_stage_tile_amd import ceiling
+    src = torch.zeros(65536 + 1024, dtype=torch.uint8, device="cuda")
+    fold = torch.zeros(grid * 512, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    out = {}
+    for op, (name, _) in ceiling.LDS_OPS.items():
+        iters = 2000 if op < 2 else 500
+        _, kern = timed_launches(lambda: ceiling.lds(op, src, fold, clocks, grid, iters), steps,
+                                 warmup)
+        c = clocks.view(grid, 2).double()
+        ghz = (c[:, 0].sum() / (c[:, 1].sum() / 100e6)).item() / 1e9
+        nbytes = ceiling.lds_bytes(op, grid, iters)
+        out[name] = {"tbs": round(nbytes / (kern * 1e-3) / 1e12, 2), "clock_ghz": round(ghz, 3),
+                     "bytes_per_clk_per_cu": round(nbytes / 256 / (kern * 1e-3 * ghz * 1e9), 1)}
+    return out
 
 
 def strip_ceilings(steps, warmup):

@@ -74,6 +74,23 @@ int ceil_strip_read(const void* src, unsigned* sink, int64_t rows, int64_t pitch
 int ceil_strip_write(void* dst, int64_t rows, int64_t pitch, int64_t width, int strip_bytes,
                      int split, hipStream_t stream);
 
+/* LDS ceilings: one kind of LDS traffic at full rate, no other work. `grid`
+ * workgroups (1 .. 65536) of 512 threads, each holding 64 KiB of LDS (two fit
+ * on a CU); every wave issues 8 conflict-free instructions per iteration for
+ * `iters` iterations (1 .. 2^20).
+ *   op 0: ds_read_b128, 1 KiB per wave instruction;
+ *   op 1: ds_read_b64_tr_b16, 512 B per wave instruction, with the address
+ *         pattern of the GEMM's B operand (32 columns of 16 K-rows);
+ *   op 2: global_load_lds_dwordx4, 1 KiB per wave instruction, from the first
+ *         65 536 + 1 024 bytes of `src` (16-byte aligned; stays in L2).
+ * `fold` (grid * 512 uint32, device) receives each thread's fold of what it
+ * read, so that no read is optimised away. `clocks` (2 * grid uint64, device)
+ * receives, per workgroup, the shader-clock cycles and the 100 MHz real-time
+ * ticks that its first wave measured around the loop. `src` is ignored unless
+ * op is 2. */
+int ceil_lds(int op, const void* src, unsigned* fold, uint64_t* clocks, int grid, int iters,
+             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

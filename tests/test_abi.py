@@ -226,6 +226,14 @@ def test_ceiling_library_exports_and_validation():
     assert L.ceil_strip_read(FAKE, FAKE + 2, *ok, None) == 2
     assert L.ceil_strip_write(None, *ok, None) == 1
     assert L.ceil_strip_write(FAKE, 1024, 32768, 32768, 1024, 1, None) == 3
+    # LDS ceilings: op, src, fold, clocks, grid, iters
+    assert L.ceil_lds(0, None, None, FAKE, 8, 10, None) == 1
+    assert L.ceil_lds(2, None, FAKE, FAKE, 8, 10, None) == 1  # the DMA op reads src
+    assert L.ceil_lds(0, None, FAKE + 2, FAKE, 8, 10, None) == 2
+    assert L.ceil_lds(0, None, FAKE, FAKE + 4, 8, 10, None) == 2
+    assert L.ceil_lds(0, None, FAKE, FAKE, 0, 10, None) == 3
+    assert L.ceil_lds(0, None, FAKE, FAKE, 8, 0, None) == 3
+    assert L.ceil_lds(3, None, FAKE, FAKE, 8, 10, None) == 3
 
 
 def test_tile_shapes():

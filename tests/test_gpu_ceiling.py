@@ -54,3 +54,40 @@ def test_strip_read_leaves_sink_alone_on_random_data(ceiling):
     # The sink is written only when a thread's fold hits one fixed word; on
     # this seeded input no thread's does.
     assert int(sink.item()) == 11
+
+
+def test_lds_read_b128_folds_the_chunks_it_claims_to_read(ceiling):
+    """Chunk i of the LDS array holds (i, 1, 2, 3), so a thread's fold is the
+    XOR of the chunk indices it read: computed here from the documented
+    address pattern (wave w, lane l, iteration t, instruction j:
+    ((8w + j) * 1024 + 16 l + 64 t) mod 65536, 16-byte aligned)."""
+    grid, iters = 4, 3
+    fold = torch.zeros(grid * 512, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    ceiling.lds(0, None, fold, clocks, grid, iters)
+    torch.cuda.synchronize()
+    want = []
+    for t in range(512):
+        w, lane = t // 64, t % 64
+        acc = 0
+        for it in range(iters):
+            for j in range(8):
+                acc ^= (((8 * w + j) * 1024 + 16 * lane + 64 * it) & 0xFFF0) // 16
+        want.append(acc)
+    got = fold.view(grid, 512).cpu()
+    assert all(got[g].tolist() == want for g in range(grid))
+    c = clocks.view(grid, 2).cpu()
+    assert bool((c[:, 0] > 0).all()) and bool((c[:, 1] > 0).all())
+
+
+@pytest.mark.parametrize("op", [1, 2])
+def test_lds_ceiling_ops_run(ceiling, op):
+    grid, iters = 8, 4
+    src = torch.zeros(65536 + 1024, dtype=torch.uint8, device="cuda")
+    fold = torch.full((grid * 512,), 7, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    ceiling.lds(op, src, fold, clocks, grid, iters)
+    torch.cuda.synchronize()
+    assert bool((clocks.view(grid, 2)[:, 0] > 0).all())
+    if op == 2:
+        assert bool((fold == 0).all())  # the DMA op reads nothing into registers
