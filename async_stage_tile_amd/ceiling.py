@@ -87,7 +87,11 @@ def strip_write(dst, strip_bytes: int, split: int = 1, stream=None) -> None:
            "ceil_strip_write")
 
 
-LDS_OPS = {0: ("ds_read_b128", 1024), 1: ("ds_read_b64_tr_b16", 512), 2: ("global_load_lds_dwordx4", 1024)}
+# op: (name, bytes per wave instruction, waves that move bytes per workgroup)
+LDS_OPS = {0: ("ds_read_b128", 1024, 8), 1: ("ds_read_b64_tr_b16", 512, 8),
+           2: ("global_load_lds_dwordx4", 1024, 8), 3: ("ds_write_b128", 1024, 8),
+           4: ("dma_waves_0_3_with_read_waves_4_7", 1024, 8), 5: ("read_waves_4_7_alone", 1024, 4),
+           6: ("dma_waves_0_3_alone", 1024, 4)}
 
 
 def lds(op: int, src, fold, clocks, grid: int, iters: int, stream=None) -> None:
@@ -97,5 +101,7 @@ def lds(op: int, src, fold, clocks, grid: int, iters: int, stream=None) -> None:
 
 
 def lds_bytes(op: int, grid: int, iters: int) -> int:
-    """Bytes one launch moves: 8 waves x 8 instructions per iteration."""
-    return grid * 8 * iters * 8 * LDS_OPS[op][1]
+    """Bytes one launch moves: the active waves x 8 instructions per iteration
+    (for op 4, half of them by DMA and half by reads)."""
+    _, per_instr, waves = LDS_OPS[op]
+    return grid * waves * iters * 8 * per_instr

@@ -131,10 +131,20 @@ int launch_strips(const void* src, void* dst, unsigned* sink, int64_t rows, int6
 // 8 instructions per iteration, all conflict-free. OP 0: ds_read_b128 (1 KiB
 // per wave instruction); OP 1: ds_read_b64_tr_b16 (512 B), with the address
 // pattern of a 32-column MFMA B operand; OP 2: global_load_lds_dwordx4 (1 KiB)
-// from a 64 KiB global buffer that stays in L2. Wave 0 records the shader clock
-// and the 100 MHz real-time clock around the loop, so the host can convert to
-// bytes per clock.
-enum LdsOp { kLdsReadB128 = 0, kLdsReadTr16 = 1, kLdsDma = 2 };
+// from a 64 KiB global buffer that stays in L2; OP 3: ds_write_b128 (1 KiB);
+// OP 4: waves 0-3 as OP 2 while waves 4-7 run OP 0; OP 5 and OP 6: one of the
+// two halves of OP 4 with the other half idle. Waves 0 and 4 record the
+// shader clock and the 100 MHz real-time clock around their loops, so the host
+// can convert to bytes per clock.
+enum LdsOp {
+  kLdsReadB128 = 0,
+  kLdsReadTr16 = 1,
+  kLdsDma = 2,
+  kLdsWriteB128 = 3,
+  kLdsDmaAndRead = 4,  // waves 0-3 DMA, waves 4-7 ds_read_b128
+  kLdsReadHalf = 5,    // waves 4-7 ds_read_b128, waves 0-3 idle
+  kLdsDmaHalf = 6,     // waves 0-3 DMA, waves 4-7 idle
+};
 constexpr int kLdsThreads = 512;
 constexpr int kLdsBytes = 65536;
 typedef __attribute__((address_space(3))) uint8_t lds_byte;
@@ -153,10 +163,18 @@ __global__ void __launch_bounds__(kLdsThreads) lds_kernel(const uint8_t* __restr
   __syncthreads();
   const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   uint32_t acc = 0;
-  for (int it = 0; it < iters; ++it) {
+  const bool idle = (OP == kLdsReadHalf && wave < 4) || (OP == kLdsDmaHalf && wave >= 4);
+  for (int it = 0; it < (idle ? 0 : iters); ++it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if constexpr (OP == kLdsReadB128) {
+      if constexpr (OP == kLdsWriteB128) {
+        const int a = ((wave * 8 + j) * 1024 + lane * 16 + it * 64) & (kLdsBytes - 16);
+        // Written as an instruction: nothing reads these bytes back, so a plain
+        // store would be dropped as dead.
+        const uint32_t la = (uint32_t)(uintptr_t)((lds_byte*)lds + a);
+        const u32x4 v = {(uint32_t)it, (uint32_t)j, 0u, 1u};
+        asm volatile("ds_write_b128 %0, %1" : : "v"(la), "v"(v) : "memory");
+      } else if (OP == kLdsReadB128 || OP == kLdsReadHalf || (OP == kLdsDmaAndRead && wave >= 4)) {
         const int a = ((wave * 8 + j) * 1024 + lane * 16 + it * 64) & (kLdsBytes - 16);
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + a);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
@@ -169,21 +187,24 @@ __global__ void __launch_bounds__(kLdsThreads) lds_kernel(const uint8_t* __restr
         const int a = (wave >> 1) * 16384 + k * 256 + (((col >> 3) ^ sw) << 4) + (col & 7) * 2;
         const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_byte*)lds + a));
         acc ^= (uint32_t)(uint16_t)v[0] ^ ((uint32_t)(uint16_t)v[3] << 16);
-      } else {
+      } else if (OP == kLdsDma || OP == kLdsDmaAndRead || OP == kLdsDmaHalf) {
         const uint8_t* g = src + (((wave * 8 + j) * 1024 + it * 4096) & (kLdsBytes - 1)) + lane * 16;
         const uint32_t base = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)((lds_byte*)lds + (((wave * 8 + j) * 1024) & (kLdsBytes - 1))));
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(base) : "memory");
       }
     }
-    if constexpr (OP == kLdsDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    if constexpr (OP == kLdsDma || OP == kLdsDmaAndRead || OP == kLdsDmaHalf)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   }
-  if constexpr (OP == kLdsDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (OP == kLdsDma || OP == kLdsDmaAndRead || OP == kLdsDmaHalf)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (OP == kLdsWriteB128) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   fold[(size_t)blockIdx.x * kLdsThreads + threadIdx.x] = acc;
-  if (threadIdx.x == 0) {
-    clocks[2 * blockIdx.x] = c1 - c0;
-    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  if (lane == 0 && (wave == 0 || wave == 4)) {
+    clocks[4 * blockIdx.x + (wave >> 1)] = c1 - c0;
+    clocks[4 * blockIdx.x + (wave >> 1) + 1] = r1 - r0;
   }
 }
 
@@ -264,9 +285,9 @@ extern "C" int ceil_strip_write(void* dst, int64_t rows, int64_t pitch, int64_t 
 
 extern "C" int ceil_lds(int op, const void* src, unsigned* fold, uint64_t* clocks, int grid,
                         int iters, hipStream_t stream) {
-  if (fold == nullptr || clocks == nullptr || (op == kLdsDma && src == nullptr)) return 1;
-  if (((uintptr_t)fold % 4) || ((uintptr_t)clocks % 8) || (op == kLdsDma && (uintptr_t)src % 16))
-    return 2;
+  const bool dma = op == kLdsDma || op == kLdsDmaAndRead || op == kLdsDmaHalf;
+  if (fold == nullptr || clocks == nullptr || (dma && src == nullptr)) return 1;
+  if (((uintptr_t)fold % 4) || ((uintptr_t)clocks % 8) || (dma && (uintptr_t)src % 16)) return 2;
   if (grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 20)) return 3;
   const dim3 g(grid), b(kLdsThreads);
   const auto* s = static_cast<const uint8_t*>(src);
@@ -276,6 +297,14 @@ extern "C" int ceil_lds(int op, const void* src, unsigned* fold, uint64_t* clock
     hipLaunchKernelGGL((lds_kernel<kLdsReadTr16>), g, b, 0, stream, s, fold, clocks, iters);
   else if (op == kLdsDma)
     hipLaunchKernelGGL((lds_kernel<kLdsDma>), g, b, 0, stream, s, fold, clocks, iters);
+  else if (op == kLdsWriteB128)
+    hipLaunchKernelGGL((lds_kernel<kLdsWriteB128>), g, b, 0, stream, s, fold, clocks, iters);
+  else if (op == kLdsDmaAndRead)
+    hipLaunchKernelGGL((lds_kernel<kLdsDmaAndRead>), g, b, 0, stream, s, fold, clocks, iters);
+  else if (op == kLdsReadHalf)
+    hipLaunchKernelGGL((lds_kernel<kLdsReadHalf>), g, b, 0, stream, s, fold, clocks, iters);
+  else if (op == kLdsDmaHalf)
+    hipLaunchKernelGGL((lds_kernel<kLdsDmaHalf>), g, b, 0, stream, s, fold, clocks, iters);
   else
     return 3;
   return hipGetLastError() == hipSuccess ? 0 : 4;

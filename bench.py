@@ -323,24 +323,35 @@ def bench_ceilings(steps, warmup):
 def lds_ceilings(steps, warmup, grid=512):
     """LDS traffic of one instruction kind at full rate (two 512-thread
     workgroups per CU): the fragment reads and the DMA writes that the GEMM
-    mainloop is made of. Bytes per clock per CU use the shader clock that the
-    kernel itself measured."""
+    mainloop is made of, alone and side by side. Bytes per clock per CU use the
+    shader clock that the kernel itself measured; for the side-by-side run each
+    half is timed over its own loop (waves 0 and 4 record their cycles)."""
     import torch
 
     from async_stage_tile_amd import ceiling
     src = torch.zeros(65536 + 1024, dtype=torch.uint8, device="cuda")
     fold = torch.zeros(grid * 512, dtype=torch.int32, device="cuda")
-    clocks = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    clocks = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
     out = {}
-    for op, (name, _) in ceiling.LDS_OPS.items():
-        iters = 2000 if op < 2 else 500
+    for op, (name, per_instr, waves) in ceiling.LDS_OPS.items():
+        iters = 500 if op in (2, 4, 6) else 2000
         _, kern = timed_launches(lambda: ceiling.lds(op, src, fold, clocks, grid, iters), steps,
                                  warmup)
-        c = clocks.view(grid, 2).double()
-        ghz = (c[:, 0].sum() / (c[:, 1].sum() / 100e6)).item() / 1e9
+        c = clocks.view(grid, 4).double()
+        col = 2 if op == 5 else 0
+        ghz = (c[:, col].sum() / (c[:, col + 1].sum() / 100e6)).item() / 1e9
+        clk = kern * 1e-3 * ghz * 1e9  # kernel duration in shader clocks
+        if op == 4:
+            half = grid * 4 * iters * 8 * per_instr
+            span = [c[:, k].mean().item() for k in (0, 2)]
+            frac = [x / max(span) for x in span]  # share of the kernel each half was busy
+            out[name] = {"clock_ghz": round(ghz, 3),
+                         "dma_bytes_per_clk_per_cu": round(half / 256 / (clk * frac[0]), 1),
+                         "read_bytes_per_clk_per_cu": round(half / 256 / (clk * frac[1]), 1)}
+            continue
         nbytes = ceiling.lds_bytes(op, grid, iters)
         out[name] = {"tbs": round(nbytes / (kern * 1e-3) / 1e12, 2), "clock_ghz": round(ghz, 3),
-                     "bytes_per_clk_per_cu": round(nbytes / 256 / (kern * 1e-3 * ghz * 1e9), 1)}
+                     "bytes_per_clk_per_cu": round(nbytes / 256 / clk, 1)}
     return out
 
 

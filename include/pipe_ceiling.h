@@ -82,12 +82,17 @@ int ceil_strip_write(void* dst, int64_t rows, int64_t pitch, int64_t width, int 
  *   op 1: ds_read_b64_tr_b16, 512 B per wave instruction, with the address
  *         pattern of the GEMM's B operand (32 columns of 16 K-rows);
  *   op 2: global_load_lds_dwordx4, 1 KiB per wave instruction, from the first
- *         65 536 + 1 024 bytes of `src` (16-byte aligned; stays in L2).
+ *         65 536 bytes of `src` (16-byte aligned; stays in L2);
+ *   op 3: ds_write_b128, 1 KiB per wave instruction;
+ *   op 4: waves 0-3 as op 2 while waves 4-7 as op 0 (the DMA writes and the
+ *         fragment reads of the GEMM mainloop, side by side);
+ *   op 5: waves 4-7 as op 0, waves 0-3 idle;
+ *   op 6: waves 0-3 as op 2, waves 4-7 idle.
  * `fold` (grid * 512 uint32, device) receives each thread's fold of what it
- * read, so that no read is optimised away. `clocks` (2 * grid uint64, device)
+ * read, so that no read is optimised away. `clocks` (4 * grid uint64, device)
  * receives, per workgroup, the shader-clock cycles and the 100 MHz real-time
- * ticks that its first wave measured around the loop. `src` is ignored unless
- * op is 2. */
+ * ticks that wave 0 measured around its loop, then the same for wave 4.
+ * `src` is ignored unless op is 2, 4 or 6. */
 int ceil_lds(int op, const void* src, unsigned* fold, uint64_t* clocks, int grid, int iters,
              hipStream_t stream);
 

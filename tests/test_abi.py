@@ -233,7 +233,9 @@ def test_ceiling_library_exports_and_validation():
     assert L.ceil_lds(0, None, FAKE, FAKE + 4, 8, 10, None) == 2
     assert L.ceil_lds(0, None, FAKE, FAKE, 0, 10, None) == 3
     assert L.ceil_lds(0, None, FAKE, FAKE, 8, 0, None) == 3
-    assert L.ceil_lds(3, None, FAKE, FAKE, 8, 10, None) == 3
+    assert L.ceil_lds(7, None, FAKE, FAKE, 8, 10, None) == 3
+    assert L.ceil_lds(4, None, FAKE, FAKE, 8, 10, None) == 1  # DMA half reads src
+    assert L.ceil_lds(6, None, FAKE, FAKE, 8, 10, None) == 1
 
 
 def test_tile_shapes():

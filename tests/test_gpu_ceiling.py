@@ -63,7 +63,7 @@ def test_lds_read_b128_folds_the_chunks_it_claims_to_read(ceiling):
     ((8w + j) * 1024 + 16 l + 64 t) mod 65536, 16-byte aligned)."""
     grid, iters = 4, 3
     fold = torch.zeros(grid * 512, dtype=torch.int32, device="cuda")
-    clocks = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    clocks = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
     ceiling.lds(0, None, fold, clocks, grid, iters)
     torch.cuda.synchronize()
     want = []
@@ -76,18 +76,19 @@ def test_lds_read_b128_folds_the_chunks_it_claims_to_read(ceiling):
         want.append(acc)
     got = fold.view(grid, 512).cpu()
     assert all(got[g].tolist() == want for g in range(grid))
-    c = clocks.view(grid, 2).cpu()
-    assert bool((c[:, 0] > 0).all()) and bool((c[:, 1] > 0).all())
+    c = clocks.view(grid, 4).cpu()
+    assert bool((c[:, 0] > 0).all()) and bool((c[:, 2] > 0).all())  # waves 0 and 4 timed their loops
 
 
-@pytest.mark.parametrize("op", [1, 2])
+@pytest.mark.parametrize("op", [1, 2, 3, 4, 5, 6])
 def test_lds_ceiling_ops_run(ceiling, op):
     grid, iters = 8, 4
     src = torch.zeros(65536 + 1024, dtype=torch.uint8, device="cuda")
     fold = torch.full((grid * 512,), 7, dtype=torch.int32, device="cuda")
-    clocks = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    clocks = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
     ceiling.lds(op, src, fold, clocks, grid, iters)
     torch.cuda.synchronize()
-    assert bool((clocks.view(grid, 2)[:, 0] > 0).all())
-    if op == 2:
-        assert bool((fold == 0).all())  # the DMA op reads nothing into registers
+    c = clocks.view(grid, 4).cpu()
+    assert bool((c[:, 0] > 0).all()) and bool((c[:, 2] > 0).all())
+    if op in (2, 3, 6):
+        assert bool((fold == 0).all())  # nothing is read into registers

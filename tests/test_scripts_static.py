@@ -1,0 +1,54 @@
+"""Static name check of the top-level scripts that only a GPU machine runs in full
+(bench.py, __graft_entry__.py): every function they call by plain name must be
+defined, imported or bound somewhere in scope, so that a helper removed by
+mistake fails here instead of midway through a GPU run."""
+import ast
+import builtins
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bound_names(node):
+    """Names bound anywhere inside `node` (parameters, assignments, imports,
+    loop and comprehension targets, with-as, except-as, nested defs)."""
+    names = set()
+    for n in ast.walk(node):
+        if isinstance(n, (ast.FunctionDef, ast.AsyncFunctionDef, ast.ClassDef)):
+            names.add(n.name)
+        if isinstance(n, (ast.FunctionDef, ast.AsyncFunctionDef, ast.Lambda)):
+            a = n.args
+            for arg in a.posonlyargs + a.args + a.kwonlyargs:
+                names.add(arg.arg)
+            if a.vararg:
+                names.add(a.vararg.arg)
+            if a.kwarg:
+                names.add(a.kwarg.arg)
+        elif isinstance(n, ast.Name) and isinstance(n.ctx, ast.Store):
+            names.add(n.id)
+        elif isinstance(n, (ast.Import, ast.ImportFrom)):
+            for al in n.names:
+                names.add((al.asname or al.name).split(".")[0])
+        elif isinstance(n, ast.ExceptHandler) and n.name:
+            names.add(n.name)
+    return names
+
+
+@pytest.mark.parametrize("script", ["bench.py", "__graft_entry__.py"])
+def test_called_names_resolve(script):
+    tree = ast.parse(open(os.path.join(ROOT, script)).read())
+    module_names = set()
+    for n in tree.body:
+        module_names |= _bound_names(n) if not isinstance(
+            n, (ast.FunctionDef, ast.AsyncFunctionDef, ast.ClassDef)) else {n.name}
+    missing = []
+    for fn in [n for n in ast.walk(tree) if isinstance(n, (ast.FunctionDef, ast.AsyncFunctionDef))]:
+        local = _bound_names(fn)
+        for call in [c for c in ast.walk(fn) if isinstance(c, ast.Call)]:
+            if isinstance(call.func, ast.Name):
+                name = call.func.id
+                if name not in local and name not in module_names and not hasattr(builtins, name):
+                    missing.append(f"{fn.name}: {name}")
+    assert not missing, missing
