@@ -28,9 +28,11 @@ FETCH_SIZE / WRITE_SIZE counters (scaled by the counts the same counters give
 for a known-size device copy), read from the committed counter summary under
 profiles/ -- reported only while the kernel sources are unchanged since.
 
-Timing: `warmup` untimed steps, then exactly `steps` steps between
-synchronisations; per-launch kernel time from HIP events recorded on the
-launch stream. Inputs are generated on the device before the timed region.
+Timing: first `--settle` seconds (default 1) of untimed headline copies so
+that the device reaches steady clocks; then, per measurement, `warmup`
+untimed steps and exactly `steps` steps between synchronisations; per-launch
+kernel time from HIP events recorded on the launch stream. Inputs are
+generated on the device before the timed region.
 
 cpu_baseline: the CPU oracle (oracle.results.tile_copy) timed on a bounded
 sample of the same matrix on the host, single-threaded numpy.
@@ -196,6 +198,31 @@ def copy_buffers():
     return _COPY_BUF["src"], _COPY_BUF["dst"]
 
 
+def run_for(fn, seconds):
+    """Untimed launches of `fn` for about `seconds`, synchronising every 100
+    launches; returns the number of launches."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(100):
+            fn()
+        torch.cuda.synchronize()
+        n += 100
+    return n
+
+
+def settle(seconds):
+    """Untimed headline copies for about `seconds`, so that clocks and power
+    state settle before anything is timed."""
+    import async_stage_tile_amd as pt
+    src, dst = copy_buffers()
+    t0 = time.perf_counter()
+    n = run_for(pt.copy_launcher(src, dst), seconds)
+    log(f"[bench] settle: {n} untimed copies in {time.perf_counter() - t0:.2f} s")
+
+
 def bench_copy(stages, steps, warmup, stats=False, **cfg):
     """The library's default copy configuration, with `stages` and any overrides."""
     import torch
@@ -255,9 +282,11 @@ def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
     return r
 
 
-def bench_gemm(steps, warmup, stages=None, out_dtype=None, **cfg):
+def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, **cfg):
     """The library's default GEMM configuration (at `stages`, if given); C in
-    fp32, or bf16 through the staged epilogue."""
+    fp32, or bf16 through the staged epilogue. `settle_s` seconds of untimed
+    launches come first: the matrix cores' clock settles apart from the
+    streaming kernels'."""
     import torch
 
     import async_stage_tile_amd as pt
@@ -270,6 +299,8 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, **cfg):
     if stages is not None:
         kw["stages"] = stages
     fn = pt.gemm_launcher(A, B, C, **kw)
+    if settle_s > 0:
+        run_for(fn, settle_s)
     wall, kern = timed_launches(fn, steps, warmup)
     med, mn = launch_stats(fn, max(steps, 20), 0)
     flops = 2.0 * n * n * n
@@ -461,8 +492,11 @@ def cpu_oracle_extras(copy_rows, rowsum_rows, gemm_rows):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed headline copies before any measurement, so that "
+                         "the device reaches steady clocks (0 = none)")
     ap.add_argument("--stages", type=int, default=None,
                     help="ring depth (default: the library default of the workload, 2 for "
                          "the copy -- the best of the S sweeps measured on MI355X); 0 = the "
@@ -524,12 +558,14 @@ def main():
         log(f"[bench] ceilings: {r}")
         return
 
+    if args.settle > 0:
+        settle(args.settle)
     extras = {}
     stages = 2 if args.stages is None else args.stages
     if not args.no_extras or stages == 0:
         sweep = []
         for s in (1, 2, 3, 4, 6, 8):
-            r = bench_copy(s, max(3, args.steps // 2), 2)
+            r = bench_copy(s, max(3, args.steps // 2), args.warmup)
             log(f"[bench] sweep S={s}: {r['gbs']:.1f} GB/s")
             sweep.append({k: r[k] for k in ("stages", "kernel_ms", "gbs", "bit_exact",
                                             "lds_bytes")})
@@ -555,7 +591,7 @@ def main():
             wide[name]["kernel_pct_of_peak"] = round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)
             log(f"[bench] copy, {name} tiles: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
         extras["copy_wide_tiles"] = wide
-        u = bench_copy(2, max(3, args.steps // 2), 2, consumer_waves=2,
+        u = bench_copy(2, max(3, args.steps // 2), args.warmup, consumer_waves=2,
                        flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
                        pt.PIPE_FLAG_XCD_REMAP)
         extras["copy_unified"] = {k: u[k] for k in ("stages", "consumer_waves", "flags",
@@ -563,35 +599,35 @@ def main():
         log(f"[bench] unified copy: {u['gbs']:.1f} GB/s")
         _COPY_BUF.clear()
         torch.cuda.empty_cache()
-        r = bench_rowsum(max(3, args.steps // 2), 2, stats=True)
+        r = bench_rowsum(max(3, args.steps // 2), args.warmup, stats=True)
         log(f"[bench] rowsum: {r['gbs']:.1f} GB/s")
         extras["rowsum_8192x65536_fp16"] = r
-        r = bench_rowsum(max(3, args.steps // 2), 2, stages=2, consumer_waves=2, split=16,
+        r = bench_rowsum(max(3, args.steps // 2), args.warmup, stages=2, consumer_waves=2, split=16,
                          flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
                          pt.PIPE_FLAG_XCD_REMAP)
         log(f"[bench] unified rowsum: {r['gbs']:.1f} GB/s")
         extras["rowsum_unified"] = r
         wide = {}
         for name, cfg in WIDE_ROWSUM.items():
-            w = bench_rowsum(max(3, args.steps // 2), 2, **cfg)
+            w = bench_rowsum(max(3, args.steps // 2), args.warmup, **cfg)
             w["kernel_pct_of_peak"] = round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)
             wide[name] = w
             log(f"[bench] rowsum, {name}: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
         extras["rowsum_wide_tiles"] = wide
         _ROWSUM_BUF.clear()
         torch.cuda.empty_cache()
-        g = bench_gemm(max(3, args.steps // 2), 2)
+        g = bench_gemm(max(3, args.steps // 2), args.warmup)
         log(f"[bench] gemm: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16"] = g
-        g = bench_gemm(max(3, args.steps // 2), 2, out_dtype=torch.bfloat16)
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, out_dtype=torch.bfloat16)
         log(f"[bench] gemm, bf16 C: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16"] = g
-        g = bench_gemm(max(3, args.steps // 2), 2, out_dtype=torch.bfloat16,
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, out_dtype=torch.bfloat16,
                        flags=pt.PIPE_FLAG_EAGER_NEWEST | pt.PIPE_FLAG_GEMM_STORE_WAVE)
         log(f"[bench] gemm, bf16 C via a store wave: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16_store_wave"] = g
         torch.cuda.empty_cache()
-        c = bench_ceilings(max(3, args.steps // 2), 2)
+        c = bench_ceilings(max(3, args.steps // 2), args.warmup)
         log(f"[bench] ceilings: copy {c['best_copy_gbs']:.1f}, read {c['best_read_gbs']:.1f} GB/s")
         c["copy_frac_of_best_copy_ceiling"] = head["kernel_gbs"] / c["best_copy_gbs"]
         s128 = c["column_strips"]["128B"]
