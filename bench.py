@@ -502,6 +502,8 @@ def main():
                          "the copy -- the best of the S sweeps measured on MI355X); 0 = the "
                          "best of this run's 1..4 copy sweep")
     ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "rowsum",
                                        "rowsum_32x256", "gemm", "gemm_bf16", "ceiling", "calib"],
                     default=None,
@@ -640,7 +642,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("[bench] cpu baseline ...")
-        cpu = cpu_baseline(args.cpu_rows)
+        cpu = cpu_baseline(args.cpu_rows, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu['value']:.2f} GB/s")
         if not args.no_extras:
             extras["cpu_oracle"] = cpu_oracle_extras(2048, 256, 64)
