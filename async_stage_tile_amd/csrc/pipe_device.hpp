@@ -9,10 +9,9 @@
 //     phase is no longer p ("cute（12）async_pipeline" 6.2; mlc.ai
 //     "chapter_async_barriers", section mbarrier). Here one LDS word per
 //     barrier, in one of two encodings (Counter, Flip; see below). gfx950 has
-//     no transaction-byte
-//     counter, so the producer arrives on "full" only after `s_waitcnt vmcnt`
-//     shows that the stage's loads have landed in LDS: arrivals == 0 and
-//     bytes == 0 collapse into one arrival.
+//     no transaction-byte counter, so the producer arrives on "full" only
+//     after `s_waitcnt vmcnt` shows that the stage's loads have landed in LDS:
+//     arrivals == 0 and bytes == 0 collapse into one arrival.
 //   * PipelineState (index, phase, count) with ++ wrapping the index and
 //     flipping the phase; producers start at phase 1 so the first lap never
 //     waits ("cute（12）async_pipeline" 2.2-2.3, 6.1). Kept in SGPRs (the
@@ -47,7 +46,6 @@ constexpr int kTileBytes = kTileRows * kRowBytes;         // 16384
 constexpr int kBlockBytes = kWave * kChunkBytes;          // 1024 = one wave-wide DMA
 constexpr int kBlocksPerTile = kTileBytes / kBlockBytes;  // 16
 constexpr int kRowsPerBlock = kBlockBytes / kRowBytes;    // 8
-
 
 // Tile shapes of the stream kernels. Every tile is 16 KiB: kRows x TC fp16
 // with TC (tileN) in {64, 128, 256} and kRows (tileM) = 128, 64, 32. One
@@ -202,16 +200,16 @@ __device__ __forceinline__ void wait_vmcnt_mul(int k) {
 }
 
 // producer_acquire with eager commits. Waits until slot `index` is released
-// (its EMPTY barrier left phase `phase`); commits arrive on FULL barriers. While the slot is still in use and
+// (its EMPTY barrier left phase `phase`). While the slot is still in use and
 // this wave has at least `eager_min` tiles in flight that it has not yet
-// committed (eager_min = 0: never), it commits the oldest of them (once its
-// LOADS loads have landed, i.e. at most LOADS * (pending - 1) remain
-// outstanding) instead of idling: the consumers may be waiting for exactly
-// that tile, and holding it back until the next issue would put a consumer
-// release and a producer wake-up between every two hand-offs. With
-// eager_min = 2 the newest tile in flight is never waited for here, so the
-// producer does not stall its next issue on a load it has only just begun.
-// Returns false on timeout.
+// committed (eager_min = 0: never), it commits the oldest of them on its FULL
+// barrier (once its LOADS loads have landed, i.e. at most
+// LOADS * (pending - 1) remain outstanding) instead of idling: the consumers
+// may be waiting for exactly that tile, and holding it back until the next
+// issue would put a consumer release and a producer wake-up between every two
+// hand-offs. With eager_min = 2 the newest tile in flight is never waited for
+// here, so the producer does not stall its next issue on a load it has only
+// just begun. Returns false on timeout.
 template <int LOADS, int S, class EMPTY, class FULL>
 __device__ __forceinline__ bool acquire_slot(uint32_t* empty_bar, uint32_t phase,
                                              uint32_t* full_bars, int index, int& pending,

@@ -9,9 +9,10 @@
 // phase 1 (2.3). The tile use of the copy is the write-back of
 // "cute（11）hopper之TMA_copy" (code step 6, section 4).
 //
-// Work decomposition: tiles are 128 rows x 64 fp16 (16 KiB). A strip is one
-// tile column walked downwards (copy default) or one tile row walked along the
-// columns (rowsum, or copy with PIPE_FLAG_ROW_STRIPS). Each strip is cut into
+// Work decomposition: tiles are 16 KiB, 128 rows x 64 fp16 (the pages' tile)
+// or the wider 64 x 128 and 32 x 256 (TileShape<TC>, TC = tile columns). A
+// strip is one tile column walked downwards (copy default) or one tile row
+// walked along the columns (rowsum, or copy with PIPE_FLAG_ROW_STRIPS). Each strip is cut into
 // `split` segments; item i is segment i / n_strips of strip i % n_strips, so
 // workgroups launched together touch neighbouring strips. A segment is either
 // a contiguous run of the strip's tiles, or (interleaved) every split-th tile
@@ -29,10 +30,12 @@
 // out-of-range positions when they store, checksum or sum. Divisible shapes
 // run the unmasked instantiation, which carries none of these tests.
 //
-// Slot layout: tile row r (128 B) holds its 16-byte chunk c at position
-// c ^ ((r >> shift) & 7). One producer DMA instruction q moves rows 8q..8q+7:
-// lane l writes LDS position l & 7 of row 8q + (l >> 3), so it fetches the
-// global chunk swz(row, l & 7). With PW producer waves (1, 2 or 4), wave w
+// Slot layout: a tile row of CPR 16-byte chunks (CPR = 8, 16, 32 for TC = 64,
+// 128, 256) holds chunk c at position c ^ ((r >> shift) & (CPR - 1)). One
+// producer DMA instruction q moves the 1 KiB block of rows RPB*q ..
+// RPB*(q+1) - 1 (RPB = 64 / CPR rows per block): lane l writes position
+// l % CPR of row RPB*q + l / CPR, so it fetches the global chunk
+// swz_n(row, l % CPR). With PW producer waves (1, 2 or 4), wave w
 // issues blocks (16/PW)w .. (16/PW)(w+1)-1 of every tile and full[s] expects PW
 // arrivals. A wave may keep `lag` committed-later tiles in flight as long as
 // (lag + 1) * 16/PW loads fit the 63-entry vmcnt counter: lag <= 2, 6, 14.

@@ -87,13 +87,45 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """sha256 (first 16 hex digits) of the device sources of the stream kernel."""
+def strip_comments(src):
+    """C/C++ source text without comments and with every run of whitespace
+    reduced to one space (string and character literals kept as they are), so
+    that edits to comments or layout do not count as kernel changes."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_hash(read=None):
+    """sha256 (first 16 hex digits) of the stream kernel's device sources with
+    comments and layout removed (strip_comments). `read(name)` returns a
+    source's text (default: the file under async_stage_tile_amd/csrc)."""
     import hashlib
+
+    def read_file(name):
+        with open(os.path.join(ROOT, "async_stage_tile_amd", "csrc", name)) as fh:
+            return fh.read()
+
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "async_stage_tile_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(strip_comments((read or read_file)(f)).encode())
     return h.hexdigest()[:16]
 
 

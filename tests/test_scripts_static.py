@@ -52,3 +52,13 @@ def test_called_names_resolve(script):
                 if name not in local and name not in module_names and not hasattr(builtins, name):
                     missing.append(f"{fn.name}: {name}")
     assert not missing, missing
+
+
+def test_kernel_hash_ignores_comments_and_layout_only():
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    src = 'int a = 1; // note\n/* block\n comment */\nasm("s_nop 0\\n\\tx // kept");  char c = \'"\';\n'
+    assert bench.strip_comments(src) == 'int a = 1; asm("s_nop 0\\n\\tx // kept"); char c = \'"\';'
+    assert bench.strip_comments(src) == bench.strip_comments(src.replace("note", "other note"))
+    assert bench.strip_comments(src) != bench.strip_comments(src.replace("a = 1", "a = 2"))
