@@ -5,7 +5,7 @@
 
 #include <mutex>
 
-#include "../../include/pipe_tile.h"
+#include "pipe_tile.h"
 #include "pipe_kernels.hpp"
 
 namespace {
