@@ -189,6 +189,21 @@ def _stream(stream=None):
     return ctypes.c_void_p(int(s.cuda_stream))
 
 
+def matrix_geometry(shape, strides, name="matrix"):
+    """(rows, cols, row pitch in elements) of a 2-D row-major view, or
+    ValueError. Columns must be adjacent (unit stride) and rows must not
+    overlap (row stride >= cols): the kernels address row r at r * pitch, so a
+    broadcast or overlapping view would make them read or write outside it."""
+    if len(shape) != 2:
+        raise ValueError(f"{name} must be 2-D")
+    rows, cols = int(shape[0]), int(shape[1])
+    if cols > 1 and strides[1] != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+    if rows > 1 and strides[0] < cols:
+        raise ValueError(f"{name} rows overlap (row stride {strides[0]} < {cols} columns)")
+    return rows, cols, max(int(strides[0]), cols)
+
+
 def _check_matrix(t, name, dtypes):
     import torch
     if not isinstance(t, torch.Tensor):
@@ -197,9 +212,7 @@ def _check_matrix(t, name, dtypes):
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} dtype {t.dtype} not in {dtypes}")
-    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
-        raise ValueError(f"{name} must be a 2-D row-major tensor (unit column stride)")
-    return t.shape[0], t.shape[1], max(t.stride(0), t.shape[1])
+    return matrix_geometry(tuple(t.shape), t.stride() if t.dim() == 2 else (), name)
 
 
 def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):

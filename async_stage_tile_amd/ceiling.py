@@ -61,10 +61,12 @@ def memcpy(src, dst, stream=None) -> None:
 
 
 def _region(t):
-    """(rows, pitch bytes, width bytes) of a row-major 2-D tensor."""
-    assert t.dim() == 2 and t.stride(1) == 1
+    """(rows, pitch bytes, width bytes) of a row-major 2-D tensor whose rows do
+    not overlap."""
+    if t.dim() != 2 or t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) < t.shape[1]):
+        raise ValueError("a 2-D row-major tensor with non-overlapping rows is required")
     es = t.element_size()
-    return t.shape[0], t.stride(0) * es, t.shape[1] * es
+    return t.shape[0], max(t.stride(0), t.shape[1]) * es, t.shape[1] * es
 
 
 def strip_copy(src, dst, strip_bytes: int, split: int = 1, stream=None) -> None:

@@ -269,3 +269,20 @@ def test_barrier_arrival_counts_stay_below_2_31():
     cfg = pt.make_config(0, stages=2, producer_waves=1, consumer_waves=8, grid=1)
     M = 128 << 28                      # 2^28 tiles in one strip, one workgroup
     assert _copy(FAKE, FAKE, M, 64, 64, 64, cfg) == pt.PIPE_ERR_SHAPE
+
+
+def test_binding_rejects_views_the_kernels_cannot_address():
+    """The binding passes (rows, cols, pitch) to the library; a view whose rows
+    overlap (a broadcast row, stride 0) or whose columns are not adjacent must
+    be refused before anything is launched."""
+    g = pt.matrix_geometry
+    assert g((4, 8), (8, 1)) == (4, 8, 8)
+    assert g((4, 8), (16, 1)) == (4, 8, 16)        # padded rows
+    assert g((1, 8), (0, 1)) == (1, 8, 8)          # a single row: its stride is never used
+    assert g((4, 1), (1, 1)) == (4, 1, 1)          # one column
+    for shape, strides in (((4, 8), (0, 1)),       # broadcast row
+                           ((4, 8), (4, 1)),       # overlapping rows
+                           ((4, 8), (1, 4)),       # column-major
+                           ((4, 8, 2), (16, 2, 1))):
+        with pytest.raises(ValueError):
+            g(shape, strides)
