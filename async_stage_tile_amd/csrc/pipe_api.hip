@@ -69,11 +69,11 @@ pipe_config_t defaults(pipe_op_t op) {
       c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP | PIPE_FLAG_LAZY_COMMIT;
       break;
     case PIPE_OP_ROWSUM:
-      c.stages = 4;
+      c.stages = 3;
       c.producer_waves = 4;
       c.consumer_waves = 4;
       c.swizzle_shift = 0;
-      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP | PIPE_FLAG_EAGER_NEWEST;
+      c.flags = PIPE_FLAG_NONTEMPORAL | PIPE_FLAG_XCD_REMAP;
       break;
     default:
       c.stages = 2;

@@ -76,7 +76,9 @@ WIDE_COPY = {
                    flags=_NT | _RM | _IL | _LZ),
 }
 WIDE_ROWSUM = {
-    "32x256": dict(tile_m=32, tile_n=256, stages=3, producer_waves=4, consumer_waves=8, split=1,
+    "64x128": dict(tile_m=64, tile_n=128, stages=3, producer_waves=4, consumer_waves=4, split=2,
+                   flags=_NT | _RM),
+    "32x256": dict(tile_m=32, tile_n=256, stages=3, producer_waves=4, consumer_waves=4, split=1,
                    flags=_NT | _RM),
     "32x256_unified": dict(tile_m=32, tile_n=256, stages=2, consumer_waves=4, split=2,
                            flags=_U | _NT | _RM),
@@ -537,7 +539,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "rowsum",
-                                       "rowsum_32x256", "gemm", "gemm_bf16", "ceiling", "calib"],
+                                       "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
+                                       "ceiling", "calib"],
                     default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
@@ -571,8 +574,8 @@ def main():
         r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
         log(f"[bench] {args.only}: {r}")
         return
-    if args.only == "rowsum_32x256":
-        r = bench_rowsum(args.steps, args.warmup, **WIDE_ROWSUM["32x256"])
+    if args.only in ("rowsum_32x256", "rowsum_64x128"):
+        r = bench_rowsum(args.steps, args.warmup, **WIDE_ROWSUM[args.only.split("_")[1]])
         log(f"[bench] {args.only}: {r}")
         return
     if args.only == "rowsum":

@@ -141,8 +141,8 @@ const char* pipe_status_str(int status);
 /* Fill *cfg with the defaults of an op (grid and split automatic):
  *   copy:   stages 2, tile 128x64, 4 producer + 4 consumer waves,
  *           flags NONTEMPORAL | XCD_REMAP | LAZY_COMMIT, swizzle shift 0;
- *   rowsum: stages 4, tile 128x64, 4 producer + 4 consumer waves,
- *           flags NONTEMPORAL | XCD_REMAP | EAGER_NEWEST, swizzle shift 0;
+ *   rowsum: stages 3, tile 128x64, 4 producer + 4 consumer waves,
+ *           flags NONTEMPORAL | XCD_REMAP (eager commits), swizzle shift 0;
  *   gemm:   stages 2, tile 128x128x64, 4 producer + 4 consumer waves,
  *           flags EAGER_NEWEST, swizzle shift 1. */
 pipe_status_t pipe_config_default(pipe_op_t op, pipe_config_t* cfg);

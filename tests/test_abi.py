@@ -40,9 +40,8 @@ def test_config_defaults():
     assert c.flags == (pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP |
                        pt.PIPE_FLAG_LAZY_COMMIT)
     r = pt.make_config(pt.PIPE_OP_ROWSUM)
-    assert (r.stages, r.producer_waves, r.consumer_waves) == (4, 4, 4)
-    assert r.flags == (pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP |
-                       pt.PIPE_FLAG_EAGER_NEWEST)
+    assert (r.stages, r.producer_waves, r.consumer_waves) == (3, 4, 4)
+    assert r.flags == (pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP)
     g = pt.make_config(pt.PIPE_OP_GEMM)
     assert (g.stages, g.tile_m, g.tile_n, g.tile_k, g.producer_waves, g.consumer_waves) \
         == (2, 128, 128, 64, 4, 4)
