@@ -21,7 +21,10 @@ Also reported (in "extras"):
     matrix in the tile stream's own pattern (column strips 128 or 512 bytes
     wide);
   * the CPU oracle on bounded samples of the copy, row sum and GEMM, on one
-    thread and on all host threads.
+    thread and on all host threads;
+  * per-launch latency of the two small functional workloads (256 x 128 in
+    2 x 2 tiles through one slot; 128 x 512 through a three-slot ring of one
+    workgroup with per-tile checksums), each checked bit for bit.
 
 roofline.traffic: HBM bytes per launch of the headline kernel from rocprofv3
 FETCH_SIZE / WRITE_SIZE counters (scaled by the counts the same counters give
@@ -348,6 +351,40 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, **cfg):
                            "median_tflops": flops / (med * 1e-3) / 1e12}}
 
 
+def bench_small(reps, warmup):
+    """The two small functional workloads, timed per launch (they are too small
+    to load HBM, so latency is what they show): a 256 x 128 index-coded matrix
+    in 2 x 2 tiles of 128 x 64 through a one-slot ring, and a 128 x 512 matrix
+    through a three-slot ring of one workgroup (1 producer + 3 consumer waves)
+    with per-tile checksums. Each is checked bit for bit; the checksums against
+    a plain tensor sum of each tile's 16-bit codes."""
+    import torch
+
+    import async_stage_tile_amd as pt
+    import synth
+    out = {}
+    src = synth.index_coded(256, 128, device="cuda")
+    dst = torch.empty_like(src)
+    fn = pt.copy_launcher(src, dst, stages=1)
+    med, mn = launch_stats(fn, reps, warmup)
+    out["copy_256x128_s1"] = {"median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                              "bit_exact": torch.equal(dst.view(torch.int16),
+                                                       src.view(torch.int16))}
+    src = synth.uniform((128, 512), torch.float16, seed=42, device="cuda")
+    dst = torch.empty_like(src)
+    chk = torch.empty(8, dtype=torch.int32, device="cuda")
+    fn = pt.copy_launcher(src, dst, checksums=chk, stages=3, producer_waves=1, consumer_waves=3,
+                          grid=1, flags=0)
+    med, mn = launch_stats(fn, reps, warmup)
+    codes = src.view(torch.int16).to(torch.int64) & 0xFFFF
+    want = codes.view(128, 8, 64).sum(dim=(0, 2))
+    out["copy_128x512_s3_1p3c"] = {
+        "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+        "bit_exact": torch.equal(dst.view(torch.int16), src.view(torch.int16)),
+        "checksums_exact": torch.equal(chk.to(torch.int64) & 0xFFFFFFFF, want)}
+    return out
+
+
 def bench_ceilings(steps, warmup):
     """Context ceilings on this device for the copy's traffic (512 MiB each way)
     and for a 1 GiB read: no LDS ring, no tiles."""
@@ -664,6 +701,9 @@ def main():
         log(f"[bench] gemm, bf16 C via a store wave: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16_store_wave"] = g
         torch.cuda.empty_cache()
+        sm = bench_small(max(20, args.steps), args.warmup)
+        log(f"[bench] small configs: {sm}")
+        extras["small_configs"] = sm
         c = bench_ceilings(max(3, args.steps // 2), args.warmup)
         log(f"[bench] ceilings: copy {c['best_copy_gbs']:.1f}, read {c['best_read_gbs']:.1f} GB/s")
         c["copy_frac_of_best_copy_ceiling"] = head["kernel_gbs"] / c["best_copy_gbs"]
