@@ -53,6 +53,7 @@ PIPE_FLAG_TEST_NO_RELEASE = 0x200
 PIPE_FLAG_EAGER_NEWEST = 0x400
 PIPE_FLAG_GEMM_C_BF16 = 0x800
 PIPE_FLAG_GEMM_STORE_WAVE = 0x1000
+PIPE_FLAG_GEMM_B_COLMAJOR = 0x2000
 
 PIPE_STATUS_TIMEOUT_PRODUCER = 0x1
 PIPE_STATUS_TIMEOUT_CONSUMER = 0x2
@@ -261,26 +262,46 @@ def pipe_rowsum(A, out=None, workspace=None, stream=None, **cfg):
     return out
 
 
-def _gemm_config(C, cfg):
-    """The GEMM config, with PIPE_FLAG_GEMM_C_BF16 set from C's dtype."""
+def _gemm_config(C, cfg, b_colmajor=False):
+    """The GEMM config, with PIPE_FLAG_GEMM_C_BF16 set from C's dtype and
+    PIPE_FLAG_GEMM_B_COLMAJOR from B's layout."""
     import torch
     c = make_config(PIPE_OP_GEMM, **cfg)
     if C.dtype == torch.bfloat16:
         c.flags |= PIPE_FLAG_GEMM_C_BF16
     else:
         c.flags &= ~PIPE_FLAG_GEMM_C_BF16
+    if b_colmajor:
+        c.flags |= PIPE_FLAG_GEMM_B_COLMAJOR
+    else:
+        c.flags &= ~PIPE_FLAG_GEMM_B_COLMAJOR
     return c
+
+
+def _gemm_b(B):
+    """(K, N, ldb, column-major) of the B operand. A row-major B (unit column
+    stride) is passed as is; a column-major one (unit row stride, e.g. the
+    transpose of a row-major N x K tensor) goes with PIPE_FLAG_GEMM_B_COLMAJOR
+    and ldb = its column stride."""
+    import torch
+    if B.dim() == 2 and B.shape[1] > 1 and B.stride(1) != 1 and B.stride(0) == 1:
+        N, K, ldb = _check_matrix(B.t(), "B (column-major)", (torch.bfloat16,))
+        return K, N, ldb, True
+    K, N, ldb = _check_matrix(B, "B", (torch.bfloat16,))
+    return K, N, ldb, False
 
 
 def pipe_gemm_mainloop(A, B, C=None, stream=None, out_dtype=None, **cfg):
     """C = A @ B (bf16 in, fp32 accumulate) with A/B tiles fed through the ring.
 
-    C is fp32 (default) or bf16 (out_dtype=torch.bfloat16, or a bf16 C): a bf16
-    C is rounded to nearest even from the fp32 sums and written through the
-    staged epilogue."""
+    B may be row-major (K x N) or column-major (a K x N view with unit row
+    stride, such as Bt.t() of a row-major N x K Bt). C is fp32 (default) or
+    bf16 (out_dtype=torch.bfloat16, or a bf16 C): a bf16 C is rounded to
+    nearest even from the fp32 sums and written through the staged
+    epilogue."""
     import torch
     M, K, lda = _check_matrix(A, "A", (torch.bfloat16,))
-    K2, N, ldb = _check_matrix(B, "B", (torch.bfloat16,))
+    K2, N, ldb, b_col = _gemm_b(B)
     if K2 != K:
         raise ValueError("inner dimensions differ")
     if C is None:
@@ -288,7 +309,7 @@ def pipe_gemm_mainloop(A, B, C=None, stream=None, out_dtype=None, **cfg):
     Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32, torch.bfloat16))
     if (Mc, Nc) != (M, N):
         raise ValueError("C shape mismatch")
-    c = _gemm_config(C, cfg)
+    c = _gemm_config(C, cfg, b_col)
     st = lib().pipe_gemm_mainloop(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                   ctypes.byref(c), _stream(stream))
     _check(st, "pipe_gemm_mainloop")
@@ -347,11 +368,11 @@ def rowsum_launcher(A, out, workspace=None, stream=None, **cfg):
 def gemm_launcher(A, B, C, stream=None, **cfg):
     import torch
     M, K, lda = _check_matrix(A, "A", (torch.bfloat16,))
-    K2, N, ldb = _check_matrix(B, "B", (torch.bfloat16,))
+    K2, N, ldb, b_col = _gemm_b(B)
     Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32, torch.bfloat16))
     if K2 != K or (Mc, Nc) != (M, N):
         raise ValueError("shape mismatch")
-    c = _gemm_config(C, cfg)
+    c = _gemm_config(C, cfg, b_col)
     fn, args = lib().pipe_gemm_mainloop, (_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                            ctypes.byref(c), _stream(stream))
 

@@ -28,6 +28,7 @@ constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_F
                                  PIPE_FLAG_SPLIT_INTERLEAVE | PIPE_FLAG_UNIFIED |
                                  PIPE_FLAG_LAZY_COMMIT | PIPE_FLAG_EAGER_NEWEST |
                                  PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE |
+                                 PIPE_FLAG_GEMM_B_COLMAJOR |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -107,7 +108,8 @@ pipe_status_t check_common(const pipe_config_t& c) {
 pipe_status_t check_stream_cfg(const pipe_config_t& c) {
   pipe_status_t s = check_common(c);
   if (s != PIPE_OK) return s;
-  if (c.flags & (PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_GEMM_STORE_WAVE))
+  if (c.flags & (PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_B_LINEAR | PIPE_FLAG_GEMM_STORE_WAVE |
+                 PIPE_FLAG_GEMM_B_COLMAJOR))
     return PIPE_ERR_CONFIG;
   if (c.stages < 1 || c.stages > 8) return PIPE_ERR_STAGES;
   // 16 KiB tiles: the pages' 128 x 64, or the wider 64 x 128 and 32 x 256.
@@ -373,12 +375,15 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
   if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE)) return PIPE_ERR_CONFIG;
   const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
   const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
+  const bool b_col = (c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) != 0;
   if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
+  if (b_col && (c.flags & PIPE_FLAG_GEMM_B_LINEAR)) return PIPE_ERR_CONFIG;
   if (gemm_lds_bytes(c.stages, c_bf16, store_wave) > kLdsLimit) return PIPE_ERR_STAGES;
-  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return PIPE_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < (b_col ? K : N) || ldc < N)
+    return PIPE_ERR_SHAPE;
   if (M % 128 != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
-  if (!extent_fits(M, lda, 2) || !extent_fits(K, ldb, 2) ||
+  if (!extent_fits(M, lda, 2) || !extent_fits(b_col ? N : K, ldb, 2) ||
       !extent_fits(M, ldc, (c.flags & PIPE_FLAG_GEMM_C_BF16) ? 2 : 4))
     return PIPE_ERR_SHAPE;
   if (M == 0 || N == 0) return PIPE_OK;
@@ -409,6 +414,7 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
   p.items = (int32_t)items;
   p.swz_shift = c.swizzle_shift;
   p.b_swz = (c.flags & PIPE_FLAG_GEMM_B_LINEAR) ? 0 : 1;
+  p.b_colmajor = b_col ? 1 : 0;
   p.eager = eager_min_pending(c.flags);
   p.c_bf16 = c_bf16 ? 1 : 0;
   p.store_wave = store_wave ? 1 : 0;
@@ -441,6 +447,8 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
     const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
     if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
+    if ((c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) && (c.flags & PIPE_FLAG_GEMM_B_LINEAR))
+      return PIPE_ERR_CONFIG;
     info->lds_bytes = gemm_lds_bytes(c.stages, c_bf16, store_wave);
     info->threads = gemm_threads(c.producer_waves, c_bf16, store_wave);
     info->items = (int32_t)items;

@@ -29,7 +29,11 @@
 // fb(k) = ((k & 3) << 2) ^ (((k >> 3) & 1) << 1), which puts the four K-rows
 // (and the two K-halves) that one transposing read touches on different banks.
 //
-// B fragments use the gfx950 transposing LDS read ds_read_b64_tr_b16. Within
+// Column-major B (PIPE_FLAG_GEMM_B_COLMAJOR, gemm_kernel_bcol): a B tile is
+// then 128 rows (output columns) of 64 K values, the shape of an A tile, and is
+// loaded, swizzled and read exactly like one (one ds_read_b128 per fragment).
+//
+// Row-major B fragments use the gfx950 transposing LDS read ds_read_b64_tr_b16. Within
 // each group of 16 lanes, lane i receives element e (0..3) from the address
 // given by lane 4e + i/4 of its group, offset by 2*(i%4) bytes (lane layout
 // checked on the device by an index-coded probe). So if lane i of the group
@@ -117,7 +121,7 @@ __device__ __forceinline__ int swz_b(int k, int on) {
   return on ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : 0;
 }
 
-template <int S, int PW>
+template <int S, int PW, bool BCOL>
 __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
   constexpr int kLoads = 32 / PW;                     // DMA instructions per stage per wave
   constexpr int kMaxLag = 48 / kLoads - 1;            // (lag + 1) stages <= 48 loads
@@ -132,7 +136,10 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
     int tm, tn;
     gemm_tile_of(p, item, tm, tn);
     const uint8_t* ga = p.A + (int64_t)tm * kGemmTile * p.lda;
-    const uint8_t* gb = p.B + (int64_t)tn * kBRowBytes;
+    // Row-major B: the tile's columns start tn * 256 bytes into each K-row.
+    // Column-major B: its rows (one per output column) start at row tn * 128.
+    const uint8_t* gb = BCOL ? p.B + (int64_t)tn * kGemmTile * p.ldb
+                             : p.B + (int64_t)tn * kBRowBytes;
     for (int ks = 0; ks < p.k_steps; ++ks) {
       if (!acquire_slot<kLoads, S, Counter<4>, Counter<PW>>(&lds.empty[w.index], w.phase,
                                                              lds.full, w.index, pending, p.eager,
@@ -150,6 +157,17 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
           const int r = q * 8 + (lane >> 3);
           const int c = swz(r, lane & 7, p.swz_shift);
           dma_block(a0 + (int64_t)r * p.lda + c * 16, sa + q * kBlockBytes);
+        }
+      } else if constexpr (BCOL) {
+        // Column-major B: the same 128 x 64 row layout and swizzle as A.
+        const uint32_t sb = uniform(lds_addr(&lds.b[w.index][0]));
+        const uint8_t* b0 = gb + (int64_t)ks * kGemmK * 2;
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+          const int q = part * kLoads + j;
+          const int r = q * 8 + (lane >> 3);
+          const int c = swz(r, lane & 7, p.swz_shift);
+          dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + q * kBlockBytes);
         }
       } else {
         const uint32_t sb = uniform(lds_addr(&lds.b[w.index][0]));
@@ -219,17 +237,28 @@ struct SubFrags {
   bf16x8 b[2];
 };
 
+// A fragment (and, for column-major B, a B fragment): lane l takes the K
+// chunk kk * 2 + l / 32 of row row0 + l % 32 of a 128 x 64 slot, one b128 read.
+__device__ __forceinline__ bf16x8 load_row_frag(const uint8_t* slot, int row0, int kk, int li,
+                                                int lk, int shift) {
+  const int r = row0 + li;
+  const int c = swz(r, kk * 2 + lk, shift);
+  return *reinterpret_cast<const bf16x8*>(slot + r * 128 + c * 16);
+}
+
+template <bool BCOL>
 __device__ __forceinline__ void load_sub(SubFrags& f, int kk, const uint8_t* sa,
                                          const uint8_t* sb, int wm, int wn, int li, int lk,
                                          int lane, const GemmParams& p) {
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int r = wm * 64 + mi * 32 + li;
-    const int c = swz(r, kk * 2 + lk, p.swz_shift);
-    f.a[mi] = *reinterpret_cast<const bf16x8*>(sa + r * 128 + c * 16);
-  }
+  for (int mi = 0; mi < 2; ++mi) f.a[mi] = load_row_frag(sa, wm * 64 + mi * 32, kk, li, lk, p.swz_shift);
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) f.b[ni] = load_b_frag(sb, kk * 16, wn * 64 + ni * 32, lane, p.b_swz);
+  for (int ni = 0; ni < 2; ++ni) {
+    if constexpr (BCOL)
+      f.b[ni] = load_row_frag(sb, wn * 64 + ni * 32, kk, li, lk, p.swz_shift);
+    else
+      f.b[ni] = load_b_frag(sb, kk * 16, wn * 64 + ni * 32, lane, p.b_swz);
+  }
 }
 
 __device__ __forceinline__ void mfma_sub(f32x16 (&acc)[2][2], const SubFrags& f) {
@@ -241,17 +270,21 @@ __device__ __forceinline__ void mfma_sub(f32x16 (&acc)[2][2], const SubFrags& f)
 }
 
 // Scheduling hint for a block that holds one sub-step's fragment reads (6 LDS
-// reads) and the previous sub-step's 4 MFMAs: alternate one MFMA with two
-// reads, so that the reads of the next sub-step issue while the matrix core
-// works, instead of being sunk next to their uses.
+// reads with row-major B) and the previous sub-step's 4 MFMAs: alternate one
+// MFMA with two reads, so that the reads of the next sub-step issue while the
+// matrix core works, instead of being sunk next to their uses.
+// Column-major B makes it 4 reads (all b128), one after each MFMA.
+template <bool BCOL>
 __device__ __forceinline__ void interleave_mfma_reads() {
+  constexpr int kReads = BCOL ? 1 : 2;  // LDS reads after each of the first MFMAs
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // LDS read
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (BCOL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 }
 
 // Consumer wave. Fragment reads run one K sub-step ahead of the MFMAs through
@@ -259,7 +292,7 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // reads of the slot to return, releases the slot, then waits on full for the
 // next stage (while the previous MFMAs still execute) and reads that stage's
 // first sub-step before issuing the last MFMAs of the current one.
-template <int S, int PW, int EPI>
+template <int S, int PW, int EPI, bool BCOL>
 __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_lds, int cw) {
   OutLds* out = static_cast<OutLds*>(out_lds);
   const int lane = lane_id();
@@ -285,17 +318,17 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
     }
     const uint8_t* sa = &lds.a[rd.index][0];
     const uint8_t* sb = &lds.b[rd.index][0];
-    load_sub(b0, 0, sa, sb, wm, wn, li, lk, lane, p);
+    load_sub<BCOL>(b0, 0, sa, sb, wm, wn, li, lk, lane, p);
     for (int ks = 0; ks < p.k_steps; ++ks) {
-      load_sub(b1, 1, sa, sb, wm, wn, li, lk, lane, p);
+      load_sub<BCOL>(b1, 1, sa, sb, wm, wn, li, lk, lane, p);
       mfma_sub(acc, b0);
-      interleave_mfma_reads();
-      load_sub(b0, 2, sa, sb, wm, wn, li, lk, lane, p);
+      interleave_mfma_reads<BCOL>();
+      load_sub<BCOL>(b0, 2, sa, sb, wm, wn, li, lk, lane, p);
       mfma_sub(acc, b1);
-      interleave_mfma_reads();
-      load_sub(b1, 3, sa, sb, wm, wn, li, lk, lane, p);
+      interleave_mfma_reads<BCOL>();
+      load_sub<BCOL>(b1, 3, sa, sb, wm, wn, li, lk, lane, p);
       mfma_sub(acc, b0);
-      interleave_mfma_reads();
+      interleave_mfma_reads<BCOL>();
       // consumer_release: this wave's reads of the slot have all returned.
       wait_lgkmcnt0();
       Counter<4>::arrive(&lds.empty[rd.index]);
@@ -307,7 +340,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
         }
         sa = &lds.a[rd.index][0];
         sb = &lds.b[rd.index][0];
-        load_sub(b0, 0, sa, sb, wm, wn, li, lk, lane, p);
+        load_sub<BCOL>(b0, 0, sa, sb, wm, wn, li, lk, lane, p);
       }
       mfma_sub(acc, b1);
     }
@@ -439,9 +472,8 @@ __device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int PW, int EPI>
-__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)))
-    gemm_kernel(GemmParams p) {
+template <int S, int PW, int EPI, bool BCOL>
+__device__ __forceinline__ void gemm_body(const GemmParams& p) {
   __shared__ GemmLds<S> lds;
   const int wave = (int)(threadIdx.x >> 6);
   if (threadIdx.x < S) {
@@ -456,30 +488,56 @@ __global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0))
     }
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW>(p, lds, wave);
+      gemm_producer<S, PW, BCOL>(p, lds, wave);
     else if (wave < PW + 4)
-      gemm_consumer<S, PW, EPI>(p, lds, &out, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL>(p, lds, &out, wave - PW);
     else
       gemm_store_wave(p, out);
   } else if constexpr (EPI == kEpiWaveStaged) {
     __shared__ WaveOutLds out;
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW>(p, lds, wave);
+      gemm_producer<S, PW, BCOL>(p, lds, wave);
     else
-      gemm_consumer<S, PW, EPI>(p, lds, &out, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL>(p, lds, &out, wave - PW);
   } else {
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW>(p, lds, wave);
+      gemm_producer<S, PW, BCOL>(p, lds, wave);
     else
-      gemm_consumer<S, PW, EPI>(p, lds, nullptr, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL>(p, lds, nullptr, wave - PW);
   }
+}
+
+// B row-major (K x N, the default) and column-major (PIPE_FLAG_GEMM_B_COLMAJOR).
+template <int S, int PW, int EPI>
+__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)))
+    gemm_kernel(GemmParams p) {
+  gemm_body<S, PW, EPI, false>(p);
+}
+
+// At most 128 VGPRs (4 waves per SIMD), so that two 8-wave workgroups share a
+// CU as with row-major B (the store-wave variant runs one per CU anyway).
+template <int S, int PW, int EPI>
+__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)),
+                                  EPI == kEpiStoreWave ? 1 : 4)
+    gemm_kernel_bcol(GemmParams p) {
+  gemm_body<S, PW, EPI, true>(p);
 }
 
 template <int PW, int EPI>
 hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t stream) {
   const dim3 g(grid), b(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)));
+  if (p.b_colmajor) {
+    switch (stages) {
+      case 1: hipLaunchKernelGGL((gemm_kernel_bcol<1, PW, EPI>), g, b, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((gemm_kernel_bcol<2, PW, EPI>), g, b, 0, stream, p); break;
+      case 3: hipLaunchKernelGGL((gemm_kernel_bcol<3, PW, EPI>), g, b, 0, stream, p); break;
+      case 4: hipLaunchKernelGGL((gemm_kernel_bcol<4, PW, EPI>), g, b, 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (stages) {
     case 1: hipLaunchKernelGGL((gemm_kernel<1, PW, EPI>), g, b, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((gemm_kernel<2, PW, EPI>), g, b, 0, stream, p); break;

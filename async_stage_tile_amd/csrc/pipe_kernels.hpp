@@ -96,7 +96,8 @@ struct GemmParams {
   int32_t tiles_m, tiles_n, k_steps;
   int32_t items;          // output tiles
   int32_t swz_shift;
-  int32_t b_swz;          // 1: XOR-swizzle the B K-rows (default)
+  int32_t b_swz;          // 1: XOR-swizzle the B K-rows (default; row-major B only)
+  int32_t b_colmajor;     // B given column-major (N x K rows of K): loaded and read like A
   uint32_t spin_limit;
   uint32_t* status;
   uint32_t* trace;

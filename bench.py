@@ -319,7 +319,8 @@ def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
     return r
 
 
-def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, **cfg):
+def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colmajor=False,
+               **cfg):
     """The library's default GEMM configuration (at `stages`, if given); C in
     fp32, or bf16 through the staged epilogue. `settle_s` seconds of untimed
     launches come first: the matrix cores' clock settles apart from the
@@ -331,6 +332,8 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, **cfg):
     n = GEMM_N
     A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device="cuda")
     B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device="cuda")
+    if b_colmajor:  # the same values, stored column-major (B[k][n] at n * K + k)
+        B = B.t().contiguous().t()
     C = torch.empty((n, n), dtype=out_dtype or torch.float32, device="cuda")
     kw = dict(cfg)
     if stages is not None:
@@ -341,8 +344,9 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, **cfg):
     wall, kern = timed_launches(fn, steps, warmup)
     med, mn = launch_stats(fn, max(steps, 20), 0)
     flops = 2.0 * n * n * n
-    c = pt._gemm_config(C, kw)
-    return {"c_dtype": str(C.dtype).replace("torch.", ""), "stages": c.stages,
+    c = pt._gemm_config(C, kw, b_colmajor)
+    return {"c_dtype": str(C.dtype).replace("torch.", ""),
+            "b_layout": "column-major" if b_colmajor else "row-major", "stages": c.stages,
             "producer_waves": c.producer_waves, "flags": c.flags,
             "wall_ms": wall, "kernel_ms": kern, "flops": flops,
             "tflops": flops / (wall * 1e-3) / 1e12,
@@ -577,7 +581,7 @@ def main():
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "rowsum",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
-                                       "ceiling", "calib"],
+                                       "gemm_bcol", "ceiling", "calib"],
                     default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
@@ -622,6 +626,10 @@ def main():
     if args.only == "gemm":
         r = bench_gemm(args.steps, args.warmup, args.stages)
         log(f"[bench] gemm: {r}")
+        return
+    if args.only == "gemm_bcol":
+        r = bench_gemm(args.steps, args.warmup, args.stages, b_colmajor=True)
+        log(f"[bench] gemm, B column-major: {r}")
         return
     if args.only == "gemm_bf16":
         r = bench_gemm(args.steps, args.warmup, args.stages, out_dtype=torch.bfloat16)
@@ -700,6 +708,13 @@ def main():
                        flags=pt.PIPE_FLAG_EAGER_NEWEST | pt.PIPE_FLAG_GEMM_STORE_WAVE)
         log(f"[bench] gemm, bf16 C via a store wave: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16_store_wave"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, b_colmajor=True)
+        log(f"[bench] gemm, B column-major: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_b_colmajor"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, b_colmajor=True,
+                       out_dtype=torch.bfloat16)
+        log(f"[bench] gemm, B column-major, bf16 C: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_b_colmajor_c_bf16"] = g
         torch.cuda.empty_cache()
         sm = bench_small(max(20, args.steps), args.warmup)
         log(f"[bench] small configs: {sm}")

@@ -85,6 +85,10 @@ typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_
 #define PIPE_FLAG_GEMM_STORE_WAVE 0x1000u /* gemm with bf16 C: stage through a one-slot ring per
                                              MFMA wave pair that a dedicated store wave drains
                                              (full/empty handshake); requires GEMM_C_BF16 */
+#define PIPE_FLAG_GEMM_B_COLMAJOR 0x2000u /* gemm: B is column-major, element (k, n) at
+                                             B[n * ldb + k] with ldb >= K; its tiles are
+                                             loaded and read like A's (no transposing LDS
+                                             read); exclusive with GEMM_B_LINEAR */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the
@@ -180,14 +184,16 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
                           void* stream);
 
 /* GEMM mainloop: C = A * B with bf16 A (M x K, row-major) and B (K x N,
- * row-major), fp32 accumulation, C (M x N, row-major) in fp32 -- or, with
+ * row-major; column-major with PIPE_FLAG_GEMM_B_COLMAJOR), fp32 accumulation,
+ * C (M x N, row-major) in fp32 -- or, with
  * PIPE_FLAG_GEMM_C_BF16, in bf16 (each fp32 sum rounded to nearest even),
  * staged through LDS so that C is written in whole 16-byte row pieces
  * (optionally by a dedicated store wave, PIPE_FLAG_GEMM_STORE_WAVE). A and B tiles
  * of each 64-deep K step pass through the LDS ring to MFMA consumer waves.
- *   M % 128 == 0, N % 128 == 0, K % 64 == 0; lda, ldb multiples of 8;
- *   ldc >= N (elements of C's type; a multiple of 8 for bf16 C, whose base
- *   must be 16-byte aligned); K == 0 gives C = 0. */
+ *   M % 128 == 0, N % 128 == 0, K % 64 == 0; lda >= K and ldb >= N (ldb >= K
+ *   for column-major B), both multiples of 8; ldc >= N (elements of C's type;
+ *   a multiple of 8 for bf16 C, whose base must be 16-byte aligned); K == 0
+ *   gives C = 0. */
 pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t M,
                                  int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                                  const pipe_config_t* cfg, void* stream);

@@ -285,3 +285,28 @@ def test_binding_rejects_views_the_kernels_cannot_address():
                            ((4, 8, 2), (16, 2, 1))):
         with pytest.raises(ValueError):
             g(shape, strides)
+
+
+def test_gemm_b_colmajor_validation():
+    """Column-major B takes ldb >= K (not >= N), rejects GEMM_B_LINEAR, and is a
+    GEMM-only flag; all checked before any launch."""
+    g = pt.make_config(pt.PIPE_OP_GEMM, flags=pt.PIPE_FLAG_GEMM_B_COLMAJOR)
+    L = pt.lib()
+    # M=256, N=512, K=128: ldb 128 is fine for column-major B, too small for row-major
+    assert L.pipe_gemm_mainloop(FAKE, FAKE, FAKE, 256, 512, 128, 128, 100, 512,
+                                ctypes.byref(g), None) == pt.PIPE_ERR_SHAPE  # ldb < K
+    assert L.pipe_gemm_mainloop(FAKE + 4, FAKE, FAKE, 256, 512, 128, 128, 128, 512,
+                                ctypes.byref(g), None) == pt.PIPE_ERR_ALIGN  # checked after shape
+    g2 = pt.make_config(pt.PIPE_OP_GEMM)
+    assert L.pipe_gemm_mainloop(FAKE + 4, FAKE, FAKE, 256, 512, 128, 128, 128, 512,
+                                ctypes.byref(g2), None) == pt.PIPE_ERR_SHAPE  # row-major: ldb < N
+    bad = pt.make_config(pt.PIPE_OP_GEMM, flags=pt.PIPE_FLAG_GEMM_B_COLMAJOR |
+                         pt.PIPE_FLAG_GEMM_B_LINEAR)
+    assert L.pipe_gemm_mainloop(FAKE, FAKE, FAKE, 256, 512, 128, 128, 128, 512,
+                                ctypes.byref(bad), None) == pt.PIPE_ERR_CONFIG
+    info = pt.pipe_kernel_info_t()
+    assert L.pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(bad), 256, 512, 128,
+                               ctypes.byref(info)) == pt.PIPE_ERR_CONFIG
+    c = pt.make_config(pt.PIPE_OP_COPY, flags=pt.PIPE_FLAG_GEMM_B_COLMAJOR)
+    assert L.pipe_tile_copy(FAKE, FAKE, 256, 128, 128, 128, ctypes.byref(c), None,
+                            None) == pt.PIPE_ERR_CONFIG

@@ -187,3 +187,96 @@ def test_gemm_bf16_out_k_zero_gives_zero():
     pt.pipe_gemm_mainloop(A, B, C)
     torch.cuda.synchronize()
     assert int((C != 0).sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# Column-major B (PIPE_FLAG_GEMM_B_COLMAJOR, chosen by the binding for a K x N
+# view with unit row stride): the same product, B tiles loaded like A's.
+# ---------------------------------------------------------------------------
+def _colmajor(Bt, pad=0):
+    """K x N column-major view of the row-major N x K matrix Bt, optionally with
+    `pad` unused elements after each of its rows (ldb = K + pad)."""
+    N, K = Bt.shape
+    if pad:
+        full = torch.zeros((N, K + pad), dtype=Bt.dtype, device=Bt.device)
+        full[:, :K] = Bt
+        Bt = full[:, :K]
+    B = Bt.t()
+    assert B.stride(0) == 1 and B.shape == (K, N)
+    return B
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("PW", [2, 4])
+@pytest.mark.parametrize("policy", ["eager", "newest"])
+def test_gemm_b_colmajor_small_integers_bit_exact(S, PW, policy):
+    M, N, K = 256, 384, 512
+    A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=13, stream=0).to(DEV)
+    Bt = synth.small_int((N, K), -2, 2, torch.bfloat16, seed=13, stream=1).to(DEV)
+    B = _colmajor(Bt)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, stages=S, producer_waves=PW, grid=5, status=st,
+                              flags=pt.PIPE_FLAG_EAGER_NEWEST if policy == "newest" else 0)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = R.gemm_f64(_f32(A), _f32(Bt).T.copy())
+    got = C.cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("shift", [0, 1, 2])
+@pytest.mark.parametrize("pad", [0, 64])
+@pytest.mark.parametrize("c_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_b_colmajor_pitch_swizzle_and_output(shift, pad, c_dtype):
+    """Padded B rows (ldb > K), every swizzle shift, fp32 and bf16 C."""
+    M, N, K = 256, 256, 384
+    A = synth.small_int((M, K), 0, 3, torch.bfloat16, seed=14, stream=0).to(DEV)
+    Bt = synth.small_int((N, K), 0, 3, torch.bfloat16, seed=14, stream=1).to(DEV)
+    C = pt.pipe_gemm_mainloop(A, _colmajor(Bt, pad), swizzle_shift=shift, out_dtype=c_dtype)
+    torch.cuda.synchronize()
+    B_np = _f32(Bt).T.copy()
+    if c_dtype == torch.bfloat16:
+        assert np.array_equal(C.float().cpu().numpy(), R.gemm_bf16(_f32(A), B_np))
+    else:
+        assert np.array_equal(C.cpu().numpy(), R.gemm_f64(_f32(A), B_np))
+
+
+def test_gemm_b_colmajor_matches_row_major_bitwise():
+    """The two layouts of one B give the same bits (same accumulation order)."""
+    M, N, K = 512, 256, 1024
+    A = synth.uniform((M, K), torch.bfloat16, seed=15, stream=0).to(DEV)
+    B = synth.uniform((K, N), torch.bfloat16, seed=15, stream=1).to(DEV)
+    C_row = pt.pipe_gemm_mainloop(A, B)
+    C_col = pt.pipe_gemm_mainloop(A, _colmajor(B.t().contiguous()))
+    torch.cuda.synchronize()
+    assert torch.equal(C_row, C_col)
+    res = R.within_tol(C_col.cpu().numpy(), R.gemm_f64(_f32(A), _f32(B)), 1e-2)
+    assert res["ok"], res
+
+
+def test_gemm_b_colmajor_full_size_sampled_rows():
+    """bf16 4096^3 uniform[-1,1), B column-major: 64 sampled rows against fp64."""
+    n = 4096
+    A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device=DEV)
+    Bt = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, Bt.t(), status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rows = np.random.default_rng(7).choice(n, 64, replace=False)
+    Bt_np = _f32(Bt)
+    ref = R.gemm_f64(_f32(A[torch.as_tensor(rows, device=DEV)]), Bt_np.T.copy())
+    res = R.within_tol(C[torch.as_tensor(rows, device=DEV)].cpu().numpy(), ref, 1e-2)
+    assert res["ok"], res
+
+
+def test_gemm_b_colmajor_rejections():
+    A = torch.zeros((128, 128), dtype=torch.bfloat16, device=DEV)
+    Bt = torch.zeros((128, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(pt.PipeError):  # exclusive with the row-major B swizzle switch
+        pt.pipe_gemm_mainloop(A, Bt.t(), flags=pt.PIPE_FLAG_GEMM_B_LINEAR)
+    over = torch.zeros(128 * 64 + 64, dtype=torch.bfloat16, device=DEV)
+    B_overlap = over.as_strided((128, 128), (1, 64))  # columns 64 apart: rows of B^T overlap
+    with pytest.raises(ValueError):
+        pt.pipe_gemm_mainloop(A, B_overlap)
