@@ -8,6 +8,7 @@ The functions carry the C ABI's names (``include/pipe_tile.h``):
     pipe_rowsum(A, out=None, workspace=None, **cfg)        -> out
     pipe_gemm_mainloop(A, B, C=None, **cfg)                -> C
     pipe_query_kernel(op, M, N, K=0, **cfg)                -> dict
+    pipe_kernel_resources(op, M, N, K=0, **cfg)            -> dict
     pipe_rowsum_workspace_bytes(M, N, **cfg)               -> int
     pipe_device_status(clear=False)                        -> int
 
@@ -101,6 +102,15 @@ class pipe_kernel_info_t(ctypes.Structure):
     ]
 
 
+class pipe_kernel_resources_t(ctypes.Structure):
+    _fields_ = [
+        ("vgprs", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32),
+        ("scratch_bytes", ctypes.c_int32),
+        ("max_threads", ctypes.c_int32),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -123,6 +133,9 @@ _SIGS = {
                                       _c.c_int64, _c.POINTER(pipe_config_t), _c.c_void_p]),
     "pipe_query_kernel": (_c.c_int, [_c.c_int, _c.POINTER(pipe_config_t), _c.c_int64,
                                      _c.c_int64, _c.c_int64, _c.POINTER(pipe_kernel_info_t)]),
+    "pipe_kernel_resources": (_c.c_int, [_c.c_int, _c.POINTER(pipe_config_t), _c.c_int64,
+                                         _c.c_int64, _c.c_int64,
+                                         _c.POINTER(pipe_kernel_resources_t)]),
     "pipe_device_status": (_c.c_int, [_c.POINTER(_c.c_uint32), _c.c_int]),
 }
 
@@ -324,6 +337,16 @@ def pipe_query_kernel(op: int, M: int, N: int, K: int = 0, **cfg) -> dict:
     return {f: getattr(info, f) for f, _ in pipe_kernel_info_t._fields_}
 
 
+def pipe_kernel_resources(op: int, M: int, N: int, K: int = 0, **cfg) -> dict:
+    """Registers, static LDS, spill bytes and maximum workgroup size of the
+    kernel the op would launch for this shape (needs a device)."""
+    c = make_config(op, **cfg)
+    out = pipe_kernel_resources_t()
+    _check(lib().pipe_kernel_resources(op, ctypes.byref(c), M, N, K, ctypes.byref(out)),
+           "pipe_kernel_resources")
+    return {f: getattr(out, f) for f, _ in pipe_kernel_resources_t._fields_}
+
+
 def pipe_device_status(clear: bool = False) -> int:
     out = ctypes.c_uint32(0)
     _check(lib().pipe_device_status(ctypes.byref(out), 1 if clear else 0), "pipe_device_status")
@@ -387,4 +410,5 @@ tile_copy = pipe_tile_copy
 rowsum = pipe_rowsum
 gemm_mainloop = pipe_gemm_mainloop
 query_kernel = pipe_query_kernel
+kernel_resources = pipe_kernel_resources
 device_status = pipe_device_status

@@ -225,6 +225,83 @@ pipe_status_t resolve_status(const pipe_config_t& c, uint32_t** out) {
 
 pipe_status_t hip_status(hipError_t e) { return e == hipSuccess ? PIPE_OK : PIPE_ERR_HIP; }
 
+
+// GEMM checks that need no pointers: the configuration ...
+pipe_status_t gemm_check_config(const pipe_config_t& c) {
+  pipe_status_t s = check_common(c);
+  if (s != PIPE_OK) return s;
+  if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
+  if (c.tile_m != 128 || c.tile_n != 128 || c.tile_k != 64) return PIPE_ERR_CONFIG;
+  if ((c.producer_waves != 2 && c.producer_waves != 4) || c.consumer_waves != 4)
+    return PIPE_ERR_CONFIG;
+  if (c.split > 1) return PIPE_ERR_CONFIG;
+  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE)) return PIPE_ERR_CONFIG;
+  const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
+  const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
+  if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
+  if ((c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) && (c.flags & PIPE_FLAG_GEMM_B_LINEAR))
+    return PIPE_ERR_CONFIG;
+  if (gemm_lds_bytes(c.stages, c_bf16, store_wave) > kLdsLimit) return PIPE_ERR_STAGES;
+  return PIPE_OK;
+}
+
+// ... the shape and pitches ...
+pipe_status_t gemm_check_shape(const pipe_config_t& c, int64_t M, int64_t N, int64_t K,
+                               int64_t lda, int64_t ldb, int64_t ldc) {
+  const bool b_col = (c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) != 0;
+  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < (b_col ? K : N) || ldc < N)
+    return PIPE_ERR_SHAPE;
+  if (M % 128 != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
+  if (!extent_fits(M, lda, 2) || !extent_fits(b_col ? N : K, ldb, 2) ||
+      !extent_fits(M, ldc, (c.flags & PIPE_FLAG_GEMM_C_BF16) ? 2 : 4))
+    return PIPE_ERR_SHAPE;
+  return PIPE_OK;
+}
+
+// ... and the launch parameters (all but the pointers) with the grid, for
+// M, N, K > 0.
+pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int64_t K,
+                               int64_t lda, int64_t ldb, int64_t ldc, GemmParams* p, int* grid) {
+  p->lda = lda * 2;
+  p->ldb = ldb * 2;
+  p->ldc = ldc;
+  p->M = (int32_t)M;
+  p->N = (int32_t)N;
+  p->K = (int32_t)K;
+  p->tiles_m = (int32_t)(M / 128);
+  p->tiles_n = (int32_t)(N / 128);
+  p->k_steps = (int32_t)(K / 64);
+  const int64_t items = (int64_t)p->tiles_m * p->tiles_n;
+  if (items > INT32_MAX) return PIPE_ERR_SHAPE;
+  p->items = (int32_t)items;
+  p->swz_shift = c.swizzle_shift;
+  p->b_swz = (c.flags & PIPE_FLAG_GEMM_B_LINEAR) ? 0 : 1;
+  p->b_colmajor = (c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) ? 1 : 0;
+  p->eager = eager_min_pending(c.flags);
+  p->c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) ? 1 : 0;
+  p->store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) ? 1 : 0;
+  p->spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
+  p->trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
+  p->trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
+  if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
+  *grid = (c.grid == 0 || c.grid > p->items) ? p->items : c.grid;
+  // Barrier words count arrivals in 32 bits (4 per stage on empty).
+  if (((int64_t)p->items + *grid - 1) / *grid * p->k_steps * 4 >= (int64_t(1) << 31))
+    return PIPE_ERR_SHAPE;
+  return PIPE_OK;
+}
+
+// Address of the kernel that `launch` would launch, without launching it.
+template <class F>
+pipe_status_t record_kernel(F launch, const void** fn) {
+  *fn = nullptr;
+  set_record_slot(fn);
+  const hipError_t e = launch();
+  set_record_slot(nullptr);
+  return (e == hipSuccess && *fn != nullptr) ? PIPE_OK : PIPE_ERR_CONFIG;
+}
+
 }  // namespace
 
 extern "C" {
@@ -365,27 +442,11 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
                                  int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                                  const pipe_config_t* cfg, void* stream) {
   const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_GEMM);
-  pipe_status_t s = check_common(c);
+  pipe_status_t s = gemm_check_config(c);
   if (s != PIPE_OK) return s;
-  if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
-  if (c.tile_m != 128 || c.tile_n != 128 || c.tile_k != 64) return PIPE_ERR_CONFIG;
-  if ((c.producer_waves != 2 && c.producer_waves != 4) || c.consumer_waves != 4)
-    return PIPE_ERR_CONFIG;
-  if (c.split > 1) return PIPE_ERR_CONFIG;
-  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE)) return PIPE_ERR_CONFIG;
+  s = gemm_check_shape(c, M, N, K, lda, ldb, ldc);
+  if (s != PIPE_OK) return s;
   const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
-  const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
-  const bool b_col = (c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) != 0;
-  if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
-  if (b_col && (c.flags & PIPE_FLAG_GEMM_B_LINEAR)) return PIPE_ERR_CONFIG;
-  if (gemm_lds_bytes(c.stages, c_bf16, store_wave) > kLdsLimit) return PIPE_ERR_STAGES;
-  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < (b_col ? K : N) || ldc < N)
-    return PIPE_ERR_SHAPE;
-  if (M % 128 != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
-  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
-  if (!extent_fits(M, lda, 2) || !extent_fits(b_col ? N : K, ldb, 2) ||
-      !extent_fits(M, ldc, (c.flags & PIPE_FLAG_GEMM_C_BF16) ? 2 : 4))
-    return PIPE_ERR_SHAPE;
   if (M == 0 || N == 0) return PIPE_OK;
   if (C == nullptr) return PIPE_ERR_NULL;
   if (c_bf16 ? (!aligned16(C) || (ldc % 8)) : !aligned4(C)) return PIPE_ERR_ALIGN;
@@ -397,35 +458,12 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
   if (A == nullptr || B == nullptr) return PIPE_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return PIPE_ERR_ALIGN;
   GemmParams p{};
+  int grid = 0;
+  s = gemm_fill_params(c, M, N, K, lda, ldb, ldc, &p, &grid);
+  if (s != PIPE_OK) return s;
   p.A = static_cast<const uint8_t*>(A);
   p.B = static_cast<const uint8_t*>(B);
   p.C = C;
-  p.lda = lda * 2;
-  p.ldb = ldb * 2;
-  p.ldc = ldc;
-  p.M = (int32_t)M;
-  p.N = (int32_t)N;
-  p.K = (int32_t)K;
-  p.tiles_m = (int32_t)(M / 128);
-  p.tiles_n = (int32_t)(N / 128);
-  p.k_steps = (int32_t)(K / 64);
-  const int64_t items = (int64_t)p.tiles_m * p.tiles_n;
-  if (items > INT32_MAX) return PIPE_ERR_SHAPE;
-  p.items = (int32_t)items;
-  p.swz_shift = c.swizzle_shift;
-  p.b_swz = (c.flags & PIPE_FLAG_GEMM_B_LINEAR) ? 0 : 1;
-  p.b_colmajor = b_col ? 1 : 0;
-  p.eager = eager_min_pending(c.flags);
-  p.c_bf16 = c_bf16 ? 1 : 0;
-  p.store_wave = store_wave ? 1 : 0;
-  p.spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
-  p.trace = (c.flags & PIPE_FLAG_TRACE) ? c.trace : nullptr;
-  p.trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
-  if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
-  const int grid = (c.grid == 0 || c.grid > p.items) ? p.items : c.grid;
-  // Barrier words count arrivals in 32 bits (4 per stage on empty).
-  if (((int64_t)p.items + grid - 1) / grid * p.k_steps * 4 >= (int64_t(1) << 31))
-    return PIPE_ERR_SHAPE;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
   return hip_status(launch_gemm(c.stages, c.producer_waves, grid, p, st));
@@ -474,6 +512,70 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   info->items = g.items;
   info->tiles_per_item = g.seg_len;
   info->split = g.split;
+  return PIPE_OK;
+}
+
+pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
+                                    int64_t K, pipe_kernel_resources_t* out) {
+  if (out == nullptr) return PIPE_ERR_NULL;
+  *out = pipe_kernel_resources_t{};
+  const pipe_config_t c = cfg ? *cfg : defaults(op);
+  const void* fn = nullptr;
+  pipe_status_t s;
+  if (op == PIPE_OP_GEMM) {
+    s = gemm_check_config(c);
+    if (s != PIPE_OK) return s;
+    const bool b_col = (c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) != 0;
+    s = gemm_check_shape(c, M, N, K, K, b_col ? K : N, N);
+    if (s != PIPE_OK) return s;
+    if (M == 0 || N == 0 || K == 0) return PIPE_ERR_SHAPE;
+    GemmParams p{};
+    int grid = 0;
+    s = gemm_fill_params(c, M, N, K, K, b_col ? K : N, N, &p, &grid);
+    if (s != PIPE_OK) return s;
+    s = record_kernel([&] { return launch_gemm(c.stages, c.producer_waves, grid, p, nullptr); },
+                      &fn);
+  } else if (op == PIPE_OP_COPY || op == PIPE_OP_ROWSUM) {
+    s = check_stream_cfg(c);
+    if (s != PIPE_OK) return s;
+    const bool rowsum = op == PIPE_OP_ROWSUM;
+    if (rowsum && (c.flags & PIPE_FLAG_ROW_STRIPS)) return PIPE_ERR_CONFIG;
+    if (M < 0 || N < 0 || N % 8 != 0 || !extent_fits(M, N, 2)) return PIPE_ERR_SHAPE;
+    if (M == 0 || N == 0) return PIPE_ERR_SHAPE;
+    const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);
+    const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
+    if (unified) {
+      s = check_unified(c, M, N, false);
+      if (s != PIPE_OK) return s;
+    }
+    StreamGeom g;
+    s = stream_geometry(M, N, c, row_strips, rowsum, &g);
+    if (s != PIPE_OK) return s;
+    StreamParams p{};
+    fill_stream_params(c, g, row_strips, &p);
+    p.ld_src = N * 2;
+    p.ld_dst = rowsum ? 0 : N * 2;
+    p.M = M;
+    p.N = N;
+    const int kop = rowsum ? kOpRowsum : kOpCopy;
+    s = record_kernel(
+        [&] {
+          return unified ? launch_unified(kop, c.stages, c.consumer_waves, c.tile_n, g.grid, p,
+                                          nullptr)
+                         : launch_stream(kop, c.stages, c.consumer_waves, c.producer_waves,
+                                         c.tile_n, g.grid, p, nullptr);
+        },
+        &fn);
+  } else {
+    return PIPE_ERR_CONFIG;
+  }
+  if (s != PIPE_OK) return s;
+  hipFuncAttributes attr{};
+  if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return PIPE_ERR_HIP;
+  out->vgprs = attr.numRegs;
+  out->lds_bytes = (int32_t)attr.sharedSizeBytes;
+  out->scratch_bytes = (int32_t)attr.localSizeBytes;
+  out->max_threads = attr.maxThreadsPerBlock;
   return PIPE_OK;
 }
 

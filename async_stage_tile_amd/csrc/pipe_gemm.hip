@@ -528,24 +528,16 @@ __global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0))
 template <int PW, int EPI>
 hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t stream) {
   const dim3 g(grid), b(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)));
-  if (p.b_colmajor) {
-    switch (stages) {
-      case 1: hipLaunchKernelGGL((gemm_kernel_bcol<1, PW, EPI>), g, b, 0, stream, p); break;
-      case 2: hipLaunchKernelGGL((gemm_kernel_bcol<2, PW, EPI>), g, b, 0, stream, p); break;
-      case 3: hipLaunchKernelGGL((gemm_kernel_bcol<3, PW, EPI>), g, b, 0, stream, p); break;
-      case 4: hipLaunchKernelGGL((gemm_kernel_bcol<4, PW, EPI>), g, b, 0, stream, p); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
+  using Kernel = void (*)(GemmParams);
+  Kernel row, col;  // the kernels for row-major and column-major B
   switch (stages) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<1, PW, EPI>), g, b, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<2, PW, EPI>), g, b, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((gemm_kernel<3, PW, EPI>), g, b, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<4, PW, EPI>), g, b, 0, stream, p); break;
+    case 1: row = gemm_kernel<1, PW, EPI>; col = gemm_kernel_bcol<1, PW, EPI>; break;
+    case 2: row = gemm_kernel<2, PW, EPI>; col = gemm_kernel_bcol<2, PW, EPI>; break;
+    case 3: row = gemm_kernel<3, PW, EPI>; col = gemm_kernel_bcol<3, PW, EPI>; break;
+    case 4: row = gemm_kernel<4, PW, EPI>; col = gemm_kernel_bcol<4, PW, EPI>; break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return launch_or_record(p.b_colmajor ? col : row, g, b, stream, p);
 }
 
 template <int EPI>

@@ -109,6 +109,23 @@ struct GemmParams {
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream);
+
+// Kernel lookup without a launch. While the calling thread's record slot is
+// set, launch_or_record stores the address of the kernel it was given there
+// and launches nothing; otherwise it launches it.
+const void** record_slot();
+void set_record_slot(const void** slot);
+
+template <class P>
+inline hipError_t launch_or_record(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream,
+                                   const P& p) {
+  if (const void** slot = record_slot()) {
+    *slot = reinterpret_cast<const void*>(kernel);
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
 int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave);
 int gemm_threads(int producers, bool c_bf16, bool store_wave);
 

@@ -393,22 +393,15 @@ static hipError_t launch_scpt(int op, int grid, const StreamParams& p, hipStream
     constexpr int R = TileShape<TC>::kRows;
     dim3 block(64 * (PW + C));
     const bool masked = (p.M % R) != 0 || (p.N % TC) != 0;
-    if (op == kOpCopy) {
-      if (masked)
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, true, TC>), dim3(grid), block, 0,
-                           stream, p);
-      else
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpCopy, false, TC>), dim3(grid), block, 0,
-                           stream, p);
-    } else {
-      if (masked)
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, true, TC>), dim3(grid), block, 0,
-                           stream, p);
-      else
-        hipLaunchKernelGGL((stream_kernel<S, C, PW, kOpRowsum, false, TC>), dim3(grid), block,
-                           0, stream, p);
-    }
-    return hipGetLastError();
+    if (op == kOpCopy)
+      return masked ? launch_or_record(stream_kernel<S, C, PW, kOpCopy, true, TC>, dim3(grid),
+                                       block, stream, p)
+                    : launch_or_record(stream_kernel<S, C, PW, kOpCopy, false, TC>, dim3(grid),
+                                       block, stream, p);
+    return masked ? launch_or_record(stream_kernel<S, C, PW, kOpRowsum, true, TC>, dim3(grid),
+                                     block, stream, p)
+                  : launch_or_record(stream_kernel<S, C, PW, kOpRowsum, false, TC>, dim3(grid),
+                                     block, stream, p);
   }
 }
 

@@ -1,10 +1,17 @@
-// Stream-kernel dispatch over the stage count, the row-sum finalize and a
-// small fill kernel. The stream kernels themselves are instantiated per stage
+// Stream-kernel dispatch over the stage count, the row-sum finalize, a small
+// fill kernel, and the per-thread slot of kernel lookups without a launch. The stream kernels themselves are instantiated per stage
 // count in the objects built from pipe_stream.hip.
 #include "pipe_device.hpp"
 #include "pipe_kernels.hpp"
 
 namespace pipe {
+
+namespace {
+thread_local const void** t_record_slot = nullptr;
+}  // namespace
+
+const void** record_slot() { return t_record_slot; }
+void set_record_slot(const void** slot) { t_record_slot = slot; }
 
 hipError_t launch_stream(int op, int stages, int consumers, int producers, int tile_n, int grid,
                          const StreamParams& p, hipStream_t stream) {

@@ -65,21 +65,16 @@ struct Walk {
   }
 };
 
+// Per-slot vmcnt marks, held as one 8-lane integer vector value (S <= 8) so
+// that the runtime slot index selects a register: as a plain array the
+// compiler placed the marks in LDS or in scratch memory.
 template <int S>
 struct Marks {
-  int m[S];
-  __device__ __forceinline__ int get(int s) const {
-    int v = m[0];
-#pragma unroll
-    for (int i = 1; i < S; ++i)
-      if (s == i) v = m[i];
-    return v;
-  }
-  __device__ __forceinline__ void set(int s, int v) {
-#pragma unroll
-    for (int i = 0; i < S; ++i)
-      if (s == i) m[i] = v;
-  }
+  static_assert(S >= 1 && S <= 8, "at most 8 slots");
+  typedef int ivec8 __attribute__((ext_vector_type(8)));
+  ivec8 m;
+  __device__ __forceinline__ int get(int s) const { return m[s]; }
+  __device__ __forceinline__ void set(int s, int v) { m[s] = v; }
 };
 
 template <int S, int W, int OP, int TC>
@@ -195,12 +190,10 @@ hipError_t launch_swt(int op, int grid, const StreamParams& p, hipStream_t strea
     return hipErrorInvalidValue;
   } else {
     if (op == kOpCopy)
-      hipLaunchKernelGGL((unified_kernel<S, W, kOpCopy, TC>), dim3(grid), dim3(64 * W), 0,
-                         stream, p);
-    else
-      hipLaunchKernelGGL((unified_kernel<S, W, kOpRowsum, TC>), dim3(grid), dim3(64 * W), 0,
-                         stream, p);
-    return hipGetLastError();
+      return launch_or_record(unified_kernel<S, W, kOpCopy, TC>, dim3(grid), dim3(64 * W), stream,
+                              p);
+    return launch_or_record(unified_kernel<S, W, kOpRowsum, TC>, dim3(grid), dim3(64 * W), stream,
+                            p);
   }
 }
 

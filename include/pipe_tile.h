@@ -56,7 +56,16 @@ typedef enum {
   PIPE_ERR_TIMEOUT = 8    /* (device status) a pipeline wait exceeded spin_limit */
 } pipe_status_t;
 
-typedef enum { PIPE_OP_COPY = 0, PIPE_OP_ROWSUM = 1, PIPE_OP_GEMM = 2 } pipe_op_t;
+/* The two sentinels give the type the range of int32, so that any int a
+ * caller passes is a value of it (and is rejected with PIPE_ERR_CONFIG when it
+ * names no op). */
+typedef enum {
+  PIPE_OP_COPY = 0,
+  PIPE_OP_ROWSUM = 1,
+  PIPE_OP_GEMM = 2,
+  PIPE_OP_RANGE_MIN_ = -0x7fffffff - 1,
+  PIPE_OP_RANGE_MAX_ = 0x7fffffff
+} pipe_op_t;
 
 /* cfg->flags */
 #define PIPE_FLAG_TRACE 0x1u           /* record per-tile cursor values into cfg->trace */
@@ -136,6 +145,14 @@ typedef struct {
   int32_t split;          /* segments per strip actually used                             */
 } pipe_kernel_info_t;
 
+typedef struct {
+  int32_t vgprs;          /* vector registers per lane, as the HIP runtime reports them
+                             (numRegs; no kernel of this library uses AGPRs)              */
+  int32_t lds_bytes;      /* static LDS per workgroup                                     */
+  int32_t scratch_bytes;  /* private memory per lane (register spills); 0 when none       */
+  int32_t max_threads;    /* largest workgroup the kernel can be launched with            */
+} pipe_kernel_resources_t;
+
 /* ABI version of the loaded library (PIPE_ABI_VERSION). */
 int pipe_abi_version(void);
 
@@ -201,6 +218,17 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
 /* Launch geometry an op would use for this shape and config (no launch). */
 pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
                                 int64_t K, pipe_kernel_info_t* info);
+
+/* Compiled resources of the main kernel that an op would launch for this
+ * shape and config (the stream, unified or GEMM kernel; not the row-sum
+ * finalize or a zero fill), from the HIP runtime's function attributes. It
+ * takes the same checks as the op's entry point minus those on pointers, with
+ * the tightest pitches (ld = N, or K for A and column-major B), and launches
+ * nothing. Unlike pipe_query_kernel it needs the HIP runtime and a device.
+ *   PIPE_ERR_SHAPE also for shapes that launch no main kernel (M or N zero,
+ *   or K zero for the GEMM); PIPE_ERR_HIP when the runtime cannot report. */
+pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
+                                    int64_t K, pipe_kernel_resources_t* out);
 
 /* Blocking read of the library's own device status word on the current
  * device (used when cfg->status is NULL); clears it when `clear` != 0. */

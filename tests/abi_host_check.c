@@ -46,6 +46,11 @@ int main(void) {
   for (int s = -3; s < 12; ++s) EXPECT(pipe_status_str(s) != NULL && strlen(pipe_status_str(s)) > 0);
   EXPECT(pipe_config_default(PIPE_OP_COPY, NULL) == PIPE_ERR_NULL);
   EXPECT(pipe_config_default((pipe_op_t)7, NULL) != PIPE_OK);
+  {
+    pipe_config_t junk;
+    EXPECT(pipe_config_default((pipe_op_t)7, &junk) == PIPE_ERR_CONFIG);
+    EXPECT(pipe_config_default((pipe_op_t)-1, &junk) == PIPE_ERR_CONFIG);
+  }
 
   /* copy: validation failures */
   pipe_config_t c = dflt(PIPE_OP_COPY);
@@ -120,8 +125,20 @@ int main(void) {
   EXPECT(pipe_gemm_mainloop(FAKE, FAKE, FAKE, 256, 256, 128, 128, 256, (int64_t)1 << 60, &g,
                             NULL) == PIPE_ERR_SHAPE);
 
-  /* pipe_query_kernel: pure host arithmetic over many configurations and shapes */
+  /* pipe_kernel_resources: every check below fails before the HIP runtime is asked */
+  pipe_kernel_resources_t res;
   pipe_kernel_info_t info;
+  EXPECT(pipe_kernel_resources(PIPE_OP_COPY, &c, 256, 128, 0, NULL) == PIPE_ERR_NULL);
+  EXPECT(pipe_kernel_resources(PIPE_OP_COPY, &c, 0, 128, 0, &res) == PIPE_ERR_SHAPE);
+  EXPECT(pipe_kernel_resources(PIPE_OP_COPY, &c, INT64_MAX, INT64_MAX & ~(int64_t)7, 0, &res) ==
+         PIPE_ERR_SHAPE);
+  EXPECT(pipe_kernel_resources(PIPE_OP_GEMM, &g, 256, 256, 0, &res) == PIPE_ERR_SHAPE);
+  EXPECT(pipe_kernel_resources(PIPE_OP_GEMM, &g, (int64_t)1 << 40, 256, 128, &res) ==
+         PIPE_ERR_SHAPE);
+  EXPECT(pipe_kernel_resources((pipe_op_t)5, &c, 256, 128, 0, &res) == PIPE_ERR_CONFIG);
+  EXPECT(pipe_query_kernel((pipe_op_t)9, &c, 256, 128, 0, &info) == PIPE_ERR_CONFIG);
+
+  /* pipe_query_kernel: pure host arithmetic over many configurations and shapes */
   EXPECT(pipe_query_kernel(PIPE_OP_COPY, &c, 16, 16, 0, NULL) == PIPE_ERR_NULL);
   EXPECT(pipe_query_kernel(PIPE_OP_GEMM, &g, (int64_t)1 << 40, (int64_t)1 << 40, 64, &info) ==
          PIPE_ERR_SHAPE);

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = pt.lib()
     declared = _declared()
-    assert len(declared) == 9
+    assert len(declared) == 10
     for name in declared:
         assert hasattr(L, name), name
     assert sorted(pt.exported_symbols()) == declared
@@ -310,3 +310,31 @@ def test_gemm_b_colmajor_validation():
     c = pt.make_config(pt.PIPE_OP_COPY, flags=pt.PIPE_FLAG_GEMM_B_COLMAJOR)
     assert L.pipe_tile_copy(FAKE, FAKE, 256, 128, 128, 128, ctypes.byref(c), None,
                             None) == pt.PIPE_ERR_CONFIG
+
+
+def test_kernel_resources_validation_runs_before_the_runtime():
+    """pipe_kernel_resources checks like the op's entry point, before it asks
+    the HIP runtime anything, so these fail the same way without a device."""
+    L = pt.lib()
+    out = pt.pipe_kernel_resources_t()
+    c = pt.make_config(pt.PIPE_OP_COPY)
+    assert L.pipe_kernel_resources(pt.PIPE_OP_COPY, ctypes.byref(c), 256, 128, 0, None) == \
+        pt.PIPE_ERR_NULL
+    assert L.pipe_kernel_resources(7, ctypes.byref(c), 256, 128, 0, ctypes.byref(out)) == \
+        pt.PIPE_ERR_CONFIG
+    for M, N in ((0, 128), (256, 0), (256, 12), (-1, 128)):
+        assert L.pipe_kernel_resources(pt.PIPE_OP_COPY, ctypes.byref(c), M, N, 0,
+                                       ctypes.byref(out)) == pt.PIPE_ERR_SHAPE
+    bad = pt.make_config(pt.PIPE_OP_COPY, stages=9)
+    assert L.pipe_kernel_resources(pt.PIPE_OP_COPY, ctypes.byref(bad), 256, 128, 0,
+                                   ctypes.byref(out)) == pt.PIPE_ERR_STAGES
+    r = pt.make_config(pt.PIPE_OP_ROWSUM, flags=pt.PIPE_FLAG_ROW_STRIPS)
+    assert L.pipe_kernel_resources(pt.PIPE_OP_ROWSUM, ctypes.byref(r), 256, 128, 0,
+                                   ctypes.byref(out)) == pt.PIPE_ERR_CONFIG
+    g = pt.make_config(pt.PIPE_OP_GEMM)
+    for M, N, K in ((256, 256, 0), (256, 100, 128), (0, 256, 128)):
+        assert L.pipe_kernel_resources(pt.PIPE_OP_GEMM, ctypes.byref(g), M, N, K,
+                                       ctypes.byref(out)) == pt.PIPE_ERR_SHAPE
+    gb = pt.make_config(pt.PIPE_OP_GEMM, flags=pt.PIPE_FLAG_GEMM_STORE_WAVE)  # needs bf16 C
+    assert L.pipe_kernel_resources(pt.PIPE_OP_GEMM, ctypes.byref(gb), 256, 256, 128,
+                                   ctypes.byref(out)) == pt.PIPE_ERR_CONFIG

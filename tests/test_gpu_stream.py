@@ -502,3 +502,31 @@ def test_unified_copy_full_size_bit_exact():
     dst = pt.pipe_tile_copy(src, stages=3, consumer_waves=4, flags=pt.PIPE_FLAG_UNIFIED)
     torch.cuda.synchronize()
     assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
+
+
+@pytest.mark.parametrize("op,M,N,K,cfg", [
+    (pt.PIPE_OP_COPY, 16384, 16384, 0, {}),
+    (pt.PIPE_OP_COPY, 1000, 1000, 0, {}),                      # ragged: the masked kernel
+    (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(tile_m=32, tile_n=256, consumer_waves=8)),
+    (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(stages=3, consumer_waves=4,
+                                            flags=pt.PIPE_FLAG_UNIFIED)),
+    (pt.PIPE_OP_ROWSUM, 8192, 65536, 0, {}),
+    (pt.PIPE_OP_ROWSUM, 8192, 65536, 0, dict(stages=8, consumer_waves=8)),
+    (pt.PIPE_OP_GEMM, 4096, 4096, 4096, {}),
+    (pt.PIPE_OP_GEMM, 4096, 4096, 4096, dict(flags=pt.PIPE_FLAG_GEMM_C_BF16 |
+                                             pt.PIPE_FLAG_EAGER_NEWEST)),
+    (pt.PIPE_OP_GEMM, 4096, 4096, 4096, dict(flags=pt.PIPE_FLAG_GEMM_B_COLMAJOR |
+                                             pt.PIPE_FLAG_EAGER_NEWEST)),
+    (pt.PIPE_OP_GEMM, 1024, 1024, 1024, dict(stages=4, producer_waves=2)),
+])
+def test_kernel_resources_agree_with_the_launch_geometry(op, M, N, K, cfg):
+    """The runtime's static LDS for the kernel an op launches equals the LDS
+    that pipe_query_kernel computes for it; the kernel fits the workgroup, and
+    the default configurations spill nothing."""
+    res = pt.pipe_kernel_resources(op, M, N, K, **cfg)
+    q = pt.pipe_query_kernel(op, M, N, K, **cfg)
+    assert res["lds_bytes"] == q["lds_bytes"], (res, q)
+    assert 0 < res["vgprs"] <= 512
+    assert res["max_threads"] >= q["threads"]
+    if not cfg:
+        assert res["scratch_bytes"] == 0
