@@ -71,13 +71,15 @@ def test_gemm_uniform_within_tolerance():
     assert res["ok"], res
 
 
-def test_gemm_full_size_sampled_rows():
-    """bf16 4096^3 uniform[-1,1): 64 sampled rows checked against fp64."""
+@pytest.mark.parametrize("cfg", [{}, dict(stages=3)], ids=["default", "S3"])
+def test_gemm_full_size_sampled_rows(cfg):
+    """bf16 4096^3 uniform[-1,1): 64 sampled rows checked against fp64, in the
+    default configuration (the one bench.py times) and on a 3-stage ring."""
     n = 4096
     A = synth.uniform((n, n), torch.bfloat16, seed=42, stream=0, device=DEV)
     B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device=DEV)
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    C = pt.pipe_gemm_mainloop(A, B, stages=3, status=st)
+    C = pt.pipe_gemm_mainloop(A, B, status=st, **cfg)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     rows = np.random.default_rng(42).choice(n, 64, replace=False)

@@ -251,14 +251,28 @@ def test_rowsum_normal_within_tolerance_and_deterministic():
     assert torch.equal(out1, out2)
 
 
-def test_rowsum_full_size_within_tolerance():
-    """fp16 8192 x 65536 normal(0,1), 3-stage ring (the full 1 GiB input)."""
+@pytest.fixture(scope="module")
+def rowsum_full():
+    """The full 1 GiB row-sum input, fp16 8192 x 65536 normal(0,1), and its exact
+    row sums (computed once for the tests below)."""
     A = synth.normal((8192, 65536), torch.float16, seed=42, device=DEV)
+    return A, R.rowsum_exact(A.cpu().numpy())
+
+
+@pytest.mark.parametrize("cfg", [
+    {},                                                        # the default 3-stage ring
+    dict(tile_m=64, tile_n=128, stages=3, producer_waves=4, consumer_waves=4, split=2,
+         flags=pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP),
+    dict(tile_m=32, tile_n=256, stages=3, producer_waves=4, consumer_waves=4, split=1,
+         flags=pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP),
+], ids=["default", "64x128", "32x256"])
+def test_rowsum_full_size_within_tolerance(rowsum_full, cfg):
+    """The full input in the configurations bench.py times."""
+    A, ref = rowsum_full
     st = _status()
-    out = pt.pipe_rowsum(A, stages=3, status=st)
+    out = pt.pipe_rowsum(A, status=st, **cfg)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    ref = R.rowsum_exact(A.cpu().numpy())
     res = R.within_tol(out.cpu().numpy(), ref, 1e-3)
     assert res["ok"], res
 
