@@ -544,3 +544,30 @@ def test_kernel_resources_agree_with_the_launch_geometry(op, M, N, K, cfg):
     assert res["max_threads"] >= q["threads"]
     if not cfg:
         assert res["scratch_bytes"] == 0
+
+
+def test_kernel_lookup_on_one_thread_never_swallows_a_launch_on_another():
+    """pipe_kernel_resources finds its kernel by running the launch path with a
+    record slot set; the slot is per thread, so copies launched meanwhile from
+    another thread must all run (ctypes releases the GIL during each call)."""
+    import threading
+    src = synth.uniform((1024, 4096), torch.float16, seed=21, device=DEV)
+    stop = threading.Event()
+    seen = []
+
+    def lookups():
+        while not stop.is_set():
+            seen.append(pt.pipe_kernel_resources(pt.PIPE_OP_COPY, 1024, 4096)["vgprs"])
+
+    t = threading.Thread(target=lookups)
+    t.start()
+    try:
+        for i in range(200):
+            dst = torch.zeros_like(src)
+            pt.pipe_tile_copy(src, dst)
+            torch.cuda.synchronize()
+            assert torch.equal(dst.view(torch.int16), src.view(torch.int16)), f"copy {i} did not run"
+    finally:
+        stop.set()
+        t.join()
+    assert len(seen) > 0 and all(v > 0 for v in seen)
