@@ -159,7 +159,10 @@ int pipe_abi_version(void);
 /* Static, human-readable name of a status code. */
 const char* pipe_status_str(int status);
 
-/* Fill *cfg with the defaults of an op (grid and split automatic):
+/* Fill *cfg with the defaults of an op (the pipeline parameters of
+ * "cute（12）async_pipeline" section 4 -- stage count, producer and consumer
+ * counts -- plus this library's tile, flag and launch choices; grid and split
+ * automatic):
  *   copy:   stages 2, tile 128x64, 4 producer + 4 consumer waves,
  *           flags NONTEMPORAL | XCD_REMAP | LAZY_COMMIT, swizzle shift 0;
  *   rowsum: stages 3, tile 128x64, 4 producer + 4 consumer waves,
@@ -184,11 +187,14 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N,
                              uint32_t* tile_checksums, void* stream);
 
 /* Bytes of workspace pipe_rowsum needs for this shape and config (0 when each
- * row strip is handled by one workgroup). */
+ * row strip is handled by one workgroup): split x M fp32 segment partials. */
 pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_config_t* cfg,
                                           size_t* bytes);
 
-/* Row sums of an fp16 matrix with fp32 accumulation: out[r] = sum_c A[r][c].
+/* Row sums of an fp16 matrix with fp32 accumulation: out[r] = sum_c A[r][c]
+ * ("cute（12）async_pipeline" 3.2: the consumer's use of each tile, here a
+ * reduction; the pages leave the use open, the strip decomposition below is
+ * this library's).
  * Row strips of 128 rows are cut into cfg->split segments along the columns;
  * segment partials go to the workspace and are added in a fixed order, so the
  * result is deterministic.
@@ -200,7 +206,9 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
                           const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* GEMM mainloop: C = A * B with bf16 A (M x K, row-major) and B (K x N,
+/* GEMM mainloop ("chapter_async_barriers", section 常见的同步规则: a stage
+ * whose copies have all landed is handed to the matrix-multiply consumers;
+ * "cute（12）async_pipeline" ring): C = A * B with bf16 A (M x K, row-major) and B (K x N,
  * row-major; column-major with PIPE_FLAG_GEMM_B_COLMAJOR), fp32 accumulation,
  * C (M x N, row-major) in fp32 -- or, with
  * PIPE_FLAG_GEMM_C_BF16, in bf16 (each fp32 sum rounded to nearest even),
@@ -215,11 +223,15 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
                                  int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                                  const pipe_config_t* cfg, void* stream);
 
-/* Launch geometry an op would use for this shape and config (no launch). */
+/* Launch geometry an op would use for this shape and config, computed on the
+ * host (no launch, no HIP call): LDS per workgroup (ring slots of
+ * "cute（12）async_pipeline" plus barrier words), threads, grid, work items,
+ * tiles per item. A diagnostic of this library, not an operation of the pages. */
 pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
                                 int64_t K, pipe_kernel_info_t* info);
 
-/* Compiled resources of the main kernel that an op would launch for this
+/* A diagnostic of this library, not an operation of the pages.
+ * Compiled resources of the main kernel that an op would launch for this
  * shape and config (the stream, unified or GEMM kernel; not the row-sum
  * finalize or a zero fill), from the HIP runtime's function attributes. It
  * takes the same checks as the op's entry point minus those on pointers, with
