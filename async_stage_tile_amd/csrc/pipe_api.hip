@@ -225,7 +225,6 @@ pipe_status_t resolve_status(const pipe_config_t& c, uint32_t** out) {
 
 pipe_status_t hip_status(hipError_t e) { return e == hipSuccess ? PIPE_OK : PIPE_ERR_HIP; }
 
-
 // GEMM checks that need no pointers: the configuration ...
 pipe_status_t gemm_check_config(const pipe_config_t& c) {
   pipe_status_t s = check_common(c);
@@ -475,18 +474,15 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   const pipe_config_t c = cfg ? *cfg : defaults(op);
   *info = pipe_kernel_info_t{};
   if (op == PIPE_OP_GEMM) {
-    pipe_status_t s = check_common(c);
+    pipe_status_t s = gemm_check_config(c);  // rejects what pipe_gemm_mainloop rejects
     if (s != PIPE_OK) return s;
-    if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
+    if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
     if (M < 0 || N < 0 || K < 0 || M % 128 || N % 128 || K % 64) return PIPE_ERR_SHAPE;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
     const int64_t items = (M / 128) * (N / 128);
     if (items > INT32_MAX) return PIPE_ERR_SHAPE;
     const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
     const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
-    if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
-    if ((c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) && (c.flags & PIPE_FLAG_GEMM_B_LINEAR))
-      return PIPE_ERR_CONFIG;
     info->lds_bytes = gemm_lds_bytes(c.stages, c_bf16, store_wave);
     info->threads = gemm_threads(c.producer_waves, c_bf16, store_wave);
     info->items = (int32_t)items;
@@ -498,10 +494,15 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   if (op != PIPE_OP_COPY && op != PIPE_OP_ROWSUM) return PIPE_ERR_CONFIG;
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
-  if (M < 0 || N < 0 || N % 8) return PIPE_ERR_SHAPE;
   const bool rowsum = op == PIPE_OP_ROWSUM;
+  if (rowsum && (c.flags & PIPE_FLAG_ROW_STRIPS)) return PIPE_ERR_CONFIG;  // always row strips
+  if (M < 0 || N < 0 || N % 8 || !extent_fits(M, N, 2)) return PIPE_ERR_SHAPE;
   const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);
   const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
+  if (unified) {
+    s = check_unified(c, M, N, false);
+    if (s != PIPE_OK) return s;
+  }
   info->lds_bytes = unified ? c.stages * 16384 : stream_lds_bytes(c.stages, c.consumer_waves);
   info->threads = 64 * (unified ? c.consumer_waves : c.producer_waves + c.consumer_waves);
   if (M == 0 || N == 0) return PIPE_OK;

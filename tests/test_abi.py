@@ -338,3 +338,45 @@ def test_kernel_resources_validation_runs_before_the_runtime():
     gb = pt.make_config(pt.PIPE_OP_GEMM, flags=pt.PIPE_FLAG_GEMM_STORE_WAVE)  # needs bf16 C
     assert L.pipe_kernel_resources(pt.PIPE_OP_GEMM, ctypes.byref(gb), 256, 256, 128,
                                    ctypes.byref(out)) == pt.PIPE_ERR_CONFIG
+
+
+def test_gemm_query_rejects_what_the_entry_point_rejects():
+    """For any configuration, pipe_query_kernel(GEMM) returns the error that
+    pipe_gemm_mainloop returns for it (the entry point's configuration checks
+    run before any pointer is looked at, so an empty product exposes them)."""
+    import random
+    rng = random.Random(5)
+    L = pt.lib()
+    info = pt.pipe_kernel_info_t()
+    for _ in range(3000):
+        c = pt.make_config(pt.PIPE_OP_GEMM, stages=rng.randrange(0, 7),
+                           producer_waves=rng.randrange(0, 6), consumer_waves=rng.randrange(0, 6),
+                           split=rng.randrange(0, 3), flags=rng.randrange(0, 0x4000) & ~0x1,
+                           tile_m=rng.choice([64, 128]), tile_n=rng.choice([64, 128]))
+        entry = L.pipe_gemm_mainloop(None, None, None, 0, 0, 0, 0, 0, 0, ctypes.byref(c), None)
+        query = L.pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 128, 128, 64,
+                                    ctypes.byref(info))
+        if entry != pt.PIPE_OK:
+            assert query == entry, (c.stages, c.producer_waves, c.consumer_waves, c.split,
+                                    hex(c.flags), c.tile_m, c.tile_n, entry, query)
+
+
+def test_stream_query_rejects_what_the_entry_points_reject():
+    """pipe_query_kernel applies the copy / row-sum entry points' own
+    configuration and shape rules (checked here without any launch)."""
+    q = pt.lib().pipe_query_kernel
+    info = pt.pipe_kernel_info_t()
+
+    def status(op, M, N, **kw):
+        return q(op, ctypes.byref(pt.make_config(op, **kw)), M, N, 0, ctypes.byref(info))
+
+    U = pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL
+    assert status(pt.PIPE_OP_ROWSUM, 256, 128, flags=pt.PIPE_FLAG_ROW_STRIPS) == pt.PIPE_ERR_CONFIG
+    assert status(pt.PIPE_OP_COPY, 256, 128, stages=2, consumer_waves=1, flags=U) == \
+        pt.PIPE_ERR_CONFIG                                   # unified needs 2, 4 or 8 waves
+    assert status(pt.PIPE_OP_COPY, 250, 128, stages=2, consumer_waves=4, flags=U) == \
+        pt.PIPE_ERR_CONFIG                                   # unified takes whole tiles only
+    assert status(pt.PIPE_OP_COPY, 256, 128, stages=2, consumer_waves=4, flags=U) == pt.PIPE_OK
+    assert status(pt.PIPE_OP_COPY, 1 << 60, 1 << 12) == pt.PIPE_ERR_SHAPE  # spans >= 2^62 bytes
+    assert status(pt.PIPE_OP_GEMM, 256, 256, flags=pt.PIPE_FLAG_TEST_START_PHASE0) == \
+        pt.PIPE_ERR_CONFIG
