@@ -28,7 +28,7 @@ constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_F
                                  PIPE_FLAG_SPLIT_INTERLEAVE | PIPE_FLAG_UNIFIED |
                                  PIPE_FLAG_LAZY_COMMIT | PIPE_FLAG_EAGER_NEWEST |
                                  PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE |
-                                 PIPE_FLAG_GEMM_B_COLMAJOR |
+                                 PIPE_FLAG_GEMM_B_COLMAJOR | PIPE_FLAG_STRIP_GROUPS |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -150,7 +150,22 @@ bool extent_fits(int64_t rows, int64_t ld, int64_t elem) {
 
 struct StreamGeom {
   int32_t tile_rows, tile_cols, n_strips, strip_len, seg_len, split, items, grid;
+  int32_t group;  // tile columns per grouped copy strip (1: plain strips)
 };
+
+// Tile columns per strip of a copy with PIPE_FLAG_STRIP_GROUPS: 4, else 2,
+// where the grouped kernels take the launch; 1 (plain strips) elsewhere.
+int copy_strip_group(const pipe_config_t& c, int64_t M, int64_t N, bool checksums) {
+  if (!(c.flags & PIPE_FLAG_STRIP_GROUPS)) return 1;
+  if (checksums || (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_UNIFIED))) return 1;
+  if (c.tile_m != 128 || c.tile_n != 64 || M % 128 != 0 || N % 64 != 0) return 1;
+  const int64_t tile_cols = N / 64;
+  for (int g = 4; g >= 2; g /= 2)
+    if (tile_cols % g == 0 &&
+        group_shape_supported(c.stages, c.consumer_waves, c.producer_waves, g))
+      return g;
+  return 1;
+}
 
 // Rowsum default split: the smallest power of two that gives >= 256 work
 // items (one workgroup per CU of an MI355X).
@@ -161,17 +176,20 @@ int rowsum_default_split(int n_strips, int strip_len) {
 }
 
 pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool row_strips,
-                              bool rowsum, StreamGeom* g) {
+                              bool rowsum, StreamGeom* g, int group = 1) {
   // Ceiling divisions written so that M or N near INT64_MAX cannot overflow.
   const int64_t tr = M / c.tile_m + (M % c.tile_m != 0);
   const int64_t tc = N / c.tile_n + (N % c.tile_n != 0);
   if (tr > INT32_MAX || tc > INT32_MAX) return PIPE_ERR_SHAPE;
   g->tile_rows = (int32_t)tr;
   g->tile_cols = (int32_t)tc;
-  g->n_strips = row_strips ? g->tile_rows : g->tile_cols;
-  g->strip_len = row_strips ? g->tile_cols : g->tile_rows;
+  g->group = group;
+  g->n_strips = row_strips ? g->tile_rows : g->tile_cols / group;
+  g->strip_len = row_strips ? g->tile_cols : g->tile_rows;  // tile rows of a grouped strip
+  // Default split: the row sum's from rowsum_default_split; a copy keeps one
+  // work item per tile column (G segments per strip of G tile columns).
   int split = c.split;
-  if (split == 0) split = rowsum ? rowsum_default_split(g->n_strips, g->strip_len) : 1;
+  if (split == 0) split = rowsum ? rowsum_default_split(g->n_strips, g->strip_len) : group;
   if (split > g->strip_len) split = g->strip_len;
   if (split < 1) split = 1;
   g->seg_len = (g->strip_len + split - 1) / split;
@@ -182,7 +200,7 @@ pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool
   g->grid = (c.grid == 0 || c.grid > g->items) ? g->items : c.grid;
   // Barrier words count arrivals in 32 bits; keep every count below 2^31 (so
   // that a wrap never occurs, whatever the arrivals per phase).
-  const int64_t per_wg = ((int64_t)g->items + g->grid - 1) / g->grid * g->seg_len;
+  const int64_t per_wg = ((int64_t)g->items + g->grid - 1) / g->grid * g->seg_len * group;
   const int64_t arrivals = c.consumer_waves > c.producer_waves ? c.consumer_waves
                                                                : c.producer_waves;
   if (per_wg * arrivals >= (int64_t(1) << 31)) return PIPE_ERR_SHAPE;
@@ -200,10 +218,12 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   p->items = g.items;
   p->row_strips = row_strips ? 1 : 0;
   p->swz_shift = c.swizzle_shift;
-  // Commit lag: at most S-1 tiles (the protocol's liveness bound) and at most
-  // what the vmcnt counter can track: (lag + 1) tiles of 16 / producer_waves loads.
+  // Commit lag: at most S-1 tiles (the protocol's liveness bound; S-G when
+  // consumers hold G slots at once) and at most what the vmcnt counter can
+  // track: (lag + 1) tiles of 16 / producer_waves loads.
   const int max_lag = stream_max_lag(c.producer_waves);
-  p->lag = c.stages - 1 < max_lag ? c.stages - 1 : max_lag;
+  const int live_lag = c.stages - g.group;
+  p->lag = live_lag < max_lag ? live_lag : max_lag;
   p->xcd_remap = ((c.flags & PIPE_FLAG_XCD_REMAP) && g.items % 8 == 0) ? 1 : 0;
   p->interleave = (c.flags & PIPE_FLAG_SPLIT_INTERLEAVE) ? 1 : 0;
   p->spin_limit = c.spin_limit ? c.spin_limit : kDefaultSpin;
@@ -234,7 +254,8 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
   if ((c.producer_waves != 2 && c.producer_waves != 4) || c.consumer_waves != 4)
     return PIPE_ERR_CONFIG;
   if (c.split > 1) return PIPE_ERR_CONFIG;
-  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE)) return PIPE_ERR_CONFIG;
+  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS))
+    return PIPE_ERR_CONFIG;
   const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
   const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
   if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
@@ -349,7 +370,8 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
     if (s != PIPE_OK) return s;
   }
   StreamGeom g;
-  s = stream_geometry(M, N, c, row_strips, false, &g);
+  s = stream_geometry(M, N, c, row_strips, false, &g,
+                      copy_strip_group(c, M, N, tile_checksums != nullptr));
   if (s != PIPE_OK) return s;
 
   StreamParams p{};
@@ -367,6 +389,9 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   if (unified)
     return hip_status(launch_unified(kOpCopy, c.stages, c.consumer_waves, c.tile_n, g.grid, p,
                                      static_cast<hipStream_t>(stream)));
+  if (g.group > 1)
+    return hip_status(launch_stream_group(c.stages, c.consumer_waves, c.producer_waves, g.group,
+                                          g.grid, p, static_cast<hipStream_t>(stream)));
   return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, c.producer_waves, c.tile_n,
                                   g.grid, p, static_cast<hipStream_t>(stream)));
 }
@@ -507,11 +532,12 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   info->threads = 64 * (unified ? c.consumer_waves : c.producer_waves + c.consumer_waves);
   if (M == 0 || N == 0) return PIPE_OK;
   StreamGeom g;
-  s = stream_geometry(M, N, c, row_strips, rowsum, &g);
+  s = stream_geometry(M, N, c, row_strips, rowsum, &g,
+                      rowsum ? 1 : copy_strip_group(c, M, N, false));
   if (s != PIPE_OK) return s;
   info->grid = g.grid;
   info->items = g.items;
-  info->tiles_per_item = g.seg_len;
+  info->tiles_per_item = g.seg_len * g.group;
   info->split = g.split;
   return PIPE_OK;
 }
@@ -550,7 +576,8 @@ pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int6
       if (s != PIPE_OK) return s;
     }
     StreamGeom g;
-    s = stream_geometry(M, N, c, row_strips, rowsum, &g);
+    s = stream_geometry(M, N, c, row_strips, rowsum, &g,
+                        rowsum ? 1 : copy_strip_group(c, M, N, false));
     if (s != PIPE_OK) return s;
     StreamParams p{};
     fill_stream_params(c, g, row_strips, &p);
@@ -561,10 +588,13 @@ pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int6
     const int kop = rowsum ? kOpRowsum : kOpCopy;
     s = record_kernel(
         [&] {
-          return unified ? launch_unified(kop, c.stages, c.consumer_waves, c.tile_n, g.grid, p,
-                                          nullptr)
-                         : launch_stream(kop, c.stages, c.consumer_waves, c.producer_waves,
-                                         c.tile_n, g.grid, p, nullptr);
+          if (unified)
+            return launch_unified(kop, c.stages, c.consumer_waves, c.tile_n, g.grid, p, nullptr);
+          if (g.group > 1)
+            return launch_stream_group(c.stages, c.consumer_waves, c.producer_waves, g.group,
+                                       g.grid, p, nullptr);
+          return launch_stream(kop, c.stages, c.consumer_waves, c.producer_waves, c.tile_n,
+                               g.grid, p, nullptr);
         },
         &fn);
   } else {

@@ -54,6 +54,12 @@ constexpr bool stream_shape_supported(int S, int C, int PW, int TC = 64) {
   return C == 1 || C == 2 || C == 3 || C == 4 || C == 8;
 }
 
+// Grouped copy strips (128 x 64 tiles; consumers store a tile row of G
+// neighbouring tiles at once): G in {2, 4} with G <= S, C in {4, 8}, PW in {2, 4}.
+constexpr bool group_shape_supported(int S, int C, int PW, int G) {
+  return (G == 2 || G == 4) && G <= S && S <= 8 && (C == 4 || C == 8) && (PW == 2 || PW == 4);
+}
+
 // Largest commit lag for PW producer waves: each wave issues 16 / PW loads per
 // tile and (lag + 1) tiles of them must fit the 63-entry vmcnt counter.
 constexpr int stream_max_lag(int PW) { return 63 / (16 / PW) - 1; }
@@ -68,6 +74,15 @@ template <int S>
 hipError_t launch_stream_stages(int op, int consumers, int producers, int tile_n, int grid,
                                 const StreamParams& p, hipStream_t stream);
 int stream_lds_bytes(int stages, int consumers);
+
+// Grouped copy strips: launch the kernel for (stages, consumers, producers,
+// group); hipErrorInvalidValue for a shape group_shape_supported rejects. The
+// commit lag in `p` must be at most stages - group.
+hipError_t launch_stream_group(int stages, int consumers, int producers, int group, int grid,
+                               const StreamParams& p, hipStream_t stream);
+template <int S>
+hipError_t launch_group_stages(int consumers, int producers, int group, int grid,
+                               const StreamParams& p, hipStream_t stream);
 
 // Unified variant: `waves` waves each load and consume 16 / waves blocks of
 // every tile; divisible shapes only, no checksums or trace. 128 x 64 tiles:

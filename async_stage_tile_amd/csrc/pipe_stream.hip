@@ -109,6 +109,24 @@ __device__ __forceinline__ int item_len(const StreamParams& p, int item) {
   return len < p.seg_len ? len : p.seg_len;
 }
 
+// Grouped column strips (copy, 128 x 64 tiles): strip i spans the G tile
+// columns G*i .. G*i + G - 1 and is walked one tile row at a time, the G tiles
+// of a tile row back to back. Segments and their lengths count tile rows.
+template <int G>
+__device__ __forceinline__ void group_tile_coords(const StreamParams& p, int item, int k,
+                                                  int& tile_row, int& tile_col) {
+  const int strip = item % p.n_strips;
+  const int seg = item / p.n_strips;
+  const int kr = k / G;
+  tile_row = p.interleave ? seg + kr * p.split : seg * p.seg_len + kr;
+  tile_col = strip * G + k % G;
+}
+
+template <int G>
+__device__ __forceinline__ int group_item_len(const StreamParams& p, int item) {
+  return G * item_len(p, item);
+}
+
 // Rows and columns of tile (tr, tc) inside the matrix (the full tile except at
 // ragged edges); wave-uniform.
 template <int TC>
@@ -131,7 +149,7 @@ __device__ __forceinline__ int cols_in(const StreamParams& p, int tc) {
 template <int OP, uint32_t E>
 using StreamBar = typename std::conditional<OP == kOpCopy, Flip<E>, Counter<E>>::type;
 
-template <int S, int C, int PW, int OP, bool MASKED, int TC>
+template <int S, int C, int PW, int OP, bool MASKED, int TC, int G = 1>
 __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
   using Sh = TileShape<TC>;
   using FullBar = StreamBar<OP, PW>;
@@ -150,7 +168,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
 
   for (int it = blockIdx.x; ok && it < p.items; it += gridDim.x) {
     const int item = item_index(p, it);
-    const int len = item_len(p, item);
+    const int len = G == 1 ? item_len(p, item) : group_item_len<G>(p, item);
     for (int k = 0; k < len; ++k, ++t) {
       // producer_acquire: wait until consumers released this slot (committing
       // landed tiles meanwhile, unless commits are lazy).
@@ -162,7 +180,10 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
       }
       if (pw == 0) trace_record(p, t, 0, w, 0);
       int tr, tc;
-      tile_coords(p, item, k, tr, tc);
+      if constexpr (G == 1)
+        tile_coords(p, item, k, tr, tc);
+      else
+        group_tile_coords<G>(p, item, k, tr, tc);
       const uint8_t* g =
           p.src + (int64_t)tr * Sh::kRows * p.ld_src + (int64_t)tc * Sh::kRowBytes;
       const uint32_t slot = uniform(lds_addr(&lds.slots[w.index][0]));
@@ -383,6 +404,104 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped copy consumers (128 x 64 tiles, divisible shapes): each consumer
+// wave waits on the G slots that hold one tile row of a grouped strip, stores
+// its share of those G tiles, then releases all G. One store instruction
+// covers 8/G rows of the group, G*128 contiguous bytes per row, where the
+// per-tile consumer stores 8 rows of 128 bytes: the rows of neighbouring tiles
+// reach memory as one run. Lane l takes tile (l/16) % G, rows 2*((l/16)/G) and
+// 2*((l/16)/G) + 1 of the instruction's rows, chunk position l % 8; so each 16
+// lanes read 256 contiguous bytes of one slot (no bank conflicts). The
+// producer's commit lag must be at most S - G, or the tile that completes a
+// group can be held back while the producer waits for that group's slots.
+// ---------------------------------------------------------------------------
+template <int S, int C, int PW, int G>
+__device__ void group_consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
+  using FullBar = StreamBar<kOpCopy, PW>;
+  using EmptyBar = StreamBar<kOpCopy, C>;
+  static_assert(G == 2 || G == 4, "groups of 2 or 4 tiles");
+  static_assert(G <= S, "a group must fit the ring");
+  constexpr int kInstr = G * kBlocksPerTile;  // 1 KiB store instructions per group
+  static_assert(kInstr % C == 0, "every wave stores the same share");
+  constexpr int NI = kInstr / C;
+  constexpr int kRowsPerInstr = kRowsPerBlock / G;
+  const int lane = lane_id();
+  const int g = (lane >> 4) & (G - 1);
+  const int rsub = ((lane >> 4) / G) * 2 + ((lane >> 3) & 1);
+  const int pos = lane & (kChunksPerRow - 1);
+  PipeState rd = consumer_start(S);
+  int t = 0;
+  bool ok = true;
+
+  for (int it = blockIdx.x; ok && it < p.items; it += gridDim.x) {
+    const int item = item_index(p, it);
+    const int len = group_item_len<G>(p, item);
+    for (int k = 0; k < len; k += G, t += G) {
+      // consumer_wait on each of the group's G slots, in ring order.
+      PipeState w = rd;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!bar_wait<FullBar>(&lds.full[w.index], w.phase, p.spin_limit)) {
+          ok = false;
+          break;
+        }
+        if (cw == 0) trace_record(p, t + j, 1, w, 1 + cw);
+        w.inc();
+      }
+      if (!ok) break;
+      int tr, tc0;
+      group_tile_coords<G>(p, item, k, tr, tc0);
+      int si = rd.index + g;
+      if (si >= S) si -= S;
+      const uint8_t* slot = &lds.slots[si][0];
+      uint8_t* gdst = p.dst + (int64_t)tr * kTileRows * p.ld_dst + (int64_t)(tc0 + g) * kRowBytes;
+      uint4 v[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = (cw + i * C) * kRowsPerInstr + rsub;
+        v[i] = *reinterpret_cast<const uint4*>(slot + r * kRowBytes + pos * kChunkBytes);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = (cw + i * C) * kRowsPerInstr + rsub;
+        const int c = swz(r, pos, p.swz_shift);
+        uint8_t* gd = gdst + (int64_t)r * p.ld_dst + c * kChunkBytes;
+        if (p.nt) {
+          const u32x4 nv = {v[i].x, v[i].y, v[i].z, v[i].w};
+          __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(gd));
+        } else {
+          *reinterpret_cast<uint4*>(gd) = v[i];
+        }
+      }
+      wait_lgkmcnt0();
+      // consumer_release of the G slots, in ring order.
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!p.no_release) EmptyBar::arrive(&lds.empty[rd.index]);
+        rd.inc();
+      }
+    }
+  }
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
+}
+
+template <int S, int C, int PW, int G>
+__global__ void __launch_bounds__(64 * (PW + C)) stream_group_kernel(StreamParams p) {
+  __shared__ StreamLds<S, C> lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  if (threadIdx.x < S) {
+    lds.full[threadIdx.x] = 0u;
+    lds.empty[threadIdx.x] = 0u;
+    lds.fin[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  if (wave < PW)
+    producer<S, C, PW, kOpCopy, false, 64, G>(p, lds, wave);
+  else
+    group_consumer<S, C, PW, G>(p, lds, wave - PW);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int S, int C, int PW, int TC>
@@ -440,12 +559,35 @@ hipError_t launch_stream_stages(int op, int consumers, int producers, int tile_n
   }
 }
 
+template <int S>
+hipError_t launch_group_stages(int consumers, int producers, int group, int grid,
+                               const StreamParams& p, hipStream_t stream) {
+  dim3 block(64 * (producers + consumers));
+#define PIPE_GROUP_CASE(C, PW, G)                                                           \
+  if constexpr (group_shape_supported(S, C, PW, G)) {                                        \
+    if (consumers == C && producers == PW && group == G)                                     \
+      return launch_or_record(stream_group_kernel<S, C, PW, G>, dim3(grid), block, stream, p); \
+  }
+  PIPE_GROUP_CASE(4, 2, 2)
+  PIPE_GROUP_CASE(4, 4, 2)
+  PIPE_GROUP_CASE(8, 2, 2)
+  PIPE_GROUP_CASE(8, 4, 2)
+  PIPE_GROUP_CASE(4, 2, 4)
+  PIPE_GROUP_CASE(4, 4, 4)
+  PIPE_GROUP_CASE(8, 2, 4)
+  PIPE_GROUP_CASE(8, 4, 4)
+#undef PIPE_GROUP_CASE
+  return hipErrorInvalidValue;
+}
+
 #if !defined(PIPE_STREAM_STAGES_LO) || !defined(PIPE_STREAM_STAGES_HI)
 #error "build with -DPIPE_STREAM_STAGES_LO=<s> -DPIPE_STREAM_STAGES_HI=<s>"
 #endif
 #define PIPE_STREAM_INSTANTIATE(S)                                                           \
   template hipError_t launch_stream_stages<S>(int, int, int, int, int, const StreamParams&, \
-                                              hipStream_t);
+                                              hipStream_t);                                 \
+  template hipError_t launch_group_stages<S>(int, int, int, int, const StreamParams&,       \
+                                             hipStream_t);
 #if PIPE_STREAM_STAGES_LO <= 1 && 1 <= PIPE_STREAM_STAGES_HI
 PIPE_STREAM_INSTANTIATE(1)
 #endif

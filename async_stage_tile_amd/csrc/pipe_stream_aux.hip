@@ -28,6 +28,20 @@ hipError_t launch_stream(int op, int stages, int consumers, int producers, int t
   }
 }
 
+hipError_t launch_stream_group(int stages, int consumers, int producers, int group, int grid,
+                               const StreamParams& p, hipStream_t stream) {
+  switch (stages) {
+    case 2: return launch_group_stages<2>(consumers, producers, group, grid, p, stream);
+    case 3: return launch_group_stages<3>(consumers, producers, group, grid, p, stream);
+    case 4: return launch_group_stages<4>(consumers, producers, group, grid, p, stream);
+    case 5: return launch_group_stages<5>(consumers, producers, group, grid, p, stream);
+    case 6: return launch_group_stages<6>(consumers, producers, group, grid, p, stream);
+    case 7: return launch_group_stages<7>(consumers, producers, group, grid, p, stream);
+    case 8: return launch_group_stages<8>(consumers, producers, group, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 int stream_lds_bytes(int stages, int consumers) {
   return stages * kTileBytes + stages * 4 * (3 + consumers);
 }

@@ -78,6 +78,11 @@ WIDE_COPY = {
     "32x256": dict(tile_m=32, tile_n=256, stages=2, producer_waves=4, consumer_waves=8, split=4,
                    flags=_NT | _RM | _IL | _LZ),
 }
+# 128 x 64 tiles down column strips 4 tile columns wide (PIPE_FLAG_STRIP_GROUPS):
+# consumers store a tile row of the strip as 512-byte row runs; 4 interleaved
+# segments per strip, the best ring measured for it.
+_G = 0x4000
+GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _RM | _IL | _LZ | _G)
 WIDE_ROWSUM = {
     "64x128": dict(tile_m=64, tile_n=128, stages=3, producer_waves=4, consumer_waves=4, split=2,
                    flags=_NT | _RM),
@@ -579,7 +584,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
-    ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "rowsum",
+    ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "copy_grouped",
+                                       "rowsum",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
                                        "gemm_bcol", "ceiling", "calib"],
                     default=None,
@@ -614,6 +620,11 @@ def main():
         cfg = dict(WIDE_COPY[args.only.split("_")[1]])
         r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
         log(f"[bench] {args.only}: {r}")
+        return
+    if args.only == "copy_grouped":
+        cfg = dict(GROUPED_COPY)
+        r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+        log(f"[bench] copy_grouped: {r}")
         return
     if args.only in ("rowsum_32x256", "rowsum_64x128"):
         r = bench_rowsum(args.steps, args.warmup, **WIDE_ROWSUM[args.only.split("_")[1]])
@@ -673,6 +684,14 @@ def main():
             wide[name]["kernel_pct_of_peak"] = round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)
             log(f"[bench] copy, {name} tiles: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
         extras["copy_wide_tiles"] = wide
+        cfg = dict(GROUPED_COPY)
+        w = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+        extras["copy_grouped_strips"] = {
+            **{k: w[k] for k in ("tile", "stages", "producer_waves", "consumer_waves", "flags",
+                                 "split", "grid", "kernel_ms", "gbs", "kernel_gbs", "bit_exact")},
+            "strip_tiles": 4,
+            "kernel_pct_of_peak": round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)}
+        log(f"[bench] copy, grouped strips: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
         u = bench_copy(2, max(3, args.steps // 2), args.warmup, consumer_waves=2,
                        flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
                        pt.PIPE_FLAG_XCD_REMAP)

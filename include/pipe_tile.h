@@ -98,6 +98,17 @@ typedef enum {
                                              B[n * ldb + k] with ldb >= K; its tiles are
                                              loaded and read like A's (no transposing LDS
                                              read); exclusive with GEMM_B_LINEAR */
+#define PIPE_FLAG_STRIP_GROUPS 0x4000u /* copy down column strips of 128 x 64 tiles: a strip
+                                          spans G neighbouring tile columns and is walked one
+                                          tile row at a time; consumers wait on the G slots of
+                                          a tile row and store it as G*128-byte row runs. G = 4,
+                                          else 2, where M % 128 == 0, N % 64 == 0, the
+                                          tile-column count is a multiple of G, G <= stages,
+                                          consumer_waves is 4 or 8, producer_waves 2 or 4, and
+                                          no checksums, row strips or unified ring are asked
+                                          for; elsewhere the flag changes nothing. The commit
+                                          lag is then at most stages - G, and split 0 means G
+                                          segments per strip (one work item per tile column) */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the
@@ -127,7 +138,9 @@ typedef struct {
                              evenly; a wave keeps up to 2, 6 or 14 tiles of commit lag)   */
   int32_t consumer_waves; /* copy/rowsum: 1, 2, 3, 4 or 8 (unified: 2, 4 or 8); gemm: 4   */
   int32_t grid;           /* workgroups; 0 = one per work item (capped by the device)     */
-  int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default 1  */
+  int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default:
+                             copy 1 (G with PIPE_FLAG_STRIP_GROUPS), rowsum the smallest
+                             power of two giving >= 256 work items                      */
   int32_t swizzle_shift;  /* row bits XOR-ed into the 16-byte chunk index: 0..3           */
   uint32_t flags;         /* PIPE_FLAG_*                                                  */
   uint32_t spin_limit;    /* polls per wait before giving up; 0 = default (1 << 22)       */

@@ -250,18 +250,30 @@ def _producer_program(S, T, mode, lag, start_phase, tail, part=0):
     return ops
 
 
-def _consumer_program(S, T, release_before_read):
+def _consumer_program(S, T, release_before_read, group=1):
+    """The consumer's instruction list.
+
+    ``group`` = 1 is the pages' consumer: wait on a stage, use it, release it.
+    With ``group`` = G > 1 the consumer takes G consecutive stages at a time:
+    it waits on all G, uses them, then releases all G (a consumer that stores
+    a row of G neighbouring tiles in one pass). T must be a multiple of G.
+    """
+    if group < 1 or T % group:
+        raise ValueError("T must be a multiple of the group")
     ops = []
     cur = PipelineState(S, 0, 0, 0)
-    for t in range(T):
-        ops.append(("wait_full", cur.index, cur.phase))
+    for t0 in range(0, T, group):
+        tiles = []
+        for t in range(t0, t0 + group):
+            ops.append(("wait_full", cur.index, cur.phase))
+            tiles.append((t, cur.index))
+            cur.inc()
         if release_before_read:
-            ops.append(("arrive_empty", cur.index))
-            ops.append(("read", t, cur.index))
+            ops += [("arrive_empty", s_) for _, s_ in tiles]
+            ops += [("read", t, s_) for t, s_ in tiles]
         else:
-            ops.append(("read", t, cur.index))
-            ops.append(("arrive_empty", cur.index))
-        cur.inc()
+            ops += [("read", t, s_) for t, s_ in tiles]
+            ops += [("arrive_empty", s_) for _, s_ in tiles]
     return ops
 
 
@@ -269,7 +281,7 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
                    producers: int = 1, producer_start_phase: int = 1, full_expected=None,
                    empty_expected=None, release_before_read: bool = False,
                    tail: bool = True, eager_min: int = 0, tile_bytes: int = 16384,
-                   max_states: int = 2_000_000) -> ProtocolResult:
+                   group: int = 1, max_states: int = 2_000_000) -> ProtocolResult:
     """Explore every interleaving of the producers, C consumers and the copy engine.
 
     ``mode="tx"``: the producer arrives with expect_tx before issuing the copy
@@ -280,7 +292,9 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
     expects one arrival per producer by default). With ``eager_min`` > 0 a
     producer whose acquire finds the slot still in use, while it has at least
     ``eager_min`` uncommitted tiles, commits its oldest uncommitted tile first
-    (waiting for that tile to land), then polls again.
+    (waiting for that tile to land), then polls again. With ``group`` = G
+    every consumer waits on G consecutive stages before it uses and releases
+    them (see ``_consumer_program``).
 
     Checked: (I1) a consumer reads a slot only after every share of that tile
     landed; (I2) a slot is not overwritten before all consumers of its previous
@@ -298,8 +312,12 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
         raise ValueError("eager commits exist in the landed mode only")
     progs = [_producer_program(S, T, mode, lag, producer_start_phase, tail, part=i)
              for i in range(P)]
-    Q = _consumer_program(S, T, release_before_read)
+    Q = _consumer_program(S, T, release_before_read, group)
     nQ = len(Q)
+    # tiles a consumer at program counter pc has released
+    released_at = [0]
+    for op in Q:
+        released_at.append(released_at[-1] + (op[0] == "arrive_empty"))
     nbar = 2 * S
     all_parts = frozenset(range(P))
 
@@ -323,10 +341,7 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
     max_ahead = 0
 
     def released_tiles(qpc):
-        done = qpc // 3
-        if qpc % 3 == 2 and release_before_read:
-            done += 1
-        return done
+        return released_at[qpc]
 
     while stack:
         if len(seen) > max_states:

@@ -380,3 +380,41 @@ def test_stream_query_rejects_what_the_entry_points_reject():
     assert status(pt.PIPE_OP_COPY, 1 << 60, 1 << 12) == pt.PIPE_ERR_SHAPE  # spans >= 2^62 bytes
     assert status(pt.PIPE_OP_GEMM, 256, 256, flags=pt.PIPE_FLAG_TEST_START_PHASE0) == \
         pt.PIPE_ERR_CONFIG
+
+
+def test_strip_groups_geometry_and_where_they_apply():
+    """PIPE_FLAG_STRIP_GROUPS: strips of 4 (else 2) tile columns where the grouped
+    kernels take the launch, the plain geometry elsewhere; never for the GEMM."""
+    G = pt.PIPE_FLAG_STRIP_GROUPS
+    q = lambda M, N, **kw: pt.pipe_query_kernel(pt.PIPE_OP_COPY, M, N, **kw)
+
+    def group(M, N, **kw):   # with one segment per strip: one item per strip
+        return (N // 64) // q(M, N, split=1, **kw)["items"]
+
+    # headline shape: 64 strips of 4 tile columns, default split 4 -> 256 items
+    h = q(16384, 16384, stages=5, flags=G)
+    assert (h["items"], h["split"], h["tiles_per_item"]) == (256, 4, 128)
+    assert group(16384, 16384, stages=5, flags=G) == 4
+    assert group(16384, 16384, stages=3, flags=G) == 2          # G <= S
+    assert group(16384, 16384, stages=1, flags=G) == 1
+    assert group(1024, 384, stages=8, flags=G) == 2             # 6 tile columns
+    assert group(1024, 320, stages=8, flags=G) == 1             # 5 tile columns
+    assert group(1024, 1024, stages=4, flags=G) == 4
+    for kw in (dict(consumer_waves=2), dict(consumer_waves=3), dict(producer_waves=1),
+               dict(tile_m=64, tile_n=128)):
+        assert q(1024, 1024, stages=4, split=1, flags=G, **kw) == \
+            q(1024, 1024, stages=4, split=1, flags=0, **kw), kw
+    for flags in (G | pt.PIPE_FLAG_ROW_STRIPS, G | pt.PIPE_FLAG_UNIFIED):
+        kw = dict(consumer_waves=4) if flags & pt.PIPE_FLAG_UNIFIED else {}
+        plain = q(1024, 1024, stages=4, split=1, flags=flags & ~G, **kw)
+        assert q(1024, 1024, stages=4, split=1, flags=flags, **kw) == plain
+    # ragged shapes take the plain (masked) path
+    assert q(1000, 1024, stages=8, split=1, flags=G) == q(1000, 1024, stages=8, split=1)
+    assert q(1024, 1000, stages=8, split=1, flags=G) == q(1024, 1000, stages=8, split=1)
+    # the row sum ignores the flag; the GEMM rejects it
+    assert pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 1024, 4096, flags=G) == \
+        pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, 1024, 4096, flags=0)
+    info = pt.pipe_kernel_info_t()
+    c = pt.make_config(pt.PIPE_OP_GEMM, flags=G)
+    assert pt.lib().pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 256, 256, 256,
+                                      ctypes.byref(info)) == pt.PIPE_ERR_CONFIG

@@ -188,6 +188,32 @@ def test_eager_commit_lifts_the_lag_bound(S):
         assert r2.completed == (S >= 2) and r2.deadlock == (S < 2), (S, L)
 
 
+@pytest.mark.parametrize("S,G", [(2, 2), (3, 2), (4, 2), (8, 2), (4, 4), (5, 4), (6, 4), (8, 4)])
+def test_grouped_consumer_lag_bound(S, G):
+    """A consumer that holds G stages at once (it waits on G consecutive
+    stages before releasing any) is live exactly when the producer's commit
+    lag L is at most S - G. Closed form: the producer commits tile j only
+    after issuing tile j + L, which needs the slot of tile j + L - S released;
+    that tile must lie in an earlier group than j's, i.e. j + L - S < j - (G - 1)
+    for the first tile j of a group."""
+    T = S + 2 * G if S + 2 * G <= 16 else 4 * G
+    T -= T % G
+    for L in range(S):
+        r = P.check_protocol(S, T, 1, mode="landed", lag=L, group=G)
+        live = L <= S - G
+        assert r.completed == live and r.deadlock == (not live), (S, G, L)
+        assert r.violations == []
+    # two consumers and two producers at the bound
+    r = P.check_protocol(S, 2 * G, 2, mode="landed", lag=S - G, group=G, producers=2)
+    assert r.completed and not r.deadlock and r.violations == []
+    assert r.max_ahead <= S
+
+
+def test_grouped_consumer_needs_whole_groups():
+    with pytest.raises(ValueError):
+        P.check_protocol(4, 6, 1, mode="landed", lag=0, group=4)
+
+
 def test_eager_commit_needs_landed_mode():
     with pytest.raises(ValueError):
         P.check_protocol(2, 3, 1, mode="tx", eager_min=1)
