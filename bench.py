@@ -720,6 +720,9 @@ def main():
         g = bench_gemm(max(3, args.steps // 2), args.warmup)
         log(f"[bench] gemm: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=3)
+        log(f"[bench] gemm, three-stage ring: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_three_stage"] = g
         g = bench_gemm(max(3, args.steps // 2), args.warmup, out_dtype=torch.bfloat16)
         log(f"[bench] gemm, bf16 C: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16"] = g
