@@ -179,15 +179,44 @@ def _check(status: int, where: str):
 
 
 def make_config(op: int, **kw) -> pipe_config_t:
+    """The op's default config with the given fields replaced. ``trace`` and
+    ``status`` may be device tensors (or raw device addresses): a tensor must
+    be contiguous and hold ``trace_capacity`` records of PIPE_TRACE_WORDS
+    32-bit words, or one 32-bit word for ``status``; the tensors are kept on
+    the config (``cfg.buffers``) for the device check of the entry points."""
     cfg = pipe_config_t()
     _check(lib().pipe_config_default(op, ctypes.byref(cfg)), "pipe_config_default")
+    buffers = {}
     for k, v in kw.items():
-        if k in ("trace", "status"):
-            v = _ptr(v) if v is not None else None
         if not hasattr(cfg, k):
             raise TypeError(f"unknown config field {k!r}")
+        if k in ("trace", "status"):
+            if v is not None and not isinstance(v, int):
+                buffers[k] = v
+            v = _ptr(v) if v is not None else None
         setattr(cfg, k, v)
+    need = {"trace": 4 * PIPE_TRACE_WORDS * max(0, int(cfg.trace_capacity)), "status": 4}
+    for k, t in buffers.items():
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{k} must be a contiguous device tensor")
+        if t.numel() * t.element_size() < need[k]:
+            raise ValueError(f"{k} holds {t.numel() * t.element_size()} bytes, "
+                             f"{need[k]} needed")
+    cfg.buffers = list(buffers.values())
     return cfg
+
+
+def _device(*tensors):
+    """The one device that all the given tensors (None skipped) live on."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+    return dev
 
 
 def _ptr(t) -> int:
@@ -198,9 +227,13 @@ def _ptr(t) -> int:
     return int(t.data_ptr())
 
 
-def _stream(stream=None):
+def _stream(stream=None, device=None):
+    """The given stream, else the current stream of `device`; it must belong
+    to `device`."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    if device is not None and s.device != device:
+        raise ValueError(f"stream of {s.device} for tensors on {device}")
     return ctypes.c_void_p(int(s.cuda_stream))
 
 
@@ -230,6 +263,11 @@ def _check_matrix(t, name, dtypes):
     return matrix_geometry(tuple(t.shape), t.stride() if t.dim() == 2 else (), name)
 
 
+def _check_vector(t, n, dtype, name):
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of >= {n} elements")
+
+
 def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):
     """Copy a 16-bit matrix through the tile ring; optionally per-tile code sums."""
     import torch
@@ -240,13 +278,15 @@ def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):
     if (Md, Nd) != (M, N):
         raise ValueError("dst shape differs from src")
     c = make_config(PIPE_OP_COPY, **cfg)
+    dev = _device(src, dst, *c.buffers)
     chk = None
     if checksums:   # one word per tile of the configured shape
         tm, tn = max(1, c.tile_m), max(1, c.tile_n)
         chk = torch.empty(((M + tm - 1) // tm) * ((N + tn - 1) // tn), dtype=torch.int32,
-                          device=src.device)
-    st = lib().pipe_tile_copy(_ptr(src), _ptr(dst), M, N, ld_src, ld_dst, ctypes.byref(c),
-                              _ptr(chk), _stream(stream))
+                          device=dev)
+    with torch.cuda.device(dev):
+        st = lib().pipe_tile_copy(_ptr(src), _ptr(dst), M, N, ld_src, ld_dst, ctypes.byref(c),
+                                  _ptr(chk), _stream(stream, dev))
     _check(st, "pipe_tile_copy")
     return (dst, chk) if checksums else dst
 
@@ -270,8 +310,13 @@ def pipe_rowsum(A, out=None, workspace=None, stream=None, **cfg):
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = make_config(PIPE_OP_ROWSUM, **cfg)
-    st = lib().pipe_rowsum(_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c), _ptr(workspace),
-                           wbytes, _stream(stream))
+    dev = _device(A, out, workspace, *c.buffers)
+    _check_vector(out, M, torch.float32, "out")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    with torch.cuda.device(dev):
+        st = lib().pipe_rowsum(_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c), _ptr(workspace),
+                               wbytes, _stream(stream, dev))
     _check(st, "pipe_rowsum")
     return out
 
@@ -324,8 +369,10 @@ def pipe_gemm_mainloop(A, B, C=None, stream=None, out_dtype=None, **cfg):
     if (Mc, Nc) != (M, N):
         raise ValueError("C shape mismatch")
     c = _gemm_config(C, cfg, b_col)
-    st = lib().pipe_gemm_mainloop(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
-                                  ctypes.byref(c), _stream(stream))
+    dev = _device(A, B, C, *c.buffers)
+    with torch.cuda.device(dev):
+        st = lib().pipe_gemm_mainloop(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                      ctypes.byref(c), _stream(stream, dev))
     _check(st, "pipe_gemm_mainloop")
     return C
 
@@ -356,8 +403,9 @@ def pipe_device_status(clear: bool = False) -> int:
 
 # ---------------------------------------------------------------------------
 # Pre-marshalled launchers: validate and marshal once, then each call is a
-# single C-ABI call on the current stream (for repeated launches on the same
-# buffers, e.g. timing loops).
+# single C-ABI call (with the tensors' device current) on the stream given, or
+# else the device's current stream at creation (for repeated launches on the
+# same buffers, e.g. timing loops).
 # ---------------------------------------------------------------------------
 def copy_launcher(src, dst, checksums=None, stream=None, **cfg):
     import torch
@@ -366,11 +414,19 @@ def copy_launcher(src, dst, checksums=None, stream=None, **cfg):
     if (Md, Nd) != (M, N):
         raise ValueError("dst shape differs from src")
     c = make_config(PIPE_OP_COPY, **cfg)
+    dev = _device(src, dst, checksums, *c.buffers)
+    if checksums is not None:
+        tm, tn = max(1, c.tile_m), max(1, c.tile_n)
+        tiles = ((M + tm - 1) // tm) * ((N + tn - 1) // tn)
+        if checksums.element_size() != 4:
+            raise ValueError("checksums must hold 32-bit words")
+        _check_vector(checksums, tiles, checksums.dtype, "checksums")
     fn, args = lib().pipe_tile_copy, (_ptr(src), _ptr(dst), M, N, ld_src, ld_dst,
-                                       ctypes.byref(c), _ptr(checksums), _stream(stream))
+                                       ctypes.byref(c), _ptr(checksums), _stream(stream, dev))
 
     def launch():
-        _check(fn(*args), "pipe_tile_copy")
+        with torch.cuda.device(dev):
+            _check(fn(*args), "pipe_tile_copy")
     launch.keep = (c, src, dst, checksums)
     return launch
 
@@ -380,11 +436,16 @@ def rowsum_launcher(A, out, workspace=None, stream=None, **cfg):
     M, N, lda = _check_matrix(A, "A", (torch.float16,))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = make_config(PIPE_OP_ROWSUM, **cfg)
+    dev = _device(A, out, workspace, *c.buffers)
+    _check_vector(out, M, torch.float32, "out")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     fn, args = lib().pipe_rowsum, (_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c),
-                                    _ptr(workspace), wbytes, _stream(stream))
+                                    _ptr(workspace), wbytes, _stream(stream, dev))
 
     def launch():
-        _check(fn(*args), "pipe_rowsum")
+        with torch.cuda.device(dev):
+            _check(fn(*args), "pipe_rowsum")
     launch.keep = (c, A, out, workspace)
     return launch
 
@@ -397,11 +458,13 @@ def gemm_launcher(A, B, C, stream=None, **cfg):
     if K2 != K or (Mc, Nc) != (M, N):
         raise ValueError("shape mismatch")
     c = _gemm_config(C, cfg, b_col)
+    dev = _device(A, B, C, *c.buffers)
     fn, args = lib().pipe_gemm_mainloop, (_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
-                                           ctypes.byref(c), _stream(stream))
+                                           ctypes.byref(c), _stream(stream, dev))
 
     def launch():
-        _check(fn(*args), "pipe_gemm_mainloop")
+        with torch.cuda.device(dev):
+            _check(fn(*args), "pipe_gemm_mainloop")
     launch.keep = (c, A, B, C)
     return launch
 

@@ -418,3 +418,18 @@ def test_strip_groups_geometry_and_where_they_apply():
     c = pt.make_config(pt.PIPE_OP_GEMM, flags=G)
     assert pt.lib().pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 256, 256, 256,
                                       ctypes.byref(info)) == pt.PIPE_ERR_CONFIG
+
+
+def test_binding_rejects_host_buffers_and_mixed_devices():
+    """trace/status must be device tensors, and every tensor of a call must live
+    on one device (checked before anything reaches the library)."""
+    import torch
+    with pytest.raises(ValueError):
+        pt.make_config(pt.PIPE_OP_COPY, status=torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        pt.make_config(pt.PIPE_OP_COPY, trace=torch.zeros(64, dtype=torch.int32),
+                       trace_capacity=8)
+    with pytest.raises(ValueError):
+        pt._device(torch.zeros(1), torch.zeros(1, device="meta"))
+    assert pt._device(None, torch.zeros(1), None) == torch.device("cpu")
+    assert pt._device() is None

@@ -571,3 +571,36 @@ def test_kernel_lookup_on_one_thread_never_swallows_a_launch_on_another():
         stop.set()
         t.join()
     assert len(seen) > 0 and all(v > 0 for v in seen)
+
+
+def test_binding_checks_buffer_sizes():
+    """Undersized trace, status, out and checksum buffers are refused by the
+    binding before any launch (the kernels would write past them)."""
+    src = synth.unique_codes(256, 256).to(DEV)
+    small_trace = torch.zeros(8 * pt.PIPE_TRACE_WORDS - 1, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        pt.pipe_tile_copy(src, flags=pt.PIPE_FLAG_TRACE, trace=small_trace, trace_capacity=8)
+    with pytest.raises(ValueError):
+        pt.pipe_tile_copy(src, status=torch.zeros(0, dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError):
+        pt.pipe_tile_copy(src, status=torch.zeros(4, dtype=torch.int32, device=DEV)[::2])
+    A = synth.small_int((256, 1024), -8, 8, torch.float16, seed=3).to(DEV)
+    with pytest.raises(ValueError):
+        pt.pipe_rowsum(A, out=torch.empty(255, device=DEV))
+    with pytest.raises(ValueError):
+        pt.pipe_rowsum(A, out=torch.empty(256, dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError):
+        pt.rowsum_launcher(A, torch.empty(256, device=DEV),
+                           workspace=torch.empty(2 * 65536, dtype=torch.uint8, device=DEV)[::2],
+                           split=4)
+    dst = torch.empty_like(src)
+    with pytest.raises(ValueError):   # 2 x 4 tiles of 128 x 64 need 8 words
+        pt.copy_launcher(src, dst, checksums=torch.zeros(7, dtype=torch.int32, device=DEV))
+    # the exact sizes are accepted
+    trace = torch.zeros(8 * pt.PIPE_TRACE_WORDS, dtype=torch.int32, device=DEV)
+    pt.pipe_tile_copy(src, dst, flags=pt.PIPE_FLAG_TRACE, trace=trace, trace_capacity=8)
+    chk = torch.zeros(8, dtype=torch.int32, device=DEV)
+    pt.copy_launcher(src, dst, checksums=chk)()
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dst), _bits(src))
+    assert np.array_equal(chk.cpu().numpy().view(np.uint32), R.tile_checksums(src.cpu().numpy()))

@@ -51,3 +51,30 @@ def test_bank_model_basics():
     assert Z.bank_conflicts(swz, 16, nbanks=32) == 0
     broadcast = [64] * 64
     assert Z.bank_conflicts(broadcast, 4, nbanks=32) == 0
+
+
+@pytest.mark.parametrize("G", [2, 4])
+@pytest.mark.parametrize("S,first", [(5, 0), (5, 3), (8, 6), (4, 2)])
+def test_grouped_store_reads_are_conflict_free(G, S, first):
+    """The grouped copy consumers' wave-wide reads: lane l takes slot
+    (first + (l/16) % G) mod S of the ring, row 2*((l/16)/G) + (l/8) % 2 of the
+    instruction's 8/G rows, chunk position l % 8. Any 16 consecutive lanes read
+    256 contiguous bytes of one slot, so the bank model finds no conflict for
+    any instruction, while the plain alternative (8 lanes per tile, the G tiles
+    side by side) puts two slots' identical offsets into one 16-lane pass."""
+    if G > S:
+        pytest.skip("a group must fit the ring")
+    rows_per_instr = 8 // G
+    for instr in range(16 * G):
+        addrs = []
+        for lane in range(64):
+            g = (lane >> 4) % G
+            slot = (first + g) % S
+            r = instr * rows_per_instr + 2 * ((lane >> 4) // G) + ((lane >> 3) & 1)
+            addrs.append(slot * 16384 + r * 128 + (lane & 7) * 16)
+        assert Z.bank_conflicts(addrs, 16, nbanks=64) == 0
+        assert Z.bank_conflicts(addrs, 16, nbanks=64, lanes_per_pass=8) == 0
+    # the naive lane order: lanes 8g..8g+7 read slot g's row, G slots per 8 rows
+    naive = [((first + (l >> 3) % G) % S) * 16384 + ((l >> 3) // G) * 128 + (l & 7) * 16
+             for l in range(64)]
+    assert Z.bank_conflicts(naive, 16, nbanks=64) > 0
