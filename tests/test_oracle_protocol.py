@@ -122,6 +122,20 @@ def test_commit_lag_rule(S):
             assert r.deadlock, (S, L)
 
 
+@pytest.mark.parametrize("S,T", [(3, 2), (2, 5)])
+def test_missing_commit_starves_the_consumers(S, T):
+    """A producer that acquires and issues but never commits: the consumers
+    never see a full phase ("cuda-features-10-pipelines" 4.10.2). With T <= S
+    the producer finishes its issues and only the consumers wait; with T > S it
+    also runs out of writable stages."""
+    r = P.check_protocol(S, T, 1, mode="landed", lag=0, commits=False, tail=False)
+    assert r.deadlock and not r.completed
+    ok = P.check_protocol(S, T, 1, mode="landed", lag=0, tail=False)
+    assert ok.completed and not ok.deadlock
+    with pytest.raises(ValueError):
+        P.check_protocol(S, T, 1, mode="tx", commits=False)
+
+
 def test_no_tail_still_consumes_everything():
     r = P.check_protocol(2, 3, 2, tail=False)
     assert r.completed

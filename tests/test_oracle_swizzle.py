@@ -78,3 +78,18 @@ def test_grouped_store_reads_are_conflict_free(G, S, first):
     naive = [((first + (l >> 3) % G) % S) * 16384 + ((l >> 3) // G) * 128 + (l & 7) * 16
              for l in range(64)]
     assert Z.bank_conflicts(naive, 16, nbanks=64) > 0
+
+
+def test_reading_the_slot_unswizzled_gives_wrong_positions():
+    """"cute（11）hopper之TMA_copy" section 4: a raw read of the swizzled buffer
+    puts elements in the wrong place. Reading chunk c of row r at its logical
+    position r*128 + c*16 finds the chunk c ^ (r & 7) instead, which is right
+    only on rows r with r & 7 == 0."""
+    wrong_rows = set()
+    for r in range(128):
+        for c in range(8):
+            found = Z.chunk_position(r, c, 0)      # the involution: position -> chunk
+            if found != c:
+                wrong_rows.add(r)
+            assert (found == c) == (r % 8 == 0)
+    assert len(wrong_rows) == 112
