@@ -366,17 +366,47 @@ def bench_small(reps, warmup):
     in 2 x 2 tiles of 128 x 64 through a one-slot ring, and a 128 x 512 matrix
     through a three-slot ring of one workgroup (1 producer + 3 consumer waves)
     with per-tile checksums. Each is checked bit for bit; the checksums against
-    a plain tensor sum of each tile's 16-bit codes."""
+    a plain tensor sum of each tile's 16-bit codes. `graph_us` is the time per
+    launch when 100 launches are captured in one HIP graph and replayed, which
+    leaves out the host's per-launch cost."""
     import torch
 
     import async_stage_tile_amd as pt
     import synth
+
+    def graph_us(make):
+        """Per-launch time of 100 launches of make()'s launcher replayed from one
+        graph (the launcher is made inside the capture, so it binds the
+        capture stream)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fn = make()
+            for _ in range(100):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return round(a.elapsed_time(b) / 1000.0 * 1e3, 2)   # ms per 1000 launches -> us
+
     out = {}
     src = synth.index_coded(256, 128, device="cuda")
     dst = torch.empty_like(src)
     fn = pt.copy_launcher(src, dst, stages=1)
     med, mn = launch_stats(fn, reps, warmup)
+    dst.zero_()
+    g_us = graph_us(lambda: pt.copy_launcher(src, dst, stages=1))
     out["copy_256x128_s1"] = {"median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                              "graph_us": g_us,
                               "bit_exact": torch.equal(dst.view(torch.int16),
                                                        src.view(torch.int16))}
     src = synth.uniform((128, 512), torch.float16, seed=42, device="cuda")
@@ -385,10 +415,15 @@ def bench_small(reps, warmup):
     fn = pt.copy_launcher(src, dst, checksums=chk, stages=3, producer_waves=1, consumer_waves=3,
                           grid=1, flags=0)
     med, mn = launch_stats(fn, reps, warmup)
+    dst.zero_()
+    chk.zero_()
+    g_us = graph_us(lambda: pt.copy_launcher(src, dst, checksums=chk, stages=3,
+                                             producer_waves=1, consumer_waves=3, grid=1,
+                                             flags=0))
     codes = src.view(torch.int16).to(torch.int64) & 0xFFFF
     want = codes.view(128, 8, 64).sum(dim=(0, 2))
     out["copy_128x512_s3_1p3c"] = {
-        "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+        "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2), "graph_us": g_us,
         "bit_exact": torch.equal(dst.view(torch.int16), src.view(torch.int16)),
         "checksums_exact": torch.equal(chk.to(torch.int64) & 0xFFFFFFFF, want)}
     return out
