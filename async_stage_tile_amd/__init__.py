@@ -56,6 +56,7 @@ PIPE_FLAG_GEMM_C_BF16 = 0x800
 PIPE_FLAG_GEMM_STORE_WAVE = 0x1000
 PIPE_FLAG_GEMM_B_COLMAJOR = 0x2000
 PIPE_FLAG_STRIP_GROUPS = 0x4000
+PIPE_FLAG_PRODUCER_VGPR = 0x8000
 
 PIPE_STATUS_TIMEOUT_PRODUCER = 0x1
 PIPE_STATUS_TIMEOUT_CONSUMER = 0x2

@@ -29,6 +29,7 @@ constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_F
                                  PIPE_FLAG_LAZY_COMMIT | PIPE_FLAG_EAGER_NEWEST |
                                  PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE |
                                  PIPE_FLAG_GEMM_B_COLMAJOR | PIPE_FLAG_STRIP_GROUPS |
+                                 PIPE_FLAG_PRODUCER_VGPR |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -117,6 +118,11 @@ pipe_status_t check_stream_cfg(const pipe_config_t& c) {
         (c.tile_m == 32 && c.tile_n == 256)))
     return PIPE_ERR_CONFIG;
   const int cw = c.consumer_waves, pw = c.producer_waves;
+  if (c.flags & PIPE_FLAG_PRODUCER_VGPR) {
+    if ((c.flags & PIPE_FLAG_UNIFIED) || c.tile_m != 128 || c.tile_n != 64 ||
+        !regs_shape_supported(c.stages, cw, pw))
+      return PIPE_ERR_CONFIG;
+  }
   if (c.flags & PIPE_FLAG_UNIFIED) {
     if (!unified_shape_supported(c.stages, cw, c.tile_n)) return PIPE_ERR_CONFIG;
     return c.stages * 16384 > kLdsLimit ? PIPE_ERR_STAGES : PIPE_OK;
@@ -156,7 +162,7 @@ struct StreamGeom {
 // Tile columns per strip of a copy with PIPE_FLAG_STRIP_GROUPS: 4, else 2,
 // where the grouped kernels take the launch; 1 (plain strips) elsewhere.
 int copy_strip_group(const pipe_config_t& c, int64_t M, int64_t N, bool checksums) {
-  if (!(c.flags & PIPE_FLAG_STRIP_GROUPS)) return 1;
+  if (!(c.flags & PIPE_FLAG_STRIP_GROUPS) || (c.flags & PIPE_FLAG_PRODUCER_VGPR)) return 1;
   if (checksums || (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_UNIFIED))) return 1;
   if (c.tile_m != 128 || c.tile_n != 64 || M % 128 != 0 || N % 64 != 0) return 1;
   const int64_t tile_cols = N / 64;
@@ -235,6 +241,21 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   p->eager = eager_min_pending(c.flags);
 }
 
+// The main kernel of a copy or row sum: the unified ring, the register
+// producer engine, grouped strips, or the DMA ring.
+hipError_t launch_stream_op(int op, const pipe_config_t& c, const StreamGeom& g,
+                            const StreamParams& p, hipStream_t stream) {
+  if (c.flags & PIPE_FLAG_UNIFIED)
+    return launch_unified(op, c.stages, c.consumer_waves, c.tile_n, g.grid, p, stream);
+  if (c.flags & PIPE_FLAG_PRODUCER_VGPR)
+    return launch_stream_regs(op, c.stages, c.consumer_waves, c.producer_waves, g.grid, p, stream);
+  if (g.group > 1)
+    return launch_stream_group(c.stages, c.consumer_waves, c.producer_waves, g.group, g.grid, p,
+                               stream);
+  return launch_stream(op, c.stages, c.consumer_waves, c.producer_waves, c.tile_n, g.grid, p,
+                       stream);
+}
+
 pipe_status_t resolve_status(const pipe_config_t& c, uint32_t** out) {
   if (c.status != nullptr) {
     *out = c.status;
@@ -254,7 +275,8 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
   if ((c.producer_waves != 2 && c.producer_waves != 4) || c.consumer_waves != 4)
     return PIPE_ERR_CONFIG;
   if (c.split > 1) return PIPE_ERR_CONFIG;
-  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS))
+  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS |
+                 PIPE_FLAG_PRODUCER_VGPR))
     return PIPE_ERR_CONFIG;
   const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
   const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
@@ -386,14 +408,7 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  if (unified)
-    return hip_status(launch_unified(kOpCopy, c.stages, c.consumer_waves, c.tile_n, g.grid, p,
-                                     static_cast<hipStream_t>(stream)));
-  if (g.group > 1)
-    return hip_status(launch_stream_group(c.stages, c.consumer_waves, c.producer_waves, g.group,
-                                          g.grid, p, static_cast<hipStream_t>(stream)));
-  return hip_status(launch_stream(kOpCopy, c.stages, c.consumer_waves, c.producer_waves, c.tile_n,
-                                  g.grid, p, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_stream_op(kOpCopy, c, g, p, static_cast<hipStream_t>(stream)));
 }
 
 pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_config_t* cfg,
@@ -453,10 +468,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  s = unified ? hip_status(launch_unified(kOpRowsum, c.stages, c.consumer_waves, c.tile_n, g.grid,
-                                          p, st))
-              : hip_status(launch_stream(kOpRowsum, c.stages, c.consumer_waves, c.producer_waves,
-                                         c.tile_n, g.grid, p, st));
+  s = hip_status(launch_stream_op(kOpRowsum, c, g, p, st));
   if (s != PIPE_OK || need == 0) return s;
   return hip_status(launch_rowsum_finalize(static_cast<const float*>(workspace), out, M,
                                            g.split, st));
@@ -586,17 +598,7 @@ pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int6
     p.M = M;
     p.N = N;
     const int kop = rowsum ? kOpRowsum : kOpCopy;
-    s = record_kernel(
-        [&] {
-          if (unified)
-            return launch_unified(kop, c.stages, c.consumer_waves, c.tile_n, g.grid, p, nullptr);
-          if (g.group > 1)
-            return launch_stream_group(c.stages, c.consumer_waves, c.producer_waves, g.group,
-                                       g.grid, p, nullptr);
-          return launch_stream(kop, c.stages, c.consumer_waves, c.producer_waves, c.tile_n,
-                               g.grid, p, nullptr);
-        },
-        &fn);
+    s = record_kernel([&] { return launch_stream_op(kop, c, g, p, nullptr); }, &fn);
   } else {
     return PIPE_ERR_CONFIG;
   }

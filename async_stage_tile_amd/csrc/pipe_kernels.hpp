@@ -60,6 +60,11 @@ constexpr bool group_shape_supported(int S, int C, int PW, int G) {
   return (G == 2 || G == 4) && G <= S && S <= 8 && (C == 4 || C == 8) && (PW == 2 || PW == 4);
 }
 
+// Register producer engine (128 x 64 tiles): S = 1..4, C in {3, 4}, PW in {1, 4}.
+constexpr bool regs_shape_supported(int S, int C, int PW) {
+  return S >= 1 && S <= 4 && (C == 3 || C == 4) && (PW == 1 || PW == 4);
+}
+
 // Largest commit lag for PW producer waves: each wave issues 16 / PW loads per
 // tile and (lag + 1) tiles of them must fit the 63-entry vmcnt counter.
 constexpr int stream_max_lag(int PW) { return 63 / (16 / PW) - 1; }
@@ -83,6 +88,15 @@ hipError_t launch_stream_group(int stages, int consumers, int producers, int gro
 template <int S>
 hipError_t launch_group_stages(int consumers, int producers, int group, int grid,
                                const StreamParams& p, hipStream_t stream);
+
+// Register producer engine: launch the stream kernel whose producers load
+// into registers and write the slots with ds_write_b128 (128 x 64 tiles);
+// hipErrorInvalidValue for a shape regs_shape_supported rejects.
+hipError_t launch_stream_regs(int op, int stages, int consumers, int producers, int grid,
+                              const StreamParams& p, hipStream_t stream);
+template <int S>
+hipError_t launch_regs_stages(int op, int consumers, int producers, int grid,
+                              const StreamParams& p, hipStream_t stream);
 
 // Unified variant: `waves` waves each load and consume 16 / waves blocks of
 // every tile; divisible shapes only, no checksums or trace. 128 x 64 tiles:

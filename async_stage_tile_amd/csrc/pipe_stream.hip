@@ -404,6 +404,191 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Register producer engine (PIPE_FLAG_PRODUCER_VGPR; 128 x 64 tiles): each
+// producer wave loads its blocks of a tile with global_load_dwordx4 into
+// registers, 8 lanes per 128-byte row piece in natural chunk order, and writes
+// them with ds_write_b128 at the swizzled slot position; the slot layout is
+// the DMA engine's. The loads run D - 1 tiles ahead of the writes (D register
+// buffers; the loads do not need a slot), and a tile is committed as soon as
+// its writes have returned (lgkmcnt), so the commit lag and commit policies
+// of the DMA engine do not apply.
+// ---------------------------------------------------------------------------
+struct TileWalk {
+  int it;    // work-item slot: blockIdx.x + n * gridDim.x
+  int item;  // the item it names (after the XCD permutation)
+  int len;   // tiles of the item
+  int k;     // tile within the item
+};
+
+// Move to the next tile that exists (the first of the next item when this
+// item is used up).
+__device__ __forceinline__ void walk_settle(const StreamParams& p, TileWalk& w) {
+  while (w.it < p.items && w.k >= w.len) {
+    w.it += gridDim.x;
+    w.k = 0;
+    if (w.it < p.items) {
+      w.item = item_index(p, w.it);
+      w.len = item_len(p, w.item);
+    }
+  }
+}
+
+__device__ __forceinline__ TileWalk walk_start(const StreamParams& p) {
+  TileWalk w{(int)blockIdx.x, 0, 0, 0};
+  if (w.it < p.items) {
+    w.item = item_index(p, w.it);
+    w.len = item_len(p, w.item);
+  }
+  walk_settle(p, w);
+  return w;
+}
+
+// Loads of one tile's blocks for producer wave `pw`; with `valid` false (past
+// the workgroup's last tile) the same number of loads re-read the matrix's
+// first chunks, so that every step issues the same instructions and the
+// compiler can count the loads still in flight exactly.
+template <int PW, bool MASKED, bool NT>
+__device__ __forceinline__ void load_tile_regs(const StreamParams& p, const TileWalk& w,
+                                               bool valid, int pw,
+                                               uint4 (&v)[kBlocksPerTile / PW]) {
+  constexpr int kLoads = kBlocksPerTile / PW;
+  const int lane = lane_id();
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  int tr = 0, tc = 0;
+  if (valid) tile_coords(p, w.item, w.k, tr, tc);
+  const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc * kRowBytes +
+                     lchunk * kChunkBytes;
+  int rin = valid ? kTileRows : 0, cin = kTileCols;
+  if constexpr (MASKED) {
+    if (valid) {
+      rin = rows_in<64>(p, tr);
+      cin = cols_in<64>(p, tc);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int r = (pw * kLoads + j) * kRowsPerBlock + lrow;
+    const uint8_t* a = g + (int64_t)r * p.ld_src;
+    if (r >= rin || lchunk * 8 >= cin) a = p.src;  // in bounds; nobody uses it
+    u32x4 x;
+    if constexpr (NT)
+      x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+    else
+      x = *reinterpret_cast<const u32x4*>(a);
+    v[j] = uint4{x.x, x.y, x.z, x.w};
+  }
+}
+
+// Register buffers per producer wave: tiles in flight, D - 1 of them ahead
+// of the one being written (4 waves: 4 buffers of 16 VGPRs; 1 wave: 2 of 64).
+template <int PW>
+constexpr int regs_depth() { return PW == 1 ? 2 : 4; }
+
+// One tile: issue the loads of the tile D - 1 ahead into `ahead_regs`, then
+// write `cur` (whose loads the compiler waits for) into the acquired slot and
+// commit it. Returns false on a timeout.
+template <int S, int C, int PW, int OP, bool MASKED, bool NT>
+__device__ __forceinline__ bool regs_step(const StreamParams& p, StreamLds<S, C>& lds, int pw,
+                                          TileWalk& ahead, PipeState& st, int& t,
+                                          const uint4 (&cur)[kBlocksPerTile / PW],
+                                          uint4 (&ahead_regs)[kBlocksPerTile / PW]) {
+  using FullBar = StreamBar<OP, PW>;
+  using EmptyBar = StreamBar<OP, C>;
+  constexpr int kLoads = kBlocksPerTile / PW;
+  const bool valid = ahead.it < p.items;
+  load_tile_regs<PW, MASKED, NT>(p, ahead, valid, pw, ahead_regs);
+  if (valid) {
+    ++ahead.k;
+    walk_settle(p, ahead);
+  }
+  // producer_acquire (no commits pending: every earlier tile is committed).
+  if (!bar_wait<EmptyBar>(&lds.empty[st.index], st.phase, p.spin_limit)) return false;
+  if (pw == 0) trace_record(p, t, 0, st, 0);
+  const int lane = lane_id();
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  uint8_t* slot = &lds.slots[st.index][0];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int r = (pw * kLoads + j) * kRowsPerBlock + lrow;
+    *reinterpret_cast<uint4*>(slot + r * kRowBytes + swz(r, lchunk, p.swz_shift) * kChunkBytes) =
+        cur[j];
+  }
+  wait_lgkmcnt0();  // the tile's writes have landed: commit
+  FullBar::arrive(&lds.full[st.index]);
+  st.inc();
+  ++t;
+  return true;
+}
+
+template <int S, int C, int PW, int OP, bool MASKED, bool NT>
+__device__ void producer_regs(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
+  using EmptyBar = StreamBar<OP, C>;
+  constexpr int kLoads = kBlocksPerTile / PW;
+  constexpr int D = regs_depth<PW>();
+  PipeState st = producer_start(S, p.start_phase);
+  int tiles = 0;  // tiles of this workgroup
+  for (int it = blockIdx.x; it < p.items; it += gridDim.x) tiles += item_len(p, item_index(p, it));
+  TileWalk ahead = walk_start(p);
+  uint4 buf[D][kLoads];
+  // Prologue: the first D - 1 tiles.
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) {
+    const bool valid = ahead.it < p.items;
+    load_tile_regs<PW, MASKED, NT>(p, ahead, valid, pw, buf[i]);
+    if (valid) {
+      ++ahead.k;
+      walk_settle(p, ahead);
+    }
+  }
+  bool ok = true;
+  int t = 0;
+  // Whole rounds of D tiles: every step runs, so each buffer's loads are
+  // waited for exactly (not drained) before its writes.
+  while (ok && t + D <= tiles) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      ok = regs_step<S, C, PW, OP, MASKED, NT>(p, lds, pw, ahead, st, t, buf[i],
+                                               buf[(i + D - 1) % D]);
+      if (!ok) break;
+    }
+  }
+  // The last tiles (fewer than D), continuing the buffer rotation.
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) {
+    if (ok && t < tiles)
+      ok = regs_step<S, C, PW, OP, MASKED, NT>(p, lds, pw, ahead, st, t, buf[i],
+                                               buf[(i + D - 1) % D]);
+  }
+  // producer_tail: S more empty phases, so every slot has been drained.
+  if (ok) {
+    for (int i = 0; i < S; ++i) {
+      if (!bar_wait<EmptyBar>(&lds.empty[st.index], st.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      st.inc();
+    }
+  }
+  if (!ok && lane_id() == 0) atomicOr(p.status, kStatusTimeoutProducer);
+}
+
+template <int S, int C, int PW, int OP, bool MASKED, bool NT>
+__global__ void __launch_bounds__(64 * (PW + C)) stream_regs_kernel(StreamParams p) {
+  __shared__ StreamLds<S, C> lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  if (threadIdx.x < S) {
+    lds.full[threadIdx.x] = 0u;
+    lds.empty[threadIdx.x] = 0u;
+    lds.fin[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  if (wave < PW)
+    producer_regs<S, C, PW, OP, MASKED, NT>(p, lds, wave);
+  else
+    consumer<S, C, PW, OP, MASKED, 64>(p, lds, wave - PW);
+}
+
+// ---------------------------------------------------------------------------
 // Grouped copy consumers (128 x 64 tiles, divisible shapes): each consumer
 // wave waits on the G slots that hold one tile row of a grouped strip, stores
 // its share of those G tiles, then releases all G. One store instruction
@@ -580,6 +765,39 @@ hipError_t launch_group_stages(int consumers, int producers, int group, int grid
   return hipErrorInvalidValue;
 }
 
+template <int S, int C, int PW, int OP, bool NT>
+static hipError_t launch_regs_op(int grid, const StreamParams& p, hipStream_t stream) {
+  const bool masked = (p.M % kTileRows) != 0 || (p.N % kTileCols) != 0;
+  const dim3 block(64 * (PW + C));
+  return masked ? launch_or_record(stream_regs_kernel<S, C, PW, OP, true, NT>, dim3(grid), block,
+                                   stream, p)
+                : launch_or_record(stream_regs_kernel<S, C, PW, OP, false, NT>, dim3(grid), block,
+                                   stream, p);
+}
+
+template <int S, int C, int PW>
+static hipError_t launch_regs_scp(int op, int grid, const StreamParams& p, hipStream_t stream) {
+  if constexpr (!regs_shape_supported(S, C, PW)) {
+    return hipErrorInvalidValue;
+  } else {
+    if (op == kOpCopy)
+      return p.nt ? launch_regs_op<S, C, PW, kOpCopy, true>(grid, p, stream)
+                  : launch_regs_op<S, C, PW, kOpCopy, false>(grid, p, stream);
+    return p.nt ? launch_regs_op<S, C, PW, kOpRowsum, true>(grid, p, stream)
+                : launch_regs_op<S, C, PW, kOpRowsum, false>(grid, p, stream);
+  }
+}
+
+template <int S>
+hipError_t launch_regs_stages(int op, int consumers, int producers, int grid,
+                              const StreamParams& p, hipStream_t stream) {
+  if (consumers == 3 && producers == 1) return launch_regs_scp<S, 3, 1>(op, grid, p, stream);
+  if (consumers == 4 && producers == 1) return launch_regs_scp<S, 4, 1>(op, grid, p, stream);
+  if (consumers == 3 && producers == 4) return launch_regs_scp<S, 3, 4>(op, grid, p, stream);
+  if (consumers == 4 && producers == 4) return launch_regs_scp<S, 4, 4>(op, grid, p, stream);
+  return hipErrorInvalidValue;
+}
+
 #if !defined(PIPE_STREAM_STAGES_LO) || !defined(PIPE_STREAM_STAGES_HI)
 #error "build with -DPIPE_STREAM_STAGES_LO=<s> -DPIPE_STREAM_STAGES_HI=<s>"
 #endif
@@ -587,7 +805,9 @@ hipError_t launch_group_stages(int consumers, int producers, int group, int grid
   template hipError_t launch_stream_stages<S>(int, int, int, int, int, const StreamParams&, \
                                               hipStream_t);                                 \
   template hipError_t launch_group_stages<S>(int, int, int, int, const StreamParams&,       \
-                                             hipStream_t);
+                                             hipStream_t);                                 \
+  template hipError_t launch_regs_stages<S>(int, int, int, int, const StreamParams&,        \
+                                            hipStream_t);
 #if PIPE_STREAM_STAGES_LO <= 1 && 1 <= PIPE_STREAM_STAGES_HI
 PIPE_STREAM_INSTANTIATE(1)
 #endif

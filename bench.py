@@ -83,6 +83,11 @@ WIDE_COPY = {
 # segments per strip, the best ring measured for it.
 _G = 0x4000
 GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _RM | _IL | _LZ | _G)
+# The register producer engine (PIPE_FLAG_PRODUCER_VGPR): global_load_dwordx4
+# into registers, then ds_write_b128 into the slot.
+_V = 0x8000
+REGS_COPY = dict(stages=2, producer_waves=4, consumer_waves=4, flags=_NT | _RM | _V)
+REGS_ROWSUM = dict(stages=4, producer_waves=4, consumer_waves=4, flags=_NT | _RM | _V)
 WIDE_ROWSUM = {
     "64x128": dict(tile_m=64, tile_n=128, stages=3, producer_waves=4, consumer_waves=4, split=2,
                    flags=_NT | _RM),
@@ -620,7 +625,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "copy_grouped",
-                                       "rowsum",
+                                       "copy_regs", "rowsum", "rowsum_regs",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
                                        "gemm_bcol", "ceiling", "calib"],
                     default=None,
@@ -660,6 +665,15 @@ def main():
         cfg = dict(GROUPED_COPY)
         r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
         log(f"[bench] copy_grouped: {r}")
+        return
+    if args.only == "copy_regs":
+        cfg = dict(REGS_COPY)
+        r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+        log(f"[bench] copy_regs: {r}")
+        return
+    if args.only == "rowsum_regs":
+        r = bench_rowsum(args.steps, args.warmup, **REGS_ROWSUM)
+        log(f"[bench] rowsum_regs: {r}")
         return
     if args.only in ("rowsum_32x256", "rowsum_64x128"):
         r = bench_rowsum(args.steps, args.warmup, **WIDE_ROWSUM[args.only.split("_")[1]])
@@ -727,6 +741,12 @@ def main():
             "strip_tiles": 4,
             "kernel_pct_of_peak": round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)}
         log(f"[bench] copy, grouped strips: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
+        cfg = dict(REGS_COPY)
+        w = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+        extras["copy_register_engine"] = {
+            k: w[k] for k in ("tile", "stages", "producer_waves", "consumer_waves", "flags",
+                              "split", "grid", "kernel_ms", "gbs", "kernel_gbs", "bit_exact")}
+        log(f"[bench] copy, register engine: {w['gbs']:.1f} GB/s")
         u = bench_copy(2, max(3, args.steps // 2), args.warmup, consumer_waves=2,
                        flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
                        pt.PIPE_FLAG_XCD_REMAP)
@@ -743,6 +763,9 @@ def main():
                          pt.PIPE_FLAG_XCD_REMAP)
         log(f"[bench] unified rowsum: {r['gbs']:.1f} GB/s")
         extras["rowsum_unified"] = r
+        r = bench_rowsum(max(3, args.steps // 2), args.warmup, **REGS_ROWSUM)
+        log(f"[bench] rowsum, register engine: {r['gbs']:.1f} GB/s")
+        extras["rowsum_register_engine"] = r
         wide = {}
         for name, cfg in WIDE_ROWSUM.items():
             w = bench_rowsum(max(3, args.steps // 2), args.warmup, **cfg)

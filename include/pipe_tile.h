@@ -109,6 +109,15 @@ typedef enum {
                                           for; elsewhere the flag changes nothing. The commit
                                           lag is then at most stages - G, and split 0 means G
                                           segments per strip (one work item per tile column) */
+#define PIPE_FLAG_PRODUCER_VGPR 0x8000u /* copy/rowsum, 128 x 64 tiles: the producers load with
+                                          global_load_dwordx4 into registers and write each
+                                          slot with ds_write_b128 at the swizzled positions
+                                          (instead of direct-to-LDS loads), one tile ahead; a
+                                          tile is committed once its writes have returned.
+                                          Rings: stages 1..4, consumer_waves 3 or 4,
+                                          producer_waves 1 or 4; not with PIPE_FLAG_UNIFIED
+                                          (else PIPE_ERR_CONFIG); PIPE_FLAG_STRIP_GROUPS is
+                                          then ignored */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the
