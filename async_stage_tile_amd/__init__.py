@@ -57,9 +57,13 @@ PIPE_FLAG_GEMM_STORE_WAVE = 0x1000
 PIPE_FLAG_GEMM_B_COLMAJOR = 0x2000
 PIPE_FLAG_STRIP_GROUPS = 0x4000
 PIPE_FLAG_PRODUCER_VGPR = 0x8000
+PIPE_FLAG_DEBUG_CHECKS = 0x10000
+PIPE_FLAG_TEST_JITTER = 0x20000
+PIPE_FLAG_TEST_EARLY_RELEASE = 0x40000
 
 PIPE_STATUS_TIMEOUT_PRODUCER = 0x1
 PIPE_STATUS_TIMEOUT_CONSUMER = 0x2
+PIPE_STATUS_INVARIANT = 0x4
 
 PIPE_TRACE_WORDS = 8
 

@@ -29,7 +29,8 @@ constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_F
                                  PIPE_FLAG_LAZY_COMMIT | PIPE_FLAG_EAGER_NEWEST |
                                  PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE |
                                  PIPE_FLAG_GEMM_B_COLMAJOR | PIPE_FLAG_STRIP_GROUPS |
-                                 PIPE_FLAG_PRODUCER_VGPR |
+                                 PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS |
+                                 PIPE_FLAG_TEST_JITTER | PIPE_FLAG_TEST_EARLY_RELEASE |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
 std::mutex g_status_mu;
@@ -119,8 +120,16 @@ pipe_status_t check_stream_cfg(const pipe_config_t& c) {
     return PIPE_ERR_CONFIG;
   const int cw = c.consumer_waves, pw = c.producer_waves;
   if (c.flags & PIPE_FLAG_PRODUCER_VGPR) {
+    if ((c.flags & (PIPE_FLAG_UNIFIED | PIPE_FLAG_DEBUG_CHECKS)) || c.tile_m != 128 ||
+        c.tile_n != 64 || !regs_shape_supported(c.stages, cw, pw))
+      return PIPE_ERR_CONFIG;
+  }
+  if ((c.flags & (PIPE_FLAG_TEST_JITTER | PIPE_FLAG_TEST_EARLY_RELEASE)) &&
+      !(c.flags & PIPE_FLAG_DEBUG_CHECKS))
+    return PIPE_ERR_CONFIG;
+  if (c.flags & PIPE_FLAG_DEBUG_CHECKS) {
     if ((c.flags & PIPE_FLAG_UNIFIED) || c.tile_m != 128 || c.tile_n != 64 ||
-        !regs_shape_supported(c.stages, cw, pw))
+        !debug_shape_supported(c.stages, cw, pw))
       return PIPE_ERR_CONFIG;
   }
   if (c.flags & PIPE_FLAG_UNIFIED) {
@@ -162,7 +171,9 @@ struct StreamGeom {
 // Tile columns per strip of a copy with PIPE_FLAG_STRIP_GROUPS: 4, else 2,
 // where the grouped kernels take the launch; 1 (plain strips) elsewhere.
 int copy_strip_group(const pipe_config_t& c, int64_t M, int64_t N, bool checksums) {
-  if (!(c.flags & PIPE_FLAG_STRIP_GROUPS) || (c.flags & PIPE_FLAG_PRODUCER_VGPR)) return 1;
+  if (!(c.flags & PIPE_FLAG_STRIP_GROUPS) ||
+      (c.flags & (PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS)))
+    return 1;
   if (checksums || (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_UNIFIED))) return 1;
   if (c.tile_m != 128 || c.tile_n != 64 || M % 128 != 0 || N % 64 != 0) return 1;
   const int64_t tile_cols = N / 64;
@@ -239,6 +250,8 @@ void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_st
   p->trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
   p->nt = (c.flags & PIPE_FLAG_NONTEMPORAL) ? 1 : 0;
   p->eager = eager_min_pending(c.flags);
+  p->jitter = (c.flags & PIPE_FLAG_TEST_JITTER) ? 1 : 0;
+  p->early_release = (c.flags & PIPE_FLAG_TEST_EARLY_RELEASE) ? 1 : 0;
 }
 
 // The main kernel of a copy or row sum: the unified ring, the register
@@ -249,6 +262,9 @@ hipError_t launch_stream_op(int op, const pipe_config_t& c, const StreamGeom& g,
     return launch_unified(op, c.stages, c.consumer_waves, c.tile_n, g.grid, p, stream);
   if (c.flags & PIPE_FLAG_PRODUCER_VGPR)
     return launch_stream_regs(op, c.stages, c.consumer_waves, c.producer_waves, g.grid, p, stream);
+  if (c.flags & PIPE_FLAG_DEBUG_CHECKS)
+    return launch_stream_debug(op, c.stages, c.consumer_waves, c.producer_waves, g.grid, p,
+                               stream);
   if (g.group > 1)
     return launch_stream_group(c.stages, c.consumer_waves, c.producer_waves, g.group, g.grid, p,
                                stream);
@@ -276,7 +292,8 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
     return PIPE_ERR_CONFIG;
   if (c.split > 1) return PIPE_ERR_CONFIG;
   if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS |
-                 PIPE_FLAG_PRODUCER_VGPR))
+                 PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS | PIPE_FLAG_TEST_JITTER |
+                 PIPE_FLAG_TEST_EARLY_RELEASE))
     return PIPE_ERR_CONFIG;
   const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
   const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;

@@ -66,6 +66,7 @@ struct TileShape {
 // Status bits written to the caller's status word.
 constexpr uint32_t kStatusTimeoutProducer = 1u;
 constexpr uint32_t kStatusTimeoutConsumer = 2u;
+constexpr uint32_t kStatusInvariant = 4u;  // a protocol check of a debug kernel failed
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -130,6 +131,8 @@ __device__ __forceinline__ uint32_t bar_read(uint32_t* bar) {
 template <uint32_t E>
 struct Counter {
   static __device__ __forceinline__ uint32_t phase(uint32_t word) { return (word / E) & 1u; }
+  // The word after `phases` completed phases and no arrival of the next one.
+  static __device__ __forceinline__ uint32_t settled(uint32_t phases) { return phases * E; }
   // One arrival on behalf of the whole wave (lane 0).
   static __device__ __forceinline__ void arrive(uint32_t* bar) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -143,6 +146,9 @@ template <uint32_t E>
 struct Flip {
   static constexpr uint32_t kPhaseBit = 0x80000000u;
   static __device__ __forceinline__ uint32_t phase(uint32_t word) { return word >> 31; }
+  static __device__ __forceinline__ uint32_t settled(uint32_t phases) {
+    return (phases & 1u) << 31;
+  }
   static __device__ __forceinline__ void arrive(uint32_t* bar) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (lane_id() == 0) {
@@ -168,6 +174,22 @@ __device__ __forceinline__ bool bar_wait(uint32_t* bar, uint32_t phase, uint32_t
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return true;
+}
+
+// ---------------------------------------------------------------------------
+// Debug kernels: a wave-uniform pseudo-random pause (stress runs shift the
+// waves' relative timing with it) and the status bit of a failed check.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void jitter_pause(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t h = a * 0x9E3779B1u ^ b * 0x85EBCA77u ^ c * 0xC2B2AE3Du;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  for (uint32_t i = uniform(h & 15u); i > 0; --i) __builtin_amdgcn_s_sleep(4);
+}
+
+__device__ __forceinline__ void flag_invariant(uint32_t* status) {
+  if (lane_id() == 0) atomicOr(status, kStatusInvariant);
 }
 
 // ---------------------------------------------------------------------------

@@ -37,6 +37,8 @@ struct StreamParams {
   int32_t xcd_remap;      // permute items so each XCD streams neighbouring strips
   int32_t interleave;     // segment s takes tiles s, s + split, s + 2 split, ...
   int32_t eager;          // eager commits while the acquire waits: min tiles in flight (0 = off)
+  int32_t jitter;         // debug kernels: pseudo-random pauses before every wait
+  int32_t early_release;  // debug kernels, test: consumers release before reading
 };
 
 // Ring shapes (stages S, consumer waves C, producer waves PW, tile columns TC)
@@ -65,6 +67,12 @@ constexpr bool regs_shape_supported(int S, int C, int PW) {
   return S >= 1 && S <= 4 && (C == 3 || C == 4) && (PW == 1 || PW == 4);
 }
 
+// Debug kernels (protocol checks at run time; 128 x 64 tiles): S = 1..4 with
+// 1 producer + 3 consumer waves or 4 + 4.
+constexpr bool debug_shape_supported(int S, int C, int PW) {
+  return S >= 1 && S <= 4 && ((C == 3 && PW == 1) || (C == 4 && PW == 4));
+}
+
 // Largest commit lag for PW producer waves: each wave issues 16 / PW loads per
 // tile and (lag + 1) tiles of them must fit the 63-entry vmcnt counter.
 constexpr int stream_max_lag(int PW) { return 63 / (16 / PW) - 1; }
@@ -87,6 +95,14 @@ hipError_t launch_stream_group(int stages, int consumers, int producers, int gro
                                const StreamParams& p, hipStream_t stream);
 template <int S>
 hipError_t launch_group_stages(int consumers, int producers, int group, int grid,
+                               const StreamParams& p, hipStream_t stream);
+
+// Debug kernel: the DMA ring with its protocol checks (and optional jitter);
+// hipErrorInvalidValue for a shape debug_shape_supported rejects.
+hipError_t launch_stream_debug(int op, int stages, int consumers, int producers, int grid,
+                               const StreamParams& p, hipStream_t stream);
+template <int S>
+hipError_t launch_debug_stages(int op, int consumers, int producers, int grid,
                                const StreamParams& p, hipStream_t stream);
 
 // Register producer engine: launch the stream kernel whose producers load

@@ -149,7 +149,7 @@ __device__ __forceinline__ int cols_in(const StreamParams& p, int tc) {
 template <int OP, uint32_t E>
 using StreamBar = typename std::conditional<OP == kOpCopy, Flip<E>, Counter<E>>::type;
 
-template <int S, int C, int PW, int OP, bool MASKED, int TC, int G = 1>
+template <int S, int C, int PW, int OP, bool MASKED, int TC, int G = 1, bool DBG = false>
 __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
   using Sh = TileShape<TC>;
   using FullBar = StreamBar<OP, PW>;
@@ -170,6 +170,9 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
     const int item = item_index(p, it);
     const int len = G == 1 ? item_len(p, item) : group_item_len<G>(p, item);
     for (int k = 0; k < len; ++k, ++t) {
+      if constexpr (DBG) {
+        if (p.jitter) jitter_pause(blockIdx.x, pw, t);
+      }
       // producer_acquire: wait until consumers released this slot (committing
       // landed tiles meanwhile, unless commits are lazy).
       if (!acquire_slot<kLoads, S, EmptyBar, FullBar>(&lds.empty[w.index], w.phase, lds.full,
@@ -177,6 +180,14 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
                                                       p.spin_limit)) {
         ok = false;
         break;
+      }
+      if constexpr (DBG) {
+        // The slot's consumers have released its previous uses and no other:
+        // its next use is not committed yet. The cursor is the closed form.
+        const uint32_t uses = (uint32_t)(t / S);
+        if (uniform(bar_read(&lds.empty[w.index])) != EmptyBar::settled(uses) ||
+            w.index != t % S || w.phase != (p.start_phase ^ (uses & 1u)))
+          flag_invariant(p.status);
       }
       if (pw == 0) trace_record(p, t, 0, w, 0);
       int tr, tc;
@@ -252,7 +263,7 @@ __device__ void producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
 // ---------------------------------------------------------------------------
 // Consumer waves
 // ---------------------------------------------------------------------------
-template <int S, int C, int PW, int OP, bool MASKED, int TC>
+template <int S, int C, int PW, int OP, bool MASKED, int TC, bool DBG = false>
 __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
   using Sh = TileShape<TC>;
   using FullBar = StreamBar<OP, PW>;
@@ -273,10 +284,29 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
     const int len = item_len(p, item);
     int tr = 0, tc = 0;
     for (int k = 0; k < len; ++k, ++t) {
+      if constexpr (DBG) {
+        if (p.jitter) jitter_pause(blockIdx.x, PW + cw, t);
+      }
       // consumer_wait: the slot's full phase must have completed.
       if (!bar_wait<FullBar>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
         ok = false;
         break;
+      }
+      uint32_t full_seen = 0;
+      if constexpr (DBG) {
+        // Exactly this use of the slot is committed: the next one needs this
+        // wave's release first. The cursor is the closed form.
+        const uint32_t uses = (uint32_t)(t / S);
+        full_seen = uniform(bar_read(&lds.full[rd.index]));
+        if (full_seen != FullBar::settled(uses + 1) || rd.index != t % S ||
+            rd.phase != (uses & 1u))
+          flag_invariant(p.status);
+        if (p.early_release) {
+          // Test only: release before reading (the mistake that lets the
+          // producer overwrite live data), then give it time to do so.
+          EmptyBar::arrive(&lds.empty[rd.index]);
+          for (int i = 0; i < 64; ++i) __builtin_amdgcn_s_sleep(8);
+        }
       }
       if (cw == 0) trace_record(p, t, 1, rd, 1 + cw);
       tile_coords(p, item, k, tr, tc);
@@ -363,8 +393,13 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
         }
         wait_lgkmcnt0();
       }
+      if constexpr (DBG) {
+        // Still the same use: nothing was committed into the slot while this
+        // wave read it.
+        if (uniform(bar_read(&lds.full[rd.index])) != full_seen) flag_invariant(p.status);
+      }
       // consumer_release.
-      if (!p.no_release) EmptyBar::arrive(&lds.empty[rd.index]);
+      if (!p.no_release && !(DBG && p.early_release)) EmptyBar::arrive(&lds.empty[rd.index]);
       rd.inc();
     }
     if constexpr (OP == kOpRowsum) {
@@ -401,6 +436,27 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_kernel(StreamParams p) {
     producer<S, C, PW, OP, MASKED, TC>(p, lds, wave);
   else
     consumer<S, C, PW, OP, MASKED, TC>(p, lds, wave - PW);
+}
+
+// ---------------------------------------------------------------------------
+// Debug kernel (PIPE_FLAG_DEBUG_CHECKS): the DMA ring of stream_kernel with
+// its protocol checks compiled in. A failed check sets kStatusInvariant in the
+// status word and the kernel carries on (every wait stays bounded).
+// ---------------------------------------------------------------------------
+template <int S, int C, int PW, int OP, bool MASKED>
+__global__ void __launch_bounds__(64 * (PW + C)) stream_debug_kernel(StreamParams p) {
+  __shared__ StreamLds<S, C> lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  if (threadIdx.x < S) {
+    lds.full[threadIdx.x] = 0u;
+    lds.empty[threadIdx.x] = 0u;
+    lds.fin[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  if (wave < PW)
+    producer<S, C, PW, OP, MASKED, 64, 1, true>(p, lds, wave);
+  else
+    consumer<S, C, PW, OP, MASKED, 64, true>(p, lds, wave - PW);
 }
 
 // ---------------------------------------------------------------------------
@@ -765,6 +821,33 @@ hipError_t launch_group_stages(int consumers, int producers, int group, int grid
   return hipErrorInvalidValue;
 }
 
+template <int S, int C, int PW>
+static hipError_t launch_debug_scp(int op, int grid, const StreamParams& p, hipStream_t stream) {
+  if constexpr (!debug_shape_supported(S, C, PW)) {
+    return hipErrorInvalidValue;
+  } else {
+    const bool masked = (p.M % kTileRows) != 0 || (p.N % kTileCols) != 0;
+    const dim3 block(64 * (PW + C));
+    if (op == kOpCopy)
+      return masked ? launch_or_record(stream_debug_kernel<S, C, PW, kOpCopy, true>, dim3(grid),
+                                       block, stream, p)
+                    : launch_or_record(stream_debug_kernel<S, C, PW, kOpCopy, false>, dim3(grid),
+                                       block, stream, p);
+    return masked ? launch_or_record(stream_debug_kernel<S, C, PW, kOpRowsum, true>, dim3(grid),
+                                     block, stream, p)
+                  : launch_or_record(stream_debug_kernel<S, C, PW, kOpRowsum, false>, dim3(grid),
+                                     block, stream, p);
+  }
+}
+
+template <int S>
+hipError_t launch_debug_stages(int op, int consumers, int producers, int grid,
+                               const StreamParams& p, hipStream_t stream) {
+  if (consumers == 3 && producers == 1) return launch_debug_scp<S, 3, 1>(op, grid, p, stream);
+  if (consumers == 4 && producers == 4) return launch_debug_scp<S, 4, 4>(op, grid, p, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int S, int C, int PW, int OP, bool NT>
 static hipError_t launch_regs_op(int grid, const StreamParams& p, hipStream_t stream) {
   const bool masked = (p.M % kTileRows) != 0 || (p.N % kTileCols) != 0;
@@ -807,7 +890,9 @@ hipError_t launch_regs_stages(int op, int consumers, int producers, int grid,
   template hipError_t launch_group_stages<S>(int, int, int, int, const StreamParams&,       \
                                              hipStream_t);                                 \
   template hipError_t launch_regs_stages<S>(int, int, int, int, const StreamParams&,        \
-                                            hipStream_t);
+                                            hipStream_t);                                  \
+  template hipError_t launch_debug_stages<S>(int, int, int, int, const StreamParams&,       \
+                                             hipStream_t);
 #if PIPE_STREAM_STAGES_LO <= 1 && 1 <= PIPE_STREAM_STAGES_HI
 PIPE_STREAM_INSTANTIATE(1)
 #endif

@@ -53,6 +53,17 @@ hipError_t launch_stream_regs(int op, int stages, int consumers, int producers, 
   }
 }
 
+hipError_t launch_stream_debug(int op, int stages, int consumers, int producers, int grid,
+                               const StreamParams& p, hipStream_t stream) {
+  switch (stages) {
+    case 1: return launch_debug_stages<1>(op, consumers, producers, grid, p, stream);
+    case 2: return launch_debug_stages<2>(op, consumers, producers, grid, p, stream);
+    case 3: return launch_debug_stages<3>(op, consumers, producers, grid, p, stream);
+    case 4: return launch_debug_stages<4>(op, consumers, producers, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 int stream_lds_bytes(int stages, int consumers) {
   return stages * kTileBytes + stages * 4 * (3 + consumers);
 }

@@ -118,6 +118,23 @@ typedef enum {
                                           producer_waves 1 or 4; not with PIPE_FLAG_UNIFIED
                                           (else PIPE_ERR_CONFIG); PIPE_FLAG_STRIP_GROUPS is
                                           then ignored */
+#define PIPE_FLAG_DEBUG_CHECKS 0x10000u /* copy/rowsum, 128 x 64 tiles: run the ring with its
+                                          protocol checks compiled in. When a wait passes, the
+                                          barrier word must hold exactly the completed phases
+                                          the protocol allows and the cursor its closed form;
+                                          a consumer's slot must not be committed again before
+                                          it releases it. A failed check sets
+                                          PIPE_STATUS_INVARIANT; the kernel carries on. Rings:
+                                          stages 1..4 with 1 producer + 3 consumer waves or
+                                          4 + 4; not with UNIFIED or PRODUCER_VGPR (else
+                                          PIPE_ERR_CONFIG); STRIP_GROUPS is then ignored */
+#define PIPE_FLAG_TEST_JITTER 0x20000u  /* test only, with DEBUG_CHECKS (else PIPE_ERR_CONFIG):
+                                          every wave pauses a pseudo-random 0..15 short sleeps
+                                          before each wait, to shake the waves' timing */
+#define PIPE_FLAG_TEST_EARLY_RELEASE 0x40000u /* test only, with DEBUG_CHECKS (else
+                                          PIPE_ERR_CONFIG): consumers release each slot before
+                                          reading it and then pause, so the producer refills
+                                          it under them; the checks must report it */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the
@@ -126,6 +143,7 @@ typedef enum {
 /* Status-word bits (cfg->status or pipe_device_status). */
 #define PIPE_STATUS_TIMEOUT_PRODUCER 0x1u
 #define PIPE_STATUS_TIMEOUT_CONSUMER 0x2u
+#define PIPE_STATUS_INVARIANT 0x4u        /* a check of PIPE_FLAG_DEBUG_CHECKS failed */
 
 /* One trace record: 8 uint32 words. Written only by workgroup 0, for the first
  * cfg->trace_capacity / 2 tiles of its stream, at record index 2*t + event.

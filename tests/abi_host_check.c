@@ -160,7 +160,7 @@ int main(void) {
       q.tile_m = tms[sh];
       q.tile_n = tns[sh];
     }
-    q.flags = rnd(2) ? q.flags : (uint32_t)rnd(0x10000);
+    q.flags = rnd(2) ? q.flags : (uint32_t)rnd(0x100000);
     q.trace = NULL;
     q.status = NULL;
     const int64_t M = dims[rnd(13)], N = dims[rnd(13)] & ~(int64_t)7, K = dims[rnd(13)];

@@ -76,7 +76,7 @@ def test_copy_validation():
     assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, tile_n=32)) == pt.PIPE_ERR_CONFIG
     assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, swizzle_shift=4)) \
         == pt.PIPE_ERR_CONFIG
-    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=0x10000)) \
+    assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=0x80000)) \
         == pt.PIPE_ERR_CONFIG
     assert _copy(FAKE, FAKE, 256, 128, 128, 128, pt.make_config(0, flags=pt.PIPE_FLAG_TRACE)) \
         == pt.PIPE_ERR_NULL
@@ -351,7 +351,7 @@ def test_gemm_query_rejects_what_the_entry_point_rejects():
     for _ in range(3000):
         c = pt.make_config(pt.PIPE_OP_GEMM, stages=rng.randrange(0, 7),
                            producer_waves=rng.randrange(0, 6), consumer_waves=rng.randrange(0, 6),
-                           split=rng.randrange(0, 3), flags=rng.randrange(0, 0x20000) & ~0x1,
+                           split=rng.randrange(0, 3), flags=rng.randrange(0, 0x100000) & ~0x1,
                            tile_m=rng.choice([64, 128]), tile_n=rng.choice([64, 128]))
         entry = L.pipe_gemm_mainloop(None, None, None, 0, 0, 0, 0, 0, 0, ctypes.byref(c), None)
         query = L.pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 128, 128, 64,
@@ -460,3 +460,30 @@ def test_register_producer_engine_configs():
     q = lambda **kw: pt.pipe_query_kernel(pt.PIPE_OP_COPY, 1024, 1024, stages=4, **kw)
     assert q(flags=V | pt.PIPE_FLAG_STRIP_GROUPS) == q(flags=V) == q(flags=0)
     assert q(flags=pt.PIPE_FLAG_STRIP_GROUPS) != q(flags=0)
+
+
+def test_debug_check_configs():
+    """DEBUG_CHECKS: 128 x 64 tiles, S 1..4 with 1 + 3 or 4 + 4 waves; JITTER and
+    EARLY_RELEASE only with it; not with UNIFIED or PRODUCER_VGPR; not for the GEMM."""
+    Dg, J, E = pt.PIPE_FLAG_DEBUG_CHECKS, pt.PIPE_FLAG_TEST_JITTER, pt.PIPE_FLAG_TEST_EARLY_RELEASE
+    info = pt.pipe_kernel_info_t()
+
+    def status(op, **kw):
+        c = pt.make_config(op, **kw)
+        return pt.lib().pipe_query_kernel(op, ctypes.byref(c), 1024, 1024, 0, ctypes.byref(info))
+
+    for op in (pt.PIPE_OP_COPY, pt.PIPE_OP_ROWSUM):
+        for S in (1, 2, 3, 4):
+            for C, PW in ((3, 1), (4, 4)):
+                for extra in (0, J, E, J | E):
+                    assert status(op, stages=S, consumer_waves=C, producer_waves=PW,
+                                  flags=Dg | extra) == pt.PIPE_OK
+        for kw in (dict(stages=5), dict(consumer_waves=4, producer_waves=1),
+                   dict(consumer_waves=8), dict(tile_m=32, tile_n=256),
+                   dict(flags=Dg | pt.PIPE_FLAG_UNIFIED),
+                   dict(flags=Dg | pt.PIPE_FLAG_PRODUCER_VGPR), dict(flags=J), dict(flags=E)):
+            kw.setdefault("flags", Dg)
+            assert status(op, **kw) == pt.PIPE_ERR_CONFIG, (op, kw)
+    assert status(pt.PIPE_OP_GEMM, flags=Dg) == pt.PIPE_ERR_CONFIG
+    q = lambda **kw: pt.pipe_query_kernel(pt.PIPE_OP_COPY, 1024, 1024, stages=4, **kw)
+    assert q(flags=Dg | pt.PIPE_FLAG_STRIP_GROUPS) == q(flags=Dg) == q(flags=0)
