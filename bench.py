@@ -270,6 +270,24 @@ def settle(seconds):
     log(f"[bench] settle: {n} untimed copies in {time.perf_counter() - t0:.2f} s")
 
 
+def kernel_resources(op, M, N, K, launch_grid, launch_threads, **cfg):
+    """Compiled resources of the main kernel an op launches (HIP runtime
+    attributes) and how many of its workgroups and waves one CU holds at once:
+    the least of what the grid gives each of the 256 CUs, what 160 KiB of LDS
+    holds, and what 512 VGPRs per SIMD lane allow (4 SIMDs per CU, at most 8
+    waves each)."""
+    import async_stage_tile_amd as pt
+    res = pt.pipe_kernel_resources(op, M, N, K, **cfg)
+    waves_per_wg = launch_threads // 64
+    per_simd = min(8, 512 // max(1, res["vgprs"]))
+    resident = min(-(-launch_grid // 256), 163840 // max(1, res["lds_bytes"]),
+                   (4 * per_simd) // waves_per_wg)
+    res["threads"] = launch_threads
+    res["resident_workgroups_per_cu"] = resident
+    res["resident_waves_per_cu"] = resident * waves_per_wg
+    return res
+
+
 def bench_copy(stages, steps, warmup, stats=False, **cfg):
     """The library's default copy configuration, with `stages` and any overrides."""
     import torch
@@ -292,6 +310,8 @@ def bench_copy(stages, steps, warmup, stats=False, **cfg):
             "grid": q["grid"], "lds_bytes": q["lds_bytes"], "wall_ms": wall, "kernel_ms": kern,
             "bytes": nbytes, "gbs": nbytes / (wall * 1e-3) / 1e9,
             "kernel_gbs": nbytes / (kern * 1e-3) / 1e9, "bit_exact": ok,
+            "resources": kernel_resources(pt.PIPE_OP_COPY, COPY_M, COPY_N, 0, q["grid"],
+                                          q["threads"], **kw),
             **({"per_launch": timing} if timing else {})}
 
 
@@ -323,7 +343,9 @@ def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
     r = {"tile": f"{c.tile_m}x{c.tile_n}", "stages": c.stages, "producer_waves": c.producer_waves,
          "consumer_waves": c.consumer_waves, "flags": c.flags, "split": q["split"],
          "grid": q["grid"], "wall_ms": wall, "kernel_ms": kern, "bytes": nbytes,
-         "gbs": nbytes / (wall * 1e-3) / 1e9, "kernel_gbs": nbytes / (kern * 1e-3) / 1e9}
+         "gbs": nbytes / (wall * 1e-3) / 1e9, "kernel_gbs": nbytes / (kern * 1e-3) / 1e9,
+         "resources": kernel_resources(pt.PIPE_OP_ROWSUM, ROWSUM_M, ROWSUM_N, 0, q["grid"],
+                                       q["threads"], **kw)}
     if timing:
         r["per_launch"] = timing
     return r
@@ -355,6 +377,9 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colma
     med, mn = launch_stats(fn, max(steps, 20), 0)
     flops = 2.0 * n * n * n
     c = pt._gemm_config(C, kw, b_colmajor)
+    gcfg = {f: getattr(c, f) for f in ("stages", "producer_waves", "flags", "swizzle_shift",
+                                       "grid")}
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, n, n, n, **gcfg)
     return {"c_dtype": str(C.dtype).replace("torch.", ""),
             "b_layout": "column-major" if b_colmajor else "row-major", "stages": c.stages,
             "producer_waves": c.producer_waves, "flags": c.flags,
@@ -362,7 +387,9 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colma
             "tflops": flops / (wall * 1e-3) / 1e12,
             "mfma_frac": flops / (wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "per_launch": {"median_ms": med, "min_ms": mn,
-                           "median_tflops": flops / (med * 1e-3) / 1e12}}
+                           "median_tflops": flops / (med * 1e-3) / 1e12},
+            "resources": kernel_resources(pt.PIPE_OP_GEMM, n, n, n, q["grid"], q["threads"],
+                                          **gcfg)}
 
 
 def bench_small(reps, warmup):
@@ -842,6 +869,7 @@ def main():
                    "split": head["split"], "grid": head["grid"], "parallelism": "1 GPU"},
         "pct_of_peak": round(100.0 * head["gbs"] / PEAK_HBM_GBS, 2),
         "bit_exact": head["bit_exact"],
+        "resources": head["resources"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": kname},
