@@ -12,8 +12,8 @@
 // Work decomposition: tiles are 16 KiB, 128 rows x 64 fp16 (the pages' tile)
 // or the wider 64 x 128 and 32 x 256 (TileShape<TC>, TC = tile columns). A
 // strip is one tile column walked downwards (copy default) or one tile row
-// walked along the columns (rowsum, or copy with PIPE_FLAG_ROW_STRIPS). Each strip is cut into
-// `split` segments; item i is segment i / n_strips of strip i % n_strips, so
+// walked along the columns (rowsum, or copy with PIPE_FLAG_ROW_STRIPS). Each
+// strip is cut into `split` segments; item i is segment i / n_strips of strip i % n_strips, so
 // workgroups launched together touch neighbouring strips. A segment is either
 // a contiguous run of the strip's tiles, or (interleaved) every split-th tile
 // starting at the segment index, so that the workgroups sharing a strip read
@@ -40,7 +40,15 @@
 // arrivals. A wave may keep `lag` committed-later tiles in flight as long as
 // (lag + 1) * 16/PW loads fit the 63-entry vmcnt counter: lag <= 2, 6, 14.
 //
-// The kernel is compiled once per stage count: this file is built several
+// Kernel families in this file, all on this ring and slot layout:
+//   stream_kernel        the ring above (every default copy and row sum);
+//   stream_group_kernel  copies down strips of G neighbouring tile columns,
+//                        whose consumers store a tile row of G tiles at once;
+//   stream_regs_kernel   producers that load into registers and write the
+//                        slots with ds_write_b128 instead of direct-to-LDS;
+//   stream_debug_kernel  the ring with its protocol checks compiled in.
+//
+// The kernels are compiled once per stage count: this file is built several
 // times, each object instantiating the stage counts PIPE_STREAM_STAGES_LO ..
 // PIPE_STREAM_STAGES_HI (so the instantiations compile in parallel).
 #include <type_traits>
