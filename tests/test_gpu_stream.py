@@ -524,8 +524,17 @@ def test_unified_copy_full_size_bit_exact():
     (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(tile_m=32, tile_n=256, consumer_waves=8)),
     (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(stages=3, consumer_waves=4,
                                             flags=pt.PIPE_FLAG_UNIFIED)),
+    (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(stages=5, producer_waves=2,
+                                            flags=pt.PIPE_FLAG_STRIP_GROUPS)),
+    (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(flags=pt.PIPE_FLAG_PRODUCER_VGPR)),
+    (pt.PIPE_OP_COPY, 1000, 1000, 0, dict(stages=3, producer_waves=1, consumer_waves=3,
+                                          flags=pt.PIPE_FLAG_PRODUCER_VGPR)),
+    (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(flags=pt.PIPE_FLAG_DEBUG_CHECKS)),
     (pt.PIPE_OP_ROWSUM, 8192, 65536, 0, {}),
     (pt.PIPE_OP_ROWSUM, 8192, 65536, 0, dict(stages=8, consumer_waves=8)),
+    (pt.PIPE_OP_ROWSUM, 8192, 65536, 0, dict(stages=4, flags=pt.PIPE_FLAG_PRODUCER_VGPR)),
+    (pt.PIPE_OP_ROWSUM, 1000, 3000, 0, dict(stages=2, producer_waves=1, consumer_waves=3,
+                                            flags=pt.PIPE_FLAG_DEBUG_CHECKS)),
     (pt.PIPE_OP_GEMM, 4096, 4096, 4096, {}),
     (pt.PIPE_OP_GEMM, 4096, 4096, 4096, dict(flags=pt.PIPE_FLAG_GEMM_C_BF16 |
                                              pt.PIPE_FLAG_EAGER_NEWEST)),
@@ -542,8 +551,8 @@ def test_kernel_resources_agree_with_the_launch_geometry(op, M, N, K, cfg):
     assert res["lds_bytes"] == q["lds_bytes"], (res, q)
     assert 0 < res["vgprs"] <= 512
     assert res["max_threads"] >= q["threads"]
-    if not cfg:
-        assert res["scratch_bytes"] == 0
+    if not cfg or cfg.get("flags", 0) & (pt.PIPE_FLAG_STRIP_GROUPS | pt.PIPE_FLAG_PRODUCER_VGPR):
+        assert res["scratch_bytes"] == 0   # defaults and the grouped / register kernels: no spills
 
 
 def test_kernel_lookup_on_one_thread_never_swallows_a_launch_on_another():
