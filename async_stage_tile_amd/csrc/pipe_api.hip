@@ -434,6 +434,7 @@ pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_confi
   const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
+  if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // as pipe_rowsum
   if (M < 0 || N < 0 || N % 8 != 0) return PIPE_ERR_SHAPE;
   *bytes = 0;
   if (M == 0 || N == 0) return PIPE_OK;

@@ -372,6 +372,10 @@ def test_stream_query_rejects_what_the_entry_points_reject():
 
     U = pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL
     assert status(pt.PIPE_OP_ROWSUM, 256, 128, flags=pt.PIPE_FLAG_ROW_STRIPS) == pt.PIPE_ERR_CONFIG
+    nbytes = ctypes.c_size_t(0)
+    rs = pt.make_config(pt.PIPE_OP_ROWSUM, flags=pt.PIPE_FLAG_ROW_STRIPS)
+    assert pt.lib().pipe_rowsum_workspace_bytes(256, 128, ctypes.byref(rs), ctypes.byref(nbytes)) \
+        == pt.PIPE_ERR_CONFIG
     assert status(pt.PIPE_OP_COPY, 256, 128, stages=2, consumer_waves=1, flags=U) == \
         pt.PIPE_ERR_CONFIG                                   # unified needs 2, 4 or 8 waves
     assert status(pt.PIPE_OP_COPY, 250, 128, stages=2, consumer_waves=4, flags=U) == \
