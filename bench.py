@@ -270,6 +270,32 @@ def settle(seconds):
     log(f"[bench] settle: {n} untimed copies in {time.perf_counter() - t0:.2f} s")
 
 
+def device_memory_peak():
+    """The HBM peak the device reports, as a cross-check of the 8 TB/s used for
+    the roofline: memory bus width and memory clock from hipDeviceGetAttribute
+    (attributes 59 and 60 of hipDeviceAttribute_t in ROCm 7's
+    hip_runtime_api.h), and the GB/s they give at 2 and at 4 transfers per
+    clock (which of the two the reported clock implies depends on the memory
+    type)."""
+    import ctypes
+
+    import torch
+
+    import async_stage_tile_amd as pt
+    # dlsym on the library's handle also searches its dependencies: this is the
+    # HIP runtime the library itself runs on (no second runtime is loaded).
+    hip = pt.lib()
+    dev = torch.cuda.current_device()
+    width, clock = ctypes.c_int(0), ctypes.c_int(0)
+    if (hip.hipDeviceGetAttribute(ctypes.byref(width), 59, dev) != 0 or
+            hip.hipDeviceGetAttribute(ctypes.byref(clock), 60, dev) != 0):
+        return None
+    per_clock = width.value / 8 * clock.value * 1e3 / 1e9   # GB/s at one transfer per clock
+    return {"bus_width_bits": width.value, "memory_clock_khz": clock.value,
+            "gbs_at_2_per_clock": round(2 * per_clock, 1),
+            "gbs_at_4_per_clock": round(4 * per_clock, 1)}
+
+
 def kernel_resources(op, M, N, K, launch_grid, launch_threads, **cfg):
     """Compiled resources of the main kernel an op launches (HIP runtime
     attributes) and how many of its workgroups and waves one CU holds at once:
@@ -836,6 +862,8 @@ def main():
         c["copy_frac_of_strip128_copy"] = head["kernel_gbs"] / s128["copy_gbs"]
         c["copy_frac_of_strip128_serial_rw"] = head["kernel_gbs"] / s128["serial_rw_gbs"]
         extras["context_ceilings"] = c
+        extras["device_memory"] = device_memory_peak()
+        log(f"[bench] device memory: {extras['device_memory']}")
     cpu = None
     if not args.no_cpu:
         log("[bench] cpu baseline ...")
