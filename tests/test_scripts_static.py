@@ -62,3 +62,35 @@ def test_kernel_hash_ignores_comments_and_layout_only():
     assert bench.strip_comments(src) == 'int a = 1; asm("s_nop 0\\n\\tx // kept"); char c = \'"\';'
     assert bench.strip_comments(src) == bench.strip_comments(src.replace("note", "other note"))
     assert bench.strip_comments(src) != bench.strip_comments(src.replace("a = 1", "a = 2"))
+
+
+def _imports(path):
+    """(module names, enclosing top-level function or None) of every import in a file."""
+    import ast
+    tree = ast.parse(open(path).read())
+    out = []
+    for top in tree.body:
+        owner = top.name if isinstance(top, (ast.FunctionDef, ast.AsyncFunctionDef)) else None
+        for node in ast.walk(top):
+            if isinstance(node, ast.Import):
+                out += [(a.name, owner) for a in node.names]
+            elif isinstance(node, ast.ImportFrom) and node.module:
+                out.append((node.module, owner))
+    return out
+
+
+def test_oracle_and_hip_path_stay_apart():
+    """The product package never imports the oracle, the oracle never imports
+    the product (or the HIP library), and bench.py uses the oracle only in its
+    CPU-baseline functions."""
+    import glob
+    pkg = glob.glob(os.path.join(ROOT, "async_stage_tile_amd", "**", "*.py"), recursive=True)
+    assert pkg
+    for f in pkg:
+        assert not [m for m, _ in _imports(f) if m.split(".")[0] == "oracle"], f
+    for f in glob.glob(os.path.join(ROOT, "oracle", "*.py")):
+        bad = [m for m, _ in _imports(f) if m.split(".")[0] in ("async_stage_tile_amd", "torch")]
+        assert not bad, (f, bad)
+        assert "libpipetile" not in open(f).read(), f
+    owners = {o for m, o in _imports(os.path.join(ROOT, "bench.py")) if m.split(".")[0] == "oracle"}
+    assert owners <= {"cpu_baseline", "cpu_oracle_extras"}, owners
