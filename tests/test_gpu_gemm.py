@@ -282,3 +282,51 @@ def test_gemm_b_colmajor_rejections():
     B_overlap = over.as_strided((128, 128), (1, 64))  # columns 64 apart: rows of B^T overlap
     with pytest.raises(ValueError):
         pt.pipe_gemm_mainloop(A, B_overlap)
+
+
+@pytest.mark.parametrize("M,N,K,grid", [
+    (128, 128, 64, 0),       # one tile, one K step
+    (128, 128, 64, 1),
+    (2048, 128, 256, 3),     # tall: 16 tiles on 3 persistent workgroups
+    (128, 2048, 256, 0),     # wide
+    (384, 640, 192, 1),      # 15 tiles on one workgroup, 3 K steps
+    (256, 256, 16384, 0),    # long K: 256 stages through the ring
+])
+@pytest.mark.parametrize("c_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_shapes_and_grids_bit_exact(M, N, K, grid, c_dtype):
+    """Small-integer data: every fp32 partial sum is an integer below 2**24
+    (|C| <= 4 K <= 65536), so C is exact in any order and must equal the oracle
+    bit for bit (its bf16 rounding too)."""
+    A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=51, stream=0).to(DEV)
+    B = synth.small_int((K, N), -2, 2, torch.bfloat16, seed=51, stream=1).to(DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, grid=grid, status=st, out_dtype=c_dtype)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = R.gemm_f64(_f32(A), _f32(B))
+    if c_dtype == torch.bfloat16:
+        assert np.array_equal(C.float().cpu().numpy(), R.gemm_bf16(_f32(A), _f32(B)))
+    else:
+        assert np.array_equal(C.cpu().numpy(), ref)
+
+
+def test_gemm_long_k_uniform_within_tolerance():
+    """256 x 256 x 16384 uniform[-1, 1): fp32 accumulation over 16384 products
+    stays within 1e-2 of the fp64 product (relative to max(|ref|, rms(ref)))."""
+    A = synth.uniform((256, 16384), torch.bfloat16, seed=52, stream=0).to(DEV)
+    B = synth.uniform((16384, 256), torch.bfloat16, seed=52, stream=1).to(DEV)
+    C = pt.pipe_gemm_mainloop(A, B)
+    torch.cuda.synchronize()
+    res = R.within_tol(C.cpu().numpy(), R.gemm_f64(_f32(A), _f32(B)), 1e-2)
+    assert res["ok"], res
+
+
+def test_gemm_strided_row_major_operands():
+    """A and B as views into wider buffers (lda = K + 64, ldb = N + 128)."""
+    M, N, K = 256, 384, 320
+    Abig = synth.small_int((M, K + 64), -2, 2, torch.bfloat16, seed=53, stream=0).to(DEV)
+    Bbig = synth.small_int((K, N + 128), -2, 2, torch.bfloat16, seed=53, stream=1).to(DEV)
+    A, B = Abig[:, 32:32 + K], Bbig[:, 64:64 + N]
+    C = pt.pipe_gemm_mainloop(A, B)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), R.gemm_f64(_f32(A.contiguous()), _f32(B.contiguous())))
