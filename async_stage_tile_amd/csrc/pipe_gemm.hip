@@ -516,11 +516,19 @@ __global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0))
   gemm_body<S, PW, EPI, false>(p);
 }
 
-// At most 128 VGPRs (4 waves per SIMD), so that two 8-wave workgroups share a
-// CU as with row-major B (the store-wave variant runs one per CU anyway).
+// Waves per SIMD the column-major kernel is compiled for (its VGPR budget):
+// two workgroups share a CU, as with row-major B, where two rings fit the LDS
+// (S <= 2; 4 waves per SIMD with 4 producer waves, i.e. at most 128 VGPRs),
+// else one. The store-wave variant runs one per CU anyway.
+constexpr int bcol_waves_per_simd(int S, int PW, int EPI) {
+  if (EPI == kEpiStoreWave) return 1;
+  const int workgroups = S <= 2 ? 2 : 1;
+  return (workgroups * (PW + 4) + 3) / 4;
+}
+
 template <int S, int PW, int EPI>
 __global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)),
-                                  EPI == kEpiStoreWave ? 1 : 4)
+                                  bcol_waves_per_simd(S, PW, EPI))
     gemm_kernel_bcol(GemmParams p) {
   gemm_body<S, PW, EPI, true>(p);
 }
