@@ -112,12 +112,13 @@ typedef enum {
 #define PIPE_FLAG_PRODUCER_VGPR 0x8000u /* copy/rowsum, 128 x 64 tiles: the producers load with
                                           global_load_dwordx4 into registers and write each
                                           slot with ds_write_b128 at the swizzled positions
-                                          (instead of direct-to-LDS loads), one tile ahead; a
-                                          tile is committed once its writes have returned.
-                                          Rings: stages 1..4, consumer_waves 3 or 4,
-                                          producer_waves 1 or 4; not with PIPE_FLAG_UNIFIED
-                                          (else PIPE_ERR_CONFIG); PIPE_FLAG_STRIP_GROUPS is
-                                          then ignored */
+                                          (instead of direct-to-LDS loads), loading up to 3
+                                          tiles ahead (1 with one producer wave); a tile is
+                                          committed once its writes have returned, so the
+                                          commit policies do not apply. Rings: stages 1..4,
+                                          consumer_waves 3 or 4, producer_waves 1 or 4; not
+                                          with UNIFIED or DEBUG_CHECKS (else PIPE_ERR_CONFIG);
+                                          STRIP_GROUPS is then ignored */
 #define PIPE_FLAG_DEBUG_CHECKS 0x10000u /* copy/rowsum, 128 x 64 tiles: run the ring with its
                                           protocol checks compiled in. When a wait passes, the
                                           barrier word must hold exactly the completed phases
