@@ -300,6 +300,9 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
   if (store_wave && !c_bf16) return PIPE_ERR_CONFIG;
   if ((c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) && (c.flags & PIPE_FLAG_GEMM_B_LINEAR))
     return PIPE_ERR_CONFIG;
+  // The trace kernel: fp32 C, row-major B.
+  if ((c.flags & PIPE_FLAG_TRACE) && (c.flags & (PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_B_COLMAJOR)))
+    return PIPE_ERR_CONFIG;
   if (gemm_lds_bytes(c.stages, c_bf16, store_wave) > kLdsLimit) return PIPE_ERR_STAGES;
   return PIPE_OK;
 }

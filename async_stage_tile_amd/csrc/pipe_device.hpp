@@ -177,6 +177,29 @@ __device__ __forceinline__ bool bar_wait(uint32_t* bar, uint32_t phase, uint32_t
 }
 
 // ---------------------------------------------------------------------------
+// Trace records (PIPE_TRACE_WORDS = 8 words each): workgroup 0 only, record
+// 2 t + event for the t-th tile (stage) of its stream, while it fits `cap`.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void trace_write(uint32_t* trace, int cap, int t, int event,
+                                            const PipeState& st, int wave) {
+  if (trace == nullptr || blockIdx.x != 0) return;
+  const int rec = 2 * t + event;
+  if (rec >= cap) return;
+  if (lane_id() == 0) {
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
+    uint32_t* r = trace + (size_t)rec * 8;
+    r[0] = (uint32_t)event;
+    r[1] = (uint32_t)t;
+    r[2] = (uint32_t)st.index;
+    r[3] = st.phase;
+    r[4] = st.count;
+    r[5] = (uint32_t)wave;
+    r[6] = (uint32_t)now;
+    r[7] = (uint32_t)(now >> 32);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Debug kernels: a wave-uniform pseudo-random pause (stress runs shift the
 // waves' relative timing with it) and the status bit of a failed check.
 // ---------------------------------------------------------------------------

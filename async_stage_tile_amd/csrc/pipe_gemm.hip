@@ -121,7 +121,7 @@ __device__ __forceinline__ int swz_b(int k, int on) {
   return on ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : 0;
 }
 
-template <int S, int PW, bool BCOL>
+template <int S, int PW, bool BCOL, bool TRACE = false>
 __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
   constexpr int kLoads = 32 / PW;                     // DMA instructions per stage per wave
   constexpr int kMaxLag = 48 / kLoads - 1;            // (lag + 1) stages <= 48 loads
@@ -131,6 +131,7 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
   PipeState w = producer_start(S, 1u);
   const int lag = S - 1 < kMaxLag ? S - 1 : kMaxLag;
   int pending = 0;
+  int t = 0;  // stage ordinal in this workgroup's stream (for the trace)
   bool ok = true;
   for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
     int tm, tn;
@@ -146,6 +147,10 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
                                                              p.spin_limit)) {
         ok = false;
         break;
+      }
+      if constexpr (TRACE) {
+        if (pw == 0) trace_write(p.trace, p.trace_cap, t, 0, w, 0);
+        ++t;
       }
       if (is_a) {
         const uint32_t sa = uniform(lds_addr(&lds.a[w.index][0]));
@@ -292,7 +297,7 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // reads of the slot to return, releases the slot, then waits on full for the
 // next stage (while the previous MFMAs still execute) and reads that stage's
 // first sub-step before issuing the last MFMAs of the current one.
-template <int S, int PW, int EPI, bool BCOL>
+template <int S, int PW, int EPI, bool BCOL, bool TRACE = false>
 __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_lds, int cw) {
   OutLds* out = static_cast<OutLds*>(out_lds);
   const int lane = lane_id();
@@ -300,6 +305,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
   const int li = lane & 31, lk = lane >> 5;
   PipeState rd = consumer_start(S);
   PipeState ost = producer_start(1, 1u);  // staging slot of this wave's pair
+  int t = 0;  // stage ordinal in this workgroup's stream (for the trace)
   bool ok = true;
   for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
     int tm, tn;
@@ -315,6 +321,9 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
     if (!bar_wait<Counter<PW>>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
       ok = false;
       break;
+    }
+    if constexpr (TRACE) {
+      if (cw == 0) trace_write(p.trace, p.trace_cap, t, 1, rd, PW);
     }
     const uint8_t* sa = &lds.a[rd.index][0];
     const uint8_t* sb = &lds.b[rd.index][0];
@@ -333,10 +342,14 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
       wait_lgkmcnt0();
       Counter<4>::arrive(&lds.empty[rd.index]);
       rd.inc();
+      if constexpr (TRACE) ++t;
       if (ks + 1 < p.k_steps) {
         if (!bar_wait<Counter<PW>>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
           ok = false;
           break;
+        }
+        if constexpr (TRACE) {
+          if (cw == 0) trace_write(p.trace, p.trace_cap, t, 1, rd, PW);
         }
         sa = &lds.a[rd.index][0];
         sb = &lds.b[rd.index][0];
@@ -472,7 +485,7 @@ __device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int PW, int EPI, bool BCOL>
+template <int S, int PW, int EPI, bool BCOL, bool TRACE = false>
 __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   __shared__ GemmLds<S> lds;
   const int wave = (int)(threadIdx.x >> 6);
@@ -503,34 +516,45 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   } else {
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW, BCOL>(p, lds, wave);
+      gemm_producer<S, PW, BCOL, TRACE>(p, lds, wave);
     else
-      gemm_consumer<S, PW, EPI, BCOL>(p, lds, nullptr, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL, TRACE>(p, lds, nullptr, wave - PW);
   }
 }
 
-// B row-major (K x N, the default) and column-major (PIPE_FLAG_GEMM_B_COLMAJOR).
-template <int S, int PW, int EPI>
-__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)))
-    gemm_kernel(GemmParams p) {
-  gemm_body<S, PW, EPI, false>(p);
-}
-
-// Waves per SIMD the column-major kernel is compiled for (its VGPR budget):
-// two workgroups share a CU, as with row-major B, where two rings fit the LDS
-// (S <= 2; 4 waves per SIMD with 4 producer waves, i.e. at most 128 VGPRs),
-// else one. The store-wave variant runs one per CU anyway.
-constexpr int bcol_waves_per_simd(int S, int PW, int EPI) {
+// Waves per SIMD the GEMM kernels are compiled for (their VGPR budget): two
+// workgroups share a CU where two rings fit the LDS (S <= 2; 4 waves per SIMD
+// with 4 producer waves, i.e. at most 128 VGPRs), else one. The store-wave
+// variant runs one per CU anyway. Without the bound a few more registers (the
+// trace's, say) can push the kernel past 128 VGPRs and halve its occupancy.
+constexpr int gemm_waves_per_simd(int S, int PW, int EPI) {
   if (EPI == kEpiStoreWave) return 1;
   const int workgroups = S <= 2 ? 2 : 1;
   return (workgroups * (PW + 4) + 3) / 4;
 }
 
+// B row-major (K x N, the default) and column-major (PIPE_FLAG_GEMM_B_COLMAJOR).
 template <int S, int PW, int EPI>
 __global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)),
-                                  bcol_waves_per_simd(S, PW, EPI))
+                                  gemm_waves_per_simd(S, PW, EPI))
+    gemm_kernel(GemmParams p) {
+  gemm_body<S, PW, EPI, false>(p);
+}
+
+template <int S, int PW, int EPI>
+__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)),
+                                  gemm_waves_per_simd(S, PW, EPI))
     gemm_kernel_bcol(GemmParams p) {
   gemm_body<S, PW, EPI, true>(p);
+}
+
+// With PIPE_FLAG_TRACE (fp32 C, row-major B): the same mainloop, recording
+// workgroup 0's acquires and waits. A separate kernel, so that the trace costs
+// the other kernels no registers.
+template <int S, int PW>
+__global__ void __launch_bounds__(64 * (PW + 4), gemm_waves_per_simd(S, PW, kEpiF32))
+    gemm_trace_kernel(GemmParams p) {
+  gemm_body<S, PW, kEpiF32, false, true>(p);
 }
 
 template <int PW, int EPI>
@@ -544,6 +568,15 @@ hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t
     case 3: row = gemm_kernel<3, PW, EPI>; col = gemm_kernel_bcol<3, PW, EPI>; break;
     case 4: row = gemm_kernel<4, PW, EPI>; col = gemm_kernel_bcol<4, PW, EPI>; break;
     default: return hipErrorInvalidValue;
+  }
+  if (p.trace != nullptr) {  // fp32 C and row-major B only (checked by the host)
+    if (EPI != kEpiF32 || p.b_colmajor) return hipErrorInvalidValue;
+    switch (stages) {
+      case 1: row = gemm_trace_kernel<1, PW>; break;
+      case 2: row = gemm_trace_kernel<2, PW>; break;
+      case 3: row = gemm_trace_kernel<3, PW>; break;
+      default: row = gemm_trace_kernel<4, PW>; break;
+    }
   }
   return launch_or_record(p.b_colmajor ? col : row, g, b, stream, p);
 }

@@ -71,21 +71,7 @@ struct StreamLds {
 
 __device__ __forceinline__ void trace_record(const StreamParams& p, int t, int event,
                                              const PipeState& st, int wave) {
-  if (p.trace == nullptr || blockIdx.x != 0) return;
-  int rec = 2 * t + event;
-  if (rec >= p.trace_cap) return;
-  if (lane_id() == 0) {
-    uint64_t now = __builtin_amdgcn_s_memrealtime();
-    uint32_t* r = p.trace + (size_t)rec * 8;
-    r[0] = (uint32_t)event;
-    r[1] = (uint32_t)t;
-    r[2] = (uint32_t)st.index;
-    r[3] = st.phase;
-    r[4] = st.count;
-    r[5] = (uint32_t)wave;
-    r[6] = (uint32_t)now;
-    r[7] = (uint32_t)(now >> 32);
-  }
+  trace_write(p.trace, p.trace_cap, t, event, st, wave);
 }
 
 // Work item taken by the workgroup for its n-th item slot.

@@ -68,7 +68,9 @@ typedef enum {
 } pipe_op_t;
 
 /* cfg->flags */
-#define PIPE_FLAG_TRACE 0x1u           /* record per-tile cursor values into cfg->trace */
+#define PIPE_FLAG_TRACE 0x1u           /* record per-tile cursor values into cfg->trace (copy,
+                                          rowsum, and gemm with fp32 C and row-major B; else
+                                          PIPE_ERR_CONFIG for the gemm) */
 #define PIPE_FLAG_ROW_STRIPS 0x2u      /* copy: walk tiles along rows instead of down columns */
 #define PIPE_FLAG_NONTEMPORAL 0x4u     /* copy/rowsum: non-temporal hint on streamed loads/stores */
 #define PIPE_FLAG_GEMM_B_LINEAR 0x8u   /* gemm: store B K-rows in LDS without the XOR swizzle */

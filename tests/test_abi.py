@@ -491,3 +491,14 @@ def test_debug_check_configs():
     assert status(pt.PIPE_OP_GEMM, flags=Dg) == pt.PIPE_ERR_CONFIG
     q = lambda **kw: pt.pipe_query_kernel(pt.PIPE_OP_COPY, 1024, 1024, stages=4, **kw)
     assert q(flags=Dg | pt.PIPE_FLAG_STRIP_GROUPS) == q(flags=Dg) == q(flags=0)
+
+
+def test_gemm_trace_needs_fp32_c_and_row_major_b():
+    info = pt.pipe_kernel_info_t()
+    T = pt.PIPE_FLAG_TRACE
+    for flags, want in ((T, pt.PIPE_OK), (T | pt.PIPE_FLAG_GEMM_C_BF16, pt.PIPE_ERR_CONFIG),
+                        (T | pt.PIPE_FLAG_GEMM_B_COLMAJOR, pt.PIPE_ERR_CONFIG)):
+        c = pt.make_config(pt.PIPE_OP_GEMM, flags=flags | pt.PIPE_FLAG_EAGER_NEWEST)
+        c.trace, c.trace_capacity = 64, 8          # any aligned address: nothing is launched
+        assert pt.lib().pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 256, 256, 256,
+                                          ctypes.byref(info)) == want, hex(flags)

@@ -5,6 +5,7 @@ import torch
 
 import async_stage_tile_amd as pt
 import synth
+from oracle import protocol as P
 from oracle import results as R
 
 pytestmark = pytest.mark.gpu
@@ -330,3 +331,30 @@ def test_gemm_strided_row_major_operands():
     C = pt.pipe_gemm_mainloop(A, B)
     torch.cuda.synchronize()
     assert np.array_equal(C.cpu().numpy(), R.gemm_f64(_f32(A.contiguous()), _f32(B.contiguous())))
+
+
+def test_gemm_trace_cursors():
+    """Workgroup 0's trace: the producer acquires stage t and MFMA wave 0 passes
+    its wait on stage t at the cursor values of the closed form, the wait after
+    the acquire, and slot reuse (stage t + S) only after stage t was waited on."""
+    S = 3
+    A = synth.small_int((256, 512), -2, 2, torch.bfloat16, seed=61, stream=0).to(DEV)
+    B = synth.small_int((512, 128), -2, 2, torch.bfloat16, seed=61, stream=1).to(DEV)
+    trace = torch.zeros(32 * pt.PIPE_TRACE_WORDS, dtype=torch.int32, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, stages=S, grid=1, flags=pt.PIPE_FLAG_TRACE |
+                              pt.PIPE_FLAG_EAGER_NEWEST, trace=trace, trace_capacity=32,
+                              status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(C.cpu().numpy(), R.gemm_f64(_f32(A), _f32(B)))
+    tr = trace.cpu().numpy().view(np.uint32).reshape(32, pt.PIPE_TRACE_WORDS)
+    prod, cons = tr[0::2], tr[1::2]      # 2 tiles x 8 K steps = 16 stages
+    clock = lambda rec: (int(rec[7]) << 32) | int(rec[6])
+    for t in range(16):
+        assert tuple(prod[t][:2]) == (0, t) and tuple(cons[t][:2]) == (1, t), t
+        assert tuple(prod[t][2:5]) == P.cursor_after(S, t, 1) + (t,)
+        assert tuple(cons[t][2:5]) == P.cursor_after(S, t, 0) + (t,)
+        assert clock(cons[t]) >= clock(prod[t])
+        if t + S < 16:
+            assert clock(prod[t + S]) >= clock(cons[t])
