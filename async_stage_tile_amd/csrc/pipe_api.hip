@@ -226,7 +226,6 @@ pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool
 
 void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_strips,
                         StreamParams* p) {
-  p->tile_rows = g.tile_rows;
   p->tile_cols = g.tile_cols;
   p->n_strips = g.n_strips;
   p->strip_len = g.strip_len;
@@ -331,10 +330,9 @@ pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int
   p->M = (int32_t)M;
   p->N = (int32_t)N;
   p->K = (int32_t)K;
-  p->tiles_m = (int32_t)(M / 128);
   p->tiles_n = (int32_t)(N / 128);
   p->k_steps = (int32_t)(K / 64);
-  const int64_t items = (int64_t)p->tiles_m * p->tiles_n;
+  const int64_t items = (M / 128) * (int64_t)p->tiles_n;
   if (items > INT32_MAX) return PIPE_ERR_SHAPE;
   p->items = (int32_t)items;
   p->swz_shift = c.swizzle_shift;

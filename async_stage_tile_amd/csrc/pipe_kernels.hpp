@@ -19,7 +19,6 @@ struct StreamParams {
   int64_t ld_dst;         // row pitch, bytes
   int64_t M;              // rows (also the rowsum partial stride)
   int64_t N;              // columns (fp16 elements, a multiple of 8)
-  int32_t tile_rows;      // ceil(M / 128)
   int32_t tile_cols;      // ceil(N / 64)
   int32_t n_strips;
   int32_t strip_len;      // tiles per strip
@@ -138,7 +137,7 @@ struct GemmParams {
   void* C;                // M x N, fp32 (or bf16 when c_bf16)
   int64_t lda, ldb, ldc;  // bytes for A, B; elements for C
   int32_t M, N, K;
-  int32_t tiles_m, tiles_n, k_steps;
+  int32_t tiles_n, k_steps;  // output tile columns; 64-deep K steps
   int32_t items;          // output tiles
   int32_t swz_shift;
   int32_t b_swz;          // 1: XOR-swizzle the B K-rows (default; row-major B only)
