@@ -245,6 +245,25 @@ def copy_buffers():
     return _COPY_BUF["src"], _COPY_BUF["dst"]
 
 
+def bench_copy_pitch(steps, warmup, cols=16320):
+    """The default copy on a contiguous 16384 x `cols` fp16 matrix: with 16320
+    columns the row pitch is 32 640 bytes instead of the headline's 32 768
+    (context for the headline: the same kernel and tiles, another pitch)."""
+    import torch
+
+    import async_stage_tile_amd as pt
+    import synth
+    src = synth.uniform((COPY_M, cols), torch.float16, seed=42, device="cuda")
+    dst = torch.empty_like(src)
+    fn = pt.copy_launcher(src, dst)
+    wall, kern = timed_launches(fn, steps, warmup)
+    nbytes = 2 * src.numel() * 2
+    ok = torch.equal(dst.view(torch.int16), src.view(torch.int16))
+    return {"shape": [COPY_M, cols], "row_pitch_bytes": cols * 2, "kernel_ms": kern,
+            "gbs": nbytes / (wall * 1e-3) / 1e9, "kernel_gbs": nbytes / (kern * 1e-3) / 1e9,
+            "bit_exact": ok}
+
+
 def run_for(fn, seconds):
     """Untimed launches of `fn` for about `seconds`, synchronising every 100
     launches; returns the number of launches."""
@@ -794,6 +813,9 @@ def main():
             "strip_tiles": 4,
             "kernel_pct_of_peak": round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)}
         log(f"[bench] copy, grouped strips: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
+        w = bench_copy_pitch(args.steps, args.warmup)
+        extras["copy_pitch_32640"] = w
+        log(f"[bench] copy, 16384 x 16320 (32 640-byte pitch): {w['gbs']:.1f} GB/s")
         cfg = dict(REGS_COPY)
         w = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
         extras["copy_register_engine"] = {
