@@ -697,7 +697,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "copy_grouped",
-                                       "copy_regs", "rowsum", "rowsum_regs",
+                                       "copy_regs", "copy_pitch", "rowsum", "rowsum_regs",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
                                        "gemm_bcol", "ceiling", "calib"],
                     default=None,
@@ -737,6 +737,10 @@ def main():
         cfg = dict(GROUPED_COPY)
         r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
         log(f"[bench] copy_grouped: {r}")
+        return
+    if args.only == "copy_pitch":
+        r = bench_copy_pitch(args.steps, args.warmup)
+        log(f"[bench] copy_pitch: {r}")
         return
     if args.only == "copy_regs":
         cfg = dict(REGS_COPY)
