@@ -472,3 +472,17 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
                 stack.append(n)
     return ProtocolResult(len(seen), deadlock, completed and not deadlock,
                           sorted(violations, key=repr), max_ahead)
+
+
+# --------------------------------------------------------------------------
+# Shared storage of the pages' pipeline
+# --------------------------------------------------------------------------
+def page_shared_storage_bytes(stages: int, tile_rows: int, tile_cols: int, elem_bytes: int = 2,
+                              barrier_bytes: int = 8, data_align: int = 128) -> dict:
+    """Byte layout of the pages' SharedStorage ("cute（12）async_pipeline" 5.1-5.2):
+    a full and an empty mbarrier of ``barrier_bytes`` per stage first, then the
+    stage buffers at the next ``data_align`` boundary."""
+    pipeline = stages * 2 * barrier_bytes
+    data = stages * tile_rows * tile_cols * elem_bytes
+    data_offset = -(-pipeline // data_align) * data_align
+    return {"pipeline_bytes": pipeline, "data_bytes": data, "total_bytes": data_offset + data}

@@ -502,3 +502,14 @@ def test_gemm_trace_needs_fp32_c_and_row_major_b():
         c.trace, c.trace_capacity = 64, 8          # any aligned address: nothing is launched
         assert pt.lib().pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 256, 256, 256,
                                           ctypes.byref(info)) == want, hex(flags)
+
+
+def test_ring_lds_layout_of_the_three_stage_program():
+    """The pages' 3-stage ring (128 x 64 fp16 tiles) on gfx950: 3 slots of 16 KiB,
+    then 32-bit full, empty and checksum words per slot and one partial per
+    consumer wave and slot (1 producer + 3 consumer waves: 49 224 bytes, against
+    the pages' 49 280 with 8-byte mbarriers placed first)."""
+    q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 128, 512, stages=3, producer_waves=1,
+                             consumer_waves=3, grid=1)
+    assert q["lds_bytes"] == 3 * 16384 + 3 * 4 * (3 + 3) == 49224
+    assert q["threads"] == 256 and q["grid"] == 1 and q["tiles_per_item"] == 8

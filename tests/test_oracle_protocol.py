@@ -265,3 +265,19 @@ def test_counter_phase_survives_the_32_bit_wrap_for_powers_of_two():
     # not so for 3: which is why the host bounds the arrivals per slot
     assert any(P.counter_phase(c % 2 ** 32, 3) != P.counter_phase(c, 3)
                for c in range(2 ** 32, 2 ** 32 + 6))
+
+
+def test_page_shared_storage_arithmetic(golden):
+    """The 3-stage program's printed shared-memory sizes follow from two 8-byte
+    barriers per stage placed first and 128-byte aligned 16 KiB tile buffers;
+    one tile is the printed transaction size, and 128 x 64 tiles of a 256 x 128
+    matrix make the printed 2 x 2 grid."""
+    kv = {ln.split()[0]: [int(x) for x in ln.split()[1:]] for ln in golden("shared_storage_12.txt")}
+    got = P.page_shared_storage_bytes(kv["stages"][0], kv["tile_rows"][0], kv["tile_cols"][0])
+    assert got == {"pipeline_bytes": kv["pipeline_bytes"][0], "data_bytes": kv["data_bytes"][0],
+                   "total_bytes": kv["total_bytes"][0]}
+    tile = P.page_shared_storage_bytes(1, kv["tile_rows"][0], kv["tile_cols"][0])["data_bytes"]
+    assert tile == kv["tx_bytes"][0]
+    assert [256 // kv["tile_rows"][0], 128 // kv["tile_cols"][0]] == kv["grid_256x128"]
+    # a plausible misreading (one barrier per stage, or unaligned data) misses the printed total
+    assert P.page_shared_storage_bytes(3, 128, 64, data_align=8)["total_bytes"] != kv["total_bytes"][0]
