@@ -512,4 +512,4 @@ def test_ring_lds_layout_of_the_three_stage_program():
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 128, 512, stages=3, producer_waves=1,
                              consumer_waves=3, grid=1)
     assert q["lds_bytes"] == 3 * 16384 + 3 * 4 * (3 + 3) == 49224
-    assert q["threads"] == 256 and q["grid"] == 1 and q["tiles_per_item"] == 8
+    assert q["threads"] == 256 and q["grid"] == 1 and (q["items"], q["tiles_per_item"]) == (8, 1)
