@@ -286,8 +286,10 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
   pipe_status_t s = check_common(c);
   if (s != PIPE_OK) return s;
   if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
-  if (c.tile_m != 128 || c.tile_n != 128 || c.tile_k != 64) return PIPE_ERR_CONFIG;
-  if ((c.producer_waves != 2 && c.producer_waves != 4) || c.consumer_waves != 4)
+  // 128 x 128 output tiles with 4 MFMA waves, or 256 x 128 with 8.
+  if ((c.tile_m != 128 && c.tile_m != 256) || c.tile_n != 128 || c.tile_k != 64)
+    return PIPE_ERR_CONFIG;
+  if ((c.producer_waves != 2 && c.producer_waves != 4) || c.consumer_waves != c.tile_m / 32)
     return PIPE_ERR_CONFIG;
   if (c.split > 1) return PIPE_ERR_CONFIG;
   if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS |
@@ -302,7 +304,11 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
   // The trace kernel: fp32 C, row-major B.
   if ((c.flags & PIPE_FLAG_TRACE) && (c.flags & (PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_B_COLMAJOR)))
     return PIPE_ERR_CONFIG;
-  if (gemm_lds_bytes(c.stages, c_bf16, store_wave) > kLdsLimit) return PIPE_ERR_STAGES;
+  // 256-row tiles: four producer waves, no store wave, no trace kernel.
+  if (c.tile_m == 256 && (c.producer_waves != 4 ||
+                          (c.flags & (PIPE_FLAG_GEMM_STORE_WAVE | PIPE_FLAG_TRACE))))
+    return PIPE_ERR_CONFIG;
+  if (gemm_lds_bytes(c.stages, c_bf16, store_wave, c.tile_m) > kLdsLimit) return PIPE_ERR_STAGES;
   return PIPE_OK;
 }
 
@@ -312,7 +318,7 @@ pipe_status_t gemm_check_shape(const pipe_config_t& c, int64_t M, int64_t N, int
   const bool b_col = (c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) != 0;
   if (M < 0 || N < 0 || K < 0 || lda < K || ldb < (b_col ? K : N) || ldc < N)
     return PIPE_ERR_SHAPE;
-  if (M % 128 != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
+  if (M % c.tile_m != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
   if (!extent_fits(M, lda, 2) || !extent_fits(b_col ? N : K, ldb, 2) ||
       !extent_fits(M, ldc, (c.flags & PIPE_FLAG_GEMM_C_BF16) ? 2 : 4))
@@ -332,7 +338,8 @@ pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int
   p->K = (int32_t)K;
   p->tiles_n = (int32_t)(N / 128);
   p->k_steps = (int32_t)(K / 64);
-  const int64_t items = (M / 128) * (int64_t)p->tiles_n;
+  const int64_t items = (M / c.tile_m) * (int64_t)p->tiles_n;
+  p->tile_m = c.tile_m;
   if (items > INT32_MAX) return PIPE_ERR_SHAPE;
   p->items = (int32_t)items;
   p->swz_shift = c.swizzle_shift;
@@ -346,8 +353,8 @@ pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int
   p->trace_cap = (c.flags & PIPE_FLAG_TRACE) ? c.trace_capacity : 0;
   if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
   *grid = (c.grid == 0 || c.grid > p->items) ? p->items : c.grid;
-  // Barrier words count arrivals in 32 bits (4 per stage on empty).
-  if (((int64_t)p->items + *grid - 1) / *grid * p->k_steps * 4 >= (int64_t(1) << 31))
+  // Barrier words count arrivals in 32 bits (one per MFMA wave and stage on empty).
+  if (((int64_t)p->items + *grid - 1) / *grid * p->k_steps * c.consumer_waves >= (int64_t(1) << 31))
     return PIPE_ERR_SHAPE;
   return PIPE_OK;
 }
@@ -533,14 +540,14 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     pipe_status_t s = gemm_check_config(c);  // rejects what pipe_gemm_mainloop rejects
     if (s != PIPE_OK) return s;
     if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
-    if (M < 0 || N < 0 || K < 0 || M % 128 || N % 128 || K % 64) return PIPE_ERR_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || M % c.tile_m || N % 128 || K % 64) return PIPE_ERR_SHAPE;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
-    const int64_t items = (M / 128) * (N / 128);
+    const int64_t items = (M / c.tile_m) * (N / 128);
     if (items > INT32_MAX) return PIPE_ERR_SHAPE;
     const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
     const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
-    info->lds_bytes = gemm_lds_bytes(c.stages, c_bf16, store_wave);
-    info->threads = gemm_threads(c.producer_waves, c_bf16, store_wave);
+    info->lds_bytes = gemm_lds_bytes(c.stages, c_bf16, store_wave, c.tile_m);
+    info->threads = gemm_threads(c.producer_waves, c_bf16, store_wave, c.tile_m);
     info->items = (int32_t)items;
     info->grid = (c.grid == 0 || c.grid > info->items) ? info->items : c.grid;
     info->tiles_per_item = (int32_t)(K / 64);

@@ -18,6 +18,12 @@
 // min(S - 1, 48 / (32 / PW) - 1) stages of lag, so that the stages in flight
 // never exceed 48 outstanding loads per wave.
 //
+// 256 x 128 output tiles (tile_m = 256): a stage holds 256 x 64 of A (two
+// 128-row halves, each laid out as above) and the same 64 x 128 of B; eight
+// consumer waves each own a 64 x 64 block, so every B byte in LDS feeds twice
+// the MFMAs. The stage's 48 one-KiB DMA blocks (A's 32, then B's 16) are dealt
+// out 12 to each of 4 producer waves, and empty expects 8 arrivals.
+//
 // Consumers read fragments one 16-deep K sub-step ahead of the MFMAs (two
 // register buffers), release a slot as soon as their reads of it have
 // returned, and wait for the next stage while the last MFMAs still run.
@@ -83,9 +89,13 @@ constexpr int kAStageBytes = kGemmTile * kGemmK * 2;  // 16 KiB
 constexpr int kBStageBytes = kGemmK * kGemmTile * 2;  // 16 KiB
 constexpr int kBRowBytes = kGemmTile * 2;             // 256
 
-template <int S>
+// MT = 1: 128 x 128 output tiles, 4 MFMA waves. MT = 2: 256 x 128 output
+// tiles, 8 MFMA waves, and A stages of 256 x 64 (two 128-row halves, each laid
+// out like an MT = 1 A stage), so each B byte brought into LDS feeds twice the
+// MFMAs.
+template <int S, int MT = 1>
 struct GemmLds {
-  uint8_t a[S][kAStageBytes];
+  uint8_t a[S][MT * kAStageBytes];
   uint8_t b[S][kBStageBytes];
   uint32_t full[S];
   uint32_t empty[S];
@@ -105,9 +115,11 @@ struct OutLds {
 constexpr int kWaveOutPitch = 64 * 2 + 16;                // 144 B: padded 64-column bf16 row
 constexpr int kWaveOutBytes = kOutRows * kWaveOutPitch;   // 2304 B per MFMA wave
 
+template <int MT = 1>
 struct WaveOutLds {
-  uint8_t buf[4][kWaveOutBytes];
+  uint8_t buf[4 * MT][kWaveOutBytes];
 };
+static_assert(sizeof(WaveOutLds<2>) == 8 * kWaveOutBytes, "staging buffers are unpadded");
 
 enum GemmEpilogue : int { kEpiF32 = 0, kEpiStoreWave = 1, kEpiWaveStaged = 2 };
 
@@ -121,9 +133,10 @@ __device__ __forceinline__ int swz_b(int k, int on) {
   return on ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : 0;
 }
 
-template <int S, int PW, bool BCOL, bool TRACE = false>
-__device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
-  constexpr int kLoads = 32 / PW;                     // DMA instructions per stage per wave
+template <int S, int PW, bool BCOL, bool TRACE = false, int MT = 1>
+__device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) {
+  constexpr int kABlocks = 16 * MT;                   // 1 KiB DMA blocks of an A stage
+  constexpr int kLoads = (kABlocks + 16) / PW;        // DMA instructions per stage per wave
   constexpr int kMaxLag = 48 / kLoads - 1;            // (lag + 1) stages <= 48 loads
   const int lane = lane_id();
   const bool is_a = pw < PW / 2;                      // first half of the waves load A
@@ -136,13 +149,13 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
   for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
     int tm, tn;
     gemm_tile_of(p, item, tm, tn);
-    const uint8_t* ga = p.A + (int64_t)tm * kGemmTile * p.lda;
+    const uint8_t* ga = p.A + (int64_t)tm * (kGemmTile * MT) * p.lda;
     // Row-major B: the tile's columns start tn * 256 bytes into each K-row.
     // Column-major B: its rows (one per output column) start at row tn * 128.
     const uint8_t* gb = BCOL ? p.B + (int64_t)tn * kGemmTile * p.ldb
                              : p.B + (int64_t)tn * kBRowBytes;
     for (int ks = 0; ks < p.k_steps; ++ks) {
-      if (!acquire_slot<kLoads, S, Counter<4>, Counter<PW>>(&lds.empty[w.index], w.phase,
+      if (!acquire_slot<kLoads, S, Counter<4 * MT>, Counter<PW>>(&lds.empty[w.index], w.phase,
                                                              lds.full, w.index, pending, p.eager,
                                                              p.spin_limit)) {
         ok = false;
@@ -152,7 +165,33 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
         if (pw == 0) trace_write(p.trace, p.trace_cap, t, 0, w, 0);
         ++t;
       }
-      if (is_a) {
+      if constexpr (MT > 1) {
+        // The stage's 16 MT + 16 blocks (A first, then B) in order, kLoads
+        // per wave; a wave's share may straddle A and B (uniform branch).
+        const uint32_t sa = uniform(lds_addr(&lds.a[w.index][0]));
+        const uint32_t sb = uniform(lds_addr(&lds.b[w.index][0]));
+        const uint8_t* a0 = ga + (int64_t)ks * kGemmK * 2;
+        const uint8_t* b0 = BCOL ? gb + (int64_t)ks * kGemmK * 2 : gb + (int64_t)ks * kGemmK * p.ldb;
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+          const int q = pw * kLoads + j;
+          if (q < kABlocks) {
+            const int r = q * 8 + (lane >> 3);
+            const int c = swz(r, lane & 7, p.swz_shift);
+            dma_block(a0 + (int64_t)r * p.lda + c * 16, sa + q * kBlockBytes);
+          } else if constexpr (BCOL) {
+            const int qb = q - kABlocks;
+            const int r = qb * 8 + (lane >> 3);
+            const int c = swz(r, lane & 7, p.swz_shift);
+            dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + qb * kBlockBytes);
+          } else {
+            const int qb = q - kABlocks;
+            const int r = qb * 4 + (lane >> 4);
+            const int c = (lane & 15) ^ swz_b(r, p.b_swz);
+            dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + qb * kBlockBytes);
+          }
+        }
+      } else if (is_a) {
         const uint32_t sa = uniform(lds_addr(&lds.a[w.index][0]));
         const uint8_t* a0 = ga + (int64_t)ks * kGemmK * 2;
 #pragma unroll
@@ -206,7 +245,7 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S>& lds, int pw) {
   }
   if (ok) {
     for (int i = 0; i < S; ++i) {
-      if (!bar_wait<Counter<4>>(&lds.empty[w.index], w.phase, p.spin_limit)) {
+      if (!bar_wait<Counter<4 * MT>>(&lds.empty[w.index], w.phase, p.spin_limit)) {
         ok = false;
         break;
       }
@@ -297,8 +336,10 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // reads of the slot to return, releases the slot, then waits on full for the
 // next stage (while the previous MFMAs still execute) and reads that stage's
 // first sub-step before issuing the last MFMAs of the current one.
-template <int S, int PW, int EPI, bool BCOL, bool TRACE = false>
-__device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_lds, int cw) {
+template <int S, int PW, int EPI, bool BCOL, bool TRACE = false, int MT = 1>
+__device__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT>& lds, void* out_lds, int cw) {
+  static_assert(MT == 1 || (EPI != kEpiStoreWave && !TRACE), "256-row tiles: no store wave, no trace");
+  constexpr int kTileM = kGemmTile * MT;
   OutLds* out = static_cast<OutLds*>(out_lds);
   const int lane = lane_id();
   const int wm = cw >> 1, wn = cw & 1;
@@ -340,7 +381,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
       interleave_mfma_reads<BCOL>();
       // consumer_release: this wave's reads of the slot have all returned.
       wait_lgkmcnt0();
-      Counter<4>::arrive(&lds.empty[rd.index]);
+      Counter<4 * MT>::arrive(&lds.empty[rd.index]);
       rd.inc();
       if constexpr (TRACE) ++t;
       if (ks + 1 < p.k_steps) {
@@ -368,14 +409,14 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
           const int col = tn * kGemmTile + wn * 64 + ni * 32 + li;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int row = tm * kGemmTile + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+            const int row = tm * kTileM + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
             C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
           }
         }
     } else if constexpr (EPI == kEpiWaveStaged) {
       // Wave-private staging: chunk c = rows 16c..16c+15 of this wave's 64 rows
       // (accumulator block mi = c / 2, element groups e / 4 = 2 (c % 2) + {0, 1}).
-      uint8_t* buf = &static_cast<WaveOutLds*>(out_lds)->buf[cw][0];
+      uint8_t* buf = &static_cast<WaveOutLds<MT>*>(out_lds)->buf[cw][0];
       uint8_t* C = static_cast<uint8_t*>(p.C);
       const int64_t ldc_bytes = p.ldc * 2;
 #pragma unroll
@@ -399,7 +440,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S>& lds, void* out_ld
           v[i] = *reinterpret_cast<const uint4*>(buf + (q >> 3) * kWaveOutPitch + (q & 7) * 16);
         }
         wait_lgkmcnt0();  // the buffer is rewritten by the next chunk
-        const int64_t row0 = (int64_t)tm * kGemmTile + wm * 64 + c * kOutRows;
+        const int64_t row0 = (int64_t)tm * kTileM + wm * 64 + c * kOutRows;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int q = i * 64 + lane;
@@ -485,9 +526,9 @@ __device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int PW, int EPI, bool BCOL, bool TRACE = false>
+template <int S, int PW, int EPI, bool BCOL, bool TRACE = false, int MT = 1>
 __device__ __forceinline__ void gemm_body(const GemmParams& p) {
-  __shared__ GemmLds<S> lds;
+  __shared__ GemmLds<S, MT> lds;
   const int wave = (int)(threadIdx.x >> 6);
   if (threadIdx.x < S) {
     lds.full[threadIdx.x] = 0u;
@@ -507,104 +548,147 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     else
       gemm_store_wave(p, out);
   } else if constexpr (EPI == kEpiWaveStaged) {
-    __shared__ WaveOutLds out;
+    __shared__ WaveOutLds<MT> out;
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW, BCOL>(p, lds, wave);
+      gemm_producer<S, PW, BCOL, false, MT>(p, lds, wave);
     else
-      gemm_consumer<S, PW, EPI, BCOL>(p, lds, &out, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL, false, MT>(p, lds, &out, wave - PW);
   } else {
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW, BCOL, TRACE>(p, lds, wave);
+      gemm_producer<S, PW, BCOL, TRACE, MT>(p, lds, wave);
     else
-      gemm_consumer<S, PW, EPI, BCOL, TRACE>(p, lds, nullptr, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL, TRACE, MT>(p, lds, nullptr, wave - PW);
   }
 }
 
 // Waves per SIMD the GEMM kernels are compiled for (their VGPR budget): two
-// workgroups share a CU where two rings fit the LDS (S <= 2; 4 waves per SIMD
-// with 4 producer waves, i.e. at most 128 VGPRs), else one. The store-wave
-// variant runs one per CU anyway. Without the bound a few more registers (the
-// trace's, say) can push the kernel past 128 VGPRs and halve its occupancy.
-constexpr int gemm_waves_per_simd(int S, int PW, int EPI) {
+// workgroups share a CU where two rings fit the LDS (S <= 2 with 128-row
+// tiles; 4 waves per SIMD with 4 producer waves, i.e. at most 128 VGPRs),
+// else one. The store-wave variant runs one per CU anyway. Without the bound a
+// few more registers (the trace's, say) can push the kernel past 128 VGPRs and
+// halve its occupancy.
+constexpr int gemm_waves_per_simd(int S, int PW, int EPI, int MT = 1) {
   if (EPI == kEpiStoreWave) return 1;
-  const int workgroups = S <= 2 ? 2 : 1;
-  return (workgroups * (PW + 4) + 3) / 4;
+  const int workgroups = (S <= 2 && MT == 1) ? 2 : 1;
+  return (workgroups * (PW + 4 * MT) + 3) / 4;
 }
+
+constexpr int gemm_block_threads(int PW, int EPI, int MT) {
+  return 64 * (PW + 4 * MT + (EPI == kEpiStoreWave ? 1 : 0));
+}
+
+// Static LDS of one workgroup: the ring, its barrier words and the bf16 staging.
+constexpr int gemm_lds_of(int S, int EPI, int MT) {
+  return S * (MT * kAStageBytes + kBStageBytes + 8) +
+         (EPI == kEpiStoreWave ? (int)sizeof(OutLds)
+                               : EPI == kEpiWaveStaged ? 4 * MT * kWaveOutBytes : 0);
+}
+
+constexpr bool gemm_fits(int S, int EPI, int MT) { return gemm_lds_of(S, EPI, MT) <= 160 * 1024; }
 
 // B row-major (K x N, the default) and column-major (PIPE_FLAG_GEMM_B_COLMAJOR).
-template <int S, int PW, int EPI>
-__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)),
-                                  gemm_waves_per_simd(S, PW, EPI))
+template <int S, int PW, int EPI, int MT = 1>
+__global__ void __launch_bounds__(gemm_block_threads(PW, EPI, MT),
+                                  gemm_waves_per_simd(S, PW, EPI, MT))
     gemm_kernel(GemmParams p) {
-  gemm_body<S, PW, EPI, false>(p);
+  gemm_body<S, PW, EPI, false, false, MT>(p);
 }
 
-template <int S, int PW, int EPI>
-__global__ void __launch_bounds__(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)),
-                                  gemm_waves_per_simd(S, PW, EPI))
+template <int S, int PW, int EPI, int MT = 1>
+__global__ void __launch_bounds__(gemm_block_threads(PW, EPI, MT),
+                                  gemm_waves_per_simd(S, PW, EPI, MT))
     gemm_kernel_bcol(GemmParams p) {
-  gemm_body<S, PW, EPI, true>(p);
+  gemm_body<S, PW, EPI, true, false, MT>(p);
 }
 
-// With PIPE_FLAG_TRACE (fp32 C, row-major B): the same mainloop, recording
-// workgroup 0's acquires and waits. A separate kernel, so that the trace costs
-// the other kernels no registers.
+// With PIPE_FLAG_TRACE (fp32 C, row-major B, 128-row tiles): the same
+// mainloop, recording workgroup 0's acquires and waits. A separate kernel, so
+// that the trace costs the other kernels no registers.
 template <int S, int PW>
 __global__ void __launch_bounds__(64 * (PW + 4), gemm_waves_per_simd(S, PW, kEpiF32))
     gemm_trace_kernel(GemmParams p) {
   gemm_body<S, PW, kEpiF32, false, true>(p);
 }
 
-template <int PW, int EPI>
-hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t stream) {
-  const dim3 g(grid), b(64 * (PW + 4 + (EPI == kEpiStoreWave ? 1 : 0)));
-  using Kernel = void (*)(GemmParams);
-  Kernel row, col;  // the kernels for row-major and column-major B
-  switch (stages) {
-    case 1: row = gemm_kernel<1, PW, EPI>; col = gemm_kernel_bcol<1, PW, EPI>; break;
-    case 2: row = gemm_kernel<2, PW, EPI>; col = gemm_kernel_bcol<2, PW, EPI>; break;
-    case 3: row = gemm_kernel<3, PW, EPI>; col = gemm_kernel_bcol<3, PW, EPI>; break;
-    case 4: row = gemm_kernel<4, PW, EPI>; col = gemm_kernel_bcol<4, PW, EPI>; break;
-    default: return hipErrorInvalidValue;
-  }
-  if (p.trace != nullptr) {  // fp32 C and row-major B only (checked by the host)
-    if (EPI != kEpiF32 || p.b_colmajor) return hipErrorInvalidValue;
-    switch (stages) {
-      case 1: row = gemm_trace_kernel<1, PW>; break;
-      case 2: row = gemm_trace_kernel<2, PW>; break;
-      case 3: row = gemm_trace_kernel<3, PW>; break;
-      default: row = gemm_trace_kernel<4, PW>; break;
-    }
-  }
-  return launch_or_record(p.b_colmajor ? col : row, g, b, stream, p);
+using GemmKernel = void (*)(GemmParams);
+
+// The kernel for ring depth S, or null where its LDS would not fit a CU.
+template <int S, int PW, int EPI, int MT>
+GemmKernel gemm_pick(bool bcol) {
+  if constexpr (gemm_fits(S, EPI, MT))
+    return bcol ? gemm_kernel_bcol<S, PW, EPI, MT> : gemm_kernel<S, PW, EPI, MT>;
+  else
+    return nullptr;
 }
 
-template <int EPI>
+template <int PW, int EPI, int MT>
+hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t stream) {
+  const dim3 g(grid), b(gemm_block_threads(PW, EPI, MT));
+  const bool bcol = p.b_colmajor != 0;
+  GemmKernel k;
+  switch (stages) {
+    case 1: k = gemm_pick<1, PW, EPI, MT>(bcol); break;
+    case 2: k = gemm_pick<2, PW, EPI, MT>(bcol); break;
+    case 3: k = gemm_pick<3, PW, EPI, MT>(bcol); break;
+    case 4: k = gemm_pick<4, PW, EPI, MT>(bcol); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (p.trace != nullptr) {  // fp32 C, row-major B, 128-row tiles (checked by the host)
+    if (EPI != kEpiF32 || bcol || MT != 1) return hipErrorInvalidValue;
+    switch (stages) {
+      case 1: k = gemm_trace_kernel<1, PW>; break;
+      case 2: k = gemm_trace_kernel<2, PW>; break;
+      case 3: k = gemm_trace_kernel<3, PW>; break;
+      default: k = gemm_trace_kernel<4, PW>; break;
+    }
+  }
+  if (k == nullptr) return hipErrorInvalidValue;
+  return launch_or_record(k, g, b, stream, p);
+}
+
+template <int EPI, int MT>
 hipError_t launch_gemm_epi(int stages, int producers, int grid, const GemmParams& p,
                            hipStream_t stream) {
-  if (producers == 4) return launch_gemm_pw<4, EPI>(stages, grid, p, stream);
-  if (producers == 2) return launch_gemm_pw<2, EPI>(stages, grid, p, stream);
+  if (producers == 4) return launch_gemm_pw<4, EPI, MT>(stages, grid, p, stream);
+  // Two producer waves would each issue 24 DMA instructions per 256-row stage
+  // and spill their addresses; 256-row tiles take four.
+  if constexpr (MT == 1)
+    if (producers == 2) return launch_gemm_pw<2, EPI, MT>(stages, grid, p, stream);
   return hipErrorInvalidValue;
+}
+
+template <int MT>
+hipError_t launch_gemm_mt(int stages, int producers, int grid, const GemmParams& p,
+                          hipStream_t stream) {
+  if (!p.c_bf16) return launch_gemm_epi<kEpiF32, MT>(stages, producers, grid, p, stream);
+  if (p.store_wave) {
+    if constexpr (MT == 1) return launch_gemm_epi<kEpiStoreWave, 1>(stages, producers, grid, p, stream);
+    return hipErrorInvalidValue;
+  }
+  return launch_gemm_epi<kEpiWaveStaged, MT>(stages, producers, grid, p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream) {
-  if (!p.c_bf16) return launch_gemm_epi<kEpiF32>(stages, producers, grid, p, stream);
-  if (p.store_wave) return launch_gemm_epi<kEpiStoreWave>(stages, producers, grid, p, stream);
-  return launch_gemm_epi<kEpiWaveStaged>(stages, producers, grid, p, stream);
+  if (p.tile_m == 256) return launch_gemm_mt<2>(stages, producers, grid, p, stream);
+  if (p.tile_m == 128) return launch_gemm_mt<1>(stages, producers, grid, p, stream);
+  return hipErrorInvalidValue;
 }
 
-int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave) {
-  const int out = !c_bf16 ? 0 : store_wave ? (int)sizeof(OutLds) : (int)sizeof(WaveOutLds);
-  return stages * (kAStageBytes + kBStageBytes) + stages * 8 + out;
+int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave, int tile_m) {
+  const int mt = tile_m / kGemmTile;
+  const int out = !c_bf16 ? 0
+                  : store_wave ? (int)sizeof(OutLds)
+                  : 4 * mt * kWaveOutBytes;
+  return stages * (mt * kAStageBytes + kBStageBytes) + stages * 8 + out;
 }
 
-int gemm_threads(int producers, bool c_bf16, bool store_wave) {
-  return 64 * (producers + 4 + (c_bf16 && store_wave ? 1 : 0));
+int gemm_threads(int producers, bool c_bf16, bool store_wave, int tile_m) {
+  return 64 * (producers + 4 * (tile_m / kGemmTile) + (c_bf16 && store_wave ? 1 : 0));
 }
 
 }  // namespace pipe

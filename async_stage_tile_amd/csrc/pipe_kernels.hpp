@@ -149,6 +149,7 @@ struct GemmParams {
   int32_t eager;          // eager commits while the acquire waits: min stages in flight (0 = off)
   int32_t c_bf16;         // C is bf16, written through an LDS-staged epilogue
   int32_t store_wave;     // bf16 C: a dedicated store wave drains the staging slots
+  int32_t tile_m;         // output tile rows: 128 (4 MFMA waves) or 256 (8 MFMA waves)
 };
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
@@ -170,7 +171,7 @@ inline hipError_t launch_or_record(void (*kernel)(P), dim3 grid, dim3 block, hip
   hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
   return hipGetLastError();
 }
-int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave);
-int gemm_threads(int producers, bool c_bf16, bool store_wave);
+int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave, int tile_m);
+int gemm_threads(int producers, bool c_bf16, bool store_wave, int tile_m);
 
 }  // namespace pipe

@@ -422,11 +422,12 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colma
     med, mn = launch_stats(fn, max(steps, 20), 0)
     flops = 2.0 * n * n * n
     c = pt._gemm_config(C, kw, b_colmajor)
-    gcfg = {f: getattr(c, f) for f in ("stages", "producer_waves", "flags", "swizzle_shift",
-                                       "grid")}
+    gcfg = {f: getattr(c, f) for f in ("stages", "producer_waves", "consumer_waves", "tile_m",
+                                       "flags", "swizzle_shift", "grid")}
     q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, n, n, n, **gcfg)
     return {"c_dtype": str(C.dtype).replace("torch.", ""),
             "b_layout": "column-major" if b_colmajor else "row-major", "stages": c.stages,
+            "tile": [c.tile_m, c.tile_n, c.tile_k],
             "producer_waves": c.producer_waves, "flags": c.flags,
             "wall_ms": wall, "kernel_ms": kern, "flops": flops,
             "tflops": flops / (wall * 1e-3) / 1e12,
@@ -860,6 +861,10 @@ def main():
         g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=3)
         log(f"[bench] gemm, three-stage ring: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_three_stage"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=3, tile_m=256,
+                       consumer_waves=8, producer_waves=4)
+        log(f"[bench] gemm, 256 x 128 tiles, three-stage ring: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_tile_256x128"] = g
         g = bench_gemm(max(3, args.steps // 2), args.warmup, out_dtype=torch.bfloat16)
         log(f"[bench] gemm, bf16 C: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16"] = g

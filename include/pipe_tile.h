@@ -161,12 +161,15 @@ typedef struct {
                              waves; the ring must fit 160 KiB of LDS); gemm 1..4          */
   int32_t tile_m;         /* copy/rowsum: 128, 64 or 32 (with tile_n 64, 128, 256: every
                              tile is 16 KiB; the wider two need S 2..4, producer_waves
-                             2 or 4, consumer_waves 4 or 8 -- unified: 2 or 4); gemm 128 */
+                             2 or 4, consumer_waves 4 or 8 -- unified: 2 or 4); gemm 128,
+                             or 256 with 8 consumer and 4 producer waves (S 1..3, S 1..2
+                             with bf16 C; no store wave, no trace)                        */
   int32_t tile_n;         /* copy/rowsum: 64, 128 or 256 fp16 (see tile_m); gemm: 128    */
   int32_t tile_k;         /* gemm only: 64                                                */
   int32_t producer_waves; /* copy/rowsum: 1, 2 or 4; gemm: 2 or 4 (each tile's loads split
                              evenly; a wave keeps up to 2, 6 or 14 tiles of commit lag)   */
-  int32_t consumer_waves; /* copy/rowsum: 1, 2, 3, 4 or 8 (unified: 2, 4 or 8); gemm: 4   */
+  int32_t consumer_waves; /* copy/rowsum: 1, 2, 3, 4 or 8 (unified: 2, 4 or 8); gemm:
+                             tile_m / 32 (4 or 8 MFMA waves, each a 64 x 64 output block) */
   int32_t grid;           /* workgroups; 0 = one per work item (capped by the device)     */
   int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default:
                              copy 1 (G with PIPE_FLAG_STRIP_GROUPS), rowsum the smallest
@@ -258,7 +261,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
  * staged through LDS so that C is written in whole 16-byte row pieces
  * (optionally by a dedicated store wave, PIPE_FLAG_GEMM_STORE_WAVE). A and B tiles
  * of each 64-deep K step pass through the LDS ring to MFMA consumer waves.
- *   M % 128 == 0, N % 128 == 0, K % 64 == 0; lda >= K and ldb >= N (ldb >= K
+ *   M % tile_m == 0, N % 128 == 0, K % 64 == 0; lda >= K and ldb >= N (ldb >= K
  *   for column-major B), both multiples of 8; ldc >= N (elements of C's type;
  *   a multiple of 8 for bf16 C, whose base must be 16-byte aligned); K == 0
  *   gives C = 0. */

@@ -350,11 +350,12 @@ def test_gemm_query_rejects_what_the_entry_point_rejects():
     info = pt.pipe_kernel_info_t()
     for _ in range(3000):
         c = pt.make_config(pt.PIPE_OP_GEMM, stages=rng.randrange(0, 7),
-                           producer_waves=rng.randrange(0, 6), consumer_waves=rng.randrange(0, 6),
+                           producer_waves=rng.randrange(0, 6),
+                           consumer_waves=rng.choice([0, 1, 2, 3, 4, 5, 8]),
                            split=rng.randrange(0, 3), flags=rng.randrange(0, 0x100000) & ~0x1,
-                           tile_m=rng.choice([64, 128]), tile_n=rng.choice([64, 128]))
+                           tile_m=rng.choice([64, 128, 256]), tile_n=rng.choice([64, 128]))
         entry = L.pipe_gemm_mainloop(None, None, None, 0, 0, 0, 0, 0, 0, ctypes.byref(c), None)
-        query = L.pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 128, 128, 64,
+        query = L.pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 256, 128, 64,
                                     ctypes.byref(info))
         if entry != pt.PIPE_OK:
             assert query == entry, (c.stages, c.producer_waves, c.consumer_waves, c.split,
@@ -513,3 +514,31 @@ def test_ring_lds_layout_of_the_three_stage_program():
                              consumer_waves=3, grid=1)
     assert q["lds_bytes"] == 3 * 16384 + 3 * 4 * (3 + 3) == 49224
     assert q["threads"] == 256 and q["grid"] == 1 and (q["items"], q["tiles_per_item"]) == (8, 1)
+
+
+def test_gemm_256_row_tiles_geometry_and_rejections():
+    """tile_m = 256: 8 MFMA + 4 producer waves, a ring of 256 x 64 A and 64 x 128
+    B stages; M must be a multiple of 256; no store wave, no trace, S <= 3
+    (S <= 2 with bf16 C, whose staging adds 8 x 16 rows of 144 bytes)."""
+    q = lambda M, N, K, **kw: pt.pipe_query_kernel(pt.PIPE_OP_GEMM, M, N, K, **kw)
+    T = dict(tile_m=256, consumer_waves=8, producer_waves=4)
+    for S in (1, 2, 3):
+        g = q(4096, 4096, 4096, stages=S, **T)
+        assert (g["items"], g["threads"], g["tiles_per_item"]) == (512, 768, 64)
+        assert g["lds_bytes"] == S * (256 * 64 * 2 + 64 * 128 * 2 + 8)
+    g = q(4096, 4096, 4096, stages=2, flags=pt.PIPE_FLAG_GEMM_C_BF16, **T)
+    assert g["lds_bytes"] == 2 * (48 * 1024 + 8) + 8 * 16 * 144
+    assert q(4096, 4096, 4096, **dict(T, tile_m=128, consumer_waves=4))["items"] == 1024
+    status = lambda M, **kw: pt.lib().pipe_query_kernel(
+        pt.PIPE_OP_GEMM, ctypes.byref(pt.make_config(pt.PIPE_OP_GEMM, **kw)), M, 128, 64,
+        ctypes.byref(pt.pipe_kernel_info_t()))
+    assert status(256, **T) == pt.PIPE_OK
+    assert status(384, **T) == pt.PIPE_ERR_SHAPE
+    assert status(256, **dict(T, consumer_waves=4)) == pt.PIPE_ERR_CONFIG
+    assert status(256, **dict(T, producer_waves=2)) == pt.PIPE_ERR_CONFIG
+    assert status(256, tile_m=128, consumer_waves=8, producer_waves=4) == pt.PIPE_ERR_CONFIG
+    assert status(256, stages=4, **T) == pt.PIPE_ERR_STAGES
+    assert status(256, stages=3, flags=pt.PIPE_FLAG_GEMM_C_BF16, **T) == pt.PIPE_ERR_STAGES
+    assert status(256, flags=pt.PIPE_FLAG_GEMM_C_BF16 | pt.PIPE_FLAG_GEMM_STORE_WAVE, **T) == \
+        pt.PIPE_ERR_CONFIG
+    assert status(256, flags=pt.PIPE_FLAG_TRACE, **T) != pt.PIPE_OK   # (no trace buffer either)
