@@ -700,7 +700,7 @@ def main():
     ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "copy_grouped",
                                        "copy_regs", "copy_pitch", "rowsum", "rowsum_regs",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
-                                       "gemm_bcol", "ceiling", "calib"],
+                                       "gemm_bcol", "gemm_tile256", "ceiling", "calib"],
                     default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
@@ -763,6 +763,11 @@ def main():
     if args.only == "gemm":
         r = bench_gemm(args.steps, args.warmup, args.stages)
         log(f"[bench] gemm: {r}")
+        return
+    if args.only == "gemm_tile256":
+        r = bench_gemm(args.steps, args.warmup, args.stages or 3, tile_m=256, consumer_waves=8,
+                       producer_waves=4)
+        log(f"[bench] gemm, 256 x 128 tiles: {r}")
         return
     if args.only == "gemm_bcol":
         r = bench_gemm(args.steps, args.warmup, args.stages, b_colmajor=True)
