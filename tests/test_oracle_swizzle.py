@@ -93,3 +93,25 @@ def test_reading_the_slot_unswizzled_gives_wrong_positions():
                 wrong_rows.add(r)
             assert (found == c) == (r % 8 == 0)
     assert len(wrong_rows) == 112
+
+
+def test_bank_model_matches_the_strided_access_closed_form():
+    """The bank model against the textbook count for strided 4-byte accesses:
+    n lanes reading words 0, s, 2s, ... (s > 0) over B banks touch
+    B / gcd(s, B) distinct banks, each holding ceil(n / (B / gcd(s, B)))
+    distinct words, so a pass of n lanes costs that many cycles, i.e. that
+    minus one extra. Broadcast (s = 0) costs nothing extra."""
+    import math
+    for B in (32, 64):
+        for n in (16, 32, 64):
+            for s in range(0, 70):
+                addrs = [4 * s * i for i in range(n)]
+                if s == 0:
+                    want = 0
+                else:
+                    distinct_banks = B // math.gcd(s, B)
+                    want = -(-n // distinct_banks) - 1
+                assert Z.bank_conflicts(addrs, 4, nbanks=B, lanes_per_pass=n) == want, (B, n, s)
+    # a wave split into passes: the extras of the passes add up
+    addrs = [4 * 64 * i for i in range(64)]          # stride of one full bank row
+    assert Z.bank_conflicts(addrs, 4, nbanks=64, lanes_per_pass=16) == 4 * 15
