@@ -224,6 +224,23 @@ pipe_status_t stream_geometry(int64_t M, int64_t N, const pipe_config_t& c, bool
   return PIPE_OK;
 }
 
+// Row-sum workspace: fp32 segment partials [split][M] from offset 0, then one
+// uint32 arrival ticket per row strip from a 256-byte aligned offset. Nothing
+// when each strip is one segment (the kernel writes `out` directly).
+struct RowsumWorkspace {
+  size_t ticket_offset;  // bytes
+  size_t bytes;          // total
+};
+
+RowsumWorkspace rowsum_workspace(const StreamGeom& g, int64_t M) {
+  RowsumWorkspace w{0, 0};
+  if (g.split <= 1) return w;
+  const size_t partials = (size_t)g.split * (size_t)M * sizeof(float);
+  w.ticket_offset = (partials + 255) & ~(size_t)255;
+  w.bytes = w.ticket_offset + (size_t)g.n_strips * sizeof(uint32_t);
+  return w;
+}
+
 void fill_stream_params(const pipe_config_t& c, const StreamGeom& g, bool row_strips,
                         StreamParams* p) {
   p->tile_cols = g.tile_cols;
@@ -359,6 +376,26 @@ pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int
   return PIPE_OK;
 }
 
+// The row sum's launches for a validated call: with segment partials, zero the
+// strips' arrival tickets, then run the stream kernel, whose last arrival per
+// strip writes `out`; else the stream kernel writes `out` itself.
+pipe_status_t launch_rowsum(const pipe_config_t& c, const StreamGeom& g,
+                            const RowsumWorkspace& ws, uint8_t* workspace, float* out,
+                            StreamParams* p, hipStream_t st) {
+  if (ws.bytes == 0) {
+    p->out = out;
+    p->final_out = nullptr;
+    p->tickets = nullptr;
+  } else {
+    p->out = reinterpret_cast<float*>(workspace);
+    p->final_out = out;
+    p->tickets = reinterpret_cast<uint32_t*>(workspace + ws.ticket_offset);
+    pipe_status_t s = hip_status(launch_fill_u32(p->tickets, g.n_strips, 0u, st));
+    if (s != PIPE_OK) return s;
+  }
+  return hip_status(launch_stream_op(kOpRowsum, c, g, *p, st));
+}
+
 // Address of the kernel that `launch` would launch, without launching it.
 template <class F>
 pipe_status_t record_kernel(F launch, const void** fn) {
@@ -449,7 +486,7 @@ pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_confi
   StreamGeom g;
   s = stream_geometry(M, N, c, true, true, &g);
   if (s != PIPE_OK) return s;
-  *bytes = g.split > 1 ? (size_t)g.split * (size_t)M * sizeof(float) : 0;
+  *bytes = rowsum_workspace(g, M).bytes;
   return PIPE_OK;
 }
 
@@ -477,16 +514,15 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   StreamGeom g;
   s = stream_geometry(M, N, c, true, true, &g);
   if (s != PIPE_OK) return s;
-  const size_t need = g.split > 1 ? (size_t)g.split * (size_t)M * sizeof(float) : 0;
-  if (need > 0) {
-    if (workspace == nullptr || workspace_bytes < need) return PIPE_ERR_WORKSPACE;
+  const RowsumWorkspace ws = rowsum_workspace(g, M);
+  if (ws.bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < ws.bytes) return PIPE_ERR_WORKSPACE;
     if (!aligned4(workspace)) return PIPE_ERR_ALIGN;
   }
   StreamParams p{};
   fill_stream_params(c, g, true, &p);
   p.src = static_cast<const uint8_t*>(A);
   p.dst = nullptr;
-  p.out = need > 0 ? static_cast<float*>(workspace) : out;
   p.checksums = nullptr;
   p.ld_src = lda * 2;
   p.ld_dst = 0;
@@ -494,10 +530,7 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
   p.N = N;
   s = resolve_status(c, &p.status);
   if (s != PIPE_OK) return s;
-  s = hip_status(launch_stream_op(kOpRowsum, c, g, p, st));
-  if (s != PIPE_OK || need == 0) return s;
-  return hip_status(launch_rowsum_finalize(static_cast<const float*>(workspace), out, M,
-                                           g.split, st));
+  return launch_rowsum(c, g, ws, static_cast<uint8_t*>(workspace), out, &p, st);
 }
 
 pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t M, int64_t N,

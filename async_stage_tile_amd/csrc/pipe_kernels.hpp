@@ -12,6 +12,8 @@ struct StreamParams {
   const uint8_t* src;     // copy source / rowsum input (fp16)
   uint8_t* dst;           // copy destination
   float* out;             // rowsum: final sums (split 1) or segment partials [split][M]
+  float* final_out;       // rowsum with split > 1: the final sums, written by the last arrival
+  uint32_t* tickets;      // rowsum with split > 1: one arrival counter per row strip, zero at launch
   uint32_t* checksums;    // copy: per-tile code sums (nullable)
   uint32_t* trace;        // nullable
   uint32_t* status;       // never null
@@ -124,8 +126,7 @@ constexpr bool unified_shape_supported(int S, int W, int TC) {
 hipError_t launch_unified(int op, int stages, int waves, int tile_n, int grid,
                           const StreamParams& p, hipStream_t stream);
 
-hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
-                                  hipStream_t stream);
+hipError_t launch_fill_u32(uint32_t* out, int64_t n, uint32_t value, hipStream_t stream);
 hipError_t launch_fill_f32(float* out, int64_t rows, int64_t cols, int64_t ld, float value,
                            hipStream_t stream);
 hipError_t launch_fill_u16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uint16_t value,

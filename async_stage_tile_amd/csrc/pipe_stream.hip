@@ -55,6 +55,7 @@
 
 #include "pipe_device.hpp"
 #include "pipe_kernels.hpp"
+#include "pipe_rowsum.hpp"
 
 namespace pipe {
 
@@ -406,10 +407,11 @@ __device__ void consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
           if (q < kBlocksPerTile) {
             const float s = sum_lanes<Sh::kChunksPerRow>(acc[j]);
             const int r = q * Sh::kRowsPerBlock + lrow;
-            if (lpos == 0 && (!MASKED || (int64_t)tr * Sh::kRows + r < p.M)) o[r] = s;
+            if (lpos == 0 && (!MASKED || (int64_t)tr * Sh::kRows + r < p.M)) store_partial(&o[r], s);
           }
           acc[j] = 0.f;
         }
+        if (p.tickets != nullptr) rowsum_strip_arrive<Sh::kRows, C>(p, item % p.n_strips);
       }
     }
   }

@@ -1,5 +1,4 @@
-// Stream-kernel dispatch over the stage count, the row-sum finalize, a small
-// fill kernel, and the per-thread slot of kernel lookups without a launch. The stream kernels themselves are instantiated per stage
+// Stream-kernel dispatch over the stage count, small fill kernels, and the per-thread slot of kernel lookups without a launch. The stream kernels themselves are instantiated per stage
 // count in the objects built from pipe_stream.hip.
 #include "pipe_device.hpp"
 #include "pipe_kernels.hpp"
@@ -68,24 +67,17 @@ int stream_lds_bytes(int stages, int consumers) {
   return stages * kTileBytes + stages * 4 * (3 + consumers);
 }
 
-// ---------------------------------------------------------------------------
-// Row-sum finalize: out[r] = sum_{s < split} partial[s][r], in order s = 0..split-1.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) rowsum_finalize(const float* __restrict__ part,
-                                                       float* __restrict__ out, int64_t M,
-                                                       int split) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= M) return;
-  float s = part[r];
-  for (int k = 1; k < split; ++k) s += part[(int64_t)k * M + r];
-  out[r] = s;
-}
-
 __global__ void __launch_bounds__(256) fill_f32(float* __restrict__ out, int64_t rows,
                                                 int64_t cols, int64_t ld, float value) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * cols) return;
   out[(i / cols) * ld + (i % cols)] = value;
+}
+
+__global__ void __launch_bounds__(256) fill_u32(uint32_t* __restrict__ out, int64_t n,
+                                                uint32_t value) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = value;
 }
 
 __global__ void __launch_bounds__(256) fill_u16(uint16_t* __restrict__ out, int64_t rows,
@@ -95,11 +87,10 @@ __global__ void __launch_bounds__(256) fill_u16(uint16_t* __restrict__ out, int6
   out[(i / cols) * ld + (i % cols)] = value;
 }
 
-hipError_t launch_rowsum_finalize(const float* partials, float* out, int64_t M, int split,
-                                  hipStream_t stream) {
-  const int64_t blocks = (M + 255) / 256;
-  hipLaunchKernelGGL(rowsum_finalize, dim3((unsigned)blocks), dim3(256), 0, stream, partials,
-                     out, M, split);
+hipError_t launch_fill_u32(uint32_t* out, int64_t n, uint32_t value, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_u32, dim3((unsigned)blocks), dim3(256), 0, stream, out, n, value);
   return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@
 // have returned (lgkmcnt), so no cross-wave barrier is needed at all.
 #include "pipe_device.hpp"
 #include "pipe_kernels.hpp"
+#include "pipe_rowsum.hpp"
 
 namespace pipe {
 
@@ -172,11 +173,13 @@ __global__ void __launch_bounds__(64 * W) unified_kernel(StreamParams p) {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
           const float rs = sum_lanes<Sh::kChunksPerRow>(acc[j]);
-          if (lpos == 0) o[(wave * kLoads + j) * Sh::kRowsPerBlock + lrow] = rs;
+          if (lpos == 0) store_partial(&o[(wave * kLoads + j) * Sh::kRowsPerBlock + lrow], rs);
           acc[j] = 0.f;
         }
-        // These partial stores are left out of `vm`: counting fewer operations
-        // than were issued only makes the batch waits stricter.
+        // These partial stores (and the arrival's atomic and loads) are left
+        // out of `vm`: counting fewer operations than were issued only makes
+        // the batch waits stricter.
+        if (p.tickets != nullptr) rowsum_strip_arrive<Sh::kRows, W>(p, use.item % p.n_strips);
       }
     }
     use.next(p);

@@ -233,7 +233,9 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N,
                              uint32_t* tile_checksums, void* stream);
 
 /* Bytes of workspace pipe_rowsum needs for this shape and config (0 when each
- * row strip is handled by one workgroup): split x M fp32 segment partials. */
+ * row strip is one segment): split x M fp32 segment partials, then, from the
+ * next 256-byte boundary, one uint32 arrival ticket per row strip. A
+ * diagnostic of this library's decomposition, not an operation of the pages. */
 pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_config_t* cfg,
                                           size_t* bytes);
 
@@ -241,13 +243,21 @@ pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_confi
  * ("cute（12）async_pipeline" 3.2: the consumer's use of each tile, here a
  * reduction; the pages leave the use open, the strip decomposition below is
  * this library's).
- * Row strips of 128 rows are cut into cfg->split segments along the columns;
- * segment partials go to the workspace and are added in a fixed order, so the
- * result is deterministic.
+ * Row strips of tile_m rows are cut into cfg->split segments along the
+ * columns. With more than one segment, each segment's fp32 partials go to the
+ * workspace and every consumer wave counts an arrival on its strip's ticket;
+ * the wave that arrives last adds the strip's partials in segment order
+ * 0, 1, ..., split - 1 and writes out, inside the same kernel. The order is
+ * fixed, so the result does not depend on timing and equals a plain
+ * fixed-order sum of the partials. The call enqueues a small fill kernel that
+ * zeroes the tickets and then the stream kernel, so the workspace may hold
+ * anything on entry; two calls that share a workspace must not overlap (use
+ * one stream, or one workspace per stream).
  *   A: device fp16, 16-byte aligned, lda multiple of 8 and >= N;
  *   N a multiple of 8, M arbitrary (partial edge tiles are masked);
  *   N == 0 gives out = 0; M == 0 is a no-op.
- *   out: device float[M]. workspace: device, >= pipe_rowsum_workspace_bytes. */
+ *   out: device float[M]. workspace: device, 4-byte aligned,
+ *   >= pipe_rowsum_workspace_bytes (else PIPE_ERR_WORKSPACE / PIPE_ERR_ALIGN). */
 pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
                           const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,
                           void* stream);
@@ -278,8 +288,8 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
 
 /* A diagnostic of this library, not an operation of the pages.
  * Compiled resources of the main kernel that an op would launch for this
- * shape and config (the stream, unified or GEMM kernel; not the row-sum
- * finalize or a zero fill), from the HIP runtime's function attributes. It
+ * shape and config (the stream, unified or GEMM kernel; not a zero fill), from
+ * the HIP runtime's function attributes. It
  * takes the same checks as the op's entry point minus those on pointers, with
  * the tightest pitches (ld = N, or K for A and column-major B), and launches
  * nothing. Unlike pipe_query_kernel it needs the HIP runtime and a device.
