@@ -6,6 +6,7 @@ The functions carry the C ABI's names (``include/pipe_tile.h``):
 
     pipe_tile_copy(src, dst=None, checksums=False, **cfg)  -> dst [, checksums]
     pipe_rowsum(A, out=None, workspace=None, **cfg)        -> out
+    pipe_rowsum_noalloc(A, out, **cfg)                     -> out
     pipe_gemm_mainloop(A, B, C=None, **cfg)                -> C
     pipe_query_kernel(op, M, N, K=0, **cfg)                -> dict
     pipe_kernel_resources(op, M, N, K=0, **cfg)            -> dict
@@ -134,6 +135,8 @@ _SIGS = {
     "pipe_rowsum": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
                                _c.POINTER(pipe_config_t), _c.c_void_p, _c.c_size_t,
                                _c.c_void_p]),
+    "pipe_rowsum_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                                       _c.c_int64, _c.POINTER(pipe_config_t), _c.c_void_p]),
     "pipe_gemm_mainloop": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                                       _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                       _c.c_int64, _c.POINTER(pipe_config_t), _c.c_void_p]),
@@ -323,6 +326,25 @@ def pipe_rowsum(A, out=None, workspace=None, stream=None, **cfg):
         st = lib().pipe_rowsum(_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c), _ptr(workspace),
                                wbytes, _stream(stream, dev))
     _check(st, "pipe_rowsum")
+    return out
+
+
+PIPE_ROWSUM_SCRATCH_BYTES = 1 << 20
+
+
+def pipe_rowsum_noalloc(A, out, stream=None, **cfg):
+    """pipe_rowsum with the workspace in the library's own per-device buffer
+    (for callers that cannot allocate). ``out`` (float32[M] on A's device) is
+    required: neither this wrapper nor the entry point allocates."""
+    import torch
+    M, N, lda = _check_matrix(A, "A", (torch.float16,))
+    c = make_config(PIPE_OP_ROWSUM, **cfg)
+    dev = _device(A, out, *c.buffers)
+    _check_vector(out, M, torch.float32, "out")
+    with torch.cuda.device(dev):
+        st = lib().pipe_rowsum_noalloc(_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c),
+                                       _stream(stream, dev))
+    _check(st, "pipe_rowsum_noalloc")
     return out
 
 

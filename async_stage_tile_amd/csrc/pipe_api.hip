@@ -51,6 +51,30 @@ pipe_status_t library_status_word(uint32_t** out) {
   return PIPE_OK;
 }
 
+// The row sum's workspace for callers that cannot allocate
+// (pipe_rowsum_noalloc): one fixed buffer per device, held until the process
+// ends. In host code `scratch` names a host-side stand-in, not the device
+// buffer: its device address comes from hipGetSymbolAddress, once per device
+// with that device current, and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[PIPE_ROWSUM_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+pipe_status_t library_scratch(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PIPE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PIPE_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return PIPE_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -396,6 +420,61 @@ pipe_status_t launch_rowsum(const pipe_config_t& c, const StreamGeom& g,
   return hip_status(launch_stream_op(kOpRowsum, c, g, *p, st));
 }
 
+// pipe_rowsum and pipe_rowsum_noalloc: the caller's workspace, or (use_scratch)
+// this device's library buffer, which calls no allocator.
+pipe_status_t rowsum_call(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
+                          const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,
+                          bool use_scratch, void* stream) {
+  const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
+  pipe_status_t s = check_stream_cfg(c);
+  if (s != PIPE_OK) return s;
+  if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // always row strips
+  if (M < 0 || N < 0 || lda < N) return PIPE_ERR_SHAPE;
+  if (N % 8 != 0 || !extent_fits(M, lda, 2)) return PIPE_ERR_SHAPE;
+  if (M == 0) return PIPE_OK;
+  if (out == nullptr) return PIPE_ERR_NULL;
+  if (!aligned4(out)) return PIPE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(launch_fill_f32(out, M, 1, 1, 0.f, st));
+  if (A == nullptr) return PIPE_ERR_NULL;
+  if (!aligned16(A) || (lda % 8)) return PIPE_ERR_ALIGN;
+  const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
+  if (unified) {
+    s = check_unified(c, M, N, false);
+    if (s != PIPE_OK) return s;
+  }
+  StreamGeom g;
+  s = stream_geometry(M, N, c, true, true, &g);
+  if (s != PIPE_OK) return s;
+  const RowsumWorkspace ws = rowsum_workspace(g, M);
+  if (use_scratch) {
+    if (ws.bytes > PIPE_ROWSUM_SCRATCH_BYTES) return PIPE_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+  } else if (ws.bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < ws.bytes) return PIPE_ERR_WORKSPACE;
+    if (!aligned4(workspace)) return PIPE_ERR_ALIGN;
+  }
+  StreamParams p{};
+  fill_stream_params(c, g, true, &p);
+  p.src = static_cast<const uint8_t*>(A);
+  p.dst = nullptr;
+  p.checksums = nullptr;
+  p.ld_src = lda * 2;
+  p.ld_dst = 0;
+  p.M = M;
+  p.N = N;
+  s = resolve_status(c, &p.status);
+  if (s != PIPE_OK) return s;
+  if (use_scratch && ws.bytes > 0) {
+    uint8_t* buf = nullptr;
+    s = library_scratch(&buf);
+    if (s != PIPE_OK) return s;
+    workspace = buf;
+  }
+  return launch_rowsum(c, g, ws, static_cast<uint8_t*>(workspace), out, &p, st);
+}
+
 // Address of the kernel that `launch` would launch, without launching it.
 template <class F>
 pipe_status_t record_kernel(F launch, const void** fn) {
@@ -493,44 +572,12 @@ pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_confi
 pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
                           const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
-  pipe_status_t s = check_stream_cfg(c);
-  if (s != PIPE_OK) return s;
-  if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // always row strips
-  if (M < 0 || N < 0 || lda < N) return PIPE_ERR_SHAPE;
-  if (N % 8 != 0 || !extent_fits(M, lda, 2)) return PIPE_ERR_SHAPE;
-  if (M == 0) return PIPE_OK;
-  if (out == nullptr) return PIPE_ERR_NULL;
-  if (!aligned4(out)) return PIPE_ERR_ALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (N == 0) return hip_status(launch_fill_f32(out, M, 1, 1, 0.f, st));
-  if (A == nullptr) return PIPE_ERR_NULL;
-  if (!aligned16(A) || (lda % 8)) return PIPE_ERR_ALIGN;
-  const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
-  if (unified) {
-    s = check_unified(c, M, N, false);
-    if (s != PIPE_OK) return s;
-  }
-  StreamGeom g;
-  s = stream_geometry(M, N, c, true, true, &g);
-  if (s != PIPE_OK) return s;
-  const RowsumWorkspace ws = rowsum_workspace(g, M);
-  if (ws.bytes > 0) {
-    if (workspace == nullptr || workspace_bytes < ws.bytes) return PIPE_ERR_WORKSPACE;
-    if (!aligned4(workspace)) return PIPE_ERR_ALIGN;
-  }
-  StreamParams p{};
-  fill_stream_params(c, g, true, &p);
-  p.src = static_cast<const uint8_t*>(A);
-  p.dst = nullptr;
-  p.checksums = nullptr;
-  p.ld_src = lda * 2;
-  p.ld_dst = 0;
-  p.M = M;
-  p.N = N;
-  s = resolve_status(c, &p.status);
-  if (s != PIPE_OK) return s;
-  return launch_rowsum(c, g, ws, static_cast<uint8_t*>(workspace), out, &p, st);
+  return rowsum_call(A, out, M, N, lda, cfg, workspace, workspace_bytes, false, stream);
+}
+
+pipe_status_t pipe_rowsum_noalloc(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
+                                  const pipe_config_t* cfg, void* stream) {
+  return rowsum_call(A, out, M, N, lda, cfg, nullptr, 0, true, stream);
 }
 
 pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t M, int64_t N,

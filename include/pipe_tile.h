@@ -262,6 +262,24 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
                           const pipe_config_t* cfg, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: pipe_rowsum
+ * with its workspace in a buffer the library owns (PIPE_ROWSUM_SCRATCH_BYTES of
+ * static device memory on each device it runs on, held until the process
+ * ends) instead of a caller's. Same kernels and bit-identical results as
+ * pipe_rowsum; the caller still passes A and out. It allocates nothing, with
+ * no allocating runtime call: the buffer's device address is looked up once
+ * per device (hipGetSymbolAddress) on the first call there. A shape whose
+ * pipe_rowsum_workspace_bytes exceeds PIPE_ROWSUM_SCRATCH_BYTES returns
+ * PIPE_ERR_WORKSPACE before anything is enqueued (a smaller cfg->split needs
+ * less). Every call on one device shares that device's buffer and finds the
+ * previous call's contents there; each call zeroes what must start at zero
+ * (the strip tickets) itself. Calls that overlap on one device -- on two
+ * streams, or from two host threads -- race on the buffer: serialise them. */
+#define PIPE_ROWSUM_SCRATCH_BYTES (1u << 20)
+pipe_status_t pipe_rowsum_noalloc(const void* A, float* out, int64_t M, int64_t N, int64_t lda,
+                                  const pipe_config_t* cfg, void* stream);
+
 /* GEMM mainloop ("chapter_async_barriers", section 常见的同步规则: a stage
  * whose copies have all landed is handed to the matrix-multiply consumers;
  * "cute（12）async_pipeline" ring): C = A * B with bf16 A (M x K, row-major) and B (K x N,

@@ -21,10 +21,30 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = pt.lib()
     declared = _declared()
-    assert len(declared) == 10
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(L, name), name
     assert sorted(pt.exported_symbols()) == declared
+
+
+def test_rowsum_noalloc_validation_needs_no_gpu():
+    """The no-allocation row sum checks everything, including that the shape's
+    workspace fits the library buffer, before any HIP call."""
+    L = pt.lib()
+    c = pt.make_config(pt.PIPE_OP_ROWSUM, split=8)
+    need = ctypes.c_size_t()
+    assert L.pipe_rowsum_workspace_bytes(65536, 4096, ctypes.byref(c), ctypes.byref(need)) == 0
+    assert need.value > pt.PIPE_ROWSUM_SCRATCH_BYTES
+    assert L.pipe_rowsum_noalloc(FAKE, FAKE, 65536, 4096, 4096, ctypes.byref(c), None) \
+        == pt.PIPE_ERR_WORKSPACE
+    assert L.pipe_rowsum_noalloc(FAKE, FAKE, 0, 4096, 4096, ctypes.byref(c), None) == pt.PIPE_OK
+    assert L.pipe_rowsum_noalloc(FAKE, None, 64, 4096, 4096, ctypes.byref(c), None) \
+        == pt.PIPE_ERR_NULL
+    assert L.pipe_rowsum_noalloc(FAKE, FAKE, 64, 4090, 4096, ctypes.byref(c), None) \
+        == pt.PIPE_ERR_SHAPE
+    bad = pt.make_config(pt.PIPE_OP_ROWSUM, stages=9)
+    assert L.pipe_rowsum_noalloc(FAKE, FAKE, 64, 4096, 4096, ctypes.byref(bad), None) \
+        == pt.PIPE_ERR_STAGES
 
 
 def test_version_and_status_strings():
