@@ -245,6 +245,18 @@ def _stream(stream=None, device=None):
     return ctypes.c_void_p(int(s.cuda_stream))
 
 
+def _hold_for(stream, device, *tensors):
+    """Tensors this wrapper allocated, used by work enqueued on `stream`: when
+    that is not the device's current stream, tell the caching allocator, so that
+    their memory is not handed out again before that stream's work is done."""
+    import torch
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def matrix_geometry(shape, strides, name="matrix"):
     """(rows, cols, row pitch in elements) of a 2-D row-major view, or
     ValueError. Columns must be adjacent (unit stride) and rows must not
@@ -280,8 +292,10 @@ def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):
     """Copy a 16-bit matrix through the tile ring; optionally per-tile code sums."""
     import torch
     M, N, ld_src = _check_matrix(src, "src", (torch.float16, torch.bfloat16, torch.int16))
+    made = []
     if dst is None:
         dst = torch.empty_like(src, memory_format=torch.contiguous_format)
+        made.append(dst)
     Md, Nd, ld_dst = _check_matrix(dst, "dst", (src.dtype,))
     if (Md, Nd) != (M, N):
         raise ValueError("dst shape differs from src")
@@ -292,10 +306,12 @@ def pipe_tile_copy(src, dst=None, checksums=False, stream=None, **cfg):
         tm, tn = max(1, c.tile_m), max(1, c.tile_n)
         chk = torch.empty(((M + tm - 1) // tm) * ((N + tn - 1) // tn), dtype=torch.int32,
                           device=dev)
+        made.append(chk)
     with torch.cuda.device(dev):
         st = lib().pipe_tile_copy(_ptr(src), _ptr(dst), M, N, ld_src, ld_dst, ctypes.byref(c),
                                   _ptr(chk), _stream(stream, dev))
     _check(st, "pipe_tile_copy")
+    _hold_for(stream, dev, *made)
     return (dst, chk) if checksums else dst
 
 
@@ -311,11 +327,14 @@ def pipe_rowsum(A, out=None, workspace=None, stream=None, **cfg):
     """fp32 row sums of an fp16 matrix streamed through the tile ring."""
     import torch
     M, N, lda = _check_matrix(A, "A", (torch.float16,))
+    made = []
     if out is None:
         out = torch.empty(M, dtype=torch.float32, device=A.device)
+        made.append(out)
     need = pipe_rowsum_workspace_bytes(M, N, **cfg)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+        made.append(workspace)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = make_config(PIPE_OP_ROWSUM, **cfg)
     dev = _device(A, out, workspace, *c.buffers)
@@ -326,6 +345,7 @@ def pipe_rowsum(A, out=None, workspace=None, stream=None, **cfg):
         st = lib().pipe_rowsum(_ptr(A), _ptr(out), M, N, lda, ctypes.byref(c), _ptr(workspace),
                                wbytes, _stream(stream, dev))
     _check(st, "pipe_rowsum")
+    _hold_for(stream, dev, *made)
     return out
 
 
@@ -390,8 +410,9 @@ def pipe_gemm_mainloop(A, B, C=None, stream=None, out_dtype=None, **cfg):
     K2, N, ldb, b_col = _gemm_b(B)
     if K2 != K:
         raise ValueError("inner dimensions differ")
+    made = None
     if C is None:
-        C = torch.empty((M, N), dtype=out_dtype or torch.float32, device=A.device)
+        C = made = torch.empty((M, N), dtype=out_dtype or torch.float32, device=A.device)
     Mc, Nc, ldc = _check_matrix(C, "C", (torch.float32, torch.bfloat16))
     if (Mc, Nc) != (M, N):
         raise ValueError("C shape mismatch")
@@ -401,6 +422,7 @@ def pipe_gemm_mainloop(A, B, C=None, stream=None, out_dtype=None, **cfg):
         st = lib().pipe_gemm_mainloop(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                       ctypes.byref(c), _stream(stream, dev))
     _check(st, "pipe_gemm_mainloop")
+    _hold_for(stream, dev, made)
     return C
 
 

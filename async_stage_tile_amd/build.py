@@ -1,10 +1,9 @@
-"""Build the HIP libraries for gfx950 with hipcc, in-tree.
+"""Build the tile-stream library for gfx950 with hipcc, in-tree.
 
-libpipetile.so  -- the tile stream: all kernels + the C ABI of include/pipe_tile.h.
-libpipeceil.so  -- context-only streaming kernels of include/pipe_ceiling.h.
+libpipetile.so -- the tile stream: all kernels + the C ABI of include/pipe_tile.h.
 
 Every translation unit compiles to its own object, in parallel; the stream
-kernel source is compiled once per group of stage counts. Then each library
+kernel source is compiled once per group of stage counts. Then the library
 is linked and moved into place atomically.
 
 Usage: python -m async_stage_tile_amd.build  (or build() from Python).
@@ -22,7 +21,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpipetile.so")
-CEIL_LIB = os.path.join(PKG, "libpipeceil.so")
 ARCH = "gfx950"
 
 # (source, object, extra defines)
@@ -36,7 +34,6 @@ UNITS = [
     ("pipe_unified.hip", "pipe_unified.o", []),
     ("pipe_gemm.hip", "pipe_gemm.o", []),
 ]
-CEIL_UNITS = [("ceiling.hip", "ceiling.o", [])]
 # Kept for callers that list the tile-stream sources.
 SOURCES = sorted({u[0] for u in UNITS})
 
@@ -81,7 +78,7 @@ def _link(units: list, out: str, verbose: bool) -> None:
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    units = UNITS + CEIL_UNITS
+    units = UNITS
     jobs = jobs or min(len(units), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_run, compile_command(s, os.path.join(OBJ, o), d), verbose)
@@ -89,7 +86,6 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         for f in futs:
             f.result()
     _link(UNITS, LIB, verbose)
-    _link(CEIL_UNITS, CEIL_LIB, verbose)
     return LIB
 
 

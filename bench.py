@@ -363,6 +363,48 @@ def bench_copy(stages, steps, warmup, stats=False, **cfg):
 _ROWSUM_BUF = {}
 
 
+SAMPLE_ROWS = 64
+
+
+def _sample_rows(n, seed):
+    import numpy as np
+    return np.sort(np.random.default_rng(seed).choice(n, SAMPLE_ROWS, replace=False))
+
+
+def _within(got, ref, rel):
+    """max |got - ref| / max(|ref|, rms(ref)) over the sample, and whether it is
+    within `rel` (the tolerance the parity tests use)."""
+    import torch
+    scale = torch.maximum(ref.abs(), ref.pow(2).mean().sqrt())
+    err = float(((got - ref).abs() / scale).max())
+    return err, bool(err <= rel)
+
+
+def rowsum_check(A, out, st):
+    """After the timed launches: the status word is clear, and 64 sampled rows
+    match a float64 torch sum of the same rows within 1e-3 (a plain reduction
+    on the host, independent of the kernels)."""
+    import torch
+    torch.cuda.synchronize()
+    status = int(st.item())
+    rows = torch.as_tensor(_sample_rows(A.shape[0], 5))
+    ref = A[rows.to(A.device)].cpu().double().sum(dim=1)
+    err, ok = _within(out[rows.to(out.device)].cpu().double(), ref, 1e-3)
+    return {"status": status, "sample_max_rel_err": err, "ok": ok and status == 0}
+
+
+def gemm_check(A, B, C, st):
+    """After the timed launches: the status word is clear, and 64 sampled rows
+    of C match a float64 torch product of the same rows within 1e-2."""
+    import torch
+    torch.cuda.synchronize()
+    status = int(st.item())
+    rows = torch.as_tensor(_sample_rows(A.shape[0], 9)).to(A.device)
+    ref = A[rows].cpu().double() @ B.cpu().double()
+    err, ok = _within(C[rows].cpu().double(), ref, 1e-2)
+    return {"status": status, "sample_max_rel_err": err, "ok": ok and status == 0}
+
+
 def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
     """The library's default row-sum configuration, with any overrides."""
     import torch
@@ -376,13 +418,15 @@ def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
     kw = dict(cfg)
     if stages is not None:
         kw["stages"] = stages
-    out = torch.empty(ROWSUM_M, dtype=torch.float32, device="cuda")
+    out = torch.full((ROWSUM_M,), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(1, pt.pipe_rowsum_workspace_bytes(ROWSUM_M, ROWSUM_N, **kw)),
                      dtype=torch.uint8, device="cuda")
-    fn = pt.rowsum_launcher(A, out, ws, **kw)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fn = pt.rowsum_launcher(A, out, ws, status=st, **kw)
     wall, kern = timed_launches(fn, steps, warmup)
     nbytes = ROWSUM_M * ROWSUM_N * 2 + ROWSUM_M * 4
     timing = hot_cold(fn, nbytes, max(steps, 20), 2) if stats else None
+    check = rowsum_check(A, out, st)
     q = pt.pipe_query_kernel(pt.PIPE_OP_ROWSUM, ROWSUM_M, ROWSUM_N, **kw)
     c = pt.make_config(pt.PIPE_OP_ROWSUM, **kw)
     r = {"tile": f"{c.tile_m}x{c.tile_n}", "stages": c.stages, "producer_waves": c.producer_waves,
@@ -390,7 +434,8 @@ def bench_rowsum(steps, warmup, stages=None, stats=False, **cfg):
          "grid": q["grid"], "wall_ms": wall, "kernel_ms": kern, "bytes": nbytes,
          "gbs": nbytes / (wall * 1e-3) / 1e9, "kernel_gbs": nbytes / (kern * 1e-3) / 1e9,
          "resources": kernel_resources(pt.PIPE_OP_ROWSUM, ROWSUM_M, ROWSUM_N, 0, q["grid"],
-                                       q["threads"], **kw)}
+                                       q["threads"], **kw),
+         **check}
     if timing:
         r["per_launch"] = timing
     return r
@@ -411,15 +456,17 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colma
     B = synth.uniform((n, n), torch.bfloat16, seed=42, stream=1, device="cuda")
     if b_colmajor:  # the same values, stored column-major (B[k][n] at n * K + k)
         B = B.t().contiguous().t()
-    C = torch.empty((n, n), dtype=out_dtype or torch.float32, device="cuda")
+    C = torch.full((n, n), float("nan"), dtype=out_dtype or torch.float32, device="cuda")
     kw = dict(cfg)
     if stages is not None:
         kw["stages"] = stages
-    fn = pt.gemm_launcher(A, B, C, **kw)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fn = pt.gemm_launcher(A, B, C, status=st, **kw)
     if settle_s > 0:
         run_for(fn, settle_s)
     wall, kern = timed_launches(fn, steps, warmup)
     med, mn = launch_stats(fn, max(steps, 20), 0)
+    check = gemm_check(A, B, C, st)
     flops = 2.0 * n * n * n
     c = pt._gemm_config(C, kw, b_colmajor)
     gcfg = {f: getattr(c, f) for f in ("stages", "producer_waves", "consumer_waves", "tile_m",
@@ -435,7 +482,8 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colma
             "per_launch": {"median_ms": med, "min_ms": mn,
                            "median_tflops": flops / (med * 1e-3) / 1e12},
             "resources": kernel_resources(pt.PIPE_OP_GEMM, n, n, n, q["grid"], q["threads"],
-                                          **gcfg)}
+                                          **gcfg),
+            **check}
 
 
 def bench_small(reps, warmup):
@@ -512,7 +560,7 @@ def bench_ceilings(steps, warmup):
     and for a 1 GiB read: no LDS ring, no tiles."""
     import torch
 
-    from async_stage_tile_amd import ceiling
+    import ceilings as ceiling
     n = 512 << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -552,7 +600,7 @@ def lds_ceilings(steps, warmup, grid=512):
     half is timed over its own loop (waves 0 and 4 record their cycles)."""
     import torch
 
-    from async_stage_tile_amd import ceiling
+    import ceilings as ceiling
     src = torch.zeros(65536 + 1024, dtype=torch.uint8, device="cuda")
     fold = torch.zeros(grid * 512, dtype=torch.int32, device="cuda")
     clocks = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
@@ -587,7 +635,7 @@ def strip_ceilings(steps, warmup):
     read-only and write-only rates: 2 / (1 / read + 1 / write)."""
     import torch
 
-    from async_stage_tile_amd import ceiling
+    import ceilings as ceiling
     src, dst = copy_buffers()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     nbytes = src.numel() * src.element_size()
@@ -680,6 +728,19 @@ def cpu_oracle_extras(copy_rows, rowsum_rows, gemm_rows):
     res["sample"] = (f"copy {copy_rows}x{COPY_N} fp16, rowsum {rowsum_rows}x{ROWSUM_N} fp16, "
                      f"gemm {gemm_rows}x{GEMM_N} @ {GEMM_N}x{GEMM_N} bf16 in fp64")
     return res
+
+
+def correctness_flags(obj):
+    """Every "ok", "bit_exact" and "checksums_exact" value in a record tree."""
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            if k in ("ok", "bit_exact", "checksums_exact"):
+                yield bool(v)
+            else:
+                yield from correctness_flags(v)
+    elif isinstance(obj, list):
+        for v in obj:
+            yield from correctness_flags(v)
 
 
 def main():
@@ -832,22 +893,42 @@ def main():
             k: w[k] for k in ("tile", "stages", "producer_waves", "consumer_waves", "flags",
                               "split", "grid", "kernel_ms", "gbs", "kernel_gbs", "bit_exact")}
         log(f"[bench] copy, register engine: {w['gbs']:.1f} GB/s")
-        u = bench_copy(2, max(3, args.steps // 2), args.warmup, consumer_waves=2,
-                       flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
-                       pt.PIPE_FLAG_XCD_REMAP)
-        extras["copy_unified"] = {k: u[k] for k in ("stages", "consumer_waves", "flags",
-                                                    "kernel_ms", "gbs", "bit_exact")}
-        log(f"[bench] unified copy: {u['gbs']:.1f} GB/s")
+        # Specialised ring against the unified (non-specialised) pipeline over the
+        # same ring depths S = 1..4.
+        uflags = pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_XCD_REMAP
+        keys = ("stages", "consumer_waves", "flags", "lds_bytes", "kernel_ms", "gbs",
+                "kernel_gbs", "bit_exact")
+        n1 = {"specialised": [{k: r[k] for k in ("stages", "lds_bytes", "kernel_ms", "gbs",
+                                                  "bit_exact")}
+                              for r in extras.get("copy_stage_sweep", []) if r["stages"] <= 4],
+              "unified": []}
+        for s_ in (1, 2, 3, 4):
+            u = bench_copy(s_, max(3, args.steps // 2), args.warmup, consumer_waves=2,
+                           flags=uflags)
+            n1["unified"].append({k: u[k] for k in keys})
+            log(f"[bench] unified copy S={s_}: {u['gbs']:.1f} GB/s (kernel {u['kernel_gbs']:.1f})")
+        extras["copy_specialised_vs_unified"] = n1
         _COPY_BUF.clear()
         torch.cuda.empty_cache()
         r = bench_rowsum(max(3, args.steps // 2), args.warmup, stats=True)
         log(f"[bench] rowsum: {r['gbs']:.1f} GB/s")
         extras["rowsum_8192x65536_fp16"] = r
-        r = bench_rowsum(max(3, args.steps // 2), args.warmup, stages=2, consumer_waves=2, split=16,
-                         flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_NONTEMPORAL |
-                         pt.PIPE_FLAG_XCD_REMAP)
-        log(f"[bench] unified rowsum: {r['gbs']:.1f} GB/s")
-        extras["rowsum_unified"] = r
+        keys = ("stages", "consumer_waves", "split", "flags", "kernel_ms", "gbs", "kernel_gbs",
+                "ok")
+        n1 = {"specialised": [], "unified": []}
+        for s_ in (1, 2, 3, 4):
+            r = bench_rowsum(max(3, args.steps // 2), args.warmup, stages=s_)
+            n1["specialised"].append({k: r[k] for k in keys})
+            r = bench_rowsum(max(3, args.steps // 2), args.warmup, stages=s_, consumer_waves=2,
+                             split=16, flags=uflags)
+            n1["unified"].append({k: r[k] for k in keys})
+            log(f"[bench] rowsum S={s_}: specialised {n1['specialised'][-1]['kernel_gbs']:.1f}, "
+                f"unified {r['kernel_gbs']:.1f} GB/s (kernel)")
+        for side in n1.values():
+            for r in side:
+                r["lds_bytes"] = r["stages"] * 16384 + (0 if r["flags"] & pt.PIPE_FLAG_UNIFIED
+                                                        else r["stages"] * 4 * 7)
+        extras["rowsum_specialised_vs_unified"] = n1
         r = bench_rowsum(max(3, args.steps // 2), args.warmup, **REGS_ROWSUM)
         log(f"[bench] rowsum, register engine: {r['gbs']:.1f} GB/s")
         extras["rowsum_register_engine"] = r
@@ -860,12 +941,14 @@ def main():
         extras["rowsum_wide_tiles"] = wide
         _ROWSUM_BUF.clear()
         torch.cuda.empty_cache()
-        g = bench_gemm(max(3, args.steps // 2), args.warmup)
-        log(f"[bench] gemm: {g['tflops']:.1f} TFLOP/s")
-        extras["gemm_4096_bf16"] = g
+        # The GEMM workload as stated: 128 x 128 x 64 tiles through a three-stage
+        # ring; the library default (two stages, two workgroups per CU) beside it.
         g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=3)
         log(f"[bench] gemm, three-stage ring: {g['tflops']:.1f} TFLOP/s")
-        extras["gemm_4096_bf16_three_stage"] = g
+        extras["gemm_4096_bf16"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=2)
+        log(f"[bench] gemm, two-stage ring (library default): {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_two_stage"] = g
         g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=3, tile_m=256,
                        consumer_waves=8, producer_waves=4)
         log(f"[bench] gemm, 256 x 128 tiles, three-stage ring: {g['tflops']:.1f} TFLOP/s")
@@ -909,6 +992,8 @@ def main():
             extras["cpu_oracle"] = cpu_oracle_extras(2048, 256, 64)
             log(f"[bench] cpu oracle extras: {extras['cpu_oracle']}")
 
+    # Every timed record that carries a correctness check passed it.
+    checks = [head["bit_exact"]] + list(correctness_flags(extras))
     achieved = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
     kname = (f"void pipe::stream_kernel<{head['stages']}, {head['consumer_waves']}, "
              f"{head['producer_waves']}, 0, false, 64>(pipe::StreamParams)")
@@ -933,6 +1018,7 @@ def main():
                    "split": head["split"], "grid": head["grid"], "parallelism": "1 GPU"},
         "pct_of_peak": round(100.0 * head["gbs"] / PEAK_HBM_GBS, 2),
         "bit_exact": head["bit_exact"],
+        "ok": all(bool(c) for c in checks),
         "resources": head["resources"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -941,6 +1027,8 @@ def main():
         "extras": extras,
     }
     print(json.dumps(line), flush=True)
+    if not head["bit_exact"]:
+        sys.exit("the headline copy was not bit-exact (or its status word was set)")
 
 
 if __name__ == "__main__":

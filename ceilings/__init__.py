@@ -1,9 +1,11 @@
-"""ctypes binding of libpipeceil.so (include/pipe_ceiling.h).
+"""Benchmark support, not part of the tile-stream library: ctypes binding and
+build of libpipeceil.so (ceiling.hip, pipe_ceiling.h in this folder).
 
-Context-only HBM ceilings, timed beside the tile stream: plain grid-stride
-streaming copy and read kernels, the runtime's device-to-device copy, and
-plain kernels that walk column strips the way the tile stream does.
-They are a measurement aid and take no part in the tile stream.
+Context-only HBM and LDS ceilings, timed beside the tile stream by bench.py:
+plain grid-stride streaming copy and read kernels, the runtime's
+device-to-device copy, plain kernels that walk column strips the way the tile
+stream does, and LDS rates per instruction kind. They take no part in the
+tile stream, and the library (libpipetile.so) neither builds nor loads them.
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built: run python -m async_stage_tile_amd.build")
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m ceilings")
         L = ctypes.CDLL(LIB_PATH)
         vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         L.ceil_copy.argtypes = [vp, vp, sz, i, i, i, vp]
@@ -107,3 +109,24 @@ def lds_bytes(op: int, grid: int, iters: int) -> int:
     (for op 4, half of them by DMA and half by reads)."""
     _, per_instr, waves = LDS_OPS[op]
     return grid * waves * iters * 8 * per_instr
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ceiling.hip for gfx950 into libpipeceil.so in this folder."""
+    import subprocess
+    import sys
+
+    from async_stage_tile_amd.build import ARCH, hipcc
+    here = os.path.dirname(os.path.abspath(__file__))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", here, os.path.join(here, "ceiling.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: ceiling.hip")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH

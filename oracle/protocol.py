@@ -47,18 +47,13 @@ class PipelineState:
         return self
 
     def advance(self, n: int) -> "PipelineState":
-        """n steps at once.
-
-        Fewer than ``stages`` steps flip the phase iff they cross the end of
-        the ring; ``stages`` or more steps flip it iff the number of ring
-        boundaries crossed, (index + n) // stages, is odd.
-        """
-        S = self.stages
-        if n < S and self.index + n >= S:
-            self.phase ^= 1
-        if n >= S and ((self.index + n) // S) % 2 == 1:
-            self.phase ^= 1
-        self.index = (self.index + n) % S
+        """n steps at once ("cute（12）async_pipeline" 6.1), as n repeated
+        increments: every wrap from the last slot to slot 0 flips the phase, and
+        n steps from slot ``index`` wrap (index + n) // stages times, so the
+        phase flips when that number is odd."""
+        wraps = (self.index + n) // self.stages
+        self.phase ^= wraps & 1
+        self.index = (self.index + n) % self.stages
         self.count += n
         return self
 

@@ -34,7 +34,7 @@ def test_short_bench_prints_the_contract_line():
         assert key in line, key
     assert line["n_gpus"] == 1 and line["steps"] == 5 and line["warmup"] == 2
     assert line["value"] > 0 and line["unit"] == "GB/s" and line["higher_is_better"] is True
-    assert line["bit_exact"] is True
+    assert line["bit_exact"] is True and line["ok"] is True
     assert "workload" in line["config"]
     roof = line["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0

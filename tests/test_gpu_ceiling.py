@@ -1,4 +1,4 @@
-"""The context-only ceiling kernels (include/pipe_ceiling.h) move the bytes
+"""The context-only ceiling kernels (ceilings/pipe_ceiling.h) move the bytes
 they claim to move: they are timed beside the tile stream, so a kernel that
 skipped work would inflate the ceiling."""
 import pytest
@@ -9,7 +9,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def ceiling():
-    from async_stage_tile_amd import ceiling as c
+    import ceilings as c
     c.lib()
     return c
 
