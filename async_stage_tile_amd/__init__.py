@@ -61,6 +61,7 @@ PIPE_FLAG_PRODUCER_VGPR = 0x8000
 PIPE_FLAG_DEBUG_CHECKS = 0x10000
 PIPE_FLAG_TEST_JITTER = 0x20000
 PIPE_FLAG_TEST_EARLY_RELEASE = 0x40000
+PIPE_FLAG_GROUP_LOADS = 0x80000
 
 PIPE_STATUS_TIMEOUT_PRODUCER = 0x1
 PIPE_STATUS_TIMEOUT_CONSUMER = 0x2

@@ -30,6 +30,7 @@ constexpr uint32_t kKnownFlags = PIPE_FLAG_TRACE | PIPE_FLAG_ROW_STRIPS | PIPE_F
                                  PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE |
                                  PIPE_FLAG_GEMM_B_COLMAJOR | PIPE_FLAG_STRIP_GROUPS |
                                  PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS |
+                                 PIPE_FLAG_GROUP_LOADS |
                                  PIPE_FLAG_TEST_JITTER | PIPE_FLAG_TEST_EARLY_RELEASE |
                                  PIPE_FLAG_TEST_START_PHASE0 | PIPE_FLAG_TEST_NO_RELEASE;
 
@@ -151,6 +152,13 @@ pipe_status_t check_stream_cfg(const pipe_config_t& c) {
   if ((c.flags & (PIPE_FLAG_TEST_JITTER | PIPE_FLAG_TEST_EARLY_RELEASE)) &&
       !(c.flags & PIPE_FLAG_DEBUG_CHECKS))
     return PIPE_ERR_CONFIG;
+  if (c.flags & PIPE_FLAG_GROUP_LOADS) {
+    if (!(c.flags & PIPE_FLAG_STRIP_GROUPS) ||
+        (c.flags & (PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS | PIPE_FLAG_UNIFIED |
+                    PIPE_FLAG_ROW_STRIPS)) ||
+        !group_load_shape_supported(c.stages, cw, pw))
+      return PIPE_ERR_CONFIG;
+  }
   if (c.flags & PIPE_FLAG_DEBUG_CHECKS) {
     if ((c.flags & PIPE_FLAG_UNIFIED) || c.tile_m != 128 || c.tile_n != 64 ||
         !debug_shape_supported(c.stages, cw, pw))
@@ -305,6 +313,9 @@ hipError_t launch_stream_op(int op, const pipe_config_t& c, const StreamGeom& g,
   if (c.flags & PIPE_FLAG_DEBUG_CHECKS)
     return launch_stream_debug(op, c.stages, c.consumer_waves, c.producer_waves, g.grid, p,
                                stream);
+  if (g.group == 4 && (c.flags & PIPE_FLAG_GROUP_LOADS))
+    return launch_stream_group_load(c.stages, c.consumer_waves, c.producer_waves, g.grid, p,
+                                    stream);
   if (g.group > 1)
     return launch_stream_group(c.stages, c.consumer_waves, c.producer_waves, g.group, g.grid, p,
                                stream);
@@ -334,6 +345,7 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
     return PIPE_ERR_CONFIG;
   if (c.split > 1) return PIPE_ERR_CONFIG;
   if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS |
+                 PIPE_FLAG_GROUP_LOADS |
                  PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS | PIPE_FLAG_TEST_JITTER |
                  PIPE_FLAG_TEST_EARLY_RELEASE))
     return PIPE_ERR_CONFIG;
@@ -428,7 +440,8 @@ pipe_status_t rowsum_call(const void* A, float* out, int64_t M, int64_t N, int64
   const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
-  if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // always row strips
+  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_GROUP_LOADS))
+    return PIPE_ERR_CONFIG;  // always row strips; grouped loads are the copy's
   if (M < 0 || N < 0 || lda < N) return PIPE_ERR_SHAPE;
   if (N % 8 != 0 || !extent_fits(M, lda, 2)) return PIPE_ERR_SHAPE;
   if (M == 0) return PIPE_OK;
@@ -558,7 +571,7 @@ pipe_status_t pipe_rowsum_workspace_bytes(int64_t M, int64_t N, const pipe_confi
   const pipe_config_t c = cfg ? *cfg : defaults(PIPE_OP_ROWSUM);
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
-  if (c.flags & PIPE_FLAG_ROW_STRIPS) return PIPE_ERR_CONFIG;  // as pipe_rowsum
+  if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_GROUP_LOADS)) return PIPE_ERR_CONFIG;  // as pipe_rowsum
   if (M < 0 || N < 0 || N % 8 != 0) return PIPE_ERR_SHAPE;
   *bytes = 0;
   if (M == 0 || N == 0) return PIPE_OK;
@@ -638,7 +651,8 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
   pipe_status_t s = check_stream_cfg(c);
   if (s != PIPE_OK) return s;
   const bool rowsum = op == PIPE_OP_ROWSUM;
-  if (rowsum && (c.flags & PIPE_FLAG_ROW_STRIPS)) return PIPE_ERR_CONFIG;  // always row strips
+  if (rowsum && (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_GROUP_LOADS)))
+    return PIPE_ERR_CONFIG;  // as pipe_rowsum
   if (M < 0 || N < 0 || N % 8 || !extent_fits(M, N, 2)) return PIPE_ERR_SHAPE;
   const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);
   const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
@@ -684,7 +698,8 @@ pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int6
     s = check_stream_cfg(c);
     if (s != PIPE_OK) return s;
     const bool rowsum = op == PIPE_OP_ROWSUM;
-    if (rowsum && (c.flags & PIPE_FLAG_ROW_STRIPS)) return PIPE_ERR_CONFIG;
+    if (rowsum && (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_GROUP_LOADS)))
+      return PIPE_ERR_CONFIG;
     if (M < 0 || N < 0 || N % 8 != 0 || !extent_fits(M, N, 2)) return PIPE_ERR_SHAPE;
     if (M == 0 || N == 0) return PIPE_ERR_SHAPE;
     const bool row_strips = rowsum || (c.flags & PIPE_FLAG_ROW_STRIPS);

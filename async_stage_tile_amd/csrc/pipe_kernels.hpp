@@ -63,6 +63,13 @@ constexpr bool group_shape_supported(int S, int C, int PW, int G) {
   return (G == 2 || G == 4) && G <= S && S <= 8 && (C == 4 || C == 8) && (PW == 2 || PW == 4);
 }
 
+// Grouped loads (strips of 4 tile columns whose producers fill the 4 slots of a
+// tile row together): S in {4, 8} (one or two interleaved groups of 4 slots),
+// C in {4, 8}, PW in {2, 4}.
+constexpr bool group_load_shape_supported(int S, int C, int PW) {
+  return (S == 4 || S == 8) && (C == 4 || C == 8) && (PW == 2 || PW == 4);
+}
+
 // Register producer engine (128 x 64 tiles): S = 1..4, C in {3, 4}, PW in {1, 4}.
 constexpr bool regs_shape_supported(int S, int C, int PW) {
   return S >= 1 && S <= 4 && (C == 3 || C == 4) && (PW == 1 || PW == 4);
@@ -97,6 +104,14 @@ hipError_t launch_stream_group(int stages, int consumers, int producers, int gro
 template <int S>
 hipError_t launch_group_stages(int consumers, int producers, int group, int grid,
                                const StreamParams& p, hipStream_t stream);
+
+// Grouped loads: launch the kernel for (stages, consumers, producers);
+// hipErrorInvalidValue for a shape group_load_shape_supported rejects.
+hipError_t launch_stream_group_load(int stages, int consumers, int producers, int grid,
+                                    const StreamParams& p, hipStream_t stream);
+template <int S>
+hipError_t launch_group_load_stages(int consumers, int producers, int grid, const StreamParams& p,
+                                    hipStream_t stream);
 
 // Debug kernel: the DMA ring with its protocol checks (and optional jitter);
 // hipErrorInvalidValue for a shape debug_shape_supported rejects.

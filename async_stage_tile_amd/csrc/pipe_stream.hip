@@ -44,6 +44,8 @@
 //   stream_kernel        the ring above (every default copy and row sum);
 //   stream_group_kernel  copies down strips of G neighbouring tile columns,
 //                        whose consumers store a tile row of G tiles at once;
+//   stream_group_load_kernel  the same strips of 4 tile columns, whose
+//                        producers also load a tile row of the 4 tiles at once;
 //   stream_regs_kernel   producers that load into registers and write the
 //                        slots with ds_write_b128 instead of direct-to-LDS;
 //   stream_debug_kernel  the ring with its protocol checks compiled in.
@@ -738,6 +740,191 @@ __global__ void __launch_bounds__(64 * (PW + C)) stream_group_kernel(StreamParam
     group_consumer<S, C, PW, G>(p, lds, wave - PW);
 }
 
+
+// ---------------------------------------------------------------------------
+// Grouped loads (PIPE_FLAG_GROUP_LOADS; 128 x 64 tiles, strips of G = 4 tile
+// columns): the producer waits on the 4 consecutive slots that receive one
+// tile row of its strip, then fills all 4 with loads that each cover 2 rows x
+// 512 contiguous bytes -- the same 128-byte row piece of the 4 neighbouring
+// tiles -- and commits the 4 tiles together once those loads have landed.
+// Since one direct-to-LDS load writes 1 KiB of contiguous LDS, the 4 slots of
+// a group are interleaved: row r of the group's tile g lives at
+// slots[first] + r * 512 + g * 128 (its chunks XOR-swizzled as in every
+// slot), so a group is one 64 KiB region and S is 4 or 8 (one or two groups).
+// Consumers wait on the 4 slots, store 2 rows x 512 bytes per instruction
+// (reading 1 KiB of contiguous LDS) and release the 4. The commit lag is at
+// most S - 4 tiles, one group when S = 8: the bound that the protocol model
+// proves live for a producer and consumers that both take 4 slots at a time.
+// ---------------------------------------------------------------------------
+constexpr int kGroupTiles = 4;
+constexpr int kGroupRowBytes = kGroupTiles * kRowBytes;  // 512
+
+template <int S, int C, int PW>
+__device__ void group_load_producer(const StreamParams& p, StreamLds<S, C>& lds, int pw) {
+  using FullBar = StreamBar<kOpCopy, PW>;
+  using EmptyBar = StreamBar<kOpCopy, C>;
+  constexpr int G = kGroupTiles;
+  static_assert(S % G == 0, "whole groups of slots");
+  constexpr int kLoads = G * kBlocksPerTile / PW;  // loads per group per wave
+  // One group of lag when two fit the ring and (lag + 1) groups of loads fit
+  // the 63-entry vmcnt counter (4 producer waves: 16 loads per group each;
+  // with 2, 32 loads, so each group is committed as soon as it has landed).
+  constexpr int kLagFit = 63 / kLoads - 1;
+  constexpr int kLagGroups = (S / G - 1) < kLagFit ? (S / G - 1) : kLagFit;
+  static_assert((kLagGroups + 1) * kLoads <= 63, "vmcnt counts at most 63 outstanding loads");
+  const int lane = lane_id();
+  const int lr = lane >> 5;          // row within the load's 2 rows
+  const int lg = (lane >> 3) & 3;    // tile of the group
+  const int lpos = lane & 7;         // chunk position within the tile row
+  PipeState w = producer_start(S, p.start_phase);
+  int pending = 0;  // groups issued, not yet committed
+  int t = 0;
+  bool ok = true;
+  for (int it = blockIdx.x; ok && it < p.items; it += gridDim.x) {
+    const int item = item_index(p, it);
+    const int len = item_len(p, item);  // tile rows of the segment
+    for (int k = 0; k < len; ++k, t += G) {
+      // producer_acquire of the group's 4 slots, in ring order.
+      PipeState a = w;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!bar_wait<EmptyBar>(&lds.empty[a.index], a.phase, p.spin_limit)) {
+          ok = false;
+          break;
+        }
+        if (pw == 0) trace_record(p, t + j, 0, a, 0);
+        a.inc();
+      }
+      if (!ok) break;
+      int tr, tc0;
+      group_tile_coords<G>(p, item, k * G, tr, tc0);
+      const uint8_t* g = p.src + (int64_t)tr * kTileRows * p.ld_src + (int64_t)tc0 * kRowBytes;
+      const uint32_t base = uniform(lds_addr(&lds.slots[w.index][0]));
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int i = pw * kLoads + j;  // 1 KiB block i of the group: rows 2i, 2i + 1
+        const int r = 2 * i + lr;
+        const int c = swz(r, lpos, p.swz_shift);
+        const uint8_t* a2 = g + (int64_t)r * p.ld_src + lg * kRowBytes + c * kChunkBytes;
+        if (p.nt)
+          dma_block_nt(a2, base + i * kBlockBytes);
+        else
+          dma_block(a2, base + i * kBlockBytes);
+      }
+      ++pending;
+      // Commit the oldest group once kLagGroups younger ones are in flight.
+      if (pending > kLagGroups) {
+        wait_vmcnt_mul<kLoads>(pending - 1);
+        int oldest = w.index - (pending - 1) * G;
+        if (oldest < 0) oldest += S;
+#pragma unroll
+        for (int j = 0; j < G; ++j) FullBar::arrive(&lds.full[oldest + j]);
+        --pending;
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) w.inc();
+    }
+  }
+  while (pending > 0) {
+    wait_vmcnt_mul<kLoads>(pending - 1);
+    int oldest = w.index - pending * G;
+    if (oldest < 0) oldest += S;
+#pragma unroll
+    for (int j = 0; j < G; ++j) FullBar::arrive(&lds.full[oldest + j]);
+    --pending;
+  }
+  // producer_tail: S more empty phases, so every slot has been drained.
+  if (ok) {
+    for (int i = 0; i < S; ++i) {
+      if (!bar_wait<EmptyBar>(&lds.empty[w.index], w.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      w.inc();
+    }
+  }
+  wait_vmcnt<0>();
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutProducer);
+}
+
+template <int S, int C, int PW>
+__device__ void group_load_consumer(const StreamParams& p, StreamLds<S, C>& lds, int cw) {
+  using FullBar = StreamBar<kOpCopy, PW>;
+  using EmptyBar = StreamBar<kOpCopy, C>;
+  constexpr int G = kGroupTiles;
+  constexpr int kInstr = G * kBlocksPerTile;  // 1 KiB blocks per group
+  static_assert(kInstr % C == 0, "every wave stores the same share");
+  constexpr int NI = kInstr / C;
+  const int lane = lane_id();
+  const int lr = lane >> 5, lg = (lane >> 3) & 3, lpos = lane & 7;
+  PipeState rd = consumer_start(S);
+  int t = 0;
+  bool ok = true;
+  for (int it = blockIdx.x; ok && it < p.items; it += gridDim.x) {
+    const int item = item_index(p, it);
+    const int len = item_len(p, item);
+    for (int k = 0; k < len; ++k, t += G) {
+      // consumer_wait on the group's 4 slots, in ring order.
+      PipeState w = rd;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!bar_wait<FullBar>(&lds.full[w.index], w.phase, p.spin_limit)) {
+          ok = false;
+          break;
+        }
+        if (cw == 0) trace_record(p, t + j, 1, w, 1 + cw);
+        w.inc();
+      }
+      if (!ok) break;
+      int tr, tc0;
+      group_tile_coords<G>(p, item, k * G, tr, tc0);
+      const uint8_t* base = &lds.slots[rd.index][0];
+      uint8_t* gdst = p.dst + (int64_t)tr * kTileRows * p.ld_dst + (int64_t)(tc0 + lg) * kRowBytes;
+      uint4 v[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        v[i] = *reinterpret_cast<const uint4*>(base + (cw + i * C) * kBlockBytes +
+                                               lane * kChunkBytes);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = 2 * (cw + i * C) + lr;
+        const int c = swz(r, lpos, p.swz_shift);
+        uint8_t* gd = gdst + (int64_t)r * p.ld_dst + c * kChunkBytes;
+        if (p.nt) {
+          const u32x4 nv = {v[i].x, v[i].y, v[i].z, v[i].w};
+          __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(gd));
+        } else {
+          *reinterpret_cast<uint4*>(gd) = v[i];
+        }
+      }
+      wait_lgkmcnt0();
+      // consumer_release of the 4 slots, in ring order.
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!p.no_release) EmptyBar::arrive(&lds.empty[rd.index]);
+        rd.inc();
+      }
+    }
+  }
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
+}
+
+template <int S, int C, int PW>
+__global__ void __launch_bounds__(64 * (PW + C)) stream_group_load_kernel(StreamParams p) {
+  __shared__ StreamLds<S, C> lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  if (threadIdx.x < S) {
+    lds.full[threadIdx.x] = 0u;
+    lds.empty[threadIdx.x] = 0u;
+    lds.fin[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  if (wave < PW)
+    group_load_producer<S, C, PW>(p, lds, wave);
+  else
+    group_load_consumer<S, C, PW>(p, lds, wave - PW);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -817,6 +1004,24 @@ hipError_t launch_group_stages(int consumers, int producers, int group, int grid
   return hipErrorInvalidValue;
 }
 
+template <int S>
+hipError_t launch_group_load_stages(int consumers, int producers, int grid, const StreamParams& p,
+                                    hipStream_t stream) {
+  dim3 block(64 * (producers + consumers));
+#define PIPE_GROUP_LOAD_CASE(C, PW)                                                           \
+  if constexpr (group_load_shape_supported(S, C, PW)) {                                       \
+    if (consumers == C && producers == PW)                                                    \
+      return launch_or_record(stream_group_load_kernel<S, C, PW>, dim3(grid), block, stream,  \
+                              p);                                                             \
+  }
+  PIPE_GROUP_LOAD_CASE(4, 2)
+  PIPE_GROUP_LOAD_CASE(4, 4)
+  PIPE_GROUP_LOAD_CASE(8, 2)
+  PIPE_GROUP_LOAD_CASE(8, 4)
+#undef PIPE_GROUP_LOAD_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int S, int C, int PW>
 static hipError_t launch_debug_scp(int op, int grid, const StreamParams& p, hipStream_t stream) {
   if constexpr (!debug_shape_supported(S, C, PW)) {
@@ -885,6 +1090,8 @@ hipError_t launch_regs_stages(int op, int consumers, int producers, int grid,
                                               hipStream_t);                                 \
   template hipError_t launch_group_stages<S>(int, int, int, int, const StreamParams&,       \
                                              hipStream_t);                                 \
+  template hipError_t launch_group_load_stages<S>(int, int, int, const StreamParams&,        \
+                                                  hipStream_t);                            \
   template hipError_t launch_regs_stages<S>(int, int, int, int, const StreamParams&,        \
                                             hipStream_t);                                  \
   template hipError_t launch_debug_stages<S>(int, int, int, int, const StreamParams&,       \

@@ -41,6 +41,15 @@ hipError_t launch_stream_group(int stages, int consumers, int producers, int gro
   }
 }
 
+hipError_t launch_stream_group_load(int stages, int consumers, int producers, int grid,
+                                    const StreamParams& p, hipStream_t stream) {
+  switch (stages) {
+    case 4: return launch_group_load_stages<4>(consumers, producers, grid, p, stream);
+    case 8: return launch_group_load_stages<8>(consumers, producers, grid, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_stream_regs(int op, int stages, int consumers, int producers, int grid,
                               const StreamParams& p, hipStream_t stream) {
   switch (stages) {

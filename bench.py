@@ -83,6 +83,11 @@ WIDE_COPY = {
 # segments per strip, the best ring measured for it.
 _G = 0x4000
 GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _RM | _IL | _LZ | _G)
+# The same strips with grouped loads (PIPE_FLAG_GROUP_LOADS): producers fill the
+# 4 slots of a tile row with 2-row x 512-byte loads.
+_GL = 0x80000
+GROUP_LOAD_COPY = dict(stages=8, producer_waves=4, consumer_waves=8,
+                       flags=_NT | _RM | _IL | _LZ | _G | _GL)
 # The register producer engine (PIPE_FLAG_PRODUCER_VGPR): global_load_dwordx4
 # into registers, then ds_write_b128 into the slot.
 _V = 0x8000
@@ -759,6 +764,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--only", choices=["copy", "copy_32x256", "copy_64x128", "copy_grouped",
+                                       "copy_group_loads",
                                        "copy_regs", "copy_pitch", "rowsum", "rowsum_regs",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
                                        "gemm_bcol", "gemm_tile256", "ceiling", "calib"],
@@ -799,6 +805,11 @@ def main():
         cfg = dict(GROUPED_COPY)
         r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
         log(f"[bench] copy_grouped: {r}")
+        return
+    if args.only == "copy_group_loads":
+        cfg = dict(GROUP_LOAD_COPY)
+        r = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+        log(f"[bench] copy_group_loads: {r}")
         return
     if args.only == "copy_pitch":
         r = bench_copy_pitch(args.steps, args.warmup)
@@ -884,6 +895,14 @@ def main():
             "strip_tiles": 4,
             "kernel_pct_of_peak": round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)}
         log(f"[bench] copy, grouped strips: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
+        cfg = dict(GROUP_LOAD_COPY)
+        w = bench_copy(cfg.pop("stages"), args.steps, args.warmup, **cfg)
+        extras["copy_group_loads"] = {
+            **{k: w[k] for k in ("tile", "stages", "producer_waves", "consumer_waves", "flags",
+                                 "split", "grid", "kernel_ms", "gbs", "kernel_gbs", "bit_exact")},
+            "strip_tiles": 4, "load_shape": "2 rows x 512 B",
+            "kernel_pct_of_peak": round(100.0 * w["kernel_gbs"] / PEAK_HBM_GBS, 2)}
+        log(f"[bench] copy, grouped loads: {w['gbs']:.1f} GB/s (kernel {w['kernel_gbs']:.1f})")
         w = bench_copy_pitch(args.steps, args.warmup)
         extras["copy_pitch_32640"] = w
         log(f"[bench] copy, 16384 x 16320 (32 640-byte pitch): {w['gbs']:.1f} GB/s")

@@ -138,6 +138,16 @@ typedef enum {
                                           PIPE_ERR_CONFIG): consumers release each slot before
                                           reading it and then pause, so the producer refills
                                           it under them; the checks must report it */
+#define PIPE_FLAG_GROUP_LOADS 0x80000u /* copy, with STRIP_GROUPS, stages 4 or 8, producer_waves
+                                          2 or 4, consumer_waves 4 or 8 (else PIPE_ERR_CONFIG):
+                                          where the strips are 4 tile columns wide, the producers
+                                          also fill the 4 slots of a tile row together, with loads
+                                          of 2 rows x 512 contiguous bytes, and commit the 4 tiles
+                                          together (lag stages - 4). The 4 slots of a group are
+                                          then interleaved in LDS (row r of tile g at
+                                          r * 512 + g * 128 from the group's first slot). Where
+                                          the strips resolve to 2 or 1 tile columns the flag
+                                          changes nothing */
 #define PIPE_FLAG_TEST_START_PHASE0 0x100u /* test only: producer starts at phase 0 (the
                                               deadlock of the pages); must end in a timeout */
 #define PIPE_FLAG_TEST_NO_RELEASE 0x200u   /* test only: consumers never release; the

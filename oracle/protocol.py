@@ -213,15 +213,20 @@ class ProtocolResult:
     max_ahead: int
 
 
-def _producer_program(S, T, mode, lag, start_phase, tail, part=0, commits=True):
+def _producer_program(S, T, mode, lag, start_phase, tail, part=0, commits=True, pgroup=1):
     """The producer's instruction list.
 
     "tx" mode is fully static. In "landed" mode the commits are dynamic: after
-    issuing a tile the producer commits its oldest uncommitted tile while more
-    than ``lag`` are uncommitted ("commit_lag"), and at the end it commits all
+    issuing a tile the producer commits its oldest uncommitted tiles, oldest
+    first, while more than ``lag`` are uncommitted ("commit_lag"), and at the
+    end it commits all
     of them ("commit_all"); each commit waits until that tile's share landed.
     ``commits=False`` leaves every commit out (the omission that
     "cuda-features-10-pipelines" 4.10.2 warns starves the consumers).
+    With ``pgroup`` = G > 1 (landed mode) the producer takes G consecutive
+    stages at a time: it waits on all G empty barriers, then issues the G
+    tiles (one load may fill parts of all G slots), then applies the commit
+    rule. T must be a multiple of G.
     """
     ops = []
     cur = PipelineState(S, 0, start_phase, 0)
@@ -232,12 +237,17 @@ def _producer_program(S, T, mode, lag, start_phase, tail, part=0, commits=True):
             ops.append(("issue", t, cur.index, part))
             cur.inc()
     elif mode == "landed":
-        for t in range(T):
-            ops.append(("wait_empty", cur.index, cur.phase))
-            ops.append(("issue", t, cur.index, part))
+        if pgroup < 1 or T % pgroup:
+            raise ValueError("T must be a multiple of the producer group")
+        for t0 in range(0, T, pgroup):
+            group = []
+            for t in range(t0, t0 + pgroup):
+                ops.append(("wait_empty", cur.index, cur.phase))
+                group.append((t, cur.index))
+                cur.inc()
+            ops += [("issue", t, s_, part) for t, s_ in group]
             if commits:
                 ops.append(("commit_lag",))
-            cur.inc()
         if commits:
             ops.append(("commit_all",))
     else:
@@ -280,7 +290,7 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
                    producers: int = 1, producer_start_phase: int = 1, full_expected=None,
                    empty_expected=None, release_before_read: bool = False,
                    tail: bool = True, eager_min: int = 0, tile_bytes: int = 16384,
-                   group: int = 1, commits: bool = True,
+                   group: int = 1, commits: bool = True, producer_group: int = 1,
                    max_states: int = 2_000_000) -> ProtocolResult:
     """Explore every interleaving of the producers, C consumers and the copy engine.
 
@@ -294,7 +304,9 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
     ``eager_min`` uncommitted tiles, commits its oldest uncommitted tile first
     (waiting for that tile to land), then polls again. With ``group`` = G
     every consumer waits on G consecutive stages before it uses and releases
-    them (see ``_consumer_program``).
+    them (see ``_consumer_program``). With ``producer_group`` = G the
+    producers acquire and issue G consecutive stages at a time (see
+    ``_producer_program``).
 
     Checked: (I1) a consumer reads a slot only after every share of that tile
     landed; (I2) a slot is not overwritten before all consumers of its previous
@@ -312,8 +324,10 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
         raise ValueError("eager commits exist in the landed mode only")
     if not commits and mode != "landed":
         raise ValueError("commits can be left out in the landed mode only")
+    if producer_group != 1 and mode != "landed":
+        raise ValueError("grouped producers exist in the landed mode only")
     progs = [_producer_program(S, T, mode, lag, producer_start_phase, tail, part=i,
-                               commits=commits) for i in range(P)]
+                               commits=commits, pgroup=producer_group) for i in range(P)]
     Q = _consumer_program(S, T, release_before_read, group)
     nQ = len(Q)
     # tiles a consumer at program counter pc has released
@@ -403,8 +417,10 @@ def check_protocol(S: int, T: int, C: int, *, mode: str = "tx", lag: int = 0,
                     sl[s_] = (t, frozenset())          # older contents destroyed
                 succ.append((npp, qpcs, bars, tuple(sl), inflight | {(t, part)}))
             elif kind == "commit_lag":
+                # commit the oldest uncommitted tile while more than `lag` are
+                # uncommitted (after a single issue that is at most one tile)
                 if issued - done > lag:
-                    n = commit_oldest(ppc + 1)
+                    n = commit_oldest(ppc)
                     if n is not None:
                         succ.append(n)
                 else:

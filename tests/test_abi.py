@@ -27,6 +27,30 @@ def test_library_exports_every_declared_symbol():
     assert sorted(pt.exported_symbols()) == declared
 
 
+def test_group_loads_flag_validation():
+    GL = pt.PIPE_FLAG_STRIP_GROUPS | pt.PIPE_FLAG_GROUP_LOADS
+    q = pt.lib().pipe_query_kernel
+    info = pt.pipe_kernel_info_t()
+
+    def status(op, **kw):
+        return q(op, ctypes.byref(pt.make_config(op, **kw)), 1024, 1024, 0, ctypes.byref(info))
+
+    assert status(pt.PIPE_OP_COPY, stages=8, flags=GL) == pt.PIPE_OK
+    assert info.items == 4 * 4 and info.tiles_per_item == 2 * 4   # 4 strips x 4 segments of 2 tile rows
+    assert status(pt.PIPE_OP_COPY, stages=4, producer_waves=2, consumer_waves=8,
+                  flags=GL) == pt.PIPE_OK
+    assert status(pt.PIPE_OP_COPY, stages=8, flags=pt.PIPE_FLAG_GROUP_LOADS) == \
+        pt.PIPE_ERR_CONFIG                                   # needs strip groups
+    for S in (2, 3, 5, 6, 7):
+        assert status(pt.PIPE_OP_COPY, stages=S, flags=GL) == pt.PIPE_ERR_CONFIG
+    assert status(pt.PIPE_OP_COPY, stages=8, producer_waves=1, flags=GL) == pt.PIPE_ERR_CONFIG
+    assert status(pt.PIPE_OP_COPY, stages=8, consumer_waves=3, flags=GL) == pt.PIPE_ERR_CONFIG
+    assert status(pt.PIPE_OP_COPY, stages=8, flags=GL | pt.PIPE_FLAG_UNIFIED) == \
+        pt.PIPE_ERR_CONFIG
+    assert status(pt.PIPE_OP_ROWSUM, stages=8, flags=GL) == pt.PIPE_ERR_CONFIG
+    assert status(pt.PIPE_OP_GEMM, flags=pt.PIPE_FLAG_GROUP_LOADS) == pt.PIPE_ERR_CONFIG
+
+
 def test_rowsum_noalloc_validation_needs_no_gpu():
     """The no-allocation row sum checks everything, including that the shape's
     workspace fits the library buffer, before any HIP call."""

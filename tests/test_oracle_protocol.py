@@ -281,3 +281,25 @@ def test_page_shared_storage_arithmetic(golden):
     assert [256 // kv["tile_rows"][0], 128 // kv["tile_cols"][0]] == kv["grid_256x128"]
     # a plausible misreading (one barrier per stage, or unaligned data) misses the printed total
     assert P.page_shared_storage_bytes(3, 128, 64, data_align=8)["total_bytes"] != kv["total_bytes"][0]
+
+
+@pytest.mark.parametrize("S,G", [(4, 4), (8, 4), (4, 2), (6, 2)])
+@pytest.mark.parametrize("C", [1, 2])
+def test_grouped_producer_lag_boundary(S, G, C):
+    """A producer that acquires G consecutive stages, issues loads spanning all
+    G and then applies the commit rule, feeding consumers that take the same G
+    stages at a time: live and safe while the commit lag (in tiles) is at most
+    S - G -- the bound the grouped-load copy keeps -- and deadlocked one tile
+    beyond it (the producer then needs the slots of a group it has not yet
+    committed)."""
+    T = S + G   # the ring wraps: the last group reuses the slots of the first
+    ok = P.check_protocol(S, T, C, mode="landed", lag=S - G, group=G, producer_group=G)
+    assert ok.completed and not ok.deadlock and not ok.violations, ok
+    assert ok.max_ahead <= S
+    bad = P.check_protocol(S, T, C, mode="landed", lag=S - G + 1, group=G, producer_group=G)
+    assert bad.deadlock and not bad.violations, bad
+
+
+def test_grouped_producer_with_two_producer_waves():
+    r = P.check_protocol(4, 8, 1, mode="landed", lag=0, producers=2, group=4, producer_group=4)
+    assert r.completed and not r.deadlock and not r.violations, r
