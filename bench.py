@@ -87,7 +87,7 @@ GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _R
 # 4 slots of a tile row with 2-row x 512-byte loads.
 _GL = 0x80000
 GROUP_LOAD_COPY = dict(stages=8, producer_waves=4, consumer_waves=8,
-                       flags=_NT | _RM | _IL | _LZ | _G | _GL)
+                       flags=_NT | _IL | _LZ | _G | _GL)
 # The register producer engine (PIPE_FLAG_PRODUCER_VGPR): global_load_dwordx4
 # into registers, then ds_write_b128 into the slot.
 _V = 0x8000
