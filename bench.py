@@ -65,7 +65,7 @@ GEMM_N = 4096
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "copy_16384x16384_counters.md")
-KERNEL_SOURCES = ("pipe_device.hpp", "pipe_kernels.hpp", "pipe_stream.hip")
+KERNEL_SOURCES = ("pipe_device.hpp", "pipe_kernels.hpp", "pipe_rowsum.hpp", "pipe_stream.hip")
 MALL_FLUSH_BYTES = 1 << 30
 
 # Wider 16 KiB tiles (64 x 128, 32 x 256) at the launch shapes measured best for
