@@ -371,7 +371,11 @@ pipe_status_t gemm_check_shape(const pipe_config_t& c, int64_t M, int64_t N, int
   const bool b_col = (c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) != 0;
   if (M < 0 || N < 0 || K < 0 || lda < K || ldb < (b_col ? K : N) || ldc < N)
     return PIPE_ERR_SHAPE;
-  if (M % c.tile_m != 0 || N % 128 != 0 || K % 64 != 0) return PIPE_ERR_SHAPE;
+  // Whole 16-byte chunks of B's and A's rows; ragged tiles are masked (the
+  // trace kernel takes whole tiles only).
+  if (N % 8 != 0 || K % 8 != 0) return PIPE_ERR_SHAPE;
+  if ((c.flags & PIPE_FLAG_TRACE) && (M % c.tile_m != 0 || N % 128 != 0 || K % 64 != 0))
+    return PIPE_ERR_SHAPE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
   if (!extent_fits(M, lda, 2) || !extent_fits(b_col ? N : K, ldb, 2) ||
       !extent_fits(M, ldc, (c.flags & PIPE_FLAG_GEMM_C_BF16) ? 2 : 4))
@@ -389,9 +393,9 @@ pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int
   p->M = (int32_t)M;
   p->N = (int32_t)N;
   p->K = (int32_t)K;
-  p->tiles_n = (int32_t)(N / 128);
-  p->k_steps = (int32_t)(K / 64);
-  const int64_t items = (M / c.tile_m) * (int64_t)p->tiles_n;
+  p->tiles_n = (int32_t)((N + 127) / 128);
+  p->k_steps = (int32_t)((K + 63) / 64);
+  const int64_t items = ((M + c.tile_m - 1) / c.tile_m) * (int64_t)p->tiles_n;
   p->tile_m = c.tile_m;
   if (items > INT32_MAX) return PIPE_ERR_SHAPE;
   p->items = (int32_t)items;
@@ -633,9 +637,10 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     pipe_status_t s = gemm_check_config(c);  // rejects what pipe_gemm_mainloop rejects
     if (s != PIPE_OK) return s;
     if (c.flags & PIPE_FLAG_TEST_START_PHASE0) return PIPE_ERR_CONFIG;
-    if (M < 0 || N < 0 || K < 0 || M % c.tile_m || N % 128 || K % 64) return PIPE_ERR_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return PIPE_ERR_SHAPE;
+    if ((c.flags & PIPE_FLAG_TRACE) && (M % c.tile_m || N % 128 || K % 64)) return PIPE_ERR_SHAPE;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
-    const int64_t items = (M / c.tile_m) * (N / 128);
+    const int64_t items = ((M + c.tile_m - 1) / c.tile_m) * ((N + 127) / 128);
     if (items > INT32_MAX) return PIPE_ERR_SHAPE;
     const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
     const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
@@ -643,7 +648,7 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     info->threads = gemm_threads(c.producer_waves, c_bf16, store_wave, c.tile_m);
     info->items = (int32_t)items;
     info->grid = (c.grid == 0 || c.grid > info->items) ? info->items : c.grid;
-    info->tiles_per_item = (int32_t)(K / 64);
+    info->tiles_per_item = (int32_t)((K + 63) / 64);
     info->split = 1;
     return PIPE_OK;
   }

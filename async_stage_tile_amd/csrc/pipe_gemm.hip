@@ -65,6 +65,15 @@
 // Slot rows are padded to 272 bytes so the two half-waves of a fragment write
 // (rows r and r + 4) fall on different banks.
 //
+// Ragged shapes (M not a multiple of the tile height, N of 128 or K of 64;
+// N and K multiples of 8, so every 16-byte chunk is wholly inside or outside
+// the operands): the host launches the MASKED instantiation. A producer lane
+// whose chunk lies outside A or B (a row past M, a column past N, a K index
+// past K) loads 16 bytes from a zero-filled device buffer instead, so the slot
+// holds exact zeros there -- the out-of-bounds fill of a tensor copy -- and the
+// MFMAs add nothing for K past K; the epilogue stores only rows below M and
+// columns below N. Divisible shapes run the instantiations without these tests.
+//
 // MFMA 32x32x16 operand layout (lane l, element e): A[i][k] with i = l % 32,
 // k = 8 * (l / 32) + e; B[k][j] with j = l % 32, k = 8 * (l / 32) + e; the
 // 16 accumulators hold D[i][j] with j = l % 32,
@@ -82,6 +91,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Source of the zero chunks of ragged-edge stages: never written, so it holds
+// the zeros of static device storage for the life of the module.
+__device__ __align__(16) uint8_t g_zero_chunks[64];
 
 constexpr int kGemmTile = 128;
 constexpr int kGemmK = 64;
@@ -133,8 +146,21 @@ __device__ __forceinline__ int swz_b(int k, int on) {
   return on ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : 0;
 }
 
-template <int S, int PW, bool BCOL, bool TRACE = false, int MT = 1>
-__device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) {
+// Global source of one 16-byte chunk: `a`, or the zero buffer where the chunk
+// lies outside the operand (MASKED kernels only).
+template <bool MASKED>
+__device__ __forceinline__ const uint8_t* chunk_src(const uint8_t* a, bool inside) {
+  if constexpr (MASKED) {
+    // Selected as integers: a select of the two pointers made the compiler
+    // emit an address-space check that does not assemble.
+    const uint64_t zero = reinterpret_cast<uint64_t>(&g_zero_chunks[0]);
+    return reinterpret_cast<const uint8_t*>(inside ? reinterpret_cast<uint64_t>(a) : zero);
+  }
+  return a;
+}
+
+template <int S, int PW, bool BCOL, bool TRACE = false, int MT = 1, bool MASKED = false>
+__device__ __forceinline__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) {
   constexpr int kABlocks = 16 * MT;                   // 1 KiB DMA blocks of an A stage
   constexpr int kLoads = (kABlocks + 16) / PW;        // DMA instructions per stage per wave
   constexpr int kMaxLag = 48 / kLoads - 1;            // (lag + 1) stages <= 48 loads
@@ -154,7 +180,11 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) 
     // Column-major B: its rows (one per output column) start at row tn * 128.
     const uint8_t* gb = BCOL ? p.B + (int64_t)tn * kGemmTile * p.ldb
                              : p.B + (int64_t)tn * kBRowBytes;
+    // Rows of A and columns of B that lie inside the operands (MASKED).
+    const int a_rows = p.M - tm * kGemmTile * MT;
+    const int b_cols = p.N - tn * kGemmTile;
     for (int ks = 0; ks < p.k_steps; ++ks) {
+      const int k_left = p.K - ks * kGemmK;  // K indices of this step inside the operands
       if (!acquire_slot<kLoads, S, Counter<4 * MT>, Counter<PW>>(&lds.empty[w.index], w.phase,
                                                              lds.full, w.index, pending, p.eager,
                                                              p.spin_limit)) {
@@ -165,9 +195,11 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) 
         if (pw == 0) trace_write(p.trace, p.trace_cap, t, 0, w, 0);
         ++t;
       }
-      if constexpr (MT > 1) {
+      if constexpr (MT > 1 || MASKED) {
         // The stage's 16 MT + 16 blocks (A first, then B) in order, kLoads
         // per wave; a wave's share may straddle A and B (uniform branch).
+        // (The masked kernels take this walk for 128-row tiles too: it deals
+        // the same blocks to the same waves as the A/B split below.)
         const uint32_t sa = uniform(lds_addr(&lds.a[w.index][0]));
         const uint32_t sb = uniform(lds_addr(&lds.b[w.index][0]));
         const uint8_t* a0 = ga + (int64_t)ks * kGemmK * 2;
@@ -178,17 +210,23 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) 
           if (q < kABlocks) {
             const int r = q * 8 + (lane >> 3);
             const int c = swz(r, lane & 7, p.swz_shift);
-            dma_block(a0 + (int64_t)r * p.lda + c * 16, sa + q * kBlockBytes);
+            dma_block(chunk_src<MASKED>(a0 + (int64_t)r * p.lda + c * 16,
+                                        r < a_rows && c * 8 < k_left),
+                      sa + q * kBlockBytes);
           } else if constexpr (BCOL) {
             const int qb = q - kABlocks;
             const int r = qb * 8 + (lane >> 3);
             const int c = swz(r, lane & 7, p.swz_shift);
-            dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + qb * kBlockBytes);
+            dma_block(chunk_src<MASKED>(b0 + (int64_t)r * p.ldb + c * 16,
+                                        r < b_cols && c * 8 < k_left),
+                      sb + qb * kBlockBytes);
           } else {
             const int qb = q - kABlocks;
             const int r = qb * 4 + (lane >> 4);
             const int c = (lane & 15) ^ swz_b(r, p.b_swz);
-            dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + qb * kBlockBytes);
+            dma_block(chunk_src<MASKED>(b0 + (int64_t)r * p.ldb + c * 16,
+                                        r < k_left && c * 8 < b_cols),
+                      sb + qb * kBlockBytes);
           }
         }
       } else if (is_a) {
@@ -200,7 +238,9 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) 
           const int q = part * kLoads + j;
           const int r = q * 8 + (lane >> 3);
           const int c = swz(r, lane & 7, p.swz_shift);
-          dma_block(a0 + (int64_t)r * p.lda + c * 16, sa + q * kBlockBytes);
+          dma_block(chunk_src<MASKED>(a0 + (int64_t)r * p.lda + c * 16,
+                                      r < a_rows && c * 8 < k_left),
+                    sa + q * kBlockBytes);
         }
       } else if constexpr (BCOL) {
         // Column-major B: the same 128 x 64 row layout and swizzle as A.
@@ -211,7 +251,9 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) 
           const int q = part * kLoads + j;
           const int r = q * 8 + (lane >> 3);
           const int c = swz(r, lane & 7, p.swz_shift);
-          dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + q * kBlockBytes);
+          dma_block(chunk_src<MASKED>(b0 + (int64_t)r * p.ldb + c * 16,
+                                      r < b_cols && c * 8 < k_left),
+                    sb + q * kBlockBytes);
         }
       } else {
         const uint32_t sb = uniform(lds_addr(&lds.b[w.index][0]));
@@ -222,7 +264,9 @@ __device__ void gemm_producer(const GemmParams& p, GemmLds<S, MT>& lds, int pw) 
           const int q = part * kLoads + j;
           const int r = q * 4 + (lane >> 4);
           const int c = (lane & 15) ^ swz_b(r, p.b_swz);
-          dma_block(b0 + (int64_t)r * p.ldb + c * 16, sb + q * kBlockBytes);
+          dma_block(chunk_src<MASKED>(b0 + (int64_t)r * p.ldb + c * 16,
+                                      r < k_left && c * 8 < b_cols),
+                    sb + q * kBlockBytes);
         }
       }
       ++pending;
@@ -336,8 +380,8 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // reads of the slot to return, releases the slot, then waits on full for the
 // next stage (while the previous MFMAs still execute) and reads that stage's
 // first sub-step before issuing the last MFMAs of the current one.
-template <int S, int PW, int EPI, bool BCOL, bool TRACE = false, int MT = 1>
-__device__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT>& lds, void* out_lds, int cw) {
+template <int S, int PW, int EPI, bool BCOL, bool TRACE = false, int MT = 1, bool MASKED = false>
+__device__ __forceinline__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT>& lds, void* out_lds, int cw) {
   static_assert(MT == 1 || (EPI != kEpiStoreWave && !TRACE), "256-row tiles: no store wave, no trace");
   constexpr int kTileM = kGemmTile * MT;
   OutLds* out = static_cast<OutLds*>(out_lds);
@@ -410,7 +454,7 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT>& lds, void* ou
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int row = tm * kTileM + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
-            C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+            if (!MASKED || (row < p.M && col < p.N)) C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
           }
         }
     } else if constexpr (EPI == kEpiWaveStaged) {
@@ -444,8 +488,9 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT>& lds, void* ou
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int q = i * 64 + lane;
-          uint8_t* g = C + (row0 + (q >> 3)) * ldc_bytes + ((int64_t)tn * kGemmTile + wn * 64) * 2 +
-                       (q & 7) * 16;
+          const int64_t col0 = (int64_t)tn * kGemmTile + wn * 64 + (q & 7) * 8;
+          if (MASKED && (row0 + (q >> 3) >= p.M || col0 >= p.N)) continue;
+          uint8_t* g = C + (row0 + (q >> 3)) * ldc_bytes + col0 * 2;
           const u32x4 nv = {v[i].x, v[i].y, v[i].z, v[i].w};
           __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(g));
         }
@@ -485,7 +530,8 @@ __device__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT>& lds, void* ou
 
 // Store wave of the staged epilogue: for every tile, drains the 4 chunks of
 // each wave pair (pair 0 and pair 1 alternately) and writes them to C.
-__device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
+template <bool MASKED>
+__device__ __forceinline__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
   const int lane = lane_id();
   PipeState rd[2] = {consumer_start(1), consumer_start(1)};
   bool ok = true;
@@ -515,7 +561,9 @@ __device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int q = i * 64 + lane;
-          uint8_t* g = C + (row0 + (q >> 4)) * ldc_bytes + (int64_t)tn * kGemmTile * 2 + (q & 15) * 16;
+          const int64_t col0 = (int64_t)tn * kGemmTile + (q & 15) * 8;
+          if (MASKED && (row0 + (q >> 4) >= p.M || col0 >= p.N)) continue;
+          uint8_t* g = C + (row0 + (q >> 4)) * ldc_bytes + col0 * 2;
           const u32x4 nv = {v[i].x, v[i].y, v[i].z, v[i].w};
           __builtin_nontemporal_store(nv, reinterpret_cast<u32x4*>(g));
         }
@@ -526,7 +574,7 @@ __device__ void gemm_store_wave(const GemmParams& p, OutLds& out) {
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-template <int S, int PW, int EPI, bool BCOL, bool TRACE = false, int MT = 1>
+template <int S, int PW, int EPI, bool BCOL, bool TRACE = false, int MT = 1, bool MASKED = false>
 __device__ __forceinline__ void gemm_body(const GemmParams& p) {
   __shared__ GemmLds<S, MT> lds;
   const int wave = (int)(threadIdx.x >> 6);
@@ -542,24 +590,24 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
     }
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW, BCOL>(p, lds, wave);
+      gemm_producer<S, PW, BCOL, false, 1, MASKED>(p, lds, wave);
     else if (wave < PW + 4)
-      gemm_consumer<S, PW, EPI, BCOL>(p, lds, &out, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL, false, 1, MASKED>(p, lds, &out, wave - PW);
     else
-      gemm_store_wave(p, out);
+      gemm_store_wave<MASKED>(p, out);
   } else if constexpr (EPI == kEpiWaveStaged) {
     __shared__ WaveOutLds<MT> out;
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW, BCOL, false, MT>(p, lds, wave);
+      gemm_producer<S, PW, BCOL, false, MT, MASKED>(p, lds, wave);
     else
-      gemm_consumer<S, PW, EPI, BCOL, false, MT>(p, lds, &out, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL, false, MT, MASKED>(p, lds, &out, wave - PW);
   } else {
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW, BCOL, TRACE, MT>(p, lds, wave);
+      gemm_producer<S, PW, BCOL, TRACE, MT, MASKED>(p, lds, wave);
     else
-      gemm_consumer<S, PW, EPI, BCOL, TRACE, MT>(p, lds, nullptr, wave - PW);
+      gemm_consumer<S, PW, EPI, BCOL, TRACE, MT, MASKED>(p, lds, nullptr, wave - PW);
   }
 }
 
@@ -589,18 +637,18 @@ constexpr int gemm_lds_of(int S, int EPI, int MT) {
 constexpr bool gemm_fits(int S, int EPI, int MT) { return gemm_lds_of(S, EPI, MT) <= 160 * 1024; }
 
 // B row-major (K x N, the default) and column-major (PIPE_FLAG_GEMM_B_COLMAJOR).
-template <int S, int PW, int EPI, int MT = 1>
+template <int S, int PW, int EPI, int MT = 1, bool MASKED = false>
 __global__ void __launch_bounds__(gemm_block_threads(PW, EPI, MT),
                                   gemm_waves_per_simd(S, PW, EPI, MT))
     gemm_kernel(GemmParams p) {
-  gemm_body<S, PW, EPI, false, false, MT>(p);
+  gemm_body<S, PW, EPI, false, false, MT, MASKED>(p);
 }
 
-template <int S, int PW, int EPI, int MT = 1>
+template <int S, int PW, int EPI, int MT = 1, bool MASKED = false>
 __global__ void __launch_bounds__(gemm_block_threads(PW, EPI, MT),
                                   gemm_waves_per_simd(S, PW, EPI, MT))
     gemm_kernel_bcol(GemmParams p) {
-  gemm_body<S, PW, EPI, true, false, MT>(p);
+  gemm_body<S, PW, EPI, true, false, MT, MASKED>(p);
 }
 
 // With PIPE_FLAG_TRACE (fp32 C, row-major B, 128-row tiles): the same
@@ -616,27 +664,32 @@ using GemmKernel = void (*)(GemmParams);
 
 // The kernel for ring depth S, or null where its LDS would not fit a CU.
 template <int S, int PW, int EPI, int MT>
-GemmKernel gemm_pick(bool bcol) {
-  if constexpr (gemm_fits(S, EPI, MT))
+GemmKernel gemm_pick(bool bcol, bool masked) {
+  if constexpr (gemm_fits(S, EPI, MT)) {
+    if (masked)
+      return bcol ? gemm_kernel_bcol<S, PW, EPI, MT, true> : gemm_kernel<S, PW, EPI, MT, true>;
     return bcol ? gemm_kernel_bcol<S, PW, EPI, MT> : gemm_kernel<S, PW, EPI, MT>;
-  else
+  } else {
     return nullptr;
+  }
 }
 
 template <int PW, int EPI, int MT>
 hipError_t launch_gemm_pw(int stages, int grid, const GemmParams& p, hipStream_t stream) {
   const dim3 g(grid), b(gemm_block_threads(PW, EPI, MT));
   const bool bcol = p.b_colmajor != 0;
+  const bool masked = (p.M % (kGemmTile * MT)) != 0 || (p.N % kGemmTile) != 0 ||
+                      (p.K % kGemmK) != 0;
   GemmKernel k;
   switch (stages) {
-    case 1: k = gemm_pick<1, PW, EPI, MT>(bcol); break;
-    case 2: k = gemm_pick<2, PW, EPI, MT>(bcol); break;
-    case 3: k = gemm_pick<3, PW, EPI, MT>(bcol); break;
-    case 4: k = gemm_pick<4, PW, EPI, MT>(bcol); break;
+    case 1: k = gemm_pick<1, PW, EPI, MT>(bcol, masked); break;
+    case 2: k = gemm_pick<2, PW, EPI, MT>(bcol, masked); break;
+    case 3: k = gemm_pick<3, PW, EPI, MT>(bcol, masked); break;
+    case 4: k = gemm_pick<4, PW, EPI, MT>(bcol, masked); break;
     default: return hipErrorInvalidValue;
   }
-  if (p.trace != nullptr) {  // fp32 C, row-major B, 128-row tiles (checked by the host)
-    if (EPI != kEpiF32 || bcol || MT != 1) return hipErrorInvalidValue;
+  if (p.trace != nullptr) {  // fp32 C, row-major B, 128-row tiles, whole tiles (checked by the host)
+    if (EPI != kEpiF32 || bcol || MT != 1 || masked) return hipErrorInvalidValue;
     switch (stages) {
       case 1: k = gemm_trace_kernel<1, PW>; break;
       case 2: k = gemm_trace_kernel<2, PW>; break;

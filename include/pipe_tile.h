@@ -299,9 +299,13 @@ pipe_status_t pipe_rowsum_noalloc(const void* A, float* out, int64_t M, int64_t 
  * staged through LDS so that C is written in whole 16-byte row pieces
  * (optionally by a dedicated store wave, PIPE_FLAG_GEMM_STORE_WAVE). A and B tiles
  * of each 64-deep K step pass through the LDS ring to MFMA consumer waves.
- *   M % tile_m == 0, N % 128 == 0, K % 64 == 0; lda >= K and ldb >= N (ldb >= K
- *   for column-major B), both multiples of 8; ldc >= N (elements of C's type;
- *   a multiple of 8 for bf16 C, whose base must be 16-byte aligned); K == 0
+ *   M arbitrary, N % 8 == 0 and K % 8 == 0 (whole 16-byte chunks; else
+ *   PIPE_ERR_SHAPE). Shapes that are not whole tiles (M % tile_m, N % 128 or
+ *   K % 64 non-zero) run a masked kernel: chunks outside A or B enter the ring
+ *   as zeros and only C's M x N elements are written (with PIPE_FLAG_TRACE
+ *   such shapes return PIPE_ERR_SHAPE). lda >= K and ldb >= N (ldb >= K for
+ *   column-major B), both multiples of 8; ldc >= N (elements of C's type; a
+ *   multiple of 8 for bf16 C, whose base must be 16-byte aligned); K == 0
  *   gives C = 0. */
 pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t M,
                                  int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,

@@ -182,8 +182,13 @@ def test_rowsum_and_gemm_validation():
     g = pt.make_config(pt.PIPE_OP_GEMM)
     args = lambda M, N, K, **kw: L.pipe_gemm_mainloop(kw.get("A", FAKE), FAKE, FAKE, M, N, K,
                                                        K, N, N, ctypes.byref(kw.get("cfg", g)), None)
-    assert args(256, 256, 100) == pt.PIPE_ERR_SHAPE
-    assert args(256, 192, 128) == pt.PIPE_ERR_SHAPE
+    assert args(256, 256, 100) == pt.PIPE_ERR_SHAPE      # K not a multiple of 8
+    assert args(256, 196, 128) == pt.PIPE_ERR_SHAPE      # N not a multiple of 8
+    # shapes that are not whole tiles are accepted (a masked kernel runs them)
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 200, 136, 72)
+    assert (q["items"], q["tiles_per_item"], q["grid"]) == (2 * 2, 2, 4)
+    tr = pt.make_config(2, flags=pt.PIPE_FLAG_TRACE, trace=FAKE, trace_capacity=8)
+    assert args(200, 136, 72, cfg=tr) == pt.PIPE_ERR_SHAPE   # the trace takes whole tiles
     assert args(256, 256, 128, A=FAKE + 4) == pt.PIPE_ERR_ALIGN
     assert args(256, 256, 128, cfg=pt.make_config(2, stages=5)) == pt.PIPE_ERR_STAGES
     assert args(256, 256, 128, cfg=pt.make_config(2, consumer_waves=3)) == pt.PIPE_ERR_CONFIG
@@ -532,7 +537,8 @@ def test_gemm_256_row_tiles_geometry_and_rejections():
         pt.PIPE_OP_GEMM, ctypes.byref(pt.make_config(pt.PIPE_OP_GEMM, **kw)), M, 128, 64,
         ctypes.byref(pt.pipe_kernel_info_t()))
     assert status(256, **T) == pt.PIPE_OK
-    assert status(384, **T) == pt.PIPE_ERR_SHAPE
+    assert status(384, **T) == pt.PIPE_OK                 # a ragged tile row (masked kernel)
+    assert status(384, **dict(T, flags=pt.PIPE_FLAG_TRACE)) != pt.PIPE_OK
     assert status(256, **dict(T, consumer_waves=4)) == pt.PIPE_ERR_CONFIG
     assert status(256, **dict(T, producer_waves=2)) == pt.PIPE_ERR_CONFIG
     assert status(256, tile_m=128, consumer_waves=8, producer_waves=4) == pt.PIPE_ERR_CONFIG

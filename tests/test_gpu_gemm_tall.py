@@ -116,10 +116,8 @@ def test_tall_strided_operands_and_c():
 
 
 def test_tall_rejections():
-    A = torch.zeros((384, 128), dtype=torch.bfloat16, device=DEV)
+    # (M not a multiple of 256 runs the masked kernel: tests/test_gpu_gemm_ragged.py)
     B = torch.zeros((128, 128), dtype=torch.bfloat16, device=DEV)
-    with pytest.raises(pt.PipeError):       # M not a multiple of 256
-        pt.pipe_gemm_mainloop(A, B, **TALL)
     A = torch.zeros((256, 128), dtype=torch.bfloat16, device=DEV)
     for kw in (dict(TALL, consumer_waves=4), dict(TALL, producer_waves=2),
                dict(TALL, stages=4), dict(TALL, stages=3, out_dtype=torch.bfloat16),
