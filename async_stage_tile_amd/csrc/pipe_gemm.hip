@@ -737,7 +737,10 @@ int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave, int tile_m) {
   const int out = !c_bf16 ? 0
                   : store_wave ? (int)sizeof(OutLds)
                   : 4 * mt * kWaveOutBytes;
-  return stages * (mt * kAStageBytes + kBStageBytes) + stages * 8 + out;
+  const int ring = stages * (mt * kAStageBytes + kBStageBytes) + stages * 8;
+  // A further LDS object of the kernel (the bf16 staging) starts on a 16-byte
+  // boundary.
+  return out > 0 ? ((ring + 15) & ~15) + out : ring;
 }
 
 int gemm_threads(int producers, bool c_bf16, bool store_wave, int tile_m) {

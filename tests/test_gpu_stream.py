@@ -541,6 +541,14 @@ def test_unified_copy_full_size_bit_exact():
     (pt.PIPE_OP_GEMM, 4096, 4096, 4096, dict(flags=pt.PIPE_FLAG_GEMM_B_COLMAJOR |
                                              pt.PIPE_FLAG_EAGER_NEWEST)),
     (pt.PIPE_OP_GEMM, 1024, 1024, 1024, dict(stages=4, producer_waves=2)),
+    (pt.PIPE_OP_GEMM, 4096, 4096, 4096, dict(stages=3, flags=pt.PIPE_FLAG_GEMM_C_BF16 |
+                                             pt.PIPE_FLAG_EAGER_NEWEST)),   # ring + staging
+    (pt.PIPE_OP_GEMM, 4096, 4096, 4096, dict(stages=3, flags=pt.PIPE_FLAG_GEMM_C_BF16 |
+                                             pt.PIPE_FLAG_GEMM_STORE_WAVE)),
+    (pt.PIPE_OP_GEMM, 1000, 1000, 1000, dict(stages=3)),             # ragged: the masked kernel
+    (pt.PIPE_OP_COPY, 16384, 16384, 0, dict(stages=8, consumer_waves=8,
+                                            flags=pt.PIPE_FLAG_STRIP_GROUPS |
+                                            pt.PIPE_FLAG_GROUP_LOADS)),
 ])
 def test_kernel_resources_agree_with_the_launch_geometry(op, M, N, K, cfg):
     """The runtime's static LDS for the kernel an op launches equals the LDS
