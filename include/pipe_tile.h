@@ -209,10 +209,13 @@ typedef struct {
   int32_t max_threads;    /* largest workgroup the kernel can be launched with            */
 } pipe_kernel_resources_t;
 
-/* ABI version of the loaded library (PIPE_ABI_VERSION). */
+/* ABI version of the loaded library (PIPE_ABI_VERSION). Part of this
+ * library's own interface, not an operation of the pages. */
 int pipe_abi_version(void);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code (never NULL; unknown codes
+ * get a fixed string). Part of this library's own interface, not an operation
+ * of the pages. */
 const char* pipe_status_str(int status);
 
 /* Fill *cfg with the defaults of an op (the pipeline parameters of
@@ -318,20 +321,21 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
 pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
                                 int64_t K, pipe_kernel_info_t* info);
 
-/* A diagnostic of this library, not an operation of the pages.
- * Compiled resources of the main kernel that an op would launch for this
+/* Compiled resources of the main kernel that an op would launch for this
  * shape and config (the stream, unified or GEMM kernel; not a zero fill), from
  * the HIP runtime's function attributes. It
  * takes the same checks as the op's entry point minus those on pointers, with
  * the tightest pitches (ld = N, or K for A and column-major B), and launches
  * nothing. Unlike pipe_query_kernel it needs the HIP runtime and a device.
+ * A diagnostic of this library, not an operation of the pages.
  *   PIPE_ERR_SHAPE also for shapes that launch no main kernel (M or N zero,
  *   or K zero for the GEMM); PIPE_ERR_HIP when the runtime cannot report. */
 pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int64_t M, int64_t N,
                                     int64_t K, pipe_kernel_resources_t* out);
 
 /* Blocking read of the library's own device status word on the current
- * device (used when cfg->status is NULL); clears it when `clear` != 0. */
+ * device (used when cfg->status is NULL); clears it when `clear` != 0.
+ * Part of this library's error reporting, not an operation of the pages. */
 pipe_status_t pipe_device_status(uint32_t* out, int clear);
 
 #ifdef __cplusplus
