@@ -80,9 +80,9 @@ WIDE_COPY = {
 }
 # 128 x 64 tiles down column strips 4 tile columns wide (PIPE_FLAG_STRIP_GROUPS):
 # consumers store a tile row of the strip as 512-byte row runs; 4 interleaved
-# segments per strip, the best ring measured for it.
+# segments per strip, the best ring measured for it (non-temporal, no XCD remap).
 _G = 0x4000
-GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _RM | _IL | _LZ | _G)
+GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _IL | _LZ | _G)
 # The same strips with grouped loads (PIPE_FLAG_GROUP_LOADS): producers fill the
 # 4 slots of a tile row with 2-row x 512-byte loads.
 _GL = 0x80000
