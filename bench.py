@@ -708,7 +708,10 @@ def cpu_oracle_extras(copy_rows, rowsum_rows, gemm_rows):
 
     copy: oracle.results.tile_copy on copy_rows x 16384; rowsum:
     oracle.results.rowsum_exact on rowsum_rows x 65536; GEMM: oracle.results.gemm_f64
-    on gemm_rows rows of A (4096^2 bf16 inputs) against all of B."""
+    on gemm_rows rows of A (4096^2 bf16 inputs) against all of B. The copy oracle
+    is a per-tile Python loop that holds the interpreter lock, so more threads
+    cannot speed it up: it is timed on one thread only. The row sum and the GEMM
+    spend their time in numpy and BLAS, which release the lock."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -723,16 +726,18 @@ def cpu_oracle_extras(copy_rows, rowsum_rows, gemm_rows):
     Gb = synth.uniform((GEMM_N, GEMM_N), torch.bfloat16, seed=42, stream=1).float().numpy()
     for label, threads in (("1_thread", 1), ("all_threads", nt)):
         with threadpool_limits(limits=threads):
-            t0 = time.perf_counter()
-            _parallel_rows(lambda a, b: R.tile_copy(src[a:b]), copy_rows, threads)
-            tc = time.perf_counter() - t0
+            tc = None
+            if threads == 1:
+                t0 = time.perf_counter()
+                R.tile_copy(src)
+                tc = time.perf_counter() - t0
             t0 = time.perf_counter()
             _parallel_rows(lambda a, b: R.rowsum_exact(A[a:b]), rowsum_rows, threads)
             tr = time.perf_counter() - t0
             t0 = time.perf_counter()
             R.gemm_f64(Ga, Gb)
             tg = time.perf_counter() - t0
-        res[label] = {"copy_gbs": 4 * copy_rows * COPY_N / tc / 1e9,
+        res[label] = {"copy_gbs": 4 * copy_rows * COPY_N / tc / 1e9 if tc else None,
                       "rowsum_gbs": 2 * rowsum_rows * ROWSUM_N / tr / 1e9,
                       "gemm_gflops": 2.0 * gemm_rows * GEMM_N * GEMM_N / tg / 1e9}
     res["sample"] = (f"copy {copy_rows}x{COPY_N} fp16, rowsum {rowsum_rows}x{ROWSUM_N} fp16, "
