@@ -869,12 +869,23 @@ def main():
     extras = {}
     stages = 2 if args.stages is None else args.stages
     if not args.no_extras or stages == 0:
+        # Two passes in opposite orders, so that no depth gains from running
+        # later in the process (clocks still settling); each point is the mean.
+        depths = (1, 2, 3, 4, 6, 8)
+        runs = {s: [] for s in depths}
+        for order in (depths, depths[::-1]):
+            for s in order:
+                runs[s].append(bench_copy(s, max(3, args.steps // 2), args.warmup))
         sweep = []
-        for s in (1, 2, 3, 4, 6, 8):
-            r = bench_copy(s, max(3, args.steps // 2), args.warmup)
-            log(f"[bench] sweep S={s}: {r['gbs']:.1f} GB/s")
-            sweep.append({k: r[k] for k in ("stages", "kernel_ms", "gbs", "bit_exact",
-                                            "lds_bytes")})
+        for s in depths:
+            a, b = runs[s]
+            sweep.append({"stages": s, "lds_bytes": a["lds_bytes"],
+                          "kernel_ms": (a["kernel_ms"] + b["kernel_ms"]) / 2,
+                          "gbs": (a["gbs"] + b["gbs"]) / 2,
+                          "gbs_passes": [a["gbs"], b["gbs"]],
+                          "bit_exact": a["bit_exact"] and b["bit_exact"]})
+            log(f"[bench] sweep S={s}: {sweep[-1]['gbs']:.1f} GB/s "
+                f"(passes {a['gbs']:.1f}, {b['gbs']:.1f})")
         extras["copy_stage_sweep"] = sweep
         if stages == 0:
             stages = max(sweep, key=lambda r: r["gbs"])["stages"]
@@ -931,10 +942,17 @@ def main():
                                                   "bit_exact")}
                               for r in extras.get("copy_stage_sweep", []) if r["stages"] <= 4],
               "unified": []}
-        for s_ in (1, 2, 3, 4):
-            u = bench_copy(s_, max(3, args.steps // 2), args.warmup, consumer_waves=2,
-                           flags=uflags)
-            n1["unified"].append({k: u[k] for k in keys})
+        urun = {s_: [] for s_ in (1, 2, 3, 4)}
+        for order in ((1, 2, 3, 4), (4, 3, 2, 1)):  # two passes, as for the stage sweep
+            for s_ in order:
+                urun[s_].append(bench_copy(s_, max(3, args.steps // 2), args.warmup,
+                                           consumer_waves=2, flags=uflags))
+        for s_, (a, b) in urun.items():
+            u = {k: a[k] for k in keys}
+            for k in ("kernel_ms", "gbs", "kernel_gbs"):
+                u[k] = (a[k] + b[k]) / 2
+            u["bit_exact"] = a["bit_exact"] and b["bit_exact"]
+            n1["unified"].append(u)
             log(f"[bench] unified copy S={s_}: {u['gbs']:.1f} GB/s (kernel {u['kernel_gbs']:.1f})")
         extras["copy_specialised_vs_unified"] = n1
         _COPY_BUF.clear()
