@@ -282,7 +282,9 @@ pipe_status_t pipe_rowsum(const void* A, float* out, int64_t M, int64_t N, int64
  * ends) instead of a caller's. Same kernels and bit-identical results as
  * pipe_rowsum; the caller still passes A and out. It allocates nothing, with
  * no allocating runtime call: the buffer's device address is looked up once
- * per device (hipGetSymbolAddress) on the first call there. A shape whose
+ * per device (hipGetSymbolAddress) on the first call there; make that first
+ * call outside stream capture, and later calls may be captured and replayed
+ * (the captured launches keep the buffer's address). A shape whose
  * pipe_rowsum_workspace_bytes exceeds PIPE_ROWSUM_SCRATCH_BYTES returns
  * PIPE_ERR_WORKSPACE before anything is enqueued (a smaller cfg->split needs
  * less). Every call on one device shares that device's buffer and finds the

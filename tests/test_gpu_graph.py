@@ -81,3 +81,34 @@ def test_copy_rowsum_gemm_replayed_from_one_graph():
         pt.pipe_tile_copy(dst, src, stages=1)
         torch.cuda.synchronize()
         assert np.array_equal(_bits(src), _bits(dst)), rep
+
+
+def test_grouped_loads_copy_replayed_from_a_graph():
+    """The grouped-load copy (strips of 4 tile columns, S = 8) captured and
+    replayed on fresh inputs, bit for bit against the oracle's copy."""
+    M, N = 1024, 2048
+    src = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    dst = torch.empty_like(src)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    cfg = dict(stages=8, producer_waves=4, consumer_waves=8, status=status,
+               flags=pt.PIPE_FLAG_STRIP_GROUPS | pt.PIPE_FLAG_GROUP_LOADS |
+               pt.PIPE_FLAG_NONTEMPORAL | pt.PIPE_FLAG_LAZY_COMMIT)
+    src.copy_(synth.uniform((M, N), torch.float16, seed=60).to(DEV))
+    pt.pipe_tile_copy(src, dst, **cfg)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pt.pipe_tile_copy(src, dst, **cfg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((61, 62, 63, 64)):
+        src.copy_(synth.uniform((M, N), torch.float16, seed=seed).to(DEV))
+        dst.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, rep
+        assert np.array_equal(_bits(dst), R.tile_copy(src.cpu().numpy()).view(np.uint16)), rep

@@ -57,3 +57,41 @@ def test_noalloc_rowsum_full_size_and_rejects_oversized():
     with pytest.raises(pt.PipeError) as e:
         pt.pipe_rowsum_noalloc(big, out, split=8)
     assert e.value.status == pt.PIPE_ERR_WORKSPACE
+
+
+@pytest.mark.gpu
+def test_noalloc_rowsum_captured_and_replayed():
+    """The allocation-free row sum inside a captured HIP graph: the first call
+    on the device runs eagerly (it looks up the buffer's address), then the
+    capture, then four replays on fresh inputs with eager row sums between
+    them, every replay checked against the oracle."""
+    print("[no_alloc] graph capture and replay", flush=True)
+    M, N = 1000, 3000                       # ragged edges, split 4 tickets
+    A = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    out = torch.empty(M, dtype=torch.float32, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    A.copy_(synth.small_int((M, N), -8, 8, torch.float16, seed=30).to(DEV))
+    pt.pipe_rowsum_noalloc(A, out, status=st)   # eager first call on this device
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pt.pipe_rowsum_noalloc(A, out, status=st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    other = synth.small_int((512, 8192), -8, 8, torch.float16, seed=31).to(DEV)
+    other_out = torch.empty(512, device=DEV)
+    for rep, seed in enumerate((32, 33, 34, 35)):
+        A.copy_(synth.small_int((M, N), -8, 8, torch.float16, seed=seed).to(DEV))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, rep
+        assert np.array_equal(out.cpu().numpy(), R.rowsum_exact(A.cpu().numpy())), rep
+        # an eager call between replays leaves its own contents in the buffer
+        pt.pipe_rowsum_noalloc(other, other_out, status=st, split=8)
+        torch.cuda.synchronize()
+        assert np.array_equal(other_out.cpu().numpy(), R.rowsum_exact(other.cpu().numpy())), rep
