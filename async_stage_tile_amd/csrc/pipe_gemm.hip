@@ -528,6 +528,96 @@ __device__ __forceinline__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
+// Consumer wave of a ring with three or more stages, 128-row tiles and fp32 C
+// (one workgroup per CU: one MFMA wave per SIMD, and registers to spare).
+// Fragment reads run two K sub-steps ahead of the MFMAs through four register
+// buffers. A stage's last reads go out with its second sub-step's MFMAs, so the
+// wave hands the slot back half-way through the stage's MFMAs, once those
+// reads have returned, and the producer can refill it sooner.
+template <int S, int PW, bool BCOL, bool MASKED>
+__device__ __forceinline__ void gemm_consumer_deep(const GemmParams& p, GemmLds<S, 1>& lds, int cw) {
+  const int lane = lane_id();
+  const int wm = cw >> 1, wn = cw & 1;
+  const int li = lane & 31, lk = lane >> 5;
+  PipeState rd = consumer_start(S);
+  bool ok = true;
+  for (int item = blockIdx.x; ok && item < p.items; item += gridDim.x) {
+    int tm, tn;
+    gemm_tile_of(p, item, tm, tn);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    SubFrags f0, f1, f2, f3;
+    if (!bar_wait<Counter<PW>>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+      ok = false;
+      break;
+    }
+    const uint8_t* sa = &lds.a[rd.index][0];
+    const uint8_t* sb = &lds.b[rd.index][0];
+    load_sub<BCOL>(f0, 0, sa, sb, wm, wn, li, lk, lane, p);
+    load_sub<BCOL>(f1, 1, sa, sb, wm, wn, li, lk, lane, p);
+    for (int ks = 0; ks + 1 < p.k_steps; ++ks) {
+      load_sub<BCOL>(f2, 2, sa, sb, wm, wn, li, lk, lane, p);
+      mfma_sub(acc, f0);
+      interleave_mfma_reads<BCOL>();
+      load_sub<BCOL>(f3, 3, sa, sb, wm, wn, li, lk, lane, p);
+      mfma_sub(acc, f1);
+      interleave_mfma_reads<BCOL>();
+      // consumer_release: every read of the slot has returned (the scheduling
+      // barrier keeps the MFMAs above ahead of the wait).
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();
+      Counter<4>::arrive(&lds.empty[rd.index]);
+      rd.inc();
+      if (!bar_wait<Counter<PW>>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
+        ok = false;
+        break;
+      }
+      sa = &lds.a[rd.index][0];
+      sb = &lds.b[rd.index][0];
+      load_sub<BCOL>(f0, 0, sa, sb, wm, wn, li, lk, lane, p);
+      mfma_sub(acc, f2);
+      interleave_mfma_reads<BCOL>();
+      load_sub<BCOL>(f1, 1, sa, sb, wm, wn, li, lk, lane, p);
+      mfma_sub(acc, f3);
+      interleave_mfma_reads<BCOL>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!ok) break;
+    // The tile's last stage.
+    load_sub<BCOL>(f2, 2, sa, sb, wm, wn, li, lk, lane, p);
+    mfma_sub(acc, f0);
+    interleave_mfma_reads<BCOL>();
+    load_sub<BCOL>(f3, 3, sa, sb, wm, wn, li, lk, lane, p);
+    mfma_sub(acc, f1);
+    interleave_mfma_reads<BCOL>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    Counter<4>::arrive(&lds.empty[rd.index]);
+    rd.inc();
+    mfma_sub(acc, f2);
+    mfma_sub(acc, f3);
+    // Epilogue: fp32 accumulators -> C.
+    float* C = static_cast<float*>(p.C);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int col = tn * kGemmTile + wn * 64 + ni * 32 + li;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = tm * kGemmTile + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+          if (!MASKED || (row < p.M && col < p.N)) C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+        }
+      }
+  }
+  if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
+}
+
 // Store wave of the staged epilogue: for every tile, drains the 4 chunks of
 // each wave pair (pair 0 and pair 1 alternately) and writes them to C.
 template <bool MASKED>
@@ -602,6 +692,12 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       gemm_producer<S, PW, BCOL, false, MT, MASKED>(p, lds, wave);
     else
       gemm_consumer<S, PW, EPI, BCOL, false, MT, MASKED>(p, lds, &out, wave - PW);
+  } else if constexpr (S >= 3 && MT == 1 && !TRACE) {
+    __syncthreads();
+    if (wave < PW)
+      gemm_producer<S, PW, BCOL, false, 1, MASKED>(p, lds, wave);
+    else
+      gemm_consumer_deep<S, PW, BCOL, MASKED>(p, lds, wave - PW);
   } else {
     __syncthreads();
     if (wave < PW)
