@@ -84,9 +84,11 @@ WIDE_COPY = {
 _G = 0x4000
 GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _IL | _LZ | _G)
 # The same strips with grouped loads (PIPE_FLAG_GROUP_LOADS): producers fill the
-# 4 slots of a tile row with 2-row x 512-byte loads.
+# 4 slots of a tile row with 2-row x 512-byte loads. 16 interleaved segments per
+# strip: 1024 workgroups of 32 tiles, four in a row on each CU (the best of the
+# ring depth, wave count and segment sweeps measured for it).
 _GL = 0x80000
-GROUP_LOAD_COPY = dict(stages=8, producer_waves=4, consumer_waves=8,
+GROUP_LOAD_COPY = dict(stages=8, producer_waves=4, consumer_waves=4, split=16,
                        flags=_NT | _IL | _LZ | _G | _GL)
 # The register producer engine (PIPE_FLAG_PRODUCER_VGPR): global_load_dwordx4
 # into registers, then ds_write_b128 into the slot.

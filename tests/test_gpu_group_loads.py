@@ -109,20 +109,24 @@ def test_group_loads_missing_release_times_out():
     assert int(st.item()) & pt.PIPE_STATUS_TIMEOUT_PRODUCER
 
 
-@pytest.mark.parametrize("S,C,PW", [(8, 4, 4), (8, 8, 4), (4, 4, 4)])
-def test_group_loads_full_size_bit_exact(S, C, PW):
-    """fp16 16384 x 16384 uniform[-1,1): 64 strips of 4 tile columns, 4
-    interleaved segments each (the launch the benchmark times)."""
-    print(f"[group_loads] full size S={S} C={C} PW={PW}", flush=True)
+@pytest.mark.parametrize("S,C,PW,split,remap", [(8, 4, 4, 4, True), (8, 8, 4, 4, True),
+                                                 (4, 4, 4, 4, True), (8, 4, 4, 16, False)])
+def test_group_loads_full_size_bit_exact(S, C, PW, split, remap):
+    """fp16 16384 x 16384 uniform[-1,1): 64 strips of 4 tile columns, in 4
+    interleaved segments each, or in 16 without the XCD remap (the launch the
+    benchmark times: 1024 workgroups of 32 tiles)."""
+    print(f"[group_loads] full size S={S} C={C} PW={PW} split={split} remap={remap}", flush=True)
     src = synth.uniform((16384, 16384), torch.float16, seed=42, device=DEV)
     flags = GL | pt.PIPE_FLAG_SPLIT_INTERLEAVE | pt.PIPE_FLAG_NONTEMPORAL | \
-        pt.PIPE_FLAG_XCD_REMAP | pt.PIPE_FLAG_LAZY_COMMIT
+        pt.PIPE_FLAG_LAZY_COMMIT | (pt.PIPE_FLAG_XCD_REMAP if remap else 0)
     q = pt.pipe_query_kernel(pt.PIPE_OP_COPY, 16384, 16384, stages=S, consumer_waves=C,
-                             producer_waves=PW, flags=flags)
-    assert (q["items"], q["grid"], q["tiles_per_item"], q["split"]) == (256, 256, 128, 4)
+                             producer_waves=PW, split=split, flags=flags)
+    items = 64 * split
+    assert (q["items"], q["grid"], q["tiles_per_item"], q["split"]) == \
+        (items, items, 128 * 4 // split, split)
     st = _status()
-    dst = pt.pipe_tile_copy(src, stages=S, consumer_waves=C, producer_waves=PW, flags=flags,
-                            status=st)
+    dst = pt.pipe_tile_copy(src, stages=S, consumer_waves=C, producer_waves=PW, split=split,
+                            flags=flags, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
