@@ -36,6 +36,28 @@ def test_gemm_small_integers_bit_exact(S, PW, policy):
     assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
 
 
+
+@pytest.mark.parametrize("S", [3, 4])
+@pytest.mark.parametrize("K", [64, 128, 192])
+@pytest.mark.parametrize("PW", [2, 4])
+@pytest.mark.parametrize("bcol", [False, True])
+def test_gemm_deep_rings_short_k_bit_exact(S, K, PW, bcol):
+    """Rings of three or more stages on whole tiles with one, two or three K
+    steps (the deep consumer's tail alone, then with one and two loop passes).
+    Six output tiles on five workgroups, so one workgroup carries the ring's
+    cursor from one tile into the next."""
+    M, N = 256, 384
+    A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=K + S, stream=0).to(DEV)
+    Bt = synth.small_int((N, K), -2, 2, torch.bfloat16, seed=K + S, stream=1).to(DEV)
+    B = _colmajor(Bt) if bcol else Bt.t().contiguous()
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, stages=S, producer_waves=PW, grid=5, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = R.gemm_f64(_f32(A), _f32(Bt).T.copy())
+    bad = np.argwhere(C.cpu().numpy() != ref)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+
 @pytest.mark.parametrize("shift", [0, 1])
 @pytest.mark.parametrize("b_linear", [False, True])
 def test_gemm_swizzle_variants_bit_exact(shift, b_linear):
