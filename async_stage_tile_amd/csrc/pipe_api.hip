@@ -323,11 +323,25 @@ hipError_t launch_stream_op(int op, const pipe_config_t& c, const StreamGeom& g,
                        stream);
 }
 
-pipe_status_t resolve_status(const pipe_config_t& c, uint32_t** out) {
+// The library's own per-device memory (status word, row-sum buffer) is looked
+// up for the current device, so a launch that uses it must go to a stream of
+// that device; the null stream always does.
+pipe_status_t check_stream_device(hipStream_t st) {
+  if (st == nullptr) return PIPE_OK;
+  int cur = 0;
+  hipDevice_t dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(st, &dev) != hipSuccess)
+    return PIPE_ERR_HIP;
+  return dev == cur ? PIPE_OK : PIPE_ERR_CONFIG;
+}
+
+pipe_status_t resolve_status(const pipe_config_t& c, hipStream_t st, uint32_t** out) {
   if (c.status != nullptr) {
     *out = c.status;
     return PIPE_OK;
   }
+  const pipe_status_t s = check_stream_device(st);
+  if (s != PIPE_OK) return s;
   return library_status_word(out);
 }
 
@@ -481,9 +495,11 @@ pipe_status_t rowsum_call(const void* A, float* out, int64_t M, int64_t N, int64
   p.ld_dst = 0;
   p.M = M;
   p.N = N;
-  s = resolve_status(c, &p.status);
+  s = resolve_status(c, st, &p.status);
   if (s != PIPE_OK) return s;
   if (use_scratch && ws.bytes > 0) {
+    s = check_stream_device(st);
+    if (s != PIPE_OK) return s;
     uint8_t* buf = nullptr;
     s = library_scratch(&buf);
     if (s != PIPE_OK) return s;
@@ -564,7 +580,7 @@ pipe_status_t pipe_tile_copy(const void* src, void* dst, int64_t M, int64_t N, i
   p.ld_dst = ld_dst * 2;
   p.M = M;
   p.N = N;
-  s = resolve_status(c, &p.status);
+  s = resolve_status(c, static_cast<hipStream_t>(stream), &p.status);
   if (s != PIPE_OK) return s;
   return hip_status(launch_stream_op(kOpCopy, c, g, p, static_cast<hipStream_t>(stream)));
 }
@@ -623,7 +639,7 @@ pipe_status_t pipe_gemm_mainloop(const void* A, const void* B, void* C, int64_t 
   p.A = static_cast<const uint8_t*>(A);
   p.B = static_cast<const uint8_t*>(B);
   p.C = C;
-  s = resolve_status(c, &p.status);
+  s = resolve_status(c, st, &p.status);
   if (s != PIPE_OK) return s;
   return hip_status(launch_gemm(c.stages, c.producer_waves, grid, p, st));
 }

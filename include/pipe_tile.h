@@ -25,6 +25,10 @@
  *     no per-call host state; it is safe to call from several host threads.
  *   - `stream` is a hipStream_t (NULL = the default stream). Calls are
  *     asynchronous: results are visible after the caller synchronises.
+ *   - Calls that use the library's own device memory -- its status word (when
+ *     cfg->status is NULL) or pipe_rowsum_noalloc's buffer -- look it up on the
+ *     current device, so a non-NULL `stream` must belong to that device (else
+ *     PIPE_ERR_CONFIG, nothing enqueued).
  *   - Arguments are validated before anything is launched; on any error no
  *     work is enqueued and the error code is returned.
  *   - A stalled handshake never hangs the device: each wait gives up after
