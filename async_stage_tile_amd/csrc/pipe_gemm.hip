@@ -528,14 +528,15 @@ __device__ __forceinline__ void gemm_consumer(const GemmParams& p, GemmLds<S, MT
   if (!ok && lane == 0) atomicOr(p.status, kStatusTimeoutConsumer);
 }
 
-// Consumer wave of a ring with three or more stages, 128-row tiles and fp32 C
-// (one workgroup per CU: one MFMA wave per SIMD, and registers to spare).
+// Consumer wave of a ring with three or more stages and fp32 C (one workgroup
+// per CU, so registers to spare: 169 VGPRs with 128-row tiles, 148 with
+// 256-row tiles, no spills).
 // Fragment reads run two K sub-steps ahead of the MFMAs through four register
 // buffers. A stage's last reads go out with its second sub-step's MFMAs, so the
 // wave hands the slot back half-way through the stage's MFMAs, once those
 // reads have returned, and the producer can refill it sooner.
-template <int S, int PW, bool BCOL, bool MASKED>
-__device__ __forceinline__ void gemm_consumer_deep(const GemmParams& p, GemmLds<S, 1>& lds, int cw) {
+template <int S, int PW, bool BCOL, bool MASKED, int MT = 1>
+__device__ __forceinline__ void gemm_consumer_deep(const GemmParams& p, GemmLds<S, MT>& lds, int cw) {
   const int lane = lane_id();
   const int wm = cw >> 1, wn = cw & 1;
   const int li = lane & 31, lk = lane >> 5;
@@ -571,7 +572,7 @@ __device__ __forceinline__ void gemm_consumer_deep(const GemmParams& p, GemmLds<
       // barrier keeps the MFMAs above ahead of the wait).
       __builtin_amdgcn_sched_barrier(0);
       wait_lgkmcnt0();
-      Counter<4>::arrive(&lds.empty[rd.index]);
+      Counter<4 * MT>::arrive(&lds.empty[rd.index]);
       rd.inc();
       if (!bar_wait<Counter<PW>>(&lds.full[rd.index], rd.phase, p.spin_limit)) {
         ok = false;
@@ -597,7 +598,7 @@ __device__ __forceinline__ void gemm_consumer_deep(const GemmParams& p, GemmLds<
     interleave_mfma_reads<BCOL>();
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();
-    Counter<4>::arrive(&lds.empty[rd.index]);
+    Counter<4 * MT>::arrive(&lds.empty[rd.index]);
     rd.inc();
     mfma_sub(acc, f2);
     mfma_sub(acc, f3);
@@ -610,7 +611,7 @@ __device__ __forceinline__ void gemm_consumer_deep(const GemmParams& p, GemmLds<
         const int col = tn * kGemmTile + wn * 64 + ni * 32 + li;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = tm * kGemmTile + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+          const int row = tm * kGemmTile * MT + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
           if (!MASKED || (row < p.M && col < p.N)) C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
         }
       }
@@ -692,12 +693,12 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p) {
       gemm_producer<S, PW, BCOL, false, MT, MASKED>(p, lds, wave);
     else
       gemm_consumer<S, PW, EPI, BCOL, false, MT, MASKED>(p, lds, &out, wave - PW);
-  } else if constexpr (S >= 3 && MT == 1 && !TRACE) {
+  } else if constexpr (S >= 3 && !TRACE) {
     __syncthreads();
     if (wave < PW)
-      gemm_producer<S, PW, BCOL, false, 1, MASKED>(p, lds, wave);
+      gemm_producer<S, PW, BCOL, false, MT, MASKED>(p, lds, wave);
     else
-      gemm_consumer_deep<S, PW, BCOL, MASKED>(p, lds, wave - PW);
+      gemm_consumer_deep<S, PW, BCOL, MASKED, MT>(p, lds, wave - PW);
   } else {
     __syncthreads();
     if (wave < PW)
