@@ -12,6 +12,7 @@ The functions carry the C ABI's names (``include/pipe_tile.h``):
     pipe_kernel_resources(op, M, N, K=0, **cfg)            -> dict
     pipe_rowsum_workspace_bytes(M, N, **cfg)               -> int
     pipe_device_status(clear=False)                        -> int
+    pipe_status_from_word(word)                            -> int (PIPE_OK / _ERR_TIMEOUT / _ERR_INVARIANT)
 
 ``cfg`` keywords are the fields of ``pipe_config_t`` (stages, consumer_waves,
 grid, split, swizzle_shift, flags, spin_limit, trace, status, ...).
@@ -37,6 +38,7 @@ PIPE_ERR_CONFIG = 5
 PIPE_ERR_WORKSPACE = 6
 PIPE_ERR_HIP = 7
 PIPE_ERR_TIMEOUT = 8
+PIPE_ERR_INVARIANT = 9
 
 PIPE_OP_COPY = 0
 PIPE_OP_ROWSUM = 1
@@ -147,6 +149,7 @@ _SIGS = {
                                          _c.c_int64, _c.c_int64,
                                          _c.POINTER(pipe_kernel_resources_t)]),
     "pipe_device_status": (_c.c_int, [_c.POINTER(_c.c_uint32), _c.c_int]),
+    "pipe_status_from_word": (_c.c_int, [_c.c_uint32]),
 }
 
 
@@ -449,6 +452,12 @@ def pipe_device_status(clear: bool = False) -> int:
     out = ctypes.c_uint32(0)
     _check(lib().pipe_device_status(ctypes.byref(out), 1 if clear else 0), "pipe_device_status")
     return int(out.value)
+
+
+def pipe_status_from_word(word: int) -> int:
+    """The error code a status word stands for (PIPE_OK, PIPE_ERR_TIMEOUT or
+    PIPE_ERR_INVARIANT); host arithmetic in the library, no device access."""
+    return int(lib().pipe_status_from_word(int(word) & 0xFFFFFFFF))
 
 
 # ---------------------------------------------------------------------------

@@ -535,6 +535,7 @@ const char* pipe_status_str(int status) {
     case PIPE_ERR_WORKSPACE: return "workspace missing or too small";
     case PIPE_ERR_HIP: return "HIP runtime error";
     case PIPE_ERR_TIMEOUT: return "pipeline wait timed out";
+    case PIPE_ERR_INVARIANT: return "pipeline invariant check failed";
     default: return "unknown status";
   }
 }
@@ -751,6 +752,12 @@ pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int6
   out->lds_bytes = (int32_t)attr.sharedSizeBytes;
   out->scratch_bytes = (int32_t)attr.localSizeBytes;
   out->max_threads = attr.maxThreadsPerBlock;
+  return PIPE_OK;
+}
+
+pipe_status_t pipe_status_from_word(uint32_t word) {
+  if (word & PIPE_STATUS_INVARIANT) return PIPE_ERR_INVARIANT;
+  if (word & (PIPE_STATUS_TIMEOUT_PRODUCER | PIPE_STATUS_TIMEOUT_CONSUMER)) return PIPE_ERR_TIMEOUT;
   return PIPE_OK;
 }
 

@@ -57,7 +57,8 @@ typedef enum {
   PIPE_ERR_CONFIG = 5,    /* unsupported tile shape, wave counts, grid, split or flags */
   PIPE_ERR_WORKSPACE = 6, /* workspace missing or smaller than required */
   PIPE_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
-  PIPE_ERR_TIMEOUT = 8    /* (device status) a pipeline wait exceeded spin_limit */
+  PIPE_ERR_TIMEOUT = 8,   /* (device status) a pipeline wait exceeded spin_limit */
+  PIPE_ERR_INVARIANT = 9  /* (device status) a check of PIPE_FLAG_DEBUG_CHECKS failed */
 } pipe_status_t;
 
 /* The two sentinels give the type the range of int32, so that any int a
@@ -343,6 +344,13 @@ pipe_status_t pipe_kernel_resources(pipe_op_t op, const pipe_config_t* cfg, int6
  * device (used when cfg->status is NULL); clears it when `clear` != 0.
  * Part of this library's error reporting, not an operation of the pages. */
 pipe_status_t pipe_device_status(uint32_t* out, int clear);
+
+/* The error code a status word stands for, on the host (no HIP call): PIPE_OK
+ * for 0, PIPE_ERR_INVARIANT when PIPE_STATUS_INVARIANT is set, else
+ * PIPE_ERR_TIMEOUT when a timeout bit is set. For a word read back from
+ * cfg->status or with pipe_device_status after the caller synchronised. Part
+ * of this library's error reporting, not an operation of the pages. */
+pipe_status_t pipe_status_from_word(uint32_t word);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = pt.lib()
     declared = _declared()
-    assert len(declared) == 11
+    assert len(declared) == 12
     for name in declared:
         assert hasattr(L, name), name
     assert sorted(pt.exported_symbols()) == declared
@@ -75,7 +75,22 @@ def test_version_and_status_strings():
     assert pt.abi_version() == 1
     assert pt.status_str(pt.PIPE_OK) == "ok"
     assert "timed out" in pt.status_str(pt.PIPE_ERR_TIMEOUT)
+    assert "invariant" in pt.status_str(pt.PIPE_ERR_INVARIANT)
     assert pt.status_str(99) == "unknown status"
+
+
+def test_status_word_to_error_code():
+    """Each status bit maps to its error code; the invariant bit wins over a
+    timeout (a broken protocol can also stall a wait)."""
+    f = pt.pipe_status_from_word
+    assert f(0) == pt.PIPE_OK
+    assert f(pt.PIPE_STATUS_TIMEOUT_PRODUCER) == pt.PIPE_ERR_TIMEOUT
+    assert f(pt.PIPE_STATUS_TIMEOUT_CONSUMER) == pt.PIPE_ERR_TIMEOUT
+    assert f(pt.PIPE_STATUS_TIMEOUT_PRODUCER | pt.PIPE_STATUS_TIMEOUT_CONSUMER) == \
+        pt.PIPE_ERR_TIMEOUT
+    assert f(pt.PIPE_STATUS_INVARIANT) == pt.PIPE_ERR_INVARIANT
+    assert f(pt.PIPE_STATUS_INVARIANT | pt.PIPE_STATUS_TIMEOUT_CONSUMER) == pt.PIPE_ERR_INVARIANT
+    assert f(0x80000000) == pt.PIPE_OK      # bits the library never sets
 
 
 def test_config_defaults():

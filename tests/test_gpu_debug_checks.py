@@ -101,6 +101,7 @@ def test_early_release_is_reported(S, C, PW):
     status = int(st.item())
     assert status & pt.PIPE_STATUS_INVARIANT
     assert not status & (pt.PIPE_STATUS_TIMEOUT_PRODUCER | pt.PIPE_STATUS_TIMEOUT_CONSUMER)
+    assert pt.pipe_status_from_word(status) == pt.PIPE_ERR_INVARIANT
 
 
 def test_full_size_copy_under_checks():

@@ -185,6 +185,7 @@ def test_start_phase_zero_times_out_instead_of_hanging():
     torch.cuda.synchronize()
     v = int(st.item())
     assert v & pt.PIPE_STATUS_TIMEOUT_PRODUCER and v & pt.PIPE_STATUS_TIMEOUT_CONSUMER
+    assert pt.pipe_status_from_word(v) == pt.PIPE_ERR_TIMEOUT
 
 
 def test_missing_release_times_out_instead_of_hanging():
