@@ -1,5 +1,5 @@
-"""Static name check of the top-level scripts that only a GPU machine runs in full
-(bench.py, __graft_entry__.py): every function they call by plain name must be
+"""Static name check of the top-level scripts that only run in full on a machine
+with a GPU (bench.py, __graft_entry__.py): every function they call by plain name must be
 defined, imported or bound somewhere in scope, so that a helper removed by
 mistake fails here instead of midway through a GPU run."""
 import ast
