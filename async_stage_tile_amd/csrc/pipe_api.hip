@@ -352,6 +352,23 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
   pipe_status_t s = check_common(c);
   if (s != PIPE_OK) return s;
   if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
+  // The unified kernel: 256 x 256 tiles, 16 waves that all load and compute, a
+  // two-stage ring, fp32 C (the producer count and commit policy do not apply).
+  if (c.flags & PIPE_FLAG_UNIFIED) {
+    if (c.tile_m != 256 || c.tile_n != 256 || c.tile_k != 64 ||
+        c.consumer_waves != kGemmUnifiedWaves)
+      return PIPE_ERR_CONFIG;
+    if (c.stages != 2) return PIPE_ERR_STAGES;
+    if (c.split > 1) return PIPE_ERR_CONFIG;
+    if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS |
+                   PIPE_FLAG_GROUP_LOADS | PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS |
+                   PIPE_FLAG_TEST_JITTER | PIPE_FLAG_TEST_EARLY_RELEASE | PIPE_FLAG_TRACE |
+                   PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE | PIPE_FLAG_TEST_START_PHASE0))
+      return PIPE_ERR_CONFIG;
+    if ((c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) && (c.flags & PIPE_FLAG_GEMM_B_LINEAR))
+      return PIPE_ERR_CONFIG;
+    return PIPE_OK;
+  }
   // 128 x 128 output tiles with 4 MFMA waves, or 256 x 128 with 8.
   if ((c.tile_m != 128 && c.tile_m != 256) || c.tile_n != 128 || c.tile_k != 64)
     return PIPE_ERR_CONFIG;
@@ -407,7 +424,8 @@ pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int
   p->M = (int32_t)M;
   p->N = (int32_t)N;
   p->K = (int32_t)K;
-  p->tiles_n = (int32_t)((N + 127) / 128);
+  p->unified = (c.flags & PIPE_FLAG_UNIFIED) ? 1 : 0;
+  p->tiles_n = (int32_t)((N + c.tile_n - 1) / c.tile_n);
   p->k_steps = (int32_t)((K + 63) / 64);
   const int64_t items = ((M + c.tile_m - 1) / c.tile_m) * (int64_t)p->tiles_n;
   p->tile_m = c.tile_m;
@@ -657,12 +675,15 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return PIPE_ERR_SHAPE;
     if ((c.flags & PIPE_FLAG_TRACE) && (M % c.tile_m || N % 128 || K % 64)) return PIPE_ERR_SHAPE;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return PIPE_ERR_SHAPE;
-    const int64_t items = ((M + c.tile_m - 1) / c.tile_m) * ((N + 127) / 128);
+    const int64_t items = ((M + c.tile_m - 1) / c.tile_m) * ((N + c.tile_n - 1) / c.tile_n);
     if (items > INT32_MAX) return PIPE_ERR_SHAPE;
     const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
     const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
-    info->lds_bytes = gemm_lds_bytes(c.stages, c_bf16, store_wave, c.tile_m);
-    info->threads = gemm_threads(c.producer_waves, c_bf16, store_wave, c.tile_m);
+    const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
+    info->lds_bytes = unified ? kGemmUnifiedLdsBytes
+                              : gemm_lds_bytes(c.stages, c_bf16, store_wave, c.tile_m);
+    info->threads = unified ? 64 * kGemmUnifiedWaves
+                            : gemm_threads(c.producer_waves, c_bf16, store_wave, c.tile_m);
     info->items = (int32_t)items;
     info->grid = (c.grid == 0 || c.grid > info->items) ? info->items : c.grid;
     info->tiles_per_item = (int32_t)((K + 63) / 64);

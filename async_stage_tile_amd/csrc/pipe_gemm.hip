@@ -761,6 +761,144 @@ __global__ void __launch_bounds__(64 * (PW + 4), gemm_waves_per_simd(S, PW, kEpi
 
 using GemmKernel = void (*)(GemmParams);
 
+// ---------------------------------------------------------------------------
+// Unified GEMM for 256 x 256 output tiles (PIPE_FLAG_UNIFIED): no producer and
+// consumer roles. All 16 waves of the workgroup (1024 threads, one workgroup
+// per CU) load a share of every stage and all compute, so each SIMD holds four
+// MFMA waves; the ring has two slots of 64 KiB (A: 256 x 64, B: 64 x 256).
+// Per K step a wave waits for its own loads of the stage (vmcnt), one
+// workgroup barrier then says that every wave's loads have landed and that
+// every wave has finished reading the other slot, the stage after next is
+// issued into that slot, and the wave runs its 16 MFMAs on its 64 x 64 block.
+// ---------------------------------------------------------------------------
+constexpr int kUniWaves = kGemmUnifiedWaves;
+constexpr int kUniStageBlocks = 64;                         // 1 KiB blocks per stage
+constexpr int kUniLoads = kUniStageBlocks / kUniWaves;      // per wave and stage
+static_assert(kUniLoads == 4, "four DMA blocks per wave and stage");
+
+struct UniLds {
+  uint8_t a[2][2 * kAStageBytes];  // 256 rows x 64 K, rows as in the 256-row ring
+  uint8_t b[2][2 * kBStageBytes];  // row-major B: two 128-column halves; column-major: 256 rows
+};
+static_assert(sizeof(UniLds) == kGemmUnifiedLdsBytes, "unified ring size");
+
+// Issue this wave's 4 DMA blocks of K step ks of output tile (tm, tn) into slot `slot`.
+template <bool BCOL, bool MASKED>
+__device__ __forceinline__ void uni_issue(const GemmParams& p, UniLds& lds, int slot, int tm,
+                                          int tn, int ks, int wave, int lane) {
+  const int k_left = p.K - ks * kGemmK;
+  const uint8_t* a0 = p.A + (int64_t)tm * 256 * p.lda + (int64_t)ks * kGemmK * 2;
+  const int a_rows = p.M - tm * 256;
+  const int b_cols = p.N - tn * 256;
+  const uint32_t sa = uniform(lds_addr(&lds.a[slot][0]));
+  const uint32_t sb = uniform(lds_addr(&lds.b[slot][0]));
+#pragma unroll
+  for (int j = 0; j < kUniLoads; ++j) {
+    const int q = wave * kUniLoads + j;  // waves 0-7 load A, waves 8-15 load B (uniform)
+    if (q < 32) {
+      const int r = q * 8 + (lane >> 3);
+      const int c = swz(r, lane & 7, p.swz_shift);
+      dma_block(chunk_src<MASKED>(a0 + (int64_t)r * p.lda + c * 16, r < a_rows && c * 8 < k_left),
+                sa + q * kBlockBytes);
+    } else if constexpr (BCOL) {
+      // Column-major B: 256 rows (output columns) of 64 K, laid out as A.
+      const int qb = q - 32;
+      const int r = qb * 8 + (lane >> 3);
+      const int c = swz(r, lane & 7, p.swz_shift);
+      const uint8_t* b0 = p.B + (int64_t)tn * 256 * p.ldb + (int64_t)ks * kGemmK * 2;
+      dma_block(chunk_src<MASKED>(b0 + (int64_t)r * p.ldb + c * 16, r < b_cols && c * 8 < k_left),
+                sb + qb * kBlockBytes);
+    } else {
+      // Row-major B: half h holds columns 128 h .. 128 h + 127 of the 64 K-rows.
+      const int qb = q - 32;
+      const int h = qb >> 4, qq = qb & 15;
+      const int r = qq * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ swz_b(r, p.b_swz);
+      const uint8_t* b0 = p.B + (int64_t)tn * 512 + (int64_t)h * kBRowBytes +
+                          (int64_t)ks * kGemmK * p.ldb;
+      dma_block(chunk_src<MASKED>(b0 + (int64_t)r * p.ldb + c * 16,
+                                  r < k_left && h * 128 + c * 8 < b_cols),
+                sb + h * kBStageBytes + qq * kBlockBytes);
+    }
+  }
+}
+
+template <bool BCOL, bool MASKED>
+__global__ void __launch_bounds__(64 * kUniWaves, 1) gemm_unified_kernel(GemmParams p) {
+  __shared__ UniLds lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int wm = wave >> 2, wn = wave & 3;  // this wave's 64 x 64 block of the 256 x 256 tile
+  const int li = lane & 31, lk = lane >> 5;
+  // Row-major B: the wave's 64 columns lie in half wn / 2; column-major B: rows of one slot.
+  const int b_off = BCOL ? 0 : (wn >> 1) * kBStageBytes;
+  const int bwn = BCOL ? wn : (wn & 1);
+  int slot = 0;
+  int item = blockIdx.x;
+  if (item < p.items) uni_issue<BCOL, MASKED>(p, lds, 0, item / p.tiles_n, item % p.tiles_n, 0, wave, lane);
+  for (; item < p.items; item += gridDim.x) {
+    const int tm = item / p.tiles_n, tn = item % p.tiles_n;
+    const int next = item + (int)gridDim.x;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int ks = 0; ks < p.k_steps; ++ks) {
+      // This wave's loads of step ks have landed; after the barrier every wave's
+      // have, and every wave has finished reading the other slot.
+      wait_vmcnt<0>();
+      __syncthreads();
+      // The next stage to fetch: this tile's next K step, or the first of the
+      // workgroup's next tile.
+      const bool more = ks + 1 < p.k_steps;
+      const int itm = more ? tm : next / p.tiles_n;
+      const int itn = more ? tn : next % p.tiles_n;
+      if (more || next < p.items)
+        uni_issue<BCOL, MASKED>(p, lds, slot ^ 1, itm, itn, more ? ks + 1 : 0, wave, lane);
+      // Four MFMA waves share each SIMD, so one wave's fragment reads are
+      // covered by the others' MFMAs: one sub-step's fragments at a time.
+      const uint8_t* sa = &lds.a[slot][0];
+      const uint8_t* sb = &lds.b[slot][b_off];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        SubFrags f;
+        load_sub<BCOL>(f, kk, sa, sb, wm, bwn, li, lk, lane, p);
+        mfma_sub(acc, f);
+      }
+      // The slot's reads have returned before the next barrier.
+      wait_lgkmcnt0();
+      slot ^= 1;
+    }
+    float* C = static_cast<float*>(p.C);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int col = tn * 256 + wn * 64 + ni * 32 + li;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = tm * 256 + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+          if (!MASKED || (row < p.M && col < p.N)) C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+        }
+      }
+  }
+  wait_vmcnt<0>();
+}
+
+hipError_t launch_gemm_unified(int stages, int grid, const GemmParams& p, hipStream_t stream) {
+  if (stages != 2 || p.c_bf16 || p.trace != nullptr) return hipErrorInvalidValue;
+  const bool bcol = p.b_colmajor != 0;
+  const bool masked = (p.M % 256) != 0 || (p.N % 256) != 0 || (p.K % kGemmK) != 0;
+  GemmKernel k = masked ? (bcol ? gemm_unified_kernel<true, true> : gemm_unified_kernel<false, true>)
+                        : (bcol ? gemm_unified_kernel<true, false> : gemm_unified_kernel<false, false>);
+  return launch_or_record(k, dim3(grid), dim3(64 * kUniWaves), stream, p);
+}
+
+
+
 // The kernel for ring depth S, or null where its LDS would not fit a CU.
 template <int S, int PW, int EPI, int MT>
 GemmKernel gemm_pick(bool bcol, bool masked) {
@@ -826,6 +964,7 @@ hipError_t launch_gemm_mt(int stages, int producers, int grid, const GemmParams&
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream) {
+  if (p.unified) return launch_gemm_unified(stages, grid, p, stream);
   if (p.tile_m == 256) return launch_gemm_mt<2>(stages, producers, grid, p, stream);
   if (p.tile_m == 128) return launch_gemm_mt<1>(stages, producers, grid, p, stream);
   return hipErrorInvalidValue;

@@ -166,10 +166,16 @@ struct GemmParams {
   int32_t c_bf16;         // C is bf16, written through an LDS-staged epilogue
   int32_t store_wave;     // bf16 C: a dedicated store wave drains the staging slots
   int32_t tile_m;         // output tile rows: 128 (4 MFMA waves) or 256 (8 MFMA waves)
+  int32_t unified;        // 256 x 256 tiles, 16 waves that all load and compute
 };
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream);
+
+// The unified GEMM (256 x 256 tiles, PIPE_FLAG_UNIFIED): 16 waves, a two-slot
+// ring of 64 KiB stages.
+constexpr int kGemmUnifiedWaves = 16;
+constexpr int kGemmUnifiedLdsBytes = 2 * (32768 + 32768);
 
 // Kernel lookup without a launch. While the calling thread's record slot is
 // set, launch_or_record stores the address of the kernel it was given there

@@ -90,6 +90,9 @@ GROUPED_COPY = dict(stages=5, producer_waves=2, consumer_waves=4, flags=_NT | _I
 _GL = 0x80000
 GROUP_LOAD_COPY = dict(stages=8, producer_waves=4, consumer_waves=4, split=16,
                        flags=_NT | _IL | _LZ | _G | _GL)
+# The GEMM without warp specialisation: 256 x 256 output tiles, all 16 waves
+# load a share of each stage and all compute, one barrier per K step.
+UNIFIED_GEMM = dict(tile_m=256, tile_n=256, consumer_waves=16, flags=_U)
 # The register producer engine (PIPE_FLAG_PRODUCER_VGPR): global_load_dwordx4
 # into registers, then ds_write_b128 into the slot.
 _V = 0x8000
@@ -482,13 +485,13 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colma
     flops = 2.0 * n * n * n
     c = pt._gemm_config(C, kw, b_colmajor)
     gcfg = {f: getattr(c, f) for f in ("stages", "producer_waves", "consumer_waves", "tile_m",
-                                       "flags", "swizzle_shift", "grid")}
+                                       "tile_n", "flags", "swizzle_shift", "grid")}
     q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, n, n, n, **gcfg)
     return {"c_dtype": str(C.dtype).replace("torch.", ""),
             "b_layout": "column-major" if b_colmajor else "row-major", "stages": c.stages,
             "tile": [c.tile_m, c.tile_n, c.tile_k],
-            "producer_waves": c.producer_waves, "flags": c.flags,
-            "wall_ms": wall, "kernel_ms": kern, "flops": flops,
+            "producer_waves": 0 if c.flags & pt.PIPE_FLAG_UNIFIED else c.producer_waves,
+            "flags": c.flags, "wall_ms": wall, "kernel_ms": kern, "flops": flops,
             "tflops": flops / (wall * 1e-3) / 1e12,
             "mfma_frac": flops / (wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "per_launch": {"median_ms": med, "min_ms": mn,
@@ -779,7 +782,7 @@ def main():
                                        "copy_group_loads",
                                        "copy_regs", "copy_pitch", "rowsum", "rowsum_regs",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
-                                       "gemm_bcol", "gemm_tile256", "ceiling", "calib"],
+                                       "gemm_bcol", "gemm_tile256", "gemm_unified", "ceiling", "calib"],
                     default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
@@ -852,6 +855,10 @@ def main():
         r = bench_gemm(args.steps, args.warmup, args.stages or 3, tile_m=256, consumer_waves=8,
                        producer_waves=4)
         log(f"[bench] gemm, 256 x 128 tiles: {r}")
+        return
+    if args.only == "gemm_unified":
+        r = bench_gemm(args.steps, args.warmup, 2, **UNIFIED_GEMM)
+        log(f"[bench] gemm, unified 256 x 256 tiles: {r}")
         return
     if args.only == "gemm_bcol":
         r = bench_gemm(args.steps, args.warmup, args.stages, b_colmajor=True)
@@ -1002,6 +1009,10 @@ def main():
                        consumer_waves=8, producer_waves=4)
         log(f"[bench] gemm, 256 x 128 tiles, three-stage ring: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_tile_256x128"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=2, **UNIFIED_GEMM)
+        log(f"[bench] gemm, unified 256 x 256 tiles (16 waves load and compute): "
+            f"{g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_unified_256x256"] = g
         g = bench_gemm(max(3, args.steps // 2), args.warmup, out_dtype=torch.bfloat16)
         log(f"[bench] gemm, bf16 C: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16"] = g

@@ -87,7 +87,13 @@ typedef enum {
                                           consumer_waves waves (2, 4 or 8) each load and use their
                                           share of every tile, with per-wave batch waits and no
                                           full/empty barriers; M % 128 == N % 64 == 0 only, no
-                                          checksums or trace (else PIPE_ERR_CONFIG) */
+                                          checksums or trace (else PIPE_ERR_CONFIG).
+                                          gemm: 256 x 256 output tiles (tile_m = tile_n = 256,
+                                          consumer_waves = 16, stages = 2, fp32 C, no trace; else
+                                          PIPE_ERR_CONFIG / PIPE_ERR_STAGES) -- all 16 waves load
+                                          a share of each stage and compute, with one workgroup
+                                          barrier per K step; producer_waves and the commit
+                                          policy do not apply */
 #define PIPE_FLAG_LAZY_COMMIT 0x80u    /* copy/rowsum/gemm (specialised ring): the producer commits
                                           a tile only once `lag` younger tiles are in flight, never
                                           while its acquire waits for a slot. Without this flag a
@@ -179,7 +185,8 @@ typedef struct {
                              2 or 4, consumer_waves 4 or 8 -- unified: 2 or 4); gemm 128,
                              or 256 with 8 consumer and 4 producer waves (S 1..3, S 1..2
                              with bf16 C; no store wave, no trace)                        */
-  int32_t tile_n;         /* copy/rowsum: 64, 128 or 256 fp16 (see tile_m); gemm: 128    */
+  int32_t tile_n;         /* copy/rowsum: 64, 128 or 256 fp16 (see tile_m); gemm: 128,   
+                             or 256 with PIPE_FLAG_UNIFIED                               */
   int32_t tile_k;         /* gemm only: 64                                                */
   int32_t producer_waves; /* copy/rowsum: 1, 2 or 4; gemm: 2 or 4 (each tile's loads split
                              evenly; a wave keeps up to 2, 6 or 14 tiles of commit lag)   */
@@ -310,7 +317,7 @@ pipe_status_t pipe_rowsum_noalloc(const void* A, float* out, int64_t M, int64_t 
  * (optionally by a dedicated store wave, PIPE_FLAG_GEMM_STORE_WAVE). A and B tiles
  * of each 64-deep K step pass through the LDS ring to MFMA consumer waves.
  *   M arbitrary, N % 8 == 0 and K % 8 == 0 (whole 16-byte chunks; else
- *   PIPE_ERR_SHAPE). Shapes that are not whole tiles (M % tile_m, N % 128 or
+ *   PIPE_ERR_SHAPE). Shapes that are not whole tiles (M % tile_m, N % tile_n or
  *   K % 64 non-zero) run a masked kernel: chunks outside A or B enter the ring
  *   as zeros and only C's M x N elements are written (with PIPE_FLAG_TRACE
  *   such shapes return PIPE_ERR_SHAPE). lda >= K and ldb >= N (ldb >= K for

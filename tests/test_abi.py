@@ -562,3 +562,36 @@ def test_gemm_256_row_tiles_geometry_and_rejections():
     assert status(256, flags=pt.PIPE_FLAG_GEMM_C_BF16 | pt.PIPE_FLAG_GEMM_STORE_WAVE, **T) == \
         pt.PIPE_ERR_CONFIG
     assert status(256, flags=pt.PIPE_FLAG_TRACE, **T) != pt.PIPE_OK   # (no trace buffer either)
+
+
+def test_gemm_unified_validation_and_geometry():
+    """The unified GEMM (256 x 256 tiles, 16 waves) is its own configuration:
+    its geometry comes back from the host query, and every neighbouring
+    setting is rejected before any HIP call."""
+    U = dict(tile_m=256, tile_n=256, consumer_waves=16, stages=2, flags=pt.PIPE_FLAG_UNIFIED)
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096, **U)
+    assert (q["items"], q["grid"], q["threads"], q["lds_bytes"], q["tiles_per_item"]) == \
+        (256, 256, 1024, 131072, 64)
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 1000, 600, 72, **U)
+    assert (q["items"], q["tiles_per_item"]) == (4 * 3, 2)
+    info = pt.pipe_kernel_info_t()
+
+    def status(**kw):
+        c = pt.make_config(pt.PIPE_OP_GEMM, **kw)
+        return pt.lib().pipe_query_kernel(pt.PIPE_OP_GEMM, ctypes.byref(c), 512, 512, 512,
+                                          ctypes.byref(info))
+
+    assert status(**U) == pt.PIPE_OK
+    assert status(**dict(U, stages=3)) == pt.PIPE_ERR_STAGES
+    assert status(**dict(U, stages=1)) == pt.PIPE_ERR_STAGES
+    assert status(**dict(U, consumer_waves=8)) == pt.PIPE_ERR_CONFIG
+    assert status(**dict(U, tile_n=128)) == pt.PIPE_ERR_CONFIG
+    assert status(**dict(U, tile_m=128)) == pt.PIPE_ERR_CONFIG
+    assert status(**dict(U, flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_GEMM_C_BF16)) == \
+        pt.PIPE_ERR_CONFIG
+    assert status(**dict(U, flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_GEMM_B_COLMAJOR |
+                         pt.PIPE_FLAG_GEMM_B_LINEAR)) == pt.PIPE_ERR_CONFIG
+    # 256-column tiles only come with the unified flag, and the flag only with them.
+    assert status(tile_m=256, tile_n=256, consumer_waves=16, stages=2) == pt.PIPE_ERR_CONFIG
+    assert status(flags=pt.PIPE_FLAG_UNIFIED) == pt.PIPE_ERR_CONFIG
+    assert status(tile_m=256, consumer_waves=8, flags=pt.PIPE_FLAG_UNIFIED) == pt.PIPE_ERR_CONFIG
