@@ -351,14 +351,21 @@ pipe_status_t hip_status(hipError_t e) { return e == hipSuccess ? PIPE_OK : PIPE
 pipe_status_t gemm_check_config(const pipe_config_t& c) {
   pipe_status_t s = check_common(c);
   if (s != PIPE_OK) return s;
-  if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
-  // The unified kernel: 256 x 256 tiles, 16 waves that all load and compute, a
-  // two-stage ring, fp32 C (the producer count and commit policy do not apply).
+  // The unified kernels: 256 x 256 tiles, waves that all load and compute,
+  // fp32 C (the producer count and commit policy do not apply). 16 waves:
+  // 64-K stages, two slots. 4 waves: the same, or 32-K stages in three to
+  // five slots.
   if (c.flags & PIPE_FLAG_UNIFIED) {
-    if (c.tile_m != 256 || c.tile_n != 256 || c.tile_k != 64 ||
-        c.consumer_waves != kGemmUnifiedWaves)
+    if (c.tile_m != 256 || c.tile_n != 256) return PIPE_ERR_CONFIG;
+    if (c.consumer_waves == kGemmUnifiedWaves) {
+      if (c.tile_k != 64) return PIPE_ERR_CONFIG;
+      if (c.stages != 2) return PIPE_ERR_STAGES;
+    } else if (c.consumer_waves == kGemmWideWaves) {
+      if (c.tile_k != 64 && c.tile_k != 32) return PIPE_ERR_CONFIG;
+      if (c.tile_k == 64 ? c.stages != 2 : (c.stages < 3 || c.stages > 5)) return PIPE_ERR_STAGES;
+    } else {
       return PIPE_ERR_CONFIG;
-    if (c.stages != 2) return PIPE_ERR_STAGES;
+    }
     if (c.split > 1) return PIPE_ERR_CONFIG;
     if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS |
                    PIPE_FLAG_GROUP_LOADS | PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS |
@@ -369,6 +376,7 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
       return PIPE_ERR_CONFIG;
     return PIPE_OK;
   }
+  if (c.stages < 1 || c.stages > 4) return PIPE_ERR_STAGES;
   // 128 x 128 output tiles with 4 MFMA waves, or 256 x 128 with 8.
   if ((c.tile_m != 128 && c.tile_m != 256) || c.tile_n != 128 || c.tile_k != 64)
     return PIPE_ERR_CONFIG;
@@ -424,9 +432,9 @@ pipe_status_t gemm_fill_params(const pipe_config_t& c, int64_t M, int64_t N, int
   p->M = (int32_t)M;
   p->N = (int32_t)N;
   p->K = (int32_t)K;
-  p->unified = (c.flags & PIPE_FLAG_UNIFIED) ? 1 : 0;
+  p->unified = (c.flags & PIPE_FLAG_UNIFIED) ? c.consumer_waves : 0;
   p->tiles_n = (int32_t)((N + c.tile_n - 1) / c.tile_n);
-  p->k_steps = (int32_t)((K + 63) / 64);
+  p->k_steps = (int32_t)((K + c.tile_k - 1) / c.tile_k);
   const int64_t items = ((M + c.tile_m - 1) / c.tile_m) * (int64_t)p->tiles_n;
   p->tile_m = c.tile_m;
   if (items > INT32_MAX) return PIPE_ERR_SHAPE;
@@ -680,13 +688,13 @@ pipe_status_t pipe_query_kernel(pipe_op_t op, const pipe_config_t* cfg, int64_t 
     const bool c_bf16 = (c.flags & PIPE_FLAG_GEMM_C_BF16) != 0;
     const bool store_wave = (c.flags & PIPE_FLAG_GEMM_STORE_WAVE) != 0;
     const bool unified = (c.flags & PIPE_FLAG_UNIFIED) != 0;
-    info->lds_bytes = unified ? kGemmUnifiedLdsBytes
+    info->lds_bytes = unified ? (c.tile_k == 32 ? c.stages * 32768 : kGemmUnifiedLdsBytes)
                               : gemm_lds_bytes(c.stages, c_bf16, store_wave, c.tile_m);
-    info->threads = unified ? 64 * kGemmUnifiedWaves
+    info->threads = unified ? 64 * c.consumer_waves
                             : gemm_threads(c.producer_waves, c_bf16, store_wave, c.tile_m);
     info->items = (int32_t)items;
     info->grid = (c.grid == 0 || c.grid > info->items) ? info->items : c.grid;
-    info->tiles_per_item = (int32_t)((K + 63) / 64);
+    info->tiles_per_item = (int32_t)((K + c.tile_k - 1) / c.tile_k);
     info->split = 1;
     return PIPE_OK;
   }

@@ -782,8 +782,9 @@ struct UniLds {
 };
 static_assert(sizeof(UniLds) == kGemmUnifiedLdsBytes, "unified ring size");
 
-// Issue this wave's 4 DMA blocks of K step ks of output tile (tm, tn) into slot `slot`.
-template <bool BCOL, bool MASKED>
+// Issue this wave's LOADS DMA blocks of K step ks of output tile (tm, tn) into
+// slot `slot`: blocks wave * LOADS .. wave * LOADS + LOADS - 1 of the stage's 64.
+template <bool BCOL, bool MASKED, int LOADS = kUniLoads>
 __device__ __forceinline__ void uni_issue(const GemmParams& p, UniLds& lds, int slot, int tm,
                                           int tn, int ks, int wave, int lane) {
   const int k_left = p.K - ks * kGemmK;
@@ -793,8 +794,8 @@ __device__ __forceinline__ void uni_issue(const GemmParams& p, UniLds& lds, int 
   const uint32_t sa = uniform(lds_addr(&lds.a[slot][0]));
   const uint32_t sb = uniform(lds_addr(&lds.b[slot][0]));
 #pragma unroll
-  for (int j = 0; j < kUniLoads; ++j) {
-    const int q = wave * kUniLoads + j;  // waves 0-7 load A, waves 8-15 load B (uniform)
+  for (int j = 0; j < LOADS; ++j) {
+    const int q = wave * LOADS + j;  // blocks 0-31 are A, 32-63 B (uniform per wave)
     if (q < 32) {
       const int r = q * 8 + (lane >> 3);
       const int c = swz(r, lane & 7, p.swz_shift);
@@ -888,10 +889,458 @@ __global__ void __launch_bounds__(64 * kUniWaves, 1) gemm_unified_kernel(GemmPar
   wait_vmcnt<0>();
 }
 
+// ---------------------------------------------------------------------------
+// The same ring with 4 waves, one per SIMD, each owning a 128 x 128 block of
+// the tile (4 x 4 MFMA blocks of 32 x 32). Per MFMA it reads half the fragment
+// bytes of a 64 x 64 block. Its 256 fp32 accumulators per lane fit only because
+// a lone wave on a SIMD may use all 512 of the SIMD's registers per lane
+// (vector and accumulation registers together). The register file is split
+// evenly between the waves resident on a SIMD, so a producer wave beside it
+// would halve that budget: this layout exists only without warp
+// specialisation. One wave per SIMD also means no other wave hides a fragment
+// read, so each wave reads the next sub-step's fragments while its 16 MFMAs
+// on the current one run.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = kGemmWideWaves;
+constexpr int kWideLoads = kUniStageBlocks / kWideWaves;  // 16 per wave and stage
+
+struct WideFrags {
+  bf16x8 a[4];
+  bf16x8 b[4];
+};
+
+template <bool BCOL>
+__device__ __forceinline__ void load_wide(WideFrags& f, int kk, const uint8_t* sa,
+                                          const uint8_t* sb, int wm, int wn, int li, int lk,
+                                          int lane, const GemmParams& p) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+    f.a[mi] = load_row_frag(sa, wm * 128 + mi * 32, kk, li, lk, p.swz_shift);
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    if constexpr (BCOL)
+      f.b[ni] = load_row_frag(sb, wn * 128 + ni * 32, kk, li, lk, p.swz_shift);
+    else
+      f.b[ni] = load_b_frag(sb, kk * 16, ni * 32, lane, p.b_swz);
+  }
+}
+
+__device__ __forceinline__ void mfma_wide(f32x16 (&acc)[4][4], const WideFrags& f) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// Output tile of work item `item` in an order that keeps each XCD's tiles
+// together. Workgroups go to the 8 XCDs in turn, so with 8 | items the items
+// are first dealt so that each XCD walks one contiguous eighth of the order;
+// the order then runs down bands of kWideGroupM tile rows, column by column,
+// so the tiles an XCD holds at once share few A rows and B columns (4 x 8 tiles
+// for a 16 x 16 grid: 12 K-slices per step where row-major order needs 18).
+// A bijection on [0, items) for every shape and grid.
+constexpr int kWideGroupM = 4;
+__device__ __forceinline__ void wide_tile_of(const GemmParams& p, int item, int& tm, int& tn) {
+  const int per_xcd = p.items >> 3;
+  const int q = (p.items & 7) ? item : (item & 7) * per_xcd + (item >> 3);
+  const int band = kWideGroupM * p.tiles_n;
+  const int first = (q / band) * kWideGroupM;
+  const int tiles_m = p.items / p.tiles_n;
+  const int rows = min(tiles_m - first, kWideGroupM);
+  const int local = q - (first / kWideGroupM) * band;
+  tm = first + local % rows;
+  tn = local / rows;
+}
+
+template <bool BCOL, bool MASKED>
+__global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_kernel(GemmParams p) {
+  __shared__ UniLds lds;
+  const int wave = (int)(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int wm = wave >> 1, wn = wave & 1;  // this wave's 128 x 128 block of the 256 x 256 tile
+  const int li = lane & 31, lk = lane >> 5;
+  // Row-major B: the wave's 128 columns are half wn of the slot; column-major B:
+  // rows wn * 128 .. wn * 128 + 127 of the slot.
+  const int b_off = BCOL ? 0 : wn * kBStageBytes;
+  int slot = 0;
+  int item = blockIdx.x;
+  if (item < p.items) {
+    int tm0, tn0;
+    wide_tile_of(p, item, tm0, tn0);
+    uni_issue<BCOL, MASKED, kWideLoads>(p, lds, 0, tm0, tn0, 0, wave, lane);
+  }
+  for (; item < p.items; item += gridDim.x) {
+    int tm, tn, ntm = 0, ntn = 0;
+    wide_tile_of(p, item, tm, tn);
+    const int next = item + (int)gridDim.x;
+    if (next < p.items) wide_tile_of(p, next, ntm, ntn);
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int ks = 0; ks < p.k_steps; ++ks) {
+      // As in the 16-wave kernel: every wave's loads of step ks have landed and
+      // every wave has finished reading the other slot.
+      wait_vmcnt<0>();
+      __syncthreads();
+      const bool more = ks + 1 < p.k_steps;
+      if (more || next < p.items)
+        uni_issue<BCOL, MASKED, kWideLoads>(p, lds, slot ^ 1, more ? tm : ntm, more ? tn : ntn,
+                                            more ? ks + 1 : 0, wave, lane);
+      const uint8_t* sa = &lds.a[slot][0];
+      const uint8_t* sb = &lds.b[slot][b_off];
+      WideFrags f[2];
+      load_wide<BCOL>(f[0], 0, sa, sb, wm, wn, li, lk, lane, p);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) load_wide<BCOL>(f[(kk + 1) & 1], kk + 1, sa, sb, wm, wn, li, lk, lane, p);
+        mfma_wide(acc, f[kk & 1]);
+      }
+      wait_lgkmcnt0();
+      slot ^= 1;
+    }
+    float* C = static_cast<float*>(p.C);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int col = tn * 256 + wn * 128 + ni * 32 + li;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = tm * 256 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+          if (!MASKED || (row < p.M && col < p.N)) C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+        }
+      }
+  }
+  wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------
+// The 4-wave unified GEMM on a deeper ring: stages of 32 K instead of 64, so 3
+// to 5 slots fit in LDS and up to S - 1 stages are in flight while the waves
+// compute. A stage holds A as 256 rows of 64 bytes and B as two 128-column
+// halves of 32 K-rows (row-major B) or as 256 rows of 64 bytes like A
+// (column-major B), 32 KiB in all; each wave issues 4 of its 16 A blocks and
+// 4 of its 16 B blocks. Rows of 64 bytes (4 chunks) take the chunk XOR
+// (row >> 2) & 3, which spreads any 16 consecutive rows' reads of one chunk
+// over all 64 banks.
+//
+// One workgroup barrier per step, half-way through it: once the wave has
+// issued its MFMAs on the step's first 16 K, it waits until its loads of the
+// next stage have landed and joins the barrier. After it, every wave's loads
+// of that stage have landed, and every wave has finished reading the slot of
+// the step before (its reads fed MFMAs that were issued before the barrier),
+// so the stage S - 1 ahead goes into that slot. The next stage's first
+// fragments are then read while the MFMAs on this step's second 16 K run.
+// Between tiles, the next tile's first S - 1 stages are issued before this
+// tile's C stores, and the wave drains its counter before the next tile's
+// first step.
+// ---------------------------------------------------------------------------
+constexpr int kDeepK = 32;                        // K per stage
+constexpr int kDeepHalfBytes = 256 * kDeepK * 2;  // 16 KiB: A, or B, of one stage
+constexpr int kDeepStageBytes = 2 * kDeepHalfBytes;
+constexpr int kDeepLoads = kDeepStageBytes / kBlockBytes / kWideWaves;  // 8 per wave and stage
+
+// Chunk position of K chunk c (0-3) in row r of a 64-byte-row slot, and back.
+__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// Sources of this wave's 8 DMA blocks of one tile, at K = 0: A blocks and B
+// blocks wave * 4 .. wave * 4 + 3 of each operand's 16. Step ks adds ks * 64
+// bytes (A, column-major B) or 32 ks K-rows (row-major B). In a 64-byte-row
+// block, lane l writes row 16 q + l / 4 at position l % 4, which holds K
+// chunk (l % 4) ^ ((l / 16) % 4) for every block q; a 256-byte K-row of
+// row-major B holds chunk (l % 16) ^ swz_b(r) at position l % 16.
+struct DeepSrc {
+  const uint8_t* a[4];
+  const uint8_t* b[4];
+  uint32_t rows_in;  // MASKED: bit j: block j's A row inside M; bit 4 + j: its B row or columns inside N
+};
+
+template <bool BCOL>
+__device__ __forceinline__ void deep_src(const GemmParams& p, int tm, int tn, int wave, int lane,
+                                         DeepSrc& s) {
+  const int c = (lane & 3) ^ ((lane >> 4) & 3);
+  s.rows_in = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int qq = wave * 4 + j;
+    const int r = qq * 16 + (lane >> 2);
+    s.a[j] = p.A + (int64_t)(tm * 256 + r) * p.lda + c * 16;
+    s.rows_in |= (r < p.M - tm * 256 ? 1u : 0u) << j;
+    if constexpr (BCOL) {
+      s.b[j] = p.B + (int64_t)(tn * 256 + r) * p.ldb + c * 16;
+      s.rows_in |= (r < p.N - tn * 256 ? 1u : 0u) << (4 + j);
+    } else {
+      const int h = qq >> 3, qb = qq & 7;
+      const int kr = qb * 4 + (lane >> 4);
+      const int cb = (lane & 15) ^ swz_b(kr, p.b_swz);
+      s.b[j] = p.B + (int64_t)kr * p.ldb + (int64_t)tn * 512 + h * kBRowBytes + cb * 16;
+      s.rows_in |= (h * 128 + cb * 8 < p.N - tn * 256 ? 1u : 0u) << (4 + j);
+    }
+  }
+}
+
+// DMA block j (0-3: A, 4-7: B) of stage ks into the slot at `sbase`.
+template <bool BCOL, bool MASKED>
+__device__ __forceinline__ void deep_dma(const GemmParams& p, const DeepSrc& s, uint32_t sbase,
+                                         int ks, int j, int wave, int lane) {
+  const int k_left = p.K - ks * kDeepK;
+  if (j < 4) {
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    dma_block(chunk_src<MASKED>(s.a[j] + ks * (kDeepK * 2), ((s.rows_in >> j) & 1) && c * 8 < k_left),
+              sbase + (wave * 4 + j) * kBlockBytes);
+  } else {
+    const int jb = j - 4;
+    const int qq = wave * 4 + jb;
+    bool inside;
+    const uint8_t* src;
+    if constexpr (BCOL) {
+      const int c = (lane & 3) ^ ((lane >> 4) & 3);
+      src = s.b[jb] + ks * (kDeepK * 2);
+      inside = ((s.rows_in >> (4 + jb)) & 1) && c * 8 < k_left;
+    } else {
+      const int kr = (qq & 7) * 4 + (lane >> 4);
+      src = s.b[jb] + (int64_t)ks * kDeepK * p.ldb;
+      inside = ((s.rows_in >> (4 + jb)) & 1) && kr < k_left;
+    }
+    dma_block(chunk_src<MASKED>(src, inside), sbase + kDeepHalfBytes + qq * kBlockBytes);
+  }
+}
+
+template <bool BCOL, bool MASKED>
+__device__ __forceinline__ void deep_issue(const GemmParams& p, const DeepSrc& s, uint32_t sbase,
+                                           int ks, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < kDeepLoads; ++j) deep_dma<BCOL, MASKED>(p, s, sbase, ks, j, wave, lane);
+}
+
+// The 16 MFMAs of one sub-step with this wave's 8 DMA blocks of stage ks
+// issued between them, one after every second MFMA, so the matrix unit is
+// fed while the loads go out.
+template <bool BCOL, bool MASKED>
+__device__ __forceinline__ void mfma_wide_with_dma(f32x16 (&acc)[4][4], const WideFrags& f,
+                                                   const GemmParams& p, const DeepSrc& s,
+                                                   uint32_t sbase, int ks, int wave, int lane) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+      if ((ni & 1) == 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        deep_dma<BCOL, MASKED>(p, s, sbase, ks, mi * 2 + (ni >> 1), wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+}
+
+// A (or column-major B) fragment of a 64-byte-row slot: lane l takes K chunk
+// kk * 2 + l / 32 of row row0 + l % 32.
+__device__ __forceinline__ bf16x8 load_row_frag4(const uint8_t* slot, int row0, int kk, int li,
+                                                 int lk) {
+  const int r = row0 + li;
+  return *reinterpret_cast<const bf16x8*>(slot + r * 64 + swz4(r, kk * 2 + lk) * 16);
+}
+
+template <bool BCOL>
+__device__ __forceinline__ void load_deep(WideFrags& f, int kk, const uint8_t* sa,
+                                          const uint8_t* sb, int wm, int wn, int li, int lk,
+                                          int lane, const GemmParams& p) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) f.a[mi] = load_row_frag4(sa, wm * 128 + mi * 32, kk, li, lk);
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    if constexpr (BCOL)
+      f.b[ni] = load_row_frag4(sb, wn * 128 + ni * 32, kk, li, lk);
+    else
+      f.b[ni] = load_b_frag(sb, kk * 16, ni * 32, lane, p.b_swz);
+  }
+}
+
+// Piece q of sub-step kk's fragments in a 64-byte-row slot: q = 0-3 the A
+// fragment of row block q, q = 4-7 the B fragment of column block q - 4 (one
+// b128 read, or two transposing b64 reads for row-major B).
+template <bool BCOL>
+__device__ __forceinline__ void load_deep_piece(WideFrags& f, int q, int kk, const uint8_t* sa,
+                                                const uint8_t* sb, int wm, int wn, int li, int lk,
+                                                int lane, const GemmParams& p) {
+  if (q < 4) {
+    f.a[q] = load_row_frag4(sa, wm * 128 + q * 32, kk, li, lk);
+  } else if constexpr (BCOL) {
+    f.b[q - 4] = load_row_frag4(sb, wn * 128 + (q - 4) * 32, kk, li, lk);
+  } else {
+    f.b[q - 4] = load_b_frag(sb, kk * 16, (q - 4) * 32, lane, p.b_swz);
+  }
+}
+
+// The 16 MFMAs of one sub-step on fragments f, with the 8 pieces of the next
+// sub-step's fragments g read one after each of the first 8 MFMAs, so the
+// LDS queue never holds a burst that would stall the wave's MFMA issue. With
+// DMA, this wave's 8 DMA blocks of stage ks go out one after every second
+// MFMA as well. Unrolled by template recursion: the schedule pins take
+// constants.
+template <int I, bool BCOL, bool MASKED, bool DMA>
+__device__ __forceinline__ void mfma_wide_pipelined(f32x16 (&acc)[4][4], const WideFrags& f,
+                                                    WideFrags& g, int kk, const uint8_t* sa,
+                                                    const uint8_t* sb, int wm, int wn, int li,
+                                                    int lk, int lane, const GemmParams& p,
+                                                    const DeepSrc& s, uint32_t sbase, int ks,
+                                                    int wave) {
+  if constexpr (I < 16) {
+    constexpr int kReads = (I < 4 || BCOL) ? 1 : 2;  // LDS reads of piece I
+    acc[I >> 2][I & 3] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[I >> 2], f.b[I & 3], acc[I >> 2][I & 3], 0, 0, 0);
+    if constexpr (I < 8) load_deep_piece<BCOL>(g, I, kk, sa, sb, wm, wn, li, lk, lane, p);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I < 8) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    if constexpr (DMA && (I & 1) == 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      deep_dma<BCOL, MASKED>(p, s, sbase, ks, I >> 1, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_wide_pipelined<I + 1, BCOL, MASKED, DMA>(acc, f, g, kk, sa, sb, wm, wn, li, lk, lane, p, s,
+                                                  sbase, ks, wave);
+  }
+}
+
+template <int S>
+struct DeepLds {
+  uint8_t ring[S][kDeepStageBytes];
+};
+
+template <int S, bool BCOL, bool MASKED>
+__global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_deep_kernel(GemmParams p) {
+  static_assert(S >= 3, "the slot refilled at a step is the one read a step earlier");
+  __shared__ DeepLds<S> lds;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = lane_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, lk = lane >> 5;
+  // Row-major B: the wave's columns are half wn of the B part (8 KiB each);
+  // column-major B: rows wn * 128 .. of the B part.
+  const int b_off = kDeepHalfBytes + (BCOL ? 0 : wn * (kDeepHalfBytes / 2));
+  const int ksteps = p.k_steps;  // stages of 32 K per tile
+  const int pro = ksteps < S - 1 ? ksteps : S - 1;  // stages issued ahead of a tile's first step
+  const uint32_t ring = uniform(lds_addr(&lds.ring[0][0]));
+  int item = blockIdx.x;
+  if (item >= p.items) return;
+  int tm, tn;
+  wide_tile_of(p, item, tm, tn);
+  DeepSrc src;
+  deep_src<BCOL>(p, tm, tn, wave, lane, src);
+  for (int g = 0; g < pro; ++g)
+    deep_issue<BCOL, MASKED>(p, src, ring + g * kDeepStageBytes, g, wave, lane);
+  // Stage 0 has landed once at most S - 2 stages' loads are younger.
+  if (pro == S - 1) wait_vmcnt<(S - 2) * kDeepLoads>();
+  else wait_vmcnt<0>();
+  for (;;) {
+    __syncthreads();
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    WideFrags f0, f1;
+    load_deep<BCOL>(f0, 0, &lds.ring[0][0], &lds.ring[0][b_off], wm, wn, li, lk, lane, p);
+    int slot = 0;
+    int ks = 0;
+    // Steady state: each step refills the slot of the step before with the
+    // stage S - 1 ahead, and at least S - 3 stages' loads are younger than
+    // the next one's.
+    for (; ks < ksteps - (S - 1); ++ks) {
+      const uint8_t* sl = &lds.ring[slot][0];
+      mfma_wide_pipelined<0, BCOL, MASKED, false>(acc, f0, f1, 1, sl, sl + b_off, wm, wn, li, lk,
+                                               lane, p, src, 0, 0, wave);
+      const int next_slot = slot + 1 == S ? 0 : slot + 1;
+      const int fill = slot == 0 ? S - 1 : slot - 1;  // the slot of step ks - 1
+      wait_vmcnt<(S - 3) * kDeepLoads>();
+      __syncthreads();
+      const uint8_t* nl = &lds.ring[next_slot][0];
+      mfma_wide_pipelined<0, BCOL, MASKED, true>(acc, f1, f0, 0, nl, nl + b_off, wm, wn, li, lk, lane,
+                                              p, src, ring + fill * kDeepStageBytes, ks + S - 1,
+                                              wave);
+      slot = next_slot;
+    }
+    // The tile's last S - 1 steps (or all of a short one) issue nothing.
+    for (; ks < ksteps; ++ks) {
+      const uint8_t* sl = &lds.ring[slot][0];
+      load_deep<BCOL>(f1, 1, sl, sl + b_off, wm, wn, li, lk, lane, p);
+      mfma_wide(acc, f0);
+      const int next_slot = slot + 1 == S ? 0 : slot + 1;
+      if (ks + 1 < ksteps) {
+        // Stage ks + 1 has landed once at most S - 3 stages' loads are
+        // younger; where fewer were issued, the wave drains.
+        if (ks + S - 2 < ksteps) wait_vmcnt<(S - 3) * kDeepLoads>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        const uint8_t* nl = &lds.ring[next_slot][0];
+        load_deep<BCOL>(f0, 0, nl, nl + b_off, wm, wn, li, lk, lane, p);
+      }
+      mfma_wide(acc, f1);
+      slot = next_slot;
+    }
+    // Every wave has issued its last MFMAs, so every slot's reads are done:
+    // the next tile's first stages may refill slots 0 .. S - 2.
+    const int next = item + (int)gridDim.x;
+    int ntm = 0, ntn = 0;
+    if (next < p.items) {
+      wide_tile_of(p, next, ntm, ntn);
+      __syncthreads();
+      deep_src<BCOL>(p, ntm, ntn, wave, lane, src);
+      for (int g = 0; g < pro; ++g)
+        deep_issue<BCOL, MASKED>(p, src, ring + g * kDeepStageBytes, g, wave, lane);
+    }
+    float* C = static_cast<float*>(p.C);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int col = tn * 256 + wn * 128 + ni * 32 + li;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = tm * 256 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
+          if (!MASKED || (row < p.M && col < p.N)) C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+        }
+      }
+    if (next >= p.items) break;
+    item = next;
+    tm = ntm;
+    tn = ntn;
+    wait_vmcnt<0>();
+  }
+  wait_vmcnt<0>();
+}
+
 hipError_t launch_gemm_unified(int stages, int grid, const GemmParams& p, hipStream_t stream) {
-  if (stages != 2 || p.c_bf16 || p.trace != nullptr) return hipErrorInvalidValue;
+  if (stages < 2 || stages > 5 || p.c_bf16 || p.trace != nullptr) return hipErrorInvalidValue;
   const bool bcol = p.b_colmajor != 0;
   const bool masked = (p.M % 256) != 0 || (p.N % 256) != 0 || (p.K % kGemmK) != 0;
+  if (p.unified == kWideWaves && stages >= 3) {
+    const bool dm = (p.M % 256) != 0 || (p.N % 256) != 0 || (p.K % kDeepK) != 0;
+    GemmKernel k = nullptr;
+#define PIPE_DEEP(SS)                                                                     \
+  if (stages == SS)                                                                       \
+    k = dm ? (bcol ? gemm_wide_deep_kernel<SS, true, true> : gemm_wide_deep_kernel<SS, false, true>) \
+           : (bcol ? gemm_wide_deep_kernel<SS, true, false> : gemm_wide_deep_kernel<SS, false, false>);
+    PIPE_DEEP(3)
+    PIPE_DEEP(4)
+    PIPE_DEEP(5)
+#undef PIPE_DEEP
+    if (k == nullptr) return hipErrorInvalidValue;
+    return launch_or_record(k, dim3(grid), dim3(64 * kWideWaves), stream, p);
+  }
+  if (p.unified == kWideWaves) {
+    GemmKernel k = masked ? (bcol ? gemm_wide_kernel<true, true> : gemm_wide_kernel<false, true>)
+                          : (bcol ? gemm_wide_kernel<true, false> : gemm_wide_kernel<false, false>);
+    return launch_or_record(k, dim3(grid), dim3(64 * kWideWaves), stream, p);
+  }
+  if (p.unified != kUniWaves || stages != 2) return hipErrorInvalidValue;
   GemmKernel k = masked ? (bcol ? gemm_unified_kernel<true, true> : gemm_unified_kernel<false, true>)
                         : (bcol ? gemm_unified_kernel<true, false> : gemm_unified_kernel<false, false>);
   return launch_or_record(k, dim3(grid), dim3(64 * kUniWaves), stream, p);

@@ -166,15 +166,16 @@ struct GemmParams {
   int32_t c_bf16;         // C is bf16, written through an LDS-staged epilogue
   int32_t store_wave;     // bf16 C: a dedicated store wave drains the staging slots
   int32_t tile_m;         // output tile rows: 128 (4 MFMA waves) or 256 (8 MFMA waves)
-  int32_t unified;        // 256 x 256 tiles, 16 waves that all load and compute
+  int32_t unified;        // 0, or the unified kernel's waves (16 or 4), which all load and compute
 };
 
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream);
 
-// The unified GEMM (256 x 256 tiles, PIPE_FLAG_UNIFIED): 16 waves, a two-slot
-// ring of 64 KiB stages.
+// The unified GEMM (256 x 256 tiles, PIPE_FLAG_UNIFIED): a two-slot ring of
+// 64 KiB stages, 16 waves of 64 x 64 output blocks or 4 of 128 x 128.
 constexpr int kGemmUnifiedWaves = 16;
+constexpr int kGemmWideWaves = 4;
 constexpr int kGemmUnifiedLdsBytes = 2 * (32768 + 32768);
 
 // Kernel lookup without a launch. While the calling thread's record slot is

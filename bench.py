@@ -93,6 +93,10 @@ GROUP_LOAD_COPY = dict(stages=8, producer_waves=4, consumer_waves=4, split=16,
 # The GEMM without warp specialisation: 256 x 256 output tiles, all 16 waves
 # load a share of each stage and all compute, one barrier per K step.
 UNIFIED_GEMM = dict(tile_m=256, tile_n=256, consumer_waves=16, flags=_U)
+# The same with 4 waves of 128 x 128 output blocks (one wave per SIMD): 64-K
+# stages in two slots, or 32-K stages in four.
+WIDE_GEMM = dict(tile_m=256, tile_n=256, consumer_waves=4, flags=_U)
+DEEP_GEMM = dict(tile_m=256, tile_n=256, tile_k=32, consumer_waves=4, flags=_U)
 # The register producer engine (PIPE_FLAG_PRODUCER_VGPR): global_load_dwordx4
 # into registers, then ds_write_b128 into the slot.
 _V = 0x8000
@@ -485,7 +489,7 @@ def bench_gemm(steps, warmup, stages=None, out_dtype=None, settle_s=0.3, b_colma
     flops = 2.0 * n * n * n
     c = pt._gemm_config(C, kw, b_colmajor)
     gcfg = {f: getattr(c, f) for f in ("stages", "producer_waves", "consumer_waves", "tile_m",
-                                       "tile_n", "flags", "swizzle_shift", "grid")}
+                                       "tile_n", "tile_k", "flags", "swizzle_shift", "grid")}
     q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, n, n, n, **gcfg)
     return {"c_dtype": str(C.dtype).replace("torch.", ""),
             "b_layout": "column-major" if b_colmajor else "row-major", "stages": c.stages,
@@ -782,7 +786,8 @@ def main():
                                        "copy_group_loads",
                                        "copy_regs", "copy_pitch", "rowsum", "rowsum_regs",
                                        "rowsum_32x256", "rowsum_64x128", "gemm", "gemm_bf16",
-                                       "gemm_bcol", "gemm_tile256", "gemm_unified", "ceiling", "calib"],
+                                       "gemm_bcol", "gemm_tile256", "gemm_unified", "gemm_wide", "gemm_deep",
+                                       "ceiling", "calib"],
                     default=None,
                     help="time one workload only (for profiling); prints no JSON line")
     ap.add_argument("--no-extras", action="store_true")
@@ -859,6 +864,14 @@ def main():
     if args.only == "gemm_unified":
         r = bench_gemm(args.steps, args.warmup, 2, **UNIFIED_GEMM)
         log(f"[bench] gemm, unified 256 x 256 tiles: {r}")
+        return
+    if args.only == "gemm_wide":
+        r = bench_gemm(args.steps, args.warmup, 2, **WIDE_GEMM)
+        log(f"[bench] gemm, unified 256 x 256 tiles, 4 waves: {r}")
+        return
+    if args.only == "gemm_deep":
+        r = bench_gemm(args.steps, args.warmup, args.stages or 4, **DEEP_GEMM)
+        log(f"[bench] gemm, unified 256 x 256 x 32 tiles, 4 waves: {r}")
         return
     if args.only == "gemm_bcol":
         r = bench_gemm(args.steps, args.warmup, args.stages, b_colmajor=True)
@@ -1013,6 +1026,12 @@ def main():
         log(f"[bench] gemm, unified 256 x 256 tiles (16 waves load and compute): "
             f"{g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_unified_256x256"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=2, **WIDE_GEMM)
+        log(f"[bench] gemm, unified 256 x 256 tiles, 4 waves: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_unified_256x256_4_waves"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=4, **DEEP_GEMM)
+        log(f"[bench] gemm, unified 256 x 256 x 32 tiles, 4 waves, S = 4: {g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_unified_256x256x32_4_waves_s4"] = g
         g = bench_gemm(max(3, args.steps // 2), args.warmup, out_dtype=torch.bfloat16)
         log(f"[bench] gemm, bf16 C: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16"] = g

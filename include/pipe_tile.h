@@ -89,11 +89,15 @@ typedef enum {
                                           full/empty barriers; M % 128 == N % 64 == 0 only, no
                                           checksums or trace (else PIPE_ERR_CONFIG).
                                           gemm: 256 x 256 output tiles (tile_m = tile_n = 256,
-                                          consumer_waves = 16, stages = 2, fp32 C, no trace; else
-                                          PIPE_ERR_CONFIG / PIPE_ERR_STAGES) -- all 16 waves load
-                                          a share of each stage and compute, with one workgroup
-                                          barrier per K step; producer_waves and the commit
-                                          policy do not apply */
+                                          fp32 C, no trace) whose waves all load a share of each
+                                          stage and compute, with one workgroup barrier per K
+                                          step; producer_waves and the commit policy do not
+                                          apply. consumer_waves = 16 (64 x 64 output blocks):
+                                          tile_k 64, stages 2. consumer_waves = 4 (128 x 128
+                                          blocks, one wave per SIMD): tile_k 64 with stages 2, or
+                                          tile_k 32 with stages 3..5 (the fastest GEMM here; its
+                                          64-byte LDS rows take a fixed chunk XOR and ignore
+                                          swizzle_shift). Else PIPE_ERR_CONFIG / PIPE_ERR_STAGES */
 #define PIPE_FLAG_LAZY_COMMIT 0x80u    /* copy/rowsum/gemm (specialised ring): the producer commits
                                           a tile only once `lag` younger tiles are in flight, never
                                           while its acquire waits for a slot. Without this flag a
@@ -179,7 +183,8 @@ typedef enum {
 
 typedef struct {
   int32_t stages;         /* S, ring depth: copy/rowsum 1..8 (5..8 need 4 or 8 consumer
-                             waves; the ring must fit 160 KiB of LDS); gemm 1..4          */
+                             waves; the ring must fit 160 KiB of LDS); gemm 1..4 (unified:
+                             see PIPE_FLAG_UNIFIED)                                       */
   int32_t tile_m;         /* copy/rowsum: 128, 64 or 32 (with tile_n 64, 128, 256: every
                              tile is 16 KiB; the wider two need S 2..4, producer_waves
                              2 or 4, consumer_waves 4 or 8 -- unified: 2 or 4); gemm 128,
@@ -187,11 +192,12 @@ typedef struct {
                              with bf16 C; no store wave, no trace)                        */
   int32_t tile_n;         /* copy/rowsum: 64, 128 or 256 fp16 (see tile_m); gemm: 128,   
                              or 256 with PIPE_FLAG_UNIFIED                               */
-  int32_t tile_k;         /* gemm only: 64                                                */
+  int32_t tile_k;         /* gemm only: 64, or 32 for the 4-wave unified GEMM             */
   int32_t producer_waves; /* copy/rowsum: 1, 2 or 4; gemm: 2 or 4 (each tile's loads split
                              evenly; a wave keeps up to 2, 6 or 14 tiles of commit lag)   */
   int32_t consumer_waves; /* copy/rowsum: 1, 2, 3, 4 or 8 (unified: 2, 4 or 8); gemm:
-                             tile_m / 32 (4 or 8 MFMA waves, each a 64 x 64 output block) */
+                             tile_m / 32 (4 or 8 MFMA waves, each a 64 x 64 output block);
+                             unified gemm: 16 or 4                                        */
   int32_t grid;           /* workgroups; 0 = one per work item (capped by the device)     */
   int32_t split;          /* copy/rowsum: segments each strip is cut into; 0 = default:
                              copy 1 (G with PIPE_FLAG_STRIP_GROUPS), rowsum the smallest
@@ -315,10 +321,10 @@ pipe_status_t pipe_rowsum_noalloc(const void* A, float* out, int64_t M, int64_t 
  * PIPE_FLAG_GEMM_C_BF16, in bf16 (each fp32 sum rounded to nearest even),
  * staged through LDS so that C is written in whole 16-byte row pieces
  * (optionally by a dedicated store wave, PIPE_FLAG_GEMM_STORE_WAVE). A and B tiles
- * of each 64-deep K step pass through the LDS ring to MFMA consumer waves.
+ * of each K step (tile_k deep) pass through the LDS ring to MFMA waves.
  *   M arbitrary, N % 8 == 0 and K % 8 == 0 (whole 16-byte chunks; else
  *   PIPE_ERR_SHAPE). Shapes that are not whole tiles (M % tile_m, N % tile_n or
- *   K % 64 non-zero) run a masked kernel: chunks outside A or B enter the ring
+ *   K % tile_k non-zero) run a masked kernel: chunks outside A or B enter the ring
  *   as zeros and only C's M x N elements are written (with PIPE_FLAG_TRACE
  *   such shapes return PIPE_ERR_SHAPE). lda >= K and ldb >= N (ldb >= K for
  *   column-major B), both multiples of 8; ldc >= N (elements of C's type; a

@@ -591,6 +591,27 @@ def test_gemm_unified_validation_and_geometry():
         pt.PIPE_ERR_CONFIG
     assert status(**dict(U, flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_GEMM_B_COLMAJOR |
                          pt.PIPE_FLAG_GEMM_B_LINEAR)) == pt.PIPE_ERR_CONFIG
+    # The 4-wave kernels: 64-K stages in two slots, or 32-K stages in 3 to 5.
+    W = dict(U, consumer_waves=4)
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096, **W)
+    assert (q["threads"], q["lds_bytes"], q["tiles_per_item"]) == (256, 131072, 64)
+    for S in (3, 4, 5):
+        q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 1000, 600, 72, **dict(W, tile_k=32, stages=S))
+        assert (q["items"], q["threads"], q["lds_bytes"], q["tiles_per_item"]) == \
+            (12, 256, S * 32768, 3)
+        assert status(**dict(W, tile_k=32, stages=S)) == pt.PIPE_OK
+    assert status(**W) == pt.PIPE_OK
+    assert status(**dict(W, tile_k=32, stages=2)) == pt.PIPE_ERR_STAGES
+    assert status(**dict(W, tile_k=32, stages=6)) == pt.PIPE_ERR_STAGES
+    assert status(**dict(W, stages=3)) == pt.PIPE_ERR_STAGES
+    assert status(**dict(W, tile_k=16, stages=4)) == pt.PIPE_ERR_CONFIG
+    assert status(**dict(U, tile_k=32, stages=4)) == pt.PIPE_ERR_CONFIG   # 16 waves: 64-K only
+    assert status(**dict(W, consumer_waves=2)) == pt.PIPE_ERR_CONFIG
+    assert status(**dict(W, tile_k=32, stages=4, flags=pt.PIPE_FLAG_UNIFIED |
+                         pt.PIPE_FLAG_GEMM_C_BF16)) == pt.PIPE_ERR_CONFIG
+    # Outside the unified flag, tile_k stays 64 and the ring 1..4 deep.
+    assert status(tile_k=32) == pt.PIPE_ERR_CONFIG
+    assert status(stages=5) == pt.PIPE_ERR_STAGES
     # 256-column tiles only come with the unified flag, and the flag only with them.
     assert status(tile_m=256, tile_n=256, consumer_waves=16, stages=2) == pt.PIPE_ERR_CONFIG
     assert status(flags=pt.PIPE_FLAG_UNIFIED) == pt.PIPE_ERR_CONFIG

@@ -1,7 +1,10 @@
-"""GPU parity of the unified GEMM (PIPE_FLAG_UNIFIED: 256 x 256 output tiles,
-16 waves that all load a share of each stage and all compute) against the fp64
+"""GPU parity of the unified GEMMs (PIPE_FLAG_UNIFIED: 256 x 256 output tiles
+whose waves all load a share of each stage and all compute) against the fp64
 CPU oracle: small-integer operands bit for bit (|C| <= 4 K < 2**24 is exact in
-fp32 in any order), uniform[-1, 1) operands within the GEMM tolerance."""
+fp32 in any order), uniform[-1, 1) operands within the GEMM tolerance. Three
+kernels: 16 waves of 64 x 64 output blocks on 64-K stages; 4 waves of
+128 x 128 blocks on 64-K stages; the same 4 waves on 32-K stages in rings of
+3 to 5 slots."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +15,15 @@ from oracle import results as R
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-U = dict(tile_m=256, tile_n=256, consumer_waves=16, stages=2, flags=pt.PIPE_FLAG_UNIFIED)
+_U = pt.PIPE_FLAG_UNIFIED
+KERNELS = {
+    "w16": dict(tile_m=256, tile_n=256, consumer_waves=16, stages=2, flags=_U),
+    "w4": dict(tile_m=256, tile_n=256, consumer_waves=4, stages=2, flags=_U),
+    "w4k32s3": dict(tile_m=256, tile_n=256, tile_k=32, consumer_waves=4, stages=3, flags=_U),
+    "w4k32s4": dict(tile_m=256, tile_n=256, tile_k=32, consumer_waves=4, stages=4, flags=_U),
+    "w4k32s5": dict(tile_m=256, tile_n=256, tile_k=32, consumer_waves=4, stages=5, flags=_U),
+}
+U = KERNELS["w16"]
 
 
 def _f32(t):
@@ -38,46 +49,71 @@ def _run(A, B, **cfg):
     return C
 
 
+def _assert_exact(C, ref):
+    bad = np.argwhere(C.cpu().numpy() != ref)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("shape", [(256, 256, 64), (512, 768, 320), (1000, 1000, 1000),
                                    (300, 264, 72), (1, 8, 8), (257, 520, 136)])
 @pytest.mark.parametrize("bcol", [False, True])
-def test_unified_gemm_small_integers_bit_exact(shape, bcol):
+def test_unified_gemm_small_integers_bit_exact(kernel, shape, bcol):
     M, N, K = shape
-    print(f"[unified] {shape} bcol={bcol}", flush=True)
+    print(f"[unified] {kernel} {shape} bcol={bcol}", flush=True)
     A, B, ref = _operands(M, N, K, seed=M + N + K, bcol=bcol)
-    bad = np.argwhere(_run(A, B, **U).cpu().numpy() != ref)
-    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+    _assert_exact(_run(A, B, **KERNELS[kernel]), ref)
 
 
+@pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("grid", [1, 3, 5])
-def test_unified_gemm_persistent_grid(grid):
-    """Twelve tiles on fewer workgroups: each workgroup fetches its next tile's
-    first stage during the last K step of the current one."""
+def test_unified_gemm_persistent_grid(kernel, grid):
+    """Twelve tiles on fewer workgroups: each workgroup's ring runs on from
+    one tile into the next."""
     A, B, ref = _operands(1024, 768, 384, seed=grid, bcol=False)
-    assert pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 1024, 768, 384, **U)["items"] == 12
-    C = _run(A, B, grid=grid, **U)
-    assert np.array_equal(C.cpu().numpy(), ref)
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 1024, 768, 384, **KERNELS[kernel])
+    assert q["items"] == 12
+    _assert_exact(_run(A, B, grid=grid, **KERNELS[kernel]), ref)
 
 
+@pytest.mark.parametrize("kernel", ["w4k32s3", "w4k32s4", "w4k32s5"])
+@pytest.mark.parametrize("K", [8, 32, 40, 64, 96, 128, 160])
+@pytest.mark.parametrize("bcol", [False, True])
+def test_deep_unified_gemm_short_k(kernel, K, bcol):
+    """K of 1 to 5 stages of 32: fewer steps than the ring is deep, the
+    steady-state loop skipped or run once, ragged last stages; six tiles on
+    five workgroups."""
+    A, B, ref = _operands(768, 512, K, seed=K, bcol=bcol)
+    _assert_exact(_run(A, B, grid=5, **KERNELS[kernel]), ref)
+
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("b_linear", [False, True])
-def test_unified_gemm_uniform_within_tolerance(b_linear):
-    flags = pt.PIPE_FLAG_UNIFIED | (pt.PIPE_FLAG_GEMM_B_LINEAR if b_linear else 0)
+def test_unified_gemm_uniform_within_tolerance(kernel, b_linear):
+    cfg = dict(KERNELS[kernel])
+    cfg["flags"] = cfg["flags"] | (pt.PIPE_FLAG_GEMM_B_LINEAR if b_linear else 0)
     A, B, ref = _operands(1024, 768, 512, seed=7, bcol=False, kind="uniform")
-    res = R.within_tol(_run(A, B, **dict(U, flags=flags)).cpu().numpy(), ref, 1e-2)
+    res = R.within_tol(_run(A, B, **cfg).cpu().numpy(), ref, 1e-2)
     assert res["ok"], res
 
 
-def test_unified_gemm_matches_the_specialised_ring_bitwise():
+@pytest.mark.parametrize("kernel", list(KERNELS))
+def test_unified_gemm_matches_the_specialised_ring_bitwise(kernel):
     """Each output element is one wave's MFMA chain over K in the same order as
-    in the 256 x 128 specialised ring: the two give the same bits."""
+    in the 256 x 128 specialised ring: the kernels give the same bits."""
     A, B, _ = _operands(1000, 1000, 1000, seed=11, bcol=False, kind="uniform")
     T = dict(tile_m=256, consumer_waves=8, producer_waves=4, stages=3,
              flags=pt.PIPE_FLAG_EAGER_NEWEST)
-    assert torch.equal(_run(A, B, **U), _run(A, B, **T))
+    assert torch.equal(_run(A, B, **KERNELS[kernel]), _run(A, B, **T))
 
 
-def test_unified_gemm_4096_small_integers_bit_exact():
-    print("[unified] 4096^3 small integers", flush=True)
+@pytest.mark.parametrize("kernel", ["w16", "w4", "w4k32s4"])
+def test_unified_gemm_4096_small_integers_bit_exact(kernel):
+    print(f"[unified] {kernel} 4096^3 small integers", flush=True)
     A, B, ref = _operands(4096, 4096, 4096, seed=5, bcol=False)
-    bad = np.argwhere(_run(A, B, **U).cpu().numpy() != ref)
-    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+    _assert_exact(_run(A, B, **KERNELS[kernel]), ref)
+
+
+def test_deep_unified_gemm_4096_column_major_bit_exact():
+    A, B, ref = _operands(4096, 4096, 4096, seed=6, bcol=True)
+    _assert_exact(_run(A, B, **KERNELS["w4k32s4"]), ref)
