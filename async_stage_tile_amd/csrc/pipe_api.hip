@@ -370,8 +370,10 @@ pipe_status_t gemm_check_config(const pipe_config_t& c) {
     if (c.flags & (PIPE_FLAG_ROW_STRIPS | PIPE_FLAG_TEST_NO_RELEASE | PIPE_FLAG_STRIP_GROUPS |
                    PIPE_FLAG_GROUP_LOADS | PIPE_FLAG_PRODUCER_VGPR | PIPE_FLAG_DEBUG_CHECKS |
                    PIPE_FLAG_TEST_JITTER | PIPE_FLAG_TEST_EARLY_RELEASE | PIPE_FLAG_TRACE |
-                   PIPE_FLAG_GEMM_C_BF16 | PIPE_FLAG_GEMM_STORE_WAVE | PIPE_FLAG_TEST_START_PHASE0))
+                   PIPE_FLAG_GEMM_STORE_WAVE | PIPE_FLAG_TEST_START_PHASE0))
       return PIPE_ERR_CONFIG;
+    // bf16 C: the 32-K kernel only.
+    if ((c.flags & PIPE_FLAG_GEMM_C_BF16) && c.tile_k != 32) return PIPE_ERR_CONFIG;
     if ((c.flags & PIPE_FLAG_GEMM_B_COLMAJOR) && (c.flags & PIPE_FLAG_GEMM_B_LINEAR))
       return PIPE_ERR_CONFIG;
     return PIPE_OK;

@@ -1212,7 +1212,7 @@ struct DeepLds {
   uint8_t ring[S][kDeepStageBytes];
 };
 
-template <int S, bool BCOL, bool MASKED>
+template <int S, bool BCOL, bool MASKED, bool CBF16 = false>
 __global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_deep_kernel(GemmParams p) {
   static_assert(S >= 3, "the slot refilled at a step is the one read a step earlier");
   __shared__ DeepLds<S> lds;
@@ -1296,16 +1296,31 @@ __global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_deep_kernel(Gemm
       for (int g = 0; g < pro; ++g)
         deep_issue<BCOL, MASKED>(p, src, ring + g * kDeepStageBytes, g, wave, lane);
     }
-    float* C = static_cast<float*>(p.C);
+    // C: each store instruction writes 32 consecutive columns of two rows,
+    // 128 bytes per row in fp32 or 64 in bf16 (rounded to nearest even).
+    // Before any accumulator is read the wave sleeps once: with the bf16
+    // conversion the compiler read the last MFMA's result registers about a
+    // dozen instructions after that MFMA issued, too early to see its sum
+    // (measured: element 2 of the last block kept its previous value). The
+    // schedule fences keep the accumulator reads block by block after it.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
+        if constexpr (CBF16) __builtin_amdgcn_sched_barrier(0);
         const int col = tn * 256 + wn * 128 + ni * 32 + li;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = tm * 256 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
-          if (!MASKED || (row < p.M && col < p.N)) C[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+          if (!MASKED || (row < p.M && col < p.N)) {
+            if constexpr (CBF16)
+              static_cast<__bf16*>(p.C)[(int64_t)row * p.ldc + col] = (__bf16)acc[mi][ni][e];
+            else
+              static_cast<float*>(p.C)[(int64_t)row * p.ldc + col] = acc[mi][ni][e];
+          }
         }
       }
     if (next >= p.items) break;
@@ -1318,20 +1333,25 @@ __global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_deep_kernel(Gemm
 }
 
 hipError_t launch_gemm_unified(int stages, int grid, const GemmParams& p, hipStream_t stream) {
-  if (stages < 2 || stages > 5 || p.c_bf16 || p.trace != nullptr) return hipErrorInvalidValue;
+  if (stages < 2 || stages > 5 || p.trace != nullptr) return hipErrorInvalidValue;
+  if (p.c_bf16 && !(p.unified == kWideWaves && stages >= 3)) return hipErrorInvalidValue;
   const bool bcol = p.b_colmajor != 0;
   const bool masked = (p.M % 256) != 0 || (p.N % 256) != 0 || (p.K % kGemmK) != 0;
   if (p.unified == kWideWaves && stages >= 3) {
     const bool dm = (p.M % 256) != 0 || (p.N % 256) != 0 || (p.K % kDeepK) != 0;
     GemmKernel k = nullptr;
-#define PIPE_DEEP(SS)                                                                     \
-  if (stages == SS)                                                                       \
-    k = dm ? (bcol ? gemm_wide_deep_kernel<SS, true, true> : gemm_wide_deep_kernel<SS, false, true>) \
-           : (bcol ? gemm_wide_deep_kernel<SS, true, false> : gemm_wide_deep_kernel<SS, false, false>);
+#define PIPE_DEEP_C(SS, CB)                                                               \
+  if (stages == SS && p.c_bf16 == (CB ? 1 : 0))                                           \
+    k = dm ? (bcol ? gemm_wide_deep_kernel<SS, true, true, CB>                            \
+                   : gemm_wide_deep_kernel<SS, false, true, CB>)                          \
+           : (bcol ? gemm_wide_deep_kernel<SS, true, false, CB>                           \
+                   : gemm_wide_deep_kernel<SS, false, false, CB>);
+#define PIPE_DEEP(SS) PIPE_DEEP_C(SS, false) PIPE_DEEP_C(SS, true)
     PIPE_DEEP(3)
     PIPE_DEEP(4)
     PIPE_DEEP(5)
 #undef PIPE_DEEP
+#undef PIPE_DEEP_C
     if (k == nullptr) return hipErrorInvalidValue;
     return launch_or_record(k, dim3(grid), dim3(64 * kWideWaves), stream, p);
   }

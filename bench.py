@@ -1032,6 +1032,11 @@ def main():
         g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=4, **DEEP_GEMM)
         log(f"[bench] gemm, unified 256 x 256 x 32 tiles, 4 waves, S = 4: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_unified_256x256x32_4_waves_s4"] = g
+        g = bench_gemm(max(3, args.steps // 2), args.warmup, stages=4, out_dtype=torch.bfloat16,
+                       **DEEP_GEMM)
+        log(f"[bench] gemm, unified 256 x 256 x 32 tiles, 4 waves, S = 4, bf16 C: "
+            f"{g['tflops']:.1f} TFLOP/s")
+        extras["gemm_4096_bf16_unified_256x256x32_4_waves_s4_c_bf16"] = g
         g = bench_gemm(max(3, args.steps // 2), args.warmup, out_dtype=torch.bfloat16)
         log(f"[bench] gemm, bf16 C: {g['tflops']:.1f} TFLOP/s")
         extras["gemm_4096_bf16_c_bf16"] = g

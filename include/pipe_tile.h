@@ -89,7 +89,7 @@ typedef enum {
                                           full/empty barriers; M % 128 == N % 64 == 0 only, no
                                           checksums or trace (else PIPE_ERR_CONFIG).
                                           gemm: 256 x 256 output tiles (tile_m = tile_n = 256,
-                                          fp32 C, no trace) whose waves all load a share of each
+                                          no trace) whose waves all load a share of each
                                           stage and compute, with one workgroup barrier per K
                                           step; producer_waves and the commit policy do not
                                           apply. consumer_waves = 16 (64 x 64 output blocks):
@@ -97,7 +97,9 @@ typedef enum {
                                           blocks, one wave per SIMD): tile_k 64 with stages 2, or
                                           tile_k 32 with stages 3..5 (the fastest GEMM here; its
                                           64-byte LDS rows take a fixed chunk XOR and ignore
-                                          swizzle_shift). Else PIPE_ERR_CONFIG / PIPE_ERR_STAGES */
+                                          swizzle_shift; it alone also takes GEMM_C_BF16, written
+                                          straight from registers). Else PIPE_ERR_CONFIG /
+                                          PIPE_ERR_STAGES */
 #define PIPE_FLAG_LAZY_COMMIT 0x80u    /* copy/rowsum/gemm (specialised ring): the producer commits
                                           a tile only once `lag` younger tiles are in flight, never
                                           while its acquire waits for a slot. Without this flag a

@@ -607,8 +607,11 @@ def test_gemm_unified_validation_and_geometry():
     assert status(**dict(W, tile_k=16, stages=4)) == pt.PIPE_ERR_CONFIG
     assert status(**dict(U, tile_k=32, stages=4)) == pt.PIPE_ERR_CONFIG   # 16 waves: 64-K only
     assert status(**dict(W, consumer_waves=2)) == pt.PIPE_ERR_CONFIG
+    # bf16 C: the 32-K kernel only.
     assert status(**dict(W, tile_k=32, stages=4, flags=pt.PIPE_FLAG_UNIFIED |
-                         pt.PIPE_FLAG_GEMM_C_BF16)) == pt.PIPE_ERR_CONFIG
+                         pt.PIPE_FLAG_GEMM_C_BF16)) == pt.PIPE_OK
+    assert status(**dict(W, flags=pt.PIPE_FLAG_UNIFIED | pt.PIPE_FLAG_GEMM_C_BF16)) == \
+        pt.PIPE_ERR_CONFIG
     # Outside the unified flag, tile_k stays 64 and the ring 1..4 deep.
     assert status(tile_k=32) == pt.PIPE_ERR_CONFIG
     assert status(stages=5) == pt.PIPE_ERR_STAGES

@@ -4,7 +4,7 @@ CPU oracle: small-integer operands bit for bit (|C| <= 4 K < 2**24 is exact in
 fp32 in any order), uniform[-1, 1) operands within the GEMM tolerance. Three
 kernels: 16 waves of 64 x 64 output blocks on 64-K stages; 4 waves of
 128 x 128 blocks on 64-K stages; the same 4 waves on 32-K stages in rings of
-3 to 5 slots."""
+3 to 5 slots, which also write bf16 C."""
 import numpy as np
 import pytest
 import torch
@@ -117,3 +117,33 @@ def test_unified_gemm_4096_small_integers_bit_exact(kernel):
 def test_deep_unified_gemm_4096_column_major_bit_exact():
     A, B, ref = _operands(4096, 4096, 4096, seed=6, bcol=True)
     _assert_exact(_run(A, B, **KERNELS["w4k32s4"]), ref)
+
+
+@pytest.mark.parametrize("kernel", ["w4k32s3", "w4k32s4", "w4k32s5"])
+@pytest.mark.parametrize("shape", [(256, 256, 64), (1000, 1000, 1000), (300, 264, 72), (1, 8, 8)])
+@pytest.mark.parametrize("bcol", [False, True])
+def test_deep_unified_gemm_bf16_c_bit_exact(kernel, shape, bcol):
+    """bf16 C: each exact fp32 sum of small integers rounded once to bf16, as
+    the oracle's gemm_bf16 rounds the fp64 product."""
+    M, N, K = shape
+    A, B, _ = _operands(M, N, K, seed=M + K, bcol=bcol)
+    cfg = dict(KERNELS[kernel], flags=_U | pt.PIPE_FLAG_GEMM_C_BF16)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    _run(A, B, C=C, **cfg)
+    ref = R.gemm_bf16(_f32(A), _f32(B.contiguous()))
+    got = C.float().cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+
+
+def test_deep_unified_gemm_bf16_c_is_the_fp32_result_rounded():
+    """On uniform operands the bf16 C of the deep kernel is its fp32 C rounded
+    to nearest even, and its 4096^3 product stays within the GEMM tolerance."""
+    A, B, ref = _operands(4096, 4096, 4096, seed=9, bcol=False, kind="uniform")
+    cfg = KERNELS["w4k32s4"]
+    C32 = _run(A, B, **cfg)
+    Cb = torch.empty(4096, 4096, dtype=torch.bfloat16, device=DEV)
+    _run(A, B, C=Cb, **dict(cfg, flags=_U | pt.PIPE_FLAG_GEMM_C_BF16))
+    assert torch.equal(Cb, C32.to(torch.bfloat16))
+    res = R.within_tol(Cb.float().cpu().numpy(), ref, 1e-2)
+    assert res["ok"], res
