@@ -13,7 +13,10 @@ shape allows, and checks rows on both sides of the mark against the oracle:
 - GEMM, bf16 A of 65 664 x 32 768 (4.30 GB) times 32 768 x 256 (whole tiles)
   and of 65 601 x 32 776 times 32 776 x 200 (the masked kernel), integers in
   [-2, 2]: 48 sampled rows of C bit for bit against ``gemm_f64``
-  (|C| <= 4 K < 2**24).
+  (|C| <= 4 K < 2**24); the same A through the 4-wave unified GEMM on 32-K
+  stages;
+- that unified GEMM with a row-major B of 32 768 x 65 664 (4.30 GB), where
+  each K step's offset into B grows past 4 GiB: 48 sampled columns of C.
 """
 import numpy as np
 import pytest
@@ -79,21 +82,47 @@ def test_rowsum_beyond_4gib_sampled_rows_bit_exact():
     _free()
 
 
-@pytest.mark.parametrize("M,N,K", [(65664, 256, 32768), (65601, 200, 32776)],
-                         ids=["whole_tiles", "masked"])
-def test_gemm_a_beyond_4gib_sampled_rows_bit_exact(M, N, K):
+DEEP = dict(tile_m=256, tile_n=256, tile_k=32, consumer_waves=4, stages=4,
+            flags=pt.PIPE_FLAG_UNIFIED)
+
+
+@pytest.mark.parametrize("M,N,K,cfg", [(65664, 256, 32768, {}), (65601, 200, 32776, {}),
+                                       (65664, 256, 32768, DEEP)],
+                         ids=["whole_tiles", "masked", "unified_deep"])
+def test_gemm_a_beyond_4gib_sampled_rows_bit_exact(M, N, K, cfg):
     assert M * K * 2 > FOUR_GIB
-    print(f"[large] gemm {M}x{N}x{K}", flush=True)
+    print(f"[large] gemm {M}x{N}x{K} {cfg}", flush=True)
     A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=93, stream=0, device=DEV)
     B = synth.small_int((K, N), -2, 2, torch.bfloat16, seed=93, stream=1, device=DEV)
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    C = pt.pipe_gemm_mainloop(A, B, status=st)
+    C = pt.pipe_gemm_mainloop(A, B, status=st, **cfg)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     rows = _rows_across(M, K * 2, seed=3)
     a = A.index_select(0, torch.as_tensor(rows, device=DEV)).float().cpu().numpy()
     want = R.gemm_f64(a, B.float().cpu().numpy())
     got = C.cpu().numpy()[rows]
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
+    del A, B, C
+    _free()
+
+
+def test_unified_gemm_b_beyond_4gib_sampled_columns_bit_exact():
+    M, N, K = 256, 65664, 32768
+    assert K * N * 2 > FOUR_GIB
+    print(f"[large] unified gemm, B {K}x{N}", flush=True)
+    A = synth.small_int((M, K), -2, 2, torch.bfloat16, seed=94, stream=0, device=DEV)
+    B = synth.small_int((K, N), -2, 2, torch.bfloat16, seed=94, stream=1, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    C = pt.pipe_gemm_mainloop(A, B, status=st, **DEEP)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rng = np.random.default_rng(4)
+    cols = np.array(sorted({0, 1, N - 2, N - 1} | set(int(c) for c in rng.choice(N, 44, replace=False))))
+    idx = torch.as_tensor(cols, device=DEV)
+    want = R.gemm_f64(A.float().cpu().numpy(), B.index_select(1, idx).float().cpu().numpy())
+    got = C.index_select(1, idx).cpu().numpy()
     bad = np.argwhere(got != want)
     assert bad.size == 0, f"{bad.shape[0]} mismatches, first {bad[:4].tolist()}"
     del A, B, C
