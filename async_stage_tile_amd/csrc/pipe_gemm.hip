@@ -1118,26 +1118,6 @@ __device__ __forceinline__ void deep_issue(const GemmParams& p, const DeepSrc& s
   for (int j = 0; j < kDeepLoads; ++j) deep_dma<BCOL, MASKED>(p, s, sbase, ks, j, wave, lane);
 }
 
-// The 16 MFMAs of one sub-step with this wave's 8 DMA blocks of stage ks
-// issued between them, one after every second MFMA, so the matrix unit is
-// fed while the loads go out.
-template <bool BCOL, bool MASKED>
-__device__ __forceinline__ void mfma_wide_with_dma(f32x16 (&acc)[4][4], const WideFrags& f,
-                                                   const GemmParams& p, const DeepSrc& s,
-                                                   uint32_t sbase, int ks, int wave, int lane) {
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
-      if ((ni & 1) == 1) {
-        __builtin_amdgcn_sched_barrier(0);
-        deep_dma<BCOL, MASKED>(p, s, sbase, ks, mi * 2 + (ni >> 1), wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-}
-
 // A (or column-major B) fragment of a 64-byte-row slot: lane l takes K chunk
 // kk * 2 + l / 32 of row row0 + l % 32.
 __device__ __forceinline__ bf16x8 load_row_frag4(const uint8_t* slot, int row0, int kk, int li,
@@ -1181,15 +1161,16 @@ __device__ __forceinline__ void load_deep_piece(WideFrags& f, int q, int kk, con
 // sub-step's fragments g read one after each of the first 8 MFMAs, so the
 // LDS queue never holds a burst that would stall the wave's MFMA issue. With
 // DMA, this wave's 8 DMA blocks of stage ks go out one after every second
-// MFMA as well. Unrolled by template recursion: the schedule pins take
-// constants.
+// MFMA as well, where `dma` holds (a wave-uniform predicate: the MFMAs are
+// one sequence either way, which keeps the accumulators in one register
+// chain). Unrolled by template recursion: the schedule pins take constants.
 template <int I, bool BCOL, bool MASKED, bool DMA>
 __device__ __forceinline__ void mfma_wide_pipelined(f32x16 (&acc)[4][4], const WideFrags& f,
                                                     WideFrags& g, int kk, const uint8_t* sa,
                                                     const uint8_t* sb, int wm, int wn, int li,
                                                     int lk, int lane, const GemmParams& p,
                                                     const DeepSrc& s, uint32_t sbase, int ks,
-                                                    int wave) {
+                                                    int wave, bool dma = true) {
   if constexpr (I < 16) {
     constexpr int kReads = (I < 4 || BCOL) ? 1 : 2;  // LDS reads of piece I
     acc[I >> 2][I & 3] =
@@ -1199,11 +1180,11 @@ __device__ __forceinline__ void mfma_wide_pipelined(f32x16 (&acc)[4][4], const W
     if constexpr (I < 8) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
     if constexpr (DMA && (I & 1) == 1) {
       __builtin_amdgcn_sched_barrier(0);
-      deep_dma<BCOL, MASKED>(p, s, sbase, ks, I >> 1, wave, lane);
+      if (dma) deep_dma<BCOL, MASKED>(p, s, sbase, ks, I >> 1, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_wide_pipelined<I + 1, BCOL, MASKED, DMA>(acc, f, g, kk, sa, sb, wm, wn, li, lk, lane, p, s,
-                                                  sbase, ks, wave);
+                                                  sbase, ks, wave, dma);
   }
 }
 
@@ -1249,40 +1230,27 @@ __global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_deep_kernel(Gemm
     WideFrags f0, f1;
     load_deep<BCOL>(f0, 0, &lds.ring[0][0], &lds.ring[0][b_off], wm, wn, li, lk, lane, p);
     int slot = 0;
-    int ks = 0;
-    // Steady state: each step refills the slot of the step before with the
-    // stage S - 1 ahead, and at least S - 3 stages' loads are younger than
-    // the next one's.
-    for (; ks < ksteps - (S - 1); ++ks) {
+    for (int ks = 0; ks < ksteps; ++ks) {
       const uint8_t* sl = &lds.ring[slot][0];
-      mfma_wide_pipelined<0, BCOL, MASKED, false>(acc, f0, f1, 1, sl, sl + b_off, wm, wn, li, lk,
-                                               lane, p, src, 0, 0, wave);
       const int next_slot = slot + 1 == S ? 0 : slot + 1;
       const int fill = slot == 0 ? S - 1 : slot - 1;  // the slot of step ks - 1
-      wait_vmcnt<(S - 3) * kDeepLoads>();
-      __syncthreads();
-      const uint8_t* nl = &lds.ring[next_slot][0];
-      mfma_wide_pipelined<0, BCOL, MASKED, true>(acc, f1, f0, 0, nl, nl + b_off, wm, wn, li, lk, lane,
-                                              p, src, ring + fill * kDeepStageBytes, ks + S - 1,
-                                              wave);
-      slot = next_slot;
-    }
-    // The tile's last S - 1 steps (or all of a short one) issue nothing.
-    for (; ks < ksteps; ++ks) {
-      const uint8_t* sl = &lds.ring[slot][0];
-      load_deep<BCOL>(f1, 1, sl, sl + b_off, wm, wn, li, lk, lane, p);
-      mfma_wide(acc, f0);
-      const int next_slot = slot + 1 == S ? 0 : slot + 1;
+      // First half: MFMAs on the step's first 16 K, reads of its second.
+      mfma_wide_pipelined<0, BCOL, MASKED, false>(acc, f0, f1, 1, sl, sl + b_off, wm, wn, li, lk,
+                                                  lane, p, src, 0, 0, wave);
       if (ks + 1 < ksteps) {
         // Stage ks + 1 has landed once at most S - 3 stages' loads are
-        // younger; where fewer were issued, the wave drains.
+        // younger; near the tile's end fewer were issued, and the wave drains.
         if (ks + S - 2 < ksteps) wait_vmcnt<(S - 3) * kDeepLoads>();
         else wait_vmcnt<0>();
         __syncthreads();
-        const uint8_t* nl = &lds.ring[next_slot][0];
-        load_deep<BCOL>(f0, 0, nl, nl + b_off, wm, wn, li, lk, lane, p);
       }
-      mfma_wide(acc, f1);
+      // Second half: MFMAs on the second 16 K, reads of the next stage's first
+      // (after the tile's last step they read a slot nobody uses), and the
+      // refill of the slot of step ks - 1 with the stage S - 1 ahead.
+      const uint8_t* nl = &lds.ring[next_slot][0];
+      mfma_wide_pipelined<0, BCOL, MASKED, true>(acc, f1, f0, 0, nl, nl + b_off, wm, wn, li, lk,
+                                                 lane, p, src, ring + fill * kDeepStageBytes,
+                                                 ks + S - 1, wave, ks + S - 1 < ksteps);
       slot = next_slot;
     }
     // Every wave has issued its last MFMAs, so every slot's reads are done:
