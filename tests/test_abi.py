@@ -619,3 +619,8 @@ def test_gemm_unified_validation_and_geometry():
     assert status(tile_m=256, tile_n=256, consumer_waves=16, stages=2) == pt.PIPE_ERR_CONFIG
     assert status(flags=pt.PIPE_FLAG_UNIFIED) == pt.PIPE_ERR_CONFIG
     assert status(tile_m=256, consumer_waves=8, flags=pt.PIPE_FLAG_UNIFIED) == pt.PIPE_ERR_CONFIG
+
+
+def test_gemm_unified_deep_preset_is_a_valid_config():
+    q = pt.pipe_query_kernel(pt.PIPE_OP_GEMM, 4096, 4096, 4096, **pt.GEMM_UNIFIED_DEEP)
+    assert (q["items"], q["threads"], q["lds_bytes"], q["tiles_per_item"]) == (256, 256, 131072, 128)
