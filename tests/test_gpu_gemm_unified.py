@@ -147,3 +147,35 @@ def test_deep_unified_gemm_bf16_c_is_the_fp32_result_rounded():
     assert torch.equal(Cb, C32.to(torch.bfloat16))
     res = R.within_tol(Cb.float().cpu().numpy(), ref, 1e-2)
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
+@pytest.mark.parametrize("bcol", [False, True])
+@pytest.mark.parametrize("c_bf16", [False, True])
+def test_unified_gemm_strided_operands(kernel, bcol, c_bf16):
+    """A, B and C as views into wider buffers (lda = K + 64, ldb = N + 128 or
+    K + 64 for column-major B, ldc = N + 64); the pitch padding of C stays
+    untouched."""
+    if c_bf16 and not kernel.startswith("w4k32"):
+        pytest.skip("bf16 C: the 32-K kernel only")
+    M, N, K = 520, 384, 328
+    Abig = synth.small_int((M, K + 64), -2, 2, torch.bfloat16, seed=71, stream=0, device=DEV)
+    A = Abig[:, 32:32 + K]
+    if bcol:
+        Btbig = synth.small_int((N, K + 64), -2, 2, torch.bfloat16, seed=71, stream=1, device=DEV)
+        B = Btbig[:, 16:16 + K].t()                  # K x N, unit row stride, ldb = K + 64
+    else:
+        Bbig = synth.small_int((K, N + 128), -2, 2, torch.bfloat16, seed=71, stream=1, device=DEV)
+        B = Bbig[:, 64:64 + N]
+    dt = torch.bfloat16 if c_bf16 else torch.float32
+    Cbig = torch.full((M, N + 64), 7.0, dtype=dt, device=DEV)
+    C = Cbig[:, 8:8 + N]
+    cfg = dict(KERNELS[kernel])
+    if c_bf16:
+        cfg["flags"] = cfg["flags"] | pt.PIPE_FLAG_GEMM_C_BF16
+    _run(A, B, C=C, **cfg)
+    a, b = _f32(A.contiguous()), _f32(B.contiguous())
+    ref = R.gemm_bf16(a, b) if c_bf16 else R.gemm_f64(a, b)
+    assert np.array_equal(C.float().cpu().numpy(), ref)
+    pad = Cbig.float().cpu().numpy()
+    assert (pad[:, :8] == 7.0).all() and (pad[:, 8 + N:] == 7.0).all()
