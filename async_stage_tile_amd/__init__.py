@@ -401,10 +401,12 @@ def _gemm_b(B):
     return K, N, ldb, False
 
 
-# The fastest GEMM configuration on MI355X: 256 x 256 output tiles whose 4
-# waves (one per SIMD) each own a 128 x 128 block, fed by a four-slot ring of
-# 32-K stages (PIPE_FLAG_UNIFIED). Pass it as keyword arguments:
-# pipe_gemm_mainloop(A, B, **GEMM_UNIFIED_DEEP). bf16 C is supported.
+# The fastest GEMM configuration on MI355X for products with at least 256
+# output tiles of 256 x 256 (one per CU; e.g. 4096 x 4096 and up): 4 waves (one
+# per SIMD) each own a 128 x 128 block, fed by a four-slot ring of 32-K stages
+# (PIPE_FLAG_UNIFIED). Pass it as keyword arguments:
+# pipe_gemm_mainloop(A, B, **GEMM_UNIFIED_DEEP). bf16 C is supported. Smaller
+# products keep more CUs busy with the default 128 x 128 tiles.
 GEMM_UNIFIED_DEEP = dict(tile_m=256, tile_n=256, tile_k=32, consumer_waves=4, stages=4,
                          flags=PIPE_FLAG_UNIFIED)
 
