@@ -1003,6 +1003,11 @@ __global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_kernel(GemmParam
       wait_lgkmcnt0();
       slot ^= 1;
     }
+    // The last MFMAs' results land before any accumulator is read (the guard of
+    // the 32-K kernel's epilogue below, where a read came too early).
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_sched_barrier(0);
     float* C = static_cast<float*>(p.C);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
