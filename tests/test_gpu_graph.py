@@ -34,6 +34,7 @@ def test_copy_rowsum_gemm_replayed_from_one_graph():
     Gb = torch.empty(512, 384, dtype=torch.bfloat16, device=DEV)
     Gc = torch.empty(256, 384, dtype=torch.float32, device=DEV)
     Gc2 = torch.empty(256, 384, dtype=torch.bfloat16, device=DEV)   # 256 x 128 tiles, bf16 C
+    Gc3 = torch.empty(256, 384, dtype=torch.float32, device=DEV)    # unified 4-wave, 32-K stages
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
 
     def fill(seed):
@@ -41,7 +42,7 @@ def test_copy_rowsum_gemm_replayed_from_one_graph():
         A.copy_(synth.small_int((1000, 3000), -8, 8, torch.float16, seed=seed + 1).to(DEV))
         Ga.copy_(synth.small_int((256, 512), -2, 2, torch.bfloat16, seed=seed + 2).to(DEV))
         Gb.copy_(synth.small_int((512, 384), -2, 2, torch.bfloat16, seed=seed + 3).to(DEV))
-        for t in (dst, chk, sums, Gc, Gc2):
+        for t in (dst, chk, sums, Gc, Gc2, Gc3):
             t.zero_()
 
     def body():
@@ -50,6 +51,7 @@ def test_copy_rowsum_gemm_replayed_from_one_graph():
         pt.pipe_rowsum(A, sums, ws, status=status)
         pt.pipe_gemm_mainloop(Ga, Gb, Gc, status=status)
         pt.pipe_gemm_mainloop(Ga, Gb, Gc2, status=status, tile_m=256, consumer_waves=8)
+        pt.pipe_gemm_mainloop(Ga, Gb, Gc3, status=status, **pt.GEMM_UNIFIED_DEEP)
 
     fill(10)
     body()                      # eager run first: the same calls, outside any graph
@@ -75,6 +77,7 @@ def test_copy_rowsum_gemm_replayed_from_one_graph():
         assert np.array_equal(sums.cpu().numpy(), R.rowsum_exact(A.cpu().numpy())), rep
         ref = R.gemm_f64(Ga.float().cpu().numpy(), Gb.float().cpu().numpy())
         assert np.array_equal(Gc.cpu().numpy(), ref), rep
+        assert np.array_equal(Gc3.cpu().numpy(), ref), rep
         assert np.array_equal(Gc2.float().cpu().numpy(),
                               R.gemm_bf16(Ga.float().cpu().numpy(), Gb.float().cpu().numpy())), rep
         # eager work between replays, on the same buffers
