@@ -1096,7 +1096,8 @@ __device__ __forceinline__ void deep_dma(const GemmParams& p, const DeepSrc& s, 
   const int k_left = p.K - ks * kDeepK;
   if (j < 4) {
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
-    dma_block(chunk_src<MASKED>(s.a[j] + ks * (kDeepK * 2), ((s.rows_in >> j) & 1) && c * 8 < k_left),
+    dma_block(chunk_src<MASKED>(s.a[j] + (int64_t)ks * (kDeepK * 2),
+                                ((s.rows_in >> j) & 1) && c * 8 < k_left),
               sbase + (wave * 4 + j) * kBlockBytes);
   } else {
     const int jb = j - 4;
@@ -1105,7 +1106,7 @@ __device__ __forceinline__ void deep_dma(const GemmParams& p, const DeepSrc& s, 
     const uint8_t* src;
     if constexpr (BCOL) {
       const int c = (lane & 3) ^ ((lane >> 4) & 3);
-      src = s.b[jb] + ks * (kDeepK * 2);
+      src = s.b[jb] + (int64_t)ks * (kDeepK * 2);
       inside = ((s.rows_in >> (4 + jb)) & 1) && c * 8 < k_left;
     } else {
       const int kr = (qq & 7) * 4 + (lane >> 4);
