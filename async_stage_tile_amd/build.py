@@ -32,7 +32,8 @@ UNITS = [
     ("pipe_stream.hip", "pipe_stream_s5_6.o", ["PIPE_STREAM_STAGES_LO=5", "PIPE_STREAM_STAGES_HI=6"]),
     ("pipe_stream.hip", "pipe_stream_s7_8.o", ["PIPE_STREAM_STAGES_LO=7", "PIPE_STREAM_STAGES_HI=8"]),
     ("pipe_unified.hip", "pipe_unified.o", []),
-    ("pipe_gemm.hip", "pipe_gemm.o", []),
+    ("pipe_gemm.hip", "pipe_gemm_ring.o", ["PIPE_GEMM_PART=1"]),
+    ("pipe_gemm.hip", "pipe_gemm_unified.o", ["PIPE_GEMM_PART=2"]),
 ]
 # Kept for callers that list the tile-stream sources.
 SOURCES = sorted({u[0] for u in UNITS})

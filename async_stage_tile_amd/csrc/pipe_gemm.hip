@@ -83,6 +83,12 @@
 
 namespace pipe {
 
+// The library builds this file as two objects, so that the compiler's work
+// splits: PIPE_GEMM_PART=1 defines the warp-specialised rings' launchers,
+// PIPE_GEMM_PART=2 the unified GEMMs' launcher (each instantiates only its own
+// kernels); without the define, one object holds both.
+hipError_t launch_gemm_unified(int stages, int grid, const GemmParams& p, hipStream_t stream);
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1306,6 +1312,9 @@ __global__ void __launch_bounds__(64 * kWideWaves, 1) gemm_wide_deep_kernel(Gemm
   wait_vmcnt<0>();
 }
 
+#if !defined(PIPE_GEMM_PART) || PIPE_GEMM_PART == 2
+}  // namespace
+
 hipError_t launch_gemm_unified(int stages, int grid, const GemmParams& p, hipStream_t stream) {
   if (stages < 2 || stages > 5 || p.trace != nullptr) return hipErrorInvalidValue;
   if (p.c_bf16 && !(p.unified == kWideWaves && stages >= 3)) return hipErrorInvalidValue;
@@ -1339,6 +1348,10 @@ hipError_t launch_gemm_unified(int stages, int grid, const GemmParams& p, hipStr
                         : (bcol ? gemm_unified_kernel<true, false> : gemm_unified_kernel<false, false>);
   return launch_or_record(k, dim3(grid), dim3(64 * kUniWaves), stream, p);
 }
+
+namespace {
+#endif
+#if !defined(PIPE_GEMM_PART) || PIPE_GEMM_PART == 1
 
 
 
@@ -1402,9 +1415,11 @@ hipError_t launch_gemm_mt(int stages, int producers, int grid, const GemmParams&
   }
   return launch_gemm_epi<kEpiWaveStaged, MT>(stages, producers, grid, p, stream);
 }
+#endif
 
 }  // namespace
 
+#if !defined(PIPE_GEMM_PART) || PIPE_GEMM_PART == 1
 hipError_t launch_gemm(int stages, int producers, int grid, const GemmParams& p,
                        hipStream_t stream) {
   if (p.unified) return launch_gemm_unified(stages, grid, p, stream);
@@ -1427,5 +1442,6 @@ int gemm_lds_bytes(int stages, bool c_bf16, bool store_wave, int tile_m) {
 int gemm_threads(int producers, bool c_bf16, bool store_wave, int tile_m) {
   return 64 * (producers + 4 * (tile_m / kGemmTile) + (c_bf16 && store_wave ? 1 : 0));
 }
+#endif
 
 }  // namespace pipe
